@@ -1,0 +1,130 @@
+"""ctypes front of the fp64 CPU oracle (oracle/lf_oracle.c).
+
+TEST INFRASTRUCTURE: only the test suite, the smoke check and the CPU
+baseline leg of the benchmark import this package.  The product path never
+does.  Inputs may be torch tensors or numpy arrays; q/k/v are passed as
+float32 (exact for bf16 and fp32 data) and results come back as float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liblforacle.so")
+_lib = None
+
+
+def open_library(path):
+    """Load an oracle build at ``path`` and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    LL = ctypes.c_longlong
+    lib.lf_oracle_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I]
+    lib.lf_oracle_fwd.restype = I
+    lib.lf_oracle_rows.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, LL, P, I]
+    lib.lf_oracle_rows.restype = I
+    lib.lf_oracle_neighbours.argtypes = [I, I, I, P, I, P, I, P]
+    lib.lf_oracle_neighbours.restype = I
+    lib.lf_oracle_count_pairs.argtypes = [I, I, I, I, P, P, I, P]
+    lib.lf_oracle_count_pairs.restype = LL
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        _lib = open_library(_LIB_PATH)
+    return _lib
+
+
+def _f32(x):
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().float().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _i32(x, n=None):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(list(x) if not isinstance(x, np.ndarray) else x, dtype=np.int32))
+    return a
+
+
+def _u8(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray((np.asarray(x) != 0).astype(np.uint8))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def fwd(q, k, v, r, dilation=None, global_idx=None, key_padding_mask=None, n_threads=0,
+        return_threads=False, lib=None):
+    """Full forward in fp64: returns out[B][H][T][d] (numpy float64)."""
+    lib = lib or _load()
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    B, H, T, d = qf.shape
+    dil = _i32(dilation)
+    g = _i32(global_idx if global_idx is not None else [])
+    pad = _u8(key_padding_mask)
+    out = np.zeros((B, H, T, d), dtype=np.float64)
+    nt = lib.lf_oracle_fwd(_ptr(qf), _ptr(kf), _ptr(vf), B, H, T, d, int(r), _ptr(dil), _ptr(g),
+                           int(g.size), _ptr(pad), _ptr(out), int(n_threads))
+    if nt < 0:
+        raise ValueError("oracle rejected its arguments")
+    return (out, nt) if return_threads else out
+
+
+def rows(q, k, v, r, rows_flat, dilation=None, global_idx=None, key_padding_mask=None,
+         n_threads=0, return_threads=False, lib=None):
+    """Selected output rows: rows_flat[e] = (b*H + h)*T + i -> out[e][d]."""
+    lib = lib or _load()
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    B, H, T, d = qf.shape
+    dil = _i32(dilation)
+    g = _i32(global_idx if global_idx is not None else [])
+    pad = _u8(key_padding_mask)
+    rr = np.ascontiguousarray(np.asarray(rows_flat, dtype=np.int64))
+    out = np.zeros((rr.size, d), dtype=np.float64)
+    nt = lib.lf_oracle_rows(_ptr(qf), _ptr(kf), _ptr(vf), B, H, T, d, int(r), _ptr(dil), _ptr(g),
+                            int(g.size), _ptr(pad), _ptr(rr), int(rr.size), _ptr(out), int(n_threads))
+    if nt < 0:
+        raise ValueError("oracle rejected its arguments")
+    return (out, nt) if return_threads else out
+
+
+def neighbours(T, r, delta, i, global_idx=None, pad_row=None, lib=None):
+    """Sorted list N(i) of one query (empty for a padded query)."""
+    lib = lib or _load()
+    g = _i32(global_idx if global_idx is not None else [])
+    pad = _u8(pad_row)
+    buf = np.zeros(T, dtype=np.int32)
+    n = lib.lf_oracle_neighbours(int(T), int(r), int(delta), _ptr(g), int(g.size), _ptr(pad), int(i),
+                                 _ptr(buf))
+    if n < 0:
+        raise ValueError("oracle rejected its arguments")
+    return [int(x) for x in buf[:n]]
+
+
+def count_pairs(B, H, T, r, dilation=None, global_idx=None, key_padding_mask=None, lib=None):
+    """Sum of |N(i)| over all rows (padded rows count 0)."""
+    lib = lib or _load()
+    dil = _i32(dilation)
+    g = _i32(global_idx if global_idx is not None else [])
+    pad = _u8(key_padding_mask)
+    n = lib.lf_oracle_count_pairs(int(B), int(H), int(T), int(r), _ptr(dil), _ptr(g), int(g.size),
+                                  _ptr(pad))
+    if n < 0:
+        raise ValueError("oracle rejected its arguments")
+    return int(n)

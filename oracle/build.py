@@ -1,0 +1,27 @@
+"""Compile the fp64 CPU oracle (plain C, gcc) into oracle/liblforacle.so.
+
+Test infrastructure: the oracle checks the HIP library; it is never part
+of the product path.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "lf_oracle.c")
+LIB = os.path.join(HERE, "liblforacle.so")
+
+
+def build(src: str = SRC, out: str = LIB, verbose: bool = False) -> str:
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+           "-shared", "-pthread", src, "-o", out + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,303 @@
+/*
+ * lf_oracle.c -- plain fp64 CPU oracle for the Longformer sparse
+ * self-attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or
+ * calls this file: only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark do.  It shares no code, header, table or
+ * helper with the HIP library; the two meet only through the seeded inputs.
+ *
+ * What it computes (sources are the pages' own sections):
+ *
+ *   Longformer (eightmm.github.io/papers/architectures/longformer),
+ *   "Sliding-Window Attention":  N_local(i) = { j : |i - j| <= r },
+ *       y_i = sum_{j in N(i)} softmax_j( q_i . k_j / sqrt(d_k) ) v_j .
+ *   same page, "Global Attention":  for i in G, N(i) = all positions;
+ *       for i not in G, N(i) = N_local(i) U G   (a set union: a global key
+ *       that is also inside the window is counted once).
+ *   same page, "Mask View": M_ij = 0 on N(i), -inf elsewhere, so the
+ *       softmax runs over exactly the allowed set.
+ *   Longformer (ciallo.wiki) §2.2.3 and "Longformer长序列处理" (aiqz.cc),
+ *       section 膨胀窗口设计: a dilated window samples every delta-th
+ *       position (distances delta, 2*delta, ...), same key count, wider
+ *       reach.  Reading used here: key j is in N_local(i) iff
+ *       |i - j| <= r*delta and (i - j) mod delta == 0.
+ *   "Longformer长序列处理", Python 演示 note 3: positions outside the
+ *       sequence are dropped (no wrap-around).
+ *   same page, "Implementation Reading" asks that padding be masked:
+ *       a padded key leaves every query's set (global rows included);
+ *       a padded query row is defined as all zeros.
+ *
+ * Indices are 0-based (the pages count from 1).  Arithmetic is IEEE fp64;
+ * inputs arrive as float32 (bf16 and fp32 inputs are exact in float32) and
+ * are widened exactly.  Sums run in ascending key order, so the result is
+ * reproducible bit for bit.
+ *
+ * Pins (checked in the CPU test suite): dense brute force with an explicit
+ * T x T boolean mask on tiny T; closed-form neighbour counts; v == 1 gives
+ * y == 1; q == 0 gives the plain mean of v over N(i); r = 0 with no globals
+ * gives y_i = v_i; r >= T-1 equals textbook dense attention; a dilated
+ * head equals delta undilated problems on the residue subsequences; keys
+ * outside N(i) do not influence row i; global rows equal dense rows.
+ */
+#define _GNU_SOURCE
+#include <math.h>
+#include <pthread.h>
+#include <sched.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* The global set G: sorted, duplicates removed, as a set of positions. */
+
+typedef struct {
+    int *pos;  /* sorted, unique */
+    int n;
+} gset_t;
+
+static int cmp_int(const void *a, const void *b) {
+    int x = *(const int *)a, y = *(const int *)b;
+    return (x > y) - (x < y);
+}
+
+static int gset_make(gset_t *g, const int *idx, int n, int T) {
+    g->n = 0;
+    g->pos = NULL;
+    if (n <= 0) return 0;
+    g->pos = (int *)malloc(sizeof(int) * (size_t)n);
+    if (!g->pos) return -1;
+    for (int i = 0; i < n; i++) {
+        if (idx[i] < 0 || idx[i] >= T) { free(g->pos); g->pos = NULL; return -1; }
+        g->pos[i] = idx[i];
+    }
+    qsort(g->pos, (size_t)n, sizeof(int), cmp_int);
+    int m = 0;
+    for (int i = 0; i < n; i++)
+        if (m == 0 || g->pos[m - 1] != g->pos[i]) g->pos[m++] = g->pos[i];
+    g->n = m;
+    return 0;
+}
+
+static int gset_has(const gset_t *g, int i) {
+    int lo = 0, hi = g->n - 1;
+    while (lo <= hi) {
+        int mid = (lo + hi) / 2;
+        if (g->pos[mid] == i) return 1;
+        if (g->pos[mid] < i) lo = mid + 1; else hi = mid - 1;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* N(i) for one query, written out as a sorted list of key positions.
+ * Returns |N(i)|; a padded query gets the empty set (its row is zero). */
+
+static int neighbours(int T, int r, int delta, const gset_t *G,
+                      const unsigned char *pad /* [T] or NULL */, int i, int *out) {
+    if (pad && pad[i]) return 0;
+    int n = 0;
+    if (gset_has(G, i)) {
+        /* global query: every valid position */
+        for (int j = 0; j < T; j++)
+            if (!(pad && pad[j])) out[n++] = j;
+        return n;
+    }
+    /* N_local(i): j = i + t*delta for t in [-r, r], inside [0, T) */
+    long long tlo = -(long long)r, thi = (long long)r;
+    long long tmin = -((long long)i / delta);            /* smallest t with j >= 0 */
+    long long tmax = ((long long)(T - 1) - i) / delta;   /* largest t with j < T  */
+    if (tlo < tmin) tlo = tmin;
+    if (thi > tmax) thi = tmax;
+    /* merge the ascending window with the ascending global list (set union) */
+    int gi = 0;
+    for (long long t = tlo; t <= thi; t++) {
+        int j = (int)((long long)i + t * delta);
+        while (gi < G->n && G->pos[gi] < j) {
+            int g = G->pos[gi++];
+            if (!(pad && pad[g])) out[n++] = g;
+        }
+        if (gi < G->n && G->pos[gi] == j) gi++; /* same key: keep one copy */
+        if (!(pad && pad[j])) out[n++] = j;
+    }
+    while (gi < G->n) {
+        int g = G->pos[gi++];
+        if (!(pad && pad[g])) out[n++] = g;
+    }
+    return n;
+}
+
+/* ------------------------------------------------------------------ */
+/* One output row: softmax over N(i) of q_i . k_j / sqrt(d), weights on v. */
+
+static void attend_row(const float *qi, const float *K, const float *V, int d,
+                       const int *nb, int n, double *s, double *yi) {
+    for (int c = 0; c < d; c++) yi[c] = 0.0;
+    if (n == 0) return;
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double m = -INFINITY;
+    for (int t = 0; t < n; t++) {
+        const float *kj = K + (size_t)nb[t] * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; c++) dot += (double)qi[c] * (double)kj[c];
+        s[t] = dot * inv_sqrt_d;
+        if (s[t] > m) m = s[t];
+    }
+    double l = 0.0;
+    for (int t = 0; t < n; t++) {
+        s[t] = exp(s[t] - m);
+        l += s[t];
+    }
+    for (int t = 0; t < n; t++) {
+        const float *vj = V + (size_t)nb[t] * d;
+        double w = s[t];
+        for (int c = 0; c < d; c++) yi[c] += w * (double)vj[c];
+    }
+    for (int c = 0; c < d; c++) yi[c] /= l;
+}
+
+/* ------------------------------------------------------------------ */
+/* Threaded driver over a list of rows. */
+
+typedef struct {
+    const float *q, *k, *v;
+    int B, H, T, d, r;
+    const int *dil;
+    const gset_t *G;
+    const unsigned char *pad;
+    const long long *rows;  /* NULL: all rows in order */
+    long long n_rows;
+    double *out;
+    int n_threads, tid;
+    int err;
+} job_t;
+
+static void *worker(void *arg) {
+    job_t *jb = (job_t *)arg;
+    int *nb = (int *)malloc(sizeof(int) * (size_t)jb->T);
+    double *s = (double *)malloc(sizeof(double) * (size_t)jb->T);
+    if (!nb || !s) { jb->err = 1; free(nb); free(s); return NULL; }
+    const long long chunk = 16;
+    for (long long c0 = (long long)jb->tid * chunk; c0 < jb->n_rows;
+         c0 += (long long)jb->n_threads * chunk) {
+        long long c1 = c0 + chunk < jb->n_rows ? c0 + chunk : jb->n_rows;
+        for (long long e = c0; e < c1; e++) {
+            long long flat = jb->rows ? jb->rows[e] : e;
+            long long bh = flat / jb->T;
+            int i = (int)(flat % jb->T);
+            int b = (int)(bh / jb->H), h = (int)(bh % jb->H);
+            int delta = jb->dil ? jb->dil[h] : 1;
+            const unsigned char *padrow = jb->pad ? jb->pad + (size_t)b * jb->T : NULL;
+            int n = neighbours(jb->T, jb->r, delta, jb->G, padrow, i, nb);
+            const size_t base = (size_t)bh * jb->T * jb->d;
+            attend_row(jb->q + base + (size_t)i * jb->d, jb->k + base, jb->v + base,
+                       jb->d, nb, n, s, jb->out + (size_t)e * jb->d);
+        }
+    }
+    free(nb);
+    free(s);
+    return NULL;
+}
+
+static int host_threads(void) {
+    cpu_set_t set;
+    if (sched_getaffinity(0, sizeof(set), &set) == 0) {
+        int c = CPU_COUNT(&set);
+        if (c > 0) return c;
+    }
+    return 1;
+}
+
+static int check_args(int B, int H, int T, int d, int r, const int *dil) {
+    if (B < 1 || H < 1 || T < 1 || d < 1 || r < 0) return -1;
+    if (dil)
+        for (int h = 0; h < H; h++)
+            if (dil[h] < 1) return -1;
+    return 0;
+}
+
+static int run(const float *q, const float *k, const float *v, int B, int H, int T, int d, int r,
+               const int *dil, const int *gidx, int ng, const unsigned char *pad,
+               const long long *rows, long long n_rows, double *out, int n_threads) {
+    if (check_args(B, H, T, d, r, dil)) return -1;
+    if (ng < 0 || (ng > 0 && !gidx)) return -1;
+    gset_t G;
+    if (gset_make(&G, gidx, ng, T)) return -1;
+    if (n_threads <= 0) n_threads = host_threads();
+    if ((long long)n_threads > n_rows) n_threads = n_rows > 0 ? (int)n_rows : 1;
+    job_t *jobs = (job_t *)calloc((size_t)n_threads, sizeof(job_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); free(G.pos); return -1; }
+    int err = 0;
+    for (int t = 0; t < n_threads; t++) {
+        job_t j = {q, k, v, B, H, T, d, r, dil, &G, pad, rows, n_rows, out, n_threads, t, 0};
+        jobs[t] = j;
+    }
+    for (int t = 1; t < n_threads; t++)
+        if (pthread_create(&th[t], NULL, worker, &jobs[t])) { jobs[t].err = 1; th[t] = 0; }
+    worker(&jobs[0]);
+    for (int t = 1; t < n_threads; t++) if (th[t]) pthread_join(th[t], NULL);
+    for (int t = 0; t < n_threads; t++) err |= jobs[t].err;
+    free(jobs);
+    free(th);
+    free(G.pos);
+    return err ? -1 : n_threads;
+}
+
+/* ------------------------------------------------------------------ */
+/* Exported entry points (plain C ABI for ctypes). */
+
+/* Full forward: out[B][H][T][d] in fp64.  Returns the thread count used,
+ * or -1 on invalid arguments. */
+int lf_oracle_fwd(const float *q, const float *k, const float *v, int B, int H, int T, int d,
+                  int r, const int *dilation, const int *global_idx, int n_global,
+                  const unsigned char *key_padding_mask, double *out, int n_threads) {
+    long long n = (long long)B * H * T;
+    return run(q, k, v, B, H, T, d, r, dilation, global_idx, n_global, key_padding_mask,
+               NULL, n, out, n_threads);
+}
+
+/* Selected rows only: rows[e] = (b*H + h)*T + i; out_rows[e][d]. */
+int lf_oracle_rows(const float *q, const float *k, const float *v, int B, int H, int T, int d,
+                   int r, const int *dilation, const int *global_idx, int n_global,
+                   const unsigned char *key_padding_mask, const long long *rows, long long n_rows,
+                   double *out_rows, int n_threads) {
+    for (long long e = 0; e < n_rows; e++)
+        if (rows[e] < 0 || rows[e] >= (long long)B * H * T) return -1;
+    return run(q, k, v, B, H, T, d, r, dilation, global_idx, n_global, key_padding_mask,
+               rows, n_rows, out_rows, n_threads);
+}
+
+/* N(i) of one query of sequence b, head stride delta: sorted positions
+ * into idx (capacity T).  Returns |N(i)|, or -1 on invalid arguments. */
+int lf_oracle_neighbours(int T, int r, int delta, const int *global_idx, int n_global,
+                         const unsigned char *pad_row, int i, int *idx) {
+    if (T < 1 || r < 0 || delta < 1 || i < 0 || i >= T) return -1;
+    gset_t G;
+    if (gset_make(&G, global_idx, n_global, T)) return -1;
+    int n = neighbours(T, r, delta, &G, pad_row, i, idx);
+    free(G.pos);
+    return n;
+}
+
+/* Sum over all (b, h, i) of |N(i)|: the number of (query, key) pairs the
+ * softmax runs over.  Returns -1 on invalid arguments. */
+long long lf_oracle_count_pairs(int B, int H, int T, int r, const int *dilation,
+                                const int *global_idx, int n_global,
+                                const unsigned char *key_padding_mask) {
+    if (check_args(B, H, T, 1, r, dilation)) return -1;
+    gset_t G;
+    if (gset_make(&G, global_idx, n_global, T)) return -1;
+    int *nb = (int *)malloc(sizeof(int) * (size_t)T);
+    if (!nb) { free(G.pos); return -1; }
+    long long total = 0;
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++) {
+            int delta = dilation ? dilation[h] : 1;
+            const unsigned char *padrow = key_padding_mask ? key_padding_mask + (size_t)b * T : NULL;
+            for (int i = 0; i < T; i++) total += neighbours(T, r, delta, &G, padrow, i, nb);
+        }
+    free(nb);
+    free(G.pos);
+    return total;
+}

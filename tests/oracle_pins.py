@@ -1,0 +1,271 @@
+"""Checks that pin the fp64 oracle to something other than itself.
+
+Each check takes an optional ``lib`` (an oracle build loaded with
+``oracle.open_library``) so the same checks can be aimed at copies of the
+oracle with a planted mistake; every planted mistake must trip at least
+one of them.  The pins:
+
+* brute force: dense masked attention with an explicit T x T mask
+  (``dense_ref``), on tiny T, random r, dilation, globals and padding;
+* closed forms of the neighbour counts (Longformer, eightmm.github.io,
+  "Sliding-Window Attention": |N_local(i)| = 2r + 1 away from the ends;
+  "Longformer长序列处理", 线性复杂度原理: cost grows 16x from 512 to 8192
+  tokens at fixed window, 256x for dense attention);
+* invariants and special cases: v == 1 gives 1; q == 0 gives the plain
+  mean over N(i); r = 0 gives v; r >= T-1 gives textbook dense attention
+  (torch's scaled_dot_product_attention in float64); a constant added to
+  every key leaves the softmax unchanged; keys outside N(i) do not reach
+  row i; a dilated head splits into delta undilated problems; global rows
+  are dense rows; padded rows are zero;
+* the set definitions N(i) = N_local(i) U G and N(i) = all for i in G.
+"""
+import numpy as np
+import torch
+
+import oracle
+from dense_ref import allowed_matrix, dense_masked_attention
+
+
+def _rand(seed, B, H, T, d):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return [torch.randn((B, H, T, d), generator=g, dtype=torch.float32) for _ in range(3)]
+
+
+def random_cases(n, seed0=0, Ts=(1, 2, 7, 33, 64, 130, 257)):
+    rng = np.random.default_rng(seed0)
+    cases = []
+    for c in range(n):
+        T = int(Ts[c % len(Ts)])
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 4))
+        d = int(rng.choice([8, 16, 64]))
+        r = int(rng.integers(0, T + 3))
+        dil = [int(x) for x in rng.integers(1, 6, size=H)]
+        kind = c % 4
+        if kind == 0:
+            G = []
+        elif kind == 1:
+            G = [int(x) for x in rng.integers(0, T, size=int(rng.integers(1, 5)))]  # dups ok
+        elif kind == 2:
+            G = list(range(T))
+        else:
+            G = [int(x) for x in rng.integers(0, T, size=2)]
+        pk = int(rng.integers(0, 3))
+        if pk == 0:
+            pad = None
+        elif pk == 1:
+            lens = rng.integers(0, T + 1, size=B)
+            pad = (np.arange(T)[None, :] >= lens[:, None]).astype(np.uint8)
+        else:
+            pad = (rng.random((B, T)) < 0.25).astype(np.uint8)
+        q, k, v = _rand(1000 + c, B, H, T, d)
+        cases.append(dict(q=q, k=k, v=v, r=r, dil=dil, G=G, pad=pad))
+    return cases
+
+
+# --------------------------------------------------------------------------
+# brute force
+
+def check_dense_bruteforce(lib=None, n=28, tol=1e-12):
+    for c in random_cases(n):
+        y = oracle.fwd(c["q"], c["k"], c["v"], c["r"], c["dil"], c["G"], c["pad"], lib=lib)
+        ref = dense_masked_attention(c["q"].numpy(), c["k"].numpy(), c["v"].numpy(), c["r"],
+                                     c["dil"], c["G"], c["pad"])
+        err = np.max(np.abs(y - ref)) if y.size else 0.0
+        assert err <= tol, f"oracle vs dense brute force: {err} (T={c['q'].shape[2]}, r={c['r']})"
+
+
+# --------------------------------------------------------------------------
+# closed-form counts
+
+def local_count(T, r):
+    """sum_i |{j in [0,T): |i-j| <= r}|, written out from min(i, r) terms."""
+    if T <= 0:
+        return 0
+    rr = min(r, T - 1)
+    # each row: 1 + min(i, rr) + min(T-1-i, rr); both sums equal S = sum_i min(i, rr)
+    S = rr * (rr - 1) // 2 + (T - rr) * rr
+    return T + 2 * S
+
+
+def dilated_count(T, r, delta):
+    return sum(local_count(len(range(c, T, delta)), r) for c in range(delta))
+
+
+def check_closed_form_counts(lib=None):
+    # T(2r+1) - r(r+1) for T >= r (the interior rows have w = 2r+1 keys)
+    for T, r in [(1024, 64), (4096, 256), (4096, 128), (300, 7), (16384, 512), (10, 9), (10, 3)]:
+        assert local_count(T, r) == T * (2 * r + 1) - r * (r + 1)
+        assert oracle.count_pairs(1, 1, T, r, lib=lib) == local_count(T, r)
+    # r beyond the sequence: dense
+    for T in (1, 5, 64):
+        assert oracle.count_pairs(1, 1, T, T + 3, lib=lib) == T * T
+    # dilated heads: delta residue classes of length ceil((T - c)/delta)
+    for T, r, dl in [(4096, 128, [1, 1, 2, 2, 2, 2, 3, 3, 3, 3, 4, 4]), (100, 5, [3, 7]), (37, 2, [5])]:
+        want = sum(dilated_count(T, r, x) for x in dl)
+        assert oracle.count_pairs(1, len(dl), T, r, dilation=dl, lib=lib) == want
+    # one global at 0 (delta = 1): non-global rows gain key 0 when it is outside the window
+    for T, r, H in [(1024, 64, 2), (4096, 256, 12)]:
+        per_head = (local_count(T, r) - (r + 1)) + T + (T - (r + 1))
+        assert oracle.count_pairs(1, H, T, r, global_idx=[0], lib=lib) == per_head * H
+    # 512 -> 8192 tokens: dense x256 exactly, fixed small window ~x16
+    assert oracle.count_pairs(1, 1, 8192, 9000, lib=lib) == 256 * oracle.count_pairs(1, 1, 512, 9000, lib=lib)
+    ratio = oracle.count_pairs(1, 1, 8192, 4, lib=lib) / oracle.count_pairs(1, 1, 512, 4, lib=lib)
+    assert abs(ratio - 16.0) < 0.16
+
+
+# --------------------------------------------------------------------------
+# set definitions
+
+def check_neighbour_sets(lib=None):
+    rng = np.random.default_rng(7)
+    for trial in range(60):
+        T = int(rng.integers(1, 80))
+        r = int(rng.integers(0, 12))
+        delta = int(rng.integers(1, 5))
+        G = [int(x) for x in rng.integers(0, T, size=int(rng.integers(0, 4)))]
+        pad = (rng.random(T) < 0.2).astype(np.uint8) if trial % 2 else None
+        for i in range(T):
+            got = oracle.neighbours(T, r, delta, i, G, pad, lib=lib)
+            valid = [j for j in range(T) if pad is None or not pad[j]]
+            if pad is not None and pad[i]:
+                want = []
+            elif i in G:
+                want = valid                                   # N(i) = all positions
+            else:
+                loc = {j for j in range(T) if abs(i - j) <= r * delta and (i - j) % delta == 0}
+                want = sorted((loc | set(G)) & set(valid))     # N_local(i) U G
+            assert got == want, (T, r, delta, G, i, got, want)
+
+
+# --------------------------------------------------------------------------
+# invariants and special cases
+
+def check_invariants(lib=None):
+    cases = random_cases(16, seed0=3)
+    for c in cases:
+        q, k, v = c["q"], c["k"], c["v"]
+        B, H, T, d = q.shape
+        pad = c["pad"]
+        valid = np.ones((B, T), bool) if pad is None else ~pad.astype(bool)
+        # v == 1 -> every valid row is exactly a convex combination of ones
+        y1 = oracle.fwd(q, k, torch.ones_like(v), c["r"], c["dil"], c["G"], pad, lib=lib)
+        for b in range(B):
+            assert np.all(np.abs(y1[b][:, valid[b]] - 1.0) <= 1e-14)
+            assert np.all(y1[b][:, ~valid[b]] == 0.0)
+        # q == 0 -> uniform weights: the mean of v over N(i) (mask from dense_ref)
+        y0 = oracle.fwd(torch.zeros_like(q), k, v, c["r"], c["dil"], c["G"], pad, lib=lib)
+        for b in range(B):
+            for h in range(H):
+                A = allowed_matrix(T, c["r"], c["dil"][h], c["G"],
+                                   None if pad is None else pad[b])
+                for i in range(T):
+                    if not valid[b, i]:
+                        continue
+                    want = v[b, h].numpy().astype(np.float64)[A[i]].mean(axis=0)
+                    assert np.max(np.abs(y0[b, h, i] - want)) <= 1e-13
+        # shift invariance of the logits: k_j + c for every j
+        base = oracle.fwd(q, k, v, c["r"], c["dil"], c["G"], pad, lib=lib)
+        shift = torch.randn(B, H, 1, d, generator=torch.Generator().manual_seed(5))
+        ys = oracle.fwd(q, (k.double() + shift.double()).float(), v, c["r"], c["dil"], c["G"], pad, lib=lib)
+        # k + shift is rounded to float32, so compare against the oracle on the rounded keys'
+        # exact effect: scores change by q.shift up to float32 rounding of k (~1e-7 relative)
+        assert np.max(np.abs(ys - base)) <= 5e-5
+    # exact shift: keys and shift on a coarse grid so k + c is exact in float32
+    g = torch.Generator().manual_seed(11)
+    q = torch.randint(-4, 5, (1, 2, 40, 8), generator=g).float() / 4
+    k = torch.randint(-4, 5, (1, 2, 40, 8), generator=g).float() / 4
+    v = torch.randn(1, 2, 40, 8, generator=g)
+    cvec = torch.randint(-8, 9, (1, 2, 1, 8), generator=g).float() / 8
+    a = oracle.fwd(q, k, v, 3, [1, 2], [5], None, lib=lib)
+    b2 = oracle.fwd(q, k + cvec, v, 3, [1, 2], [5], None, lib=lib)
+    assert np.max(np.abs(a - b2)) <= 1e-12
+
+
+def check_identity_and_dense_limits(lib=None):
+    g = torch.Generator().manual_seed(21)
+    for T in (1, 9, 64, 130):
+        q, k, v = [torch.randn(2, 3, T, 16, generator=g) for _ in range(3)]
+        # r = 0, no globals: each valid row attends only to itself
+        y = oracle.fwd(q, k, v, 0, [1, 2, 3], [], None, lib=lib)
+        assert np.array_equal(y, v.numpy().astype(np.float64))
+        # r >= T - 1, delta = 1, no padding: textbook dense attention
+        yd = oracle.fwd(q, k, v, T - 1, None, [], None, lib=lib)
+        ref = torch.nn.functional.scaled_dot_product_attention(q.double(), k.double(), v.double()).numpy()
+        assert np.max(np.abs(yd - ref)) <= 1e-12
+        # globals do not change the dense limit
+        yg = oracle.fwd(q, k, v, T + 5, None, [0, T - 1], None, lib=lib)
+        assert np.max(np.abs(yg - ref)) <= 1e-12
+    # global rows: dense attention over the valid keys
+    T = 50
+    q, k, v = [torch.randn(1, 2, T, 16, generator=g) for _ in range(3)]
+    pad = np.zeros((1, T), np.uint8)
+    pad[0, 40:] = 1
+    pad[0, 7] = 1
+    G = [3, 7, 20]
+    y = oracle.fwd(q, k, v, 2, [1, 3], G, pad, lib=lib)
+    keep = ~pad[0].astype(bool)
+    for h in range(2):
+        for i in G:
+            if pad[0, i]:
+                assert np.all(y[0, h, i] == 0.0)
+                continue
+            s = (q[0, h, i].double() @ k[0, h].double().T / 4.0).numpy()
+            s = s[keep]
+            p = np.exp(s - s.max())
+            want = (p[:, None] * v[0, h].double().numpy()[keep]).sum(0) / p.sum()
+            assert np.max(np.abs(y[0, h, i] - want)) <= 1e-12
+    assert np.all(y[0][:, 40:] == 0.0) and np.all(y[0][:, 7] == 0.0)
+
+
+def check_window_exclusivity(lib=None):
+    g = torch.Generator().manual_seed(31)
+    T, d = 90, 16
+    q, k, v = [torch.randn(1, 1, T, d, generator=g) for _ in range(3)]
+    r, delta, G = 4, 3, [10, 70]
+    base = oracle.fwd(q, k, v, r, [delta], G, None, lib=lib)
+    for i in (0, 20, 45, 89):
+        inside = set(j for j in range(T) if abs(i - j) <= r * delta and (i - j) % delta == 0) | set(G)
+        outside = [j for j in range(T) if j not in inside]
+        k2, v2 = k.clone(), v.clone()
+        junk = torch.randn(len(outside), d, generator=g) * 10
+        k2[0, 0, outside] = junk
+        v2[0, 0, outside] = -junk
+        y = oracle.fwd(q, k2, v2, r, [delta], G, None, lib=lib)
+        assert np.array_equal(y[0, 0, i], base[0, 0, i])
+        # permuting the keys that sit outside the window also changes nothing
+        perm = np.random.default_rng(i).permutation(outside)
+        k3, v3 = k.clone(), v.clone()
+        k3[0, 0, outside] = k[0, 0, perm]
+        v3[0, 0, outside] = v[0, 0, perm]
+        y3 = oracle.fwd(q, k3, v3, r, [delta], G, None, lib=lib)
+        assert np.array_equal(y3[0, 0, i], base[0, 0, i])
+
+
+def check_dilation_split(lib=None):
+    g = torch.Generator().manual_seed(41)
+    T, d = 103, 8
+    q, k, v = [torch.randn(1, 1, T, d, generator=g) for _ in range(3)]
+    rng = np.random.default_rng(3)
+    pad = (rng.random((1, T)) < 0.15).astype(np.uint8)
+    for delta in (2, 3, 5):
+        for r in (0, 1, 6):
+            y = oracle.fwd(q, k, v, r, [delta], [], pad, lib=lib)
+            for c in range(delta):
+                idx = list(range(c, T, delta))
+                ys = oracle.fwd(q[:, :, idx], k[:, :, idx], v[:, :, idx], r, [1], [], pad[:, idx], lib=lib)
+                assert np.array_equal(y[0, 0, idx], ys[0, 0])
+
+
+def check_rows_entry_point(lib=None):
+    c = random_cases(3, seed0=9, Ts=(33, 64, 130))[2]
+    full = oracle.fwd(c["q"], c["k"], c["v"], c["r"], c["dil"], c["G"], c["pad"], lib=lib)
+    B, H, T, d = c["q"].shape
+    sel = np.random.default_rng(0).choice(B * H * T, size=min(50, B * H * T), replace=False)
+    part = oracle.rows(c["q"], c["k"], c["v"], c["r"], sel, c["dil"], c["G"], c["pad"], lib=lib)
+    assert np.array_equal(part, full.reshape(-1, d)[sel])
+
+
+ALL_CHECKS = [check_dense_bruteforce, check_closed_form_counts, check_neighbour_sets,
+              check_invariants, check_identity_and_dense_limits, check_window_exclusivity,
+              check_dilation_split, check_rows_entry_point]
