@@ -1,0 +1,109 @@
+/*
+ * lf_attn.h -- C ABI of liblfattn.so: the Longformer sparse self-attention
+ * forward pass (sliding window, optional per-head dilation, global tokens,
+ * key padding) on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (Longformer, eightmm.github.io/papers/architectures/
+ * longformer, sections "Sliding-Window Attention", "Global Attention" and
+ * "Mask View"), with 0-based positions:
+ *
+ *   N_local(i) = { j : |i - j| <= r * delta_h  and  (i - j) mod delta_h == 0 }
+ *   N(i)       = N_local(i) U G           for i not in G   (set union)
+ *   N(i)       = { 0 .. T-1 }              for i in G
+ *   keys j with key_padding_mask[b][j] != 0 are removed from every N(i);
+ *   y_i = sum_{j in N(i)} softmax_j( q_i . k_j / sqrt(d) ) v_j ;
+ *   a query row i with key_padding_mask[b][i] != 0 is written as zeros.
+ *
+ * The dilated window follows Longformer (ciallo.wiki) section 2.2.3 and
+ * "Longformer长序列处理" (aiqz.cc), section 膨胀窗口设计: the window's keys
+ * sit delta apart, the count stays 2r+1 and the reach grows delta-fold.
+ * Positions that fall outside [0, T) are dropped ("Longformer长序列处理",
+ * Python 演示, note 3).
+ *
+ * Thread safety: every call may come from any thread.  Calls on the same
+ * stream are ordered by the stream; calls on different streams use separate
+ * workspaces.  The same inputs give a bit-identical output (no atomics touch
+ * data).
+ */
+#ifndef LF_ATTN_H
+#define LF_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and out. */
+typedef enum {
+    LF_F32 = 0,  /* IEEE binary32; products use a hi/lo bf16 split with fp32 accumulation */
+    LF_BF16 = 1  /* bfloat16; fp32 accumulation; out rounded to nearest-even */
+} lf_dtype_t;
+
+typedef enum {
+    LF_OK = 0,
+    LF_E_INVALID = 1,     /* an argument breaks the contract below; nothing was enqueued */
+    LF_E_UNSUPPORTED = 2, /* valid but outside what this build implements; nothing enqueued */
+    LF_E_NOMEM = 3,       /* the workspace could not be allocated; nothing enqueued */
+    LF_E_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} lf_status_t;
+
+/* Limits of this build (LF_E_UNSUPPORTED beyond them). */
+#define LF_HEAD_DIM 64        /* d must equal this */
+#define LF_MAX_HEADS 128      /* H */
+#define LF_MAX_GLOBALS 512    /* distinct global positions */
+#define LF_MAX_SEQ (1 << 24)  /* T */
+#define LF_MAX_DILATION 65535 /* delta */
+
+/*
+ * lf_attn_fwd -- enqueue the forward pass on `stream`.
+ *
+ *   q, k, v   DEVICE pointers, each [B][H][T][d] contiguous row-major in
+ *             `dtype`, 16-byte aligned.  Read only.
+ *   B, H, T   batch, heads, sequence length; each >= 1 (T <= LF_MAX_SEQ,
+ *             H <= LF_MAX_HEADS).
+ *   d         head dimension; must be LF_HEAD_DIM (64).
+ *   r         one-sided window radius in window steps, r >= 0; the window
+ *             holds 2r+1 keys away from the sequence ends.  r >= T means
+ *             every key of the (dilated) class.
+ *   dilation  HOST array [H] of per-head strides delta_h >= 1, or NULL for
+ *             all 1.  Read during the call only.
+ *   global_idx HOST array [n_global] of 0-based positions in [0, T); any
+ *             order; duplicates are allowed and count once.  May be NULL
+ *             when n_global == 0.  Read during the call only.
+ *   n_global  >= 0; at most LF_MAX_GLOBALS distinct positions.
+ *   key_padding_mask DEVICE array [B][T] of bytes, nonzero = padded, or
+ *             NULL for no padding.  Any alignment.
+ *   out       DEVICE pointer [B][H][T][d] in `dtype`, 16-byte aligned,
+ *             must not overlap q, k or v.  Every element is written.
+ *   dtype     LF_F32 or LF_BF16.
+ *   stream    a hipStream_t (NULL = the null stream).  All work is enqueued
+ *             there asynchronously; the call returns before it finishes.
+ *
+ * Ownership: the caller owns every buffer; the library keeps no pointer
+ * after returning.  The library keeps one small device workspace per
+ * (device, stream) pair for the global rows; it grows with hipMalloc on
+ * first use of a larger problem (so call once outside graph capture before
+ * capturing) and lives until the process exits.
+ *
+ * Errors: all argument checks run before any HIP call; on LF_E_INVALID or
+ * LF_E_UNSUPPORTED nothing is enqueued and `out` is untouched.  On any
+ * non-OK status lf_last_error() describes the cause.
+ */
+lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v,
+                        int B, int H, int T, int d, int r,
+                        const int32_t *dilation,
+                        const int32_t *global_idx, int n_global,
+                        const uint8_t *key_padding_mask,
+                        void *out, lf_dtype_t dtype, void *stream);
+
+/* Text describing the last non-OK status returned on the calling thread
+ * (empty string if none).  The pointer stays valid until the next call on
+ * this thread. */
+const char *lf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LF_ATTN_H */

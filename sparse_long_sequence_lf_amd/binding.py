@@ -1,0 +1,130 @@
+"""Thin ctypes binding of liblfattn.so (include/lf_attn.h).
+
+Argument marshalling only: torch supplies device memory and the stream;
+every step of the forward pass runs in the library's HIP kernels.  If the
+library is not built, calls raise -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblfattn.so")
+
+LF_F32 = 0
+LF_BF16 = 1
+LF_OK = 0
+LF_E_INVALID = 1
+LF_E_UNSUPPORTED = 2
+LF_E_NOMEM = 3
+LF_E_HIP = 4
+STATUS_NAMES = {0: "LF_OK", 1: "LF_E_INVALID", 2: "LF_E_UNSUPPORTED", 3: "LF_E_NOMEM", 4: "LF_E_HIP"}
+HEAD_DIM = 64
+MAX_HEADS = 128
+MAX_GLOBALS = 512
+
+_lib = None
+
+
+class LfError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def load():
+    """Load liblfattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m sparse_long_sequence_lf_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.lf_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I, P]
+    lib.lf_attn_fwd.restype = I
+    lib.lf_last_error.argtypes = []
+    lib.lf_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().lf_last_error().decode()
+
+
+def raw_fwd(q_ptr, k_ptr, v_ptr, B, H, T, d, r, dilation, global_idx, n_global, kpm_ptr, out_ptr,
+            dtype, stream_ptr) -> int:
+    """Call lf_attn_fwd with raw integer device pointers; returns the status."""
+    lib = load()
+    dil = None
+    if dilation is not None:
+        dil = (ctypes.c_int32 * len(dilation))(*[int(x) for x in dilation])
+    g = None
+    if global_idx is not None:
+        g = (ctypes.c_int32 * max(1, len(global_idx)))(*[int(x) for x in global_idx])
+    return lib.lf_attn_fwd(q_ptr, k_ptr, v_ptr, int(B), int(H), int(T), int(d), int(r), dil, g,
+                           int(n_global), kpm_ptr, out_ptr, int(dtype), stream_ptr)
+
+
+def attn_fwd(q, k, v, r: int, dilation: Optional[Sequence[int]] = None,
+             global_idx: Optional[Sequence[int]] = None, global_attention_mask=None,
+             key_padding_mask=None, out=None, stream=None):
+    """Longformer sparse attention forward on torch tensors [B, H, T, 64].
+
+    ``global_attention_mask`` (a 0/1 tensor of shape [T] or [B, T], 1 =
+    global, as in the Hugging Face convention) is turned into the index list
+    ``global_idx``; a [B, T] mask must mark the same positions in every
+    sequence.  ``key_padding_mask`` is [B, T], nonzero = padded.
+    """
+    import torch
+
+    if q.dtype == torch.bfloat16:
+        dt = LF_BF16
+    elif q.dtype == torch.float32:
+        dt = LF_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype or t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{name} must match q in dtype, shape and device")
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, d]")
+    if not (q.is_cuda and q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, T, d = q.shape
+    if global_attention_mask is not None:
+        if global_idx is not None:
+            raise ValueError("give global_idx or global_attention_mask, not both")
+        gm = global_attention_mask.detach().to("cpu")
+        if gm.dim() == 2:
+            if not bool((gm == gm[0:1]).all()):
+                raise ValueError("global_attention_mask must mark the same positions in every sequence")
+            gm = gm[0]
+        global_idx = torch.nonzero(gm != 0).flatten().tolist()
+    gl = list(global_idx) if global_idx is not None else []
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    kpm_ptr = None
+    if key_padding_mask is not None:
+        kpm = key_padding_mask
+        if kpm.dtype == torch.bool:
+            kpm = kpm.to(torch.uint8)
+        if kpm.dtype != torch.uint8 or tuple(kpm.shape) != (B, T) or not kpm.is_cuda:
+            raise ValueError("key_padding_mask must be a uint8/bool device tensor [B, T]")
+        kpm = kpm.contiguous()
+        kpm_ptr = kpm.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = raw_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, r, dilation,
+                 gl if gl else None, len(gl), kpm_ptr, out.data_ptr(), dt, sptr)
+    if st != LF_OK:
+        raise LfError(st, last_error())
+    return out

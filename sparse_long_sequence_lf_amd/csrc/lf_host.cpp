@@ -1,0 +1,174 @@
+// lf_host.cpp -- the C ABI of liblfattn.so: argument checks, the global-set
+// normalisation, task planning, the per-stream workspace and the launches.
+//
+// Every argument check runs before the first HIP call, so a rejected call
+// enqueues nothing and leaves `out` untouched (and works without a GPU).
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "lf_attn.h"
+#include "lf_kernels.h"
+
+extern "C" hipError_t lfk_launch(const lfk::Params *P, int dtype_bf16, void *stream);
+
+namespace {
+
+thread_local std::string g_err;
+
+lf_status_t fail(lf_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Device workspace for the global-row partials, one per (device, stream).
+// Calls on one stream are ordered, so they can share it; calls on other
+// streams get their own.  It only grows; the old buffer is released after
+// the stream has drained it.
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, void *>, Workspace> g_ws;
+
+lf_status_t workspace(size_t bytes, void *stream, float **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(LF_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            e = hipStreamSynchronize((hipStream_t)stream);
+            if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        const size_t want = std::max(bytes, (size_t)1 << 20);
+        e = hipMalloc(&w.ptr, want);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            (void)hipGetLastError();
+            return fail(LF_E_NOMEM, "workspace of %zu bytes: %s", want, hipGetErrorString(e));
+        }
+        w.bytes = want;
+    }
+    *out = (float *)w.ptr;
+    return LF_OK;
+}
+
+}  // namespace
+
+extern "C" const char *lf_last_error(void) { return g_err.c_str(); }
+
+extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T,
+                                   int d, int r, const int32_t *dilation, const int32_t *global_idx,
+                                   int n_global, const uint8_t *key_padding_mask, void *out,
+                                   lf_dtype_t dtype, void *stream) {
+    g_err.clear();
+    // ---- argument checks: no HIP call before all of them pass
+    if (!q || !k || !v || !out) return fail(LF_E_INVALID, "q, k, v and out must be non-null");
+    if (dtype != LF_F32 && dtype != LF_BF16) return fail(LF_E_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (B < 1 || H < 1 || T < 1) return fail(LF_E_INVALID, "B, H, T must be >= 1 (got %d, %d, %d)", B, H, T);
+    if (d != LF_HEAD_DIM) return fail(LF_E_UNSUPPORTED, "head dimension %d: only %d is built", d, LF_HEAD_DIM);
+    if (H > LF_MAX_HEADS) return fail(LF_E_UNSUPPORTED, "H = %d exceeds %d", H, LF_MAX_HEADS);
+    if (T > LF_MAX_SEQ) return fail(LF_E_UNSUPPORTED, "T = %d exceeds %d", T, LF_MAX_SEQ);
+    if (r < 0) return fail(LF_E_INVALID, "window radius r = %d must be >= 0", r);
+    if (n_global < 0) return fail(LF_E_INVALID, "n_global = %d must be >= 0", n_global);
+    if (n_global > 0 && !global_idx) return fail(LF_E_INVALID, "global_idx is NULL with n_global = %d", n_global);
+    if (dilation) {
+        for (int h = 0; h < H; h++) {
+            if (dilation[h] < 1) return fail(LF_E_INVALID, "dilation[%d] = %d must be >= 1", h, dilation[h]);
+            if (dilation[h] > LF_MAX_DILATION)
+                return fail(LF_E_UNSUPPORTED, "dilation[%d] = %d exceeds %d", h, dilation[h], LF_MAX_DILATION);
+        }
+    }
+    for (int i = 0; i < n_global; i++)
+        if (global_idx[i] < 0 || global_idx[i] >= T)
+            return fail(LF_E_INVALID, "global_idx[%d] = %d outside [0, %d)", i, global_idx[i], T);
+    const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u;
+    if (mis) return fail(LF_E_INVALID, "q, k, v and out must be 16-byte aligned");
+    const size_t esize = dtype == LF_BF16 ? 2 : 4;
+    const size_t nbytes = (size_t)B * (size_t)H * (size_t)T * (size_t)d * esize;
+    if ((size_t)B * (size_t)H > (size_t)1 << 24)
+        return fail(LF_E_UNSUPPORTED, "B*H = %lld too large", (long long)B * H);
+    if (overlaps(out, nbytes, q, nbytes) || overlaps(out, nbytes, k, nbytes) || overlaps(out, nbytes, v, nbytes))
+        return fail(LF_E_INVALID, "out overlaps q, k or v");
+
+    // ---- normalise G: a set of positions, ascending
+    std::vector<int32_t> G(global_idx, global_idx + n_global);
+    std::sort(G.begin(), G.end());
+    G.erase(std::unique(G.begin(), G.end()), G.end());
+    if ((int)G.size() > LF_MAX_GLOBALS)
+        return fail(LF_E_UNSUPPORTED, "%zu distinct globals exceed %d", G.size(), LF_MAX_GLOBALS);
+
+    // ---- plan
+    constexpr int QB = LFK_QB;
+    constexpr int BM = 32 * QB;
+    lfk::Params P;
+    std::memset(&P, 0, sizeof P);
+    P.q = q; P.k = k; P.v = v; P.out = out;
+    P.pad = key_padding_mask;
+    P.B = B; P.H = H; P.T = T;
+    P.r = r < T ? r : T;  // |i - j| < T always, so larger radii change nothing
+    P.n_g = (int)G.size();
+    for (int i = 0; i < P.n_g; i++) P.glob[i] = G[i];
+    long long start = 0;
+    for (int h = 0; h < H; h++) {
+        const int delta = dilation ? dilation[h] : 1;
+        P.dil[h] = (uint16_t)delta;
+        P.head_start[h] = (int)start;
+        const long long qq = T / delta, rem = T % delta;
+        start += rem * cdiv(qq + 1, BM) + (delta - rem) * cdiv(qq, BM);
+    }
+    P.head_start[H] = (int)start;
+    P.band_tasks_per_batch = (int)start;
+    const long long n_band = (long long)B * start;
+    long long n_glob_tasks = 0;
+    size_t ws_bytes = 0;
+    if (P.n_g > 0) {
+        P.n_ggroups = (int)cdiv(cdiv(P.n_g, 32), QB);
+        P.g_pad = P.n_ggroups * BM;
+        int sl = (int)cdiv(cdiv(T, 16), 32) * 32;
+        P.split_len = sl < 256 ? 256 : sl;
+        P.n_split = (int)cdiv(T, P.split_len);
+        n_glob_tasks = (long long)B * H * P.n_split * P.n_ggroups;
+        ws_bytes = (size_t)B * H * P.n_split * P.g_pad * (LF_HEAD_DIM + 2) * sizeof(float);
+    }
+    if (n_band + n_glob_tasks > (1LL << 30))
+        return fail(LF_E_UNSUPPORTED, "problem needs %lld workgroups", n_band + n_glob_tasks);
+    P.n_band_tasks = (int)n_band;
+    P.n_tasks = (int)(n_band + n_glob_tasks);
+
+    // ---- HIP work
+    if (P.n_g > 0) {
+        lf_status_t st = workspace(ws_bytes, stream, &P.part);
+        if (st != LF_OK) return st;
+    }
+    hipError_t e = lfk_launch(&P, dtype == LF_BF16, stream);
+    if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return LF_OK;
+}

@@ -126,8 +126,9 @@ def make_inputs(w: Workload, dtype: Optional[str] = None, T: Optional[int] = Non
     lengths = None
     kpm = None
     if w.len_lo is not None:
-        lo = min(w.len_lo, T_)
-        hi = min(w.len_hi, T_)
+        # a shrunk sequence keeps the same fraction of padding
+        lo = max(1, (w.len_lo * T_) // w.T)
+        hi = max(lo, (w.len_hi * T_) // w.T)
         lengths = [int(x) for x in rng.integers(lo, hi + 1, size=B_)]
         pos = torch.arange(T_).unsqueeze(0)
         kpm = (pos >= torch.tensor(lengths).unsqueeze(1)).to(torch.uint8).contiguous()

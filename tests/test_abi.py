@@ -1,0 +1,115 @@
+"""CPU tests of the C-ABI library: it loads, exports every function that
+include/lf_attn.h declares, and rejects bad arguments before any HIP call
+(so these run without a GPU): documented status, message, no write."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import sparse_long_sequence_lf_amd as lf
+from sparse_long_sequence_lf_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lf_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from sparse_long_sequence_lf_amd import build
+        build.build()
+    return lf.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lf_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert "lf_attn_fwd" in names and "lf_last_error" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_header_limits_match_binding():
+    text = open(HEADER).read()
+    assert re.search(r"#define LF_HEAD_DIM (\d+)", text).group(1) == str(binding.HEAD_DIM)
+    assert re.search(r"#define LF_MAX_HEADS (\d+)", text).group(1) == str(binding.MAX_HEADS)
+    assert re.search(r"#define LF_MAX_GLOBALS (\d+)", text).group(1) == str(binding.MAX_GLOBALS)
+
+
+# fake, aligned, never-dereferenced device addresses
+Q, K, V, OUT = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+GOOD = dict(q=Q, k=K, v=V, B=1, H=2, T=128, d=64, r=8, dil=[1, 2], g=[0], ng=1, kpm=None,
+            out=OUT, dtype=lf.LF_BF16)
+
+
+def call(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return lf.raw_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], a["r"], a["dil"],
+                      a["g"], a["ng"], a["kpm"], a["out"], a["dtype"], None)
+
+
+BAD = [
+    ("null_q", dict(q=None), lf.LF_E_INVALID),
+    ("null_out", dict(out=None), lf.LF_E_INVALID),
+    ("B_zero", dict(B=0), lf.LF_E_INVALID),
+    ("H_neg", dict(H=-1, dil=None), lf.LF_E_INVALID),
+    ("T_zero", dict(T=0), lf.LF_E_INVALID),
+    ("d_32", dict(d=32), lf.LF_E_UNSUPPORTED),
+    ("d_128", dict(d=128), lf.LF_E_UNSUPPORTED),
+    ("r_neg", dict(r=-1), lf.LF_E_INVALID),
+    ("dilation_zero", dict(dil=[1, 0]), lf.LF_E_INVALID),
+    ("dilation_huge", dict(dil=[1, 70000]), lf.LF_E_UNSUPPORTED),
+    ("global_out_of_range", dict(g=[128], ng=1), lf.LF_E_INVALID),
+    ("global_negative", dict(g=[0, -3], ng=2), lf.LF_E_INVALID),
+    ("n_global_negative", dict(ng=-1), lf.LF_E_INVALID),
+    ("global_null", dict(g=None, ng=2), lf.LF_E_INVALID),
+    ("misaligned_q", dict(q=Q + 2), lf.LF_E_INVALID),
+    ("misaligned_out", dict(out=OUT + 8), lf.LF_E_INVALID),
+    ("out_aliases_q", dict(out=Q + 64 * 2 * 16), lf.LF_E_INVALID),
+    ("out_is_v", dict(out=V), lf.LF_E_INVALID),
+    ("bad_dtype", dict(dtype=7), lf.LF_E_UNSUPPORTED),
+    ("too_many_heads", dict(H=129, dil=None), lf.LF_E_UNSUPPORTED),
+    ("too_many_globals", dict(T=4096, g=list(range(600)), ng=600), lf.LF_E_UNSUPPORTED),
+    ("T_too_long", dict(T=(1 << 24) + 1), lf.LF_E_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD, ids=[b[0] for b in BAD])
+def test_invalid_arguments_rejected(lib, name, kw, status):
+    st = call(**kw)
+    assert st == status, (name, st, lf.last_error())
+    assert lf.last_error() != ""
+
+
+def test_rejected_call_touches_nothing(lib):
+    # host buffers stand in for the device pointers: a rejected call must not
+    # read or write them
+    buf = np.full(1 * 2 * 128 * 64, 3.0, dtype=np.float32)
+    out = np.full_like(buf, 5.0)
+    st = call(q=buf.ctypes.data, k=buf.ctypes.data, v=buf.ctypes.data, out=out.ctypes.data,
+              dtype=lf.LF_F32, r=-5)
+    assert st == lf.LF_E_INVALID
+    assert np.all(buf == 3.0) and np.all(out == 5.0)
+
+
+def test_duplicate_globals_count_once(lib):
+    # 600 copies of one position are a single global, so the global limit is not
+    # hit; the call is then refused for its size (far too many workgroups), which
+    # is checked after the global set has been normalised
+    st = call(B=4096, H=128, dil=None, T=1 << 20, g=[5] * 600, ng=600,
+              q=1 << 48, k=2 << 48, v=3 << 48, out=4 << 48)
+    assert st == lf.LF_E_UNSUPPORTED
+    assert "workgroups" in lf.last_error()

@@ -1,0 +1,200 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+identical seeded inputs.
+
+Bar: max |gpu - oracle| <= 1e-4 for fp32 inputs, <= 2e-2 for bf16 inputs
+(fp32 accumulation).  Every workload shape also runs in fp32, where one
+missing or doubled key is far above the bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_long_sequence_lf_amd as lf
+from sparse_long_sequence_lf_amd import workloads as W
+from parity_utils import TOL, gpu_fwd, max_err, oracle_full, require_gpu, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# ---- every workload at a size the oracle finishes in seconds (full compare)
+REDUCED = {
+    "fp32-b1h2t1024-r64-g1": dict(),
+    "bf16-b1h12t4096-r256-g1": dict(T=1280),
+    "bf16-b1h12t4096-r128-dil": dict(T=1100),
+    "bf16-b2h12t4096-r256-g68": dict(T=1000, H=6),
+    "bf16-b4h16t16384-r512-g8-pad": dict(T=2100, H=3),
+}
+
+
+@pytest.mark.parametrize("dtype", ["native", "f32"])
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_workload_reduced_full_compare(name, dtype):
+    w = W.workload(name)
+    dt = w.dtype if dtype == "native" else "f32"
+    inp = W.make_inputs(w, dtype=dt, **REDUCED[name])
+    print(f"case {name} dtype={dt} shape={tuple(inp.q.shape)}", flush=True)
+    out = gpu_fwd(inp)
+    ref = oracle_full(inp)
+    err = max_err(out, ref)
+    print(f"  max abs err {err:.3e}", flush=True)
+    assert err <= TOL[dt]
+
+
+# ---- every workload at its full size (the size the benchmark times): sampled rows
+@pytest.mark.parametrize("dtype", ["native", "f32"])
+@pytest.mark.parametrize("name", [w.name for w in W.WORKLOADS])
+def test_workload_full_size_sampled(name, dtype):
+    w = W.workload(name)
+    dt = w.dtype if dtype == "native" else "f32"
+    inp = W.make_inputs(w, dtype=dt)
+    print(f"case {name} dtype={dt} shape={tuple(inp.q.shape)} full size", flush=True)
+    out = gpu_fwd(inp)
+    rows = sample_rows(inp, n_random=1500, seed=w.seed)
+    ref = oracle.rows(inp.q, inp.k, inp.v, inp.r, rows, inp.dilation, inp.global_idx,
+                      inp.key_padding_mask)
+    got = out.float().cpu().double().reshape(-1, w.d).numpy()[rows]
+    err = float(np.max(np.abs(got - ref)))
+    print(f"  {len(rows)} rows, max abs err {err:.3e}", flush=True)
+    assert err <= TOL[dt]
+    if inp.key_padding_mask is not None:
+        # every padded query row is exactly zero
+        pad = inp.key_padding_mask.bool()
+        o = out.float().cpu()
+        for b in range(w.B):
+            assert torch.all(o[b][:, pad[b]] == 0)
+
+
+# ---- random edge cases: ragged T, r around T, dilation, duplicates, padding patterns
+EDGE_T = [1, 2, 3, 31, 32, 33, 63, 64, 65, 97, 130, 257, 300]
+
+
+@pytest.mark.parametrize("pad", ["none", "right", "random"])
+@pytest.mark.parametrize("T", EDGE_T)
+def test_edge_cases(T, pad):
+    for dt in ("f32", "bf16"):
+        for seed in range(2):
+            inp = W.random_case(seed * 1000 + T, B=2, H=3, T=T, dtype=dt, pad=pad)
+            print(f"case T={T} pad={pad} dt={dt} seed={seed} r={inp.r} dil={inp.dilation} "
+                  f"G={inp.global_idx}", flush=True)
+            out = gpu_fwd(inp)
+            err = max_err(out, oracle_full(inp))
+            assert err <= TOL[dt], err
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_named_edge_cases(dt):
+    base = W.random_case(5, B=2, H=2, T=200, dtype=dt, pad="none")
+    cases = []
+    # r = 0, no globals (identity); r >= T (dense); T < r; G = all positions
+    for r, G, dil in [(0, [], [1, 1]), (300, [], [1, 1]), (250, [3], [1, 2]), (5, list(range(200)), [1, 3]),
+                      (7, [10, 12, 100], [1, 1]),        # global inside and outside the window
+                      (3, [0, 199], [4, 5]),             # delta not dividing T
+                      (40, [50, 50, 50, 51], [3, 1])]:   # duplicated globals
+        cases.append((r, G, dil, None))
+    kpm = torch.zeros(2, 200, dtype=torch.uint8)
+    kpm[0, 150:] = 1
+    kpm[1, :] = 1                                         # a fully padded sequence
+    cases.append((9, [20, 160], [1, 2], kpm))             # a global inside the padding
+    kpm2 = torch.zeros(2, 200, dtype=torch.uint8)
+    kpm2[1, 90:] = 1
+    cases.append((30, [95], [2, 1], kpm2))
+    for r, G, dil, m in cases:
+        inp = W.Inputs(base.q, base.k, base.v, r, dil, G, None, m)
+        print(f"case r={r} G={G[:6]} dil={dil} pad={'yes' if m is not None else 'no'}", flush=True)
+        out = gpu_fwd(inp)
+        err = max_err(out, oracle_full(inp))
+        assert err <= TOL[dt], err
+        if r == 0 and not G and dt == "bf16":
+            assert torch.equal(out.cpu(), base.v)   # a single key: y_i = v_i exactly
+
+
+# ---- the neighbour set itself, at bf16: q = 0 makes every weight exactly 1, and
+# one-hot values count the keys of each residue mod 64 in N(i)
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_tracer_counts_exact_neighbour_sets(dt):
+    for name in ["bf16-b1h12t4096-r256-g1", "bf16-b1h12t4096-r128-dil", "bf16-b2h12t4096-r256-g68",
+                 "bf16-b4h16t16384-r512-g8-pad"]:
+        w = W.workload(name)
+        inp = W.make_inputs(w, dtype=dt, T=min(w.T, 1500), H=min(w.H, 4))
+        B, H, T, d = inp.q.shape
+        q0 = torch.zeros_like(inp.q)
+        onehot = (torch.arange(T)[:, None] % d == torch.arange(d)[None, :]).to(inp.q.dtype)
+        v1 = onehot.expand(B, H, T, d).contiguous()
+        print(f"case {name} dt={dt} tracer", flush=True)
+        out = gpu_fwd(inp, q=q0, v=v1).float().cpu().double().numpy()
+        ref = oracle_full(inp, q=q0, v=v1)
+        rel = np.abs(out - ref) / np.maximum(np.abs(ref), 1e-30)
+        # bf16 output rounding is the only error left: 2^-8 relative
+        assert float(np.max(np.where(ref != 0, rel, np.abs(out)))) <= 2 ** -8
+
+
+def test_nan_in_padded_positions_is_ignored():
+    w = W.workload("bf16-b4h16t16384-r512-g8-pad")
+    inp = W.make_inputs(w, T=1500, H=2)
+    clean = gpu_fwd(inp).cpu()
+    pad = inp.key_padding_mask.bool()
+    q, k, v = inp.q.clone(), inp.k.clone(), inp.v.clone()
+    for b in range(w.B):
+        q[b][:, pad[b]] = float("nan")
+        k[b][:, pad[b]] = float("nan")
+        v[b][:, pad[b]] = float("inf")
+    dirty = gpu_fwd(inp, q=q, k=k, v=v).cpu()
+    assert torch.equal(clean, dirty)
+
+
+def test_bitwise_deterministic_and_stream():
+    w = W.workload("bf16-b2h12t4096-r256-g68")
+    inp = W.make_inputs(w, T=2048)
+    a = gpu_fwd(inp)
+    b = gpu_fwd(inp)
+    assert torch.equal(a, b)
+    s = torch.cuda.Stream()
+    q, k, v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c = lf.attn_fwd(q, k, v, inp.r, inp.dilation, inp.global_idx)
+    s.synchronize()
+    assert torch.equal(a, c)
+
+
+def test_no_writes_outside_out():
+    w = W.workload("bf16-b1h12t4096-r256-g1")
+    inp = W.make_inputs(w, T=777, H=3)
+    q, k, v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    n = q.numel()
+    guard = 4096
+    big = torch.full((n + 2 * guard,), 7.0, dtype=q.dtype, device="cuda")
+    out = big[guard:guard + n].view_as(q)
+    lf.attn_fwd(q, k, v, inp.r, inp.dilation, inp.global_idx, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(big[:guard] == 7.0) and torch.all(big[guard + n:] == 7.0)
+    ref = oracle_full(inp)
+    assert max_err(out, ref) <= TOL["bf16"]
+
+
+def test_hf_style_global_mask_matches_index_list():
+    w = W.workload("bf16-b2h12t4096-r256-g68")
+    inp = W.make_inputs(w, T=600, H=2)
+    q, k, v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    gm = torch.zeros(w.B, 600, dtype=torch.long)
+    gm[:, inp.global_idx] = 1
+    a = lf.attn_fwd(q, k, v, inp.r, global_attention_mask=gm)
+    b = lf.attn_fwd(q, k, v, inp.r, global_idx=inp.global_idx)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_rejected_call_leaves_out_untouched():
+    q = torch.randn(1, 2, 64, 64, device="cuda", dtype=torch.bfloat16)
+    out = torch.full_like(q, 3.0)
+    with pytest.raises(lf.LfError) as e:
+        lf.attn_fwd(q, q, q, 4, global_idx=[64], out=out)   # global index out of range
+    assert e.value.status == lf.LF_E_INVALID
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
