@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of the Longformer sparse self-attention forward on one MI355X.
+
+One step = one lf_attn_fwd call over the whole hot path (band tiles of
+every dilation class, global-key columns, split global rows and their
+combine) on one batch of seeded synthetic input already resident in HBM.
+
+Prints one JSON line:
+  value      useful TFLOP/s (4*d per allowed (query, key) pair) of the path
+  roofline   the tile kernel against the bf16 dense MFMA peak (2.5 PFLOP/s)
+  cpu_baseline  the fp64 oracle on the host cores (a baseline, not a target)
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+--profile-mode runs only W + K eager calls plus a copy of known size (the
+calibration kernel for rocprofv3 HBM-byte counters) and prints no JSON.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HEADLINE = "bf16-b1h12t4096-r256-g1"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+KERNEL_SOURCES = ["sparse_long_sequence_lf_amd/csrc/lf_attn_kernels.hip",
+                  "sparse_long_sequence_lf_amd/csrc/lf_kernels.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tile_kernel_hbm_traffic.json")
+COPY_BYTES = 1 << 28        # calibration copy: 256 MiB read + 256 MiB written
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_sha") != kernel_sha():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, flops, seconds):
+    """The fp64 oracle, unmodified, on the host cores: whole-workload passes
+    repeated until about `seconds` of wall time."""
+    import oracle
+    reps = 0
+    t0 = time.perf_counter()
+    threads = 0
+    while True:
+        _, threads = oracle.fwd(inp.q, inp.k, inp.v, inp.r, inp.dilation, inp.global_idx,
+                                inp.key_padding_mask, return_threads=True)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 64:
+            break
+    return {"value": flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole workload ({inp.q.shape[0] * inp.q.shape[1] * inp.q.shape[2]} query rows), "
+                      f"{reps} passes in {el:.1f} s, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-mode", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; --gpus must be 1 "
+              "(the per-(batch, head) sharding across GPUs is described in DESIGN.md, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_long_sequence_lf_amd as lf
+    from sparse_long_sequence_lf_amd import metrics
+    from sparse_long_sequence_lf_amd import workloads as W
+
+    w = W.workload(args.workload)
+    inp = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    kpm = None if inp.key_padding_mask is None else inp.key_padding_mask.to(dev)
+    B, H, T, d = q.shape
+    stream = torch.cuda.current_stream(dev)
+    call = lf.Prepared(q, k, v, inp.r, inp.dilation, inp.global_idx, kpm, stream=stream)
+
+    if args.profile_mode:
+        for _ in range(args.warmup + args.steps):
+            call()
+        torch.cuda.synchronize()
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"profile mode: {args.warmup + args.steps} calls of {w.name}, one {COPY_BYTES} B copy", flush=True)
+        return
+
+    pairs = metrics.useful_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask)
+    flops = 4 * d * pairs
+
+    # eager: back-to-back calls, events on the call stream
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_eager = e0.elapsed_time(e1) / args.steps
+    ref_out = call.out.clone()
+
+    # the same K calls captured in one HIP graph and replayed (no host launch gaps)
+    ms_graph = None
+    graph_ok = False
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            gcall = lf.Prepared(q, k, v, inp.r, inp.dilation, inp.global_idx, kpm, out=call.out, stream=side)
+            gcall()   # the workspace for this stream is allocated outside capture
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(args.steps):
+                    gcall()
+        torch.cuda.synchronize()
+        call.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        graph_ok = torch.equal(call.out, ref_out)
+        e2 = torch.cuda.Event(enable_timing=True)
+        e3 = torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        g.replay()
+        e3.record(stream)
+        torch.cuda.synchronize()
+        ms_graph = e2.elapsed_time(e3) / args.steps
+    except Exception as ex:  # graph capture is an optimisation of the timing loop only
+        print(f"bench.py: graph capture unavailable ({ex}); reporting the eager loop", file=sys.stderr)
+
+    use_graph = ms_graph is not None and graph_ok
+    ms = ms_graph if use_graph else ms_eager
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    traffic = measured_traffic(w.name)
+    line = {
+        "metric": "useful TFLOP/s + % bf16 MFMA peak, sliding-window+global attn fwd T=4096",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v; no dataset, no weights)",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "d": d, "r": inp.r,
+                   "dilation": inp.dilation, "n_global": len(set(inp.global_idx)),
+                   "padded": inp.key_padding_mask is not None, "useful_pairs": pairs,
+                   "useful_gflop": round(flops / 1e9, 4), "parallelism": "single GPU",
+                   "timing": "hip graph of K calls" if use_graph else "eager back-to-back calls"},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "ms_per_step_eager": round(ms_eager, 5),
+        "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
+        "wall_s_eager_loop": round(wall, 4),
+        "roofline": {"bound": "mfma", "kernel": "lfk::tile_kernel", "achieved": round(tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes": metrics.algorithmic_bytes(B, H, T, d, q.element_size(),
+                                                                    inp.key_padding_mask)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, flops, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

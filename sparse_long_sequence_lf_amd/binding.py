@@ -128,3 +128,40 @@ def attn_fwd(q, k, v, r: int, dilation: Optional[Sequence[int]] = None,
     if st != LF_OK:
         raise LfError(st, last_error())
     return out
+
+
+class Prepared:
+    """lf_attn_fwd with every argument marshalled once, for tight loops.
+
+    Holds references to the tensors it was built from; ``__call__`` is one
+    ctypes call into the library on the given stream.
+    """
+
+    def __init__(self, q, k, v, r, dilation=None, global_idx=None, key_padding_mask=None, out=None,
+                 stream=None):
+        import torch
+
+        lib = load()
+        self._keep = [q, k, v]
+        B, H, T, d = q.shape
+        dt = LF_BF16 if q.dtype == torch.bfloat16 else LF_F32
+        self.out = torch.empty_like(q) if out is None else out
+        gl = list(global_idx) if global_idx is not None else []
+        self._dil = (ctypes.c_int32 * H)(*[int(x) for x in dilation]) if dilation is not None else None
+        self._g = (ctypes.c_int32 * max(1, len(gl)))(*gl) if gl else None
+        kpm = None
+        if key_padding_mask is not None:
+            kpm = key_padding_mask.to(torch.uint8).contiguous()
+            self._keep.append(kpm)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        self._fn = lib.lf_attn_fwd
+        self._args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, int(r), self._dil, self._g,
+                      len(gl), None if kpm is None else kpm.data_ptr(), self.out.data_ptr(), dt, sptr)
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != LF_OK:
+            raise LfError(st, last_error())
+        return self.out

@@ -13,9 +13,12 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblfattn.so")
 SOURCES = [os.path.join(CSRC, "lf_host.cpp"), os.path.join(CSRC, "lf_attn_kernels.hip")]
 
-# gfx950 only; packed fp32 VALU ops are kept out of the generated code.
+# gfx950 only; packed fp32 VALU ops are kept out of the generated code, and
+# MFMA accumulators live in ordinary VGPRs (no AGPR copies around the softmax
+# rescale of O).
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wno-unused-command-line-argument"]
 
 

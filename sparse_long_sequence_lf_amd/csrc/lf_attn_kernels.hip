@@ -151,94 +151,245 @@ __device__ __forceinline__ bf16x8 cat_tr(i16x4 a, i16x4 b) {
 struct Task {
     int kind;        // 0 = band tile, 1 = global-row split
     int b, h, bh;
-    int delta, c;    // residue class (band); delta = 1, c = 0 for global tasks
-    int n;           // class length (band) / T (global)
-    int m0;          // first query (class index) of the tile / first G-block slot
-    int nband;       // band blocks
-    int kb_lo;       // first band block (class block index)
-    int nblk;        // total blocks incl. global blocks
+    int delta, c;    // residue class (band); delta = 1, c = 0 for global-row tasks
+    int n;           // class length (band) / T (global rows)
+    int m0;          // first query (class index) of the tile / first global slot
+    int kb_lo;       // first key block (class block index)
+    int nband;       // band (or dense) key blocks
     int key_end;     // keys >= key_end are out of range (class index)
-    int split;       // global tasks: split index
+    int split;       // global-row tasks: split index
 };
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 template <int QB>
-__device__ Task decode_task(const Params& P, int t) {
+__device__ __forceinline__ Task decode_task(const Params& P, int t) {
     constexpr int BM = 32 * QB;
     Task k;
     if (t < P.n_band_tasks) {
         k.kind = 0;
         k.b = t / P.band_tasks_per_batch;
         int x = t - k.b * P.band_tasks_per_batch;
-        int h = 0;
-        // heads are few (<= LF_MAX_HEADS); binary search on the prefix
+        // heads are few (<= LF_MAX_HEADS): binary search on the band-task prefix
         int lo = 0, hi = P.H - 1;
         while (lo < hi) {
-            int mid = (lo + hi + 1) >> 1;
+            const int mid = (lo + hi + 1) >> 1;
             if (P.head_start[mid] <= x) lo = mid; else hi = mid - 1;
         }
-        h = lo;
+        const int h = lo;
         x -= P.head_start[h];
         k.h = h;
         k.bh = k.b * P.H + h;
-        int delta = P.dil[h];
-        int q = P.T / delta, rem = P.T % delta;
-        int tb = cdiv(q + 1, BM), ts = cdiv(q, BM);
+        const int delta = P.dil[h];
+        const int q = P.T / delta, rem = P.T - q * delta;
+        const int tb = cdiv(q + 1, BM), ts = cdiv(q, BM);
         int c, tile;
         if (x < rem * tb) { c = x / tb; tile = x - c * tb; }
-        else { int y = x - rem * tb; c = rem + y / ts; tile = y - (c - rem) * ts; }
+        else { const int y = x - rem * tb; c = rem + y / ts; tile = y - (c - rem) * ts; }
         k.delta = delta;
         k.c = c;
         k.n = (P.T - c + delta - 1) / delta;
         k.m0 = tile * BM;
-        int r = P.r;
+        const int r = P.r;
         int lo_k = k.m0 - r; if (lo_k < 0) lo_k = 0;
         int hi_k = k.m0 + BM - 1 + r; if (hi_k > k.n - 1) hi_k = k.n - 1;
         k.kb_lo = lo_k / KBLK;
         k.nband = hi_k / KBLK - k.kb_lo + 1;
-        k.nblk = k.nband + cdiv(P.n_g, KBLK);
         k.key_end = k.n;
         k.split = 0;
     } else {
         k.kind = 1;
-        int g = t - P.n_band_tasks;
-        int per_bh = P.n_split * P.n_ggroups;
+        const int g = t - P.n_band_tasks;
+        const int per_bh = P.n_split * P.n_ggroups;
         k.bh = g / per_bh;
-        int rem = g - k.bh * per_bh;
-        int grp = rem / P.n_split;
+        const int rem = g - k.bh * per_bh;
+        const int grp = rem / P.n_split;
         k.split = rem - grp * P.n_split;
         k.b = k.bh / P.H;
         k.h = k.bh - k.b * P.H;
         k.delta = 1;
         k.c = 0;
         k.n = P.T;
-        k.m0 = grp * BM;  // first global slot of this group
-        int j0 = k.split * P.split_len;
+        k.m0 = grp * BM;
+        const int j0 = k.split * P.split_len;
         int j1 = j0 + P.split_len; if (j1 > P.T) j1 = P.T;
         k.kb_lo = j0 / KBLK;
         k.nband = cdiv(j1 - j0, KBLK);
-        k.nblk = k.nband;
         k.key_end = j1;
     }
     return k;
+}
+
+// is position pos one of the (sorted) global positions?
+__device__ __forceinline__ bool is_global(const Params& P, int pos) {
+    int lo = 0, hi = P.n_g - 1;
+    while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        const int g = P.glob[mid];
+        if (g == pos) return true;
+        if (g < pos) lo = mid + 1; else hi = mid - 1;
+    }
+    return false;
+}
+
+// max over the two 32-lane halves (lanes l and l^32 hold the two key halves of
+// a query): one v_permlane32_swap, no LDS round trip
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    const f32x2 f = __builtin_bit_cast(f32x2, r);
+    return __builtin_fmaxf(f[0], f[1]);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    const f32x2 f = __builtin_bit_cast(f32x2, r);
+    return f[0] + f[1];
+}
+
+// agent-scope relaxed atomic accesses (coherent across the XCDs' L2s)
+__device__ __forceinline__ void store_coherent(uint32_t* p, float x) {
+    __hip_atomic_store(p, __builtin_bit_cast(uint32_t, x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const uint32_t* p) {
+    return __builtin_bit_cast(float, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Block masks.  Bit t of a block's mask word is set when key row t of the
+// block is not a real key (beyond the sequence/class/split, or padded).
+enum BlockMode { kInterior = 0, kBandEdge = 1, kGlobalKeys = 2, kDense = 3 };
+
+// ---------------------------------------------------------------------------
+// Per-wave attention state and the work on one 32-key block.
+
+template <int NP>
+struct WaveState {
+    bf16x8 qh[4], ql[4];  // Q^T operands (lo part only for fp32 inputs)
+    f32x16 o0, o1;        // O^T: channels 0..31 and 32..63 of this lane's query
+    float ms;             // running max in scaled base-2 units
+    float lp;             // this lane's part of the running sum
+};
+
+template <int MODE, int KS, int NP>
+__device__ __forceinline__ void attend_block(WaveState<NP>& W, const char* buf, int blk, int key0, int m,
+                                             int r, int lane) {
+    using SG = Stage<KS, NP>;
+    const int lq = lane & 31, lg = lane >> 5;
+    // S^T = K Q^T for this block: 32 keys x 32 queries
+    f32x16 s = {};
+    const char* kb = buf + SG::kOff(0, blk);
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+        const bf16x8 kf = as_bf16x8(*(const u32x4*)(kb + swzK(lq, 2 * ks + lg)));
+        s = mfma(kf, W.qh[ks], s);
+        if constexpr (NP == 2) {
+            const bf16x8 kfl = as_bf16x8(*(const u32x4*)(buf + SG::kOff(1, blk) + swzK(lq, 2 * ks + lg)));
+            s = mfma(kf, W.ql[ks], s);
+            s = mfma(kfl, W.qh[ks], s);
+        }
+    }
+    if constexpr (MODE != kInterior) {
+        const uint32_t bad = *(const uint32_t*)(buf + SG::maskOff + blk * 4);
+        const int* gcls = (const int*)(buf + SG::gclsOff) + blk * KBLK;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int kl = 8 * (i >> 2) + 4 * lg + (i & 3);   // key row inside the block
+            bool ok = ((bad >> kl) & 1u) == 0u;
+            if constexpr (MODE == kBandEdge) {
+                const int dk = key0 + kl - m;
+                ok = ok && (uint32_t)(dk + r) <= (uint32_t)(2 * r);
+            } else if constexpr (MODE == kGlobalKeys) {
+                const int dk = gcls[kl] - m;
+                ok = ok && (uint32_t)(dk + r) > (uint32_t)(2 * r);   // not already in the window
+            }
+            s[i] = ok ? s[i] : kNegInf;
+        }
+    }
+    // running max: raw-score max of the block, scaled; O is rescaled only when
+    // the max grows by more than 2^8 (then every later p stays <= 2^8)
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; i++) mx = __builtin_fmaxf(mx, s[i]);
+    mx = halves_max(mx);
+    const float mxs = mx * kScaleLog2;
+    const bool need = mxs > W.ms + 8.0f;
+    if (__ballot(need)) {
+        const float msn = need ? mxs : W.ms;
+        const float alpha = need ? __builtin_amdgcn_exp2f(W.ms - msn) : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) { W.o0[i] *= alpha; W.o1[i] *= alpha; }
+        W.lp *= alpha;
+        W.ms = msn;
+    }
+    const float nms = (W.ms == kNegInf) ? 0.0f : -W.ms;
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], kScaleLog2, nms));
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) ps += p[i];
+    W.lp += ps;
+    // P^T operands: step st covers accumulator elements 8st .. 8st+7
+    bf16x8 pb[2], pbl[2];
+#pragma unroll
+    for (int st = 0; st < 2; st++) {
+        u32x4 w, wl;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float a = p[8 * st + 2 * e], b = p[8 * st + 2 * e + 1];
+            const uint32_t hw = pack_bf16(a, b);
+            w[e] = hw;
+            if constexpr (NP == 2) {
+                const float ah = __builtin_bit_cast(float, hw << 16);
+                const float bh = __builtin_bit_cast(float, hw & 0xffff0000u);
+                wl[e] = pack_bf16(a - ah, b - bh);
+            }
+        }
+        pb[st] = as_bf16x8(w);
+        if constexpr (NP == 2) pbl[st] = as_bf16x8(wl);
+    }
+    // O^T += V^T P^T; V^T operands by transposing reads: lane (16G + L) supplies
+    // row 16st + 8hf + 4(G>>1) + (L>>2), channels 32cb + 16(G&1) + 4(L&3)
+    const int G = lane >> 4, L = lane & 15;
+    const int t0 = 4 * (G >> 1) + (L >> 2);
+#pragma unroll
+    for (int st = 0; st < 2; st++) {
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++) {
+            const int byte = 64 * cb + 32 * (G & 1) + 8 * (L & 3);
+            const int ch = byte >> 4, inner = byte & 15;
+            const int ta = 16 * st + t0, tb = ta + 8;
+            const char* vb = buf + SG::vOff(0, blk);
+            const bf16x8 va = cat_tr(ds_tr16(vb + swzV(ta, ch) + inner), ds_tr16(vb + swzV(tb, ch) + inner));
+            f32x16& oc = cb ? W.o1 : W.o0;
+            oc = mfma(va, pb[st], oc);
+            if constexpr (NP == 2) {
+                const char* vbl = buf + SG::vOff(1, blk);
+                const bf16x8 val = cat_tr(ds_tr16(vbl + swzV(ta, ch) + inner), ds_tr16(vbl + swzV(tb, ch) + inner));
+                oc = mfma(va, pbl[st], oc);
+                oc = mfma(val, pb[st], oc);
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
 // The tile kernel.
 
 template <int QB, int KS, typename ET, typename OT>
-__global__ __launch_bounds__(64 * QB * KS) void tile_kernel(const Params P) {
+__global__ __launch_bounds__(64 * QB * KS) __attribute__((amdgpu_waves_per_eu(LFK_WAVES_PER_EU))) void tile_kernel(const Params P) {
     constexpr int NT = 64 * QB * KS;
     constexpr int NP = Elem<ET>::NP;
     using SG = Stage<KS, NP>;
-    constexpr int CHUNKS = KS * KBLK * 8;              // 16-byte (8-channel) chunks per tensor per stage
-    constexpr int CPT = (CHUNKS + NT - 1) / NT;         // chunks per thread
+    constexpr int R = KS * KBLK;               // key rows per stage
+    constexpr int CHUNKS = R * 8;              // 8-channel chunks per tensor per stage
+    static_assert(CHUNKS % NT == 0, "stage chunks must divide evenly over the workgroup");
+    constexpr int CPT = CHUNKS / NT;           // chunks per thread per tensor
     constexpr int MERGE_BYTES = (KS - 1) * QB * 64 * 36 * 4;
     constexpr int SMEM = (2 * SG::bytes > MERGE_BYTES) ? 2 * SG::bytes : MERGE_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
-    // ---- which task (XCD-aware: the 8 dies take contiguous task ranges)
+    // ---- which task (XCD-aware: each of the 8 dies takes a contiguous task range)
     const int per_xcd = gridDim.x >> 3;
     const int task_id = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (task_id >= P.n_tasks) return;
@@ -250,7 +401,7 @@ __global__ __launch_bounds__(64 * QB * KS) void tile_kernel(const Params P) {
     const int qb = wave % QB;
     const int ph = wave / QB;          // key phase of this wave
     const int lq = lane & 31;          // query column owned by this lane
-    const int lg = lane >> 5;          // which half of the keys of a tile column
+    const int lg = lane >> 5;
 
     const size_t head_off = (size_t)tk.bh * P.T * D;
     const ET* __restrict__ Kg = (const ET*)P.k + head_off;
@@ -259,23 +410,22 @@ __global__ __launch_bounds__(64 * QB * KS) void tile_kernel(const Params P) {
     const uint8_t* __restrict__ padrow = P.pad ? P.pad + (size_t)tk.b * P.T : nullptr;
     const int r = P.r;
 
-    // ---- this wave's queries
-    const int mq0 = tk.m0 + 32 * qb;   // first query (class index or global slot)
+    // ---- this wave's 32 queries
+    const int mq0 = tk.m0 + 32 * qb;   // first query (class index, or global slot)
     bool wave_active;
     int my_pos = -1;                   // position of this lane's query
     if (tk.kind == 0) {
         wave_active = mq0 < tk.n;
-        int m = mq0 + lq;
+        const int m = mq0 + lq;
         if (m < tk.n) my_pos = tk.c + tk.delta * m;
     } else {
         wave_active = mq0 < P.n_g;
-        int s = mq0 + lq;
-        if (s < P.n_g) my_pos = P.glob[s];
+        const int sl = mq0 + lq;
+        if (sl < P.n_g) my_pos = P.glob[sl];
     }
-    bool my_pad = (my_pos >= 0 && padrow) ? padrow[my_pos] != 0 : false;
+    const bool my_pad = (my_pos >= 0 && padrow) ? padrow[my_pos] != 0 : false;
 
-    // Q^T fragments: lane (query lq, half lg) holds channels 16*ks + 8*lg .. +7
-    bf16x8 qh[4], ql[4];
+    WaveState<NP> W;
     {
         const bool ok = my_pos >= 0 && !my_pad;
         const ET* qrow = Qg + (size_t)(ok ? my_pos : 0) * D;
@@ -283,22 +433,26 @@ __global__ __launch_bounds__(64 * QB * KS) void tile_kernel(const Params P) {
         for (int ks = 0; ks < 4; ks++) {
             const int c0 = 16 * ks + 8 * lg;
             if constexpr (NP == 1) {
-                u32x4 x = ok ? *(const u32x4*)(qrow + c0) : (u32x4){0, 0, 0, 0};
-                qh[ks] = as_bf16x8(x);
-                ql[ks] = as_bf16x8((u32x4){0, 0, 0, 0});
+                const u32x4 x = *(const u32x4*)(qrow + c0);
+                W.qh[ks] = as_bf16x8(ok ? x : (u32x4){0, 0, 0, 0});
             } else {
                 Raw32 x;
-                if (ok) { x.a = *(const u32x4*)(qrow + c0); x.b = *(const u32x4*)(qrow + c0 + 4); }
-                else { x.a = (u32x4){0, 0, 0, 0}; x.b = x.a; }
+                x.a = *(const u32x4*)(qrow + c0);
+                x.b = *(const u32x4*)(qrow + c0 + 4);
+                if (!ok) { x.a = (u32x4){0, 0, 0, 0}; x.b = x.a; }
                 u32x4 hi, lo;
                 split8(x, hi, lo);
-                qh[ks] = as_bf16x8(hi);
-                ql[ks] = as_bf16x8(lo);
+                W.qh[ks] = as_bf16x8(hi);
+                W.ql[ks] = as_bf16x8(lo);
             }
         }
     }
+    W.o0 = (f32x16){};
+    W.o1 = (f32x16){};
+    W.ms = kNegInf;
+    W.lp = 0.f;
 
-    // wave's own window, in band blocks (class block indices)
+    // band blocks this wave's queries can reach
     int wb_lo = 0, wb_hi = -1;
     if (tk.kind == 0) {
         int a = mq0 - r; if (a < 0) a = 0;
@@ -307,254 +461,149 @@ __global__ __launch_bounds__(64 * QB * KS) void tile_kernel(const Params P) {
         wb_hi = z / KBLK;
     }
 
-    // ---- running state
-    f32x16 o0 = {}, o1 = {};
-    float ms = kNegInf;  // running max, already in scaled base-2 units
-    float lp = 0.f;      // this lane's part of the row sum
+    // ---- stage plan: band (or dense) stages, then global-key stages
+    const int ngb = tk.kind == 0 ? cdiv(P.n_g, KBLK) : 0;
+    const int NSb = cdiv(tk.nband, KS);
+    const int NS = NSb + cdiv(ngb, KS);
 
-    const int NS = (tk.nblk + KS - 1) / KS;
+    // loader geometry: chunk j of this thread is row (tid >> 3) + j * NT/8, channels 8*(tid & 7)..+7
+    const int lch = tid & 7;
+    const int lrow0 = tid >> 3;
+    const int key_base = tk.kb_lo * KBLK;
 
-    // ---- stage loader (global -> registers -> LDS)
     struct Regs {
-        u32x4 k[CPT][NP == 1 ? 1 : 2];
-        u32x4 v[CPT][NP == 1 ? 1 : 2];
-        int pos[CPT];
-        bool inr[CPT];
+        u32x4 k[CPT][NP];
+        u32x4 v[CPT][NP];
+        bool ok[CPT];
+        uint32_t mword;   // mask lanes: this lane's row validity is folded in at commit
+        bool mvalid;
+        int gcls;
     };
 
-    auto row_of = [&](int stage, int idx, int& pos, bool& inr, int& gcls) {
-        const int blk = idx >> 8;
-        const int t = (idx >> 3) & 31;
-        const int jb = stage * KS + blk;
-        pos = 0; inr = false; gcls = kNotInClass;
-        if (jb >= tk.nblk) return;
-        if (jb < tk.nband) {
-            const int kk = (tk.kb_lo + jb) * KBLK + t;
-            if (kk < tk.key_end) { inr = true; pos = tk.c + tk.delta * kk; }
+    // position of stage row `row` of stage `st` (and whether it is a real key)
+    auto row_pos = [&](int st, int row, int& pos, bool& inr) {
+        if (st < NSb) {
+            const int kk = key_base + st * R + row;
+            inr = kk < tk.key_end;
+            pos = inr ? tk.c + tk.delta * kk : 0;
         } else {
-            const int s = (jb - tk.nband) * KBLK + t;
-            if (s < P.n_g) {
-                inr = true;
-                pos = P.glob[s];
+            const int slot = (st - NSb) * R + row;
+            inr = slot < P.n_g;
+            pos = inr ? P.glob[slot] : 0;
+        }
+    };
+
+    auto issue = [&](int st, Regs& Rg) {
+#pragma unroll
+        for (int j = 0; j < CPT; j++) {
+            int pos; bool inr;
+            row_pos(st, lrow0 + j * (NT / 8), pos, inr);
+            const size_t off = (size_t)pos * D + lch * 8;
+#pragma unroll
+            for (int p = 0; p < NP; p++) {
+                Rg.k[j][p] = *(const u32x4*)(Kg + off + 4 * p);
+                Rg.v[j][p] = *(const u32x4*)(Vg + off + 4 * p);
+            }
+            bool ok = inr;
+            if (padrow) ok = ok && padrow[pos] == 0;
+            Rg.ok[j] = ok;
+        }
+        // mask lanes: waves 0..KS-1, lanes 0..31 own stage row 32*wave + lane
+        if (wave < KS) {
+            int pos; bool inr;
+            row_pos(st, 32 * wave + lq, pos, inr);
+            bool ok = inr && lg == 0;
+            if (padrow) ok = ok && padrow[pos] == 0;
+            Rg.mvalid = ok;
+            Rg.gcls = kNotInClass;
+            if (st >= NSb && inr) {
                 const int dpos = pos - tk.c;
-                if (dpos >= 0 && dpos % tk.delta == 0) gcls = dpos / tk.delta;
+                if (dpos >= 0 && dpos % tk.delta == 0) Rg.gcls = dpos / tk.delta;
             }
         }
     };
 
-    auto issue = [&](int stage, Regs& R) {
+    auto commit = [&](const Regs& Rg, char* buf) {
+        const u32x4 z = {0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < CPT; j++) {
-            const int idx = tid + j * NT;
-            R.inr[j] = false;
-            R.pos[j] = 0;
-            if (idx < CHUNKS) {
-                int pos, gcls; bool inr;
-                row_of(stage, idx, pos, inr, gcls);
-                R.inr[j] = inr;
-                R.pos[j] = pos;
-                const int ch = idx & 7;
-                if (inr) {
-                    const ET* kp = Kg + (size_t)pos * D + ch * 8;
-                    const ET* vp = Vg + (size_t)pos * D + ch * 8;
-                    R.k[j][0] = *(const u32x4*)kp;
-                    R.v[j][0] = *(const u32x4*)vp;
-                    if constexpr (NP == 2) {
-                        R.k[j][1] = *(const u32x4*)(kp + 4);
-                        R.v[j][1] = *(const u32x4*)(vp + 4);
-                    }
+            const int row = lrow0 + j * (NT / 8);
+            const int blk = row >> 5, t = row & 31;
+            if constexpr (NP == 1) {
+                *(u32x4*)(buf + SG::kOff(0, blk) + swzK(t, lch)) = Rg.ok[j] ? Rg.k[j][0] : z;
+                *(u32x4*)(buf + SG::vOff(0, blk) + swzV(t, lch)) = Rg.ok[j] ? Rg.v[j][0] : z;
+            } else {
+                u32x4 kh = z, kl = z, vh = z, vl = z;
+                if (Rg.ok[j]) {
+                    split8(Raw32{Rg.k[j][0], Rg.k[j][1]}, kh, kl);
+                    split8(Raw32{Rg.v[j][0], Rg.v[j][1]}, vh, vl);
                 }
+                *(u32x4*)(buf + SG::kOff(0, blk) + swzK(t, lch)) = kh;
+                *(u32x4*)(buf + SG::kOff(1, blk) + swzK(t, lch)) = kl;
+                *(u32x4*)(buf + SG::vOff(0, blk) + swzV(t, lch)) = vh;
+                *(u32x4*)(buf + SG::vOff(1, blk) + swzV(t, lch)) = vl;
             }
+        }
+        if (wave < KS) {
+            const uint32_t good = (uint32_t)__ballot(Rg.mvalid);   // lanes 0..31 only
+            if (lane == 0) *(uint32_t*)(buf + SG::maskOff + wave * 4) = ~good;
+            if (lg == 0) ((int*)(buf + SG::gclsOff))[wave * KBLK + lq] = Rg.gcls;
         }
     };
 
-    auto commit = [&](int stage, const Regs& R, char* buf) {
-#pragma unroll
-        for (int j = 0; j < CPT; j++) {
-            const int idx = tid + j * NT;
-            if (idx < CHUNKS) {  // wave-uniform: NT is a multiple of 64
-                const int blk = idx >> 8;
-                const int t = (idx >> 3) & 31;
-                const int ch = idx & 7;
-                bool valid = R.inr[j];
-                if (valid && padrow) valid = padrow[R.pos[j]] == 0;
-                u32x4 z = {0, 0, 0, 0};
-                if constexpr (NP == 1) {
-                    *(u32x4*)(buf + SG::kOff(0, blk) + swzK(t, ch)) = valid ? R.k[j][0] : z;
-                    *(u32x4*)(buf + SG::vOff(0, blk) + swzV(t, ch)) = valid ? R.v[j][0] : z;
-                } else {
-                    u32x4 kh = z, kl = z, vh = z, vl = z;
-                    if (valid) {
-                        Raw32 rk{R.k[j][0], R.k[j][1]}, rv{R.v[j][0], R.v[j][1]};
-                        split8(rk, kh, kl);
-                        split8(rv, vh, vl);
-                    }
-                    *(u32x4*)(buf + SG::kOff(0, blk) + swzK(t, ch)) = kh;
-                    *(u32x4*)(buf + SG::kOff(1, blk) + swzK(t, ch)) = kl;
-                    *(u32x4*)(buf + SG::vOff(0, blk) + swzV(t, ch)) = vh;
-                    *(u32x4*)(buf + SG::vOff(1, blk) + swzV(t, ch)) = vl;
-                }
-                // one mask bit per row: lanes 8u .. 8u+7 of a wave cover row u
-                uint64_t bad = __ballot(!valid);
-                if (lane == 0) {
-                    uint64_t m8 = bad & 0x0101010101010101ull;
-                    uint32_t bits = (uint32_t)((m8 * 0x0102040810204080ull) >> 56);
-                    // bit u of the byte = row u of this wave's 8 rows
-                    ((uint8_t*)(buf + SG::maskOff))[blk * 4 + (t >> 3)] = (uint8_t)bits;
-                }
-                if (ch == 0) {
-                    int pos, gcls; bool inr;
-                    row_of(stage, idx, pos, inr, gcls);
-                    ((int*)(buf + SG::gclsOff))[blk * KBLK + t] = gcls;
-                }
-            }
-        }
-    };
-
-    // ---- one block of 32 keys against this wave's 32 queries
-    auto compute = [&](const char* buf, int blk, int mode, int key0) {
-        // mode 0: interior band block (no masking)   1: masked band block
-        //      2: global-key block                    3: dense block (global rows)
-        const uint32_t mword = *(const uint32_t*)(buf + SG::maskOff + blk * 4);
-        f32x16 s = {};
-        const char* kb = buf + SG::kOff(0, blk);
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-            const bf16x8 kf = as_bf16x8(*(const u32x4*)(kb + swzK(lq, 2 * ks + lg)));
-            s = mfma(kf, qh[ks], s);
-            if constexpr (NP == 2) {
-                const bf16x8 kfl = as_bf16x8(*(const u32x4*)(buf + SG::kOff(1, blk) + swzK(lq, 2 * ks + lg)));
-                s = mfma(kf, ql[ks], s);
-                s = mfma(kfl, qh[ks], s);
-            }
-        }
-        if (mode != 0) {
-            const int m = mq0 + lq;
-            const int* gcls = (const int*)(buf + SG::gclsOff) + blk * KBLK;
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int kl = 8 * (i >> 2) + 4 * lg + (i & 3);   // key row inside the block
-                bool ok = ((mword >> kl) & 1u) == 0u;
-                if (mode == 1) {
-                    const int dk = key0 + kl - m;
-                    ok = ok && dk <= r && dk >= -r;
-                } else if (mode == 2) {
-                    const int dk = gcls[kl] - m;
-                    ok = ok && !(dk <= r && dk >= -r);   // already counted in the window
-                }
-                s[i] = ok ? s[i] : kNegInf;
-            }
-        }
-        // row max over this block: 16 keys here, 16 in lane ^ 32
-        float mx = s[0];
-#pragma unroll
-        for (int i = 1; i < 16; i++) mx = __builtin_fmaxf(mx, s[i]);
-        mx = __builtin_fmaxf(mx, wave_xor32(mx));
-        const float mxs = mx * kScaleLog2;
-        const bool need = mxs > ms + 8.0f;
-        if (__ballot(need)) {
-            const float msn = need ? mxs : ms;
-            const float alpha = need ? __builtin_amdgcn_exp2f(ms - msn) : 1.0f;
-#pragma unroll
-            for (int i = 0; i < 16; i++) { o0[i] *= alpha; o1[i] *= alpha; }
-            lp *= alpha;
-            ms = msn;
-        }
-        const float nms = (ms == kNegInf) ? 0.0f : -ms;
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 16; i++) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], kScaleLog2, nms));
-        float ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; i++) ps += p[i];
-        lp += ps;
-        // P^T operands: step st covers accumulator elements 8st .. 8st+7
-        bf16x8 pb[2], pbl[2];
-#pragma unroll
-        for (int st = 0; st < 2; st++) {
-            u32x4 w, wl;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const float a = p[8 * st + 2 * e], b = p[8 * st + 2 * e + 1];
-                w[e] = pack_bf16(a, b);
-                if constexpr (NP == 2) {
-                    const uint32_t hw = w[e];
-                    const float ah = __builtin_bit_cast(float, hw << 16);
-                    const float bh = __builtin_bit_cast(float, hw & 0xffff0000u);
-                    wl[e] = pack_bf16(a - ah, b - bh);
-                }
-            }
-            pb[st] = as_bf16x8(w);
-            if constexpr (NP == 2) pbl[st] = as_bf16x8(wl);
-        }
-        // V^T operands by transposing reads: lane (16G + L) supplies row
-        // 16st + 8hf + 4(G>>1) + (L>>2), channels 32cb + 16(G&1) + 4(L&3)
-        const int G = lane >> 4, L = lane & 15;
-#pragma unroll
-        for (int st = 0; st < 2; st++) {
-#pragma unroll
-            for (int cb = 0; cb < 2; cb++) {
-                const int t0 = 16 * st + 4 * (G >> 1) + (L >> 2);
-                const int byte = 64 * cb + 32 * (G & 1) + 8 * (L & 3);
-                const int ch = byte >> 4, inner = byte & 15;
-                const char* vb = buf + SG::vOff(0, blk);
-                const bf16x8 va = cat_tr(ds_tr16(vb + swzV(t0, ch) + inner), ds_tr16(vb + swzV(t0 + 8, ch) + inner));
-                f32x16& oc = cb ? o1 : o0;
-                oc = mfma(va, pb[st], oc);
-                if constexpr (NP == 2) {
-                    const char* vbl = buf + SG::vOff(1, blk);
-                    const bf16x8 val = cat_tr(ds_tr16(vbl + swzV(t0, ch) + inner), ds_tr16(vbl + swzV(t0 + 8, ch) + inner));
-                    oc = mfma(va, pbl[st], oc);
-                    oc = mfma(val, pb[st], oc);
-                }
-            }
-        }
-    };
-
-    // ---- main loop over stages, double-buffered
-    char* buf0 = smem;
-    char* buf1 = smem + SG::bytes;
+    // ---- main loop over stages, double-buffered through LDS
+    char* const buf0 = smem;
+    char* const buf1 = smem + SG::bytes;
     {
-        Regs R;
-        issue(0, R);
-        commit(0, R, buf0);
+        Regs Rg;
+        issue(0, Rg);
+        commit(Rg, buf0);
         __syncthreads();
     }
+    const int m_me = mq0 + lq;         // this lane's query (class index / global slot)
     for (int st = 0; st < NS; st++) {
-        Regs R;
+        Regs Rg;
         const bool more = st + 1 < NS;
-        if (more) issue(st + 1, R);
+        if (more) issue(st + 1, Rg);
         const char* cur = (st & 1) ? buf1 : buf0;
-        const int jb = st * KS + ph;
-        if (wave_active && jb < tk.nblk) {
-            if (tk.kind == 1) {
-                compute(cur, ph, 3, 0);
-            } else if (jb < tk.nband) {
-                const int kb = tk.kb_lo + jb;
-                if (kb >= wb_lo && kb <= wb_hi) {
+        if (wave_active) {
+            if (st < NSb) {
+                const int jb = st * KS + ph;
+                if (jb < tk.nband) {
+                    const uint32_t bad = *(const uint32_t*)(cur + SG::maskOff + ph * 4);
+                    const int kb = tk.kb_lo + jb;
                     const int key0 = kb * KBLK;
-                    const uint32_t mword = *(const uint32_t*)(cur + SG::maskOff + ph * 4);
-                    const bool interior = mword == 0u && key0 >= mq0 + 31 - r && key0 + 31 <= mq0 + r;
-                    if (mword != 0xffffffffu) compute(cur, ph, interior ? 0 : 1, key0);
+                    if (bad != 0xffffffffu) {
+                        if (tk.kind == 1) {
+                            attend_block<kDense, KS, NP>(W, cur, ph, key0, m_me, r, lane);
+                        } else if (kb >= wb_lo && kb <= wb_hi) {
+                            const bool interior = bad == 0u && key0 >= mq0 + 31 - r && key0 + 31 <= mq0 + r;
+                            if (interior) attend_block<kInterior, KS, NP>(W, cur, ph, key0, m_me, r, lane);
+                            else attend_block<kBandEdge, KS, NP>(W, cur, ph, key0, m_me, r, lane);
+                        }
+                    }
                 }
             } else {
-                const uint32_t mword = *(const uint32_t*)(cur + SG::maskOff + ph * 4);
-                if (mword != 0xffffffffu) compute(cur, ph, 2, 0);
+                const int jg = (st - NSb) * KS + ph;
+                if (jg < ngb) {
+                    const uint32_t bad = *(const uint32_t*)(cur + SG::maskOff + ph * 4);
+                    if (bad != 0xffffffffu) attend_block<kGlobalKeys, KS, NP>(W, cur, ph, 0, m_me, r, lane);
+                }
             }
         }
-        if (more) commit(st + 1, R, (st & 1) ? buf0 : buf1);
+        if (more) commit(Rg, (st & 1) ? buf0 : buf1);
         __syncthreads();
     }
 
-    // ---- merge the KS phases of each query block (LDS), phase 0 keeps the result
+    // ---- merge the KS phases of each query block (LDS); phase 0 keeps the result
     if constexpr (KS > 1) {
         float* mbuf = (float*)smem;
         if (ph > 0) {
             float* dst = mbuf + (((ph - 1) * QB + qb) * 64 + lane) * 36;
-            dst[0] = ms;
-            dst[1] = lp;
+            dst[0] = W.ms;
+            dst[1] = W.lp;
 #pragma unroll
-            for (int i = 0; i < 16; i++) { dst[2 + i] = o0[i]; dst[18 + i] = o1[i]; }
+            for (int i = 0; i < 16; i++) { dst[2 + i] = W.o0[i]; dst[18 + i] = W.o1[i]; }
         }
         __syncthreads();
         if (ph == 0) {
@@ -562,136 +611,135 @@ __global__ __launch_bounds__(64 * QB * KS) void tile_kernel(const Params P) {
             for (int p2 = 1; p2 < KS; p2++) {
                 const float* src = mbuf + (((p2 - 1) * QB + qb) * 64 + lane) * 36;
                 const float ms2 = src[0], lp2 = src[1];
-                const float mn = __builtin_fmaxf(ms, ms2);
-                const float a1 = (ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ms - mn);
+                const float mn = __builtin_fmaxf(W.ms, ms2);
+                const float a1 = (W.ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(W.ms - mn);
                 const float a2 = (ms2 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ms2 - mn);
 #pragma unroll
                 for (int i = 0; i < 16; i++) {
-                    o0[i] = o0[i] * a1 + src[2 + i] * a2;
-                    o1[i] = o1[i] * a1 + src[18 + i] * a2;
+                    W.o0[i] = W.o0[i] * a1 + src[2 + i] * a2;
+                    W.o1[i] = W.o1[i] * a1 + src[18 + i] * a2;
                 }
-                lp = lp * a1 + lp2 * a2;
-                ms = mn;
+                W.lp = W.lp * a1 + lp2 * a2;
+                W.ms = mn;
             }
         }
     }
-    if (ph != 0 || !wave_active) return;
 
-    const float l = lp + wave_xor32(lp);
+    const bool writer = ph == 0 && wave_active;
+    const float l = halves_sum(W.lp);
 
     if (tk.kind == 0) {
-        // ---- epilogue: y = O / l for the tile's valid queries; padded rows -> 0
-        if (my_pos < 0) return;
+        // ---- epilogue: y = O / l for the tile's valid queries; padded rows -> 0.
+        // Rows of global queries are left to the global-row combine.
+        if (!writer || my_pos < 0) return;
+        if (P.n_g > 0 && is_global(P, my_pos)) return;
         OT* orow = (OT*)P.out + head_off + (size_t)my_pos * D;
         const float inv = (my_pad || l == 0.f) ? 0.f : 1.0f / l;
 #pragma unroll
         for (int cb = 0; cb < 2; cb++) {
-            const f32x16& oc = cb ? o1 : o0;
+            const f32x16& oc = cb ? W.o1 : W.o0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int c0 = 32 * cb + 8 * j + 4 * lg;
                 const float y0 = oc[4 * j + 0] * inv, y1 = oc[4 * j + 1] * inv;
                 const float y2 = oc[4 * j + 2] * inv, y3 = oc[4 * j + 3] * inv;
                 if constexpr (sizeof(OT) == 2) {
-                    u32x2 w = {pack_bf16(y0, y1), pack_bf16(y2, y3)};
+                    const u32x2 w = {pack_bf16(y0, y1), pack_bf16(y2, y3)};
                     *(u32x2*)(orow + c0) = w;
                 } else {
-                    f32x4 w = {y0, y1, y2, y3};
+                    const f32x4 w = {y0, y1, y2, y3};
                     *(f32x4*)(orow + c0) = w;
                 }
             }
         }
-    } else {
-        // ---- global rows: write this split's (max, sum, O) for each global slot
-        const int slot = mq0 + lq;
-        if (slot >= P.n_g) return;
-        float* part = P.part + (((size_t)tk.bh * P.n_split + tk.split) * P.g_pad + slot) * (D + 2);
-        if (lg == 0) { part[0] = ms; part[1] = l; }
+        return;
+    }
+
+    // ---- global rows: write this split's (max, sum, O) for each global slot.
+    // Partials cross dies (each XCD has its own L2), so they are written and
+    // read as agent-scope relaxed atomics, which go to the coherent memory
+    // side without writing back or invalidating whole L2s the way a
+    // device-wide fence does.
+    const int slot = mq0 + lq;
+    if (writer && slot < P.n_g) {
+        uint32_t* part = (uint32_t*)P.part + (((size_t)tk.bh * P.n_split + tk.split) * P.g_pad + slot) * (D + 2);
+        if (lg == 0) {
+            store_coherent(part + 0, W.ms);
+            store_coherent(part + 1, l);
+        }
 #pragma unroll
         for (int cb = 0; cb < 2; cb++) {
-            const f32x16& oc = cb ? o1 : o0;
+            const f32x16& oc = cb ? W.o1 : W.o0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int c0 = 32 * cb + 8 * j + 4 * lg;
-                part[2 + c0 + 0] = oc[4 * j + 0];
-                part[2 + c0 + 1] = oc[4 * j + 1];
-                part[2 + c0 + 2] = oc[4 * j + 2];
-                part[2 + c0 + 3] = oc[4 * j + 3];
+#pragma unroll
+                for (int e = 0; e < 4; e++) store_coherent(part + 2 + c0 + e, oc[4 * j + e]);
             }
         }
     }
-}
-
-// ---------------------------------------------------------------------------
-// Combine the split partials of each global row (rescale to a common max,
-// add, divide) and write the row.  One 64-lane workgroup per (b, h, global).
-
-template <typename OT>
-__global__ __launch_bounds__(64) void combine_kernel(const Params P) {
-    const int gi = blockIdx.x % P.n_g;
-    const int bh = blockIdx.x / P.n_g;
-    const int b = bh / P.H;
-    const int c = threadIdx.x;
-    const int pos = P.glob[gi];
-    OT* orow = (OT*)P.out + ((size_t)bh * P.T + pos) * D;
-    const bool padded = P.pad && P.pad[(size_t)b * P.T + pos] != 0;
-    float y = 0.f;
-    if (!padded) {
-        const float* base = P.part + ((size_t)bh * P.n_split * P.g_pad + gi) * (D + 2);
-        const size_t stride = (size_t)P.g_pad * (D + 2);
-        float M = kNegInf;
-        for (int s = 0; s < P.n_split; s++) M = __builtin_fmaxf(M, base[s * stride]);
-        float Lsum = 0.f, O = 0.f;
-        if (M != kNegInf) {
-            for (int s = 0; s < P.n_split; s++) {
-                const float* p = base + s * stride;
-                const float w = (p[0] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(p[0] - M);
-                Lsum += p[1] * w;
-                O += p[2 + c] * w;
-            }
+    // The last of the n_split * n_ggroups workgroups of head (b, h) to finish
+    // rescales and adds the partials of every global row of that head.  The
+    // counter is returned to zero by that workgroup, ready for the next call.
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores have completed
+    __syncthreads();
+    int* flag = (int*)smem;
+    if (tid == 0) {
+        const int done = __hip_atomic_fetch_add(P.counter + tk.bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = done == P.n_split * P.n_ggroups - 1;
+    }
+    __syncthreads();
+    if (*flag == 0) return;
+    // one wave per global row; lanes first span the splits (max and sum of the
+    // rescaled partial sums), then the 64 channels (rescaled partial outputs,
+    // loads issued back to back)
+    constexpr int NW = NT / 64;
+    const size_t stride = (size_t)P.g_pad * (D + 2);
+    for (int gi = wave; gi < P.n_g; gi += NW) {
+        const int pos = P.glob[gi];
+        OT* orow = (OT*)P.out + head_off + (size_t)pos * D;
+        const bool padded = padrow && padrow[pos] != 0;
+        const uint32_t* base = (const uint32_t*)P.part + ((size_t)tk.bh * P.n_split * P.g_pad + gi) * (D + 2);
+        const bool mine = lane < P.n_split;
+        const float m_s = mine ? load_coherent(base + lane * stride) : kNegInf;
+        const float l_s = mine ? load_coherent(base + lane * stride + 1) : 0.f;
+        float M = m_s;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, off));
+        const float w_s = (m_s == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_s - M);
+        float Lsum = l_s * w_s;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) Lsum += __shfl_xor(Lsum, off);
+        float O = 0.f;
+        for (int s0 = 0; s0 < P.n_split; s0 += 16) {
+            float ov[16];
+#pragma unroll
+            for (int j = 0; j < 16; j++) ov[j] = (s0 + j < P.n_split) ? load_coherent(base + (s0 + j) * stride + 2 + lane) : 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; j++) O += ov[j] * __shfl(w_s, s0 + j);
         }
-        y = Lsum > 0.f ? O / Lsum : 0.f;
+        const float y = (padded || !(Lsum > 0.f)) ? 0.f : O / Lsum;
+        if constexpr (sizeof(OT) == 2) {
+            orow[lane] = (OT)(pack_bf16(y, 0.f) & 0xffffu);
+        } else {
+            orow[lane] = y;
+        }
     }
-    if constexpr (sizeof(OT) == 2) {
-        __bf16 yb = (__bf16)y;
-        orow[c] = __builtin_bit_cast(OT, yb);
-    } else {
-        orow[c] = y;
-    }
+    if (tid == 0) __hip_atomic_store(P.counter + tk.bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace lfk
 
 // ---------------------------------------------------------------------------
-// launchers (called from the host library)
-
-namespace lfk {
-
-template <int QB, int KS, typename ET, typename OT>
-static hipError_t launch_tiles(const Params& P, int first_task, int n_tasks, hipStream_t s) {
-    (void)first_task;
-    const int grid = ((n_tasks + 7) / 8) * 8;
-    hipLaunchKernelGGL((tile_kernel<QB, KS, ET, OT>), dim3(grid), dim3(64 * QB * KS), 0, s, P);
-    return hipGetLastError();
-}
-
-}  // namespace lfk
+// launcher (called from the host library)
 
 extern "C" hipError_t lfk_launch(const lfk::Params* P, int dtype_bf16, void* stream) {
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e;
+    constexpr int QB = LFK_QB, KS = LFK_KS;
+    const int grid = ((P->n_tasks + 7) / 8) * 8;
     if (dtype_bf16)
-        e = lfk::launch_tiles<LFK_QB, LFK_KS, __bf16, uint16_t>(*P, 0, P->n_tasks, s);
+        hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, __bf16, uint16_t>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
     else
-        e = lfk::launch_tiles<LFK_QB, LFK_KS, float, float>(*P, 0, P->n_tasks, s);
-    if (e != hipSuccess) return e;
-    if (P->n_g > 0) {
-        const int grid = P->B * P->H * P->n_g;
-        if (dtype_bf16)
-            hipLaunchKernelGGL(lfk::combine_kernel<uint16_t>, dim3(grid), dim3(64), 0, s, *P);
-        else
-            hipLaunchKernelGGL(lfk::combine_kernel<float>, dim3(grid), dim3(64), 0, s, *P);
-        e = hipGetLastError();
-    }
-    return e;
+        hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, float, float>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
+    return hipGetLastError();
 }

@@ -37,6 +37,8 @@ lf_status_t fail(lf_status_t st, const char *fmt, ...) {
 
 long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 
+size_t counter_bytes(int B, int H) { return (((size_t)B * H * sizeof(int)) + 255) / 256 * 256; }
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
     return a0 < b0 + nb && b0 < a0 + na;
@@ -53,7 +55,7 @@ struct Workspace {
 std::mutex g_ws_mu;
 std::map<std::pair<int, void *>, Workspace> g_ws;
 
-lf_status_t workspace(size_t bytes, void *stream, float **out) {
+lf_status_t workspace(size_t bytes, void *stream, char **out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(LF_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -74,9 +76,16 @@ lf_status_t workspace(size_t bytes, void *stream, float **out) {
             (void)hipGetLastError();
             return fail(LF_E_NOMEM, "workspace of %zu bytes: %s", want, hipGetErrorString(e));
         }
+        // the completion counters must start at zero; every call leaves them at zero
+        e = hipMemset(w.ptr, 0, want);
+        if (e != hipSuccess) {
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            return fail(LF_E_HIP, "hipMemset: %s", hipGetErrorString(e));
+        }
         w.bytes = want;
     }
-    *out = (float *)w.ptr;
+    *out = (char *)w.ptr;
     return LF_OK;
 }
 
@@ -154,9 +163,10 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
         P.g_pad = P.n_ggroups * BM;
         int sl = (int)cdiv(cdiv(T, 16), 32) * 32;
         P.split_len = sl < 256 ? 256 : sl;
-        P.n_split = (int)cdiv(T, P.split_len);
+        P.n_split = (int)cdiv(T, P.split_len);  // <= 16: the combine spans splits with one wave's lanes
         n_glob_tasks = (long long)B * H * P.n_split * P.n_ggroups;
-        ws_bytes = (size_t)B * H * P.n_split * P.g_pad * (LF_HEAD_DIM + 2) * sizeof(float);
+        // [B*H completion counters, padded to 256 B][partials]
+        ws_bytes = counter_bytes(B, H) + (size_t)B * H * P.n_split * P.g_pad * (LF_HEAD_DIM + 2) * sizeof(float);
     }
     if (n_band + n_glob_tasks > (1LL << 30))
         return fail(LF_E_UNSUPPORTED, "problem needs %lld workgroups", n_band + n_glob_tasks);
@@ -165,8 +175,11 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
 
     // ---- HIP work
     if (P.n_g > 0) {
-        lf_status_t st = workspace(ws_bytes, stream, &P.part);
+        char *ws = nullptr;
+        lf_status_t st = workspace(ws_bytes, stream, &ws);
         if (st != LF_OK) return st;
+        P.counter = (int *)ws;
+        P.part = (float *)(ws + counter_bytes(B, H));
     }
     hipError_t e = lfk_launch(&P, dtype == LF_BF16, stream);
     if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));

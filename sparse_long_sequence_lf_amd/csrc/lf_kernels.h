@@ -16,6 +16,10 @@
 #ifndef LFK_KS
 #define LFK_KS 2
 #endif
+// Register budget: waves per SIMD the tile kernel is compiled for.
+#ifndef LFK_WAVES_PER_EU
+#define LFK_WAVES_PER_EU 2
+#endif
 
 namespace lfk {
 
@@ -25,6 +29,7 @@ struct Params {
     void *out;
     const uint8_t *pad;      // [B][T] or null
     float *part;             // global-row partials [B*H][n_split][g_pad][66]
+    int *counter;            // [B*H] finished global-row workgroups; zero between calls
     int B, H, T, r;          // r already clamped to T
     int n_g;                 // distinct globals (sorted ascending in glob)
     int g_pad;               // n_ggroups * 32 * LFK_QB
