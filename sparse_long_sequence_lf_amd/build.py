@@ -13,12 +13,14 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblfattn.so")
 SOURCES = [os.path.join(CSRC, "lf_host.cpp"), os.path.join(CSRC, "lf_attn_kernels.hip")]
 
-# gfx950 only; packed fp32 VALU ops are kept out of the generated code, and
+# gfx950 only; packed fp32 VALU ops are kept out of the generated code;
 # MFMA accumulators live in ordinary VGPRs (no AGPR copies around the softmax
-# rescale of O).
+# rescale of O); machine sinking is off so the next stage's K/V loads stay
+# ahead of the current stage's compute instead of being sunk next to their
+# LDS stores (which would serialise load latency and compute).
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-mllvm", "-amdgpu-mfma-vgpr-form",
+             "-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-disable-machine-sink",
              "-Wno-unused-command-line-argument"]
 
 

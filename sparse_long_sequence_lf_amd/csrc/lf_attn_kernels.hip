@@ -181,14 +181,20 @@ __device__ __forceinline__ Task decode_task(const Params& P, int t) {
         k.h = h;
         k.bh = k.b * P.H + h;
         const int delta = P.dil[h];
-        const int q = P.T / delta, rem = P.T - q * delta;
-        const int tb = cdiv(q + 1, BM), ts = cdiv(q, BM);
         int c, tile;
-        if (x < rem * tb) { c = x / tb; tile = x - c * tb; }
-        else { const int y = x - rem * tb; c = rem + y / ts; tile = y - (c - rem) * ts; }
+        if (delta == 1) {
+            c = 0;
+            tile = x;
+            k.n = P.T;
+        } else {
+            const int q = P.T / delta, rem = P.T - q * delta;
+            const int tb = cdiv(q + 1, BM), ts = cdiv(q, BM);
+            if (x < rem * tb) { c = x / tb; tile = x - c * tb; }
+            else { const int y = x - rem * tb; c = rem + y / ts; tile = y - (c - rem) * ts; }
+            k.n = (P.T - c + delta - 1) / delta;
+        }
         k.delta = delta;
         k.c = c;
-        k.n = (P.T - c + delta - 1) / delta;
         k.m0 = tile * BM;
         const int r = P.r;
         int lo_k = k.m0 - r; if (lo_k < 0) lo_k = 0;
@@ -270,12 +276,12 @@ struct WaveState {
     float lp;             // this lane's part of the running sum
 };
 
+// S^T = K Q^T for one block (32 keys x this wave's 32 queries), masked per MODE.
 template <int MODE, int KS, int NP>
-__device__ __forceinline__ void attend_block(WaveState<NP>& W, const char* buf, int blk, int key0, int m,
-                                             int r, int lane) {
+__device__ __forceinline__ f32x16 block_scores(const WaveState<NP>& W, const char* buf, int blk, int key0,
+                                               uint32_t bad, int m, int r, int lane) {
     using SG = Stage<KS, NP>;
     const int lq = lane & 31, lg = lane >> 5;
-    // S^T = K Q^T for this block: 32 keys x 32 queries
     f32x16 s = {};
     const char* kb = buf + SG::kOff(0, blk);
 #pragma unroll
@@ -289,27 +295,48 @@ __device__ __forceinline__ void attend_block(WaveState<NP>& W, const char* buf, 
         }
     }
     if constexpr (MODE != kInterior) {
-        const uint32_t bad = *(const uint32_t*)(buf + SG::maskOff + blk * 4);
         const int* gcls = (const int*)(buf + SG::gclsOff) + blk * KBLK;
+        // this lane's 16 keys are rows 8*(i>>2) + 4*lg + (i&3): shift the mask
+        // word so that bit i of `badl` belongs to accumulator element i
+        const uint32_t sh = bad >> (4 * lg);
+        const uint32_t badl = (sh & 0xfu) | ((sh >> 4) & 0xf0u) | ((sh >> 8) & 0xf00u) | ((sh >> 12) & 0xf000u);
+        int gc[16];
+        if constexpr (MODE == kGlobalKeys) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++) {
+                const u32x4 g4 = *(const u32x4*)(gcls + 8 * q4 + 4 * lg);
+                gc[4 * q4 + 0] = (int)g4[0]; gc[4 * q4 + 1] = (int)g4[1];
+                gc[4 * q4 + 2] = (int)g4[2]; gc[4 * q4 + 3] = (int)g4[3];
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const int kl = 8 * (i >> 2) + 4 * lg + (i & 3);   // key row inside the block
-            bool ok = ((bad >> kl) & 1u) == 0u;
+            bool ok = ((badl >> i) & 1u) == 0u;
             if constexpr (MODE == kBandEdge) {
                 const int dk = key0 + kl - m;
-                ok = ok && (uint32_t)(dk + r) <= (uint32_t)(2 * r);
+                ok &= (uint32_t)(dk + r) <= (uint32_t)(2 * r);
             } else if constexpr (MODE == kGlobalKeys) {
-                const int dk = gcls[kl] - m;
-                ok = ok && (uint32_t)(dk + r) > (uint32_t)(2 * r);   // not already in the window
+                const int dk = gc[i] - m;
+                ok &= (uint32_t)(dk + r) > (uint32_t)(2 * r);   // not already in the window
             }
             s[i] = ok ? s[i] : kNegInf;
         }
     }
-    // running max: raw-score max of the block, scaled; O is rescaled only when
-    // the max grows by more than 2^8 (then every later p stays <= 2^8)
-    float mx = s[0];
+    return s;
+}
+
+// Running max/sum update for the scores of NB blocks at once: the raw-score
+// max is taken to base 2 with the 1/sqrt(d) scale, and O is rescaled only when
+// the max grows by more than 2^8 (so every exponent stays <= 8 and the final
+// O / l is unaffected).
+template <int NB, int NP>
+__device__ __forceinline__ void update_max(WaveState<NP>& W, const f32x16 (&s)[NB]) {
+    float mx = s[0][0];
 #pragma unroll
-    for (int i = 1; i < 16; i++) mx = __builtin_fmaxf(mx, s[i]);
+    for (int b = 0; b < NB; b++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) mx = __builtin_fmaxf(mx, s[b][i]);
     mx = halves_max(mx);
     const float mxs = mx * kScaleLog2;
     const bool need = mxs > W.ms + 8.0f;
@@ -321,6 +348,12 @@ __device__ __forceinline__ void attend_block(WaveState<NP>& W, const char* buf, 
         W.lp *= alpha;
         W.ms = msn;
     }
+}
+
+// p = 2^(s*scale - m) for one block, its row-sum, and O^T += V^T P^T
+template <int KS, int NP>
+__device__ __forceinline__ void block_pv(WaveState<NP>& W, const f32x16& s, const char* buf, int blk, int lane) {
+    using SG = Stage<KS, NP>;
     const float nms = (W.ms == kNegInf) ? 0.0f : -W.ms;
     float p[16];
 #pragma unroll
@@ -348,8 +381,8 @@ __device__ __forceinline__ void attend_block(WaveState<NP>& W, const char* buf, 
         pb[st] = as_bf16x8(w);
         if constexpr (NP == 2) pbl[st] = as_bf16x8(wl);
     }
-    // O^T += V^T P^T; V^T operands by transposing reads: lane (16G + L) supplies
-    // row 16st + 8hf + 4(G>>1) + (L>>2), channels 32cb + 16(G&1) + 4(L&3)
+    // V^T operands by transposing reads: lane (16G + L) supplies row
+    // 16st + 8hf + 4(G>>1) + (L>>2), channels 32cb + 16(G&1) + 4(L&3)
     const int G = lane >> 4, L = lane & 15;
     const int t0 = 4 * (G >> 1) + (L >> 2);
 #pragma unroll
@@ -373,20 +406,109 @@ __device__ __forceinline__ void attend_block(WaveState<NP>& W, const char* buf, 
     }
 }
 
+// One block: `bad` has bit t set when key row t of the block is not a real key.
+template <int MODE, int KS, int NP>
+__device__ __forceinline__ void attend_block(WaveState<NP>& W, const char* buf, int blk, int key0, uint32_t bad,
+                                             int m, int r, int lane) {
+    f32x16 s[1] = {block_scores<MODE, KS, NP>(W, buf, blk, key0, bad, m, r, lane)};
+    update_max<1, NP>(W, s);
+    block_pv<KS, NP>(W, s[0], buf, blk, lane);
+}
+
+// two blocks with one max update: the second block's score MFMAs are issued
+// before the first block's softmax, so they overlap its VALU work
+template <int MODE0, int MODE1, int KS, int NP>
+__device__ __forceinline__ void attend_pair(WaveState<NP>& W, const char* buf, int blk0, int key0, uint32_t bad0,
+                                            int blk1, int key1, uint32_t bad1, int m, int r, int lane) {
+    f32x16 s[2];
+    s[0] = block_scores<MODE0, KS, NP>(W, buf, blk0, key0, bad0, m, r, lane);
+    s[1] = block_scores<MODE1, KS, NP>(W, buf, blk1, key1, bad1, m, r, lane);
+    update_max<2, NP>(W, s);
+    block_pv<KS, NP>(W, s[0], buf, blk0, lane);
+    block_pv<KS, NP>(W, s[1], buf, blk1, lane);
+}
+
+// Masking chosen at run time (wave-uniform), so one code path serves every
+// block kind and O stays in one set of registers.
+enum MaskKind { kMaskNone = 0, kMaskBand = 1, kMaskGlobal = 2, kMaskBad = 3 };
+
+__device__ __forceinline__ void apply_mask(f32x16& s, int kind, uint32_t bad, int key0, const int* gcls,
+                                           int m, int r, int lg) {
+    if (kind == kMaskNone) return;
+    const uint32_t sh = bad >> (4 * lg);
+    const uint32_t badl = (sh & 0xfu) | ((sh >> 4) & 0xf0u) | ((sh >> 8) & 0xf00u) | ((sh >> 12) & 0xf000u);
+    if (kind == kMaskBand) {
+        // keys key0 + kl with kl = 8*(i>>2) + 4*lg + (i&3) must lie in [m - r, m + r]
+        const int lo = m - r - key0 - 4 * lg, hi = m + r - key0 - 4 * lg;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int kc = 8 * (i >> 2) + (i & 3);
+            const bool ok = ((badl >> i) & 1u) == 0u && kc >= lo && kc <= hi;
+            s[i] = ok ? s[i] : kNegInf;
+        }
+    } else if (kind == kMaskGlobal) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+            const u32x4 g4 = *(const u32x4*)(gcls + 8 * q4 + 4 * lg);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int i = 4 * q4 + e;
+                const int dk = (int)g4[e] - m;
+                const bool ok = ((badl >> i) & 1u) == 0u && (uint32_t)(dk + r) > (uint32_t)(2 * r);
+                s[i] = ok ? s[i] : kNegInf;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; i++) s[i] = ((badl >> i) & 1u) ? kNegInf : s[i];
+    }
+}
+
+// Up to two blocks of one stage for one wave.  live0/live1 say whether each
+// block has work for this wave (a dead block costs no MFMA and adds nothing).
+template <int KS, int NP>
+__device__ __forceinline__ void attend_stage(WaveState<NP>& W, const char* buf, int blk0, bool live0, int kind0,
+                                             uint32_t bad0, int key0, bool live1, int kind1, uint32_t bad1,
+                                             int key1, int m, int r, int lane) {
+    using SG = Stage<KS, NP>;
+    const int lg = lane >> 5;
+    const int* gcls = (const int*)(buf + SG::gclsOff);
+    f32x16 s[2];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const bool live = u ? live1 : live0;
+        if (live) {
+            s[u] = block_scores<kInterior, KS, NP>(W, buf, blk0 + u, 0, 0u, m, r, lane);
+            apply_mask(s[u], u ? kind1 : kind0, u ? bad1 : bad0, u ? key1 : key0, gcls + (blk0 + u) * KBLK,
+                       m, r, lg);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; i++) s[u][i] = kNegInf;
+        }
+    }
+    update_max<2, NP>(W, s);
+    if (live0) block_pv<KS, NP>(W, s[0], buf, blk0, lane);
+    if (live1) block_pv<KS, NP>(W, s[1], buf, blk0 + 1, lane);
+}
+
 // ---------------------------------------------------------------------------
 // The tile kernel.
 
 template <int QB, int KS, typename ET, typename OT>
-__global__ __launch_bounds__(64 * QB * KS) __attribute__((amdgpu_waves_per_eu(LFK_WAVES_PER_EU))) void tile_kernel(const Params P) {
+__global__ __launch_bounds__(64 * QB * KS) __attribute__((amdgpu_waves_per_eu(LFK_WAVES_PER_EU)))
+void tile_kernel(const Params P) {
     constexpr int NT = 64 * QB * KS;
     constexpr int NP = Elem<ET>::NP;
-    using SG = Stage<KS, NP>;
-    constexpr int R = KS * KBLK;               // key rows per stage
+    constexpr int NBW = NP == 1 ? 2 : 1;       // blocks per wave per stage (processed as a pair)
+    constexpr int NBLK = KS * NBW;             // blocks per stage
+    static_assert(NBLK <= QB * KS, "one mask wave per block");
+    using SG = Stage<NBLK, NP>;
+    constexpr int R = NBLK * KBLK;             // key rows per stage
     constexpr int CHUNKS = R * 8;              // 8-channel chunks per tensor per stage
     static_assert(CHUNKS % NT == 0, "stage chunks must divide evenly over the workgroup");
     constexpr int CPT = CHUNKS / NT;           // chunks per thread per tensor
     constexpr int MERGE_BYTES = (KS - 1) * QB * 64 * 36 * 4;
-    constexpr int SMEM = (2 * SG::bytes > MERGE_BYTES) ? 2 * SG::bytes : MERGE_BYTES;
+    constexpr int SMEM = (SG::bytes > MERGE_BYTES) ? SG::bytes : MERGE_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     // ---- which task (XCD-aware: each of the 8 dies takes a contiguous task range)
@@ -463,137 +585,217 @@ __global__ __launch_bounds__(64 * QB * KS) __attribute__((amdgpu_waves_per_eu(LF
 
     // ---- stage plan: band (or dense) stages, then global-key stages
     const int ngb = tk.kind == 0 ? cdiv(P.n_g, KBLK) : 0;
-    const int NSb = cdiv(tk.nband, KS);
-    const int NS = NSb + cdiv(ngb, KS);
+    const int NSb = cdiv(tk.nband, NBLK);
+    const int NS = NSb + cdiv(ngb, NBLK);
+    // LDS mask words are only needed where the key range alone does not say
+    // which rows are real: with padding, and for the global-key stages
+    const bool lds_mask_band = padrow != nullptr;
 
-    // loader geometry: chunk j of this thread is row (tid >> 3) + j * NT/8, channels 8*(tid & 7)..+7
+    // loader geometry: chunk j of this thread is stage row lrow0 + j * NT/8,
+    // channels 8*lch .. 8*lch+7; band rows advance by R keys per stage
     const int lch = tid & 7;
     const int lrow0 = tid >> 3;
     const int key_base = tk.kb_lo * KBLK;
+    const int rowstep = tk.delta * D;                 // elements between consecutive class keys
 
     struct Regs {
         u32x4 k[CPT][NP];
         u32x4 v[CPT][NP];
-        bool ok[CPT];
-        uint32_t mword;   // mask lanes: this lane's row validity is folded in at commit
-        bool mvalid;
+        uint32_t inr;         // bit j: chunk j's row is a real position
+        bool full;            // every row of the stage is a real, unpadded key
+        uint8_t padb[CPT];    // that position's padding byte (0 without padding)
+        bool minr;            // mask lanes: row is a real position
+        uint8_t mpad;         // ... and its padding byte
         int gcls;
     };
 
-    // position of stage row `row` of stage `st` (and whether it is a real key)
-    auto row_pos = [&](int st, int row, int& pos, bool& inr) {
-        if (st < NSb) {
-            const int kk = key_base + st * R + row;
-            inr = kk < tk.key_end;
-            pos = inr ? tk.c + tk.delta * kk : 0;
-        } else {
-            const int slot = (st - NSb) * R + row;
-            inr = slot < P.n_g;
-            pos = inr ? P.glob[slot] : 0;
-        }
-    };
-
+    // Loads are issued unconditionally from clamped (always valid) addresses;
+    // whether a row is real or padded is only applied when the registers are
+    // written to LDS, so no branch waits on these loads before the compute.
+    // Order inside a stage load: every position lookup and every small load
+    // (padding bytes, global classes) first, the K/V loads last.  Nothing is
+    // then written after the K/V loads into a register an earlier load could
+    // still own, so the compiler places no wait on them before the compute.
     auto issue = [&](int st, Regs& Rg) {
+        const bool band = st < NSb;
+        const bool masklane = (!band || lds_mask_band) && wave < NBLK;
+        int pos[CPT];
+        int mpos = 0;
+        bool minr = false;
+        Rg.inr = 0;
+        Rg.full = band && !padrow && key_base + (st + 1) * R <= tk.key_end;
+        if (band) {
+#pragma unroll
+            for (int j = 0; j < CPT; j++) {
+                const int kk = key_base + st * R + lrow0 + j * (NT / 8);
+                const bool inr = kk < tk.key_end;
+                pos[j] = inr ? tk.c + tk.delta * kk : 0;
+                Rg.inr |= (uint32_t)inr << j;
+            }
+            if (masklane) {
+                const int kk = key_base + st * R + 32 * wave + lq;
+                minr = kk < tk.key_end;
+                mpos = minr ? tk.c + tk.delta * kk : 0;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < CPT; j++) {
+                const int slot = (st - NSb) * R + lrow0 + j * (NT / 8);
+                const bool inr = slot < P.n_g;
+                pos[j] = P.glob[inr ? slot : 0];
+                Rg.inr |= (uint32_t)inr << j;
+            }
+            if (masklane) {
+                const int slot = (st - NSb) * R + 32 * wave + lq;
+                minr = slot < P.n_g;
+                mpos = P.glob[minr ? slot : 0];
+            }
+        }
+        if (masklane) {
+            Rg.minr = minr && lg == 0;
+            Rg.mpad = padrow ? padrow[mpos] : (uint8_t)0;
+            const int dpos = mpos - tk.c;
+            const int q = dpos / tk.delta;
+            Rg.gcls = (!band && minr && dpos >= 0 && q * tk.delta == dpos) ? q : kNotInClass;
+        }
+        if (padrow) {
+#pragma unroll
+            for (int j = 0; j < CPT; j++) Rg.padb[j] = padrow[pos[j]];
+        }
 #pragma unroll
         for (int j = 0; j < CPT; j++) {
-            int pos; bool inr;
-            row_pos(st, lrow0 + j * (NT / 8), pos, inr);
-            const size_t off = (size_t)pos * D + lch * 8;
+            const size_t off = (size_t)pos[j] * D + lch * 8;
 #pragma unroll
             for (int p = 0; p < NP; p++) {
                 Rg.k[j][p] = *(const u32x4*)(Kg + off + 4 * p);
                 Rg.v[j][p] = *(const u32x4*)(Vg + off + 4 * p);
             }
-            bool ok = inr;
-            if (padrow) ok = ok && padrow[pos] == 0;
-            Rg.ok[j] = ok;
-        }
-        // mask lanes: waves 0..KS-1, lanes 0..31 own stage row 32*wave + lane
-        if (wave < KS) {
-            int pos; bool inr;
-            row_pos(st, 32 * wave + lq, pos, inr);
-            bool ok = inr && lg == 0;
-            if (padrow) ok = ok && padrow[pos] == 0;
-            Rg.mvalid = ok;
-            Rg.gcls = kNotInClass;
-            if (st >= NSb && inr) {
-                const int dpos = pos - tk.c;
-                if (dpos >= 0 && dpos % tk.delta == 0) Rg.gcls = dpos / tk.delta;
-            }
         }
     };
 
-    auto commit = [&](const Regs& Rg, char* buf) {
+    auto commit = [&](int st, const Regs& Rg) {
         const u32x4 z = {0, 0, 0, 0};
+        char* buf = smem;
 #pragma unroll
         for (int j = 0; j < CPT; j++) {
             const int row = lrow0 + j * (NT / 8);
             const int blk = row >> 5, t = row & 31;
+            const bool ok = Rg.full || (((Rg.inr >> j) & 1u) != 0u && (!padrow || Rg.padb[j] == 0));
             if constexpr (NP == 1) {
-                *(u32x4*)(buf + SG::kOff(0, blk) + swzK(t, lch)) = Rg.ok[j] ? Rg.k[j][0] : z;
-                *(u32x4*)(buf + SG::vOff(0, blk) + swzV(t, lch)) = Rg.ok[j] ? Rg.v[j][0] : z;
+                *(u32x4*)(buf + SG::kOff(0, blk) + swzK(t, lch)) = ok ? Rg.k[j][0] : z;
+                *(u32x4*)(buf + SG::vOff(0, blk) + swzV(t, lch)) = ok ? Rg.v[j][0] : z;
             } else {
-                u32x4 kh = z, kl = z, vh = z, vl = z;
-                if (Rg.ok[j]) {
-                    split8(Raw32{Rg.k[j][0], Rg.k[j][1]}, kh, kl);
-                    split8(Raw32{Rg.v[j][0], Rg.v[j][1]}, vh, vl);
-                }
-                *(u32x4*)(buf + SG::kOff(0, blk) + swzK(t, lch)) = kh;
-                *(u32x4*)(buf + SG::kOff(1, blk) + swzK(t, lch)) = kl;
-                *(u32x4*)(buf + SG::vOff(0, blk) + swzV(t, lch)) = vh;
-                *(u32x4*)(buf + SG::vOff(1, blk) + swzV(t, lch)) = vl;
+                u32x4 kh, kl, vh, vl;
+                split8(Raw32{Rg.k[j][0], Rg.k[j][1]}, kh, kl);
+                split8(Raw32{Rg.v[j][0], Rg.v[j][1]}, vh, vl);
+                *(u32x4*)(buf + SG::kOff(0, blk) + swzK(t, lch)) = ok ? kh : z;
+                *(u32x4*)(buf + SG::kOff(1, blk) + swzK(t, lch)) = ok ? kl : z;
+                *(u32x4*)(buf + SG::vOff(0, blk) + swzV(t, lch)) = ok ? vh : z;
+                *(u32x4*)(buf + SG::vOff(1, blk) + swzV(t, lch)) = ok ? vl : z;
             }
         }
-        if (wave < KS) {
-            const uint32_t good = (uint32_t)__ballot(Rg.mvalid);   // lanes 0..31 only
+        if ((st >= NSb || lds_mask_band) && wave < NBLK) {
+            const uint32_t good = (uint32_t)__ballot(Rg.minr && Rg.mpad == 0);   // lanes 0..31 only
             if (lane == 0) *(uint32_t*)(buf + SG::maskOff + wave * 4) = ~good;
             if (lg == 0) ((int*)(buf + SG::gclsOff))[wave * KBLK + lq] = Rg.gcls;
         }
     };
 
-    // ---- main loop over stages, double-buffered through LDS
-    char* const buf0 = smem;
-    char* const buf1 = smem + SG::bytes;
+    // mask word of stage block `blk`: from LDS, or from the key range alone
+    auto block_bad = [&](int st, int blk) -> uint32_t {
+        if (st >= NSb || lds_mask_band) return *(const uint32_t*)(smem + SG::maskOff + blk * 4);
+        const int key0 = key_base + st * R + blk * KBLK;
+        const int valid = tk.key_end - key0;
+        return valid >= KBLK ? 0u : (valid <= 0 ? 0xffffffffu : (0xffffffffu << valid));
+    };
+
+    // ---- main loop: prefetch stage st+1 into registers while stage st is in LDS
     {
         Regs Rg;
         issue(0, Rg);
-        commit(Rg, buf0);
+        commit(0, Rg);
         __syncthreads();
     }
     const int m_me = mq0 + lq;         // this lane's query (class index / global slot)
-    for (int st = 0; st < NS; st++) {
-        Regs Rg;
-        const bool more = st + 1 < NS;
-        if (more) issue(st + 1, Rg);
-        const char* cur = (st & 1) ? buf1 : buf0;
-        if (wave_active) {
+    // which of this wave's blocks of stage st have work, and how to mask them
+    struct StagePlan {
+        bool live[NBW];
+        int kind[NBW], key0[NBW];
+        uint32_t bad[NBW];
+    };
+    const int b0 = ph * NBW;           // this wave's blocks: NBW consecutive blocks of phase ph
+    auto plan = [&](int st) {
+        StagePlan sp;
+#pragma unroll
+        for (int u = 0; u < NBW; u++) {
+            sp.bad[u] = block_bad(st, b0 + u);
             if (st < NSb) {
-                const int jb = st * KS + ph;
-                if (jb < tk.nband) {
-                    const uint32_t bad = *(const uint32_t*)(cur + SG::maskOff + ph * 4);
-                    const int kb = tk.kb_lo + jb;
-                    const int key0 = kb * KBLK;
-                    if (bad != 0xffffffffu) {
-                        if (tk.kind == 1) {
-                            attend_block<kDense, KS, NP>(W, cur, ph, key0, m_me, r, lane);
-                        } else if (kb >= wb_lo && kb <= wb_hi) {
-                            const bool interior = bad == 0u && key0 >= mq0 + 31 - r && key0 + 31 <= mq0 + r;
-                            if (interior) attend_block<kInterior, KS, NP>(W, cur, ph, key0, m_me, r, lane);
-                            else attend_block<kBandEdge, KS, NP>(W, cur, ph, key0, m_me, r, lane);
-                        }
-                    }
-                }
+                const int jb = st * NBLK + b0 + u;
+                const int kb = tk.kb_lo + jb;
+                sp.key0[u] = kb * KBLK;
+                sp.live[u] = wave_active && jb < tk.nband && sp.bad[u] != 0xffffffffu &&
+                             (tk.kind == 1 || (kb >= wb_lo && kb <= wb_hi));
+                const bool interior = tk.kind == 0 && sp.bad[u] == 0u && sp.key0[u] >= mq0 + 31 - r &&
+                                      sp.key0[u] + 31 <= mq0 + r;
+                sp.kind[u] = tk.kind == 1 ? kMaskBad : (interior ? kMaskNone : kMaskBand);
             } else {
-                const int jg = (st - NSb) * KS + ph;
-                if (jg < ngb) {
-                    const uint32_t bad = *(const uint32_t*)(cur + SG::maskOff + ph * 4);
-                    if (bad != 0xffffffffu) attend_block<kGlobalKeys, KS, NP>(W, cur, ph, 0, m_me, r, lane);
-                }
+                const int jg = (st - NSb) * NBLK + b0 + u;
+                sp.key0[u] = 0;
+                sp.live[u] = wave_active && jg < ngb && sp.bad[u] != 0xffffffffu;
+                sp.kind[u] = kMaskGlobal;
             }
         }
-        if (more) commit(Rg, (st & 1) ? buf0 : buf1);
-        __syncthreads();
+        return sp;
+    };
+    // the score MFMAs of the stage's blocks
+    auto scores = [&](const StagePlan& sp, f32x16 (&sc)[NBW]) {
+#pragma unroll
+        for (int u = 0; u < NBW; u++)
+            if (sp.live[u]) sc[u] = block_scores<kInterior, NBLK, NP>(W, smem, b0 + u, 0, 0u, m_me, r, lane);
+    };
+    // masking, running max/sum and O += P V
+    auto finish = [&](const StagePlan& sp, f32x16 (&sc)[NBW]) {
+        bool any = false;
+#pragma unroll
+        for (int u = 0; u < NBW; u++) any = any || sp.live[u];
+        if (!any) return;
+        const int* gcls = (const int*)(smem + SG::gclsOff);
+#pragma unroll
+        for (int u = 0; u < NBW; u++) {
+            if (sp.live[u]) {
+                apply_mask(sc[u], sp.kind[u], sp.bad[u], sp.key0[u], gcls + (b0 + u) * KBLK, m_me, r, lg);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; i++) sc[u][i] = kNegInf;
+            }
+        }
+        update_max<NBW, NP>(W, sc);
+#pragma unroll
+        for (int u = 0; u < NBW; u++)
+            if (sp.live[u]) block_pv<NBLK, NP>(W, sc[u], smem, b0 + u, lane);
+    };
+
+    // Every stage but the last: score MFMAs, then the next stage's loads (they
+    // queue while the matrix cores run), then the softmax and PV, then the LDS
+    // hand-over.  Straight-line code, so the loads stay where they are.
+    for (int st = 0; st + 1 < NS; st++) {
+        const StagePlan sp = plan(st);
+        f32x16 sc[NBW];
+        scores(sp, sc);
+        Regs Rg;
+        issue(st + 1, Rg);
+        finish(sp, sc);
+        __syncthreads();               // every wave is done reading stage st
+        commit(st + 1, Rg);
+        __syncthreads();               // stage st+1 is in LDS
     }
+    {
+        const StagePlan sp = plan(NS - 1);
+        f32x16 sc[NBW];
+        scores(sp, sc);
+        finish(sp, sc);
+    }
+    __syncthreads();
 
     // ---- merge the KS phases of each query block (LDS); phase 0 keeps the result
     if constexpr (KS > 1) {
