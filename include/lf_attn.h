@@ -52,7 +52,7 @@ typedef enum {
 #define LF_HEAD_DIM 64        /* d must equal this */
 #define LF_MAX_HEADS 128      /* H */
 #define LF_MAX_GLOBALS 512    /* distinct global positions */
-#define LF_MAX_SEQ (1 << 24)  /* T */
+#define LF_MAX_SEQ ((1 << 24) - 1)  /* T: one head of fp32 K or V stays below 4 GiB */
 #define LF_MAX_DILATION 65535 /* delta */
 
 /*

@@ -11,8 +11,8 @@
 //    inside the window is counted once);
 //  * global-row tasks: up to 32*QB global queries of head (b, h) against
 //    one contiguous split of all T keys ("Global Attention": a global token
-//    reads every position), written as partial (max, sum, weighted-sum)
-//    triples that the combine kernel rescales and adds.
+//    reads every position).  Each writes partial (max, sum, weighted-sum)
+//    triples; the last split of a head to finish rescales and adds them.
 //
 // Residue classes: with stride delta the positions c, c+delta, c+2*delta,
 // ... form an undilated sequence of length n_c = ceil((T-c)/delta) on which
@@ -23,22 +23,25 @@
 // Per wave: 32 queries.  S^T = K Q^T and O^T = V^T P^T are computed with
 // v_mfma_f32_32x32x16_bf16, so every lane owns one query (column) in both
 // accumulators and the softmax needs only one cross-lane exchange (lanes l
-// and l^32 hold the two halves of a query's keys).  K reaches the MFMA A
-// operand by ds_read_b128 from a swizzled LDS tile; V reaches it through
-// ds_read_b64_tr_b16 (transposing LDS read).  The softmax is the running
-// max/sum form (blockwise accumulation, "Longformer长序列处理", 显存优化技巧)
-// kept in base 2 with the 1/sqrt(d) scale folded into one FMA; the running
-// max is only moved (and O rescaled) when a block raises it by more than
-// 2^8, which keeps every exponent <= 8 and leaves the final O/l exact.
+// and l^32 hold the two halves of a query's keys).  The softmax is the
+// running max/sum form (blockwise accumulation, "Longformer长序列处理",
+// 显存优化技巧) kept in base 2 with the 1/sqrt(d) scale folded into one FMA;
+// the running max only moves (and O is rescaled) when a block raises it by
+// more than 2^8, which keeps every exponent <= 8 and leaves O / l exact.
 //
-// KS waves share each query block: the key blocks of a tile are dealt out
-// round-robin to KS "phases", and the KS partial states are merged in LDS
-// at the end.  This gives the chip 4 waves per 64 queries instead of 2.
+// Key blocks (32 keys) reach LDS straight from memory (buffer_load ... lds,
+// no register staging) through a ring of three stages of two blocks each.
+// Step s of the loop: one barrier (stage s+1 has landed, stage s-1 is free),
+// the loads of stage s+2 go out, the score MFMAs of this wave's block of
+// stage s+1 are issued, and the softmax and PV of its block of stage s run
+// while they execute.  Rows past the end of the head read as zero.  The two
+// "phases" of a query block take the two blocks of each stage and are
+// merged at the end.
 //
-// fp32 inputs are split into bf16 hi + lo parts when staged; each product
-// uses hi*hi + hi*lo + lo*hi (three MFMAs), which keeps the score and output
-// error near 2^-16 relative while the tiling, masking and softmax code is
-// the very code the bf16 path runs.
+// fp32 inputs: a pre-pass splits K and V into bf16 hi + lo planes and Q is
+// split when loaded; each product uses hi*hi + hi*lo + lo*hi (three MFMAs),
+// which keeps the score and output error near 2^-16 relative while the
+// tiling, masking and softmax code is the very code the bf16 path runs.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -48,61 +51,56 @@
 namespace lfk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
 constexpr int D = 64;
 constexpr int KBLK = 32;                  // keys per block (one S^T tile)
-constexpr int BLK_BYTES = KBLK * D * 2;   // one bf16 plane of a block: 4 KiB
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kNotInClass = -(1 << 30);
+constexpr int kRawBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format, no swizzle
 
 // log2(e) / sqrt(64): scores are taken to base 2 with the 1/sqrt(d) scale.
 constexpr float kScaleLog2 = 0.18033688011112042f;
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
-
 // ---------------------------------------------------------------------------
-// LDS tile geometry.  A stage holds KS blocks of 32 keys; per block and
-// plane, K and V are 32 rows x 128 B.  NP = 1 (bf16) or 2 (fp32: hi, lo).
-template <int KS, int NP>
-struct Stage {
-    static constexpr int kOff(int p, int blk) { return (p * KS + blk) * BLK_BYTES; }
-    static constexpr int vOff(int p, int blk) { return (NP * KS + p * KS + blk) * BLK_BYTES; }
-    static constexpr int maskOff = 2 * NP * KS * BLK_BYTES;            // KS x 4 bytes
-    static constexpr int gclsOff = maskOff + ((KS * 4 + 15) / 16) * 16;  // KS x 32 int32
-    static constexpr int bytes = gclsOff + KS * KBLK * 4;
+// LDS layout.  A block holds, per bf16 plane (NP = 1 for bf16, 2 for the
+// hi/lo planes of fp32), 32 K rows then 32 V rows:
+//
+//   K: byte ks*1024 + row*32 + hs*16 holds channels 16ks + 8h .. +7 with
+//      hs = h ^ ((row >> 3) & 1).  The 16 lanes of one ds_read_b128 (rows
+//      t..t+15, one h) then touch 16 distinct 4-bank groups.
+//   V: byte 4096 + cb*2048 + row*64 + 16j holds channels 32cb + 8j .. +7.
+//      Half a wave of ds_read_b64_tr_b16 reads rows t..t+3 x 64 B: 256
+//      consecutive bytes, all 64 banks once.
+//
+// Each 1 KiB piece (a K slice, or 16 V rows of one cb) is what one
+// buffer_load_dwordx4 ... lds of 64 lanes writes, lane p at byte 16p.
+template <int NP>
+struct Ring {
+    static constexpr int PLANE = 8192;
+    static constexpr int BLK = NP * PLANE;
+    static constexpr int STAGE = 2 * BLK;                       // two blocks: one per phase
+    static constexpr int NBUF = 3;
+    static constexpr int maskOff = NBUF * STAGE;                // [NBUF][2] mask words
+    static constexpr int gposOff = maskOff + 32;                // global positions
+    static constexpr int gclsOff = gposOff + 4 * LF_MAX_GLOBALS; // their class index, or kNotInClass
+    static constexpr int gbadOff = gclsOff + 4 * LF_MAX_GLOBALS; // per global block: missing / padded slots
+    static constexpr int bytes = gbadOff + 4 * (LF_MAX_GLOBALS / 32);
 };
-
-// K rows: 16-byte chunk ch of row t lives at chunk ch ^ ((t >> 1) & 7), so
-// the 16 lanes that read one chunk column of 16 consecutive rows hit 16
-// different bank groups.
-__device__ __forceinline__ int swzK(int t, int ch) { return t * 128 + ((ch ^ ((t >> 1) & 7)) << 4); }
-// V rows: chunk ch of row t lives at ch ^ (4 * ((t >> 1) & 1)); a transposing
-// read touches 8 rows x 64 B and this spreads them over all 64 banks.
-__device__ __forceinline__ int swzV(int t, int ch) { return t * 128 + ((ch ^ (((t >> 1) & 1) << 2)) << 4); }
-
-// ---------------------------------------------------------------------------
-// element-type traits
 
 template <typename T> struct Elem;
-template <> struct Elem<__bf16> {
-    static constexpr int NP = 1;
-    static constexpr int CHUNK_BYTES = 16;  // 8 channels
-};
-template <> struct Elem<float> {
-    static constexpr int NP = 2;
-    static constexpr int CHUNK_BYTES = 32;
-};
+template <> struct Elem<__bf16> { static constexpr int NP = 1; };
+template <> struct Elem<float> { static constexpr int NP = 2; };
 
-struct Raw16 { u32x4 a; };
 struct Raw32 { u32x4 a, b; };
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // two floats -> two bf16 (round to nearest even) in one dword; one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -133,16 +131,32 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ i16x4 ds_tr16(const char* lds_ptr) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(lds_ptr));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lds_ptr));
 }
 
 __device__ __forceinline__ bf16x8 cat_tr(i16x4 a, i16x4 b) {
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    i16x8 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-    return __builtin_bit_cast(bf16x8, r);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// raw buffer over [base, base + bytes): accesses at offsets >= bytes read zero
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+
+// 16 bytes per lane from rsrc at voff + soff into LDS at dst + 16 * lane
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(dst), 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Barrier after which every wave's loads into LDS have landed.  A plain
+// __syncthreads() waits only for LDS instructions (lgkmcnt), not for
+// buffer_load ... lds, which counts on vmcnt: each wave first waits for its
+// own (s_waitcnt vmcnt(0): gfx9 encoding, expcnt and lgkmcnt left open).
+__device__ __forceinline__ void barrier_lds_loads() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -170,14 +184,20 @@ __device__ __forceinline__ Task decode_task(const Params& P, int t) {
         k.kind = 0;
         k.b = t / P.band_tasks_per_batch;
         int x = t - k.b * P.band_tasks_per_batch;
-        // heads are few (<= LF_MAX_HEADS): binary search on the band-task prefix
-        int lo = 0, hi = P.H - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (P.head_start[mid] <= x) lo = mid; else hi = mid - 1;
+        int h;
+        if (P.uniform_head_tasks > 0) {
+            h = x / P.uniform_head_tasks;
+            x -= h * P.uniform_head_tasks;
+        } else {
+            // heads are few (<= LF_MAX_HEADS): binary search on the band-task prefix
+            int lo = 0, hi = P.H - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (P.head_start[mid] <= x) lo = mid; else hi = mid - 1;
+            }
+            h = lo;
+            x -= P.head_start[h];
         }
-        const int h = lo;
-        x -= P.head_start[h];
         k.h = h;
         k.bh = k.b * P.H + h;
         const int delta = P.dil[h];
@@ -226,20 +246,8 @@ __device__ __forceinline__ Task decode_task(const Params& P, int t) {
     return k;
 }
 
-// is position pos one of the (sorted) global positions?
-__device__ __forceinline__ bool is_global(const Params& P, int pos) {
-    int lo = 0, hi = P.n_g - 1;
-    while (lo <= hi) {
-        const int mid = (lo + hi) >> 1;
-        const int g = P.glob[mid];
-        if (g == pos) return true;
-        if (g < pos) lo = mid + 1; else hi = mid - 1;
-    }
-    return false;
-}
-
-// max over the two 32-lane halves (lanes l and l^32 hold the two key halves of
-// a query): one v_permlane32_swap, no LDS round trip
+// reductions over the two 32-lane halves (lanes l and l^32 hold the two key
+// halves of a query): one v_permlane32_swap, no LDS round trip
 __device__ __forceinline__ float halves_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
                                                     __builtin_bit_cast(uint32_t, x), false, false);
@@ -261,10 +269,6 @@ __device__ __forceinline__ float load_coherent(const uint32_t* p) {
     return __builtin_bit_cast(float, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-// Block masks.  Bit t of a block's mask word is set when key row t of the
-// block is not a real key (beyond the sequence/class/split, or padded).
-enum BlockMode { kInterior = 0, kBandEdge = 1, kGlobalKeys = 2, kDense = 3 };
-
 // ---------------------------------------------------------------------------
 // Per-wave attention state and the work on one 32-key block.
 
@@ -274,167 +278,52 @@ struct WaveState {
     f32x16 o0, o1;        // O^T: channels 0..31 and 32..63 of this lane's query
     float ms;             // running max in scaled base-2 units
     float lp;             // this lane's part of the running sum
+    int kbase;            // LDS offset of this lane's K operand bytes inside a block
+    int vbase;            // LDS offset of this lane's V^T operand bytes inside a block
 };
 
-// S^T = K Q^T for one block (32 keys x this wave's 32 queries), masked per MODE.
-template <int MODE, int KS, int NP>
-__device__ __forceinline__ f32x16 block_scores(const WaveState<NP>& W, const char* buf, int blk, int key0,
-                                               uint32_t bad, int m, int r, int lane) {
-    using SG = Stage<KS, NP>;
-    const int lq = lane & 31, lg = lane >> 5;
+// K operands of one block for S^T = K Q^T (32 keys x this wave's 32
+// queries): lane l supplies key row l%32, channels 16ks + 8(l/32) .. +7
+template <int NP>
+struct KFrag { u32x4 k[4][NP]; };
+
+template <int NP>
+__device__ __forceinline__ KFrag<NP> load_k(const WaveState<NP>& W, const char* blk) {
+    using RG = Ring<NP>;
+    KFrag<NP> f;
+    const char* kb = blk + W.kbase;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+        for (int p = 0; p < NP; p++) f.k[ks][p] = *(const u32x4*)(kb + p * RG::PLANE + 1024 * ks);
+    return f;
+}
+
+template <int NP>
+__device__ __forceinline__ f32x16 block_scores(const WaveState<NP>& W, const KFrag<NP>& f) {
     f32x16 s = {};
-    const char* kb = buf + SG::kOff(0, blk);
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
-        const bf16x8 kf = as_bf16x8(*(const u32x4*)(kb + swzK(lq, 2 * ks + lg)));
-        s = mfma(kf, W.qh[ks], s);
+        s = mfma(as_bf16x8(f.k[ks][0]), W.qh[ks], s);
         if constexpr (NP == 2) {
-            const bf16x8 kfl = as_bf16x8(*(const u32x4*)(buf + SG::kOff(1, blk) + swzK(lq, 2 * ks + lg)));
-            s = mfma(kf, W.ql[ks], s);
-            s = mfma(kfl, W.qh[ks], s);
-        }
-    }
-    if constexpr (MODE != kInterior) {
-        const int* gcls = (const int*)(buf + SG::gclsOff) + blk * KBLK;
-        // this lane's 16 keys are rows 8*(i>>2) + 4*lg + (i&3): shift the mask
-        // word so that bit i of `badl` belongs to accumulator element i
-        const uint32_t sh = bad >> (4 * lg);
-        const uint32_t badl = (sh & 0xfu) | ((sh >> 4) & 0xf0u) | ((sh >> 8) & 0xf00u) | ((sh >> 12) & 0xf000u);
-        int gc[16];
-        if constexpr (MODE == kGlobalKeys) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; q4++) {
-                const u32x4 g4 = *(const u32x4*)(gcls + 8 * q4 + 4 * lg);
-                gc[4 * q4 + 0] = (int)g4[0]; gc[4 * q4 + 1] = (int)g4[1];
-                gc[4 * q4 + 2] = (int)g4[2]; gc[4 * q4 + 3] = (int)g4[3];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const int kl = 8 * (i >> 2) + 4 * lg + (i & 3);   // key row inside the block
-            bool ok = ((badl >> i) & 1u) == 0u;
-            if constexpr (MODE == kBandEdge) {
-                const int dk = key0 + kl - m;
-                ok &= (uint32_t)(dk + r) <= (uint32_t)(2 * r);
-            } else if constexpr (MODE == kGlobalKeys) {
-                const int dk = gc[i] - m;
-                ok &= (uint32_t)(dk + r) > (uint32_t)(2 * r);   // not already in the window
-            }
-            s[i] = ok ? s[i] : kNegInf;
+            s = mfma(as_bf16x8(f.k[ks][0]), W.ql[ks], s);
+            s = mfma(as_bf16x8(f.k[ks][1]), W.qh[ks], s);
         }
     }
     return s;
 }
 
-// Running max/sum update for the scores of NB blocks at once: the raw-score
-// max is taken to base 2 with the 1/sqrt(d) scale, and O is rescaled only when
-// the max grows by more than 2^8 (so every exponent stays <= 8 and the final
-// O / l is unaffected).
-template <int NB, int NP>
-__device__ __forceinline__ void update_max(WaveState<NP>& W, const f32x16 (&s)[NB]) {
-    float mx = s[0][0];
-#pragma unroll
-    for (int b = 0; b < NB; b++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) mx = __builtin_fmaxf(mx, s[b][i]);
-    mx = halves_max(mx);
-    const float mxs = mx * kScaleLog2;
-    const bool need = mxs > W.ms + 8.0f;
-    if (__ballot(need)) {
-        const float msn = need ? mxs : W.ms;
-        const float alpha = need ? __builtin_amdgcn_exp2f(W.ms - msn) : 1.0f;
-#pragma unroll
-        for (int i = 0; i < 16; i++) { W.o0[i] *= alpha; W.o1[i] *= alpha; }
-        W.lp *= alpha;
-        W.ms = msn;
-    }
-}
-
-// p = 2^(s*scale - m) for one block, its row-sum, and O^T += V^T P^T
-template <int KS, int NP>
-__device__ __forceinline__ void block_pv(WaveState<NP>& W, const f32x16& s, const char* buf, int blk, int lane) {
-    using SG = Stage<KS, NP>;
-    const float nms = (W.ms == kNegInf) ? 0.0f : -W.ms;
-    float p[16];
-#pragma unroll
-    for (int i = 0; i < 16; i++) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], kScaleLog2, nms));
-    float ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; i++) ps += p[i];
-    W.lp += ps;
-    // P^T operands: step st covers accumulator elements 8st .. 8st+7
-    bf16x8 pb[2], pbl[2];
-#pragma unroll
-    for (int st = 0; st < 2; st++) {
-        u32x4 w, wl;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const float a = p[8 * st + 2 * e], b = p[8 * st + 2 * e + 1];
-            const uint32_t hw = pack_bf16(a, b);
-            w[e] = hw;
-            if constexpr (NP == 2) {
-                const float ah = __builtin_bit_cast(float, hw << 16);
-                const float bh = __builtin_bit_cast(float, hw & 0xffff0000u);
-                wl[e] = pack_bf16(a - ah, b - bh);
-            }
-        }
-        pb[st] = as_bf16x8(w);
-        if constexpr (NP == 2) pbl[st] = as_bf16x8(wl);
-    }
-    // V^T operands by transposing reads: lane (16G + L) supplies row
-    // 16st + 8hf + 4(G>>1) + (L>>2), channels 32cb + 16(G&1) + 4(L&3)
-    const int G = lane >> 4, L = lane & 15;
-    const int t0 = 4 * (G >> 1) + (L >> 2);
-#pragma unroll
-    for (int st = 0; st < 2; st++) {
-#pragma unroll
-        for (int cb = 0; cb < 2; cb++) {
-            const int byte = 64 * cb + 32 * (G & 1) + 8 * (L & 3);
-            const int ch = byte >> 4, inner = byte & 15;
-            const int ta = 16 * st + t0, tb = ta + 8;
-            const char* vb = buf + SG::vOff(0, blk);
-            const bf16x8 va = cat_tr(ds_tr16(vb + swzV(ta, ch) + inner), ds_tr16(vb + swzV(tb, ch) + inner));
-            f32x16& oc = cb ? W.o1 : W.o0;
-            oc = mfma(va, pb[st], oc);
-            if constexpr (NP == 2) {
-                const char* vbl = buf + SG::vOff(1, blk);
-                const bf16x8 val = cat_tr(ds_tr16(vbl + swzV(ta, ch) + inner), ds_tr16(vbl + swzV(tb, ch) + inner));
-                oc = mfma(va, pbl[st], oc);
-                oc = mfma(val, pb[st], oc);
-            }
-        }
-    }
-}
-
-// One block: `bad` has bit t set when key row t of the block is not a real key.
-template <int MODE, int KS, int NP>
-__device__ __forceinline__ void attend_block(WaveState<NP>& W, const char* buf, int blk, int key0, uint32_t bad,
-                                             int m, int r, int lane) {
-    f32x16 s[1] = {block_scores<MODE, KS, NP>(W, buf, blk, key0, bad, m, r, lane)};
-    update_max<1, NP>(W, s);
-    block_pv<KS, NP>(W, s[0], buf, blk, lane);
-}
-
-// two blocks with one max update: the second block's score MFMAs are issued
-// before the first block's softmax, so they overlap its VALU work
-template <int MODE0, int MODE1, int KS, int NP>
-__device__ __forceinline__ void attend_pair(WaveState<NP>& W, const char* buf, int blk0, int key0, uint32_t bad0,
-                                            int blk1, int key1, uint32_t bad1, int m, int r, int lane) {
-    f32x16 s[2];
-    s[0] = block_scores<MODE0, KS, NP>(W, buf, blk0, key0, bad0, m, r, lane);
-    s[1] = block_scores<MODE1, KS, NP>(W, buf, blk1, key1, bad1, m, r, lane);
-    update_max<2, NP>(W, s);
-    block_pv<KS, NP>(W, s[0], buf, blk0, lane);
-    block_pv<KS, NP>(W, s[1], buf, blk1, lane);
-}
-
-// Masking chosen at run time (wave-uniform), so one code path serves every
-// block kind and O stays in one set of registers.
+// Masking (chosen at run time, wave-uniform, so one code path serves every
+// block kind).  Bit t of `bad` is set when key row t of the block is not a
+// real key (past the sequence, class or split end, padded, or an unused
+// global slot).
 enum MaskKind { kMaskNone = 0, kMaskBand = 1, kMaskGlobal = 2, kMaskBad = 3 };
 
 __device__ __forceinline__ void apply_mask(f32x16& s, int kind, uint32_t bad, int key0, const int* gcls,
                                            int m, int r, int lg) {
     if (kind == kMaskNone) return;
+    // this lane's 16 keys are rows 8*(i>>2) + 4*lg + (i&3): bit i of badl
+    // belongs to accumulator element i
     const uint32_t sh = bad >> (4 * lg);
     const uint32_t badl = (sh & 0xfu) | ((sh >> 4) & 0xf0u) | ((sh >> 8) & 0xf00u) | ((sh >> 12) & 0xf000u);
     if (kind == kMaskBand) {
@@ -447,6 +336,7 @@ __device__ __forceinline__ void apply_mask(f32x16& s, int kind, uint32_t bad, in
             s[i] = ok ? s[i] : kNegInf;
         }
     } else if (kind == kMaskGlobal) {
+        // a global key already inside this query's window is counted by the band
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
             const u32x4 g4 = *(const u32x4*)(gcls + 8 * q4 + 4 * lg);
@@ -464,31 +354,95 @@ __device__ __forceinline__ void apply_mask(f32x16& s, int kind, uint32_t bad, in
     }
 }
 
-// Up to two blocks of one stage for one wave.  live0/live1 say whether each
-// block has work for this wave (a dead block costs no MFMA and adds nothing).
-template <int KS, int NP>
-__device__ __forceinline__ void attend_stage(WaveState<NP>& W, const char* buf, int blk0, bool live0, int kind0,
-                                             uint32_t bad0, int key0, bool live1, int kind1, uint32_t bad1,
-                                             int key1, int m, int r, int lane) {
-    using SG = Stage<KS, NP>;
-    const int lg = lane >> 5;
-    const int* gcls = (const int*)(buf + SG::gclsOff);
-    f32x16 s[2];
+// Running max/sum update for one block's scores.  The raw-score max is taken
+// to base 2 with the 1/sqrt(d) scale, and O is rescaled only when the max
+// grows by more than 2^8.
+template <int NP>
+__device__ __forceinline__ void update_max(WaveState<NP>& W, const f32x16& s) {
+    float mx = s[0];
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-        const bool live = u ? live1 : live0;
-        if (live) {
-            s[u] = block_scores<kInterior, KS, NP>(W, buf, blk0 + u, 0, 0u, m, r, lane);
-            apply_mask(s[u], u ? kind1 : kind0, u ? bad1 : bad0, u ? key1 : key0, gcls + (blk0 + u) * KBLK,
-                       m, r, lg);
-        } else {
+    for (int i = 1; i < 16; i++) mx = __builtin_fmaxf(mx, s[i]);
+    mx = halves_max(mx);
+    const float mxs = mx * kScaleLog2;
+    const bool need = mxs > W.ms + 8.0f;
+    if (__ballot(need)) {
+        const float msn = need ? mxs : W.ms;
+        const float alpha = need ? __builtin_amdgcn_exp2f(W.ms - msn) : 1.0f;
 #pragma unroll
-            for (int i = 0; i < 16; i++) s[u][i] = kNegInf;
+        for (int i = 0; i < 16; i++) { W.o0[i] *= alpha; W.o1[i] *= alpha; }
+        W.lp *= alpha;
+        W.ms = msn;
+    }
+}
+
+// V^T operands of one block, by transposing reads: lane (16G + L) supplies
+// row 16st + 8hf + 4(G>>1) + (L>>2), channels 32cb + 16(G&1) + 4(L&3) .. +3
+// (the lane-dependent part is W.vbase)
+template <int NP>
+struct VFrag { bf16x8 v[2][2][NP]; };   // [st][cb][plane]
+
+template <int NP>
+__device__ __forceinline__ VFrag<NP> load_v(const WaveState<NP>& W, const char* blk) {
+    using RG = Ring<NP>;
+    VFrag<NP> f;
+    const char* vb = blk + 4096 + W.vbase;
+#pragma unroll
+    for (int st = 0; st < 2; st++)
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+            for (int p = 0; p < NP; p++) {
+                const char* a = vb + p * RG::PLANE + cb * 2048 + 16 * st * 64;
+                f.v[st][cb][p] = cat_tr(ds_tr16(a), ds_tr16(a + 8 * 64));
+            }
+    return f;
+}
+
+// p = 2^(s*scale - m) for one block, its row sum, and O^T += V^T P^T
+template <int NP>
+__device__ __forceinline__ void block_pv(WaveState<NP>& W, const f32x16& s, const VFrag<NP>& f) {
+    const float nms = (W.ms == kNegInf) ? 0.0f : -W.ms;
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], kScaleLog2, nms));
+    // P^T operands: step st covers accumulator elements 8st .. 8st+7
+    bf16x8 pb[2], pbl[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; st++) {
+        u32x4 w, wl;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float a = p[8 * st + 2 * e], b = p[8 * st + 2 * e + 1];
+            const uint32_t hw = pack_bf16(a, b);
+            w[e] = hw;
+            if constexpr (NP == 2) {
+                const float ah = __builtin_bit_cast(float, hw << 16);
+                const float bh = __builtin_bit_cast(float, hw & 0xffff0000u);
+                wl[e] = pack_bf16(a - ah, b - bh);
+                ps += a + b;
+            } else {
+                // the row sum of the very bf16 weights that multiply V
+                ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hw),
+                                                     (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, ps, false);
+            }
+        }
+        pb[st] = as_bf16x8(w);
+        if constexpr (NP == 2) pbl[st] = as_bf16x8(wl);
+    }
+    W.lp += ps;
+#pragma unroll
+    for (int st = 0; st < 2; st++) {
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++) {
+            f32x16& oc = cb ? W.o1 : W.o0;
+            oc = mfma(f.v[st][cb][0], pb[st], oc);
+            if constexpr (NP == 2) {
+                oc = mfma(f.v[st][cb][0], pbl[st], oc);
+                oc = mfma(f.v[st][cb][1], pb[st], oc);
+            }
         }
     }
-    update_max<2, NP>(W, s);
-    if (live0) block_pv<KS, NP>(W, s[0], buf, blk0, lane);
-    if (live1) block_pv<KS, NP>(W, s[1], buf, blk0 + 1, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -497,40 +451,53 @@ __device__ __forceinline__ void attend_stage(WaveState<NP>& W, const char* buf, 
 template <int QB, int KS, typename ET, typename OT>
 __global__ __launch_bounds__(64 * QB * KS) __attribute__((amdgpu_waves_per_eu(LFK_WAVES_PER_EU)))
 void tile_kernel(const Params P) {
+    static_assert(QB == 2 && KS == 2, "four waves: two phases of two query blocks");
     constexpr int NT = 64 * QB * KS;
     constexpr int NP = Elem<ET>::NP;
-    constexpr int NBW = NP == 1 ? 2 : 1;       // blocks per wave per stage (processed as a pair)
-    constexpr int NBLK = KS * NBW;             // blocks per stage
-    static_assert(NBLK <= QB * KS, "one mask wave per block");
-    using SG = Stage<NBLK, NP>;
-    constexpr int R = NBLK * KBLK;             // key rows per stage
-    constexpr int CHUNKS = R * 8;              // 8-channel chunks per tensor per stage
-    static_assert(CHUNKS % NT == 0, "stage chunks must divide evenly over the workgroup");
-    constexpr int CPT = CHUNKS / NT;           // chunks per thread per tensor
+    constexpr int ROWB = NP * 128;             // bytes per K/V row in the bf16-plane layout
+    using RG = Ring<NP>;
     constexpr int MERGE_BYTES = (KS - 1) * QB * 64 * 36 * 4;
-    constexpr int SMEM = (SG::bytes > MERGE_BYTES) ? SG::bytes : MERGE_BYTES;
-    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    static_assert(MERGE_BYTES <= RG::NBUF * RG::STAGE, "merge area inside the ring");
+    __shared__ __attribute__((aligned(16))) char smem[RG::bytes];
+    const int* gpos = (const int*)(smem + RG::gposOff);
+    const int* gcls = (const int*)(smem + RG::gclsOff);
+    const uint32_t* gbad = (const uint32_t*)(smem + RG::gbadOff);
+    uint32_t* maskw = (uint32_t*)(smem + RG::maskOff);
 
-    // ---- which task (XCD-aware: each of the 8 dies takes a contiguous task range)
-    const int per_xcd = gridDim.x >> 3;
-    const int task_id = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    if (task_id >= P.n_tasks) return;
+    // ---- which task.  Each of the 8 dies (blockIdx % 8) takes a contiguous
+    // eighth of the band tasks (neighbouring tiles share keys in its L2), then
+    // an eighth of the global-row tasks.
+    const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
+    int task_id;
+    {
+        const int nb = P.n_band_tasks, ng = P.n_tasks - P.n_band_tasks;
+        const int nb_x = (nb >> 3) + (xcd < (nb & 7)), nb_o = xcd * (nb >> 3) + min(xcd, nb & 7);
+        const int ng_x = (ng >> 3) + (xcd < (ng & 7)), ng_o = xcd * (ng >> 3) + min(xcd, ng & 7);
+        if (slot_in_xcd < nb_x) task_id = nb_o + slot_in_xcd;
+        else if (slot_in_xcd - nb_x < ng_x) task_id = nb + ng_o + (slot_in_xcd - nb_x);
+        else return;
+    }
     const Task tk = decode_task<QB>(P, task_id);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = uniform(tid >> 6);
     const int qb = wave % QB;
-    const int ph = wave / QB;          // key phase of this wave
+    const int ph = wave / QB;          // key phase of this wave: block ph of every stage
     const int lq = lane & 31;          // query column owned by this lane
     const int lg = lane >> 5;
 
     const size_t head_off = (size_t)tk.bh * P.T * D;
-    const ET* __restrict__ Kg = (const ET*)P.k + head_off;
-    const ET* __restrict__ Vg = (const ET*)P.v + head_off;
     const ET* __restrict__ Qg = (const ET*)P.q + head_off;
     const uint8_t* __restrict__ padrow = P.pad ? P.pad + (size_t)tk.b * P.T : nullptr;
-    const int r = P.r;
+    // kernel-argument scalars used inside the loop live in registers (a value
+    // select between an LDS table entry and a kernel argument would otherwise
+    // become a flat load, which waits on every load in flight)
+    const int T = P.T, n_g = P.n_g, r = P.r;
+    const uint32_t head_bytes = (uint32_t)T * ROWB;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((const char*)P.kp + (size_t)tk.bh * head_bytes, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc((const char*)P.vp + (size_t)tk.bh * head_bytes, head_bytes);
+    const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, padrow ? (uint32_t)T : 0u);
 
     // ---- this wave's 32 queries
     const int mq0 = tk.m0 + 32 * qb;   // first query (class index, or global slot)
@@ -545,10 +512,186 @@ void tile_kernel(const Params P) {
         const int sl = mq0 + lq;
         if (sl < P.n_g) my_pos = P.glob[sl];
     }
-    const bool my_pad = (my_pos >= 0 && padrow) ? padrow[my_pos] != 0 : false;
+    const int m_me = mq0 + lq;         // this lane's query (class index / global slot)
+
+    // band blocks this wave's queries can reach
+    int wb_lo = 0, wb_hi = -1;
+    if (tk.kind == 0) {
+        int a = mq0 - r; if (a < 0) a = 0;
+        int z = mq0 + 31 + r; if (z > tk.n - 1) z = tk.n - 1;
+        wb_lo = a / KBLK;
+        wb_hi = z / KBLK;
+    }
+
+    // ---- block list: band (or dense) blocks, then global-key blocks; stage s
+    // holds blocks 2s and 2s+1
+    const int ngb = tk.kind == 0 ? cdiv(P.n_g, KBLK) : 0;
+    const int nblk = tk.nband + ngb;
+    const int NS = cdiv(nblk, 2);
+
+    // ---- global-key tables (band tasks): positions, class indices, and per
+    // global block the slots that are no key (unused or padded)
+    if (ngb > 0) {
+        for (int base = 64 * wave; base < ngb * KBLK; base += NT) {
+            const int slot = base + lane;
+            const bool inr = slot < P.n_g;
+            const int pos = inr ? P.glob[slot] : P.T;
+            const bool padded = inr && padrow && padrow[pos] != 0;
+            int cls = kNotInClass;
+            const int dpos = pos - tk.c;
+            if (inr && dpos >= 0) {
+                const int q = dpos / tk.delta;
+                if (q * tk.delta == dpos) cls = q;
+            }
+            if (slot < LF_MAX_GLOBALS) {
+                ((int*)gpos)[slot] = pos;
+                ((int*)gcls)[slot] = cls;
+            }
+            const uint64_t badm = __ballot(!inr || padded);
+            if (lane == 0 && base < LF_MAX_GLOBALS) {
+                ((uint32_t*)gbad)[base >> 5] = (uint32_t)badm;
+                if (base + 32 < LF_MAX_GLOBALS) ((uint32_t*)gbad)[(base >> 5) + 1] = (uint32_t)(badm >> 32);
+            }
+        }
+        __syncthreads();
+    }
+
+    // memory position of row `row` of block jb (T for no row: reads zero)
+    auto row_pos = [&](int jb, int row) -> uint32_t {
+        if (jb < tk.nband) {
+            const int pos = tk.c + tk.delta * ((tk.kb_lo + jb) * KBLK + row);
+            return (uint32_t)min(pos, T);
+        }
+        const int slot = (jb - tk.nband) * KBLK + row;
+        const int g = gpos[min(slot, LF_MAX_GLOBALS - 1)];
+        return (uint32_t)(slot < n_g ? g : T);
+    };
+
+    // Loads of stage s into ring slot s % 3: waves 0/1 bring the K rows of
+    // blocks 0/1, waves 2/3 their V rows.
+    auto issue_stage = [&](int s) {
+        const int b = wave & 1;
+        const int jb = 2 * s + b;
+        if (jb >= nblk) return;
+        char* dst = smem + (s % RG::NBUF) * RG::STAGE + b * RG::BLK;
+        if (wave < 2) {
+            const int row = lane >> 1;
+            const uint32_t voff = row_pos(jb, row) * ROWB + 16 * ((lane & 1) ^ ((row >> 3) & 1));
+#pragma unroll
+            for (int p = 0; p < NP; p++)
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++)
+                    load_lds16(rk, dst + p * RG::PLANE + ks * 1024, voff, 32 * ks + 128 * p);
+        } else {
+#pragma unroll
+            for (int hf = 0; hf < 2; hf++) {
+                const int row = 16 * hf + (lane >> 2);
+                const uint32_t voff = row_pos(jb, row) * ROWB + 16 * (lane & 3);
+#pragma unroll
+                for (int p = 0; p < NP; p++)
+#pragma unroll
+                    for (int cb = 0; cb < 2; cb++)
+                        load_lds16(rv, dst + p * RG::PLANE + 4096 + cb * 2048 + hf * 1024, voff, 64 * cb + 128 * p);
+            }
+        }
+    };
+
+    // With padding: waves 0/1 read the padding bytes of their block's rows
+    // (lanes 0..31) one step ahead ...
+    auto load_pad = [&](int s) -> uint32_t {
+        if (!padrow || wave >= 2) return 0u;
+        const int jb = 2 * s + wave;
+        if (jb >= tk.nband) return 0u;
+        return __builtin_amdgcn_raw_buffer_load_b8(rpad, row_pos(jb, lane & 31), 0, 0);
+    };
+    // ... and once the stage has landed, publish its mask word and zero the V
+    // rows of keys that are not real (so that NaN or Inf stored in padded
+    // positions cannot reach the products).
+    auto fix_stage = [&](int s, uint32_t padv) {
+        if (!padrow || wave >= 2) return;
+        const int jb = 2 * s + wave;
+        if (jb >= nblk) return;
+        uint32_t badw;
+        if (jb < tk.nband) {
+            const uint32_t padbits = (uint32_t)__ballot(lane < 32 && padv != 0u);
+            const int valid = tk.key_end - (tk.kb_lo + jb) * KBLK;
+            badw = padbits | (valid >= KBLK ? 0u : (valid <= 0 ? 0xffffffffu : (0xffffffffu << valid)));
+        } else {
+            badw = gbad[jb - tk.nband];
+        }
+        if (lane == 0) maskw[(s % RG::NBUF) * 2 + wave] = badw;
+        if (badw != 0u) {
+            const int row = lane >> 1, cb = lane & 1;
+            if ((badw >> row) & 1u) {
+                char* vrow = smem + (s % RG::NBUF) * RG::STAGE + wave * RG::BLK + 4096 + cb * 2048 + row * 64;
+                const u32x4 z = {0, 0, 0, 0};
+#pragma unroll
+                for (int p = 0; p < NP; p++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++) *(u32x4*)(vrow + p * RG::PLANE + 16 * j) = z;
+            }
+        }
+    };
+
+    // does this wave's block of stage s hold keys for its queries?
+    auto live_of = [&](int s) -> bool {
+        const int jb = 2 * s + ph;
+        if (!wave_active || jb >= nblk) return false;
+        if (jb < tk.nband) {
+            const int kb = tk.kb_lo + jb;
+            return tk.kind == 1 || (kb >= wb_lo && kb <= wb_hi);
+        }
+        return true;
+    };
+    // mask word of this wave's block of stage s
+    auto block_bad = [&](int s) -> uint32_t {
+        const int jb = 2 * s + ph;
+        if (jb >= tk.nband) return gbad[jb - tk.nband];
+        if (padrow) return maskw[(s % RG::NBUF) * 2 + ph];
+        const int valid = tk.key_end - (tk.kb_lo + jb) * KBLK;
+        return valid >= KBLK ? 0u : (valid <= 0 ? 0xffffffffu : (0xffffffffu << valid));
+    };
 
     WaveState<NP> W;
+    W.o0 = (f32x16){};
+    W.o1 = (f32x16){};
+    W.ms = kNegInf;
+    W.lp = 0.f;
+    W.kbase = ph * RG::BLK + lq * 32 + ((lg ^ ((lq >> 3) & 1)) << 4);
+    W.vbase = ph * RG::BLK + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+
+    // masking of this wave's block of stage s (scores in sc); false when the
+    // block holds no key for this wave's queries.  Reads LDS (mask word,
+    // global-key classes), so it runs before the step's loads are issued.
+    auto mask_block = [&](int s, f32x16& sc) -> bool {
+        if (!live_of(s)) return false;
+        const uint32_t bad = block_bad(s);
+        if (bad == 0xffffffffu) return false;
+        const int jb = 2 * s + ph;
+        int kind, key0 = 0;
+        const int* gc = gcls;
+        if (jb < tk.nband) {
+            key0 = (tk.kb_lo + jb) * KBLK;
+            const bool interior = tk.kind == 0 && bad == 0u && key0 >= mq0 + 31 - r && key0 + 31 <= mq0 + r;
+            kind = tk.kind == 1 ? kMaskBad : (interior ? kMaskNone : kMaskBand);
+        } else {
+            kind = kMaskGlobal;
+            gc = gcls + (jb - tk.nband) * KBLK;
+        }
+        apply_mask(sc, kind, bad, key0, gc, m_me, r, lg);
+        return true;
+    };
+
+    // ---- prologue: stages 0 and 1 in flight, then Q
+    issue_stage(0);
+    const uint32_t pad0 = load_pad(0);
+    uint32_t pad_pending = 0u;
+    if (NS > 1) {
+        issue_stage(1);
+        pad_pending = load_pad(1);
+    }
     {
+        const bool my_pad = (my_pos >= 0 && padrow) ? padrow[my_pos] != 0 : false;
         const bool ok = my_pos >= 0 && !my_pad;
         const ET* qrow = Qg + (size_t)(ok ? my_pos : 0) * D;
 #pragma unroll
@@ -569,231 +712,36 @@ void tile_kernel(const Params P) {
             }
         }
     }
-    W.o0 = (f32x16){};
-    W.o1 = (f32x16){};
-    W.ms = kNegInf;
-    W.lp = 0.f;
+    barrier_lds_loads();               // stages 0 and 1 have landed
+    fix_stage(0, pad0);
+    f32x16 sc = {};
+    if (live_of(0)) sc = block_scores<NP>(W, load_k<NP>(W, smem));
 
-    // band blocks this wave's queries can reach
-    int wb_lo = 0, wb_hi = -1;
-    if (tk.kind == 0) {
-        int a = mq0 - r; if (a < 0) a = 0;
-        int z = mq0 + 31 + r; if (z > tk.n - 1) z = tk.n - 1;
-        wb_lo = a / KBLK;
-        wb_hi = z / KBLK;
-    }
-
-    // ---- stage plan: band (or dense) stages, then global-key stages
-    const int ngb = tk.kind == 0 ? cdiv(P.n_g, KBLK) : 0;
-    const int NSb = cdiv(tk.nband, NBLK);
-    const int NS = NSb + cdiv(ngb, NBLK);
-    // LDS mask words are only needed where the key range alone does not say
-    // which rows are real: with padding, and for the global-key stages
-    const bool lds_mask_band = padrow != nullptr;
-
-    // loader geometry: chunk j of this thread is stage row lrow0 + j * NT/8,
-    // channels 8*lch .. 8*lch+7; band rows advance by R keys per stage
-    const int lch = tid & 7;
-    const int lrow0 = tid >> 3;
-    const int key_base = tk.kb_lo * KBLK;
-    const int rowstep = tk.delta * D;                 // elements between consecutive class keys
-
-    struct Regs {
-        u32x4 k[CPT][NP];
-        u32x4 v[CPT][NP];
-        uint32_t inr;         // bit j: chunk j's row is a real position
-        bool full;            // every row of the stage is a real, unpadded key
-        uint8_t padb[CPT];    // that position's padding byte (0 without padding)
-        bool minr;            // mask lanes: row is a real position
-        uint8_t mpad;         // ... and its padding byte
-        int gcls;
-    };
-
-    // Loads are issued unconditionally from clamped (always valid) addresses;
-    // whether a row is real or padded is only applied when the registers are
-    // written to LDS, so no branch waits on these loads before the compute.
-    // Order inside a stage load: every position lookup and every small load
-    // (padding bytes, global classes) first, the K/V loads last.  Nothing is
-    // then written after the K/V loads into a register an earlier load could
-    // still own, so the compiler places no wait on them before the compute.
-    auto issue = [&](int st, Regs& Rg) {
-        const bool band = st < NSb;
-        const bool masklane = (!band || lds_mask_band) && wave < NBLK;
-        int pos[CPT];
-        int mpos = 0;
-        bool minr = false;
-        Rg.inr = 0;
-        Rg.full = band && !padrow && key_base + (st + 1) * R <= tk.key_end;
-        if (band) {
-#pragma unroll
-            for (int j = 0; j < CPT; j++) {
-                const int kk = key_base + st * R + lrow0 + j * (NT / 8);
-                const bool inr = kk < tk.key_end;
-                pos[j] = inr ? tk.c + tk.delta * kk : 0;
-                Rg.inr |= (uint32_t)inr << j;
-            }
-            if (masklane) {
-                const int kk = key_base + st * R + 32 * wave + lq;
-                minr = kk < tk.key_end;
-                mpos = minr ? tk.c + tk.delta * kk : 0;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < CPT; j++) {
-                const int slot = (st - NSb) * R + lrow0 + j * (NT / 8);
-                const bool inr = slot < P.n_g;
-                pos[j] = P.glob[inr ? slot : 0];
-                Rg.inr |= (uint32_t)inr << j;
-            }
-            if (masklane) {
-                const int slot = (st - NSb) * R + 32 * wave + lq;
-                minr = slot < P.n_g;
-                mpos = P.glob[minr ? slot : 0];
-            }
+    // ---- main loop: one barrier per step.  Every LDS read of a step comes
+    // before that step's loads into LDS are issued: the compiler makes any
+    // LDS read that follows such a load wait for it.
+    for (int s = 0; s < NS; s++) {
+        barrier_lds_loads();           // stage s+1 landed; stage s fixed up; stage s-1 no longer read
+        const bool next = s + 1 < NS && live_of(s + 1);
+        KFrag<NP> kf;
+        if (next) kf = load_k<NP>(W, smem + ((s + 1) % RG::NBUF) * RG::STAGE);
+        const bool cur = mask_block(s, sc);
+        VFrag<NP> vf;
+        if (cur) vf = load_v<NP>(W, smem + (s % RG::NBUF) * RG::STAGE);
+        if (s + 1 < NS) fix_stage(s + 1, pad_pending);
+        uint32_t pad_next = 0u;
+        if (s + 2 < NS) {
+            issue_stage(s + 2);
+            pad_next = load_pad(s + 2);
         }
-        if (masklane) {
-            Rg.minr = minr && lg == 0;
-            Rg.mpad = padrow ? padrow[mpos] : (uint8_t)0;
-            const int dpos = mpos - tk.c;
-            const int q = dpos / tk.delta;
-            Rg.gcls = (!band && minr && dpos >= 0 && q * tk.delta == dpos) ? q : kNotInClass;
+        f32x16 sn = {};
+        if (next) sn = block_scores<NP>(W, kf);
+        if (cur) {
+            update_max<NP>(W, sc);
+            block_pv<NP>(W, sc, vf);
         }
-        if (padrow) {
-#pragma unroll
-            for (int j = 0; j < CPT; j++) Rg.padb[j] = padrow[pos[j]];
-        }
-#pragma unroll
-        for (int j = 0; j < CPT; j++) {
-            const size_t off = (size_t)pos[j] * D + lch * 8;
-#pragma unroll
-            for (int p = 0; p < NP; p++) {
-                Rg.k[j][p] = *(const u32x4*)(Kg + off + 4 * p);
-                Rg.v[j][p] = *(const u32x4*)(Vg + off + 4 * p);
-            }
-        }
-    };
-
-    auto commit = [&](int st, const Regs& Rg) {
-        const u32x4 z = {0, 0, 0, 0};
-        char* buf = smem;
-#pragma unroll
-        for (int j = 0; j < CPT; j++) {
-            const int row = lrow0 + j * (NT / 8);
-            const int blk = row >> 5, t = row & 31;
-            const bool ok = Rg.full || (((Rg.inr >> j) & 1u) != 0u && (!padrow || Rg.padb[j] == 0));
-            if constexpr (NP == 1) {
-                *(u32x4*)(buf + SG::kOff(0, blk) + swzK(t, lch)) = ok ? Rg.k[j][0] : z;
-                *(u32x4*)(buf + SG::vOff(0, blk) + swzV(t, lch)) = ok ? Rg.v[j][0] : z;
-            } else {
-                u32x4 kh, kl, vh, vl;
-                split8(Raw32{Rg.k[j][0], Rg.k[j][1]}, kh, kl);
-                split8(Raw32{Rg.v[j][0], Rg.v[j][1]}, vh, vl);
-                *(u32x4*)(buf + SG::kOff(0, blk) + swzK(t, lch)) = ok ? kh : z;
-                *(u32x4*)(buf + SG::kOff(1, blk) + swzK(t, lch)) = ok ? kl : z;
-                *(u32x4*)(buf + SG::vOff(0, blk) + swzV(t, lch)) = ok ? vh : z;
-                *(u32x4*)(buf + SG::vOff(1, blk) + swzV(t, lch)) = ok ? vl : z;
-            }
-        }
-        if ((st >= NSb || lds_mask_band) && wave < NBLK) {
-            const uint32_t good = (uint32_t)__ballot(Rg.minr && Rg.mpad == 0);   // lanes 0..31 only
-            if (lane == 0) *(uint32_t*)(buf + SG::maskOff + wave * 4) = ~good;
-            if (lg == 0) ((int*)(buf + SG::gclsOff))[wave * KBLK + lq] = Rg.gcls;
-        }
-    };
-
-    // mask word of stage block `blk`: from LDS, or from the key range alone
-    auto block_bad = [&](int st, int blk) -> uint32_t {
-        if (st >= NSb || lds_mask_band) return *(const uint32_t*)(smem + SG::maskOff + blk * 4);
-        const int key0 = key_base + st * R + blk * KBLK;
-        const int valid = tk.key_end - key0;
-        return valid >= KBLK ? 0u : (valid <= 0 ? 0xffffffffu : (0xffffffffu << valid));
-    };
-
-    // ---- main loop: prefetch stage st+1 into registers while stage st is in LDS
-    {
-        Regs Rg;
-        issue(0, Rg);
-        commit(0, Rg);
-        __syncthreads();
-    }
-    const int m_me = mq0 + lq;         // this lane's query (class index / global slot)
-    // which of this wave's blocks of stage st have work, and how to mask them
-    struct StagePlan {
-        bool live[NBW];
-        int kind[NBW], key0[NBW];
-        uint32_t bad[NBW];
-    };
-    const int b0 = ph * NBW;           // this wave's blocks: NBW consecutive blocks of phase ph
-    auto plan = [&](int st) {
-        StagePlan sp;
-#pragma unroll
-        for (int u = 0; u < NBW; u++) {
-            sp.bad[u] = block_bad(st, b0 + u);
-            if (st < NSb) {
-                const int jb = st * NBLK + b0 + u;
-                const int kb = tk.kb_lo + jb;
-                sp.key0[u] = kb * KBLK;
-                sp.live[u] = wave_active && jb < tk.nband && sp.bad[u] != 0xffffffffu &&
-                             (tk.kind == 1 || (kb >= wb_lo && kb <= wb_hi));
-                const bool interior = tk.kind == 0 && sp.bad[u] == 0u && sp.key0[u] >= mq0 + 31 - r &&
-                                      sp.key0[u] + 31 <= mq0 + r;
-                sp.kind[u] = tk.kind == 1 ? kMaskBad : (interior ? kMaskNone : kMaskBand);
-            } else {
-                const int jg = (st - NSb) * NBLK + b0 + u;
-                sp.key0[u] = 0;
-                sp.live[u] = wave_active && jg < ngb && sp.bad[u] != 0xffffffffu;
-                sp.kind[u] = kMaskGlobal;
-            }
-        }
-        return sp;
-    };
-    // the score MFMAs of the stage's blocks
-    auto scores = [&](const StagePlan& sp, f32x16 (&sc)[NBW]) {
-#pragma unroll
-        for (int u = 0; u < NBW; u++)
-            if (sp.live[u]) sc[u] = block_scores<kInterior, NBLK, NP>(W, smem, b0 + u, 0, 0u, m_me, r, lane);
-    };
-    // masking, running max/sum and O += P V
-    auto finish = [&](const StagePlan& sp, f32x16 (&sc)[NBW]) {
-        bool any = false;
-#pragma unroll
-        for (int u = 0; u < NBW; u++) any = any || sp.live[u];
-        if (!any) return;
-        const int* gcls = (const int*)(smem + SG::gclsOff);
-#pragma unroll
-        for (int u = 0; u < NBW; u++) {
-            if (sp.live[u]) {
-                apply_mask(sc[u], sp.kind[u], sp.bad[u], sp.key0[u], gcls + (b0 + u) * KBLK, m_me, r, lg);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; i++) sc[u][i] = kNegInf;
-            }
-        }
-        update_max<NBW, NP>(W, sc);
-#pragma unroll
-        for (int u = 0; u < NBW; u++)
-            if (sp.live[u]) block_pv<NBLK, NP>(W, sc[u], smem, b0 + u, lane);
-    };
-
-    // Every stage but the last: score MFMAs, then the next stage's loads (they
-    // queue while the matrix cores run), then the softmax and PV, then the LDS
-    // hand-over.  Straight-line code, so the loads stay where they are.
-    for (int st = 0; st + 1 < NS; st++) {
-        const StagePlan sp = plan(st);
-        f32x16 sc[NBW];
-        scores(sp, sc);
-        Regs Rg;
-        issue(st + 1, Rg);
-        finish(sp, sc);
-        __syncthreads();               // every wave is done reading stage st
-        commit(st + 1, Rg);
-        __syncthreads();               // stage st+1 is in LDS
-    }
-    {
-        const StagePlan sp = plan(NS - 1);
-        f32x16 sc[NBW];
-        scores(sp, sc);
-        finish(sp, sc);
+        sc = sn;
+        pad_pending = pad_next;
     }
     __syncthreads();
 
@@ -801,25 +749,32 @@ void tile_kernel(const Params P) {
     if constexpr (KS > 1) {
         float* mbuf = (float*)smem;
         if (ph > 0) {
-            float* dst = mbuf + (((ph - 1) * QB + qb) * 64 + lane) * 36;
-            dst[0] = W.ms;
-            dst[1] = W.lp;
+            f32x4* dst = (f32x4*)(mbuf + (((ph - 1) * QB + qb) * 64 + lane) * 36);
 #pragma unroll
-            for (int i = 0; i < 16; i++) { dst[2 + i] = W.o0[i]; dst[18 + i] = W.o1[i]; }
+            for (int i = 0; i < 4; i++) {
+                dst[i] = (f32x4){W.o0[4 * i], W.o0[4 * i + 1], W.o0[4 * i + 2], W.o0[4 * i + 3]};
+                dst[4 + i] = (f32x4){W.o1[4 * i], W.o1[4 * i + 1], W.o1[4 * i + 2], W.o1[4 * i + 3]};
+            }
+            dst[8] = (f32x4){W.ms, W.lp, 0.f, 0.f};
         }
         __syncthreads();
         if (ph == 0) {
 #pragma unroll
             for (int p2 = 1; p2 < KS; p2++) {
-                const float* src = mbuf + (((p2 - 1) * QB + qb) * 64 + lane) * 36;
-                const float ms2 = src[0], lp2 = src[1];
+                const f32x4* src = (const f32x4*)(mbuf + (((p2 - 1) * QB + qb) * 64 + lane) * 36);
+                const f32x4 tail = src[8];
+                const float ms2 = tail[0], lp2 = tail[1];
                 const float mn = __builtin_fmaxf(W.ms, ms2);
                 const float a1 = (W.ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(W.ms - mn);
                 const float a2 = (ms2 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ms2 - mn);
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    W.o0[i] = W.o0[i] * a1 + src[2 + i] * a2;
-                    W.o1[i] = W.o1[i] * a1 + src[18 + i] * a2;
+                for (int i = 0; i < 4; i++) {
+                    const f32x4 x0 = src[i], x1 = src[4 + i];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        W.o0[4 * i + e] = W.o0[4 * i + e] * a1 + x0[e] * a2;
+                        W.o1[4 * i + e] = W.o1[4 * i + e] * a1 + x1[e] * a2;
+                    }
                 }
                 W.lp = W.lp * a1 + lp2 * a2;
                 W.ms = mn;
@@ -834,7 +789,15 @@ void tile_kernel(const Params P) {
         // ---- epilogue: y = O / l for the tile's valid queries; padded rows -> 0.
         // Rows of global queries are left to the global-row combine.
         if (!writer || my_pos < 0) return;
-        if (P.n_g > 0 && is_global(P, my_pos)) return;
+        if (P.n_g > 0) {
+            int lo = 0, hi = P.n_g - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (gpos[mid] < my_pos) lo = mid + 1; else hi = mid;
+            }
+            if (gpos[lo] == my_pos) return;
+        }
+        const bool my_pad = padrow ? padrow[my_pos] != 0 : false;
         OT* orow = (OT*)P.out + head_off + (size_t)my_pos * D;
         const float inv = (my_pad || l == 0.f) ? 0.f : 1.0f / l;
 #pragma unroll
@@ -930,18 +893,49 @@ void tile_kernel(const Params P) {
     if (tid == 0) __hip_atomic_store(P.counter + tk.bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// fp32 K and V -> bf16 hi/lo planes [rows][2][64] (hi = RNE(x), lo = RNE(x - hi)),
+// one thread per 8 channels of a row; blockIdx.y picks K or V
+__global__ __launch_bounds__(256) void split_planes_kernel(const float* __restrict__ k, const float* __restrict__ v,
+                                                           uint16_t* __restrict__ kp, uint16_t* __restrict__ vp,
+                                                           long long chunks) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= chunks) return;
+    const float* src = blockIdx.y ? v : k;
+    uint16_t* dst = blockIdx.y ? vp : kp;
+    const long long row = i >> 3;
+    const int ch = (int)(i & 7);
+    Raw32 x;
+    x.a = *(const u32x4*)(src + row * D + ch * 8);
+    x.b = *(const u32x4*)(src + row * D + ch * 8 + 4);
+    u32x4 hi, lo;
+    split8(x, hi, lo);
+    *(u32x4*)(dst + row * 2 * D + ch * 8) = hi;
+    *(u32x4*)(dst + row * 2 * D + D + ch * 8) = lo;
+}
+
 }  // namespace lfk
 
 // ---------------------------------------------------------------------------
-// launcher (called from the host library)
+// launchers (called from the host library)
+
+// grid: the task slots of the 8 dies, each die holding ceil(n/8) band and
+// ceil(n/8) global-row slots
+extern "C" int lfk_grid(const lfk::Params* P) {
+    const int nb = P->n_band_tasks, ng = P->n_tasks - P->n_band_tasks;
+    return 8 * ((nb + 7) / 8 + (ng + 7) / 8);
+}
 
 extern "C" hipError_t lfk_launch(const lfk::Params* P, int dtype_bf16, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     constexpr int QB = LFK_QB, KS = LFK_KS;
-    const int grid = ((P->n_tasks + 7) / 8) * 8;
-    if (dtype_bf16)
+    const int grid = lfk_grid(P);
+    if (dtype_bf16) {
         hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, __bf16, uint16_t>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
-    else
+    } else {
+        const long long chunks = (long long)P->B * P->H * P->T * 8;
+        hipLaunchKernelGGL(lfk::split_planes_kernel, dim3((unsigned)((chunks + 255) / 256), 2), dim3(256), 0, s,
+                           (const float*)P->k, (const float*)P->v, (uint16_t*)P->kp, (uint16_t*)P->vp, chunks);
         hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, float, float>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
+    }
     return hipGetLastError();
 }

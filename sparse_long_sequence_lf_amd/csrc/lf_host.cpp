@@ -37,55 +37,73 @@ lf_status_t fail(lf_status_t st, const char *fmt, ...) {
 
 long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 
-size_t counter_bytes(int B, int H) { return (((size_t)B * H * sizeof(int)) + 255) / 256 * 256; }
-
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Device workspace for the global-row partials, one per (device, stream).
-// Calls on one stream are ordered, so they can share it; calls on other
-// streams get their own.  It only grows; the old buffer is released after
-// the stream has drained it.
-struct Workspace {
+// Device workspaces, one set per (device, stream): calls on one stream are
+// ordered, so they can share it; calls on other streams get their own.
+//
+//  * counters: the global-row completion counters, one int per (b, h).  They
+//    must read zero at the start of every call: the allocation is zeroed
+//    and every call's kernel returns each counter it uses to zero.  Nothing
+//    else is ever stored there.
+//  * scratch: the global-row partials and, for fp32 input, the bf16 hi/lo
+//    planes of K and V; no contents carry over between calls.
+//
+// Both only grow; an old buffer is released after the stream has drained it.
+struct Buffer {
     void *ptr = nullptr;
     size_t bytes = 0;
+};
+struct Workspace {
+    Buffer counters, scratch;
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, void *>, Workspace> g_ws;
 
-lf_status_t workspace(size_t bytes, void *stream, char **out) {
+lf_status_t grow(Buffer &b, size_t bytes, bool zero, void *stream) {
+    if (b.bytes >= bytes) return LF_OK;
+    hipError_t e;
+    if (b.ptr) {
+        e = hipStreamSynchronize((hipStream_t)stream);
+        if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+        (void)hipFree(b.ptr);
+        b.ptr = nullptr;
+        b.bytes = 0;
+    }
+    const size_t want = std::max(bytes, (size_t)1 << 16);
+    e = hipMalloc(&b.ptr, want);
+    if (e != hipSuccess) {
+        b.ptr = nullptr;
+        (void)hipGetLastError();
+        return fail(LF_E_NOMEM, "workspace of %zu bytes: %s", want, hipGetErrorString(e));
+    }
+    if (zero) {
+        e = hipMemset(b.ptr, 0, want);
+        if (e != hipSuccess) {
+            (void)hipFree(b.ptr);
+            b.ptr = nullptr;
+            return fail(LF_E_HIP, "hipMemset: %s", hipGetErrorString(e));
+        }
+    }
+    b.bytes = want;
+    return LF_OK;
+}
+
+lf_status_t workspace(size_t counter_bytes, size_t scratch_bytes, void *stream, int **counters, char **scratch) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(LF_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
     std::lock_guard<std::mutex> lock(g_ws_mu);
     Workspace &w = g_ws[std::make_pair(dev, stream)];
-    if (w.bytes < bytes) {
-        if (w.ptr) {
-            e = hipStreamSynchronize((hipStream_t)stream);
-            if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        const size_t want = std::max(bytes, (size_t)1 << 20);
-        e = hipMalloc(&w.ptr, want);
-        if (e != hipSuccess) {
-            w.ptr = nullptr;
-            (void)hipGetLastError();
-            return fail(LF_E_NOMEM, "workspace of %zu bytes: %s", want, hipGetErrorString(e));
-        }
-        // the completion counters must start at zero; every call leaves them at zero
-        e = hipMemset(w.ptr, 0, want);
-        if (e != hipSuccess) {
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            return fail(LF_E_HIP, "hipMemset: %s", hipGetErrorString(e));
-        }
-        w.bytes = want;
-    }
-    *out = (char *)w.ptr;
+    lf_status_t st = grow(w.counters, counter_bytes, true, stream);
+    if (st != LF_OK) return st;
+    st = grow(w.scratch, scratch_bytes, false, stream);
+    if (st != LF_OK) return st;
+    *counters = (int *)w.counters.ptr;
+    *scratch = (char *)w.scratch.ptr;
     return LF_OK;
 }
 
@@ -154,10 +172,13 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
         start += rem * cdiv(qq + 1, BM) + (delta - rem) * cdiv(qq, BM);
     }
     P.head_start[H] = (int)start;
+    P.uniform_head_tasks = (int)(start / H);
+    for (int h = 0; h < H; h++)
+        if (P.head_start[h + 1] - P.head_start[h] != P.uniform_head_tasks) P.uniform_head_tasks = 0;
     P.band_tasks_per_batch = (int)start;
     const long long n_band = (long long)B * start;
     long long n_glob_tasks = 0;
-    size_t ws_bytes = 0;
+    size_t cnt_bytes = 0, scratch_bytes = 0;
     if (P.n_g > 0) {
         P.n_ggroups = (int)cdiv(cdiv(P.n_g, 32), QB);
         P.g_pad = P.n_ggroups * BM;
@@ -165,21 +186,39 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
         P.split_len = sl < 256 ? 256 : sl;
         P.n_split = (int)cdiv(T, P.split_len);  // <= 16: the combine spans splits with one wave's lanes
         n_glob_tasks = (long long)B * H * P.n_split * P.n_ggroups;
-        // [B*H completion counters, padded to 256 B][partials]
-        ws_bytes = counter_bytes(B, H) + (size_t)B * H * P.n_split * P.g_pad * (LF_HEAD_DIM + 2) * sizeof(float);
+        cnt_bytes = (size_t)B * H * sizeof(int);
+        scratch_bytes = (size_t)B * H * P.n_split * P.g_pad * (LF_HEAD_DIM + 2) * sizeof(float);
     }
     if (n_band + n_glob_tasks > (1LL << 30))
         return fail(LF_E_UNSUPPORTED, "problem needs %lld workgroups", n_band + n_glob_tasks);
     P.n_band_tasks = (int)n_band;
     P.n_tasks = (int)(n_band + n_glob_tasks);
+    // fp32: K and V are split into bf16 hi/lo planes (same byte size as the
+    // fp32 tensors) ahead of the tile kernel
+    size_t planes_off = 0;
+    if (dtype == LF_F32) {
+        if ((long long)B * H * T * 8 / 256 >= (1LL << 31))
+            return fail(LF_E_UNSUPPORTED, "fp32 problem too large for the plane split");
+        planes_off = (scratch_bytes + 255) / 256 * 256;
+        scratch_bytes = planes_off + 2 * nbytes;
+    }
 
     // ---- HIP work
-    if (P.n_g > 0) {
+    P.kp = k;
+    P.vp = v;
+    if (scratch_bytes > 0) {
+        int *cnt = nullptr;
         char *ws = nullptr;
-        lf_status_t st = workspace(ws_bytes, stream, &ws);
+        lf_status_t st = workspace(cnt_bytes, scratch_bytes, stream, &cnt, &ws);
         if (st != LF_OK) return st;
-        P.counter = (int *)ws;
-        P.part = (float *)(ws + counter_bytes(B, H));
+        if (P.n_g > 0) {
+            P.counter = cnt;
+            P.part = (float *)ws;
+        }
+        if (dtype == LF_F32) {
+            P.kp = ws + planes_off;
+            P.vp = ws + planes_off + nbytes;
+        }
     }
     hipError_t e = lfk_launch(&P, dtype == LF_BF16, stream);
     if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));

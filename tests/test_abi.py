@@ -83,7 +83,7 @@ BAD = [
     ("bad_dtype", dict(dtype=7), lf.LF_E_UNSUPPORTED),
     ("too_many_heads", dict(H=129, dil=None), lf.LF_E_UNSUPPORTED),
     ("too_many_globals", dict(T=4096, g=list(range(600)), ng=600), lf.LF_E_UNSUPPORTED),
-    ("T_too_long", dict(T=(1 << 24) + 1), lf.LF_E_UNSUPPORTED),
+    ("T_too_long", dict(T=1 << 24), lf.LF_E_UNSUPPORTED),
 ]
 
 

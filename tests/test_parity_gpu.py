@@ -198,3 +198,29 @@ def test_rejected_call_leaves_out_untouched():
     assert e.value.status == lf.LF_E_INVALID
     torch.cuda.synchronize()
     assert torch.all(out == 3.0)
+
+
+def test_workspace_reuse_across_dtypes_and_shapes():
+    """Calls of different dtype and shape share one stream's workspace: an
+    fp32 call without globals (K/V planes in scratch), then calls with
+    globals whose B*H grows (completion counters must still read zero), each
+    against the oracle, with `out` prefilled with NaN so a row the kernel
+    never writes shows up."""
+    cases = [
+        dict(seed=71, B=1, H=2, T=700, dtype="f32", r=40, n_global=0, pad="none"),
+        dict(seed=72, B=1, H=3, T=500, dtype="bf16", r=30, n_global=40, pad="none"),
+        dict(seed=73, B=3, H=5, T=400, dtype="bf16", r=20, n_global=70, pad="right"),
+        dict(seed=74, B=2, H=2, T=600, dtype="f32", r=50, n_global=5, pad="random"),
+        dict(seed=75, B=4, H=7, T=300, dtype="bf16", r=10, n_global=3, pad="none"),
+    ]
+    for c in cases:
+        inp = W.random_case(c.pop("seed"), **c, max_dil=3)
+        q, k, v = (x.to("cuda:0") for x in (inp.q, inp.k, inp.v))
+        kpm = None if inp.key_padding_mask is None else inp.key_padding_mask.to("cuda:0")
+        out = torch.full_like(q, float("nan"))
+        lf.attn_fwd(q, k, v, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm, out=out)
+        torch.cuda.synchronize()
+        err = max_err(out, oracle_full(inp))
+        dt = "f32" if inp.q.dtype == torch.float32 else "bf16"
+        print(f"  {tuple(inp.q.shape)} {dt} n_g={len(set(inp.global_idx))}: max abs err {err:.3e}", flush=True)
+        assert err <= TOL[dt]
