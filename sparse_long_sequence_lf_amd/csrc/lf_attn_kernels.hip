@@ -448,7 +448,7 @@ __device__ __forceinline__ void block_pv(WaveState<NP>& W, const f32x16& s, cons
 // ---------------------------------------------------------------------------
 // The tile kernel.
 
-template <int QB, int KS, typename ET, typename OT>
+template <int QB, int KS, typename ET, typename OT, bool PAD>
 __global__ __launch_bounds__(64 * QB * KS) __attribute__((amdgpu_waves_per_eu(LFK_WAVES_PER_EU)))
 void tile_kernel(const Params P) {
     static_assert(QB == 2 && KS == 2, "four waves: two phases of two query blocks");
@@ -489,7 +489,7 @@ void tile_kernel(const Params P) {
 
     const size_t head_off = (size_t)tk.bh * P.T * D;
     const ET* __restrict__ Qg = (const ET*)P.q + head_off;
-    const uint8_t* __restrict__ padrow = P.pad ? P.pad + (size_t)tk.b * P.T : nullptr;
+    const uint8_t* __restrict__ padrow = PAD ? P.pad + (size_t)tk.b * P.T : nullptr;
     // kernel-argument scalars used inside the loop live in registers (a value
     // select between an LDS table entry and a kernel argument would otherwise
     // become a flat load, which waits on every load in flight)
@@ -497,7 +497,7 @@ void tile_kernel(const Params P) {
     const uint32_t head_bytes = (uint32_t)T * ROWB;
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((const char*)P.kp + (size_t)tk.bh * head_bytes, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc((const char*)P.vp + (size_t)tk.bh * head_bytes, head_bytes);
-    const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, padrow ? (uint32_t)T : 0u);
+    const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, PAD ? (uint32_t)T : 0u);
 
     // ---- this wave's 32 queries
     const int mq0 = tk.m0 + 32 * qb;   // first query (class index, or global slot)
@@ -524,19 +524,42 @@ void tile_kernel(const Params P) {
     }
 
     // ---- block list: band (or dense) blocks, then global-key blocks; stage s
-    // holds blocks 2s and 2s+1
-    const int ngb = tk.kind == 0 ? cdiv(P.n_g, KBLK) : 0;
-    const int nblk = tk.nband + ngb;
+    // holds blocks 2s and 2s+1, and this wave works on block jb = 2s + ph
+    const int nb = tk.nband;
+    const int ngb = tk.kind == 0 ? cdiv(n_g, KBLK) : 0;
+    const int nblk = nb + ngb;
     const int NS = cdiv(nblk, 2);
+    const int sb_end = (nb - ph + 1) >> 1;       // steps [0, sb_end): band (or dense) blocks
+    int s_lo = 0, s_hi = -1;                     // band steps with keys for this wave's queries
+    int si_lo = 0, si_hi = -1;                   // band steps whose block needs no mask
+    int sg_end = sb_end;                         // steps [sb_end, sg_end): global-key blocks
+    if (wave_active) {
+        int j_lo = 0, j_hi = nb - 1, ji_lo = 0, ji_hi;
+        if (tk.kind == 0) {
+            j_lo = wb_lo - tk.kb_lo;
+            j_hi = wb_hi - tk.kb_lo;
+            // key0 = 32 (kb_lo + jb) >= mq0 + 31 - r, key0 + 31 <= mq0 + r, key0 + 32 <= key_end
+            ji_lo = ((mq0 + 31 - r + 31) >> 5) - tk.kb_lo;
+            ji_hi = min((mq0 + r - 31) >> 5, (tk.key_end - 32) >> 5) - tk.kb_lo;
+        } else {
+            ji_hi = ((tk.key_end - 32) >> 5) - tk.kb_lo;
+        }
+        s_lo = max(0, (j_lo - ph + 1) >> 1);
+        s_hi = min(sb_end - 1, (j_hi - ph) >> 1);
+        si_lo = max(0, (ji_lo - ph + 1) >> 1);
+        si_hi = min(sb_end - 1, (ji_hi - ph) >> 1);
+        sg_end = (nblk - ph + 1) >> 1;
+    }
+    auto live_of = [&](int s) -> bool { return s < sb_end ? (s >= s_lo && s <= s_hi) : (s < sg_end); };
 
     // ---- global-key tables (band tasks): positions, class indices, and per
     // global block the slots that are no key (unused or padded)
     if (ngb > 0) {
         for (int base = 64 * wave; base < ngb * KBLK; base += NT) {
             const int slot = base + lane;
-            const bool inr = slot < P.n_g;
-            const int pos = inr ? P.glob[slot] : P.T;
-            const bool padded = inr && padrow && padrow[pos] != 0;
+            const bool inr = slot < n_g;
+            const int pos = inr ? P.glob[slot] : T;
+            const bool padded = PAD && inr && padrow[pos] != 0;
             int cls = kNotInClass;
             const int dpos = pos - tk.c;
             if (inr && dpos >= 0) {
@@ -556,74 +579,85 @@ void tile_kernel(const Params P) {
         __syncthreads();
     }
 
-    // memory position of row `row` of block jb (T for no row: reads zero)
-    auto row_pos = [&](int jb, int row) -> uint32_t {
-        if (jb < tk.nband) {
-            const int pos = tk.c + tk.delta * ((tk.kb_lo + jb) * KBLK + row);
-            return (uint32_t)min(pos, T);
-        }
-        const int slot = (jb - tk.nband) * KBLK + row;
+    // ---- loads.  Waves 0/1 bring the K rows of blocks 0/1 of a stage (lane
+    // p: row p/2), waves 2/3 their V rows (lane p: rows p/4 and 16 + p/4).
+    // Band rows of stage s sit 64*delta positions after those of stage 0.
+    const int bw = wave & 1;
+    const int rowA = wave < 2 ? (lane >> 1) : (lane >> 2);
+    const int rowB = 16 + (lane >> 2);
+    const uint32_t colA = wave < 2 ? 16u * ((lane & 1) ^ ((rowA >> 3) & 1)) : 16u * (lane & 3);
+    const uint32_t colB = 16u * (lane & 3);
+    const int row0 = tk.c + tk.delta * (tk.kb_lo + bw) * KBLK;   // position of row 0 of this wave's stage-0 block
+    const int pos_step = 2 * KBLK * tk.delta;
+    const int posA0 = row0 + tk.delta * rowA, posB0 = row0 + tk.delta * rowB;
+    const int padpos0 = row0 + tk.delta * (lane & 31);
+    auto global_pos = [&](int slot) -> uint32_t {
         const int g = gpos[min(slot, LF_MAX_GLOBALS - 1)];
         return (uint32_t)(slot < n_g ? g : T);
     };
-
-    // Loads of stage s into ring slot s % 3: waves 0/1 bring the K rows of
-    // blocks 0/1, waves 2/3 their V rows.
-    auto issue_stage = [&](int s) {
-        const int b = wave & 1;
-        const int jb = 2 * s + b;
+    auto issue_stage = [&](int s, int off) {
+        const int jb = 2 * s + bw;
         if (jb >= nblk) return;
-        char* dst = smem + (s % RG::NBUF) * RG::STAGE + b * RG::BLK;
+        char* dst = smem + off + bw * RG::BLK;
+        uint32_t voA, voB;
+        if (jb < nb) {
+            const int d = s * pos_step;
+            voA = (uint32_t)min(posA0 + d, T) * ROWB + colA;
+            voB = (uint32_t)min(posB0 + d, T) * ROWB + colB;
+        } else {
+            const int sl0 = (jb - nb) * KBLK;
+            voA = global_pos(sl0 + rowA) * ROWB + colA;
+            voB = global_pos(sl0 + rowB) * ROWB + colB;
+        }
         if (wave < 2) {
-            const int row = lane >> 1;
-            const uint32_t voff = row_pos(jb, row) * ROWB + 16 * ((lane & 1) ^ ((row >> 3) & 1));
 #pragma unroll
             for (int p = 0; p < NP; p++)
 #pragma unroll
                 for (int ks = 0; ks < 4; ks++)
-                    load_lds16(rk, dst + p * RG::PLANE + ks * 1024, voff, 32 * ks + 128 * p);
+                    load_lds16(rk, dst + p * RG::PLANE + ks * 1024, voA, 32 * ks + 128 * p);
         } else {
 #pragma unroll
-            for (int hf = 0; hf < 2; hf++) {
-                const int row = 16 * hf + (lane >> 2);
-                const uint32_t voff = row_pos(jb, row) * ROWB + 16 * (lane & 3);
+            for (int p = 0; p < NP; p++)
 #pragma unroll
-                for (int p = 0; p < NP; p++)
-#pragma unroll
-                    for (int cb = 0; cb < 2; cb++)
-                        load_lds16(rv, dst + p * RG::PLANE + 4096 + cb * 2048 + hf * 1024, voff, 64 * cb + 128 * p);
-            }
+                for (int cb = 0; cb < 2; cb++) {
+                    load_lds16(rv, dst + p * RG::PLANE + 4096 + cb * 2048, voA, 64 * cb + 128 * p);
+                    load_lds16(rv, dst + p * RG::PLANE + 4096 + cb * 2048 + 1024, voB, 64 * cb + 128 * p);
+                }
         }
+    };
+    // mask word slot of the ring slot at byte offset `off`
+    auto maskw_at = [&](int off, int blk) -> uint32_t* {
+        return maskw + (off / RG::STAGE) * 2 + blk;
     };
 
     // With padding: waves 0/1 read the padding bytes of their block's rows
     // (lanes 0..31) one step ahead ...
     auto load_pad = [&](int s) -> uint32_t {
-        if (!padrow || wave >= 2) return 0u;
-        const int jb = 2 * s + wave;
-        if (jb >= tk.nband) return 0u;
-        return __builtin_amdgcn_raw_buffer_load_b8(rpad, row_pos(jb, lane & 31), 0, 0);
+        if (wave >= 2) return 0u;
+        const int jb = 2 * s + bw;
+        if (jb >= nb) return 0u;
+        return __builtin_amdgcn_raw_buffer_load_b8(rpad, min(padpos0 + s * pos_step, T), 0, 0);
     };
     // ... and once the stage has landed, publish its mask word and zero the V
     // rows of keys that are not real (so that NaN or Inf stored in padded
     // positions cannot reach the products).
-    auto fix_stage = [&](int s, uint32_t padv) {
-        if (!padrow || wave >= 2) return;
-        const int jb = 2 * s + wave;
+    auto fix_stage = [&](int s, int off, uint32_t padv) {
+        if (wave >= 2) return;
+        const int jb = 2 * s + bw;
         if (jb >= nblk) return;
         uint32_t badw;
-        if (jb < tk.nband) {
+        if (jb < nb) {
             const uint32_t padbits = (uint32_t)__ballot(lane < 32 && padv != 0u);
             const int valid = tk.key_end - (tk.kb_lo + jb) * KBLK;
             badw = padbits | (valid >= KBLK ? 0u : (valid <= 0 ? 0xffffffffu : (0xffffffffu << valid)));
         } else {
-            badw = gbad[jb - tk.nband];
+            badw = gbad[jb - nb];
         }
-        if (lane == 0) maskw[(s % RG::NBUF) * 2 + wave] = badw;
+        if (lane == 0) *maskw_at(off, bw) = badw;
         if (badw != 0u) {
             const int row = lane >> 1, cb = lane & 1;
             if ((badw >> row) & 1u) {
-                char* vrow = smem + (s % RG::NBUF) * RG::STAGE + wave * RG::BLK + 4096 + cb * 2048 + row * 64;
+                char* vrow = smem + off + bw * RG::BLK + 4096 + cb * 2048 + row * 64;
                 const u32x4 z = {0, 0, 0, 0};
 #pragma unroll
                 for (int p = 0; p < NP; p++)
@@ -631,25 +665,6 @@ void tile_kernel(const Params P) {
                     for (int j = 0; j < 4; j++) *(u32x4*)(vrow + p * RG::PLANE + 16 * j) = z;
             }
         }
-    };
-
-    // does this wave's block of stage s hold keys for its queries?
-    auto live_of = [&](int s) -> bool {
-        const int jb = 2 * s + ph;
-        if (!wave_active || jb >= nblk) return false;
-        if (jb < tk.nband) {
-            const int kb = tk.kb_lo + jb;
-            return tk.kind == 1 || (kb >= wb_lo && kb <= wb_hi);
-        }
-        return true;
-    };
-    // mask word of this wave's block of stage s
-    auto block_bad = [&](int s) -> uint32_t {
-        const int jb = 2 * s + ph;
-        if (jb >= tk.nband) return gbad[jb - tk.nband];
-        if (padrow) return maskw[(s % RG::NBUF) * 2 + ph];
-        const int valid = tk.key_end - (tk.kb_lo + jb) * KBLK;
-        return valid >= KBLK ? 0u : (valid <= 0 ? 0xffffffffu : (0xffffffffu << valid));
     };
 
     WaveState<NP> W;
@@ -660,38 +675,16 @@ void tile_kernel(const Params P) {
     W.kbase = ph * RG::BLK + lq * 32 + ((lg ^ ((lq >> 3) & 1)) << 4);
     W.vbase = ph * RG::BLK + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
-    // masking of this wave's block of stage s (scores in sc); false when the
-    // block holds no key for this wave's queries.  Reads LDS (mask word,
-    // global-key classes), so it runs before the step's loads are issued.
-    auto mask_block = [&](int s, f32x16& sc) -> bool {
-        if (!live_of(s)) return false;
-        const uint32_t bad = block_bad(s);
-        if (bad == 0xffffffffu) return false;
-        const int jb = 2 * s + ph;
-        int kind, key0 = 0;
-        const int* gc = gcls;
-        if (jb < tk.nband) {
-            key0 = (tk.kb_lo + jb) * KBLK;
-            const bool interior = tk.kind == 0 && bad == 0u && key0 >= mq0 + 31 - r && key0 + 31 <= mq0 + r;
-            kind = tk.kind == 1 ? kMaskBad : (interior ? kMaskNone : kMaskBand);
-        } else {
-            kind = kMaskGlobal;
-            gc = gcls + (jb - tk.nband) * KBLK;
-        }
-        apply_mask(sc, kind, bad, key0, gc, m_me, r, lg);
-        return true;
-    };
-
     // ---- prologue: stages 0 and 1 in flight, then Q
-    issue_stage(0);
-    const uint32_t pad0 = load_pad(0);
-    uint32_t pad_pending = 0u;
+    issue_stage(0, 0);
+    uint32_t pad0 = 0u, pad_pending = 0u;
+    if constexpr (PAD) pad0 = load_pad(0);
     if (NS > 1) {
-        issue_stage(1);
-        pad_pending = load_pad(1);
+        issue_stage(1, RG::STAGE);
+        if constexpr (PAD) pad_pending = load_pad(1);
     }
     {
-        const bool my_pad = (my_pos >= 0 && padrow) ? padrow[my_pos] != 0 : false;
+        const bool my_pad = (PAD && my_pos >= 0) ? padrow[my_pos] != 0 : false;
         const bool ok = my_pos >= 0 && !my_pad;
         const ET* qrow = Qg + (size_t)(ok ? my_pos : 0) * D;
 #pragma unroll
@@ -713,35 +706,74 @@ void tile_kernel(const Params P) {
         }
     }
     barrier_lds_loads();               // stages 0 and 1 have landed
-    fix_stage(0, pad0);
-    f32x16 sc = {};
-    if (live_of(0)) sc = block_scores<NP>(W, load_k<NP>(W, smem));
+    if constexpr (PAD) fix_stage(0, 0, pad0);
+    f32x16 sa, sb;                     // scores of the current / next block (roles alternate)
+    if (live_of(0)) sa = block_scores<NP>(W, load_k<NP>(W, smem));
 
-    // ---- main loop: one barrier per step.  Every LDS read of a step comes
-    // before that step's loads into LDS are issued: the compiler makes any
-    // LDS read that follows such a load wait for it.
-    for (int s = 0; s < NS; s++) {
+    // One step: this wave's block of stage s is in ring slot oc, stage s+1 in
+    // on, and stage s+2 goes to onn.  Every LDS read of a step comes before
+    // that step's loads into LDS are issued: the compiler makes any LDS read
+    // that follows such a load wait for it.
+    auto step = [&](int s, int oc, int on, int onn, f32x16& scur, f32x16& snext) {
         barrier_lds_loads();           // stage s+1 landed; stage s fixed up; stage s-1 no longer read
+        const bool cur = live_of(s);
         const bool next = s + 1 < NS && live_of(s + 1);
+        const bool band = s < sb_end;
         KFrag<NP> kf;
-        if (next) kf = load_k<NP>(W, smem + ((s + 1) % RG::NBUF) * RG::STAGE);
-        const bool cur = mask_block(s, sc);
+        if (next) kf = load_k<NP>(W, smem + on);
         VFrag<NP> vf;
-        if (cur) vf = load_v<NP>(W, smem + (s % RG::NBUF) * RG::STAGE);
-        if (s + 1 < NS) fix_stage(s + 1, pad_pending);
+        uint32_t bad = 0u;
+        if (cur) {
+            vf = load_v<NP>(W, smem + oc);
+            if (band) {
+                if constexpr (PAD) {
+                    bad = *maskw_at(oc, ph);
+                } else {
+                    const int valid = tk.key_end - (tk.kb_lo + 2 * s + ph) * KBLK;
+                    bad = valid >= KBLK ? 0u : (0xffffffffu << max(valid, 0));
+                    if (valid <= 0) bad = 0xffffffffu;
+                }
+            } else {
+                // global keys: their mask needs LDS, so it is applied before the loads go out
+                const int jg = 2 * s + ph - nb;
+                apply_mask(scur, kMaskGlobal, gbad[jg], 0, gcls + jg * KBLK, m_me, r, lg);
+            }
+        }
+        if constexpr (PAD) {
+            if (s + 1 < NS) fix_stage(s + 1, on, pad_pending);
+        }
         uint32_t pad_next = 0u;
         if (s + 2 < NS) {
-            issue_stage(s + 2);
-            pad_next = load_pad(s + 2);
+            issue_stage(s + 2, onn);
+            if constexpr (PAD) pad_next = load_pad(s + 2);
         }
-        f32x16 sn = {};
-        if (next) sn = block_scores<NP>(W, kf);
-        if (cur) {
-            update_max<NP>(W, sc);
-            block_pv<NP>(W, sc, vf);
+        if (next) snext = block_scores<NP>(W, kf);
+        if (cur && bad != 0xffffffffu) {
+            if (band) {
+                const bool interior = s >= si_lo && s <= si_hi && (!PAD || bad == 0u);
+                if (!interior) {
+                    const int key0 = (tk.kb_lo + 2 * s + ph) * KBLK;
+                    apply_mask(scur, tk.kind == 0 ? kMaskBand : kMaskBad, bad, key0, gcls, m_me, r, lg);
+                }
+            }
+            update_max<NP>(W, scur);
+            block_pv<NP>(W, scur, vf);
         }
-        sc = sn;
         pad_pending = pad_next;
+    };
+
+    // ---- main loop: one barrier per step; ring slots rotate
+    {
+        int o0 = 0, o1 = RG::STAGE, o2 = 2 * RG::STAGE;
+        for (int s = 0; s < NS; s += 2) {
+            step(s, o0, o1, o2, sa, sb);
+            if (s + 1 >= NS) break;
+            step(s + 1, o1, o2, o0, sb, sa);
+            const int t = o0;
+            o0 = o2;
+            o2 = o1;
+            o1 = t;
+        }
     }
     __syncthreads();
 
@@ -929,13 +961,20 @@ extern "C" hipError_t lfk_launch(const lfk::Params* P, int dtype_bf16, void* str
     hipStream_t s = (hipStream_t)stream;
     constexpr int QB = LFK_QB, KS = LFK_KS;
     const int grid = lfk_grid(P);
+    const bool pad = P->pad != nullptr;
     if (dtype_bf16) {
-        hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, __bf16, uint16_t>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
+        if (pad)
+            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, __bf16, uint16_t, true>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
+        else
+            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, __bf16, uint16_t, false>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
     } else {
         const long long chunks = (long long)P->B * P->H * P->T * 8;
         hipLaunchKernelGGL(lfk::split_planes_kernel, dim3((unsigned)((chunks + 255) / 256), 2), dim3(256), 0, s,
                            (const float*)P->k, (const float*)P->v, (uint16_t*)P->kp, (uint16_t*)P->vp, chunks);
-        hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, float, float>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
+        if (pad)
+            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, float, float, true>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
+        else
+            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, float, float, false>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
     }
     return hipGetLastError();
 }
