@@ -177,7 +177,7 @@ struct Task {
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 template <int QB>
-__device__ __forceinline__ Task decode_task(const Params& P, int t) {
+__device__ __forceinline__ Task decode_task(const Plan& P, int t) {
     constexpr int BM = 32 * QB;
     Task k;
     if (t < P.n_band_tasks) {
@@ -313,44 +313,47 @@ __device__ __forceinline__ f32x16 block_scores(const WaveState<NP>& W, const KFr
     return s;
 }
 
-// Masking (chosen at run time, wave-uniform, so one code path serves every
-// block kind).  Bit t of `bad` is set when key row t of the block is not a
-// real key (past the sequence, class or split end, padded, or an unused
-// global slot).
-enum MaskKind { kMaskNone = 0, kMaskBand = 1, kMaskGlobal = 2, kMaskBad = 3 };
+// Masking.  Lane l holds the scores of keys 8*(i>>2) + 4*(l/32) + (i&3) of
+// the block in accumulator element i.  Bit t of a block's `bad` word is set
+// when key row t is not a real key (past the sequence, class or split end,
+// padded, or an unused global slot).
 
-__device__ __forceinline__ void apply_mask(f32x16& s, int kind, uint32_t bad, int key0, const int* gcls,
-                                           int m, int r, int lg) {
-    if (kind == kMaskNone) return;
-    // this lane's 16 keys are rows 8*(i>>2) + 4*lg + (i&3): bit i of badl
-    // belongs to accumulator element i
-    const uint32_t sh = bad >> (4 * lg);
-    const uint32_t badl = (sh & 0xfu) | ((sh >> 4) & 0xf0u) | ((sh >> 8) & 0xf00u) | ((sh >> 12) & 0xf000u);
-    if (kind == kMaskBand) {
-        // keys key0 + kl with kl = 8*(i>>2) + 4*lg + (i&3) must lie in [m - r, m + r]
-        const int lo = m - r - key0 - 4 * lg, hi = m + r - key0 - 4 * lg;
+// keep bits of this lane's 16 elements from a 32-bit row word
+__device__ __forceinline__ uint32_t lane_bits(uint32_t rows, int lg) {
+    const uint32_t sh = rows >> (4 * lg);
+    return (sh & 0xfu) | ((sh >> 4) & 0xf0u) | ((sh >> 8) & 0xf00u) | ((sh >> 12) & 0xf000u);
+}
+
+// band block whose rows are all real keys: keep kc in [lo, lo + 2r], where
+// kc is the element's key row minus 4*lg and lo = m - r - key0 - 4*lg
+__device__ __forceinline__ void mask_window(f32x16& s, int lo, int two_r) {
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const int kc = 8 * (i >> 2) + (i & 3);
-            const bool ok = ((badl >> i) & 1u) == 0u && kc >= lo && kc <= hi;
+    for (int i = 0; i < 16; i++) {
+        const int kc = 8 * (i >> 2) + (i & 3);
+        s[i] = (uint32_t)(kc - lo) <= (uint32_t)two_r ? s[i] : kNegInf;
+    }
+}
+
+// keep the elements whose bit is set in keep16
+__device__ __forceinline__ void mask_bits(f32x16& s, uint32_t keep16) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) s[i] = ((keep16 >> i) & 1u) ? s[i] : kNegInf;
+}
+
+// global-key block: drop unused / padded slots and keys already inside this
+// query's window (the band counts those)
+__device__ __forceinline__ void mask_global(f32x16& s, uint32_t bad, const int* gcls, int m, int r, int lg) {
+    const uint32_t badl = lane_bits(bad, lg);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+        const u32x4 g4 = *(const u32x4*)(gcls + 8 * q4 + 4 * lg);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int i = 4 * q4 + e;
+            const int dk = (int)g4[e] - m;
+            const bool ok = ((badl >> i) & 1u) == 0u && (uint32_t)(dk + r) > (uint32_t)(2 * r);
             s[i] = ok ? s[i] : kNegInf;
         }
-    } else if (kind == kMaskGlobal) {
-        // a global key already inside this query's window is counted by the band
-#pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-            const u32x4 g4 = *(const u32x4*)(gcls + 8 * q4 + 4 * lg);
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int i = 4 * q4 + e;
-                const int dk = (int)g4[e] - m;
-                const bool ok = ((badl >> i) & 1u) == 0u && (uint32_t)(dk + r) > (uint32_t)(2 * r);
-                s[i] = ok ? s[i] : kNegInf;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; i++) s[i] = ((badl >> i) & 1u) ? kNegInf : s[i];
     }
 }
 
@@ -450,7 +453,7 @@ __device__ __forceinline__ void block_pv(WaveState<NP>& W, const f32x16& s, cons
 
 template <int QB, int KS, typename ET, typename OT, bool PAD>
 __global__ __launch_bounds__(64 * QB * KS) __attribute__((amdgpu_waves_per_eu(LFK_WAVES_PER_EU)))
-void tile_kernel(const Params P) {
+void tile_kernel(const Args A) {
     static_assert(QB == 2 && KS == 2, "four waves: two phases of two query blocks");
     constexpr int NT = 64 * QB * KS;
     constexpr int NP = Elem<ET>::NP;
@@ -459,6 +462,7 @@ void tile_kernel(const Params P) {
     constexpr int MERGE_BYTES = (KS - 1) * QB * 64 * 36 * 4;
     static_assert(MERGE_BYTES <= RG::NBUF * RG::STAGE, "merge area inside the ring");
     __shared__ __attribute__((aligned(16))) char smem[RG::bytes];
+    const Plan& P = *A.plan;
     const int* gpos = (const int*)(smem + RG::gposOff);
     const int* gcls = (const int*)(smem + RG::gclsOff);
     const uint32_t* gbad = (const uint32_t*)(smem + RG::gbadOff);
@@ -488,15 +492,17 @@ void tile_kernel(const Params P) {
     const int lg = lane >> 5;
 
     const size_t head_off = (size_t)tk.bh * P.T * D;
-    const ET* __restrict__ Qg = (const ET*)P.q + head_off;
-    const uint8_t* __restrict__ padrow = PAD ? P.pad + (size_t)tk.b * P.T : nullptr;
+    const ET* __restrict__ Qg = (const ET*)A.q + head_off;
+    const uint8_t* __restrict__ padrow = PAD ? A.pad + (size_t)tk.b * P.T : nullptr;
     // kernel-argument scalars used inside the loop live in registers (a value
     // select between an LDS table entry and a kernel argument would otherwise
     // become a flat load, which waits on every load in flight)
     const int T = P.T, n_g = P.n_g, r = P.r;
     const uint32_t head_bytes = (uint32_t)T * ROWB;
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((const char*)P.kp + (size_t)tk.bh * head_bytes, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc((const char*)P.vp + (size_t)tk.bh * head_bytes, head_bytes);
+    const void* kplanes = NP == 1 ? A.k : P.kp;   // bf16 input is its own plane
+    const void* vplanes = NP == 1 ? A.v : P.vp;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((const char*)kplanes + (size_t)tk.bh * head_bytes, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc((const char*)vplanes + (size_t)tk.bh * head_bytes, head_bytes);
     const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, PAD ? (uint32_t)T : 0u);
 
     // ---- this wave's 32 queries
@@ -719,24 +725,20 @@ void tile_kernel(const Params P) {
         const bool cur = live_of(s);
         const bool next = s + 1 < NS && live_of(s + 1);
         const bool band = s < sb_end;
+        const int jb = 2 * s + ph;
         KFrag<NP> kf;
         if (next) kf = load_k<NP>(W, smem + on);
         VFrag<NP> vf;
         uint32_t bad = 0u;
         if (cur) {
             vf = load_v<NP>(W, smem + oc);
-            if (band) {
-                if constexpr (PAD) {
-                    bad = *maskw_at(oc, ph);
-                } else {
-                    const int valid = tk.key_end - (tk.kb_lo + 2 * s + ph) * KBLK;
-                    bad = valid >= KBLK ? 0u : (0xffffffffu << max(valid, 0));
-                    if (valid <= 0) bad = 0xffffffffu;
-                }
+            if (!band) {
+                bad = gbad[jb - nb];
+            } else if constexpr (PAD) {
+                bad = *maskw_at(oc, ph);
             } else {
-                // global keys: their mask needs LDS, so it is applied before the loads go out
-                const int jg = 2 * s + ph - nb;
-                apply_mask(scur, kMaskGlobal, gbad[jg], 0, gcls + jg * KBLK, m_me, r, lg);
+                const int valid = tk.key_end - (tk.kb_lo + jb) * KBLK;
+                bad = valid <= 0 ? 0xffffffffu : (valid >= KBLK ? 0u : (0xffffffffu << valid));
             }
         }
         if constexpr (PAD) {
@@ -749,12 +751,16 @@ void tile_kernel(const Params P) {
         }
         if (next) snext = block_scores<NP>(W, kf);
         if (cur && bad != 0xffffffffu) {
-            if (band) {
-                const bool interior = s >= si_lo && s <= si_hi && (!PAD || bad == 0u);
-                if (!interior) {
-                    const int key0 = (tk.kb_lo + 2 * s + ph) * KBLK;
-                    apply_mask(scur, tk.kind == 0 ? kMaskBand : kMaskBad, bad, key0, gcls, m_me, r, lg);
+            // one masking point (the global-key mask reads LDS; global-key
+            // stages come last, where steps issue loads only past 128 globals)
+            if (!band) {
+                mask_global(scur, bad, gcls + (jb - nb) * KBLK, m_me, r, lg);
+            } else if (!(s >= si_lo && s <= si_hi && bad == 0u)) {
+                if (tk.kind == 0) {
+                    const int key0 = (tk.kb_lo + jb) * KBLK;
+                    mask_window(scur, m_me - r - key0 - 4 * lg, 2 * r);
                 }
+                if (bad != 0u) mask_bits(scur, ~lane_bits(bad, lg));
             }
             update_max<NP>(W, scur);
             block_pv<NP>(W, scur, vf);
@@ -830,7 +836,7 @@ void tile_kernel(const Params P) {
             if (gpos[lo] == my_pos) return;
         }
         const bool my_pad = padrow ? padrow[my_pos] != 0 : false;
-        OT* orow = (OT*)P.out + head_off + (size_t)my_pos * D;
+        OT* orow = (OT*)A.out + head_off + (size_t)my_pos * D;
         const float inv = (my_pad || l == 0.f) ? 0.f : 1.0f / l;
 #pragma unroll
         for (int cb = 0; cb < 2; cb++) {
@@ -894,7 +900,7 @@ void tile_kernel(const Params P) {
     const size_t stride = (size_t)P.g_pad * (D + 2);
     for (int gi = wave; gi < P.n_g; gi += NW) {
         const int pos = P.glob[gi];
-        OT* orow = (OT*)P.out + head_off + (size_t)pos * D;
+        OT* orow = (OT*)A.out + head_off + (size_t)pos * D;
         const bool padded = padrow && padrow[pos] != 0;
         const uint32_t* base = (const uint32_t*)P.part + ((size_t)tk.bh * P.n_split * P.g_pad + gi) * (D + 2);
         const bool mine = lane < P.n_split;
@@ -952,29 +958,30 @@ __global__ __launch_bounds__(256) void split_planes_kernel(const float* __restri
 
 // grid: the task slots of the 8 dies, each die holding ceil(n/8) band and
 // ceil(n/8) global-row slots
-extern "C" int lfk_grid(const lfk::Params* P) {
+extern "C" int lfk_grid(const lfk::Plan* P) {
     const int nb = P->n_band_tasks, ng = P->n_tasks - P->n_band_tasks;
     return 8 * ((nb + 7) / 8 + (ng + 7) / 8);
 }
 
-extern "C" hipError_t lfk_launch(const lfk::Params* P, int dtype_bf16, void* stream) {
+// A: kernel argument (A->plan is the device copy of *P); P: host copy of the plan
+extern "C" hipError_t lfk_launch(const lfk::Args* A, const lfk::Plan* P, int dtype_bf16, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     constexpr int QB = LFK_QB, KS = LFK_KS;
     const int grid = lfk_grid(P);
-    const bool pad = P->pad != nullptr;
+    const bool pad = A->pad != nullptr;
     if (dtype_bf16) {
         if (pad)
-            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, __bf16, uint16_t, true>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
+            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, __bf16, uint16_t, true>), dim3(grid), dim3(64 * QB * KS), 0, s, *A);
         else
-            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, __bf16, uint16_t, false>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
+            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, __bf16, uint16_t, false>), dim3(grid), dim3(64 * QB * KS), 0, s, *A);
     } else {
         const long long chunks = (long long)P->B * P->H * P->T * 8;
         hipLaunchKernelGGL(lfk::split_planes_kernel, dim3((unsigned)((chunks + 255) / 256), 2), dim3(256), 0, s,
-                           (const float*)P->k, (const float*)P->v, (uint16_t*)P->kp, (uint16_t*)P->vp, chunks);
+                           (const float*)A->k, (const float*)A->v, (uint16_t*)P->kp, (uint16_t*)P->vp, chunks);
         if (pad)
-            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, float, float, true>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
+            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, float, float, true>), dim3(grid), dim3(64 * QB * KS), 0, s, *A);
         else
-            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, float, float, false>), dim3(grid), dim3(64 * QB * KS), 0, s, *P);
+            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, float, float, false>), dim3(grid), dim3(64 * QB * KS), 0, s, *A);
     }
     return hipGetLastError();
 }

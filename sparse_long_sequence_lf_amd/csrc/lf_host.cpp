@@ -19,7 +19,7 @@
 #include "lf_attn.h"
 #include "lf_kernels.h"
 
-extern "C" hipError_t lfk_launch(const lfk::Params *P, int dtype_bf16, void *stream);
+extern "C" hipError_t lfk_launch(const lfk::Args *A, const lfk::Plan *P, int dtype_bf16, void *stream);
 
 namespace {
 
@@ -51,14 +51,18 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 //    else is ever stored there.
 //  * scratch: the global-row partials and, for fp32 input, the bf16 hi/lo
 //    planes of K and V; no contents carry over between calls.
+//  * plan: the device copy of the call's lfk::Plan, with a host shadow of
+//    what it holds; it is re-uploaded (in stream order) only when it changes.
 //
-// Both only grow; an old buffer is released after the stream has drained it.
+// Buffers only grow; an old buffer is released after the stream has drained it.
 struct Buffer {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
 struct Workspace {
-    Buffer counters, scratch;
+    Buffer counters, scratch, plan;
+    lfk::Plan shadow;
+    bool shadow_valid = false;
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, void *>, Workspace> g_ws;
@@ -92,18 +96,35 @@ lf_status_t grow(Buffer &b, size_t bytes, bool zero, void *stream) {
     return LF_OK;
 }
 
-lf_status_t workspace(size_t counter_bytes, size_t scratch_bytes, void *stream, int **counters, char **scratch) {
+Workspace *workspace_for(void *stream) {
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(LF_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-    std::lock_guard<std::mutex> lock(g_ws_mu);
-    Workspace &w = g_ws[std::make_pair(dev, stream)];
-    lf_status_t st = grow(w.counters, counter_bytes, true, stream);
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    return &g_ws[std::make_pair(dev, stream)];
+}
+
+// Device copy of *P on this stream's workspace; uploads only when it differs
+// from the last upload.  An upload cannot be recorded into a graph (its source
+// is a host temporary), so a changed plan during stream capture is refused.
+lf_status_t upload_plan(Workspace &w, const lfk::Plan &P, void *stream, const lfk::Plan **dev_plan) {
+    lf_status_t st = grow(w.plan, sizeof(lfk::Plan), false, stream);
     if (st != LF_OK) return st;
-    st = grow(w.scratch, scratch_bytes, false, stream);
-    if (st != LF_OK) return st;
-    *counters = (int *)w.counters.ptr;
-    *scratch = (char *)w.scratch.ptr;
+    if (!w.shadow_valid || std::memcmp(&w.shadow, &P, sizeof P) != 0) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
+        if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+        if (cs != hipStreamCaptureStatusNone)
+            return fail(LF_E_UNSUPPORTED,
+                        "the call's shape, dilation or global set differs from the previous call on this stream "
+                        "during stream capture; make one identical call outside capture first");
+        e = hipMemcpyAsync(w.plan.ptr, &P, sizeof P, hipMemcpyHostToDevice, (hipStream_t)stream);
+        if (e != hipSuccess) {
+            w.shadow_valid = false;
+            return fail(LF_E_HIP, "plan upload: %s", hipGetErrorString(e));
+        }
+        std::memcpy(&w.shadow, &P, sizeof P);
+        w.shadow_valid = true;
+    }
+    *dev_plan = (const lfk::Plan *)w.plan.ptr;
     return LF_OK;
 }
 
@@ -155,10 +176,8 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
     // ---- plan
     constexpr int QB = LFK_QB;
     constexpr int BM = 32 * QB;
-    lfk::Params P;
+    lfk::Plan P;
     std::memset(&P, 0, sizeof P);
-    P.q = q; P.k = k; P.v = v; P.out = out;
-    P.pad = key_padding_mask;
     P.B = B; P.H = H; P.T = T;
     P.r = r < T ? r : T;  // |i - j| < T always, so larger radii change nothing
     P.n_g = (int)G.size();
@@ -204,15 +223,17 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
     }
 
     // ---- HIP work
-    P.kp = k;
-    P.vp = v;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    Workspace *w = workspace_for(stream);
+    if (!w) return fail(LF_E_HIP, "hipGetDevice failed");
     if (scratch_bytes > 0) {
-        int *cnt = nullptr;
-        char *ws = nullptr;
-        lf_status_t st = workspace(cnt_bytes, scratch_bytes, stream, &cnt, &ws);
+        lf_status_t st = grow(w->counters, cnt_bytes, true, stream);
         if (st != LF_OK) return st;
+        st = grow(w->scratch, scratch_bytes, false, stream);
+        if (st != LF_OK) return st;
+        char *ws = (char *)w->scratch.ptr;
         if (P.n_g > 0) {
-            P.counter = cnt;
+            P.counter = (int *)w->counters.ptr;
             P.part = (float *)ws;
         }
         if (dtype == LF_F32) {
@@ -220,7 +241,12 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
             P.vp = ws + planes_off + nbytes;
         }
     }
-    hipError_t e = lfk_launch(&P, dtype == LF_BF16, stream);
+    lfk::Args A;
+    A.q = q; A.k = k; A.v = v; A.out = out;
+    A.pad = key_padding_mask;
+    lf_status_t st = upload_plan(*w, P, stream, &A.plan);
+    if (st != LF_OK) return st;
+    hipError_t e = lfk_launch(&A, &P, dtype == LF_BF16, stream);
     if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
     return LF_OK;
 }

@@ -1,4 +1,4 @@
-// lf_kernels.h -- the launch record shared by the host planner
+// lf_kernels.h -- the launch records shared by the host planner
 // (lf_host.cpp) and the gfx950 kernels (lf_attn_kernels.hip).  Internal to
 // liblfattn.so; the public interface is include/lf_attn.h.
 #ifndef LF_KERNELS_H
@@ -20,12 +20,12 @@
 
 namespace lfk {
 
-// Passed by value as the kernel argument (fits the 4 KiB kernarg limit).
-struct Params {
-    const void *q, *k, *v;
-    const void *kp, *vp;     // K and V as bf16 planes: [B*H][T][NP][64] (bf16 input: k and v)
-    void *out;
-    const uint8_t *pad;      // [B][T] or null
+// Everything about a call except the tensors: shape, per-head tables, the
+// global set and workspace pointers.  Lives in device memory (one copy per
+// (device, stream) workspace), re-uploaded only when it changes, so the
+// kernel argument stays small (launch cost grows with argument size).
+struct Plan {
+    const void *kp, *vp;     // K and V as bf16 planes [B*H][T][2][64] (fp32 input only)
     float *part;             // global-row partials [B*H][n_split][g_pad][66]
     int *counter;            // [B*H] finished global-row workgroups; zero between calls
     int B, H, T, r;          // r already clamped to T
@@ -40,6 +40,14 @@ struct Params {
     int head_start[LF_MAX_HEADS + 1];  // band-task prefix over heads
     uint16_t dil[LF_MAX_HEADS];
     int32_t glob[LF_MAX_GLOBALS];
+};
+
+// The kernel argument: the call's tensors and the device copy of its plan.
+struct Args {
+    const void *q, *k, *v;
+    void *out;
+    const uint8_t *pad;      // [B][T] or null
+    const Plan *plan;
 };
 
 }  // namespace lfk
