@@ -66,6 +66,8 @@ constexpr int KBLK = 32;                  // keys per block (one S^T tile)
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kNotInClass = -(1 << 30);
 constexpr int kRawBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format, no swizzle
+constexpr int kCoherent = 16;                  // buffer cache policy sc1: coherent across the dies' L2s
+constexpr int kRecBytes = 272;                 // global-row partial record: O[64], m, l, pad[2]
 
 // log2(e) / sqrt(64): scores are taken to base 2 with the 1/sqrt(d) scale.
 constexpr float kScaleLog2 = 0.18033688011112042f;
@@ -259,14 +261,6 @@ __device__ __forceinline__ float halves_sum(float x) {
                                                     __builtin_bit_cast(uint32_t, x), false, false);
     const f32x2 f = __builtin_bit_cast(f32x2, r);
     return f[0] + f[1];
-}
-
-// agent-scope relaxed atomic accesses (coherent across the XCDs' L2s)
-__device__ __forceinline__ void store_coherent(uint32_t* p, float x) {
-    __hip_atomic_store(p, __builtin_bit_cast(uint32_t, x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const uint32_t* p) {
-    return __builtin_bit_cast(float, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // ---------------------------------------------------------------------------
@@ -858,28 +852,30 @@ void tile_kernel(const Args A) {
         return;
     }
 
-    // ---- global rows: write this split's (max, sum, O) for each global slot.
-    // Partials cross dies (each XCD has its own L2), so they are written and
-    // read as agent-scope relaxed atomics, which go to the coherent memory
-    // side without writing back or invalidating whole L2s the way a
-    // device-wide fence does.
+    // ---- global rows: write this split's partial for each global slot, a
+    // 272-byte record [O[0..63], m, l, 0, 0].  Partials cross dies (each XCD
+    // has its own L2), so they are written and read with the agent-coherent
+    // cache policy (sc1) instead of fences, which would write back and
+    // invalidate whole L2s.
+    const uint32_t stride = (uint32_t)P.g_pad * kRecBytes;          // bytes between splits of a slot
+    const __amdgpu_buffer_rsrc_t rpart =
+        buffer_rsrc((const char*)P.part + (size_t)tk.bh * P.n_split * stride, (uint32_t)P.n_split * stride);
     const int slot = mq0 + lq;
-    if (writer && slot < P.n_g) {
-        uint32_t* part = (uint32_t*)P.part + (((size_t)tk.bh * P.n_split + tk.split) * P.g_pad + slot) * (D + 2);
-        if (lg == 0) {
-            store_coherent(part + 0, W.ms);
-            store_coherent(part + 1, l);
-        }
+    if (writer && slot < n_g) {
+        const uint32_t rec = (uint32_t)tk.split * stride + (uint32_t)slot * kRecBytes;
 #pragma unroll
         for (int cb = 0; cb < 2; cb++) {
             const f32x16& oc = cb ? W.o1 : W.o0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const int c0 = 32 * cb + 8 * j + 4 * lg;
-#pragma unroll
-                for (int e = 0; e < 4; e++) store_coherent(part + 2 + c0 + e, oc[4 * j + e]);
+                const f32x4 o4 = {oc[4 * j], oc[4 * j + 1], oc[4 * j + 2], oc[4 * j + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), rpart,
+                                                       rec + 4 * (32 * cb + 8 * j + 4 * lg), 0, kCoherent);
             }
         }
+        if (lg == 0)
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, (f32x2){W.ms, l}), rpart, rec + 256, 0,
+                                                  kCoherent);
     }
     // The last of the n_split * n_ggroups workgroups of head (b, h) to finish
     // rescales and adds the partials of every global row of that head.  The
@@ -893,39 +889,39 @@ void tile_kernel(const Args A) {
     }
     __syncthreads();
     if (*flag == 0) return;
-    // one wave per global row; lanes first span the splits (max and sum of the
-    // rescaled partial sums), then the 64 channels (rescaled partial outputs,
-    // loads issued back to back)
-    constexpr int NW = NT / 64;
-    const size_t stride = (size_t)P.g_pad * (D + 2);
-    for (int gi = wave; gi < P.n_g; gi += NW) {
-        const int pos = P.glob[gi];
-        OT* orow = (OT*)A.out + head_off + (size_t)pos * D;
-        const bool padded = padrow && padrow[pos] != 0;
-        const uint32_t* base = (const uint32_t*)P.part + ((size_t)tk.bh * P.n_split * P.g_pad + gi) * (D + 2);
-        const bool mine = lane < P.n_split;
-        const float m_s = mine ? load_coherent(base + lane * stride) : kNegInf;
-        const float l_s = mine ? load_coherent(base + lane * stride + 1) : 0.f;
-        float M = m_s;
+    // Each thread combines 4 channels of one global row over all splits; all
+    // of its loads are issued before any is used (splits past n_split repeat
+    // the last one and get weight 0).
+    for (int task = tid; task < n_g * 16; task += NT) {
+        const int gi = task >> 4, c4 = task & 15;
+        f32x2 ml[16];
+        f32x4 o[16];
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, off));
-        const float w_s = (m_s == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_s - M);
-        float Lsum = l_s * w_s;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) Lsum += __shfl_xor(Lsum, off);
-        float O = 0.f;
-        for (int s0 = 0; s0 < P.n_split; s0 += 16) {
-            float ov[16];
-#pragma unroll
-            for (int j = 0; j < 16; j++) ov[j] = (s0 + j < P.n_split) ? load_coherent(base + (s0 + j) * stride + 2 + lane) : 0.f;
-#pragma unroll
-            for (int j = 0; j < 16; j++) O += ov[j] * __shfl(w_s, s0 + j);
+        for (int sp = 0; sp < 16; sp++) {
+            const uint32_t rec = (uint32_t)min(sp, P.n_split - 1) * stride + (uint32_t)gi * kRecBytes;
+            ml[sp] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rpart, rec + 256, 0, kCoherent));
+            o[sp] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rpart, rec + 16 * c4, 0, kCoherent));
         }
-        const float y = (padded || !(Lsum > 0.f)) ? 0.f : O / Lsum;
+        float M = kNegInf;
+#pragma unroll
+        for (int sp = 0; sp < 16; sp++) M = __builtin_fmaxf(M, ml[sp][0]);
+        float L = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sp = 0; sp < 16; sp++) {
+            const float w = (sp < P.n_split && ml[sp][0] != kNegInf) ? __builtin_amdgcn_exp2f(ml[sp][0] - M) : 0.f;
+            L += ml[sp][1] * w;
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[e] += o[sp][e] * w;
+        }
+        const int pos = P.glob[gi];
+        const bool padded = padrow && padrow[pos] != 0;
+        const float inv = (padded || !(L > 0.f)) ? 0.f : 1.0f / L;
+        OT* orow = (OT*)A.out + head_off + (size_t)pos * D + 4 * c4;
         if constexpr (sizeof(OT) == 2) {
-            orow[lane] = (OT)(pack_bf16(y, 0.f) & 0xffffu);
+            *(u32x2*)orow = (u32x2){pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
         } else {
-            orow[lane] = y;
+            *(f32x4*)orow = (f32x4){acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
         }
     }
     if (tid == 0) __hip_atomic_store(P.counter + tk.bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

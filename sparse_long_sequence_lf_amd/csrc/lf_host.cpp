@@ -206,7 +206,7 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
         P.n_split = (int)cdiv(T, P.split_len);  // <= 16: the combine spans splits with one wave's lanes
         n_glob_tasks = (long long)B * H * P.n_split * P.n_ggroups;
         cnt_bytes = (size_t)B * H * sizeof(int);
-        scratch_bytes = (size_t)B * H * P.n_split * P.g_pad * (LF_HEAD_DIM + 2) * sizeof(float);
+        scratch_bytes = (size_t)B * H * P.n_split * P.g_pad * 272;  // 272-byte partial records
     }
     if (n_band + n_glob_tasks > (1LL << 30))
         return fail(LF_E_UNSUPPORTED, "problem needs %lld workgroups", n_band + n_glob_tasks);

@@ -26,7 +26,7 @@ namespace lfk {
 // kernel argument stays small (launch cost grows with argument size).
 struct Plan {
     const void *kp, *vp;     // K and V as bf16 planes [B*H][T][2][64] (fp32 input only)
-    float *part;             // global-row partials [B*H][n_split][g_pad][66]
+    float *part;             // global-row partials [B*H][n_split][g_pad] x 272 B: O[64], m, l, 0, 0
     int *counter;            // [B*H] finished global-row workgroups; zero between calls
     int B, H, T, r;          // r already clamped to T
     int n_g;                 // distinct globals (sorted ascending in glob)
