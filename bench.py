@@ -16,7 +16,6 @@ Prints one JSON line:
 calibration kernel for rocprofv3 HBM-byte counters) and prints no JSON.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -27,21 +26,11 @@ sys.path.insert(0, ROOT)
 
 HEADLINE = "bf16-b1h12t4096-r256-g1"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
-KERNEL_SOURCES = ["sparse_long_sequence_lf_amd/csrc/lf_attn_kernels.hip",
-                  "sparse_long_sequence_lf_amd/csrc/lf_kernels.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tile_kernel_hbm_traffic.json")
-COPY_BYTES = 1 << 28        # calibration copy: 256 MiB read + 256 MiB written
-
-
-def kernel_sha():
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload):
+    from sparse_long_sequence_lf_amd.profiling import kernel_sha
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or was taken on other kernel sources."""
     try:
@@ -67,7 +56,7 @@ def cpu_baseline(inp, flops, seconds):
                                 inp.key_padding_mask, return_threads=True)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 64:
+        if el >= seconds or reps >= 1024:
             break
     return {"value": flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole workload ({inp.q.shape[0] * inp.q.shape[1] * inp.q.shape[2]} query rows), "
@@ -111,6 +100,7 @@ def main():
         for _ in range(args.warmup + args.steps):
             call()
         torch.cuda.synchronize()
+        from sparse_long_sequence_lf_amd.profiling import COPY_BYTES
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -167,6 +157,18 @@ def main():
     except Exception as ex:  # graph capture is an optimisation of the timing loop only
         print(f"bench.py: graph capture unavailable ({ex}); reporting the eager loop", file=sys.stderr)
 
+    # the kernel's own average duration: an event pair around each launch
+    # (bf16: one kernel per call; fp32: the plane split and the tile kernel)
+    n_each = min(args.steps, 200)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_each)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms_launch = sum(a.elapsed_time(b) for a, b in ev) / n_each
+
     use_graph = ms_graph is not None and graph_ok
     ms = ms_graph if use_graph else ms_eager
     tflops = flops / (ms * 1e-3) / 1e12
@@ -194,9 +196,13 @@ def main():
         "ms_per_step_eager": round(ms_eager, 5),
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
         "wall_s_eager_loop": round(wall, 4),
-        "roofline": {"bound": "mfma", "kernel": "lfk::tile_kernel", "achieved": round(tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "lfk::tile_kernel",
+                     "achieved": round(flops / (ms_launch * 1e-3) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (ms_launch * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
+                     "launch_us": round(ms_launch * 1e3, 3),
+                     "algorithmic_flops": flops,
                      "algorithmic_bytes": metrics.algorithmic_bytes(B, H, T, d, q.element_size(),
                                                                     inp.key_padding_mask)},
     }

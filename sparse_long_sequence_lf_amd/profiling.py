@@ -1,0 +1,152 @@
+"""Summaries of rocprofv3 output for the tile kernel (the text files under
+profiles/ and the HBM-traffic record bench.py reads).
+
+    python -m sparse_long_sequence_lf_amd.profiling stats DIR --workload W --cmd "..." --out FILE
+    python -m sparse_long_sequence_lf_amd.profiling traffic FETCH_DIR WRITE_DIR --workload W \
+        --cmd "..." --out-json profiles/tile_kernel_hbm_traffic.json --out-txt FILE
+
+DIR, FETCH_DIR, WRITE_DIR are rocprofv3 output directories written with
+`-f csv` (kernel trace with --stats; one --pmc FETCH_SIZE run; one --pmc
+WRITE_SIZE run) of `bench.py --profile-mode`, whose calls end with one copy of
+COPY_BYTES bytes.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the tile
+kernel are scaled by what the same counter reads for that copy: a copy of N
+bytes fetches N and writes N.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+from typing import Dict, List
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+KERNEL_SOURCES = ["sparse_long_sequence_lf_amd/csrc/lf_attn_kernels.hip",
+                  "sparse_long_sequence_lf_amd/csrc/lf_kernels.h"]
+KERNEL_NAME = "tile_kernel"
+COPY_BYTES = 1 << 28   # the calibration copy in bench.py --profile-mode
+
+
+def kernel_sha() -> str:
+    """Digest of the kernel sources: a traffic record taken on other sources is stale."""
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise SystemExit(f"no file matches {pattern}")
+    return hits[0]
+
+
+def kernel_durations(d: str) -> Dict[str, List[int]]:
+    """Kernel name -> list of dispatch durations (ns) from a kernel trace."""
+    out: Dict[str, List[int]] = {}
+    with open(_one(os.path.join(d, "**", "*kernel_trace.csv"))) as f:
+        for r in csv.DictReader(f):
+            out.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
+
+
+def counter_per_dispatch(d: str, counter: str) -> Dict[int, tuple]:
+    """Dispatch id -> (kernel name, counter value summed over its instances)."""
+    out: Dict[int, list] = {}
+    with open(_one(os.path.join(d, "**", "*counter_collection.csv"))) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            e = out.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])
+            e[1] += float(r["Counter_Value"])
+    return {k: tuple(v) for k, v in out.items()}
+
+
+def _copy_value(vals: Dict[int, tuple]) -> float:
+    # the calibration copy is the largest non-tile dispatch of the run
+    cands = [v for (name, v) in vals.values() if KERNEL_NAME not in name]
+    if not cands:
+        raise SystemExit("no calibration copy dispatch found")
+    return max(cands)
+
+
+def cmd_stats(a) -> None:
+    durs = kernel_durations(a.dir)
+    lines = [f"# rocprofv3 kernel trace: {a.workload}", "", "command:", f"    {a.cmd}", "",
+             f"{'kernel':70s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        short = name if len(name) <= 70 else name[:67] + "..."
+        lines.append(f"{short:70s} {len(v):6d} {statistics.mean(v) / 1e3:9.2f} {min(v) / 1e3:9.2f} {max(v) / 1e3:9.2f}")
+    tile = [x for n, v in durs.items() if KERNEL_NAME in n for x in v]
+    if tile:
+        lines += ["", f"tile kernel average duration: {statistics.mean(tile) / 1e3:.2f} us over {len(tile)} dispatches",
+                  f"kernel sources sha: {kernel_sha()}"]
+    text = "\n".join(lines) + "\n"
+    with open(a.out, "w") as f:
+        f.write(text)
+    sys.stdout.write(text)
+
+
+def cmd_traffic(a) -> None:
+    fetch = counter_per_dispatch(a.fetch_dir, "FETCH_SIZE")
+    write = counter_per_dispatch(a.write_dir, "WRITE_SIZE")
+    f_copy, w_copy = _copy_value(fetch), _copy_value(write)
+    f_scale = COPY_BYTES / (f_copy * 1024.0)
+    w_scale = COPY_BYTES / (w_copy * 1024.0)
+    f_tile = [v for (n, v) in fetch.values() if KERNEL_NAME in n]
+    w_tile = [v for (n, v) in write.values() if KERNEL_NAME in n]
+    if not f_tile or not w_tile:
+        raise SystemExit("no tile kernel dispatches in the counter runs")
+    fetch_b = statistics.mean(f_tile) * 1024.0 * f_scale
+    write_b = statistics.mean(w_tile) * 1024.0 * w_scale
+    rec = {"kernel_sha": kernel_sha(), "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
+           "fetch_bytes": int(round(fetch_b)), "write_bytes": int(round(write_b)),
+           "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+           "dispatches": [len(f_tile), len(w_tile)], "command": a.cmd}
+    table = {}
+    if os.path.exists(a.out_json):
+        with open(a.out_json) as f:
+            table = json.load(f)
+    table[a.workload] = rec
+    with open(a.out_json, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
+    text = (f"# HBM traffic of the tile kernel: {a.workload}\n\ncommand (one run per counter):\n    {a.cmd}\n\n"
+            f"calibration copy of {COPY_BYTES} B: FETCH_SIZE {f_copy:.0f} KiB, WRITE_SIZE {w_copy:.0f} KiB\n"
+            f"scale factors (bytes per counted KiB / 1024): fetch {f_scale:.5f}, write {w_scale:.5f}\n\n"
+            f"tile kernel per launch ({len(f_tile)} / {len(w_tile)} dispatches):\n"
+            f"    fetched {fetch_b / 1e6:.3f} MB, written {write_b / 1e6:.3f} MB, total {(fetch_b + write_b) / 1e6:.3f} MB\n"
+            f"kernel sources sha: {kernel_sha()}\n")
+    with open(a.out_txt, "w") as f:
+        f.write(text)
+    sys.stdout.write(text)
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--workload", required=True)
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--out-json", required=True)
+    t.add_argument("--out-txt", required=True)
+    a = ap.parse_args(argv)
+    cmd_stats(a) if a.what == "stats" else cmd_traffic(a)
+
+
+if __name__ == "__main__":
+    main()
