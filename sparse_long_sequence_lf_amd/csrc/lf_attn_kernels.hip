@@ -583,10 +583,20 @@ void tile_kernel(const Args A) {
     // p: row p/2), waves 2/3 their V rows (lane p: rows p/4 and 16 + p/4).
     // Band rows of stage s sit 64*delta positions after those of stage 0.
     const int bw = wave & 1;
-    const int rowA = wave < 2 ? (lane >> 1) : (lane >> 2);
-    const int rowB = 16 + (lane >> 2);
-    const uint32_t colA = wave < 2 ? 16u * ((lane & 1) ^ ((rowA >> 3) & 1)) : 16u * (lane & 3);
-    const uint32_t colB = 16u * (lane & 3);
+    const bool kwave = wave < 2;
+    const int rowA = kwave ? (lane >> 1) : (lane >> 2);
+    const int rowB = kwave ? rowA : 16 + (lane >> 2);
+    const uint32_t colA = kwave ? 16u * ((lane & 1) ^ ((rowA >> 3) & 1)) : 16u * (lane & 3);
+    const uint32_t colB = kwave ? colA : 16u * (lane & 3);
+    // piece i of this wave's load of a block: LDS offset, scalar byte offset;
+    // odd pieces of the V loaders take the second row (voB)
+    const __amdgpu_buffer_rsrc_t rkv = kwave ? rk : rv;
+    int pdst[4], psoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        pdst[i] = kwave ? i * 1024 : 4096 + (i >> 1) * 2048 + (i & 1) * 1024;
+        psoff[i] = kwave ? 32 * i : 64 * (i >> 1);
+    }
     const int row0 = tk.c + tk.delta * (tk.kb_lo + bw) * KBLK;   // position of row 0 of this wave's stage-0 block
     const int pos_step = 2 * KBLK * tk.delta;
     const int posA0 = row0 + tk.delta * rowA, posB0 = row0 + tk.delta * rowB;
@@ -609,21 +619,11 @@ void tile_kernel(const Args A) {
             voA = global_pos(sl0 + rowA) * ROWB + colA;
             voB = global_pos(sl0 + rowB) * ROWB + colB;
         }
-        if (wave < 2) {
 #pragma unroll
-            for (int p = 0; p < NP; p++)
+        for (int p = 0; p < NP; p++)
 #pragma unroll
-                for (int ks = 0; ks < 4; ks++)
-                    load_lds16(rk, dst + p * RG::PLANE + ks * 1024, voA, 32 * ks + 128 * p);
-        } else {
-#pragma unroll
-            for (int p = 0; p < NP; p++)
-#pragma unroll
-                for (int cb = 0; cb < 2; cb++) {
-                    load_lds16(rv, dst + p * RG::PLANE + 4096 + cb * 2048, voA, 64 * cb + 128 * p);
-                    load_lds16(rv, dst + p * RG::PLANE + 4096 + cb * 2048 + 1024, voB, 64 * cb + 128 * p);
-                }
-        }
+            for (int i = 0; i < 4; i++)
+                load_lds16(rkv, dst + p * RG::PLANE + pdst[i], (i & 1) ? voB : voA, psoff[i] + 128 * p);
     };
     // mask word slot of the ring slot at byte offset `off`
     auto maskw_at = [&](int off, int blk) -> uint32_t* {
@@ -717,24 +717,21 @@ void tile_kernel(const Args A) {
     auto step = [&](int s, int oc, int on, int onn, f32x16& scur, f32x16& snext) {
         barrier_lds_loads();           // stage s+1 landed; stage s fixed up; stage s-1 no longer read
         const bool cur = live_of(s);
-        const bool next = s + 1 < NS && live_of(s + 1);
         const bool band = s < sb_end;
         const int jb = 2 * s + ph;
-        KFrag<NP> kf;
-        if (next) kf = load_k<NP>(W, smem + on);
-        VFrag<NP> vf;
-        uint32_t bad = 0u;
-        if (cur) {
-            vf = load_v<NP>(W, smem + oc);
-            if (!band) {
-                bad = gbad[jb - nb];
-            } else if constexpr (PAD) {
-                bad = *maskw_at(oc, ph);
-            } else {
-                const int valid = tk.key_end - (tk.kb_lo + jb) * KBLK;
-                bad = valid <= 0 ? 0xffffffffu : (valid >= KBLK ? 0u : (0xffffffffu << valid));
-            }
+        // fragment reads and the next block's score MFMAs run unconditionally
+        // (a dead block's scores are never used): fewer branches per step
+        const KFrag<NP> kf = load_k<NP>(W, smem + on);
+        const VFrag<NP> vf = load_v<NP>(W, smem + oc);
+        uint32_t bad;
+        if constexpr (PAD) {
+            bad = band ? *maskw_at(oc, ph) : gbad[min(max(jb - nb, 0), LF_MAX_GLOBALS / KBLK - 1)];
+        } else {
+            const int valid = tk.key_end - (tk.kb_lo + jb) * KBLK;
+            const uint32_t rb = valid <= 0 ? 0xffffffffu : (valid >= KBLK ? 0u : (0xffffffffu << valid));
+            bad = band ? rb : gbad[min(max(jb - nb, 0), LF_MAX_GLOBALS / KBLK - 1)];
         }
+        if (!cur) bad = 0xffffffffu;
         if constexpr (PAD) {
             if (s + 1 < NS) fix_stage(s + 1, on, pad_pending);
         }
@@ -743,10 +740,12 @@ void tile_kernel(const Args A) {
             issue_stage(s + 2, onn);
             if constexpr (PAD) pad_next = load_pad(s + 2);
         }
-        if (next) snext = block_scores<NP>(W, kf);
-        if (cur && bad != 0xffffffffu) {
-            // one masking point (the global-key mask reads LDS; global-key
-            // stages come last, where steps issue loads only past 128 globals)
+        snext = block_scores<NP>(W, kf);
+        // one masking point (the global-key mask reads LDS; global-key stages
+        // come last, where steps issue loads only past 128 globals).  A block
+        // with no key for this wave's queries is skipped: its LDS may hold
+        // anything (zero weights times NaN would still be NaN).
+        if (bad != 0xffffffffu) {
             if (!band) {
                 mask_global(scur, bad, gcls + (jb - nb) * KBLK, m_me, r, lg);
             } else if (!(s >= si_lo && s <= si_hi && bad == 0u)) {
