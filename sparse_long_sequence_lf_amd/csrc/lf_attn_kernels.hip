@@ -462,17 +462,19 @@ void tile_kernel(const Args A) {
     const uint32_t* gbad = (const uint32_t*)(smem + RG::gbadOff);
     uint32_t* maskw = (uint32_t*)(smem + RG::maskOff);
 
-    // ---- which task.  Each of the 8 dies (blockIdx % 8) takes a contiguous
-    // eighth of the band tasks (neighbouring tiles share keys in its L2), then
-    // an eighth of the global-row tasks.
+    // ---- which task.  Each of the 8 dies (blockIdx % 8) takes an eighth of
+    // the global-row tasks first (they are shorter and light on memory, so
+    // they overlap the band tiles' first loads instead of trailing them), then
+    // a contiguous eighth of the band tasks (neighbouring tiles share keys in
+    // its L2).
     const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
     int task_id;
     {
         const int nb = P.n_band_tasks, ng = P.n_tasks - P.n_band_tasks;
         const int nb_x = (nb >> 3) + (xcd < (nb & 7)), nb_o = xcd * (nb >> 3) + min(xcd, nb & 7);
         const int ng_x = (ng >> 3) + (xcd < (ng & 7)), ng_o = xcd * (ng >> 3) + min(xcd, ng & 7);
-        if (slot_in_xcd < nb_x) task_id = nb_o + slot_in_xcd;
-        else if (slot_in_xcd - nb_x < ng_x) task_id = nb + ng_o + (slot_in_xcd - nb_x);
+        if (slot_in_xcd < ng_x) task_id = nb + ng_o + slot_in_xcd;
+        else if (slot_in_xcd - ng_x < nb_x) task_id = nb_o + (slot_in_xcd - ng_x);
         else return;
     }
     const Task tk = decode_task<QB>(P, task_id);
