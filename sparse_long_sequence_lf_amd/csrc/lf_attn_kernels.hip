@@ -66,6 +66,7 @@ constexpr int KBLK = 32;                  // keys per block (one S^T tile)
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kNotInClass = -(1 << 30);
 constexpr int kRawBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format, no swizzle
+constexpr uint32_t kPastEnd = 0xFFFFFF00u;     // buffer offset past any resource's end (reads zero)
 constexpr int kCoherent = 16;                  // buffer cache policy sc1: coherent across the dies' L2s
 constexpr int kRecBytes = 272;                 // global-row partial record: O[64], m, l, pad[2]
 
@@ -554,33 +555,6 @@ void tile_kernel(const Args A) {
     }
     auto live_of = [&](int s) -> bool { return s < sb_end ? (s >= s_lo && s <= s_hi) : (s < sg_end); };
 
-    // ---- global-key tables (band tasks): positions, class indices, and per
-    // global block the slots that are no key (unused or padded)
-    if (ngb > 0) {
-        for (int base = 64 * wave; base < ngb * KBLK; base += NT) {
-            const int slot = base + lane;
-            const bool inr = slot < n_g;
-            const int pos = inr ? P.glob[slot] : T;
-            const bool padded = PAD && inr && padrow[pos] != 0;
-            int cls = kNotInClass;
-            const int dpos = pos - tk.c;
-            if (inr && dpos >= 0) {
-                const int q = dpos / tk.delta;
-                if (q * tk.delta == dpos) cls = q;
-            }
-            if (slot < LF_MAX_GLOBALS) {
-                ((int*)gpos)[slot] = pos;
-                ((int*)gcls)[slot] = cls;
-            }
-            const uint64_t badm = __ballot(!inr || padded);
-            if (lane == 0 && base < LF_MAX_GLOBALS) {
-                ((uint32_t*)gbad)[base >> 5] = (uint32_t)badm;
-                if (base + 32 < LF_MAX_GLOBALS) ((uint32_t*)gbad)[(base >> 5) + 1] = (uint32_t)(badm >> 32);
-            }
-        }
-        __syncthreads();
-    }
-
     // ---- loads.  Waves 0/1 bring the K rows of blocks 0/1 of a stage (lane
     // p: row p/2), waves 2/3 their V rows (lane p: rows p/4 and 16 + p/4).
     // Band rows of stage s sit 64*delta positions after those of stage 0.
@@ -677,38 +651,78 @@ void tile_kernel(const Args A) {
     W.kbase = ph * RG::BLK + lq * 32 + ((lg ^ ((lq >> 3) & 1)) << 4);
     W.vbase = ph * RG::BLK + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
-    // ---- prologue: stages 0 and 1 in flight, then Q
-    issue_stage(0, 0);
-    uint32_t pad0 = 0u, pad_pending = 0u;
-    if constexpr (PAD) pad0 = load_pad(0);
-    if (NS > 1) {
-        issue_stage(1, RG::STAGE);
-        if constexpr (PAD) pad_pending = load_pad(1);
-    }
+    // Q rows through a buffer resource: a lane with no query reads past its
+    // end and gets zeros, so nothing consumes the loaded registers before the
+    // barrier that waits for the stages (a padded query keeps its row; the
+    // epilogues write zeros for it)
+    u32x4 qraw[4 * NP];
     {
-        const bool my_pad = (PAD && my_pos >= 0) ? padrow[my_pos] != 0 : false;
-        const bool ok = my_pos >= 0 && !my_pad;
-        const ET* qrow = Qg + (size_t)(ok ? my_pos : 0) * D;
+        constexpr uint32_t esz = sizeof(ET);
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(Qg, (uint32_t)T * D * esz);
+        const uint32_t qoff = my_pos >= 0 ? (uint32_t)my_pos * D * esz : kPastEnd;
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-            const int c0 = 16 * ks + 8 * lg;
-            if constexpr (NP == 1) {
-                const u32x4 x = *(const u32x4*)(qrow + c0);
-                W.qh[ks] = as_bf16x8(ok ? x : (u32x4){0, 0, 0, 0});
-            } else {
-                Raw32 x;
-                x.a = *(const u32x4*)(qrow + c0);
-                x.b = *(const u32x4*)(qrow + c0 + 4);
-                if (!ok) { x.a = (u32x4){0, 0, 0, 0}; x.b = x.a; }
-                u32x4 hi, lo;
-                split8(x, hi, lo);
-                W.qh[ks] = as_bf16x8(hi);
-                W.ql[ks] = as_bf16x8(lo);
+        for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+            for (int p = 0; p < NP; p++)
+                qraw[NP * ks + p] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (16 * ks + 8 * lg + 4 * p) * esz, 0, 0));
+    }
+    // ---- prologue: Q and stages 0 and 1 in flight, then the global-key
+    // tables (a global-key block among the first two stages, found only when
+    // the band has fewer than four blocks, is loaded once its table is there)
+    const bool early0 = bw < nb, early1 = NS > 1 && 2 + bw < nb;
+    if (early0) issue_stage(0, 0);
+    if (early1) issue_stage(1, RG::STAGE);
+    uint32_t pad0 = 0u, pad_pending = 0u;
+    if constexpr (PAD) {
+        pad0 = load_pad(0);
+        if (NS > 1) pad_pending = load_pad(1);
+    }
+    // global-key tables (band tasks): positions, class indices, and per
+    // global block the slots that are no key (unused or padded)
+    if (ngb > 0) {
+        for (int base = 64 * wave; base < ngb * KBLK; base += NT) {
+            const int slot = base + lane;
+            const bool inr = slot < n_g;
+            const int pos = inr ? P.glob[slot] : T;
+            const bool padded = PAD && inr && padrow[pos] != 0;
+            int cls = kNotInClass;
+            const int dpos = pos - tk.c;
+            if (inr && dpos >= 0) {
+                const int q = dpos / tk.delta;
+                if (q * tk.delta == dpos) cls = q;
+            }
+            if (slot < LF_MAX_GLOBALS) {
+                ((int*)gpos)[slot] = pos;
+                ((int*)gcls)[slot] = cls;
+            }
+            const uint64_t badm = __ballot(!inr || padded);
+            if (lane == 0 && base < LF_MAX_GLOBALS) {
+                ((uint32_t*)gbad)[base >> 5] = (uint32_t)badm;
+                if (base + 32 < LF_MAX_GLOBALS) ((uint32_t*)gbad)[(base >> 5) + 1] = (uint32_t)(badm >> 32);
             }
         }
+        __syncthreads();
     }
-    barrier_lds_loads();               // stages 0 and 1 have landed
+
+    if (!early0) issue_stage(0, 0);
+    if (NS > 1 && !early1) issue_stage(1, RG::STAGE);
+    barrier_lds_loads();               // Q and stages 0 and 1 have landed
     if constexpr (PAD) fix_stage(0, 0, pad0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+        if constexpr (NP == 1) {
+            W.qh[ks] = as_bf16x8(qraw[ks]);
+        } else {
+            Raw32 x;
+            x.a = qraw[2 * ks];
+            x.b = qraw[2 * ks + 1];
+            u32x4 hi, lo;
+            split8(x, hi, lo);
+            W.qh[ks] = as_bf16x8(hi);
+            W.ql[ks] = as_bf16x8(lo);
+        }
+    }
     f32x16 sa, sb;                     // scores of the current / next block (roles alternate)
     if (live_of(0)) sa = block_scores<NP>(W, load_k<NP>(W, smem));
 
@@ -832,15 +846,17 @@ void tile_kernel(const Args A) {
         }
         const bool my_pad = padrow ? padrow[my_pos] != 0 : false;
         OT* orow = (OT*)A.out + head_off + (size_t)my_pos * D;
-        const float inv = (my_pad || l == 0.f) ? 0.f : 1.0f / l;
+        // a padded query's row is written as zeros, whatever its Q held
+        const bool zero = my_pad || l == 0.f;
+        const float inv = zero ? 0.f : 1.0f / l;
 #pragma unroll
         for (int cb = 0; cb < 2; cb++) {
             const f32x16& oc = cb ? W.o1 : W.o0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int c0 = 32 * cb + 8 * j + 4 * lg;
-                const float y0 = oc[4 * j + 0] * inv, y1 = oc[4 * j + 1] * inv;
-                const float y2 = oc[4 * j + 2] * inv, y3 = oc[4 * j + 3] * inv;
+                const float y0 = zero ? 0.f : oc[4 * j + 0] * inv, y1 = zero ? 0.f : oc[4 * j + 1] * inv;
+                const float y2 = zero ? 0.f : oc[4 * j + 2] * inv, y3 = zero ? 0.f : oc[4 * j + 3] * inv;
                 if constexpr (sizeof(OT) == 2) {
                     const u32x2 w = {pack_bf16(y0, y1), pack_bf16(y2, y3)};
                     *(u32x2*)(orow + c0) = w;
@@ -917,6 +933,7 @@ void tile_kernel(const Args A) {
         }
         const int pos = P.glob[gi];
         const bool padded = padrow && padrow[pos] != 0;
+        if (padded || !(L > 0.f)) acc = (f32x4){0.f, 0.f, 0.f, 0.f};   // zeros even if the partials hold NaN
         const float inv = (padded || !(L > 0.f)) ? 0.f : 1.0f / L;
         OT* orow = (OT*)A.out + head_off + (size_t)pos * D + 4 * c4;
         if constexpr (sizeof(OT) == 2) {

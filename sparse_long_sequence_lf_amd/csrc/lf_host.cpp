@@ -185,7 +185,7 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
     long long start = 0;
     for (int h = 0; h < H; h++) {
         const int delta = dilation ? dilation[h] : 1;
-        P.dil[h] = (uint16_t)delta;
+        P.dil[h] = delta;
         P.head_start[h] = (int)start;
         const long long qq = T / delta, rem = T % delta;
         start += rem * cdiv(qq + 1, BM) + (delta - rem) * cdiv(qq, BM);

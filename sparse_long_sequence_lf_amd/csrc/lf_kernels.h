@@ -38,7 +38,7 @@ struct Plan {
     int uniform_head_tasks;  // band tasks per head when every head has the same count, else 0
     int n_tasks;             // band + global-row tasks
     int head_start[LF_MAX_HEADS + 1];  // band-task prefix over heads
-    uint16_t dil[LF_MAX_HEADS];
+    int32_t dil[LF_MAX_HEADS];      // 32-bit: a head's entry is one scalar load
     int32_t glob[LF_MAX_GLOBALS];
 };
 
