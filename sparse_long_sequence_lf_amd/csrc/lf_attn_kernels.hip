@@ -255,7 +255,7 @@ __device__ __forceinline__ float halves_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
                                                     __builtin_bit_cast(uint32_t, x), false, false);
     const f32x2 f = __builtin_bit_cast(f32x2, r);
-    return __builtin_fmaxf(f[0], f[1]);
+    return __builtin_elementwise_maximum(f[0], f[1]);
 }
 __device__ __forceinline__ float halves_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
@@ -272,6 +272,8 @@ struct WaveState {
     bf16x8 qh[4], ql[4];  // Q^T operands (lo part only for fp32 inputs)
     f32x16 o0, o1;        // O^T: channels 0..31 and 32..63 of this lane's query
     float ms;             // running max in scaled base-2 units
+    float nms;            // -ms, or 0 while ms is -inf (the exponent offset)
+    float thr;            // raw score above which the max must move: (ms + 8) / scale
     float lp;             // this lane's part of the running sum
     int kbase;            // LDS offset of this lane's K operand bytes inside a block
     int vbase;            // LDS offset of this lane's V^T operand bytes inside a block
@@ -357,19 +359,22 @@ __device__ __forceinline__ void mask_global(f32x16& s, uint32_t bad, const int* 
 // grows by more than 2^8.
 template <int NP>
 __device__ __forceinline__ void update_max(WaveState<NP>& W, const f32x16& s) {
+    // maximum (not fmax): NaN-propagating, so no quieting of the MFMA results
     float mx = s[0];
 #pragma unroll
-    for (int i = 1; i < 16; i++) mx = __builtin_fmaxf(mx, s[i]);
+    for (int i = 1; i < 16; i++) mx = __builtin_elementwise_maximum(mx, s[i]);
     mx = halves_max(mx);
-    const float mxs = mx * kScaleLog2;
-    const bool need = mxs > W.ms + 8.0f;
+    const bool need = mx > W.thr;
     if (__ballot(need)) {
+        const float mxs = mx * kScaleLog2;
         const float msn = need ? mxs : W.ms;
         const float alpha = need ? __builtin_amdgcn_exp2f(W.ms - msn) : 1.0f;
 #pragma unroll
         for (int i = 0; i < 16; i++) { W.o0[i] *= alpha; W.o1[i] *= alpha; }
         W.lp *= alpha;
         W.ms = msn;
+        W.nms = msn == kNegInf ? 0.0f : -msn;
+        W.thr = (msn + 8.0f) * (1.0f / kScaleLog2);
     }
 }
 
@@ -399,7 +404,7 @@ __device__ __forceinline__ VFrag<NP> load_v(const WaveState<NP>& W, const char* 
 // p = 2^(s*scale - m) for one block, its row sum, and O^T += V^T P^T
 template <int NP>
 __device__ __forceinline__ void block_pv(WaveState<NP>& W, const f32x16& s, const VFrag<NP>& f) {
-    const float nms = (W.ms == kNegInf) ? 0.0f : -W.ms;
+    const float nms = W.nms;
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], kScaleLog2, nms));
@@ -498,8 +503,6 @@ void tile_kernel(const Args A) {
     const uint32_t head_bytes = (uint32_t)T * ROWB;
     const void* kplanes = NP == 1 ? A.k : P.kp;   // bf16 input is its own plane
     const void* vplanes = NP == 1 ? A.v : P.vp;
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((const char*)kplanes + (size_t)tk.bh * head_bytes, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc((const char*)vplanes + (size_t)tk.bh * head_bytes, head_bytes);
     const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, PAD ? (uint32_t)T : 0u);
 
     // ---- this wave's 32 queries
@@ -566,7 +569,7 @@ void tile_kernel(const Args A) {
     const uint32_t colB = kwave ? colA : 16u * (lane & 3);
     // piece i of this wave's load of a block: LDS offset, scalar byte offset;
     // odd pieces of the V loaders take the second row (voB)
-    const __amdgpu_buffer_rsrc_t rkv = kwave ? rk : rv;
+    const char* kvhead = (const char*)(kwave ? kplanes : vplanes) + (size_t)tk.bh * head_bytes;
     int pdst[4], psoff[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -576,22 +579,37 @@ void tile_kernel(const Args A) {
     const int row0 = tk.c + tk.delta * (tk.kb_lo + bw) * KBLK;   // position of row 0 of this wave's stage-0 block
     const int pos_step = 2 * KBLK * tk.delta;
     const int posA0 = row0 + tk.delta * rowA, posB0 = row0 + tk.delta * rowB;
+    // Band stage s reads through a window that starts s * pos_step rows
+    // further on and ends where the head ends, so that the lane offsets stay
+    // fixed and rows past the end read zeros: scalar work per step, no vector
+    // work.  A step longer than the head is cut to the head (all later rows
+    // read zeros either way).
+    const uint32_t voA0 = (uint32_t)min(posA0, T) * ROWB + colA;
+    const uint32_t voB0 = (uint32_t)min(posB0, T) * ROWB + colB;
+    const uint32_t step_bytes = (uint32_t)min((uint64_t)pos_step * ROWB, (uint64_t)head_bytes);
+    struct Window { const char* base; uint32_t n; };
+    auto advance = [&](Window w) -> Window {
+        return {w.base + step_bytes, w.n > step_bytes ? w.n - step_bytes : 0u};
+    };
     const int padpos0 = row0 + tk.delta * (lane & 31);
     auto global_pos = [&](int slot) -> uint32_t {
         const int g = gpos[min(slot, LF_MAX_GLOBALS - 1)];
         return (uint32_t)(slot < n_g ? g : T);
     };
-    auto issue_stage = [&](int s, int off) {
+    // stage s into the ring slot at byte offset off; w is stage s's window
+    auto issue_stage = [&](int s, int off, Window w) {
         const int jb = 2 * s + bw;
         if (jb >= nblk) return;
         char* dst = smem + off + bw * RG::BLK;
         uint32_t voA, voB;
+        __amdgpu_buffer_rsrc_t rs;
         if (jb < nb) {
-            const int d = s * pos_step;
-            voA = (uint32_t)min(posA0 + d, T) * ROWB + colA;
-            voB = (uint32_t)min(posB0 + d, T) * ROWB + colB;
+            rs = buffer_rsrc(w.base, __builtin_amdgcn_readfirstlane(w.n));
+            voA = voA0;
+            voB = voB0;
         } else {
             const int sl0 = (jb - nb) * KBLK;
+            rs = buffer_rsrc(kvhead, head_bytes);
             voA = global_pos(sl0 + rowA) * ROWB + colA;
             voB = global_pos(sl0 + rowB) * ROWB + colB;
         }
@@ -599,7 +617,7 @@ void tile_kernel(const Args A) {
         for (int p = 0; p < NP; p++)
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                load_lds16(rkv, dst + p * RG::PLANE + pdst[i], (i & 1) ? voB : voA, psoff[i] + 128 * p);
+                load_lds16(rs, dst + p * RG::PLANE + pdst[i], (i & 1) ? voB : voA, psoff[i] + 128 * p);
     };
     // mask word slot of the ring slot at byte offset `off`
     auto maskw_at = [&](int off, int blk) -> uint32_t* {
@@ -647,6 +665,8 @@ void tile_kernel(const Args A) {
     W.o0 = (f32x16){};
     W.o1 = (f32x16){};
     W.ms = kNegInf;
+    W.nms = 0.f;
+    W.thr = kNegInf;
     W.lp = 0.f;
     W.kbase = ph * RG::BLK + lq * 32 + ((lg ^ ((lq >> 3) & 1)) << 4);
     W.vbase = ph * RG::BLK + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
@@ -671,8 +691,10 @@ void tile_kernel(const Args A) {
     // tables (a global-key block among the first two stages, found only when
     // the band has fewer than four blocks, is loaded once its table is there)
     const bool early0 = bw < nb, early1 = NS > 1 && 2 + bw < nb;
-    if (early0) issue_stage(0, 0);
-    if (early1) issue_stage(1, RG::STAGE);
+    const Window w0 = {kvhead, head_bytes}, w1 = advance(w0);
+    Window wn = advance(w1);           // window of stage s+2 in step s
+    if (early0) issue_stage(0, 0, w0);
+    if (early1) issue_stage(1, RG::STAGE, w1);
     uint32_t pad0 = 0u, pad_pending = 0u;
     if constexpr (PAD) {
         pad0 = load_pad(0);
@@ -705,8 +727,8 @@ void tile_kernel(const Args A) {
         __syncthreads();
     }
 
-    if (!early0) issue_stage(0, 0);
-    if (NS > 1 && !early1) issue_stage(1, RG::STAGE);
+    if (!early0) issue_stage(0, 0, w0);
+    if (NS > 1 && !early1) issue_stage(1, RG::STAGE, w1);
     barrier_lds_loads();               // Q and stages 0 and 1 have landed
     if constexpr (PAD) fix_stage(0, 0, pad0);
 #pragma unroll
@@ -735,8 +757,6 @@ void tile_kernel(const Args A) {
         const bool cur = live_of(s);
         const bool band = s < sb_end;
         const int jb = 2 * s + ph;
-        // fragment reads and the next block's score MFMAs run unconditionally
-        // (a dead block's scores are never used): fewer branches per step
         const KFrag<NP> kf = load_k<NP>(W, smem + on);
         const VFrag<NP> vf = load_v<NP>(W, smem + oc);
         uint32_t bad;
@@ -753,9 +773,10 @@ void tile_kernel(const Args A) {
         }
         uint32_t pad_next = 0u;
         if (s + 2 < NS) {
-            issue_stage(s + 2, onn);
+            issue_stage(s + 2, onn, wn);
             if constexpr (PAD) pad_next = load_pad(s + 2);
         }
+        wn = advance(wn);
         snext = block_scores<NP>(W, kf);
         // one masking point (the global-key mask reads LDS; global-key stages
         // come last, where steps issue loads only past 128 globals).  A block
