@@ -30,13 +30,15 @@
 // more than 2^8, which keeps every exponent <= 8 and leaves O / l exact.
 //
 // Key blocks (32 keys) reach LDS straight from memory (buffer_load ... lds,
-// no register staging) through a ring of three stages of two blocks each.
-// Step s of the loop: one barrier (stage s+1 has landed, stage s-1 is free),
-// the loads of stage s+2 go out, the score MFMAs of this wave's block of
-// stage s+1 are issued, and the softmax and PV of its block of stage s run
-// while they execute.  Rows past the end of the head read as zero.  The two
-// "phases" of a query block take the two blocks of each stage and are
-// merged at the end.
+// no register staging) through a ring of two stages of two blocks each.
+// Step s of the loop: one barrier (stage s has landed, stage s-1 is free),
+// this wave's fragment reads of its block of stage s, the loads of stage s+1
+// into the free slot, then the score MFMAs, softmax and PV of the block.  The
+// ring and tables take 38 KiB, so four workgroups share a compute unit (128
+// VGPRs per lane for bf16) and the waves of the others run while one waits.
+// Rows past the end of the head, and V rows of padded keys, read as zero.
+// The two "phases" of a query block take the two blocks of each stage and
+// are merged at the end.
 //
 // fp32 inputs: a pre-pass splits K and V into bf16 hi + lo planes and Q is
 // split when loaded; each product uses hi*hi + hi*lo + lo*hi (three MFMAs),
@@ -91,10 +93,10 @@ struct Ring {
     static constexpr int PLANE = 8192;
     static constexpr int BLK = NP * PLANE;
     static constexpr int STAGE = 2 * BLK;                       // two blocks: one per phase
-    static constexpr int NBUF = 3;
-    static constexpr int maskOff = NBUF * STAGE;                // [NBUF][2] mask words
-    static constexpr int gposOff = maskOff + 32;                // global positions
-    static constexpr int gclsOff = gposOff + 4 * LF_MAX_GLOBALS; // their class index, or kNotInClass
+    static constexpr int NBUF = 2;
+    static constexpr int gposOff = NBUF * STAGE;                // global positions (sorted)
+    static constexpr int gldOff = gposOff + 4 * LF_MAX_GLOBALS;  // position each slot loads (T: none)
+    static constexpr int gclsOff = gldOff + 4 * LF_MAX_GLOBALS;  // class index, or kNotInClass
     static constexpr int gbadOff = gclsOff + 4 * LF_MAX_GLOBALS; // per global block: missing / padded slots
     static constexpr int bytes = gbadOff + 4 * (LF_MAX_GLOBALS / 32);
 };
@@ -452,7 +454,7 @@ __device__ __forceinline__ void block_pv(WaveState<NP>& W, const f32x16& s, cons
 // The tile kernel.
 
 template <int QB, int KS, typename ET, typename OT, bool PAD>
-__global__ __launch_bounds__(64 * QB * KS) __attribute__((amdgpu_waves_per_eu(LFK_WAVES_PER_EU)))
+__global__ __launch_bounds__(64 * QB * KS) __attribute__((amdgpu_waves_per_eu(Elem<ET>::NP == 1 ? LFK_WAVES_PER_EU_BF16 : LFK_WAVES_PER_EU_F32)))
 void tile_kernel(const Args A) {
     static_assert(QB == 2 && KS == 2, "four waves: two phases of two query blocks");
     constexpr int NT = 64 * QB * KS;
@@ -465,8 +467,8 @@ void tile_kernel(const Args A) {
     const Plan& P = *A.plan;
     const int* gpos = (const int*)(smem + RG::gposOff);
     const int* gcls = (const int*)(smem + RG::gclsOff);
+    const int* gld = (const int*)(smem + RG::gldOff);
     const uint32_t* gbad = (const uint32_t*)(smem + RG::gbadOff);
-    uint32_t* maskw = (uint32_t*)(smem + RG::maskOff);
 
     // ---- which task.  Each of the 8 dies (blockIdx % 8) takes an eighth of
     // the global-row tasks first (they are shorter and light on memory, so
@@ -503,7 +505,6 @@ void tile_kernel(const Args A) {
     const uint32_t head_bytes = (uint32_t)T * ROWB;
     const void* kplanes = NP == 1 ? A.k : P.kp;   // bf16 input is its own plane
     const void* vplanes = NP == 1 ? A.v : P.vp;
-    const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, PAD ? (uint32_t)T : 0u);
 
     // ---- this wave's 32 queries
     const int mq0 = tk.m0 + 32 * qb;   // first query (class index, or global slot)
@@ -558,11 +559,12 @@ void tile_kernel(const Args A) {
     }
     auto live_of = [&](int s) -> bool { return s < sb_end ? (s >= s_lo && s <= s_hi) : (s < sg_end); };
 
-    // ---- loads.  Waves 0/1 bring the K rows of blocks 0/1 of a stage (lane
-    // p: row p/2), waves 2/3 their V rows (lane p: rows p/4 and 16 + p/4).
-    // Band rows of stage s sit 64*delta positions after those of stage 0.
-    const int bw = wave & 1;
-    const bool kwave = wave < 2;
+    // ---- loads.  The two waves of a phase bring their own block of each
+    // stage: query block 0 its K rows (lane p: row p/2), query block 1 its V
+    // rows (lane p: rows p/4 and 16 + p/4).  Band rows of stage s sit
+    // 64*delta positions after those of stage 0.
+    const int bw = ph;
+    const bool kwave = qb == 0;
     const int rowA = kwave ? (lane >> 1) : (lane >> 2);
     const int rowB = kwave ? rowA : 16 + (lane >> 2);
     const uint32_t colA = kwave ? 16u * ((lane & 1) ^ ((rowA >> 3) & 1)) : 16u * (lane & 3);
@@ -591,13 +593,17 @@ void tile_kernel(const Args A) {
     auto advance = [&](Window w) -> Window {
         return {w.base + step_bytes, w.n > step_bytes ? w.n - step_bytes : 0u};
     };
-    const int padpos0 = row0 + tk.delta * (lane & 31);
-    auto global_pos = [&](int slot) -> uint32_t {
-        const int g = gpos[min(slot, LF_MAX_GLOBALS - 1)];
+    auto global_pos = [&](int slot) -> uint32_t {   // position a loader lane reads for a global slot
+        const int g = gld[min(slot, LF_MAX_GLOBALS - 1)];
         return (uint32_t)(slot < n_g ? g : T);
     };
-    // stage s into the ring slot at byte offset off; w is stage s's window
-    auto issue_stage = [&](int s, int off, Window w) {
+    // stage s into the ring slot at byte offset off; w is stage s's window.
+    // pm: padded rows of this wave's block of stage s, whose V rows are
+    // loaded as zeros (so that NaN or Inf stored at padded positions cannot
+    // reach the products); padded global keys load as zeros through their
+    // table entry.
+    auto issue_stage = [&](int s, int off, Window w, uint32_t pm) {
+        const bool padA = !kwave && ((pm >> rowA) & 1u), padB = !kwave && ((pm >> rowB) & 1u);
         const int jb = 2 * s + bw;
         if (jb >= nblk) return;
         char* dst = smem + off + bw * RG::BLK;
@@ -605,8 +611,8 @@ void tile_kernel(const Args A) {
         __amdgpu_buffer_rsrc_t rs;
         if (jb < nb) {
             rs = buffer_rsrc(w.base, __builtin_amdgcn_readfirstlane(w.n));
-            voA = voA0;
-            voB = voB0;
+            voA = padA ? kPastEnd : voA0;
+            voB = padB ? kPastEnd : voB0;
         } else {
             const int sl0 = (jb - nb) * KBLK;
             rs = buffer_rsrc(kvhead, head_bytes);
@@ -619,47 +625,18 @@ void tile_kernel(const Args A) {
             for (int i = 0; i < 4; i++)
                 load_lds16(rs, dst + p * RG::PLANE + pdst[i], (i & 1) ? voB : voA, psoff[i] + 128 * p);
     };
-    // mask word slot of the ring slot at byte offset `off`
-    auto maskw_at = [&](int off, int blk) -> uint32_t* {
-        return maskw + (off / RG::STAGE) * 2 + blk;
-    };
 
-    // With padding: waves 0/1 read the padding bytes of their block's rows
-    // (lanes 0..31) one step ahead ...
-    auto load_pad = [&](int s) -> uint32_t {
-        if (wave >= 2) return 0u;
-        const int jb = 2 * s + bw;
-        if (jb >= nb) return 0u;
-        return __builtin_amdgcn_raw_buffer_load_b8(rpad, min(padpos0 + s * pos_step, T), 0, 0);
+    // With padding, lane l < 32 reads the padding byte of row l of this
+    // wave's block two stages ahead; one step ahead a ballot turns the bytes
+    // into the block's padded-row word, which the step uses for the V rows it
+    // loads and, one step later, for the scores.  Positions past the end read
+    // zero (not padded; the range test covers them).
+    const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, PAD ? (uint32_t)T : 0u);
+    const int prow0 = tk.c + tk.delta * ((tk.kb_lo + ph) * KBLK + lq);
+    auto pad_at = [&](int s) -> uint32_t {
+        return __builtin_amdgcn_raw_buffer_load_b8(rpad, (uint32_t)min(prow0 + s * pos_step, T), 0, 0);
     };
-    // ... and once the stage has landed, publish its mask word and zero the V
-    // rows of keys that are not real (so that NaN or Inf stored in padded
-    // positions cannot reach the products).
-    auto fix_stage = [&](int s, int off, uint32_t padv) {
-        if (wave >= 2) return;
-        const int jb = 2 * s + bw;
-        if (jb >= nblk) return;
-        uint32_t badw;
-        if (jb < nb) {
-            const uint32_t padbits = (uint32_t)__ballot(lane < 32 && padv != 0u);
-            const int valid = tk.key_end - (tk.kb_lo + jb) * KBLK;
-            badw = padbits | (valid >= KBLK ? 0u : (valid <= 0 ? 0xffffffffu : (0xffffffffu << valid)));
-        } else {
-            badw = gbad[jb - nb];
-        }
-        if (lane == 0) *maskw_at(off, bw) = badw;
-        if (badw != 0u) {
-            const int row = lane >> 1, cb = lane & 1;
-            if ((badw >> row) & 1u) {
-                char* vrow = smem + off + bw * RG::BLK + 4096 + cb * 2048 + row * 64;
-                const u32x4 z = {0, 0, 0, 0};
-#pragma unroll
-                for (int p = 0; p < NP; p++)
-#pragma unroll
-                    for (int j = 0; j < 4; j++) *(u32x4*)(vrow + p * RG::PLANE + 16 * j) = z;
-            }
-        }
-    };
+    auto pad_word = [&](uint32_t byte) -> uint32_t { return (uint32_t)__ballot(lane < 32 && byte != 0u); };
 
     WaveState<NP> W;
     W.o0 = (f32x16){};
@@ -673,7 +650,7 @@ void tile_kernel(const Args A) {
 
     // Q rows through a buffer resource: a lane with no query reads past its
     // end and gets zeros, so nothing consumes the loaded registers before the
-    // barrier that waits for the stages (a padded query keeps its row; the
+    // barrier that waits for stage 0 (a padded query keeps its row; the
     // epilogues write zeros for it)
     u32x4 qraw[4 * NP];
     {
@@ -687,21 +664,24 @@ void tile_kernel(const Args A) {
                 qraw[NP * ks + p] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (16 * ks + 8 * lg + 4 * p) * esz, 0, 0));
     }
-    // ---- prologue: Q and stages 0 and 1 in flight, then the global-key
-    // tables (a global-key block among the first two stages, found only when
-    // the band has fewer than four blocks, is loaded once its table is there)
-    const bool early0 = bw < nb, early1 = NS > 1 && 2 + bw < nb;
-    const Window w0 = {kvhead, head_bytes}, w1 = advance(w0);
-    Window wn = advance(w1);           // window of stage s+2 in step s
-    if (early0) issue_stage(0, 0, w0);
-    if (early1) issue_stage(1, RG::STAGE, w1);
-    uint32_t pad0 = 0u, pad_pending = 0u;
+    // ---- prologue: stage 0 and Q in flight, then the global-key tables (a
+    // global-key block in stage 0, found only when the band has fewer than
+    // two blocks, is loaded once its table is there).  Padded V rows of stage
+    // 0 are cleared once it has landed.
+    const bool early0 = bw < nb;
+    const Window w0 = {kvhead, head_bytes};
+    Window wn = advance(w0);           // window of stage s+1 in step s
+    if (early0) issue_stage(0, 0, w0, 0u);
+    // padding: pm_cur = padded rows of this wave's block of stage s (in step
+    // s), pbyte = the bytes of stage s+1 (in flight)
+    uint32_t pm_cur = 0u, pbyte = 0u;
     if constexpr (PAD) {
-        pad0 = load_pad(0);
-        if (NS > 1) pad_pending = load_pad(1);
+        pm_cur = pad_at(0);
+        pbyte = pad_at(1);
     }
-    // global-key tables (band tasks): positions, class indices, and per
-    // global block the slots that are no key (unused or padded)
+    // global-key tables (band tasks): positions, load positions, class
+    // indices, and per global block the slots that are no key (unused or
+    // padded)
     if (ngb > 0) {
         for (int base = 64 * wave; base < ngb * KBLK; base += NT) {
             const int slot = base + lane;
@@ -716,6 +696,7 @@ void tile_kernel(const Args A) {
             }
             if (slot < LF_MAX_GLOBALS) {
                 ((int*)gpos)[slot] = pos;
+                ((int*)gld)[slot] = padded ? T : pos;
                 ((int*)gcls)[slot] = cls;
             }
             const uint64_t badm = __ballot(!inr || padded);
@@ -726,11 +707,22 @@ void tile_kernel(const Args A) {
         }
         __syncthreads();
     }
-
-    if (!early0) issue_stage(0, 0, w0);
-    if (NS > 1 && !early1) issue_stage(1, RG::STAGE, w1);
-    barrier_lds_loads();               // Q and stages 0 and 1 have landed
-    if constexpr (PAD) fix_stage(0, 0, pad0);
+    if (!early0) issue_stage(0, 0, w0, 0u);
+    barrier_lds_loads();               // Q and stage 0 have landed
+    if constexpr (PAD) {
+        pm_cur = pad_word(pm_cur);
+        // the V loader clears the 16-byte pieces it brought for padded rows
+        const bool padA = ((pm_cur >> rowA) & 1u) != 0u, padB = ((pm_cur >> rowB) & 1u) != 0u;
+        if (!kwave && early0 && (padA || padB)) {
+            char* dst = smem + bw * RG::BLK + 16 * lane;
+#pragma unroll
+            for (int p = 0; p < NP; p++)
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    if ((i & 1) ? padB : padA) *(u32x4*)(dst + p * RG::PLANE + pdst[i]) = (u32x4){0, 0, 0, 0};
+        }
+        __syncthreads();
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
         if constexpr (NP == 1) {
@@ -745,71 +737,66 @@ void tile_kernel(const Args A) {
             W.ql[ks] = as_bf16x8(lo);
         }
     }
-    f32x16 sa, sb;                     // scores of the current / next block (roles alternate)
-    if (live_of(0)) sa = block_scores<NP>(W, load_k<NP>(W, smem));
 
-    // One step: this wave's block of stage s is in ring slot oc, stage s+1 in
-    // on, and stage s+2 goes to onn.  Every LDS read of a step comes before
-    // that step's loads into LDS are issued: the compiler makes any LDS read
-    // that follows such a load wait for it.
-    auto step = [&](int s, int oc, int on, int onn, f32x16& scur, f32x16& snext) {
-        barrier_lds_loads();           // stage s+1 landed; stage s fixed up; stage s-1 no longer read
+    // One step: stage s is in the ring slot at byte offset oc, stage s+1 goes
+    // to on.  Every LDS read of a step comes before that step's loads into
+    // LDS are issued (the compiler makes any LDS read that follows such a load
+    // wait for it); the score MFMAs wait for the K reads, the PV MFMAs for the
+    // V reads, and the other waves of the SIMD run meanwhile.
+    auto step = [&](int s, int oc, int on) {
+        barrier_lds_loads();           // stage s landed; stage s-1 no longer read
         const bool cur = live_of(s);
         const bool band = s < sb_end;
         const int jb = 2 * s + ph;
-        const KFrag<NP> kf = load_k<NP>(W, smem + on);
+        // The block's bad-row word, wave-uniform so that every test on it is
+        // scalar: a global-key block's comes from LDS (read ahead of the
+        // fragments), a band block's from its range and the padding ballot.
+        uint32_t gword = 0u;
+        if (!band) gword = gbad[min(max(jb - nb, 0), LF_MAX_GLOBALS / KBLK - 1)];
+        const KFrag<NP> kf = load_k<NP>(W, smem + oc);
         const VFrag<NP> vf = load_v<NP>(W, smem + oc);
         uint32_t bad;
-        if constexpr (PAD) {
-            bad = band ? *maskw_at(oc, ph) : gbad[min(max(jb - nb, 0), LF_MAX_GLOBALS / KBLK - 1)];
-        } else {
+        if (band) {
             const int valid = tk.key_end - (tk.kb_lo + jb) * KBLK;
-            const uint32_t rb = valid <= 0 ? 0xffffffffu : (valid >= KBLK ? 0u : (0xffffffffu << valid));
-            bad = band ? rb : gbad[min(max(jb - nb, 0), LF_MAX_GLOBALS / KBLK - 1)];
+            bad = valid <= 0 ? 0xffffffffu : (valid >= KBLK ? 0u : (0xffffffffu << valid));
+            if constexpr (PAD) bad |= pm_cur;
+        } else {
+            bad = (uint32_t)uniform((int)gword);
         }
         if (!cur) bad = 0xffffffffu;
+        uint32_t pm_next = 0u;
         if constexpr (PAD) {
-            if (s + 1 < NS) fix_stage(s + 1, on, pad_pending);
+            pm_next = pad_word(pbyte);
+            pbyte = pad_at(s + 2);
         }
-        uint32_t pad_next = 0u;
-        if (s + 2 < NS) {
-            issue_stage(s + 2, onn, wn);
-            if constexpr (PAD) pad_next = load_pad(s + 2);
-        }
+        if (s + 1 < NS) issue_stage(s + 1, on, wn, pm_next);
         wn = advance(wn);
-        snext = block_scores<NP>(W, kf);
-        // one masking point (the global-key mask reads LDS; global-key stages
-        // come last, where steps issue loads only past 128 globals).  A block
-        // with no key for this wave's queries is skipped: its LDS may hold
-        // anything (zero weights times NaN would still be NaN).
+        f32x16 sc = block_scores<NP>(W, kf);
+        // one masking point (the global-key mask reads LDS; it waits for the
+        // loads in flight only where the global keys fill two stages or more).
+        // A block with no key for this wave's queries is skipped: its LDS may
+        // hold anything (zero weights times NaN would still be NaN).
         if (bad != 0xffffffffu) {
             if (!band) {
-                mask_global(scur, bad, gcls + (jb - nb) * KBLK, m_me, r, lg);
+                mask_global(sc, bad, gcls + (jb - nb) * KBLK, m_me, r, lg);
             } else if (!(s >= si_lo && s <= si_hi && bad == 0u)) {
                 if (tk.kind == 0) {
                     const int key0 = (tk.kb_lo + jb) * KBLK;
-                    mask_window(scur, m_me - r - key0 - 4 * lg, 2 * r);
+                    mask_window(sc, m_me - r - key0 - 4 * lg, 2 * r);
                 }
-                if (bad != 0u) mask_bits(scur, ~lane_bits(bad, lg));
+                if (bad != 0u) mask_bits(sc, ~lane_bits(bad, lg));
             }
-            update_max<NP>(W, scur);
-            block_pv<NP>(W, scur, vf);
+            update_max<NP>(W, sc);
+            block_pv<NP>(W, sc, vf);
         }
-        pad_pending = pad_next;
+        pm_cur = pm_next;
     };
 
-    // ---- main loop: one barrier per step; ring slots rotate
-    {
-        int o0 = 0, o1 = RG::STAGE, o2 = 2 * RG::STAGE;
-        for (int s = 0; s < NS; s += 2) {
-            step(s, o0, o1, o2, sa, sb);
-            if (s + 1 >= NS) break;
-            step(s + 1, o1, o2, o0, sb, sa);
-            const int t = o0;
-            o0 = o2;
-            o2 = o1;
-            o1 = t;
-        }
+    // ---- main loop: one barrier per step; the two ring slots alternate
+    for (int s = 0; s < NS; s += 2) {
+        step(s, 0, RG::STAGE);
+        if (s + 1 >= NS) break;
+        step(s + 1, RG::STAGE, 0);
     }
     __syncthreads();
 
@@ -927,30 +914,38 @@ void tile_kernel(const Args A) {
     }
     __syncthreads();
     if (*flag == 0) return;
-    // Each thread combines 4 channels of one global row over all splits; all
-    // of its loads are issued before any is used (splits past n_split repeat
-    // the last one and get weight 0).
+    // Each thread combines 4 channels of one global row over all splits,
+    // eight splits at a time with all of their loads in flight (splits past
+    // n_split repeat the last one and get weight 0), folding each group into
+    // a running (max, sum, weighted sum).
     for (int task = tid; task < n_g * 16; task += NT) {
         const int gi = task >> 4, c4 = task & 15;
-        f32x2 ml[16];
-        f32x4 o[16];
-#pragma unroll
-        for (int sp = 0; sp < 16; sp++) {
-            const uint32_t rec = (uint32_t)min(sp, P.n_split - 1) * stride + (uint32_t)gi * kRecBytes;
-            ml[sp] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rpart, rec + 256, 0, kCoherent));
-            o[sp] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rpart, rec + 16 * c4, 0, kCoherent));
-        }
-        float M = kNegInf;
-#pragma unroll
-        for (int sp = 0; sp < 16; sp++) M = __builtin_fmaxf(M, ml[sp][0]);
-        float L = 0.f;
+        float M = kNegInf, L = 0.f;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int sp0 = 0; sp0 < P.n_split; sp0 += 8) {
+            f32x2 ml[8];
+            f32x4 o[8];
 #pragma unroll
-        for (int sp = 0; sp < 16; sp++) {
-            const float w = (sp < P.n_split && ml[sp][0] != kNegInf) ? __builtin_amdgcn_exp2f(ml[sp][0] - M) : 0.f;
-            L += ml[sp][1] * w;
+            for (int i = 0; i < 8; i++) {
+                const uint32_t rec = (uint32_t)min(sp0 + i, P.n_split - 1) * stride + (uint32_t)gi * kRecBytes;
+                ml[i] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rpart, rec + 256, 0, kCoherent));
+                o[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rpart, rec + 16 * c4, 0, kCoherent));
+            }
+            float Mn = M;
 #pragma unroll
-            for (int e = 0; e < 4; e++) acc[e] += o[sp][e] * w;
+            for (int i = 0; i < 8; i++) Mn = __builtin_fmaxf(Mn, ml[i][0]);
+            const float a = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+            L *= a;
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[e] *= a;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const float w = (sp0 + i < P.n_split && ml[i][0] != kNegInf) ? __builtin_amdgcn_exp2f(ml[i][0] - Mn) : 0.f;
+                L += ml[i][1] * w;
+#pragma unroll
+                for (int e = 0; e < 4; e++) acc[e] += o[i][e] * w;
+            }
+            M = Mn;
         }
         const int pos = P.glob[gi];
         const bool padded = padrow && padrow[pos] != 0;

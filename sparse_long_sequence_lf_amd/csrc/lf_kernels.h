@@ -12,10 +12,14 @@
 // per query block (waves per workgroup = LFK_QB * LFK_KS = 4).
 #define LFK_QB 2
 #define LFK_KS 2
-// Register budget: waves per SIMD the tile kernel is compiled for (three
-// workgroups of four waves per compute unit).
-#ifndef LFK_WAVES_PER_EU
-#define LFK_WAVES_PER_EU 3
+// Register budget: waves per SIMD the tile kernel is compiled for, one per
+// workgroup of four waves resident on a compute unit (bf16: four workgroups,
+// as many as its LDS allows; fp32 inputs double the LDS and the registers).
+#ifndef LFK_WAVES_PER_EU_BF16
+#define LFK_WAVES_PER_EU_BF16 4
+#endif
+#ifndef LFK_WAVES_PER_EU_F32
+#define LFK_WAVES_PER_EU_F32 2
 #endif
 
 namespace lfk {
