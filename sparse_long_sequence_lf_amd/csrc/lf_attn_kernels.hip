@@ -48,6 +48,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "lf_kernels.h"
 
 namespace lfk {
@@ -589,41 +591,39 @@ void tile_kernel(const Args A) {
     const uint32_t voA0 = (uint32_t)min(posA0, T) * ROWB + colA;
     const uint32_t voB0 = (uint32_t)min(posB0, T) * ROWB + colB;
     const uint32_t step_bytes = (uint32_t)min((uint64_t)pos_step * ROWB, (uint64_t)head_bytes);
-    struct Window { const char* base; uint32_t n; };
-    auto advance = [&](Window w) -> Window {
-        return {w.base + step_bytes, w.n > step_bytes ? w.n - step_bytes : 0u};
+    const int s_full = uniform((int)((head_bytes + step_bytes - 1) / step_bytes));   // stages with rows left
+    auto window = [&](int s) -> __amdgpu_buffer_rsrc_t {
+        return buffer_rsrc(kvhead + (uint64_t)s * step_bytes, s < s_full ? head_bytes - (uint32_t)s * step_bytes : 0u);
     };
     auto global_pos = [&](int slot) -> uint32_t {   // position a loader lane reads for a global slot
         const int g = gld[min(slot, LF_MAX_GLOBALS - 1)];
         return (uint32_t)(slot < n_g ? g : T);
     };
-    // stage s into the ring slot at byte offset off; w is stage s's window.
+    // stage s into the ring slot at byte offset off.
     // pm: padded rows of this wave's block of stage s, whose V rows are
     // loaded as zeros (so that NaN or Inf stored at padded positions cannot
     // reach the products); padded global keys load as zeros through their
     // table entry.
-    auto issue_stage = [&](int s, int off, Window w, uint32_t pm) {
+    auto issue_stage = [&](int s, int off, uint32_t pm) {
         const bool padA = !kwave && ((pm >> rowA) & 1u), padB = !kwave && ((pm >> rowB) & 1u);
         const int jb = 2 * s + bw;
         if (jb >= nblk) return;
         char* dst = smem + off + bw * RG::BLK;
-        uint32_t voA, voB;
-        __amdgpu_buffer_rsrc_t rs;
+        auto put = [&](__amdgpu_buffer_rsrc_t rs, uint32_t voA, uint32_t voB) {
+#pragma unroll
+            for (int p = 0; p < NP; p++)
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    load_lds16(rs, dst + p * RG::PLANE + pdst[i], (i & 1) ? voB : voA, psoff[i] + 128 * p);
+        };
+        // two copies of the loads: band offsets stay in their registers
         if (jb < nb) {
-            rs = buffer_rsrc(w.base, __builtin_amdgcn_readfirstlane(w.n));
-            voA = padA ? kPastEnd : voA0;
-            voB = padB ? kPastEnd : voB0;
+            put(window(s), padA ? kPastEnd : voA0, padB ? kPastEnd : voB0);
         } else {
             const int sl0 = (jb - nb) * KBLK;
-            rs = buffer_rsrc(kvhead, head_bytes);
-            voA = global_pos(sl0 + rowA) * ROWB + colA;
-            voB = global_pos(sl0 + rowB) * ROWB + colB;
+            put(buffer_rsrc(kvhead, head_bytes), global_pos(sl0 + rowA) * ROWB + colA,
+                global_pos(sl0 + rowB) * ROWB + colB);
         }
-#pragma unroll
-        for (int p = 0; p < NP; p++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                load_lds16(rs, dst + p * RG::PLANE + pdst[i], (i & 1) ? voB : voA, psoff[i] + 128 * p);
     };
 
     // With padding, lane l < 32 reads the padding byte of row l of this
@@ -669,9 +669,7 @@ void tile_kernel(const Args A) {
     // two blocks, is loaded once its table is there).  Padded V rows of stage
     // 0 are cleared once it has landed.
     const bool early0 = bw < nb;
-    const Window w0 = {kvhead, head_bytes};
-    Window wn = advance(w0);           // window of stage s+1 in step s
-    if (early0) issue_stage(0, 0, w0, 0u);
+    if (early0) issue_stage(0, 0, 0u);
     // padding: pm_cur = padded rows of this wave's block of stage s (in step
     // s), pbyte = the bytes of stage s+1 (in flight)
     uint32_t pm_cur = 0u, pbyte = 0u;
@@ -707,7 +705,7 @@ void tile_kernel(const Args A) {
         }
         __syncthreads();
     }
-    if (!early0) issue_stage(0, 0, w0, 0u);
+    if (!early0) issue_stage(0, 0, 0u);
     barrier_lds_loads();               // Q and stage 0 have landed
     if constexpr (PAD) {
         pm_cur = pad_word(pm_cur);
@@ -743,16 +741,19 @@ void tile_kernel(const Args A) {
     // LDS are issued (the compiler makes any LDS read that follows such a load
     // wait for it); the score MFMAs wait for the K reads, the PV MFMAs for the
     // V reads, and the other waves of the SIMD run meanwhile.
-    auto step = [&](int s, int oc, int on) {
+    // (ANY_GLOBAL false: a stage whose blocks are band blocks for both
+    // phases; such steps have no global-key code at all)
+    auto step = [&](auto any_global, int s, int oc, int on) {
+        constexpr bool ANY_GLOBAL = decltype(any_global)::value;
         barrier_lds_loads();           // stage s landed; stage s-1 no longer read
         const bool cur = live_of(s);
-        const bool band = s < sb_end;
+        const bool band = !ANY_GLOBAL || s < sb_end;
         const int jb = 2 * s + ph;
         // The block's bad-row word, wave-uniform so that every test on it is
         // scalar: a global-key block's comes from LDS (read ahead of the
         // fragments), a band block's from its range and the padding ballot.
         uint32_t gword = 0u;
-        if (!band) gword = gbad[min(max(jb - nb, 0), LF_MAX_GLOBALS / KBLK - 1)];
+        if (ANY_GLOBAL && !band) gword = gbad[min(max(jb - nb, 0), LF_MAX_GLOBALS / KBLK - 1)];
         const KFrag<NP> kf = load_k<NP>(W, smem + oc);
         const VFrag<NP> vf = load_v<NP>(W, smem + oc);
         uint32_t bad;
@@ -769,15 +770,14 @@ void tile_kernel(const Args A) {
             pm_next = pad_word(pbyte);
             pbyte = pad_at(s + 2);
         }
-        if (s + 1 < NS) issue_stage(s + 1, on, wn, pm_next);
-        wn = advance(wn);
+        if (s + 1 < NS) issue_stage(s + 1, on, pm_next);
         f32x16 sc = block_scores<NP>(W, kf);
         // one masking point (the global-key mask reads LDS; it waits for the
         // loads in flight only where the global keys fill two stages or more).
         // A block with no key for this wave's queries is skipped: its LDS may
         // hold anything (zero weights times NaN would still be NaN).
         if (bad != 0xffffffffu) {
-            if (!band) {
+            if (ANY_GLOBAL && !band) {
                 mask_global(sc, bad, gcls + (jb - nb) * KBLK, m_me, r, lg);
             } else if (!(s >= si_lo && s <= si_hi && bad == 0u)) {
                 if (tk.kind == 0) {
@@ -792,12 +792,22 @@ void tile_kernel(const Args A) {
         pm_cur = pm_next;
     };
 
-    // ---- main loop: one barrier per step; the two ring slots alternate
-    for (int s = 0; s < NS; s += 2) {
-        step(s, 0, RG::STAGE);
-        if (s + 1 >= NS) break;
-        step(s + 1, RG::STAGE, 0);
+    // ---- main loop: one barrier per step; the two ring slots alternate.
+    // Stages [0, nb/2) hold band blocks only; the rest (at most one mixed
+    // stage, then global-key blocks) take the general step.
+    using BandOnly = std::integral_constant<bool, false>;
+    using General = std::integral_constant<bool, true>;
+    const int s_band = nb >> 1;
+    int s = 0;
+    for (; s + 1 < s_band; s += 2) {
+        step(BandOnly{}, s, 0, RG::STAGE);
+        step(BandOnly{}, s + 1, RG::STAGE, 0);
     }
+    if (s < s_band) {
+        step(BandOnly{}, s, 0, RG::STAGE);
+        s++;
+    }
+    for (; s < NS; s++) step(General{}, s, (s & 1) * RG::STAGE, ((s + 1) & 1) * RG::STAGE);
     __syncthreads();
 
     // ---- merge the KS phases of each query block (LDS); phase 0 keeps the result
