@@ -86,7 +86,10 @@ def cmd_stats(a) -> None:
         lines.append(f"{short:70s} {len(v):6d} {statistics.mean(v) / 1e3:9.2f} {min(v) / 1e3:9.2f} {max(v) / 1e3:9.2f}")
     tile = [x for n, v in durs.items() if KERNEL_NAME in n for x in v]
     if tile:
+        steady = tile[a.skip:] if len(tile) > a.skip else tile
         lines += ["", f"tile kernel average duration: {statistics.mean(tile) / 1e3:.2f} us over {len(tile)} dispatches",
+                  f"tile kernel steady-state average (first {a.skip} dispatches, the warmup calls, left out): "
+                  f"{statistics.mean(steady) / 1e3:.2f} us over {len(steady)}, median {statistics.median(steady) / 1e3:.2f} us",
                   f"kernel sources sha: {kernel_sha()}"]
     text = "\n".join(lines) + "\n"
     with open(a.out, "w") as f:
@@ -137,6 +140,7 @@ def main(argv=None) -> None:
     s.add_argument("--workload", required=True)
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
+    s.add_argument("--skip", type=int, default=0, help="leading tile dispatches (warmup calls) left out of the steady-state figures")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
