@@ -473,10 +473,10 @@ void tile_kernel(const Args A) {
     const uint32_t* gbad = (const uint32_t*)(smem + RG::gbadOff);
 
     // ---- which task.  Each of the 8 dies (blockIdx % 8) takes an eighth of
-    // the global-row tasks first (they are shorter and light on memory, so
-    // they overlap the band tiles' first loads instead of trailing them), then
-    // a contiguous eighth of the band tasks (neighbouring tiles share keys in
-    // its L2).
+    // the global-row tasks first, then a contiguous eighth of the band tasks
+    // (neighbouring tiles share keys in its L2).  Global-row tasks first was
+    // measured faster than band tasks first, also where the tasks outnumber
+    // the workgroup slots.
     const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
     int task_id;
     {

@@ -201,9 +201,16 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
     if (P.n_g > 0) {
         P.n_ggroups = (int)cdiv(cdiv(P.n_g, 32), QB);
         P.g_pad = P.n_ggroups * BM;
-        int sl = (int)cdiv(cdiv(T, 16), 32) * 32;
-        P.split_len = sl < 256 ? 256 : sl;
-        P.n_split = (int)cdiv(T, P.split_len);  // <= 16: the combine spans splits with one wave's lanes
+        // a split about as long as a band tile's key range (64 + 2r keys),
+        // so both kinds of task cost about the same (measured faster than
+        // the shortest splits); at least 256 keys, and at most 16 splits
+        // (bounds the partial records and the combine's reads)
+        long long sl = cdiv((long long)BM + 2LL * P.r, 64) * 64;
+        if (sl < 256) sl = 256;
+        const long long sl16 = cdiv(cdiv(T, 16), 32) * 32;
+        if (sl < sl16) sl = sl16;
+        P.split_len = (int)(sl < T ? sl : cdiv(T, 32) * 32);
+        P.n_split = (int)cdiv(T, P.split_len);
         n_glob_tasks = (long long)B * H * P.n_split * P.n_ggroups;
         cnt_bytes = (size_t)B * H * sizeof(int);
         scratch_bytes = (size_t)B * H * P.n_split * P.g_pad * 272;  // 272-byte partial records
