@@ -532,34 +532,37 @@ void tile_kernel(const Args A) {
         wb_hi = z / KBLK;
     }
 
-    // ---- block list: band (or dense) blocks, then global-key blocks; stage s
-    // holds blocks 2s and 2s+1, and this wave works on block jb = 2s + ph
+    // ---- block list: nb band (or dense) blocks, then the global-key blocks,
+    // in sequence positions q; stage s holds positions 2s and 2s+1, and this
+    // wave works on position 2s + ph.  Band blocks are visited in a rotated
+    // order: position q < nb holds band block j = (q - kb_lo) mod nb (block
+    // kb_lo + j of the class), so that the tiles around one another, whose
+    // bands are the same class blocks shifted by two, load the same block in
+    // the same step: the first step of every tile no longer needs its own
+    // K/V from memory at once, and each block's first read is shared.
     const int nb = tk.nband;
     const int ngb = tk.kind == 0 ? cdiv(n_g, KBLK) : 0;
     const int nblk = nb + ngb;
     const int NS = cdiv(nblk, 2);
+    const int rot = tk.kind == 0 ? tk.kb_lo % nb : 0;
+    auto band_block = [&](int q) -> int { const int x = q - rot; return x < 0 ? x + nb : x; };
     const int sb_end = (nb - ph + 1) >> 1;       // steps [0, sb_end): band (or dense) blocks
-    int s_lo = 0, s_hi = -1;                     // band steps with keys for this wave's queries
-    int si_lo = 0, si_hi = -1;                   // band steps whose block needs no mask
+    int j_lo = 0, j_hi = -1;                     // band blocks with keys for this wave's queries
+    int ji_lo = 0, ji_hi = -1;                   // band blocks that need no mask
     int sg_end = sb_end;                         // steps [sb_end, sg_end): global-key blocks
     if (wave_active) {
-        int j_lo = 0, j_hi = nb - 1, ji_lo = 0, ji_hi;
+        j_hi = nb - 1;
         if (tk.kind == 0) {
             j_lo = wb_lo - tk.kb_lo;
             j_hi = wb_hi - tk.kb_lo;
-            // key0 = 32 (kb_lo + jb) >= mq0 + 31 - r, key0 + 31 <= mq0 + r, key0 + 32 <= key_end
+            // key0 = 32 (kb_lo + j) >= mq0 + 31 - r, key0 + 31 <= mq0 + r, key0 + 32 <= key_end
             ji_lo = ((mq0 + 31 - r + 31) >> 5) - tk.kb_lo;
             ji_hi = min((mq0 + r - 31) >> 5, (tk.key_end - 32) >> 5) - tk.kb_lo;
         } else {
             ji_hi = ((tk.key_end - 32) >> 5) - tk.kb_lo;
         }
-        s_lo = max(0, (j_lo - ph + 1) >> 1);
-        s_hi = min(sb_end - 1, (j_hi - ph) >> 1);
-        si_lo = max(0, (ji_lo - ph + 1) >> 1);
-        si_hi = min(sb_end - 1, (ji_hi - ph) >> 1);
         sg_end = (nblk - ph + 1) >> 1;
     }
-    auto live_of = [&](int s) -> bool { return s < sb_end ? (s >= s_lo && s <= s_hi) : (s < sg_end); };
 
     // ---- loads.  The two waves of a phase bring their own block of each
     // stage: query block 0 its K rows (lane p: row p/2), query block 1 its V
@@ -580,20 +583,16 @@ void tile_kernel(const Args A) {
         pdst[i] = kwave ? i * 1024 : 4096 + (i >> 1) * 2048 + (i & 1) * 1024;
         psoff[i] = kwave ? 32 * i : 64 * (i >> 1);
     }
-    const int row0 = tk.c + tk.delta * (tk.kb_lo + bw) * KBLK;   // position of row 0 of this wave's stage-0 block
-    const int pos_step = 2 * KBLK * tk.delta;
-    const int posA0 = row0 + tk.delta * rowA, posB0 = row0 + tk.delta * rowB;
-    // Band stage s reads through a window that starts s * pos_step rows
-    // further on and ends where the head ends, so that the lane offsets stay
-    // fixed and rows past the end read zeros: scalar work per step, no vector
-    // work.  A step longer than the head is cut to the head (all later rows
-    // read zeros either way).
-    const uint32_t voA0 = (uint32_t)min(posA0, T) * ROWB + colA;
-    const uint32_t voB0 = (uint32_t)min(posB0, T) * ROWB + colB;
-    const uint32_t step_bytes = (uint32_t)min((uint64_t)pos_step * ROWB, (uint64_t)head_bytes);
-    const int s_full = uniform((int)((head_bytes + step_bytes - 1) / step_bytes));   // stages with rows left
-    auto window = [&](int s) -> __amdgpu_buffer_rsrc_t {
-        return buffer_rsrc(kvhead + (uint64_t)s * step_bytes, s < s_full ? head_bytes - (uint32_t)s * step_bytes : 0u);
+    // A band block is read through a window that starts at the block's row 0
+    // and ends where the head ends, so that the lane offsets (rows delta
+    // apart) stay fixed and rows past the end read zeros: scalar work per
+    // block, no vector work.
+    auto row0_of = [&](int j) -> int { return tk.c + tk.delta * (tk.kb_lo + j) * KBLK; };   // position of row 0
+    const uint32_t voA0 = (uint32_t)min((long long)tk.delta * rowA, (long long)T) * ROWB + colA;
+    const uint32_t voB0 = (uint32_t)min((long long)tk.delta * rowB, (long long)T) * ROWB + colB;
+    auto window = [&](int j) -> __amdgpu_buffer_rsrc_t {
+        const int p0 = row0_of(j);
+        return buffer_rsrc(kvhead + (uint64_t)p0 * ROWB, p0 < T ? (uint32_t)(T - p0) * ROWB : 0u);
     };
     auto global_pos = [&](int slot) -> uint32_t {   // position a loader lane reads for a global slot
         const int g = gld[min(slot, LF_MAX_GLOBALS - 1)];
@@ -618,7 +617,7 @@ void tile_kernel(const Args A) {
         };
         // two copies of the loads: band offsets stay in their registers
         if (jb < nb) {
-            put(window(s), padA ? kPastEnd : voA0, padB ? kPastEnd : voB0);
+            put(window(band_block(jb)), padA ? kPastEnd : voA0, padB ? kPastEnd : voB0);
         } else {
             const int sl0 = (jb - nb) * KBLK;
             put(buffer_rsrc(kvhead, head_bytes), global_pos(sl0 + rowA) * ROWB + colA,
@@ -632,9 +631,10 @@ void tile_kernel(const Args A) {
     // loads and, one step later, for the scores.  Positions past the end read
     // zero (not padded; the range test covers them).
     const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, PAD ? (uint32_t)T : 0u);
-    const int prow0 = tk.c + tk.delta * ((tk.kb_lo + ph) * KBLK + lq);
     auto pad_at = [&](int s) -> uint32_t {
-        return __builtin_amdgcn_raw_buffer_load_b8(rpad, (uint32_t)min(prow0 + s * pos_step, T), 0, 0);
+        const int q = 2 * s + ph;
+        const int pos = q < nb ? row0_of(band_block(q)) + tk.delta * lq : T;
+        return __builtin_amdgcn_raw_buffer_load_b8(rpad, (uint32_t)min(pos, T), 0, 0);
     };
     auto pad_word = [&](uint32_t byte) -> uint32_t { return (uint32_t)__ballot(lane < 32 && byte != 0u); };
 
@@ -746,9 +746,10 @@ void tile_kernel(const Args A) {
     auto step = [&](auto any_global, int s, int oc, int on) {
         constexpr bool ANY_GLOBAL = decltype(any_global)::value;
         barrier_lds_loads();           // stage s landed; stage s-1 no longer read
-        const bool cur = live_of(s);
         const bool band = !ANY_GLOBAL || s < sb_end;
-        const int jb = 2 * s + ph;
+        const int jb = 2 * s + ph;     // sequence position
+        const int j = band_block(min(jb, nb - 1));   // its band block (band positions)
+        const bool cur = band ? (j >= j_lo && j <= j_hi) : (s < sg_end);
         // The block's bad-row word, wave-uniform so that every test on it is
         // scalar: a global-key block's comes from LDS (read ahead of the
         // fragments), a band block's from its range and the padding ballot.
@@ -758,7 +759,7 @@ void tile_kernel(const Args A) {
         const VFrag<NP> vf = load_v<NP>(W, smem + oc);
         uint32_t bad;
         if (band) {
-            const int valid = tk.key_end - (tk.kb_lo + jb) * KBLK;
+            const int valid = tk.key_end - (tk.kb_lo + j) * KBLK;
             bad = valid <= 0 ? 0xffffffffu : (valid >= KBLK ? 0u : (0xffffffffu << valid));
             if constexpr (PAD) bad |= pm_cur;
         } else {
@@ -779,9 +780,9 @@ void tile_kernel(const Args A) {
         if (bad != 0xffffffffu) {
             if (ANY_GLOBAL && !band) {
                 mask_global(sc, bad, gcls + (jb - nb) * KBLK, m_me, r, lg);
-            } else if (!(s >= si_lo && s <= si_hi && bad == 0u)) {
+            } else if (!(j >= ji_lo && j <= ji_hi && bad == 0u)) {
                 if (tk.kind == 0) {
-                    const int key0 = (tk.kb_lo + jb) * KBLK;
+                    const int key0 = (tk.kb_lo + j) * KBLK;
                     mask_window(sc, m_me - r - key0 - 4 * lg, 2 * r);
                 }
                 if (bad != 0u) mask_bits(sc, ~lane_bits(bad, lg));
