@@ -134,6 +134,37 @@ def test_tracer_counts_exact_neighbour_sets(dt):
         assert float(np.max(np.where(ref != 0, rel, np.abs(out)))) <= 2 ** -8
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_large_score_range(dt):
+    """Scores up to a few hundred (in units of the softmax's exponent) and
+    keys whose scores grow along the sequence, so that the running max of a
+    query moves on many blocks and the weights span many binades."""
+    base = W.random_case(77, B=1, H=2, T=700, dtype=dt, pad="none")
+    ramp = torch.linspace(0.2, 3.0, 700).view(1, 1, 700, 1)
+    q = (base.q.float() * 4.0).to(base.q.dtype)
+    k = (base.k.float() * 4.0 * ramp).to(base.k.dtype)
+    tol = TOL[dt]
+    if dt == "f32":
+        # fp32 inputs run as bf16 hi + lo parts (three MFMAs per product,
+        # lo*lo dropped): a score is off by at most
+        # eps = 3.5 * 2^-16 * sum_d |q_d k_d| / sqrt(d) (two 2^-16 terms for the
+        # parts' rounding, one for the dropped product, fp32 accumulation
+        # below 2^-18), and scores off by <= eps
+        # move a softmax average by <= (e^(2 eps) - 1) * max|v|.  The 1e-4 bar
+        # of the workloads holds while eps stays small (scores of a few units).
+        qa, ka = q.double().abs(), k.double().abs()
+        smax = float(torch.einsum("bhid,bhjd->bhij", qa, ka).max()) / 8.0
+        eps = 3.5 * 2.0 ** -16 * smax
+        tol = TOL[dt] + (np.exp(2 * eps) - 1) * float(base.v.abs().max())
+    for r, G, dil in [(200, [5, 650], [1, 2]), (700, [], [1, 1])]:
+        inp = W.Inputs(q, k, base.v, r, dil, G, None, None)
+        print(f"case dt={dt} r={r} G={G} dil={dil} tol={tol:.2e}", flush=True)
+        out = gpu_fwd(inp)
+        err = max_err(out, oracle_full(inp))
+        print(f"  max abs err {err:.3e}", flush=True)
+        assert err <= tol, err
+
+
 def test_nan_in_padded_positions_is_ignored():
     w = W.workload("bf16-b4h16t16384-r512-g8-pad")
     inp = W.make_inputs(w, T=1500, H=2)
