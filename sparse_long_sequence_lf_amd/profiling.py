@@ -4,6 +4,8 @@ profiles/ and the HBM-traffic record bench.py reads).
     python -m sparse_long_sequence_lf_amd.profiling stats DIR --workload W --cmd "..." --out FILE
     python -m sparse_long_sequence_lf_amd.profiling traffic FETCH_DIR WRITE_DIR --workload W \
         --cmd "..." --out-json profiles/tile_kernel_hbm_traffic.json --out-txt FILE
+    python -m sparse_long_sequence_lf_amd.profiling counters DIR --workload W --cmd "..." --out FILE \
+        [--useful-flops F --kernel-us U --hbm-bytes B]
 
 DIR, FETCH_DIR, WRITE_DIR are rocprofv3 output directories written with
 `-f csv` (kernel trace with --stats; one --pmc FETCH_SIZE run; one --pmc
@@ -132,6 +134,43 @@ def cmd_traffic(a) -> None:
     sys.stdout.write(text)
 
 
+COUNTER_SET = ["MfmaUtil", "VALUBusy", "SALUBusy", "MfmaFlopsBF16", "LDSBankConflict"]
+
+
+def cmd_counters(a) -> None:
+    """Utilisation counters of the tile kernel (median over its dispatches),
+    next to the useful work of one launch."""
+    vals: Dict[int, Dict[str, float]] = {}
+    names: Dict[int, str] = {}
+    with open(_one(os.path.join(a.dir, "**", "*counter_collection.csv"))) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            names[d] = r["Kernel_Name"]
+            vals.setdefault(d, {}).setdefault(r["Counter_Name"], 0.0)
+            vals[d][r["Counter_Name"]] += float(r["Counter_Value"])
+    tile = [v for d, v in vals.items() if KERNEL_NAME in names[d]]
+    if not tile:
+        raise SystemExit("no tile kernel dispatches in the counter run")
+    med = {k: statistics.median(v[k] for v in tile if k in v) for k in tile[0]}
+    lines = [f"# rocprofv3 utilisation counters of the tile kernel: {a.workload}", "", "command:", f"    {a.cmd}", "",
+             f"median over {len(tile)} dispatches (rocprofv3's derived metrics of this GPU):"]
+    for k in sorted(med):
+        lines.append(f"    {k:18s} {med[k]:16.4f}")
+    if "MfmaFlopsBF16" in med and a.useful_flops:
+        lines += ["", f"useful FLOPs per launch (the allowed (query, key) pairs x 4 d): {a.useful_flops:.4e}",
+                  f"MFMA FLOPs issued per launch: {med['MfmaFlopsBF16']:.4e} "
+                  f"(useful share {a.useful_flops / med['MfmaFlopsBF16']:.3f}; the rest is masked or padded "
+                  f"work inside 32x32 blocks)"]
+    if a.kernel_us and a.hbm_bytes:
+        lines.append(f"HBM traffic {a.hbm_bytes / 1e6:.2f} MB per launch over {a.kernel_us:.2f} us: "
+                     f"{a.hbm_bytes / (a.kernel_us * 1e-6) / 1e9:.0f} GB/s")
+    lines.append(f"kernel sources sha: {kernel_sha()}")
+    text = "\n".join(lines) + "\n"
+    with open(a.out, "w") as f:
+        f.write(text)
+    sys.stdout.write(text)
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -148,8 +187,16 @@ def main(argv=None) -> None:
     t.add_argument("--cmd", required=True)
     t.add_argument("--out-json", required=True)
     t.add_argument("--out-txt", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--useful-flops", type=float, default=0.0)
+    c.add_argument("--kernel-us", type=float, default=0.0)
+    c.add_argument("--hbm-bytes", type=float, default=0.0)
     a = ap.parse_args(argv)
-    cmd_stats(a) if a.what == "stats" else cmd_traffic(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
 
 
 if __name__ == "__main__":
