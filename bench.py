@@ -44,6 +44,37 @@ def measured_traffic(workload):
     return e.get("hbm_bytes_per_launch")
 
 
+def mfma_achievable_tflops(stream):
+    """The dense bf16 MFMA rate this GPU reaches in a loop of nothing but
+    MFMAs (libmfmapeak.so, built beside the library), or None if absent."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "sparse_long_sequence_lf_amd", "libmfmapeak.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.lf_mfma_peak_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lf_mfma_peak_launch.restype = ctypes.c_int
+    lib.lf_mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.lf_mfma_peak_flops.restype = ctypes.c_double
+    blocks, iters = 256 * 8, 2048
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    if lib.lf_mfma_peak_launch(blocks, iters, None, sptr) != 0:
+        return None
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        lib.lf_mfma_peak_launch(blocks, iters, None, sptr)
+        b.record(stream)
+        torch.cuda.synchronize()
+        t = lib.lf_mfma_peak_flops(blocks, iters) / (a.elapsed_time(b) * 1e-3) / 1e12
+        best = t if best is None else max(best, t)
+    return best
+
+
 def cpu_baseline(inp, flops, seconds):
     """The fp64 oracle, unmodified, on the host cores: whole-workload passes
     repeated until about `seconds` of wall time."""
@@ -169,6 +200,22 @@ def main():
     torch.cuda.synchronize()
     ms_launch = sum(a.elapsed_time(b) for a, b in ev) / n_each
 
+    # cold caches: before each timed call, 512 MiB are written so that the
+    # L2s and the MALL hold none of q, k, v; the events bracket the call only
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n_cold = min(args.steps, 20)
+    evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+    torch.cuda.synchronize()
+    for a, b in evc:
+        flush.zero_()
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms_cold = sum(a.elapsed_time(b) for a, b in evc) / n_cold
+    del flush
+    achievable = mfma_achievable_tflops(stream)
+
     use_graph = ms_graph is not None and graph_ok
     ms = ms_graph if use_graph else ms_eager
     tflops = flops / (ms * 1e-3) / 1e12
@@ -200,6 +247,7 @@ def main():
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "ms_per_step_eager": round(ms_eager, 5),
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
+        "ms_per_step_cold": round(ms_cold, 5),
         "wall_s_eager_loop": round(wall, 4),
         "roofline": {"bound": "mfma", "kernel": "lfk::tile_kernel",
                      "achieved": round(flops / (ms_kernel * 1e-3) / 1e12, 2),
@@ -209,6 +257,9 @@ def main():
                      "kernel_us": round(ms_kernel * 1e3, 3),
                      "kernel_us_source": "timed region / K" + (" (includes the fp32 plane split)" if w.dtype != "bf16" else ""),
                      "launch_us_event_pairs": round(ms_launch * 1e3, 3),
+                     "achievable_peak": None if achievable is None else round(achievable, 1),
+                     "frac_of_achievable": None if achievable is None else
+                     round(flops / (ms_kernel * 1e-3) / 1e12 / achievable, 4),
                      "algorithmic_flops": flops,
                      "algorithmic_bytes": metrics.algorithmic_bytes(B, H, T, d, q.element_size(),
                                                                     inp.key_padding_mask)},

@@ -1,4 +1,5 @@
-"""Build liblfattn.so (the C-ABI library) for gfx950 with hipcc, in-tree.
+"""Build liblfattn.so (the C-ABI library) for gfx950 with hipcc, in-tree,
+and libmfmapeak.so (the benchmark's MFMA-rate probe, not part of the library).
 
     python -m sparse_long_sequence_lf_amd.build
 """
@@ -12,6 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblfattn.so")
 SOURCES = [os.path.join(CSRC, "lf_host.cpp"), os.path.join(CSRC, "lf_attn_kernels.hip")]
+PEAK_LIB = os.path.join(PKG, "libmfmapeak.so")
+PEAK_SOURCE = os.path.join(CSRC, "mfma_peak.hip")
 
 # gfx950 only; packed fp32 VALU ops are kept out of the generated code;
 # MFMA accumulators live in ordinary VGPRs (no AGPR copies around the softmax
@@ -46,6 +49,17 @@ def build(out: str = LIB, defines=(), verbose: bool = False) -> str:
     return out
 
 
+def build_peak_probe(out: str = PEAK_LIB, verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    cmd = [hipcc] + HIP_FLAGS + ["-shared", PEAK_SOURCE, "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_peak_probe(verbose=True)
     sys.exit(0)
