@@ -94,6 +94,52 @@ def cpu_baseline(inp, flops, seconds):
                       f"{reps} passes in {el:.1f} s, fp64"}
 
 
+def global_rows_probe(lf, W, steps):
+    """HBM rate of the global-row work: the padded shape with r = 0 (band
+    queries read one key plus the globals) timed with its 8 globals and with
+    none; the difference is charged to the global rows, whose algorithmic
+    bytes are every valid K and V row of each (b, h) once.  An upper bound on
+    their time (the band tiles' global-key blocks fall in it too), so the
+    rate is a lower bound."""
+    import torch
+    dev = torch.device("cuda:0")
+    w = W.workload("bf16-b4h16t16384-r0-g8-pad")
+    inp = W.make_inputs(w)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    kpm = inp.key_padding_mask.to(dev)
+    H, d = inp.q.shape[1], inp.q.shape[3]
+    kv_bytes = sum(inp.lengths) * H * 2 * d * inp.q.element_size()
+    us = {}
+    for name, G in (("with_globals", list(inp.global_idx)), ("without_globals", [])):
+        side = torch.cuda.Stream(dev)
+        with torch.cuda.stream(side):
+            call = lf.Prepared(q, k, v, inp.r, inp.dilation, G, kpm, stream=side)
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(steps):
+                    call()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / steps * 1e3
+            best = t if best is None else min(best, t)
+        us[name] = best
+    dt = us["with_globals"] - us["without_globals"]
+    print(json.dumps({"probe": "global-row HBM rate", "workload": w.name,
+                      "us_per_call": {k_: round(v_, 3) for k_, v_ in us.items()},
+                      "global_row_us": round(dt, 3), "global_row_algorithmic_bytes": kv_bytes,
+                      "global_row_GBps_lower_bound": round(kv_bytes / (dt * 1e-6) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +149,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-mode", action="store_true")
+    ap.add_argument("--global-rows-probe", action="store_true",
+                    help="print the global-row HBM rate probe's line instead of the benchmark line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -116,6 +164,11 @@ def main():
     import sparse_long_sequence_lf_amd as lf
     from sparse_long_sequence_lf_amd import metrics
     from sparse_long_sequence_lf_amd import workloads as W
+
+    if args.global_rows_probe:
+        torch.cuda.set_device(0)
+        global_rows_probe(lf, W, min(args.steps, 50))
+        return
 
     w = W.workload(args.workload)
     inp = W.make_inputs(w)
