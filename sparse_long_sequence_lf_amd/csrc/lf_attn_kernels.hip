@@ -73,6 +73,7 @@ constexpr int kRawBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format,
 constexpr uint32_t kPastEnd = 0xFFFFFF00u;     // buffer offset past any resource's end (reads zero)
 constexpr int kCoherent = 16;                  // buffer cache policy sc1: coherent across the dies' L2s
 constexpr int kRecBytes = 272;                 // global-row partial record: O[64], m, l, pad[2]
+constexpr int kVecGlobals = 2;                 // band tasks take up to this many global keys on the VALU
 
 // log2(e) / sqrt(64): scores are taken to base 2 with the 1/sqrt(d) scale.
 constexpr float kScaleLog2 = 0.18033688011112042f;
@@ -452,6 +453,108 @@ __device__ __forceinline__ void block_pv(WaveState<NP>& W, const f32x16& s, cons
     }
 }
 
+// A global key taken on the vector units: the K channels of this lane's half
+// of the query (the Q operand layout) and the V channels of its O^T rows.
+template <int NP>
+struct GKey {
+    u32x4 kh[4], kl[4];   // bf16 K (hi and, for fp32 inputs, lo part): channels 16ks + 8lg .. +7
+    u32x4 v[8];           // V channels 32cb + 8j + 4lg .. +3 ([4cb + j]); bf16 inputs use .xy
+};
+
+// rk: K as bf16 rows of NP planes (NP * 128 bytes a row); rv: V rows in the
+// input type.  pos past the end (or none) reads zeros.
+template <int NP>
+__device__ __forceinline__ GKey<NP> load_gkey(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t pos,
+                                               int lg) {
+    GKey<NP> g;
+    const uint32_t kro = pos * (uint32_t)(NP * 128u), vro = pos * (uint32_t)(NP * 128u);
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+        const uint32_t o = kro + 2u * (16 * ks + 8 * lg);
+        g.kh[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+        if constexpr (NP == 2)
+            g.kl[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o + 128u, 0, 0));
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int ch = 32 * cb + 8 * j + 4 * lg;
+            if constexpr (NP == 1) {
+                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, vro + 2u * ch, 0, 0));
+                g.v[4 * cb + j] = (u32x4){x[0], x[1], 0u, 0u};
+            } else {
+                g.v[4 * cb + j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vro + 4u * ch, 0, 0));
+            }
+        }
+    return g;
+}
+
+// this lane's half of q . k (fp32 inputs: qh kh + qh kl + ql kh, as the MFMA
+// path).  Pairs are taken from whole bf16x8 vectors by shuffles: bit-casting
+// single elements of an ext_vector miscompiles with this clang.
+__device__ __forceinline__ bf16x2 pair(bf16x8 x, int e) {
+    switch (e) {
+        case 0: return __builtin_shufflevector(x, x, 0, 1);
+        case 1: return __builtin_shufflevector(x, x, 2, 3);
+        case 2: return __builtin_shufflevector(x, x, 4, 5);
+        default: return __builtin_shufflevector(x, x, 6, 7);
+    }
+}
+
+template <int NP>
+__device__ __forceinline__ float gkey_dot(const WaveState<NP>& W, const GKey<NP>& g) {
+    float s = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+        const bf16x8 kh = as_bf16x8(g.kh[ks]);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            s = __builtin_amdgcn_fdot2_f32_bf16(pair(W.qh[ks], e), pair(kh, e), s, false);
+            if constexpr (NP == 2) {
+                const bf16x8 kl = as_bf16x8(g.kl[ks]);
+                s = __builtin_amdgcn_fdot2_f32_bf16(pair(W.qh[ks], e), pair(kl, e), s, false);
+                s = __builtin_amdgcn_fdot2_f32_bf16(pair(W.ql[ks], e), pair(kh, e), s, false);
+            }
+        }
+    }
+    return s;
+}
+
+// fold one key (scaled base-2 score sc, -inf when the key is not in the
+// query's set) into the running (m, l, O): the running-max update of the
+// blocks, for a single key.  lg == 0 lanes count its weight in l.
+template <int NP>
+__device__ __forceinline__ void gkey_fold(WaveState<NP>& W, const GKey<NP>& g, float sc, int lg) {
+    const float mn = __builtin_fmaxf(W.ms, sc);
+    const float alpha = W.ms == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(W.ms - mn);
+    const float p = sc == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(sc - mn);
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++) {
+        f32x16& oc = cb ? W.o1 : W.o0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const u32x4 x = g.v[4 * cb + j];
+            float v4[4];
+            if constexpr (NP == 1) {
+                // bf16 -> fp32 is the bf16 in the upper half: shift / mask whole vectors
+                const f32x4 f = __builtin_bit_cast(
+                    f32x4, (u32x4){x[0] << 16, x[0] & 0xffff0000u, x[1] << 16, x[1] & 0xffff0000u});
+                v4[0] = f[0]; v4[1] = f[1]; v4[2] = f[2]; v4[3] = f[3];
+            } else {
+                const f32x4 f = __builtin_bit_cast(f32x4, x);
+                v4[0] = f[0]; v4[1] = f[1]; v4[2] = f[2]; v4[3] = f[3];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e++) oc[4 * j + e] = __builtin_fmaf(oc[4 * j + e], alpha, p * v4[e]);
+        }
+    }
+    W.lp = __builtin_fmaf(W.lp, alpha, lg == 0 ? p : 0.0f);
+    W.ms = mn;
+    W.nms = mn == kNegInf ? 0.0f : -mn;
+    W.thr = (mn + 8.0f) * (1.0f / kScaleLog2);
+}
+
 // ---------------------------------------------------------------------------
 // The tile kernel.
 
@@ -541,7 +644,12 @@ void tile_kernel(const Args A) {
     // the same step: the first step of every tile no longer needs its own
     // K/V from memory at once, and each block's first read is shared.
     const int nb = tk.nband;
-    const int ngb = tk.kind == 0 ? cdiv(n_g, KBLK) : 0;
+    // A band task with at most kVecGlobals globals takes the global keys on
+    // the vector units before the band (below): a global-key block would cost
+    // a whole step of the loop for one or two keys.  With more globals they
+    // follow the band blocks in the ring.
+    const bool gvec = tk.kind == 0 && n_g > 0 && n_g <= kVecGlobals;
+    const int ngb = (tk.kind == 0 && !gvec) ? cdiv(n_g, KBLK) : 0;
     const int nblk = nb + ngb;
     const int NS = cdiv(nblk, 2);
     const int rot = tk.kind == 0 ? tk.kb_lo % nb : 0;
@@ -664,6 +772,12 @@ void tile_kernel(const Args A) {
                 qraw[NP * ks + p] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (16 * ks + 8 * lg + 4 * p) * esz, 0, 0));
     }
+    // the first vector-path global key's K and V rows travel with Q
+    const __amdgpu_buffer_rsrc_t rgk = buffer_rsrc((const char*)kplanes + (size_t)tk.bh * head_bytes, head_bytes);
+    const __amdgpu_buffer_rsrc_t rgv = buffer_rsrc((const char*)A.v + tk.bh * (size_t)T * D * sizeof(ET),
+                                                   (uint32_t)T * D * (uint32_t)sizeof(ET));
+    GKey<NP> gk0;
+    if (gvec && ph == 0) gk0 = load_gkey<NP>(rgk, rgv, (uint32_t)P.glob[0], lg);
     // ---- prologue: stage 0 and Q in flight, then the global-key tables (a
     // global-key block in stage 0, found only when the band has fewer than
     // two blocks, is loaded once its table is there).  Padded V rows of stage
@@ -733,6 +847,23 @@ void tile_kernel(const Args A) {
             split8(x, hi, lo);
             W.qh[ks] = as_bf16x8(hi);
             W.ql[ks] = as_bf16x8(lo);
+        }
+    }
+    // ---- vector-path global keys: the phase-0 waves (the phases are merged
+    // at the end, so one of them takes the keys), every query, each key in
+    // turn, unless the key is padded or already in the query's window (its
+    // class, |class distance| <= r: the band counts it)
+    if (gvec && ph == 0) {
+        for (int g = 0; g < n_g; g++) {
+            const int pos = P.glob[g];
+            const GKey<NP> gk = g == 0 ? gk0 : load_gkey<NP>(rgk, rgv, (uint32_t)pos, lg);
+            const float s = halves_sum(gkey_dot<NP>(W, gk));
+            const int dpos = pos - tk.c;
+            const bool in_class = dpos >= 0 && dpos % tk.delta == 0;
+            const int dk = dpos / tk.delta - m_me;
+            const bool padded = PAD && padrow[pos] != 0;
+            const bool ok = my_pos >= 0 && !padded && !(in_class && dk >= -r && dk <= r);
+            gkey_fold<NP>(W, gk, ok ? s * kScaleLog2 : kNegInf, lg);
         }
     }
 
@@ -855,7 +986,10 @@ void tile_kernel(const Args A) {
         // ---- epilogue: y = O / l for the tile's valid queries; padded rows -> 0.
         // Rows of global queries are left to the global-row combine.
         if (!writer || my_pos < 0) return;
-        if (P.n_g > 0) {
+        if (gvec) {
+            for (int g = 0; g < n_g; g++)
+                if (P.glob[g] == my_pos) return;
+        } else if (P.n_g > 0) {
             int lo = 0, hi = P.n_g - 1;
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
