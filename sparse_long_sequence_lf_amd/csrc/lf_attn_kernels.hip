@@ -368,9 +368,11 @@ __device__ __forceinline__ void update_max(WaveState<NP>& W, const f32x16& s) {
     float mx = s[0];
 #pragma unroll
     for (int i = 1; i < 16; i++) mx = __builtin_elementwise_maximum(mx, s[i]);
-    mx = halves_max(mx);
-    const bool need = mx > W.thr;
-    if (__ballot(need)) {
+    // a row's maximum passes the threshold exactly when one of its halves
+    // does, so the two halves meet only when some row moves
+    if (__ballot(mx > W.thr)) {
+        mx = halves_max(mx);
+        const bool need = mx > W.thr;
         const float mxs = mx * kScaleLog2;
         const float msn = need ? mxs : W.ms;
         const float alpha = need ? __builtin_amdgcn_exp2f(W.ms - msn) : 1.0f;
@@ -406,16 +408,19 @@ __device__ __forceinline__ VFrag<NP> load_v(const WaveState<NP>& W, const char* 
     return f;
 }
 
-// p = 2^(s*scale - m) for one block, its row sum, and O^T += V^T P^T
+// P^T operands of one block (bf16; for fp32 inputs also the low parts)
 template <int NP>
-__device__ __forceinline__ void block_pv(WaveState<NP>& W, const f32x16& s, const VFrag<NP>& f) {
+struct PFrag { bf16x8 h[2], l[2]; };
+
+// p = 2^(s*scale - m) for one block as P^T operands; returns ps plus this
+// lane's part of the block's row sum
+template <int NP>
+__device__ __forceinline__ float block_weights(const WaveState<NP>& W, const f32x16& s, PFrag<NP>& pf, float ps) {
     const float nms = W.nms;
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], kScaleLog2, nms));
     // P^T operands: step st covers accumulator elements 8st .. 8st+7
-    bf16x8 pb[2], pbl[2];
-    float ps = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; st++) {
         u32x4 w, wl;
@@ -435,22 +440,34 @@ __device__ __forceinline__ void block_pv(WaveState<NP>& W, const f32x16& s, cons
                                                      (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, ps, false);
             }
         }
-        pb[st] = as_bf16x8(w);
-        if constexpr (NP == 2) pbl[st] = as_bf16x8(wl);
+        pf.h[st] = as_bf16x8(w);
+        if constexpr (NP == 2) pf.l[st] = as_bf16x8(wl);
     }
-    W.lp += ps;
+    return ps;
+}
+
+// O^T += V^T P^T
+template <int NP>
+__device__ __forceinline__ void block_product(WaveState<NP>& W, const PFrag<NP>& pf, const VFrag<NP>& f) {
 #pragma unroll
     for (int st = 0; st < 2; st++) {
 #pragma unroll
         for (int cb = 0; cb < 2; cb++) {
             f32x16& oc = cb ? W.o1 : W.o0;
-            oc = mfma(f.v[st][cb][0], pb[st], oc);
+            oc = mfma(f.v[st][cb][0], pf.h[st], oc);
             if constexpr (NP == 2) {
-                oc = mfma(f.v[st][cb][0], pbl[st], oc);
-                oc = mfma(f.v[st][cb][1], pb[st], oc);
+                oc = mfma(f.v[st][cb][0], pf.l[st], oc);
+                oc = mfma(f.v[st][cb][1], pf.h[st], oc);
             }
         }
     }
+}
+
+template <int NP>
+__device__ __forceinline__ void block_pv(WaveState<NP>& W, const f32x16& s, const VFrag<NP>& f) {
+    PFrag<NP> pf;
+    W.lp = block_weights<NP>(W, s, pf, W.lp);
+    block_product<NP>(W, pf, f);
 }
 
 // A global key taken on the vector units: the K channels of this lane's half
@@ -909,15 +926,18 @@ void tile_kernel(const Args A) {
         // A block with no key for this wave's queries is skipped: its LDS may
         // hold anything (zero weights times NaN would still be NaN).
         if (bad != 0xffffffffu) {
-            if (ANY_GLOBAL && !band) {
-                mask_global(sc, bad, gcls + (jb - nb) * KBLK, m_me, r, lg);
-            } else if (!(j >= ji_lo && j <= ji_hi && bad == 0u)) {
-                if (tk.kind == 0) {
-                    const int key0 = (tk.kb_lo + j) * KBLK;
-                    mask_window(sc, m_me - r - key0 - 4 * lg, 2 * r);
+            auto mask = [&](f32x16& x) {
+                if (ANY_GLOBAL && !band) {
+                    mask_global(x, bad, gcls + (jb - nb) * KBLK, m_me, r, lg);
+                } else if (!(j >= ji_lo && j <= ji_hi && bad == 0u)) {
+                    if (tk.kind == 0) {
+                        const int key0 = (tk.kb_lo + j) * KBLK;
+                        mask_window(x, m_me - r - key0 - 4 * lg, 2 * r);
+                    }
+                    if (bad != 0u) mask_bits(x, ~lane_bits(bad, lg));
                 }
-                if (bad != 0u) mask_bits(sc, ~lane_bits(bad, lg));
-            }
+            };
+            mask(sc);
             update_max<NP>(W, sc);
             block_pv<NP>(W, sc, vf);
         }
@@ -1005,16 +1025,32 @@ void tile_kernel(const Args A) {
 #pragma unroll
         for (int cb = 0; cb < 2; cb++) {
             const f32x16& oc = cb ? W.o1 : W.o0;
+            if constexpr (sizeof(OT) == 2) {
+                // Channel groups 8j+4lg..+3 packed to bf16 (two dwords each). Lanes l
+                // and l+32 trade groups with one v_permlane32_swap per dword so that
+                // each ends up with 8 consecutive channels: the lower lane keeps group
+                // 2m and takes its partner's, the upper lane keeps 2m+1 likewise.
+                uint32_t g[4][2];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int c0 = 32 * cb + 8 * j + 4 * lg;
-                const float y0 = zero ? 0.f : oc[4 * j + 0] * inv, y1 = zero ? 0.f : oc[4 * j + 1] * inv;
-                const float y2 = zero ? 0.f : oc[4 * j + 2] * inv, y3 = zero ? 0.f : oc[4 * j + 3] * inv;
-                if constexpr (sizeof(OT) == 2) {
-                    const u32x2 w = {pack_bf16(y0, y1), pack_bf16(y2, y3)};
-                    *(u32x2*)(orow + c0) = w;
-                } else {
-                    const f32x4 w = {y0, y1, y2, y3};
+                for (int j = 0; j < 4; j++) {
+                    const float y0 = zero ? 0.f : oc[4 * j + 0] * inv, y1 = zero ? 0.f : oc[4 * j + 1] * inv;
+                    const float y2 = zero ? 0.f : oc[4 * j + 2] * inv, y3 = zero ? 0.f : oc[4 * j + 3] * inv;
+                    g[j][0] = pack_bf16(y0, y1);
+                    g[j][1] = pack_bf16(y2, y3);
+                }
+#pragma unroll
+                for (int m = 0; m < 2; m++) {
+                    const auto r0 = __builtin_amdgcn_permlane32_swap(g[2 * m][0], g[2 * m + 1][0], false, false);
+                    const auto r1 = __builtin_amdgcn_permlane32_swap(g[2 * m][1], g[2 * m + 1][1], false, false);
+                    const u32x4 w = {r0[0], r1[0], r0[1], r1[1]};
+                    *(u32x4*)(orow + 32 * cb + 16 * m + 8 * lg) = w;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int c0 = 32 * cb + 8 * j + 4 * lg;
+                    const f32x4 w = {zero ? 0.f : oc[4 * j + 0] * inv, zero ? 0.f : oc[4 * j + 1] * inv,
+                                     zero ? 0.f : oc[4 * j + 2] * inv, zero ? 0.f : oc[4 * j + 3] * inv};
                     *(f32x4*)(orow + c0) = w;
                 }
             }
