@@ -90,7 +90,7 @@ def cmd_stats(a) -> None:
     if tile:
         steady = tile[a.skip:] if len(tile) > a.skip else tile
         lines += ["", f"tile kernel average duration: {statistics.mean(tile) / 1e3:.2f} us over {len(tile)} dispatches",
-                  f"tile kernel steady-state average (first {a.skip} dispatches, the warmup calls, left out): "
+                  f"tile kernel steady-state average (first {a.skip} dispatches, the untimed warmup and clock-settle calls, left out): "
                   f"{statistics.mean(steady) / 1e3:.2f} us over {len(steady)}, median {statistics.median(steady) / 1e3:.2f} us",
                   f"kernel sources sha: {kernel_sha()}"]
     text = "\n".join(lines) + "\n"
@@ -179,7 +179,7 @@ def main(argv=None) -> None:
     s.add_argument("--workload", required=True)
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
-    s.add_argument("--skip", type=int, default=0, help="leading tile dispatches (warmup calls) left out of the steady-state figures")
+    s.add_argument("--skip", type=int, default=0, help="leading tile dispatches (untimed warmup and clock-settle calls) left out of the steady-state figures")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
