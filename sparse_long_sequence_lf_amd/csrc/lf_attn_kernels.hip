@@ -608,6 +608,31 @@ void tile_kernel(const Args A) {
         else return;
     }
     const Task tk = decode_task<QB>(P, task_id);
+    if constexpr (PAD) {
+        // A band tile whose queries are all padded writes zero rows and ends
+        // here: a padded query's output is zero whatever its keys.  Every
+        // wave tests all of the tile's queries (lane l: query m0 + l), so the
+        // decision is the same in each and no barrier is needed.
+        if (tk.kind == 0) {
+            const int l = threadIdx.x & 63;
+            const int mq = tk.m0 + l;
+            const int pos = tk.c + tk.delta * mq;
+            const uint8_t* prow = A.pad + (size_t)tk.b * P.T;
+            const bool live = l < 32 * QB && mq < tk.n && prow[pos] == 0;
+            if (__ballot(live) == 0) {
+                const int t = threadIdx.x, q = tk.m0 + (t >> 2);
+                const int qp = tk.c + tk.delta * q;
+                bool global = false;
+                for (int g = 0; g < P.n_g; g++) global |= P.glob[g] == qp;
+                if ((t >> 2) < 32 * QB && q < tk.n && !global) {
+                    OT* orow = (OT*)A.out + (size_t)tk.bh * P.T * D + (size_t)qp * D + 16 * (t & 3);
+#pragma unroll
+                    for (int i = 0; i < 16 * (int)sizeof(OT) / 16; i++) ((u32x4*)orow)[i] = (u32x4){0u, 0u, 0u, 0u};
+                }
+                return;
+            }
+        }
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -668,7 +693,18 @@ void tile_kernel(const Args A) {
     const bool gvec = tk.kind == 0 && n_g > 0 && n_g <= kVecGlobals;
     const int ngb = (tk.kind == 0 && !gvec) ? cdiv(n_g, KBLK) : 0;
     const int nblk = nb + ngb;
-    const int NS = cdiv(nblk, 2);
+    // a global-row split whose keys are all padded contributes nothing: no
+    // steps (its partial records get max -inf and sum 0)
+    bool dead = false;
+    if constexpr (PAD) {
+        if (tk.kind == 1) {
+            const uint8_t* prow = A.pad + (size_t)tk.b * P.T;
+            bool any = false;
+            for (int j = tk.kb_lo * KBLK + lane; j < tk.key_end; j += 64) any |= prow[j] == 0;
+            dead = __ballot(any) == 0;
+        }
+    }
+    const int NS = dead ? 0 : cdiv(nblk, 2);
     const int rot = tk.kind == 0 ? tk.kb_lo % nb : 0;
     auto band_block = [&](int q) -> int { const int x = q - rot; return x < 0 ? x + nb : x; };
     const int sb_end = (nb - ph + 1) >> 1;       // steps [0, sb_end): band (or dense) blocks
@@ -949,7 +985,7 @@ void tile_kernel(const Args A) {
     // stage, then global-key blocks) take the general step.
     using BandOnly = std::integral_constant<bool, false>;
     using General = std::integral_constant<bool, true>;
-    const int s_band = nb >> 1;
+    const int s_band = dead ? 0 : nb >> 1;
     int s = 0;
     for (; s + 1 < s_band; s += 2) {
         step(BandOnly{}, s, 0, RG::STAGE);

@@ -165,6 +165,31 @@ def test_large_score_range(dt):
         assert err <= tol, err
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_fully_padded_tiles(dt):
+    """Right padding that leaves whole 64-query tiles of every residue class
+    padded (one sequence entirely): those rows come out exactly zero even
+    over an output filled with NaN, the rest matches the oracle, and globals
+    sit inside and outside the padding."""
+    B, H, T = 3, 4, 900
+    base = W.random_case(91, B=B, H=H, T=T, dtype=dt, pad="none")
+    kpm = torch.zeros(B, T, dtype=torch.uint8)
+    kpm[0, 130:] = 1
+    kpm[1, 700:] = 1
+    kpm[2, :] = 1
+    inp = W.Inputs(base.q, base.k, base.v, 40, [1, 2, 3, 1], [5, 400, 800], None, kpm)
+    print(f"case dt={dt} fully padded tiles", flush=True)
+    q, k, v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    out = torch.full_like(q, float("nan"))
+    lf.attn_fwd(q, k, v, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm.cuda(), out=out)
+    torch.cuda.synchronize()
+    err = max_err(out, oracle_full(inp))
+    assert err <= TOL[dt], err
+    o = out.float().cpu()
+    for b in range(B):
+        assert torch.all(o[b][:, kpm[b].bool()] == 0)
+
+
 def test_nan_in_padded_positions_is_ignored():
     w = W.workload("bf16-b4h16t16384-r512-g8-pad")
     inp = W.make_inputs(w, T=1500, H=2)
