@@ -24,6 +24,13 @@
  *       |i - j| <= r*delta and (i - j) mod delta == 0.
  *   "Longformer长序列处理", Python 演示 note 3: positions outside the
  *       sequence are dropped (no wrap-around).
+ *   same page, HF实践: the window may be given per layer as a list; here a
+ *       call may give one radius per head (r_h), the same rule per head.
+ *   Longformer (eightmm.github.io), "Implementation Reading" asks whether
+ *       windows are one-sided or two-sided.  One-sided reading used here:
+ *       key j is in N_local(i) iff 0 <= i - j <= r*delta and
+ *       (i - j) mod delta == 0 (the query and the keys before it); global
+ *       rows and global keys are as in the two-sided case.
  *   same page, "Implementation Reading" asks that padding be masked:
  *       a padded key leaves every query's set (global rows included);
  *       a padded query row is defined as all zeros.
@@ -93,7 +100,7 @@ static int gset_has(const gset_t *g, int i) {
 /* N(i) for one query, written out as a sorted list of key positions.
  * Returns |N(i)|; a padded query gets the empty set (its row is zero). */
 
-static int neighbours(int T, int r, int delta, const gset_t *G,
+static int neighbours(int T, int r, int delta, int one_sided, const gset_t *G,
                       const unsigned char *pad /* [T] or NULL */, int i, int *out) {
     if (pad && pad[i]) return 0;
     int n = 0;
@@ -105,6 +112,7 @@ static int neighbours(int T, int r, int delta, const gset_t *G,
     }
     /* N_local(i): j = i + t*delta for t in [-r, r], inside [0, T) */
     long long tlo = -(long long)r, thi = (long long)r;
+    if (one_sided) thi = 0;                              /* keys at or before i only */
     long long tmin = -((long long)i / delta);            /* smallest t with j >= 0 */
     long long tmax = ((long long)(T - 1) - i) / delta;   /* largest t with j < T  */
     if (tlo < tmin) tlo = tmin;
@@ -162,6 +170,8 @@ static void attend_row(const float *qi, const float *K, const float *V, int d,
 typedef struct {
     const float *q, *k, *v;
     int B, H, T, d, r;
+    const int *rad;         /* [H] radius per head, or NULL: r for every head */
+    int one_sided;
     const int *dil;
     const gset_t *G;
     const unsigned char *pad;
@@ -187,8 +197,9 @@ static void *worker(void *arg) {
             int i = (int)(flat % jb->T);
             int b = (int)(bh / jb->H), h = (int)(bh % jb->H);
             int delta = jb->dil ? jb->dil[h] : 1;
+            int rh = jb->rad ? jb->rad[h] : jb->r;
             const unsigned char *padrow = jb->pad ? jb->pad + (size_t)b * jb->T : NULL;
-            int n = neighbours(jb->T, jb->r, delta, jb->G, padrow, i, nb);
+            int n = neighbours(jb->T, rh, delta, jb->one_sided, jb->G, padrow, i, nb);
             const size_t base = (size_t)bh * jb->T * jb->d;
             attend_row(jb->q + base + (size_t)i * jb->d, jb->k + base, jb->v + base,
                        jb->d, nb, n, s, jb->out + (size_t)e * jb->d);
@@ -208,18 +219,23 @@ static int host_threads(void) {
     return 1;
 }
 
-static int check_args(int B, int H, int T, int d, int r, const int *dil) {
+static int check_args(int B, int H, int T, int d, int r, const int *rad, int one_sided, const int *dil) {
     if (B < 1 || H < 1 || T < 1 || d < 1 || r < 0) return -1;
+    if (one_sided != 0 && one_sided != 1) return -1;
     if (dil)
         for (int h = 0; h < H; h++)
             if (dil[h] < 1) return -1;
+    if (rad)
+        for (int h = 0; h < H; h++)
+            if (rad[h] < 0) return -1;
     return 0;
 }
 
 static int run(const float *q, const float *k, const float *v, int B, int H, int T, int d, int r,
-               const int *dil, const int *gidx, int ng, const unsigned char *pad,
-               const long long *rows, long long n_rows, double *out, int n_threads) {
-    if (check_args(B, H, T, d, r, dil)) return -1;
+               const int *rad, int one_sided, const int *dil, const int *gidx, int ng,
+               const unsigned char *pad, const long long *rows, long long n_rows, double *out,
+               int n_threads) {
+    if (check_args(B, H, T, d, r, rad, one_sided, dil)) return -1;
     if (ng < 0 || (ng > 0 && !gidx)) return -1;
     gset_t G;
     if (gset_make(&G, gidx, ng, T)) return -1;
@@ -230,7 +246,7 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     if (!jobs || !th) { free(jobs); free(th); free(G.pos); return -1; }
     int err = 0;
     for (int t = 0; t < n_threads; t++) {
-        job_t j = {q, k, v, B, H, T, d, r, dil, &G, pad, rows, n_rows, out, n_threads, t, 0};
+        job_t j = {q, k, v, B, H, T, d, r, rad, one_sided, dil, &G, pad, rows, n_rows, out, n_threads, t, 0};
         jobs[t] = j;
     }
     for (int t = 1; t < n_threads; t++)
@@ -247,45 +263,68 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
 /* ------------------------------------------------------------------ */
 /* Exported entry points (plain C ABI for ctypes). */
 
-/* Full forward: out[B][H][T][d] in fp64.  Returns the thread count used,
- * or -1 on invalid arguments. */
+/* Full forward: out[B][H][T][d] in fp64.  radius: [H] per-head radii or
+ * NULL (then r for every head); one_sided: 0 two-sided, 1 one-sided.
+ * Returns the thread count used, or -1 on invalid arguments. */
+int lf_oracle_fwd2(const float *q, const float *k, const float *v, int B, int H, int T, int d,
+                   int r, const int *radius, int one_sided, const int *dilation,
+                   const int *global_idx, int n_global, const unsigned char *key_padding_mask,
+                   double *out, int n_threads) {
+    long long n = (long long)B * H * T;
+    return run(q, k, v, B, H, T, d, r, radius, one_sided, dilation, global_idx, n_global,
+               key_padding_mask, NULL, n, out, n_threads);
+}
+
 int lf_oracle_fwd(const float *q, const float *k, const float *v, int B, int H, int T, int d,
                   int r, const int *dilation, const int *global_idx, int n_global,
                   const unsigned char *key_padding_mask, double *out, int n_threads) {
-    long long n = (long long)B * H * T;
-    return run(q, k, v, B, H, T, d, r, dilation, global_idx, n_global, key_padding_mask,
-               NULL, n, out, n_threads);
+    return lf_oracle_fwd2(q, k, v, B, H, T, d, r, NULL, 0, dilation, global_idx, n_global,
+                          key_padding_mask, out, n_threads);
 }
 
 /* Selected rows only: rows[e] = (b*H + h)*T + i; out_rows[e][d]. */
+int lf_oracle_rows2(const float *q, const float *k, const float *v, int B, int H, int T, int d,
+                    int r, const int *radius, int one_sided, const int *dilation,
+                    const int *global_idx, int n_global, const unsigned char *key_padding_mask,
+                    const long long *rows, long long n_rows, double *out_rows, int n_threads) {
+    for (long long e = 0; e < n_rows; e++)
+        if (rows[e] < 0 || rows[e] >= (long long)B * H * T) return -1;
+    return run(q, k, v, B, H, T, d, r, radius, one_sided, dilation, global_idx, n_global,
+               key_padding_mask, rows, n_rows, out_rows, n_threads);
+}
+
 int lf_oracle_rows(const float *q, const float *k, const float *v, int B, int H, int T, int d,
                    int r, const int *dilation, const int *global_idx, int n_global,
                    const unsigned char *key_padding_mask, const long long *rows, long long n_rows,
                    double *out_rows, int n_threads) {
-    for (long long e = 0; e < n_rows; e++)
-        if (rows[e] < 0 || rows[e] >= (long long)B * H * T) return -1;
-    return run(q, k, v, B, H, T, d, r, dilation, global_idx, n_global, key_padding_mask,
-               rows, n_rows, out_rows, n_threads);
+    return lf_oracle_rows2(q, k, v, B, H, T, d, r, NULL, 0, dilation, global_idx, n_global,
+                           key_padding_mask, rows, n_rows, out_rows, n_threads);
 }
 
-/* N(i) of one query of sequence b, head stride delta: sorted positions
- * into idx (capacity T).  Returns |N(i)|, or -1 on invalid arguments. */
-int lf_oracle_neighbours(int T, int r, int delta, const int *global_idx, int n_global,
-                         const unsigned char *pad_row, int i, int *idx) {
-    if (T < 1 || r < 0 || delta < 1 || i < 0 || i >= T) return -1;
+/* N(i) of one query of sequence b, head radius r and stride delta: sorted
+ * positions into idx (capacity T).  Returns |N(i)|, or -1 on invalid
+ * arguments. */
+int lf_oracle_neighbours2(int T, int r, int delta, int one_sided, const int *global_idx, int n_global,
+                          const unsigned char *pad_row, int i, int *idx) {
+    if (T < 1 || r < 0 || delta < 1 || i < 0 || i >= T || (one_sided != 0 && one_sided != 1)) return -1;
     gset_t G;
     if (gset_make(&G, global_idx, n_global, T)) return -1;
-    int n = neighbours(T, r, delta, &G, pad_row, i, idx);
+    int n = neighbours(T, r, delta, one_sided, &G, pad_row, i, idx);
     free(G.pos);
     return n;
 }
 
+int lf_oracle_neighbours(int T, int r, int delta, const int *global_idx, int n_global,
+                         const unsigned char *pad_row, int i, int *idx) {
+    return lf_oracle_neighbours2(T, r, delta, 0, global_idx, n_global, pad_row, i, idx);
+}
+
 /* Sum over all (b, h, i) of |N(i)|: the number of (query, key) pairs the
  * softmax runs over.  Returns -1 on invalid arguments. */
-long long lf_oracle_count_pairs(int B, int H, int T, int r, const int *dilation,
-                                const int *global_idx, int n_global,
-                                const unsigned char *key_padding_mask) {
-    if (check_args(B, H, T, 1, r, dilation)) return -1;
+long long lf_oracle_count_pairs2(int B, int H, int T, int r, const int *radius, int one_sided,
+                                 const int *dilation, const int *global_idx, int n_global,
+                                 const unsigned char *key_padding_mask) {
+    if (check_args(B, H, T, 1, r, radius, one_sided, dilation)) return -1;
     gset_t G;
     if (gset_make(&G, global_idx, n_global, T)) return -1;
     int *nb = (int *)malloc(sizeof(int) * (size_t)T);
@@ -294,10 +333,17 @@ long long lf_oracle_count_pairs(int B, int H, int T, int r, const int *dilation,
     for (int b = 0; b < B; b++)
         for (int h = 0; h < H; h++) {
             int delta = dilation ? dilation[h] : 1;
+            int rh = radius ? radius[h] : r;
             const unsigned char *padrow = key_padding_mask ? key_padding_mask + (size_t)b * T : NULL;
-            for (int i = 0; i < T; i++) total += neighbours(T, r, delta, &G, padrow, i, nb);
+            for (int i = 0; i < T; i++) total += neighbours(T, rh, delta, one_sided, &G, padrow, i, nb);
         }
     free(nb);
     free(G.pos);
     return total;
+}
+
+long long lf_oracle_count_pairs(int B, int H, int T, int r, const int *dilation,
+                                const int *global_idx, int n_global,
+                                const unsigned char *key_padding_mask) {
+    return lf_oracle_count_pairs2(B, H, T, r, NULL, 0, dilation, global_idx, n_global, key_padding_mask);
 }

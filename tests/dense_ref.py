@@ -9,12 +9,15 @@ code with the oracle (which walks each query's neighbour list instead).
 import numpy as np
 
 
-def allowed_matrix(T, r, delta, globals_, pad_row):
-    """A[i, j] = True iff key j is in N(i) (no padding applied to rows here)."""
+def allowed_matrix(T, r, delta, globals_, pad_row, one_sided=False):
+    """A[i, j] = True iff key j is in N(i) (no padding applied to rows here).
+    One-sided: the window keeps only keys at or before the query."""
     i = np.arange(T)[:, None]
     j = np.arange(T)[None, :]
     dist = i - j
     local = (np.abs(dist) <= r * delta) & (dist % delta == 0)
+    if one_sided:
+        local &= dist >= 0
     g = np.zeros(T, dtype=bool)
     for x in globals_:
         g[x] = True
@@ -24,7 +27,8 @@ def allowed_matrix(T, r, delta, globals_, pad_row):
     return A
 
 
-def dense_masked_attention(q, k, v, r, dilation=None, globals_=(), pad=None):
+def dense_masked_attention(q, k, v, r, dilation=None, globals_=(), pad=None, one_sided=False):
+    """r: one radius, or a list with one radius per head."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -34,7 +38,8 @@ def dense_masked_attention(q, k, v, r, dilation=None, globals_=(), pad=None):
         pad_row = None if pad is None else np.asarray(pad[b]).astype(bool)
         for h in range(H):
             delta = 1 if dilation is None else int(dilation[h])
-            A = allowed_matrix(T, r, delta, globals_, pad_row)
+            rh = int(r) if np.isscalar(r) else int(r[h])
+            A = allowed_matrix(T, rh, delta, globals_, pad_row, one_sided)
             S = q[b, h] @ k[b, h].T / np.sqrt(d)
             S = np.where(A, S, -np.inf)
             rows_ok = A.any(axis=1)

@@ -17,7 +17,14 @@ one of them.  The pins:
   every key leaves the softmax unchanged; keys outside N(i) do not reach
   row i; a dilated head splits into delta undilated problems; global rows
   are dense rows; padded rows are zero;
-* the set definitions N(i) = N_local(i) U G and N(i) = all for i in G.
+* the set definitions N(i) = N_local(i) U G and N(i) = all for i in G;
+* per-head radii and one-sided windows (the window list of "Longformer长序列
+  处理", HF实践, and the one- or two-sided question of Longformer,
+  eightmm.github.io, "Implementation Reading"): the brute force with the
+  window taken per head and cut to keys at or before the query, the
+  one-sided closed form sum_i (min(i, r) + 1) = T(r+1) - r(r+1)/2, and the
+  one-sided dense limit equal to causal attention (torch's
+  scaled_dot_product_attention with is_causal, float64).
 """
 import numpy as np
 import torch
@@ -59,7 +66,10 @@ def random_cases(n, seed0=0, Ts=(1, 2, 7, 33, 64, 130, 257)):
         else:
             pad = (rng.random((B, T)) < 0.25).astype(np.uint8)
         q, k, v = _rand(1000 + c, B, H, T, d)
-        cases.append(dict(q=q, k=k, v=v, r=r, dil=dil, G=G, pad=pad))
+        # every third case one-sided, every other case one radius per head
+        one = c % 3 == 2
+        rr = [int(x) for x in rng.integers(0, T + 3, size=H)] if c % 2 else r
+        cases.append(dict(q=q, k=k, v=v, r=rr, dil=dil, G=G, pad=pad, one=one))
     return cases
 
 
@@ -68,11 +78,11 @@ def random_cases(n, seed0=0, Ts=(1, 2, 7, 33, 64, 130, 257)):
 
 def check_dense_bruteforce(lib=None, n=28, tol=1e-12):
     for c in random_cases(n):
-        y = oracle.fwd(c["q"], c["k"], c["v"], c["r"], c["dil"], c["G"], c["pad"], lib=lib)
+        y = oracle.fwd(c["q"], c["k"], c["v"], c["r"], c["dil"], c["G"], c["pad"], lib=lib, one_sided=c["one"])
         ref = dense_masked_attention(c["q"].numpy(), c["k"].numpy(), c["v"].numpy(), c["r"],
-                                     c["dil"], c["G"], c["pad"])
+                                     c["dil"], c["G"], c["pad"], c["one"])
         err = np.max(np.abs(y - ref)) if y.size else 0.0
-        assert err <= tol, f"oracle vs dense brute force: {err} (T={c['q'].shape[2]}, r={c['r']})"
+        assert err <= tol, f"oracle vs dense brute force: {err} (T={c['q'].shape[2]}, r={c['r']}, one={c['one']})"
 
 
 # --------------------------------------------------------------------------
@@ -108,6 +118,16 @@ def check_closed_form_counts(lib=None):
     for T, r, H in [(1024, 64, 2), (4096, 256, 12)]:
         per_head = (local_count(T, r) - (r + 1)) + T + (T - (r + 1))
         assert oracle.count_pairs(1, H, T, r, global_idx=[0], lib=lib) == per_head * H
+    # one-sided: row i keeps min(i, r) + 1 keys, T(r+1) - r(r+1)/2 in all for T >= r
+    for T, r in [(1024, 64), (4096, 256), (300, 7), (10, 9), (10, 3), (1, 0)]:
+        want = sum(min(i, r) + 1 for i in range(T))
+        assert want == T * (r + 1) - r * (r + 1) // 2
+        assert oracle.count_pairs(1, 1, T, r, lib=lib, one_sided=True) == want
+    # one radius per head: the sum of the per-head closed forms
+    rads = [0, 3, 64, 200]
+    assert oracle.count_pairs(2, 4, 1000, rads, lib=lib) == 2 * sum(local_count(1000, x) for x in rads)
+    assert oracle.count_pairs(1, 4, 1000, rads, lib=lib, one_sided=True) == sum(
+        1000 * (x + 1) - x * (x + 1) // 2 for x in rads)
     # 512 -> 8192 tokens: dense x256 exactly, fixed small window ~x16
     assert oracle.count_pairs(1, 1, 8192, 9000, lib=lib) == 256 * oracle.count_pairs(1, 1, 512, 9000, lib=lib)
     ratio = oracle.count_pairs(1, 1, 8192, 4, lib=lib) / oracle.count_pairs(1, 1, 512, 4, lib=lib)
@@ -136,6 +156,14 @@ def check_neighbour_sets(lib=None):
                 loc = {j for j in range(T) if abs(i - j) <= r * delta and (i - j) % delta == 0}
                 want = sorted((loc | set(G)) & set(valid))     # N_local(i) U G
             assert got == want, (T, r, delta, G, i, got, want)
+            # one-sided: the window part keeps the keys at or before i
+            got1 = oracle.neighbours(T, r, delta, i, G, pad, lib=lib, one_sided=True)
+            if (pad is not None and pad[i]) or i in G:
+                want1 = want
+            else:
+                loc1 = {j for j in range(T) if 0 <= i - j <= r * delta and (i - j) % delta == 0}
+                want1 = sorted((loc1 | set(G)) & set(valid))
+            assert got1 == want1, (T, r, delta, G, i, got1, want1)
 
 
 # --------------------------------------------------------------------------
@@ -149,25 +177,28 @@ def check_invariants(lib=None):
         pad = c["pad"]
         valid = np.ones((B, T), bool) if pad is None else ~pad.astype(bool)
         # v == 1 -> every valid row is exactly a convex combination of ones
-        y1 = oracle.fwd(q, k, torch.ones_like(v), c["r"], c["dil"], c["G"], pad, lib=lib)
+        one = c["one"]
+        y1 = oracle.fwd(q, k, torch.ones_like(v), c["r"], c["dil"], c["G"], pad, lib=lib, one_sided=one)
         for b in range(B):
             assert np.all(np.abs(y1[b][:, valid[b]] - 1.0) <= 1e-14)
             assert np.all(y1[b][:, ~valid[b]] == 0.0)
         # q == 0 -> uniform weights: the mean of v over N(i) (mask from dense_ref)
-        y0 = oracle.fwd(torch.zeros_like(q), k, v, c["r"], c["dil"], c["G"], pad, lib=lib)
+        y0 = oracle.fwd(torch.zeros_like(q), k, v, c["r"], c["dil"], c["G"], pad, lib=lib, one_sided=one)
         for b in range(B):
             for h in range(H):
-                A = allowed_matrix(T, c["r"], c["dil"][h], c["G"],
-                                   None if pad is None else pad[b])
+                rh = c["r"] if np.isscalar(c["r"]) else c["r"][h]
+                A = allowed_matrix(T, rh, c["dil"][h], c["G"],
+                                   None if pad is None else pad[b], one)
                 for i in range(T):
                     if not valid[b, i]:
                         continue
                     want = v[b, h].numpy().astype(np.float64)[A[i]].mean(axis=0)
                     assert np.max(np.abs(y0[b, h, i] - want)) <= 1e-13
         # shift invariance of the logits: k_j + c for every j
-        base = oracle.fwd(q, k, v, c["r"], c["dil"], c["G"], pad, lib=lib)
+        base = oracle.fwd(q, k, v, c["r"], c["dil"], c["G"], pad, lib=lib, one_sided=one)
         shift = torch.randn(B, H, 1, d, generator=torch.Generator().manual_seed(5))
-        ys = oracle.fwd(q, (k.double() + shift.double()).float(), v, c["r"], c["dil"], c["G"], pad, lib=lib)
+        ys = oracle.fwd(q, (k.double() + shift.double()).float(), v, c["r"], c["dil"], c["G"], pad, lib=lib,
+                        one_sided=one)
         # k + shift is rounded to float32, so compare against the oracle on the rounded keys'
         # exact effect: scores change by q.shift up to float32 rounding of k (~1e-7 relative)
         assert np.max(np.abs(ys - base)) <= 5e-5
@@ -196,6 +227,14 @@ def check_identity_and_dense_limits(lib=None):
         # globals do not change the dense limit
         yg = oracle.fwd(q, k, v, T + 5, None, [0, T - 1], None, lib=lib)
         assert np.max(np.abs(yg - ref)) <= 1e-12
+        # one-sided, r >= T - 1, no globals: textbook causal attention
+        yc = oracle.fwd(q, k, v, [T - 1, T + 2, 10 * T], None, [], None, lib=lib, one_sided=True)
+        refc = torch.nn.functional.scaled_dot_product_attention(q.double(), k.double(), v.double(),
+                                                                 is_causal=True).numpy()
+        assert np.max(np.abs(yc - refc)) <= 1e-12
+        # one-sided, r = 0: each row attends to itself only
+        y1 = oracle.fwd(q, k, v, 0, [2, 1, 3], [], None, lib=lib, one_sided=True)
+        assert np.array_equal(y1, v.numpy().astype(np.float64))
     # global rows: dense attention over the valid keys
     T = 50
     q, k, v = [torch.randn(1, 2, T, 16, generator=g) for _ in range(3)]
@@ -259,11 +298,13 @@ def check_dilation_split(lib=None):
 
 def check_rows_entry_point(lib=None):
     c = random_cases(3, seed0=9, Ts=(33, 64, 130))[2]
-    full = oracle.fwd(c["q"], c["k"], c["v"], c["r"], c["dil"], c["G"], c["pad"], lib=lib)
     B, H, T, d = c["q"].shape
     sel = np.random.default_rng(0).choice(B * H * T, size=min(50, B * H * T), replace=False)
-    part = oracle.rows(c["q"], c["k"], c["v"], c["r"], sel, c["dil"], c["G"], c["pad"], lib=lib)
-    assert np.array_equal(part, full.reshape(-1, d)[sel])
+    for one in (False, True):
+        full = oracle.fwd(c["q"], c["k"], c["v"], c["r"], c["dil"], c["G"], c["pad"], lib=lib, one_sided=one)
+        part = oracle.rows(c["q"], c["k"], c["v"], c["r"], sel, c["dil"], c["G"], c["pad"], lib=lib,
+                           one_sided=one)
+        assert np.array_equal(part, full.reshape(-1, d)[sel])
 
 
 ALL_CHECKS = [check_dense_bruteforce, check_closed_form_counts, check_neighbour_sets,

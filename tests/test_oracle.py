@@ -36,6 +36,9 @@ MUTANTS = [
     ("padded_query_not_zero", "if (pad && pad[i]) return 0;", ""),
     ("globals_padded_kept", "if (!(pad && pad[g])) out[n++] = g;\n        }", "out[n++] = g;\n        }"),
     ("q_row_offset", "jb->q + base + (size_t)i * jb->d", "jb->q + base + (size_t)(i + 1 < jb->T ? i + 1 : i) * jb->d"),
+    ("one_sided_ignored", "if (one_sided) thi = 0;", ""),
+    ("one_sided_wrong_side", "if (one_sided) thi = 0;", "if (one_sided) tlo = 0;"),
+    ("head_radius_ignored", "int rh = jb->rad ? jb->rad[h] : jb->r;", "int rh = jb->r;"),
 ]
 
 
