@@ -85,7 +85,7 @@ def cpu_baseline(inp, flops, seconds):
     threads = 0
     while True:
         _, threads = oracle.fwd(inp.q, inp.k, inp.v, inp.r, inp.dilation, inp.global_idx,
-                                inp.key_padding_mask, return_threads=True)
+                                inp.key_padding_mask, return_threads=True, one_sided=inp.one_sided)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1024:
@@ -179,7 +179,8 @@ def main():
     kpm = None if inp.key_padding_mask is None else inp.key_padding_mask.to(dev)
     B, H, T, d = q.shape
     stream = torch.cuda.current_stream(dev)
-    call = lf.Prepared(q, k, v, inp.r, inp.dilation, inp.global_idx, kpm, stream=stream)
+    call = lf.Prepared(q, k, v, inp.r, inp.dilation, inp.global_idx, kpm, stream=stream,
+                       one_sided=inp.one_sided)
 
     if args.profile_mode:
         # warmup calls, then more untimed calls for at least SETTLE_MS (the
@@ -207,7 +208,8 @@ def main():
               f"one {COPY_BYTES} B copy", flush=True)
         return
 
-    pairs = metrics.useful_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask)
+    pairs = metrics.useful_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
+                                 one_sided=inp.one_sided)
     flops = 4 * d * pairs
 
     # eager: back-to-back calls, events on the call stream (after the warmup
@@ -241,7 +243,8 @@ def main():
         side = torch.cuda.Stream(dev)
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            gcall = lf.Prepared(q, k, v, inp.r, inp.dilation, inp.global_idx, kpm, out=call.out, stream=side)
+            gcall = lf.Prepared(q, k, v, inp.r, inp.dilation, inp.global_idx, kpm, out=call.out, stream=side,
+                                one_sided=inp.one_sided)
             gcall()   # the workspace for this stream is allocated outside capture
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=side):
@@ -324,6 +327,7 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) q/k/v; no dataset, no weights)",
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "d": d, "r": inp.r,
+                   "one_sided": inp.one_sided,
                    "dilation": inp.dilation, "n_global": len(set(inp.global_idx)),
                    "padded": inp.key_padding_mask is not None, "useful_pairs": pairs,
                    "useful_gflop": round(flops / 1e9, 4), "parallelism": "single GPU",

@@ -97,6 +97,34 @@ lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v,
                         const uint8_t *key_padding_mask,
                         void *out, lf_dtype_t dtype, void *stream);
 
+/*
+ * lf_attn_fwd_ex -- lf_attn_fwd with one window radius per head and a
+ * choice of two-sided or one-sided windows.
+ *
+ * The window list of "Longformer长序列处理" (section HF实践: one window per
+ * layer, given as an int or a list) applied per head of one call, and the
+ * one- or two-sided question of Longformer (eightmm.github.io), section
+ * "Implementation Reading".
+ *
+ *   radius    HOST array [H] of radii r_h >= 0 (must not be NULL); head h
+ *             uses r_h where lf_attn_fwd uses r.  Read during the call only.
+ *   one_sided 0: the window of query i holds the class keys j with
+ *             |i - j| <= r_h delta_h (as lf_attn_fwd).  1: only those with
+ *             0 <= i - j <= r_h delta_h, the query and the keys before it.
+ *             Global rows and global keys are the same in both cases (a
+ *             global row sees every valid key; every row sees the globals).
+ *   All other arguments, the ownership and the error behaviour are those
+ *   of lf_attn_fwd; one_sided outside {0, 1} or a negative radius is
+ *   LF_E_INVALID.
+ */
+lf_status_t lf_attn_fwd_ex(const void *q, const void *k, const void *v,
+                           int B, int H, int T, int d,
+                           const int32_t *radius, int one_sided,
+                           const int32_t *dilation,
+                           const int32_t *global_idx, int n_global,
+                           const uint8_t *key_padding_mask,
+                           void *out, lf_dtype_t dtype, void *stream);
+
 /* Text describing the last non-OK status returned on the calling thread
  * (empty string if none).  The pointer stays valid until the next call on
  * this thread. */

@@ -47,6 +47,8 @@ def load():
     I = ctypes.c_int
     lib.lf_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I, P]
     lib.lf_attn_fwd.restype = I
+    lib.lf_attn_fwd_ex.argtypes = [P, P, P, I, I, I, I, P, I, P, P, I, P, P, I, P]
+    lib.lf_attn_fwd_ex.restype = I
     lib.lf_last_error.argtypes = []
     lib.lf_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -57,9 +59,16 @@ def last_error() -> str:
     return load().lf_last_error().decode()
 
 
+def _per_head(r):
+    """True when r is a list of per-head radii rather than one int."""
+    return not isinstance(r, int) and hasattr(r, "__len__")
+
+
 def raw_fwd(q_ptr, k_ptr, v_ptr, B, H, T, d, r, dilation, global_idx, n_global, kpm_ptr, out_ptr,
-            dtype, stream_ptr) -> int:
-    """Call lf_attn_fwd with raw integer device pointers; returns the status."""
+            dtype, stream_ptr, one_sided=False) -> int:
+    """Call the library with raw integer device pointers; returns the status.
+    ``r`` is one radius (lf_attn_fwd) or a list of H radii; a list or
+    ``one_sided`` goes to lf_attn_fwd_ex."""
     lib = load()
     dil = None
     if dilation is not None:
@@ -67,14 +76,23 @@ def raw_fwd(q_ptr, k_ptr, v_ptr, B, H, T, d, r, dilation, global_idx, n_global, 
     g = None
     if global_idx is not None:
         g = (ctypes.c_int32 * max(1, len(global_idx)))(*[int(x) for x in global_idx])
+    if _per_head(r) or one_sided:
+        rl = [int(x) for x in r] if _per_head(r) else [int(r)] * int(H)
+        rad = (ctypes.c_int32 * max(1, len(rl)))(*rl)
+        return lib.lf_attn_fwd_ex(q_ptr, k_ptr, v_ptr, int(B), int(H), int(T), int(d), rad,
+                                  int(bool(one_sided)), dil, g, int(n_global), kpm_ptr, out_ptr, int(dtype),
+                                  stream_ptr)
     return lib.lf_attn_fwd(q_ptr, k_ptr, v_ptr, int(B), int(H), int(T), int(d), int(r), dil, g,
                            int(n_global), kpm_ptr, out_ptr, int(dtype), stream_ptr)
 
 
-def attn_fwd(q, k, v, r: int, dilation: Optional[Sequence[int]] = None,
+def attn_fwd(q, k, v, r, dilation: Optional[Sequence[int]] = None,
              global_idx: Optional[Sequence[int]] = None, global_attention_mask=None,
-             key_padding_mask=None, out=None, stream=None):
+             key_padding_mask=None, out=None, stream=None, one_sided: bool = False):
     """Longformer sparse attention forward on torch tensors [B, H, T, 64].
+
+    ``r`` is the window radius, or a list with one radius per head;
+    ``one_sided`` keeps only the window keys at or before each query.
 
     ``global_attention_mask`` (a 0/1 tensor of shape [T] or [B, T], 1 =
     global, as in the Hugging Face convention) is turned into the index list
@@ -123,8 +141,10 @@ def attn_fwd(q, k, v, r: int, dilation: Optional[Sequence[int]] = None,
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if _per_head(r) and len(r) != H:
+        raise ValueError(f"r has {len(r)} radii for {H} heads")
     st = raw_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, r, dilation,
-                 gl if gl else None, len(gl), kpm_ptr, out.data_ptr(), dt, sptr)
+                 gl if gl else None, len(gl), kpm_ptr, out.data_ptr(), dt, sptr, one_sided)
     if st != LF_OK:
         raise LfError(st, last_error())
     return out
@@ -138,7 +158,7 @@ class Prepared:
     """
 
     def __init__(self, q, k, v, r, dilation=None, global_idx=None, key_padding_mask=None, out=None,
-                 stream=None):
+                 stream=None, one_sided=False):
         import torch
 
         lib = load()
@@ -156,9 +176,17 @@ class Prepared:
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-        self._fn = lib.lf_attn_fwd
-        self._args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, int(r), self._dil, self._g,
-                      len(gl), None if kpm is None else kpm.data_ptr(), self.out.data_ptr(), dt, sptr)
+        kptr = None if kpm is None else kpm.data_ptr()
+        if _per_head(r) or one_sided:
+            rl = [int(x) for x in r] if _per_head(r) else [int(r)] * H
+            self._rad = (ctypes.c_int32 * H)(*rl)
+            self._fn = lib.lf_attn_fwd_ex
+            self._args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, self._rad, int(bool(one_sided)),
+                          self._dil, self._g, len(gl), kptr, self.out.data_ptr(), dt, sptr)
+        else:
+            self._fn = lib.lf_attn_fwd
+            self._args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, int(r), self._dil, self._g,
+                          len(gl), kptr, self.out.data_ptr(), dt, sptr)
 
     def __call__(self):
         st = self._fn(*self._args)

@@ -180,6 +180,7 @@ struct Task {
     int nband;       // band (or dense) key blocks
     int key_end;     // keys >= key_end are out of range (class index)
     int split;       // global-row tasks: split index
+    int r, ra;       // band: the window reaches r keys back and ra forward (ra = 0 one-sided)
 };
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -224,15 +225,19 @@ __device__ __forceinline__ Task decode_task(const Plan& P, int t) {
         k.delta = delta;
         k.c = c;
         k.m0 = tile * BM;
-        const int r = P.r;
+        const int r = P.rad[h];
+        k.r = r;
+        k.ra = P.one_sided ? 0 : r;
         int lo_k = k.m0 - r; if (lo_k < 0) lo_k = 0;
-        int hi_k = k.m0 + BM - 1 + r; if (hi_k > k.n - 1) hi_k = k.n - 1;
+        int hi_k = k.m0 + BM - 1 + k.ra; if (hi_k > k.n - 1) hi_k = k.n - 1;
         k.kb_lo = lo_k / KBLK;
         k.nband = hi_k / KBLK - k.kb_lo + 1;
         k.key_end = k.n;
         k.split = 0;
     } else {
         k.kind = 1;
+        k.r = 0;
+        k.ra = 0;
         const int g = t - P.n_band_tasks;
         const int per_bh = P.n_split * P.n_ggroups;
         k.bh = g / per_bh;
@@ -326,13 +331,14 @@ __device__ __forceinline__ uint32_t lane_bits(uint32_t rows, int lg) {
     return (sh & 0xfu) | ((sh >> 4) & 0xf0u) | ((sh >> 8) & 0xf00u) | ((sh >> 12) & 0xf000u);
 }
 
-// band block whose rows are all real keys: keep kc in [lo, lo + 2r], where
-// kc is the element's key row minus 4*lg and lo = m - r - key0 - 4*lg
-__device__ __forceinline__ void mask_window(f32x16& s, int lo, int two_r) {
+// band block whose rows are all real keys: keep kc in [lo, lo + width], where
+// kc is the element's key row minus 4*lg and lo = m - r - key0 - 4*lg (the
+// window reaches r keys back and width - r forward)
+__device__ __forceinline__ void mask_window(f32x16& s, int lo, int width) {
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         const int kc = 8 * (i >> 2) + (i & 3);
-        s[i] = (uint32_t)(kc - lo) <= (uint32_t)two_r ? s[i] : kNegInf;
+        s[i] = (uint32_t)(kc - lo) <= (uint32_t)width ? s[i] : kNegInf;
     }
 }
 
@@ -343,8 +349,9 @@ __device__ __forceinline__ void mask_bits(f32x16& s, uint32_t keep16) {
 }
 
 // global-key block: drop unused / padded slots and keys already inside this
-// query's window (the band counts those)
-__device__ __forceinline__ void mask_global(f32x16& s, uint32_t bad, const int* gcls, int m, int r, int lg) {
+// query's window, class distance in [-r, width - r] (the band counts those)
+__device__ __forceinline__ void mask_global(f32x16& s, uint32_t bad, const int* gcls, int m, int r, int width,
+                                            int lg) {
     const uint32_t badl = lane_bits(bad, lg);
 #pragma unroll
     for (int q4 = 0; q4 < 4; q4++) {
@@ -353,7 +360,7 @@ __device__ __forceinline__ void mask_global(f32x16& s, uint32_t bad, const int* 
         for (int e = 0; e < 4; e++) {
             const int i = 4 * q4 + e;
             const int dk = (int)g4[e] - m;
-            const bool ok = ((badl >> i) & 1u) == 0u && (uint32_t)(dk + r) > (uint32_t)(2 * r);
+            const bool ok = ((badl >> i) & 1u) == 0u && (uint32_t)(dk + r) > (uint32_t)width;
             s[i] = ok ? s[i] : kNegInf;
         }
     }
@@ -648,7 +655,7 @@ void tile_kernel(const Args A) {
     // kernel-argument scalars used inside the loop live in registers (a value
     // select between an LDS table entry and a kernel argument would otherwise
     // become a flat load, which waits on every load in flight)
-    const int T = P.T, n_g = P.n_g, r = P.r;
+    const int T = P.T, n_g = P.n_g, r = tk.r, ra = tk.ra;
     const uint32_t head_bytes = (uint32_t)T * ROWB;
     const void* kplanes = NP == 1 ? A.k : P.kp;   // bf16 input is its own plane
     const void* vplanes = NP == 1 ? A.v : P.vp;
@@ -672,7 +679,7 @@ void tile_kernel(const Args A) {
     int wb_lo = 0, wb_hi = -1;
     if (tk.kind == 0) {
         int a = mq0 - r; if (a < 0) a = 0;
-        int z = mq0 + 31 + r; if (z > tk.n - 1) z = tk.n - 1;
+        int z = mq0 + 31 + ra; if (z > tk.n - 1) z = tk.n - 1;
         wb_lo = a / KBLK;
         wb_hi = z / KBLK;
     }
@@ -716,9 +723,9 @@ void tile_kernel(const Args A) {
         if (tk.kind == 0) {
             j_lo = wb_lo - tk.kb_lo;
             j_hi = wb_hi - tk.kb_lo;
-            // key0 = 32 (kb_lo + j) >= mq0 + 31 - r, key0 + 31 <= mq0 + r, key0 + 32 <= key_end
+            // key0 = 32 (kb_lo + j) >= mq0 + 31 - r, key0 + 31 <= mq0 + ra, key0 + 32 <= key_end
             ji_lo = ((mq0 + 31 - r + 31) >> 5) - tk.kb_lo;
-            ji_hi = min((mq0 + r - 31) >> 5, (tk.key_end - 32) >> 5) - tk.kb_lo;
+            ji_hi = min((mq0 + ra - 31) >> 5, (tk.key_end - 32) >> 5) - tk.kb_lo;
         } else {
             ji_hi = ((tk.key_end - 32) >> 5) - tk.kb_lo;
         }
@@ -905,7 +912,7 @@ void tile_kernel(const Args A) {
     // ---- vector-path global keys: the phase-0 waves (the phases are merged
     // at the end, so one of them takes the keys), every query, each key in
     // turn, unless the key is padded or already in the query's window (its
-    // class, |class distance| <= r: the band counts it)
+    // class, class distance in [-r, ra]: the band counts it)
     if (gvec && ph == 0) {
         for (int g = 0; g < n_g; g++) {
             const int pos = P.glob[g];
@@ -915,7 +922,7 @@ void tile_kernel(const Args A) {
             const bool in_class = dpos >= 0 && dpos % tk.delta == 0;
             const int dk = dpos / tk.delta - m_me;
             const bool padded = PAD && padrow[pos] != 0;
-            const bool ok = my_pos >= 0 && !padded && !(in_class && dk >= -r && dk <= r);
+            const bool ok = my_pos >= 0 && !padded && !(in_class && dk >= -r && dk <= ra);
             gkey_fold<NP>(W, gk, ok ? s * kScaleLog2 : kNegInf, lg);
         }
     }
@@ -964,11 +971,11 @@ void tile_kernel(const Args A) {
         if (bad != 0xffffffffu) {
             auto mask = [&](f32x16& x) {
                 if (ANY_GLOBAL && !band) {
-                    mask_global(x, bad, gcls + (jb - nb) * KBLK, m_me, r, lg);
+                    mask_global(x, bad, gcls + (jb - nb) * KBLK, m_me, r, r + ra, lg);
                 } else if (!(j >= ji_lo && j <= ji_hi && bad == 0u)) {
                     if (tk.kind == 0) {
                         const int key0 = (tk.kb_lo + j) * KBLK;
-                        mask_window(x, m_me - r - key0 - 4 * lg, 2 * r);
+                        mask_window(x, m_me - r - key0 - 4 * lg, r + ra);
                     }
                     if (bad != 0u) mask_bits(x, ~lane_bits(bad, lg));
                 }

@@ -132,10 +132,14 @@ lf_status_t upload_plan(Workspace &w, const lfk::Plan &P, void *stream, const lf
 
 extern "C" const char *lf_last_error(void) { return g_err.c_str(); }
 
-extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T,
-                                   int d, int r, const int32_t *dilation, const int32_t *global_idx,
-                                   int n_global, const uint8_t *key_padding_mask, void *out,
-                                   lf_dtype_t dtype, void *stream) {
+namespace {
+
+// The call behind both entry points: radius is NULL (r for every head) or
+// one radius per head.
+lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T, int d, int r,
+                     const int32_t *radius, int one_sided, const int32_t *dilation,
+                     const int32_t *global_idx, int n_global, const uint8_t *key_padding_mask, void *out,
+                     lf_dtype_t dtype, void *stream) {
     g_err.clear();
     // ---- argument checks: no HIP call before all of them pass
     if (!q || !k || !v || !out) return fail(LF_E_INVALID, "q, k, v and out must be non-null");
@@ -145,6 +149,10 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
     if (H > LF_MAX_HEADS) return fail(LF_E_UNSUPPORTED, "H = %d exceeds %d", H, LF_MAX_HEADS);
     if (T > LF_MAX_SEQ) return fail(LF_E_UNSUPPORTED, "T = %d exceeds %d", T, LF_MAX_SEQ);
     if (r < 0) return fail(LF_E_INVALID, "window radius r = %d must be >= 0", r);
+    if (one_sided != 0 && one_sided != 1) return fail(LF_E_INVALID, "one_sided = %d must be 0 or 1", one_sided);
+    if (radius)
+        for (int h = 0; h < H; h++)
+            if (radius[h] < 0) return fail(LF_E_INVALID, "radius[%d] = %d must be >= 0", h, radius[h]);
     if (n_global < 0) return fail(LF_E_INVALID, "n_global = %d must be >= 0", n_global);
     if (n_global > 0 && !global_idx) return fail(LF_E_INVALID, "global_idx is NULL with n_global = %d", n_global);
     if (dilation) {
@@ -179,7 +187,14 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
     lfk::Plan P;
     std::memset(&P, 0, sizeof P);
     P.B = B; P.H = H; P.T = T;
-    P.r = r < T ? r : T;  // |i - j| < T always, so larger radii change nothing
+    // |i - j| < T always, so radii beyond T change nothing
+    P.r = 0;
+    for (int h = 0; h < H; h++) {
+        const int rh = radius ? radius[h] : r;
+        P.rad[h] = rh < T ? rh : T;
+        P.r = std::max(P.r, P.rad[h]);
+    }
+    P.one_sided = one_sided;
     P.n_g = (int)G.size();
     for (int i = 0; i < P.n_g; i++) P.glob[i] = G[i];
     long long start = 0;
@@ -256,4 +271,25 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
     hipError_t e = lfk_launch(&A, &P, dtype == LF_BF16, stream);
     if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
     return LF_OK;
+}
+
+}  // namespace
+
+extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T,
+                                   int d, int r, const int32_t *dilation, const int32_t *global_idx,
+                                   int n_global, const uint8_t *key_padding_mask, void *out,
+                                   lf_dtype_t dtype, void *stream) {
+    return attn_fwd(q, k, v, B, H, T, d, r, nullptr, 0, dilation, global_idx, n_global, key_padding_mask,
+                    out, dtype, stream);
+}
+
+extern "C" lf_status_t lf_attn_fwd_ex(const void *q, const void *k, const void *v, int B, int H, int T,
+                                      int d, const int32_t *radius, int one_sided, const int32_t *dilation,
+                                      const int32_t *global_idx, int n_global,
+                                      const uint8_t *key_padding_mask, void *out, lf_dtype_t dtype,
+                                      void *stream) {
+    g_err.clear();
+    if (!radius) return fail(LF_E_INVALID, "radius must be a host array of H radii");
+    return attn_fwd(q, k, v, B, H, T, d, 0, radius, one_sided, dilation, global_idx, n_global,
+                    key_padding_mask, out, dtype, stream);
 }

@@ -43,6 +43,8 @@ struct Plan {
     int n_tasks;             // band + global-row tasks
     int head_start[LF_MAX_HEADS + 1];  // band-task prefix over heads
     int32_t dil[LF_MAX_HEADS];      // 32-bit: a head's entry is one scalar load
+    int32_t rad[LF_MAX_HEADS];      // window radius per head (clamped to T)
+    int one_sided;                  // 1: the window keeps the keys at or before the query
     int32_t glob[LF_MAX_GLOBALS];
 };
 

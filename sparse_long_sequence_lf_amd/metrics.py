@@ -17,9 +17,12 @@ from typing import Optional, Sequence
 import numpy as np
 
 
-def pair_counts(B: int, H: int, T: int, r: int, dilation: Optional[Sequence[int]] = None,
-                global_idx: Optional[Sequence[int]] = None, key_padding_mask=None) -> np.ndarray:
-    """|N(i)| for every row, as an int64 array [B, H, T] (padded rows give 0)."""
+def pair_counts(B: int, H: int, T: int, r, dilation: Optional[Sequence[int]] = None,
+                global_idx: Optional[Sequence[int]] = None, key_padding_mask=None,
+                one_sided: bool = False) -> np.ndarray:
+    """|N(i)| for every row, as an int64 array [B, H, T] (padded rows give 0).
+    ``r`` is one radius or one per head; ``one_sided`` windows keep only the
+    keys at or before the query."""
     G = np.unique(np.asarray(list(global_idx) if global_idx is not None else [], dtype=np.int64))
     if key_padding_mask is None:
         valid = np.ones((B, T), dtype=bool)
@@ -37,14 +40,16 @@ def pair_counts(B: int, H: int, T: int, r: int, dilation: Optional[Sequence[int]
         Gv = G[vb[G]] if G.size else G          # globals that are real (unpadded) keys
         for h in range(H):
             delta = int(dilation[h]) if dilation is not None else 1
+            rb = int(r) if np.isscalar(r) else int(r[h])   # reach back
+            ra = 0 if one_sided else rb                    # reach forward
             cnt = np.zeros(T, dtype=np.int64)
             for c in range(min(delta, T)):
                 pos = np.arange(c, T, delta)
                 n = pos.size
                 pre = np.concatenate([[0], np.cumsum(vb[pos].astype(np.int64))])
                 m_ = np.arange(n)
-                lo = np.maximum(0, m_ - r)
-                hi = np.minimum(n, m_ + r + 1)
+                lo = np.maximum(0, m_ - rb)
+                hi = np.minimum(n, m_ + ra + 1)
                 win = pre[hi] - pre[lo]                  # valid keys of the window
                 # valid globals not already inside the window: add |Gv| and take
                 # back one for every window that contains a valid global of class c
@@ -53,8 +58,9 @@ def pair_counts(B: int, H: int, T: int, r: int, dilation: Optional[Sequence[int]
                 if gc.size:
                     diff = np.zeros(n + 1, dtype=np.int64)
                     mg = (gc - c) // delta
-                    np.add.at(diff, np.maximum(0, mg - r), -1)
-                    np.add.at(diff, np.minimum(n, mg + r + 1), 1)
+                    # key mg is in the window of the queries m in [mg - ra, mg + rb]
+                    np.add.at(diff, np.maximum(0, mg - ra), -1)
+                    np.add.at(diff, np.minimum(n, mg + rb + 1), 1)
                     extra += np.cumsum(diff[:-1])
                 cnt[pos] = win + extra
             cnt[is_g] = n_valid                          # global rows read every valid key

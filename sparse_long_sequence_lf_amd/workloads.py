@@ -53,6 +53,8 @@ class Workload:
     len_lo: Optional[int] = None
     len_hi: Optional[int] = None
     description: str = ""
+    radius: Optional[tuple] = None  # one radius per head (replaces r), None = r for all
+    one_sided: bool = False         # window keeps only the keys at or before the query
 
 
 WORKLOADS: List[Workload] = [
@@ -71,6 +73,14 @@ WORKLOADS: List[Workload] = [
     Workload("bf16-b4h16t16384-r512-g8-pad", 1005, 4, 16, 16384, 64, 512, "bf16", scale=0.5,
              n_random_globals=8, random_global_hi_from_min_len=True, len_lo=8192, len_hi=16384,
              description="B=4 H=16 T=16384 r=512, 8 random globals, valid lengths U{8192..16384} with right padding, bf16 0.5*N(0,1)"),
+    # the two window forms beyond the five configurations: one-sided windows and one
+    # radius per head (the per-layer window list applied per head)
+    Workload("bf16-b1h12t4096-r256-g1-onesided", 1006, 1, 12, 4096, 64, 256, "bf16",
+             fixed_globals=(0,), one_sided=True,
+             description="the headline shape with one-sided windows (the query and the 256 keys before it), global at 0"),
+    Workload("bf16-b1h12t4096-rhead-g1", 1007, 1, 12, 4096, 64, 512, "bf16",
+             fixed_globals=(0,), radius=(32, 32, 64, 64, 128, 128, 256, 256, 384, 384, 512, 512),
+             description="one radius per head, 32..512 in pairs, global at 0, bf16 N(0,1)"),
 ]
 
 
@@ -105,6 +115,7 @@ class Inputs:
     lengths: Optional[List[int]]
     key_padding_mask: Optional[torch.Tensor]  # uint8 [B][T], nonzero = padded
     extra: dict = field(default_factory=dict)
+    one_sided: bool = False                   # r: one radius, or a list with one per head
 
 
 def _draw_qkv(seed, B, H, T, d, scale, dtype):
@@ -157,7 +168,8 @@ def make_inputs(w: Workload, dtype: Optional[str] = None, T: Optional[int] = Non
     dil = list(w.dilation)[:H_] if w.dilation else None
     if dil is not None and len(dil) < H_:
         dil = dil + [1] * (H_ - len(dil))
-    return Inputs(q, k, v, w.r, dil, glob, lengths, kpm)
+    r = list(w.radius)[:H_] if w.radius else w.r
+    return Inputs(q, k, v, r, dil, glob, lengths, kpm, one_sided=w.one_sided)
 
 
 def random_case(seed: int, B: int, H: int, T: int, d: int = 64, dtype: str = "f32",

@@ -30,7 +30,8 @@ def gpu_fwd(inp, q=None, k=None, v=None):
         kd = k.to("cuda:0")
     if v is not None:
         vd = v.to("cuda:0")
-    out = lf.attn_fwd(qd, kd, vd, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm)
+    out = lf.attn_fwd(qd, kd, vd, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm,
+                      one_sided=inp.one_sided)
     torch.cuda.synchronize()
     return out
 
@@ -38,7 +39,7 @@ def gpu_fwd(inp, q=None, k=None, v=None):
 def oracle_full(inp, q=None, k=None, v=None):
     return oracle.fwd(inp.q if q is None else q, inp.k if k is None else k,
                       inp.v if v is None else v, inp.r, inp.dilation, inp.global_idx,
-                      inp.key_padding_mask)
+                      inp.key_padding_mask, one_sided=inp.one_sided)
 
 
 def max_err(gpu_out, ref):
@@ -62,7 +63,8 @@ def sample_rows(inp, n_random, seed=0):
                 for i in (c, c + delta, (T - 1 - c) - ((T - 1 - c) - c) % delta):
                     if 0 <= i < T:
                         rows.add(base + i)
-            for x in (0, 1, inp.r, inp.r + 1, T - 1 - inp.r, T - 2, T - 1):
+            rh = inp.r if isinstance(inp.r, int) else inp.r[h]
+            for x in (0, 1, rh, rh + 1, T - 1 - rh, T - 2, T - 1):
                 if 0 <= x < T:
                     rows.add(base + x)
             if inp.lengths is not None:

@@ -113,3 +113,43 @@ def test_duplicate_globals_count_once(lib):
               q=1 << 48, k=2 << 48, v=3 << 48, out=4 << 48)
     assert st == lf.LF_E_UNSUPPORTED
     assert "workgroups" in lf.last_error()
+
+
+def call_ex(radius, one_sided, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return lf.raw_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], radius, a["dil"],
+                      a["g"], a["ng"], a["kpm"], a["out"], a["dtype"], None, one_sided)
+
+
+BAD_EX = [
+    ("radius_negative", dict(radius=[3, -1], one_sided=False), lf.LF_E_INVALID),
+    ("one_sided_two", dict(radius=[3, 4], one_sided=2), lf.LF_E_INVALID),
+    ("d_32", dict(radius=[3, 4], one_sided=True, d=32), lf.LF_E_UNSUPPORTED),
+    ("null_q", dict(radius=[3, 4], one_sided=True, q=None), lf.LF_E_INVALID),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_EX, ids=[b[0] for b in BAD_EX])
+def test_ex_invalid_arguments_rejected(lib, name, kw, status):
+    kw = dict(kw)
+    radius, one = kw.pop("radius"), kw.pop("one_sided")
+    if one == 2:
+        # raw_fwd passes a boolean; the integer 2 goes straight to the C entry point
+        a = dict(GOOD)
+        rad = (ctypes.c_int32 * 2)(*radius)
+        dil = (ctypes.c_int32 * 2)(*a["dil"])
+        g = (ctypes.c_int32 * 1)(*a["g"])
+        st = lib.lf_attn_fwd_ex(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], rad, 2, dil, g,
+                                a["ng"], None, a["out"], a["dtype"], None)
+    else:
+        st = call_ex(radius, one, **kw)
+    assert st == status, (name, st, lf.last_error())
+    assert lf.last_error() != ""
+
+
+def test_ex_null_radius_rejected(lib):
+    a = dict(GOOD)
+    st = lib.lf_attn_fwd_ex(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], None, 0, None, None, 0,
+                            None, a["out"], a["dtype"], None)
+    assert st == lf.LF_E_INVALID and "radius" in lf.last_error()

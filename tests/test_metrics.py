@@ -21,6 +21,20 @@ def test_counter_matches_enumeration_random(seed):
     assert metrics.useful_pairs(B, H, T, r, dil, G, pad) == want
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_counter_matches_enumeration_per_head_one_sided(seed):
+    rng = np.random.default_rng(100 + seed)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 5))
+    T = int(rng.integers(1, 300))
+    rads = [int(x) for x in rng.integers(0, T + 3, size=H)]
+    dil = [int(x) for x in rng.integers(1, 6, size=H)]
+    G = [int(x) for x in rng.integers(0, T, size=int(rng.integers(0, 7)))]
+    pad = (rng.random((B, T)) < 0.2).astype(np.uint8) if seed % 2 else None
+    one = seed % 3 != 0
+    want = oracle.count_pairs(B, H, T, rads, dil, G, pad, one_sided=one)
+    assert metrics.useful_pairs(B, H, T, rads, dil, G, pad, one_sided=one) == want
+
+
 @pytest.mark.parametrize("name", [w.name for w in W.WORKLOADS])
 def test_counter_matches_enumeration_workloads(name):
     w = W.workload(name)
@@ -29,8 +43,10 @@ def test_counter_matches_enumeration_workloads(name):
         kw = dict(T=4096, H=4)
     inp = W.make_inputs(w, **kw)
     B, H, T, d = inp.q.shape
-    want = oracle.count_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask)
-    got = metrics.useful_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask)
+    want = oracle.count_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
+                              one_sided=inp.one_sided)
+    got = metrics.useful_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
+                               one_sided=inp.one_sided)
     assert got == want
 
 

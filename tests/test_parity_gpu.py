@@ -29,6 +29,8 @@ REDUCED = {
     "bf16-b1h12t4096-r128-dil": dict(T=1100),
     "bf16-b2h12t4096-r256-g68": dict(T=1000, H=6),
     "bf16-b4h16t16384-r512-g8-pad": dict(T=2100, H=3),
+    "bf16-b1h12t4096-r256-g1-onesided": dict(T=1300),
+    "bf16-b1h12t4096-rhead-g1": dict(T=1400),
 }
 
 
@@ -57,7 +59,7 @@ def test_workload_full_size_sampled(name, dtype):
     out = gpu_fwd(inp)
     rows = sample_rows(inp, n_random=1500, seed=w.seed)
     ref = oracle.rows(inp.q, inp.k, inp.v, inp.r, rows, inp.dilation, inp.global_idx,
-                      inp.key_padding_mask)
+                      inp.key_padding_mask, one_sided=inp.one_sided)
     got = out.float().cpu().double().reshape(-1, w.d).numpy()[rows]
     err = float(np.max(np.abs(got - ref)))
     print(f"  {len(rows)} rows, max abs err {err:.3e}", flush=True)
@@ -81,6 +83,25 @@ def test_edge_cases(T, pad):
         for seed in range(2):
             inp = W.random_case(seed * 1000 + T, B=2, H=3, T=T, dtype=dt, pad=pad)
             print(f"case T={T} pad={pad} dt={dt} seed={seed} r={inp.r} dil={inp.dilation} "
+                  f"G={inp.global_idx}", flush=True)
+            out = gpu_fwd(inp)
+            err = max_err(out, oracle_full(inp))
+            assert err <= TOL[dt], err
+
+
+# ---- one radius per head and one-sided windows (lf_attn_fwd_ex): ragged T,
+# radii around T, dilation, duplicated globals, every padding pattern
+@pytest.mark.parametrize("one_sided", [True, False])
+@pytest.mark.parametrize("T", [1, 2, 31, 33, 64, 65, 130, 257, 300])
+def test_window_forms(T, one_sided):
+    for dt in ("f32", "bf16"):
+        for seed, pad in enumerate(("none", "right", "random")):
+            base = W.random_case(seed * 7919 + T + 11, B=2, H=3, T=T, dtype=dt, pad=pad)
+            rng = np.random.default_rng(seed * 31 + T)
+            rads = [int(x) for x in rng.integers(0, T + 3, size=3)]
+            inp = W.Inputs(base.q, base.k, base.v, rads, base.dilation, base.global_idx, base.lengths,
+                           base.key_padding_mask, one_sided=one_sided)
+            print(f"case T={T} one_sided={one_sided} dt={dt} pad={pad} radii={rads} dil={inp.dilation} "
                   f"G={inp.global_idx}", flush=True)
             out = gpu_fwd(inp)
             err = max_err(out, oracle_full(inp))
@@ -119,7 +140,8 @@ def test_named_edge_cases(dt):
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_tracer_counts_exact_neighbour_sets(dt):
     for name in ["bf16-b1h12t4096-r256-g1", "bf16-b1h12t4096-r128-dil", "bf16-b2h12t4096-r256-g68",
-                 "bf16-b4h16t16384-r512-g8-pad"]:
+                 "bf16-b4h16t16384-r512-g8-pad", "bf16-b1h12t4096-r256-g1-onesided",
+                 "bf16-b1h12t4096-rhead-g1"]:
         w = W.workload(name)
         inp = W.make_inputs(w, dtype=dt, T=min(w.T, 1500), H=min(w.H, 4))
         B, H, T, d = inp.q.shape
