@@ -610,9 +610,20 @@ void tile_kernel(const Args A) {
         const int nb = P.n_band_tasks, ng = P.n_tasks - P.n_band_tasks;
         const int nb_x = (nb >> 3) + (xcd < (nb & 7)), nb_o = xcd * (nb >> 3) + min(xcd, nb & 7);
         const int ng_x = (ng >> 3) + (xcd < (ng & 7)), ng_o = xcd * (ng >> 3) + min(xcd, ng & 7);
-        if (slot_in_xcd < ng_x) task_id = nb + ng_o + slot_in_xcd;
-        else if (slot_in_xcd - ng_x < nb_x) task_id = nb_o + (slot_in_xcd - ng_x);
-        else return;
+        if (slot_in_xcd < ng_x) {
+            task_id = nb + ng_o + slot_in_xcd;
+        } else if (P.band_chunk > 0) {
+            // tiles of unequal cost (one radius per head): runs of C tiles go
+            // to the dies in turn, so that every die gets a share of each head
+            const int C = P.band_chunk, sb = slot_in_xcd - ng_x;
+            const int t = ((sb / C) * 8 + xcd) * C + sb % C;
+            if (t >= nb) return;
+            task_id = t;
+        } else if (slot_in_xcd - ng_x < nb_x) {
+            task_id = nb_o + (slot_in_xcd - ng_x);
+        } else {
+            return;
+        }
     }
     const Task tk = decode_task<QB>(P, task_id);
     if constexpr (PAD) {
@@ -1214,7 +1225,9 @@ __global__ __launch_bounds__(256) void split_planes_kernel(const float* __restri
 // ceil(n/8) global-row slots
 extern "C" int lfk_grid(const lfk::Plan* P) {
     const int nb = P->n_band_tasks, ng = P->n_tasks - P->n_band_tasks;
-    return 8 * ((nb + 7) / 8 + (ng + 7) / 8);
+    const int C = P->band_chunk;
+    const int band_slots = C > 0 ? ((nb + C - 1) / C + 7) / 8 * C : (nb + 7) / 8;
+    return 8 * (band_slots + (ng + 7) / 8);
 }
 
 // A: kernel argument (A->plan is the device copy of *P); P: host copy of the plan

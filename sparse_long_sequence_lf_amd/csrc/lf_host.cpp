@@ -195,6 +195,11 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
         P.r = std::max(P.r, P.rad[h]);
     }
     P.one_sided = one_sided;
+    // heads with unequal radii make tiles of unequal cost: deal runs of 8
+    // tiles to the dies in turn instead of one contiguous eighth per die
+    P.band_chunk = 0;
+    for (int h = 1; h < H; h++)
+        if (P.rad[h] != P.rad[0]) P.band_chunk = 8;
     P.n_g = (int)G.size();
     for (int i = 0; i < P.n_g; i++) P.glob[i] = G[i];
     long long start = 0;

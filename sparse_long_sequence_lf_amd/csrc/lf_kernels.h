@@ -45,6 +45,8 @@ struct Plan {
     int32_t dil[LF_MAX_HEADS];      // 32-bit: a head's entry is one scalar load
     int32_t rad[LF_MAX_HEADS];      // window radius per head (clamped to T)
     int one_sided;                  // 1: the window keeps the keys at or before the query
+    int band_chunk;                 // 0: each die takes a contiguous eighth of the band tiles;
+                                    // C > 0: runs of C tiles are dealt to the dies in turn
     int32_t glob[LF_MAX_GLOBALS];
 };
 
