@@ -31,13 +31,13 @@ def open_library(path):
     lib.lf_oracle_neighbours.restype = I
     lib.lf_oracle_count_pairs.argtypes = [I, I, I, I, P, P, I, P]
     lib.lf_oracle_count_pairs.restype = LL
-    lib.lf_oracle_fwd2.argtypes = [P, P, P, I, I, I, I, I, P, I, P, P, I, P, P, I]
+    lib.lf_oracle_fwd2.argtypes = [P, P, P, I, I, I, I, I, P, I, P, I, P, P, I, P, P, I]
     lib.lf_oracle_fwd2.restype = I
-    lib.lf_oracle_rows2.argtypes = [P, P, P, I, I, I, I, I, P, I, P, P, I, P, P, LL, P, I]
+    lib.lf_oracle_rows2.argtypes = [P, P, P, I, I, I, I, I, P, I, P, I, P, P, I, P, P, LL, P, I]
     lib.lf_oracle_rows2.restype = I
-    lib.lf_oracle_neighbours2.argtypes = [I, I, I, I, P, I, P, I, P]
+    lib.lf_oracle_neighbours2.argtypes = [I, I, I, I, P, I, P, I, P, I, P]
     lib.lf_oracle_neighbours2.restype = I
-    lib.lf_oracle_count_pairs2.argtypes = [I, I, I, I, P, I, P, P, I, P]
+    lib.lf_oracle_count_pairs2.argtypes = [I, I, I, I, P, I, P, I, P, P, I, P]
     lib.lf_oracle_count_pairs2.restype = LL
     return lib
 
@@ -77,6 +77,20 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+RAND_BLOCK = 64
+
+
+def _rand_blocks(rb, H, T):
+    """(array, n_rand): the random key blocks [H][ceil(T/64)][n_rand] or (None, 0)."""
+    if rb is None:
+        return None, 0
+    a = np.ascontiguousarray(np.asarray(rb, dtype=np.int32))
+    nqb = (T + RAND_BLOCK - 1) // RAND_BLOCK
+    if a.ndim != 3 or a.shape[0] != H or a.shape[1] != nqb:
+        raise ValueError("random blocks must be [H][ceil(T/64)][n_rand]")
+    return a, int(a.shape[2])
+
+
 def _radius(r, H):
     """(scalar r, per-head array or None): r is an int, or one radius per head."""
     if isinstance(r, (int, np.integer)):
@@ -88,68 +102,75 @@ def _radius(r, H):
 
 
 def fwd(q, k, v, r, dilation=None, global_idx=None, key_padding_mask=None, n_threads=0,
-        return_threads=False, lib=None, one_sided=False):
+        return_threads=False, lib=None, one_sided=False, random_blocks=None):
     """Full forward in fp64: returns out[B][H][T][d] (numpy float64).  ``r``
     is one radius or one per head; ``one_sided`` keeps only the keys at or
-    before each query in its window."""
+    before each query in its window; ``random_blocks`` [H][ceil(T/64)][n]
+    lists the key blocks of 64 each query block of 64 also attends to."""
     lib = lib or _load()
     qf, kf, vf = _f32(q), _f32(k), _f32(v)
     B, H, T, d = qf.shape
     r0, rad = _radius(r, H)
+    rb, nr = _rand_blocks(random_blocks, H, T)
     dil = _i32(dilation)
     g = _i32(global_idx if global_idx is not None else [])
     pad = _u8(key_padding_mask)
     out = np.zeros((B, H, T, d), dtype=np.float64)
     nt = lib.lf_oracle_fwd2(_ptr(qf), _ptr(kf), _ptr(vf), B, H, T, d, r0, _ptr(rad), int(bool(one_sided)),
-                            _ptr(dil), _ptr(g), int(g.size), _ptr(pad), _ptr(out), int(n_threads))
+                            _ptr(rb), nr, _ptr(dil), _ptr(g), int(g.size), _ptr(pad), _ptr(out), int(n_threads))
     if nt < 0:
         raise ValueError("oracle rejected its arguments")
     return (out, nt) if return_threads else out
 
 
 def rows(q, k, v, r, rows_flat, dilation=None, global_idx=None, key_padding_mask=None,
-         n_threads=0, return_threads=False, lib=None, one_sided=False):
+         n_threads=0, return_threads=False, lib=None, one_sided=False, random_blocks=None):
     """Selected output rows: rows_flat[e] = (b*H + h)*T + i -> out[e][d]."""
     lib = lib or _load()
     qf, kf, vf = _f32(q), _f32(k), _f32(v)
     B, H, T, d = qf.shape
     r0, rad = _radius(r, H)
+    rb, nr = _rand_blocks(random_blocks, H, T)
     dil = _i32(dilation)
     g = _i32(global_idx if global_idx is not None else [])
     pad = _u8(key_padding_mask)
     rr = np.ascontiguousarray(np.asarray(rows_flat, dtype=np.int64))
     out = np.zeros((rr.size, d), dtype=np.float64)
     nt = lib.lf_oracle_rows2(_ptr(qf), _ptr(kf), _ptr(vf), B, H, T, d, r0, _ptr(rad), int(bool(one_sided)),
-                             _ptr(dil), _ptr(g), int(g.size), _ptr(pad), _ptr(rr), int(rr.size), _ptr(out),
-                             int(n_threads))
+                             _ptr(rb), nr, _ptr(dil), _ptr(g), int(g.size), _ptr(pad), _ptr(rr), int(rr.size),
+                             _ptr(out), int(n_threads))
     if nt < 0:
         raise ValueError("oracle rejected its arguments")
     return (out, nt) if return_threads else out
 
 
-def neighbours(T, r, delta, i, global_idx=None, pad_row=None, lib=None, one_sided=False):
-    """Sorted list N(i) of one query (empty for a padded query)."""
+def neighbours(T, r, delta, i, global_idx=None, pad_row=None, lib=None, one_sided=False,
+               random_blocks=None):
+    """Sorted list N(i) of one query (empty for a padded query).
+    ``random_blocks``: this head's [ceil(T/64)][n] key blocks, or None."""
     lib = lib or _load()
+    rb, nr = (None, 0) if random_blocks is None else _rand_blocks(np.asarray(random_blocks)[None], 1, T)
     g = _i32(global_idx if global_idx is not None else [])
     pad = _u8(pad_row)
     buf = np.zeros(T, dtype=np.int32)
-    n = lib.lf_oracle_neighbours2(int(T), int(r), int(delta), int(bool(one_sided)), _ptr(g), int(g.size),
-                                  _ptr(pad), int(i), _ptr(buf))
+    n = lib.lf_oracle_neighbours2(int(T), int(r), int(delta), int(bool(one_sided)), _ptr(rb), nr, _ptr(g),
+                                  int(g.size), _ptr(pad), int(i), _ptr(buf))
     if n < 0:
         raise ValueError("oracle rejected its arguments")
     return [int(x) for x in buf[:n]]
 
 
 def count_pairs(B, H, T, r, dilation=None, global_idx=None, key_padding_mask=None, lib=None,
-                one_sided=False):
+                one_sided=False, random_blocks=None):
     """Sum of |N(i)| over all rows (padded rows count 0)."""
     lib = lib or _load()
     r0, rad = _radius(r, H)
+    rb, nr = _rand_blocks(random_blocks, H, T)
     dil = _i32(dilation)
     g = _i32(global_idx if global_idx is not None else [])
     pad = _u8(key_padding_mask)
-    n = lib.lf_oracle_count_pairs2(int(B), int(H), int(T), r0, _ptr(rad), int(bool(one_sided)), _ptr(dil),
-                                   _ptr(g), int(g.size), _ptr(pad))
+    n = lib.lf_oracle_count_pairs2(int(B), int(H), int(T), r0, _ptr(rad), int(bool(one_sided)), _ptr(rb), nr,
+                                   _ptr(dil), _ptr(g), int(g.size), _ptr(pad))
     if n < 0:
         raise ValueError("oracle rejected its arguments")
     return int(n)

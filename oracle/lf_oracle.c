@@ -31,6 +31,16 @@
  *       key j is in N_local(i) iff 0 <= i - j <= r*delta and
  *       (i - j) mod delta == 0 (the query and the keys before it); global
  *       rows and global keys are as in the two-sided case.
+ *   BigBird, as the pages describe it beside Longformer (the mhpn.cn guide
+ *       to long-text models, BERT to Longformer, BigBird and RoPE, §2.2.1
+ *       and §2.2.2; Longformer (ciallo.wiki) on BigBird): each token also
+ *       attends to a few randomly chosen other tokens; the sparse pattern
+ *       works in blocks of block_size, usually 64.  Reading used here: the caller draws, for every head
+ *       and every query block of 64 positions, n_rand key blocks of 64
+ *       positions; a non-global query i also attends to every valid key of
+ *       the blocks drawn for its block i / 64 (a set union with the window
+ *       and G: each key counts once).  Heads with random blocks have
+ *       delta = 1, as in BigBird.
  *   same page, "Implementation Reading" asks that padding be masked:
  *       a padded key leaves every query's set (global rows included);
  *       a padded query row is defined as all zeros.
@@ -100,8 +110,12 @@ static int gset_has(const gset_t *g, int i) {
 /* N(i) for one query, written out as a sorted list of key positions.
  * Returns |N(i)|; a padded query gets the empty set (its row is zero). */
 
+#define RAND_BLOCK 64
+
 static int neighbours(int T, int r, int delta, int one_sided, const gset_t *G,
-                      const unsigned char *pad /* [T] or NULL */, int i, int *out) {
+                      const unsigned char *pad /* [T] or NULL */, int i, int *out,
+                      const int *rblk /* this head's [ceil(T/64)][n_rand] or NULL */, int n_rand,
+                      unsigned char *mark /* [T] scratch when rblk is given */) {
     if (pad && pad[i]) return 0;
     int n = 0;
     if (gset_has(G, i)) {
@@ -131,6 +145,22 @@ static int neighbours(int T, int r, int delta, int one_sided, const gset_t *G,
     while (gi < G->n) {
         int g = G->pos[gi++];
         if (!(pad && pad[g])) out[n++] = g;
+    }
+    if (rblk && n_rand > 0) {
+        /* add the valid keys of the random blocks of i's query block: mark
+         * every key of the set so far and of the blocks, then list them in
+         * ascending order (a key in both counts once) */
+        memset(mark, 0, (size_t)T);
+        for (int t = 0; t < n; t++) mark[out[t]] = 1;
+        const int *rb = rblk + (size_t)(i / RAND_BLOCK) * n_rand;
+        for (int e = 0; e < n_rand; e++) {
+            const int j0 = rb[e] * RAND_BLOCK;
+            for (int j = j0; j < j0 + RAND_BLOCK && j < T; j++)
+                if (!(pad && pad[j])) mark[j] = 1;
+        }
+        n = 0;
+        for (int j = 0; j < T; j++)
+            if (mark[j]) out[n++] = j;
     }
     return n;
 }
@@ -172,6 +202,8 @@ typedef struct {
     int B, H, T, d, r;
     const int *rad;         /* [H] radius per head, or NULL: r for every head */
     int one_sided;
+    const int *rblk;        /* [H][ceil(T/64)][n_rand] random key blocks, or NULL */
+    int n_rand;
     const int *dil;
     const gset_t *G;
     const unsigned char *pad;
@@ -186,7 +218,9 @@ static void *worker(void *arg) {
     job_t *jb = (job_t *)arg;
     int *nb = (int *)malloc(sizeof(int) * (size_t)jb->T);
     double *s = (double *)malloc(sizeof(double) * (size_t)jb->T);
-    if (!nb || !s) { jb->err = 1; free(nb); free(s); return NULL; }
+    unsigned char *mark = (unsigned char *)malloc((size_t)jb->T);
+    if (!nb || !s || !mark) { jb->err = 1; free(nb); free(s); free(mark); return NULL; }
+    const size_t nqb = ((size_t)jb->T + RAND_BLOCK - 1) / RAND_BLOCK;
     const long long chunk = 16;
     for (long long c0 = (long long)jb->tid * chunk; c0 < jb->n_rows;
          c0 += (long long)jb->n_threads * chunk) {
@@ -199,7 +233,8 @@ static void *worker(void *arg) {
             int delta = jb->dil ? jb->dil[h] : 1;
             int rh = jb->rad ? jb->rad[h] : jb->r;
             const unsigned char *padrow = jb->pad ? jb->pad + (size_t)b * jb->T : NULL;
-            int n = neighbours(jb->T, rh, delta, jb->one_sided, jb->G, padrow, i, nb);
+            const int *rb = jb->rblk ? jb->rblk + (size_t)h * nqb * jb->n_rand : NULL;
+            int n = neighbours(jb->T, rh, delta, jb->one_sided, jb->G, padrow, i, nb, rb, jb->n_rand, mark);
             const size_t base = (size_t)bh * jb->T * jb->d;
             attend_row(jb->q + base + (size_t)i * jb->d, jb->k + base, jb->v + base,
                        jb->d, nb, n, s, jb->out + (size_t)e * jb->d);
@@ -207,6 +242,7 @@ static void *worker(void *arg) {
     }
     free(nb);
     free(s);
+    free(mark);
     return NULL;
 }
 
@@ -217,6 +253,20 @@ static int host_threads(void) {
         if (c > 0) return c;
     }
     return 1;
+}
+
+static int check_rand(int H, int T, const int *dil, const int *rblk, int n_rand) {
+    if (n_rand < 0 || (n_rand > 0 && !rblk)) return -1;
+    if (!rblk || n_rand == 0) return 0;
+    const long long nqb = ((long long)T + RAND_BLOCK - 1) / RAND_BLOCK;
+    for (int h = 0; h < H; h++) {
+        if (dil && dil[h] != 1) return -1;
+        for (long long e = 0; e < nqb * n_rand; e++) {
+            const int x = rblk[(size_t)h * nqb * n_rand + e];
+            if (x < 0 || x >= nqb) return -1;
+        }
+    }
+    return 0;
 }
 
 static int check_args(int B, int H, int T, int d, int r, const int *rad, int one_sided, const int *dil) {
@@ -232,10 +282,11 @@ static int check_args(int B, int H, int T, int d, int r, const int *rad, int one
 }
 
 static int run(const float *q, const float *k, const float *v, int B, int H, int T, int d, int r,
-               const int *rad, int one_sided, const int *dil, const int *gidx, int ng,
-               const unsigned char *pad, const long long *rows, long long n_rows, double *out,
-               int n_threads) {
+               const int *rad, int one_sided, const int *rblk, int n_rand, const int *dil,
+               const int *gidx, int ng, const unsigned char *pad, const long long *rows,
+               long long n_rows, double *out, int n_threads) {
     if (check_args(B, H, T, d, r, rad, one_sided, dil)) return -1;
+    if (check_rand(H, T, dil, rblk, n_rand)) return -1;
     if (ng < 0 || (ng > 0 && !gidx)) return -1;
     gset_t G;
     if (gset_make(&G, gidx, ng, T)) return -1;
@@ -246,7 +297,8 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     if (!jobs || !th) { free(jobs); free(th); free(G.pos); return -1; }
     int err = 0;
     for (int t = 0; t < n_threads; t++) {
-        job_t j = {q, k, v, B, H, T, d, r, rad, one_sided, dil, &G, pad, rows, n_rows, out, n_threads, t, 0};
+        job_t j = {q, k, v, B, H, T, d, r, rad, one_sided, rblk, n_rand, dil, &G, pad, rows, n_rows, out,
+                   n_threads, t, 0};
         jobs[t] = j;
     }
     for (int t = 1; t < n_threads; t++)
@@ -267,77 +319,91 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
  * NULL (then r for every head); one_sided: 0 two-sided, 1 one-sided.
  * Returns the thread count used, or -1 on invalid arguments. */
 int lf_oracle_fwd2(const float *q, const float *k, const float *v, int B, int H, int T, int d,
-                   int r, const int *radius, int one_sided, const int *dilation,
-                   const int *global_idx, int n_global, const unsigned char *key_padding_mask,
-                   double *out, int n_threads) {
+                   int r, const int *radius, int one_sided, const int *rand_blocks, int n_rand,
+                   const int *dilation, const int *global_idx, int n_global,
+                   const unsigned char *key_padding_mask, double *out, int n_threads) {
     long long n = (long long)B * H * T;
-    return run(q, k, v, B, H, T, d, r, radius, one_sided, dilation, global_idx, n_global,
-               key_padding_mask, NULL, n, out, n_threads);
+    return run(q, k, v, B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
+               n_global, key_padding_mask, NULL, n, out, n_threads);
 }
 
 int lf_oracle_fwd(const float *q, const float *k, const float *v, int B, int H, int T, int d,
                   int r, const int *dilation, const int *global_idx, int n_global,
                   const unsigned char *key_padding_mask, double *out, int n_threads) {
-    return lf_oracle_fwd2(q, k, v, B, H, T, d, r, NULL, 0, dilation, global_idx, n_global,
+    return lf_oracle_fwd2(q, k, v, B, H, T, d, r, NULL, 0, NULL, 0, dilation, global_idx, n_global,
                           key_padding_mask, out, n_threads);
 }
 
 /* Selected rows only: rows[e] = (b*H + h)*T + i; out_rows[e][d]. */
 int lf_oracle_rows2(const float *q, const float *k, const float *v, int B, int H, int T, int d,
-                    int r, const int *radius, int one_sided, const int *dilation,
-                    const int *global_idx, int n_global, const unsigned char *key_padding_mask,
-                    const long long *rows, long long n_rows, double *out_rows, int n_threads) {
+                    int r, const int *radius, int one_sided, const int *rand_blocks, int n_rand,
+                    const int *dilation, const int *global_idx, int n_global,
+                    const unsigned char *key_padding_mask, const long long *rows, long long n_rows,
+                    double *out_rows, int n_threads) {
     for (long long e = 0; e < n_rows; e++)
         if (rows[e] < 0 || rows[e] >= (long long)B * H * T) return -1;
-    return run(q, k, v, B, H, T, d, r, radius, one_sided, dilation, global_idx, n_global,
-               key_padding_mask, rows, n_rows, out_rows, n_threads);
+    return run(q, k, v, B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
+               n_global, key_padding_mask, rows, n_rows, out_rows, n_threads);
 }
 
 int lf_oracle_rows(const float *q, const float *k, const float *v, int B, int H, int T, int d,
                    int r, const int *dilation, const int *global_idx, int n_global,
                    const unsigned char *key_padding_mask, const long long *rows, long long n_rows,
                    double *out_rows, int n_threads) {
-    return lf_oracle_rows2(q, k, v, B, H, T, d, r, NULL, 0, dilation, global_idx, n_global,
+    return lf_oracle_rows2(q, k, v, B, H, T, d, r, NULL, 0, NULL, 0, dilation, global_idx, n_global,
                            key_padding_mask, rows, n_rows, out_rows, n_threads);
 }
 
 /* N(i) of one query of sequence b, head radius r and stride delta: sorted
  * positions into idx (capacity T).  Returns |N(i)|, or -1 on invalid
  * arguments. */
-int lf_oracle_neighbours2(int T, int r, int delta, int one_sided, const int *global_idx, int n_global,
-                          const unsigned char *pad_row, int i, int *idx) {
+int lf_oracle_neighbours2(int T, int r, int delta, int one_sided, const int *rand_blocks, int n_rand,
+                          const int *global_idx, int n_global, const unsigned char *pad_row, int i,
+                          int *idx) {
     if (T < 1 || r < 0 || delta < 1 || i < 0 || i >= T || (one_sided != 0 && one_sided != 1)) return -1;
+    const int one_delta = delta;
+    if (check_rand(1, T, &one_delta, rand_blocks, n_rand)) return -1;
     gset_t G;
     if (gset_make(&G, global_idx, n_global, T)) return -1;
-    int n = neighbours(T, r, delta, one_sided, &G, pad_row, i, idx);
+    unsigned char *mark = (unsigned char *)malloc((size_t)T);
+    if (!mark) { free(G.pos); return -1; }
+    int n = neighbours(T, r, delta, one_sided, &G, pad_row, i, idx, rand_blocks, n_rand, mark);
+    free(mark);
     free(G.pos);
     return n;
 }
 
 int lf_oracle_neighbours(int T, int r, int delta, const int *global_idx, int n_global,
                          const unsigned char *pad_row, int i, int *idx) {
-    return lf_oracle_neighbours2(T, r, delta, 0, global_idx, n_global, pad_row, i, idx);
+    return lf_oracle_neighbours2(T, r, delta, 0, NULL, 0, global_idx, n_global, pad_row, i, idx);
 }
 
 /* Sum over all (b, h, i) of |N(i)|: the number of (query, key) pairs the
  * softmax runs over.  Returns -1 on invalid arguments. */
 long long lf_oracle_count_pairs2(int B, int H, int T, int r, const int *radius, int one_sided,
-                                 const int *dilation, const int *global_idx, int n_global,
+                                 const int *rand_blocks, int n_rand, const int *dilation,
+                                 const int *global_idx, int n_global,
                                  const unsigned char *key_padding_mask) {
     if (check_args(B, H, T, 1, r, radius, one_sided, dilation)) return -1;
+    if (check_rand(H, T, dilation, rand_blocks, n_rand)) return -1;
     gset_t G;
     if (gset_make(&G, global_idx, n_global, T)) return -1;
     int *nb = (int *)malloc(sizeof(int) * (size_t)T);
-    if (!nb) { free(G.pos); return -1; }
+    unsigned char *mark = (unsigned char *)malloc((size_t)T);
+    if (!nb || !mark) { free(nb); free(mark); free(G.pos); return -1; }
+    const size_t nqb = ((size_t)T + RAND_BLOCK - 1) / RAND_BLOCK;
     long long total = 0;
     for (int b = 0; b < B; b++)
         for (int h = 0; h < H; h++) {
             int delta = dilation ? dilation[h] : 1;
             int rh = radius ? radius[h] : r;
             const unsigned char *padrow = key_padding_mask ? key_padding_mask + (size_t)b * T : NULL;
-            for (int i = 0; i < T; i++) total += neighbours(T, rh, delta, one_sided, &G, padrow, i, nb);
+            const int *rb = rand_blocks ? rand_blocks + (size_t)h * nqb * n_rand : NULL;
+            for (int i = 0; i < T; i++)
+                total += neighbours(T, rh, delta, one_sided, &G, padrow, i, nb, rb, n_rand, mark);
         }
     free(nb);
+    free(mark);
     free(G.pos);
     return total;
 }
@@ -345,5 +411,6 @@ long long lf_oracle_count_pairs2(int B, int H, int T, int r, const int *radius, 
 long long lf_oracle_count_pairs(int B, int H, int T, int r, const int *dilation,
                                 const int *global_idx, int n_global,
                                 const unsigned char *key_padding_mask) {
-    return lf_oracle_count_pairs2(B, H, T, r, NULL, 0, dilation, global_idx, n_global, key_padding_mask);
+    return lf_oracle_count_pairs2(B, H, T, r, NULL, 0, NULL, 0, dilation, global_idx, n_global,
+                                  key_padding_mask);
 }

@@ -19,10 +19,12 @@ import numpy as np
 
 def pair_counts(B: int, H: int, T: int, r, dilation: Optional[Sequence[int]] = None,
                 global_idx: Optional[Sequence[int]] = None, key_padding_mask=None,
-                one_sided: bool = False) -> np.ndarray:
+                one_sided: bool = False, random_blocks=None) -> np.ndarray:
     """|N(i)| for every row, as an int64 array [B, H, T] (padded rows give 0).
     ``r`` is one radius or one per head; ``one_sided`` windows keep only the
-    keys at or before the query."""
+    keys at or before the query; ``random_blocks`` [H][ceil(T/64)][n] adds
+    to each query of block i // 64 the valid keys of those key blocks of 64
+    (heads with random blocks are undilated)."""
     G = np.unique(np.asarray(list(global_idx) if global_idx is not None else [], dtype=np.int64))
     if key_padding_mask is None:
         valid = np.ones((B, T), dtype=bool)
@@ -63,10 +65,37 @@ def pair_counts(B: int, H: int, T: int, r, dilation: Optional[Sequence[int]] = N
                     np.add.at(diff, np.minimum(n, mg + rb + 1), 1)
                     extra += np.cumsum(diff[:-1])
                 cnt[pos] = win + extra
+            if random_blocks is not None and np.asarray(random_blocks).shape[2] > 0:
+                cnt += _random_extra(T, rb, ra, vb, is_g, np.asarray(random_blocks)[h])
             cnt[is_g] = n_valid                          # global rows read every valid key
             cnt[~vb] = 0                                 # padded rows are zero rows
             out[b, h] = cnt
     return out
+
+
+def _random_extra(T, rb, ra, vb, is_g, blocks):
+    """Per row: the valid keys of the row's random blocks that are neither in
+    its window [i - rb, i + ra] nor global (those are counted already)."""
+    pv = np.concatenate([[0], np.cumsum(vb.astype(np.int64))])            # valid keys
+    pg = np.concatenate([[0], np.cumsum((vb & is_g).astype(np.int64))])   # valid globals
+    i = np.arange(T)
+    w_lo = np.maximum(0, i - rb)
+    w_hi = np.minimum(T, i + ra + 1)
+    extra = np.zeros(T, dtype=np.int64)
+    qb = i // 64
+    for e in range(blocks.shape[1]):
+        blk = blocks[qb, e].astype(np.int64)
+        # a block drawn twice for one query block counts once
+        dup = np.zeros(T, dtype=bool)
+        for e2 in range(e):
+            dup |= blocks[qb, e2] == blocks[qb, e]
+        lo = np.minimum(T, 64 * blk)
+        hi = np.minimum(T, 64 * blk + 64)
+        ilo = np.maximum(lo, w_lo)
+        ihi = np.maximum(ilo, np.minimum(hi, w_hi))                       # block cut by the window
+        add = (pv[hi] - pv[lo]) - (pv[ihi] - pv[ilo]) - ((pg[hi] - pg[lo]) - (pg[ihi] - pg[ilo]))
+        extra += np.where(dup, 0, add)
+    return extra
 
 
 def useful_pairs(*args, **kw) -> int:

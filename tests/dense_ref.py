@@ -9,9 +9,11 @@ code with the oracle (which walks each query's neighbour list instead).
 import numpy as np
 
 
-def allowed_matrix(T, r, delta, globals_, pad_row, one_sided=False):
+def allowed_matrix(T, r, delta, globals_, pad_row, one_sided=False, rand_blocks=None):
     """A[i, j] = True iff key j is in N(i) (no padding applied to rows here).
-    One-sided: the window keeps only keys at or before the query."""
+    One-sided: the window keeps only keys at or before the query.
+    rand_blocks: [ceil(T/64)][n] key blocks of 64 that every query of block
+    i // 64 also sees (global rows see everything anyway)."""
     i = np.arange(T)[:, None]
     j = np.arange(T)[None, :]
     dist = i - j
@@ -21,14 +23,22 @@ def allowed_matrix(T, r, delta, globals_, pad_row, one_sided=False):
     g = np.zeros(T, dtype=bool)
     for x in globals_:
         g[x] = True
+    if rand_blocks is not None:
+        rb = np.zeros((T, T), dtype=bool)
+        for i_ in range(T):
+            for blk in np.asarray(rand_blocks)[i_ // 64]:
+                rb[i_, 64 * int(blk):64 * int(blk) + 64] = True
+        local = local | rb
     A = local | g[None, :] | g[:, None]   # every row sees G; global rows see all
     if pad_row is not None:
         A &= ~pad_row.astype(bool)[None, :]
     return A
 
 
-def dense_masked_attention(q, k, v, r, dilation=None, globals_=(), pad=None, one_sided=False):
-    """r: one radius, or a list with one radius per head."""
+def dense_masked_attention(q, k, v, r, dilation=None, globals_=(), pad=None, one_sided=False,
+                           rand_blocks=None):
+    """r: one radius, or a list with one radius per head; rand_blocks:
+    [H][ceil(T/64)][n] or None."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -39,7 +49,8 @@ def dense_masked_attention(q, k, v, r, dilation=None, globals_=(), pad=None, one
         for h in range(H):
             delta = 1 if dilation is None else int(dilation[h])
             rh = int(r) if np.isscalar(r) else int(r[h])
-            A = allowed_matrix(T, rh, delta, globals_, pad_row, one_sided)
+            A = allowed_matrix(T, rh, delta, globals_, pad_row, one_sided,
+                               None if rand_blocks is None else rand_blocks[h])
             S = q[b, h] @ k[b, h].T / np.sqrt(d)
             S = np.where(A, S, -np.inf)
             rows_ok = A.any(axis=1)

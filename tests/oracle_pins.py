@@ -24,7 +24,11 @@ one of them.  The pins:
   window taken per head and cut to keys at or before the query, the
   one-sided closed form sum_i (min(i, r) + 1) = T(r+1) - r(r+1)/2, and the
   one-sided dense limit equal to causal attention (torch's
-  scaled_dot_product_attention with is_causal, float64).
+  scaled_dot_product_attention with is_causal, float64);
+* random key blocks (BigBird as the pages describe it: random attention in
+  blocks of 64): the brute force with the blocks added to each row's mask,
+  an exact count for r = 0, and every block drawn for every query block
+  giving dense attention.
 """
 import numpy as np
 import torch
@@ -69,7 +73,13 @@ def random_cases(n, seed0=0, Ts=(1, 2, 7, 33, 64, 130, 257)):
         # every third case one-sided, every other case one radius per head
         one = c % 3 == 2
         rr = [int(x) for x in rng.integers(0, T + 3, size=H)] if c % 2 else r
-        cases.append(dict(q=q, k=k, v=v, r=rr, dil=dil, G=G, pad=pad, one=one))
+        # every fourth case (from the second on) with random key blocks, on undilated heads
+        rb = None
+        if c % 4 == 1:
+            dil = [1] * H
+            nqb = (T + 63) // 64
+            rb = rng.integers(0, nqb, size=(H, nqb, int(rng.integers(1, 4)))).astype(np.int32)
+        cases.append(dict(q=q, k=k, v=v, r=rr, dil=dil, G=G, pad=pad, one=one, rb=rb))
     return cases
 
 
@@ -78,9 +88,10 @@ def random_cases(n, seed0=0, Ts=(1, 2, 7, 33, 64, 130, 257)):
 
 def check_dense_bruteforce(lib=None, n=28, tol=1e-12):
     for c in random_cases(n):
-        y = oracle.fwd(c["q"], c["k"], c["v"], c["r"], c["dil"], c["G"], c["pad"], lib=lib, one_sided=c["one"])
+        y = oracle.fwd(c["q"], c["k"], c["v"], c["r"], c["dil"], c["G"], c["pad"], lib=lib, one_sided=c["one"],
+                       random_blocks=c["rb"])
         ref = dense_masked_attention(c["q"].numpy(), c["k"].numpy(), c["v"].numpy(), c["r"],
-                                     c["dil"], c["G"], c["pad"], c["one"])
+                                     c["dil"], c["G"], c["pad"], c["one"], c["rb"])
         err = np.max(np.abs(y - ref)) if y.size else 0.0
         assert err <= tol, f"oracle vs dense brute force: {err} (T={c['q'].shape[2]}, r={c['r']}, one={c['one']})"
 
@@ -128,6 +139,19 @@ def check_closed_form_counts(lib=None):
     assert oracle.count_pairs(2, 4, 1000, rads, lib=lib) == 2 * sum(local_count(1000, x) for x in rads)
     assert oracle.count_pairs(1, 4, 1000, rads, lib=lib, one_sided=True) == sum(
         1000 * (x + 1) - x * (x + 1) // 2 for x in rads)
+    # random key blocks with r = 0 and no globals: row i sees itself and the
+    # keys of its block's random blocks (its own block counts once)
+    rng = np.random.default_rng(17)
+    for T in (64, 200, 1000):
+        nqb = (T + 63) // 64
+        rb = rng.integers(0, nqb, size=(1, nqb, 2)).astype(np.int32)
+        want = 0
+        for i in range(T):
+            keys = {i}
+            for blk in set(int(x) for x in rb[0, i // 64]):
+                keys |= set(range(64 * blk, min(64 * blk + 64, T)))
+            want += len(keys)
+        assert oracle.count_pairs(1, 1, T, 0, lib=lib, random_blocks=rb) == want
     # 512 -> 8192 tokens: dense x256 exactly, fixed small window ~x16
     assert oracle.count_pairs(1, 1, 8192, 9000, lib=lib) == 256 * oracle.count_pairs(1, 1, 512, 9000, lib=lib)
     ratio = oracle.count_pairs(1, 1, 8192, 4, lib=lib) / oracle.count_pairs(1, 1, 512, 4, lib=lib)
@@ -232,6 +256,11 @@ def check_identity_and_dense_limits(lib=None):
         refc = torch.nn.functional.scaled_dot_product_attention(q.double(), k.double(), v.double(),
                                                                  is_causal=True).numpy()
         assert np.max(np.abs(yc - refc)) <= 1e-12
+        # every key block drawn for every query block: dense attention
+        nqb = (T + 63) // 64
+        allb = np.tile(np.arange(nqb, dtype=np.int32), (3, nqb, 1))
+        yr = oracle.fwd(q, k, v, 0, [1, 1, 1], [], None, lib=lib, random_blocks=allb)
+        assert np.max(np.abs(yr - ref)) <= 1e-12
         # one-sided, r = 0: each row attends to itself only
         y1 = oracle.fwd(q, k, v, 0, [2, 1, 3], [], None, lib=lib, one_sided=True)
         assert np.array_equal(y1, v.numpy().astype(np.float64))

@@ -35,6 +35,21 @@ def test_counter_matches_enumeration_per_head_one_sided(seed):
     assert metrics.useful_pairs(B, H, T, rads, dil, G, pad, one_sided=one) == want
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_counter_matches_enumeration_random_blocks(seed):
+    rng = np.random.default_rng(200 + seed)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    T = int(rng.integers(1, 400))
+    rads = [int(x) for x in rng.integers(0, 100, size=H)]
+    G = [int(x) for x in rng.integers(0, T, size=int(rng.integers(0, 7)))]
+    pad = (rng.random((B, T)) < 0.2).astype(np.uint8) if seed % 2 else None
+    one = seed % 3 == 0
+    nqb = (T + 63) // 64
+    rb = rng.integers(0, nqb, size=(H, nqb, int(rng.integers(1, 4)))).astype(np.int32)
+    want = oracle.count_pairs(B, H, T, rads, None, G, pad, one_sided=one, random_blocks=rb)
+    assert metrics.useful_pairs(B, H, T, rads, None, G, pad, one_sided=one, random_blocks=rb) == want
+
+
 @pytest.mark.parametrize("name", [w.name for w in W.WORKLOADS])
 def test_counter_matches_enumeration_workloads(name):
     w = W.workload(name)

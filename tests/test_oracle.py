@@ -39,6 +39,10 @@ MUTANTS = [
     ("one_sided_ignored", "if (one_sided) thi = 0;", ""),
     ("one_sided_wrong_side", "if (one_sided) thi = 0;", "if (one_sided) tlo = 0;"),
     ("head_radius_ignored", "int rh = jb->rad ? jb->rad[h] : jb->r;", "int rh = jb->r;"),
+    ("random_blocks_ignored", "if (rblk && n_rand > 0) {", "if (0) {"),
+    ("random_block_shifted", "const int j0 = rb[e] * RAND_BLOCK;", "const int j0 = rb[e] * RAND_BLOCK + 1;"),
+    ("random_padded_kept", "if (!(pad && pad[j])) mark[j] = 1;", "mark[j] = 1;"),
+    ("random_block_of_wrong_query", "rblk + (size_t)(i / RAND_BLOCK) * n_rand", "rblk + (size_t)(i / RAND_BLOCK / 2) * n_rand"),
 ]
 
 
