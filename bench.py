@@ -85,7 +85,8 @@ def cpu_baseline(inp, flops, seconds):
     threads = 0
     while True:
         _, threads = oracle.fwd(inp.q, inp.k, inp.v, inp.r, inp.dilation, inp.global_idx,
-                                inp.key_padding_mask, return_threads=True, one_sided=inp.one_sided)
+                                inp.key_padding_mask, return_threads=True, one_sided=inp.one_sided,
+                                random_blocks=inp.random_blocks)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1024:
@@ -180,7 +181,7 @@ def main():
     B, H, T, d = q.shape
     stream = torch.cuda.current_stream(dev)
     call = lf.Prepared(q, k, v, inp.r, inp.dilation, inp.global_idx, kpm, stream=stream,
-                       one_sided=inp.one_sided)
+                       one_sided=inp.one_sided, random_blocks=inp.random_blocks)
 
     if args.profile_mode:
         # warmup calls, then more untimed calls for at least SETTLE_MS (the
@@ -209,7 +210,7 @@ def main():
         return
 
     pairs = metrics.useful_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
-                                 one_sided=inp.one_sided)
+                                 one_sided=inp.one_sided, random_blocks=inp.random_blocks)
     flops = 4 * d * pairs
 
     # eager: back-to-back calls, events on the call stream (after the warmup
@@ -244,7 +245,7 @@ def main():
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             gcall = lf.Prepared(q, k, v, inp.r, inp.dilation, inp.global_idx, kpm, out=call.out, stream=side,
-                                one_sided=inp.one_sided)
+                                one_sided=inp.one_sided, random_blocks=inp.random_blocks)
             gcall()   # the workspace for this stream is allocated outside capture
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=side):
@@ -328,6 +329,7 @@ def main():
         "data": "synthetic (seeded N(0,1) q/k/v; no dataset, no weights)",
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "d": d, "r": inp.r,
                    "one_sided": inp.one_sided,
+                   "n_rand": 0 if inp.random_blocks is None else int(inp.random_blocks.shape[2]),
                    "dilation": inp.dilation, "n_global": len(set(inp.global_idx)),
                    "padded": inp.key_padding_mask is not None, "useful_pairs": pairs,
                    "useful_gflop": round(flops / 1e9, 4), "parallelism": "single GPU",

@@ -54,6 +54,7 @@ typedef enum {
 #define LF_MAX_GLOBALS 512    /* distinct global positions */
 #define LF_MAX_SEQ ((1 << 24) - 1)  /* T: one head of fp32 K or V stays below 4 GiB */
 #define LF_MAX_DILATION 65535 /* delta */
+#define LF_MAX_RAND_BLOCKS 8  /* random key blocks per query block (lf_attn_fwd_ex) */
 
 /*
  * lf_attn_fwd -- enqueue the forward pass on `stream`.
@@ -98,13 +99,16 @@ lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v,
                         void *out, lf_dtype_t dtype, void *stream);
 
 /*
- * lf_attn_fwd_ex -- lf_attn_fwd with one window radius per head and a
- * choice of two-sided or one-sided windows.
+ * lf_attn_fwd_ex -- lf_attn_fwd with one window radius per head, a choice
+ * of two-sided or one-sided windows, and random key blocks.
  *
  * The window list of "Longformer长序列处理" (section HF实践: one window per
- * layer, given as an int or a list) applied per head of one call, and the
- * one- or two-sided question of Longformer (eightmm.github.io), section
- * "Implementation Reading".
+ * layer, given as an int or a list) applied per head of one call; the one-
+ * or two-sided question of Longformer (eightmm.github.io), section
+ * "Implementation Reading"; and BigBird's random attention as the pages set
+ * it beside Longformer (the mhpn.cn guide to long-text models, §2.2.1 and
+ * §2.2.2: each token also attends to randomly chosen tokens, in blocks of
+ * block_size, usually 64).
  *
  *   radius    HOST array [H] of radii r_h >= 0 (must not be NULL); head h
  *             uses r_h where lf_attn_fwd uses r.  Read during the call only.
@@ -113,13 +117,24 @@ lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v,
  *             0 <= i - j <= r_h delta_h, the query and the keys before it.
  *             Global rows and global keys are the same in both cases (a
  *             global row sees every valid key; every row sees the globals).
+ *   rand_blocks HOST array [H][ceil(T/64)][n_rand] of key-block indices in
+ *             [0, ceil(T/64)), or NULL when n_rand == 0: a non-global query
+ *             i of head h also attends to the valid keys of positions
+ *             [64 b, 64 b + 64) for every b in rand_blocks[h][i / 64]
+ *             (a set union with the window and the globals: each key counts
+ *             once; a block listed twice counts once).  The caller draws
+ *             them.  Read during the call only.
+ *   n_rand    random key blocks per query block, 0 .. LF_MAX_RAND_BLOCKS;
+ *             with n_rand > 0 every head must be undilated (delta = 1), else
+ *             LF_E_UNSUPPORTED.
  *   All other arguments, the ownership and the error behaviour are those
- *   of lf_attn_fwd; one_sided outside {0, 1} or a negative radius is
- *   LF_E_INVALID.
+ *   of lf_attn_fwd; one_sided outside {0, 1}, a negative radius or n_rand,
+ *   or a block index out of range is LF_E_INVALID.
  */
 lf_status_t lf_attn_fwd_ex(const void *q, const void *k, const void *v,
                            int B, int H, int T, int d,
                            const int32_t *radius, int one_sided,
+                           const int32_t *rand_blocks, int n_rand,
                            const int32_t *dilation,
                            const int32_t *global_idx, int n_global,
                            const uint8_t *key_padding_mask,

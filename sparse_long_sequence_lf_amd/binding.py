@@ -24,6 +24,7 @@ STATUS_NAMES = {0: "LF_OK", 1: "LF_E_INVALID", 2: "LF_E_UNSUPPORTED", 3: "LF_E_N
 HEAD_DIM = 64
 MAX_HEADS = 128
 MAX_GLOBALS = 512
+MAX_RAND_BLOCKS = 8
 
 _lib = None
 
@@ -47,7 +48,7 @@ def load():
     I = ctypes.c_int
     lib.lf_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I, P]
     lib.lf_attn_fwd.restype = I
-    lib.lf_attn_fwd_ex.argtypes = [P, P, P, I, I, I, I, P, I, P, P, I, P, P, I, P]
+    lib.lf_attn_fwd_ex.argtypes = [P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, I, P]
     lib.lf_attn_fwd_ex.restype = I
     lib.lf_last_error.argtypes = []
     lib.lf_last_error.restype = ctypes.c_char_p
@@ -64,11 +65,23 @@ def _per_head(r):
     return not isinstance(r, int) and hasattr(r, "__len__")
 
 
+def _rand_table(random_blocks):
+    """(ctypes int32 array, n_rand) of random key blocks [H][ceil(T/64)][n], or (None, 0)."""
+    if random_blocks is None:
+        return None, 0
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(random_blocks, dtype=np.int32))
+    if a.ndim != 3:
+        raise ValueError("random_blocks must be [H][ceil(T/64)][n_rand]")
+    flat = a.reshape(-1)
+    return (ctypes.c_int32 * max(1, flat.size))(*flat.tolist()), int(a.shape[2])
+
+
 def raw_fwd(q_ptr, k_ptr, v_ptr, B, H, T, d, r, dilation, global_idx, n_global, kpm_ptr, out_ptr,
-            dtype, stream_ptr, one_sided=False) -> int:
+            dtype, stream_ptr, one_sided=False, random_blocks=None) -> int:
     """Call the library with raw integer device pointers; returns the status.
-    ``r`` is one radius (lf_attn_fwd) or a list of H radii; a list or
-    ``one_sided`` goes to lf_attn_fwd_ex."""
+    ``r`` is one radius (lf_attn_fwd) or a list of H radii; a list,
+    ``one_sided`` or ``random_blocks`` goes to lf_attn_fwd_ex."""
     lib = load()
     dil = None
     if dilation is not None:
@@ -76,23 +89,26 @@ def raw_fwd(q_ptr, k_ptr, v_ptr, B, H, T, d, r, dilation, global_idx, n_global, 
     g = None
     if global_idx is not None:
         g = (ctypes.c_int32 * max(1, len(global_idx)))(*[int(x) for x in global_idx])
-    if _per_head(r) or one_sided:
+    if _per_head(r) or one_sided or random_blocks is not None:
         rl = [int(x) for x in r] if _per_head(r) else [int(r)] * int(H)
         rad = (ctypes.c_int32 * max(1, len(rl)))(*rl)
+        rt, nr = _rand_table(random_blocks)
         return lib.lf_attn_fwd_ex(q_ptr, k_ptr, v_ptr, int(B), int(H), int(T), int(d), rad,
-                                  int(bool(one_sided)), dil, g, int(n_global), kpm_ptr, out_ptr, int(dtype),
-                                  stream_ptr)
+                                  int(one_sided) if not isinstance(one_sided, bool) else int(one_sided),
+                                  rt, nr, dil, g, int(n_global), kpm_ptr, out_ptr, int(dtype), stream_ptr)
     return lib.lf_attn_fwd(q_ptr, k_ptr, v_ptr, int(B), int(H), int(T), int(d), int(r), dil, g,
                            int(n_global), kpm_ptr, out_ptr, int(dtype), stream_ptr)
 
 
 def attn_fwd(q, k, v, r, dilation: Optional[Sequence[int]] = None,
              global_idx: Optional[Sequence[int]] = None, global_attention_mask=None,
-             key_padding_mask=None, out=None, stream=None, one_sided: bool = False):
+             key_padding_mask=None, out=None, stream=None, one_sided: bool = False, random_blocks=None):
     """Longformer sparse attention forward on torch tensors [B, H, T, 64].
 
     ``r`` is the window radius, or a list with one radius per head;
-    ``one_sided`` keeps only the window keys at or before each query.
+    ``one_sided`` keeps only the window keys at or before each query;
+    ``random_blocks`` ([H][ceil(T/64)][n] key-block indices) adds BigBird-style
+    random key blocks of 64 to every query block of 64.
 
     ``global_attention_mask`` (a 0/1 tensor of shape [T] or [B, T], 1 =
     global, as in the Hugging Face convention) is turned into the index list
@@ -144,7 +160,7 @@ def attn_fwd(q, k, v, r, dilation: Optional[Sequence[int]] = None,
     if _per_head(r) and len(r) != H:
         raise ValueError(f"r has {len(r)} radii for {H} heads")
     st = raw_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, r, dilation,
-                 gl if gl else None, len(gl), kpm_ptr, out.data_ptr(), dt, sptr, one_sided)
+                 gl if gl else None, len(gl), kpm_ptr, out.data_ptr(), dt, sptr, one_sided, random_blocks)
     if st != LF_OK:
         raise LfError(st, last_error())
     return out
@@ -158,7 +174,7 @@ class Prepared:
     """
 
     def __init__(self, q, k, v, r, dilation=None, global_idx=None, key_padding_mask=None, out=None,
-                 stream=None, one_sided=False):
+                 stream=None, one_sided=False, random_blocks=None):
         import torch
 
         lib = load()
@@ -177,12 +193,13 @@ class Prepared:
             stream = torch.cuda.current_stream(q.device)
         sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
         kptr = None if kpm is None else kpm.data_ptr()
-        if _per_head(r) or one_sided:
+        if _per_head(r) or one_sided or random_blocks is not None:
             rl = [int(x) for x in r] if _per_head(r) else [int(r)] * H
             self._rad = (ctypes.c_int32 * H)(*rl)
+            self._rt, nr = _rand_table(random_blocks)
             self._fn = lib.lf_attn_fwd_ex
             self._args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, self._rad, int(bool(one_sided)),
-                          self._dil, self._g, len(gl), kptr, self.out.data_ptr(), dt, sptr)
+                          self._rt, nr, self._dil, self._g, len(gl), kptr, self.out.data_ptr(), dt, sptr)
         else:
             self._fn = lib.lf_attn_fwd
             self._args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, int(r), self._dil, self._g,

@@ -342,6 +342,16 @@ __device__ __forceinline__ void mask_window(f32x16& s, int lo, int width) {
     }
 }
 
+// random key block: drop the keys inside this query's window (the band
+// counts those): kc in [lo, lo + width] as in mask_window
+__device__ __forceinline__ void mask_window_out(f32x16& s, int lo, int width) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int kc = 8 * (i >> 2) + (i & 3);
+        s[i] = (uint32_t)(kc - lo) <= (uint32_t)width ? kNegInf : s[i];
+    }
+}
+
 // keep the elements whose bit is set in keep16
 __device__ __forceinline__ void mask_bits(f32x16& s, uint32_t keep16) {
 #pragma unroll
@@ -710,7 +720,19 @@ void tile_kernel(const Args A) {
     // follow the band blocks in the ring.
     const bool gvec = tk.kind == 0 && n_g > 0 && n_g <= kVecGlobals;
     const int ngb = (tk.kind == 0 && !gvec) ? cdiv(n_g, KBLK) : 0;
-    const int nblk = nb + ngb;
+    // random key blocks of this query block (undilated heads): each block of
+    // 64 keys is two 32-key blocks, after the band and the global-key blocks
+    const int nrb = tk.kind == 0 ? 2 * P.n_rand : 0;
+    const int32_t* rrow = nrb > 0 ? P.rtab + ((size_t)tk.h * ((T + 63) >> 6) + (tk.m0 >> 6)) * P.n_rand : nullptr;
+    // position of row 0 of random block position jr, or T for none (an empty
+    // entry, or a position past this tile's list: a phase's last step can
+    // fall past the end, and its entry must not be read)
+    auto rand_p0 = [&](int jr) -> int {
+        if (jr < 0 || jr >= nrb) return T;
+        const int rho = rrow[jr >> 1];
+        return rho >= 0 ? 64 * rho + 32 * (jr & 1) : T;
+    };
+    const int nblk = nb + nrb + ngb;
     // a global-row split whose keys are all padded contributes nothing: no
     // steps (its partial records get max -inf and sum 0)
     bool dead = false;
@@ -797,6 +819,10 @@ void tile_kernel(const Args A) {
         // two copies of the loads: band offsets stay in their registers
         if (jb < nb) {
             put(window(band_block(jb)), padA ? kPastEnd : voA0, padB ? kPastEnd : voB0);
+        } else if (jb >= nb + ngb) {
+            const int p0 = rand_p0(jb - nb - ngb);
+            put(buffer_rsrc(kvhead + (uint64_t)p0 * ROWB, p0 < T ? (uint32_t)(T - p0) * ROWB : 0u),
+                padA ? kPastEnd : voA0, padB ? kPastEnd : voB0);
         } else {
             const int sl0 = (jb - nb) * KBLK;
             put(buffer_rsrc(kvhead, head_bytes), global_pos(sl0 + rowA) * ROWB + colA,
@@ -812,7 +838,8 @@ void tile_kernel(const Args A) {
     const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, PAD ? (uint32_t)T : 0u);
     auto pad_at = [&](int s) -> uint32_t {
         const int q = 2 * s + ph;
-        const int pos = q < nb ? row0_of(band_block(q)) + tk.delta * lq : T;
+        const int pos = q < nb ? row0_of(band_block(q)) + tk.delta * lq
+                               : (q >= nb + ngb && q < nblk ? rand_p0(q - nb - ngb) + lq : T);
         return __builtin_amdgcn_raw_buffer_load_b8(rpad, (uint32_t)min(pos, T), 0, 0);
     };
     auto pad_word = [&](uint32_t byte) -> uint32_t { return (uint32_t)__ballot(lane < 32 && byte != 0u); };
@@ -943,10 +970,14 @@ void tile_kernel(const Args A) {
     // LDS are issued (the compiler makes any LDS read that follows such a load
     // wait for it); the score MFMAs wait for the K reads, the PV MFMAs for the
     // V reads, and the other waves of the SIMD run meanwhile.
+    // (MODE 0: a stage whose blocks are band blocks for both phases, with no
+    // global-key or random-block code at all; MODE 1: band or global-key
+    // blocks; MODE 2: also random key blocks.)
     // (ANY_GLOBAL false: a stage whose blocks are band blocks for both
     // phases; such steps have no global-key code at all)
     auto step = [&](auto any_global, int s, int oc, int on) {
-        constexpr bool ANY_GLOBAL = decltype(any_global)::value;
+        constexpr int MODE = decltype(any_global)::value;
+        constexpr bool ANY_GLOBAL = MODE > 0;
         barrier_lds_loads();           // stage s landed; stage s-1 no longer read
         const bool band = !ANY_GLOBAL || s < sb_end;
         const int jb = 2 * s + ph;     // sequence position
@@ -956,14 +987,24 @@ void tile_kernel(const Args A) {
         // scalar: a global-key block's comes from LDS (read ahead of the
         // fragments), a band block's from its range and the padding ballot.
         uint32_t gword = 0u;
-        if (ANY_GLOBAL && !band) gword = gbad[min(max(jb - nb, 0), LF_MAX_GLOBALS / KBLK - 1)];
+        const bool rnd = MODE == 2 && !band && jb >= nb + ngb;   // a random key block
+        if (ANY_GLOBAL && !band && !rnd) gword = gbad[min(max(jb - nb, 0), LF_MAX_GLOBALS / KBLK - 1)];
         const KFrag<NP> kf = load_k<NP>(W, smem + oc);
         const VFrag<NP> vf = load_v<NP>(W, smem + oc);
         uint32_t bad;
+        int p0r = T;
         if (band) {
             const int valid = tk.key_end - (tk.kb_lo + j) * KBLK;
             bad = valid <= 0 ? 0xffffffffu : (valid >= KBLK ? 0u : (0xffffffffu << valid));
             if constexpr (PAD) bad |= pm_cur;
+        } else if (MODE == 2 && rnd) {
+            // rows past the end, padded rows and global keys (the globals are
+            // counted by their own path) are not keys of a random block
+            p0r = rand_p0(jb - nb - ngb);
+            const int valid = T - p0r;
+            bad = valid <= 0 ? 0xffffffffu : (valid >= KBLK ? 0u : (0xffffffffu << valid));
+            if constexpr (PAD) bad |= pm_cur;
+            if (n_g > 0 && p0r < T) bad |= P.gmap[p0r >> 5];
         } else {
             bad = (uint32_t)uniform((int)gword);
         }
@@ -981,7 +1022,11 @@ void tile_kernel(const Args A) {
         // hold anything (zero weights times NaN would still be NaN).
         if (bad != 0xffffffffu) {
             auto mask = [&](f32x16& x) {
-                if (ANY_GLOBAL && !band) {
+                if (MODE == 2 && rnd) {
+                    if (p0r + 31 >= mq0 - r && p0r <= mq0 + 31 + ra)   // may meet this wave's windows
+                        mask_window_out(x, m_me - r - p0r - 4 * lg, r + ra);
+                    if (bad != 0u) mask_bits(x, ~lane_bits(bad, lg));
+                } else if (ANY_GLOBAL && !band) {
                     mask_global(x, bad, gcls + (jb - nb) * KBLK, m_me, r, r + ra, lg);
                 } else if (!(j >= ji_lo && j <= ji_hi && bad == 0u)) {
                     if (tk.kind == 0) {
@@ -1001,8 +1046,9 @@ void tile_kernel(const Args A) {
     // ---- main loop: one barrier per step; the two ring slots alternate.
     // Stages [0, nb/2) hold band blocks only; the rest (at most one mixed
     // stage, then global-key blocks) take the general step.
-    using BandOnly = std::integral_constant<bool, false>;
-    using General = std::integral_constant<bool, true>;
+    using BandOnly = std::integral_constant<int, 0>;
+    using General = std::integral_constant<int, 1>;
+    using WithRandom = std::integral_constant<int, 2>;
     const int s_band = dead ? 0 : nb >> 1;
     int s = 0;
     for (; s + 1 < s_band; s += 2) {
@@ -1013,7 +1059,10 @@ void tile_kernel(const Args A) {
         step(BandOnly{}, s, 0, RG::STAGE);
         s++;
     }
-    for (; s < NS; s++) step(General{}, s, (s & 1) * RG::STAGE, ((s + 1) & 1) * RG::STAGE);
+    // stages from the first random block on take the step with random blocks
+    const int s_rand = nrb > 0 ? (nb + ngb) >> 1 : NS;
+    for (; s < min(NS, s_rand); s++) step(General{}, s, (s & 1) * RG::STAGE, ((s + 1) & 1) * RG::STAGE);
+    for (; s < NS; s++) step(WithRandom{}, s, (s & 1) * RG::STAGE, ((s + 1) & 1) * RG::STAGE);
     __syncthreads();
 
     // ---- merge the KS phases of each query block (LDS); phase 0 keeps the result

@@ -60,9 +60,10 @@ struct Buffer {
     size_t bytes = 0;
 };
 struct Workspace {
-    Buffer counters, scratch, plan;
+    Buffer counters, scratch, plan, aux;
     lfk::Plan shadow;
     bool shadow_valid = false;
+    std::vector<uint32_t> aux_shadow;   // what aux holds: random-block table and global bitmap
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, void *>, Workspace> g_ws;
@@ -137,9 +138,9 @@ namespace {
 // The call behind both entry points: radius is NULL (r for every head) or
 // one radius per head.
 lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T, int d, int r,
-                     const int32_t *radius, int one_sided, const int32_t *dilation,
-                     const int32_t *global_idx, int n_global, const uint8_t *key_padding_mask, void *out,
-                     lf_dtype_t dtype, void *stream) {
+                     const int32_t *radius, int one_sided, const int32_t *rand_blocks, int n_rand,
+                     const int32_t *dilation, const int32_t *global_idx, int n_global,
+                     const uint8_t *key_padding_mask, void *out, lf_dtype_t dtype, void *stream) {
     g_err.clear();
     // ---- argument checks: no HIP call before all of them pass
     if (!q || !k || !v || !out) return fail(LF_E_INVALID, "q, k, v and out must be non-null");
@@ -165,6 +166,20 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
     for (int i = 0; i < n_global; i++)
         if (global_idx[i] < 0 || global_idx[i] >= T)
             return fail(LF_E_INVALID, "global_idx[%d] = %d outside [0, %d)", i, global_idx[i], T);
+    const long long nqb = cdiv(T, 64);
+    if (n_rand < 0) return fail(LF_E_INVALID, "n_rand = %d must be >= 0", n_rand);
+    if (n_rand > 0) {
+        if (!rand_blocks) return fail(LF_E_INVALID, "rand_blocks is NULL with n_rand = %d", n_rand);
+        if (n_rand > LF_MAX_RAND_BLOCKS)
+            return fail(LF_E_UNSUPPORTED, "n_rand = %d exceeds %d", n_rand, LF_MAX_RAND_BLOCKS);
+        for (int h = 0; h < H; h++)
+            if (dilation && dilation[h] != 1)
+                return fail(LF_E_UNSUPPORTED, "random key blocks need undilated heads (dilation[%d] = %d)", h,
+                            dilation[h]);
+        for (long long e = 0; e < (long long)H * nqb * n_rand; e++)
+            if (rand_blocks[e] < 0 || rand_blocks[e] >= nqb)
+                return fail(LF_E_INVALID, "rand_blocks[%lld] = %d outside [0, %lld)", e, rand_blocks[e], nqb);
+    }
     const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u;
     if (mis) return fail(LF_E_INVALID, "q, k, v and out must be 16-byte aligned");
     const size_t esize = dtype == LF_BF16 ? 2 : 4;
@@ -195,6 +210,23 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
         P.r = std::max(P.r, P.rad[h]);
     }
     P.one_sided = one_sided;
+    // random key blocks: each query block's list sorted, duplicates dropped
+    // (-1 fills the rest), then a bitmap of the global positions (a random
+    // block leaves the globals to their own path)
+    std::vector<uint32_t> aux;
+    if (n_rand > 0) {
+        const size_t nt = (size_t)H * nqb * n_rand;
+        aux.resize(nt + (size_t)cdiv(T, 32), 0u);
+        std::vector<int32_t> row(n_rand);
+        for (size_t base = 0; base < nt; base += n_rand) {
+            std::copy(rand_blocks + base, rand_blocks + base + n_rand, row.begin());
+            std::sort(row.begin(), row.end());
+            const size_t u = std::unique(row.begin(), row.end()) - row.begin();
+            for (int e = 0; e < n_rand; e++) aux[base + e] = (uint32_t)(e < (int)u ? row[e] : -1);
+        }
+        for (int g : G) aux[nt + (g >> 5)] |= 1u << (g & 31);
+    }
+    P.n_rand = n_rand;
     // heads with unequal radii make tiles of unequal cost: deal runs of 8
     // tiles to the dies in turn instead of one contiguous eighth per die
     P.band_chunk = 0;
@@ -268,6 +300,28 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
             P.vp = ws + planes_off + nbytes;
         }
     }
+    if (n_rand > 0) {
+        lf_status_t st = grow(w->aux, aux.size() * sizeof(uint32_t), false, stream);
+        if (st != LF_OK) return st;
+        if (w->aux_shadow != aux) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
+            if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+            if (cs != hipStreamCaptureStatusNone)
+                return fail(LF_E_UNSUPPORTED,
+                            "the random key blocks differ from the previous call on this stream during stream "
+                            "capture; make one identical call outside capture first");
+            e = hipMemcpyAsync(w->aux.ptr, aux.data(), aux.size() * sizeof(uint32_t), hipMemcpyHostToDevice,
+                               (hipStream_t)stream);
+            if (e != hipSuccess) {
+                w->aux_shadow.clear();
+                return fail(LF_E_HIP, "random-block upload: %s", hipGetErrorString(e));
+            }
+            w->aux_shadow = aux;
+        }
+        P.rtab = (const int32_t *)w->aux.ptr;
+        P.gmap = (const uint32_t *)w->aux.ptr + (size_t)H * nqb * n_rand;
+    }
     lfk::Args A;
     A.q = q; A.k = k; A.v = v; A.out = out;
     A.pad = key_padding_mask;
@@ -284,17 +338,17 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
                                    int d, int r, const int32_t *dilation, const int32_t *global_idx,
                                    int n_global, const uint8_t *key_padding_mask, void *out,
                                    lf_dtype_t dtype, void *stream) {
-    return attn_fwd(q, k, v, B, H, T, d, r, nullptr, 0, dilation, global_idx, n_global, key_padding_mask,
-                    out, dtype, stream);
+    return attn_fwd(q, k, v, B, H, T, d, r, nullptr, 0, nullptr, 0, dilation, global_idx, n_global,
+                    key_padding_mask, out, dtype, stream);
 }
 
 extern "C" lf_status_t lf_attn_fwd_ex(const void *q, const void *k, const void *v, int B, int H, int T,
-                                      int d, const int32_t *radius, int one_sided, const int32_t *dilation,
-                                      const int32_t *global_idx, int n_global,
-                                      const uint8_t *key_padding_mask, void *out, lf_dtype_t dtype,
-                                      void *stream) {
+                                      int d, const int32_t *radius, int one_sided, const int32_t *rand_blocks,
+                                      int n_rand, const int32_t *dilation, const int32_t *global_idx,
+                                      int n_global, const uint8_t *key_padding_mask, void *out,
+                                      lf_dtype_t dtype, void *stream) {
     g_err.clear();
     if (!radius) return fail(LF_E_INVALID, "radius must be a host array of H radii");
-    return attn_fwd(q, k, v, B, H, T, d, 0, radius, one_sided, dilation, global_idx, n_global,
-                    key_padding_mask, out, dtype, stream);
+    return attn_fwd(q, k, v, B, H, T, d, 0, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
+                    n_global, key_padding_mask, out, dtype, stream);
 }

@@ -45,6 +45,9 @@ struct Plan {
     int32_t dil[LF_MAX_HEADS];      // 32-bit: a head's entry is one scalar load
     int32_t rad[LF_MAX_HEADS];      // window radius per head (clamped to T)
     int one_sided;                  // 1: the window keeps the keys at or before the query
+    const int32_t *rtab;            // random key blocks [H][ceil(T/64)][n_rand] (-1 = none), or null
+    const uint32_t *gmap;           // bit j set iff position j is global ([ceil(T/32)] words), or null
+    int n_rand;                     // random key blocks (of 64 keys) per query block of 64
     int band_chunk;                 // 0: each die takes a contiguous eighth of the band tiles;
                                     // C > 0: runs of C tiles are dealt to the dies in turn
     int32_t glob[LF_MAX_GLOBALS];

@@ -55,6 +55,7 @@ class Workload:
     description: str = ""
     radius: Optional[tuple] = None  # one radius per head (replaces r), None = r for all
     one_sided: bool = False         # window keeps only the keys at or before the query
+    n_rand: int = 0                 # random key blocks of 64 per query block of 64 (drawn last)
 
 
 WORKLOADS: List[Workload] = [
@@ -81,6 +82,11 @@ WORKLOADS: List[Workload] = [
     Workload("bf16-b1h12t4096-rhead-g1", 1007, 1, 12, 4096, 64, 512, "bf16",
              fixed_globals=(0,), radius=(32, 32, 64, 64, 128, 128, 256, 256, 384, 384, 512, 512),
              description="one radius per head, 32..512 in pairs, global at 0, bf16 N(0,1)"),
+    # BigBird-style: window of about three blocks, the first and last token global,
+    # three random key blocks of 64 per query block of 64
+    Workload("bf16-b1h12t4096-r96-g2-rand3", 1008, 1, 12, 4096, 64, 96, "bf16",
+             fixed_globals=(0, 4095), n_rand=3,
+             description="r=96, globals 0 and T-1, 3 random key blocks of 64 per query block (per head), bf16 N(0,1)"),
 ]
 
 
@@ -116,6 +122,7 @@ class Inputs:
     key_padding_mask: Optional[torch.Tensor]  # uint8 [B][T], nonzero = padded
     extra: dict = field(default_factory=dict)
     one_sided: bool = False                   # r: one radius, or a list with one per head
+    random_blocks: Optional[np.ndarray] = None  # int32 [H][ceil(T/64)][n_rand] key-block indices
 
 
 def _draw_qkv(seed, B, H, T, d, scale, dtype):
@@ -169,12 +176,18 @@ def make_inputs(w: Workload, dtype: Optional[str] = None, T: Optional[int] = Non
     if dil is not None and len(dil) < H_:
         dil = dil + [1] * (H_ - len(dil))
     r = list(w.radius)[:H_] if w.radius else w.r
-    return Inputs(q, k, v, r, dil, glob, lengths, kpm, one_sided=w.one_sided)
+    rb = None
+    if w.n_rand:
+        # per head and query block: n_rand distinct key blocks, uniform
+        nqb = (T_ + 63) // 64
+        rb = np.stack([np.stack([rng.choice(nqb, size=min(w.n_rand, nqb), replace=False) for _ in range(nqb)])
+                       for _ in range(H_)]).astype(np.int32)
+    return Inputs(q, k, v, r, dil, glob, lengths, kpm, one_sided=w.one_sided, random_blocks=rb)
 
 
 def random_case(seed: int, B: int, H: int, T: int, d: int = 64, dtype: str = "f32",
                 r: Optional[int] = None, max_dil: int = 4, n_global: Optional[int] = None,
-                pad: str = "random") -> Inputs:
+                pad: str = "random", n_rand: int = 0) -> Inputs:
     """A small random case for edge-case sweeps.
 
     pad: "none", "right" (random valid length per sequence, possibly 0) or
@@ -197,4 +210,10 @@ def random_case(seed: int, B: int, H: int, T: int, d: int = 64, dtype: str = "f3
         kpm = (pos >= torch.tensor(lengths).unsqueeze(1)).to(torch.uint8).contiguous()
     elif pad == "random":
         kpm = torch.from_numpy((rng.random((B, T)) < 0.2).astype(np.uint8)).contiguous()
-    return Inputs(q, k, v, r, dil, glob, lengths, kpm)
+    rb = None
+    if n_rand:
+        # random key blocks need undilated heads; blocks may repeat (they count once)
+        dil = [1] * H
+        nqb = (T + 63) // 64
+        rb = rng.integers(0, nqb, size=(H, nqb, n_rand)).astype(np.int32)
+    return Inputs(q, k, v, r, dil, glob, lengths, kpm, random_blocks=rb)

@@ -31,7 +31,7 @@ def gpu_fwd(inp, q=None, k=None, v=None):
     if v is not None:
         vd = v.to("cuda:0")
     out = lf.attn_fwd(qd, kd, vd, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm,
-                      one_sided=inp.one_sided)
+                      one_sided=inp.one_sided, random_blocks=inp.random_blocks)
     torch.cuda.synchronize()
     return out
 
@@ -39,7 +39,7 @@ def gpu_fwd(inp, q=None, k=None, v=None):
 def oracle_full(inp, q=None, k=None, v=None):
     return oracle.fwd(inp.q if q is None else q, inp.k if k is None else k,
                       inp.v if v is None else v, inp.r, inp.dilation, inp.global_idx,
-                      inp.key_padding_mask, one_sided=inp.one_sided)
+                      inp.key_padding_mask, one_sided=inp.one_sided, random_blocks=inp.random_blocks)
 
 
 def max_err(gpu_out, ref):

@@ -140,7 +140,7 @@ def test_ex_invalid_arguments_rejected(lib, name, kw, status):
         rad = (ctypes.c_int32 * 2)(*radius)
         dil = (ctypes.c_int32 * 2)(*a["dil"])
         g = (ctypes.c_int32 * 1)(*a["g"])
-        st = lib.lf_attn_fwd_ex(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], rad, 2, dil, g,
+        st = lib.lf_attn_fwd_ex(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], rad, 2, None, 0, dil, g,
                                 a["ng"], None, a["out"], a["dtype"], None)
     else:
         st = call_ex(radius, one, **kw)
@@ -150,6 +150,38 @@ def test_ex_invalid_arguments_rejected(lib, name, kw, status):
 
 def test_ex_null_radius_rejected(lib):
     a = dict(GOOD)
-    st = lib.lf_attn_fwd_ex(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], None, 0, None, None, 0,
-                            None, a["out"], a["dtype"], None)
+    st = lib.lf_attn_fwd_ex(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], None, 0, None, 0, None, None,
+                            0, None, a["out"], a["dtype"], None)
     assert st == lf.LF_E_INVALID and "radius" in lf.last_error()
+
+
+def _rb(H, T, n, fill=0):
+    return np.full((H, (T + 63) // 64, n), fill, dtype=np.int32)
+
+
+BAD_RAND = [
+    ("block_out_of_range", dict(rb=_rb(2, 128, 2, 2), dil=None), lf.LF_E_INVALID),
+    ("block_negative", dict(rb=_rb(2, 128, 1, -1), dil=None), lf.LF_E_INVALID),
+    ("too_many_blocks", dict(rb=_rb(2, 128, 9), dil=None), lf.LF_E_UNSUPPORTED),
+    ("dilated_head", dict(rb=_rb(2, 128, 1), dil=[1, 2]), lf.LF_E_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_RAND, ids=[b[0] for b in BAD_RAND])
+def test_random_blocks_invalid_rejected(lib, name, kw, status):
+    kw = dict(kw)
+    rb = kw.pop("rb")
+    a = dict(GOOD)
+    a.update(kw)
+    st = lf.raw_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], 8, a["dil"], a["g"], a["ng"],
+                    a["kpm"], a["out"], a["dtype"], None, False, rb)
+    assert st == status, (name, st, lf.last_error())
+    assert lf.last_error() != ""
+
+
+def test_random_blocks_null_table_rejected(lib):
+    a = dict(GOOD)
+    rad = (ctypes.c_int32 * 2)(8, 8)
+    st = lib.lf_attn_fwd_ex(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], rad, 0, None, 2, None, None,
+                            0, None, a["out"], a["dtype"], None)
+    assert st == lf.LF_E_INVALID and "rand_blocks" in lf.last_error()

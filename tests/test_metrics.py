@@ -59,9 +59,9 @@ def test_counter_matches_enumeration_workloads(name):
     inp = W.make_inputs(w, **kw)
     B, H, T, d = inp.q.shape
     want = oracle.count_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
-                              one_sided=inp.one_sided)
+                              one_sided=inp.one_sided, random_blocks=inp.random_blocks)
     got = metrics.useful_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
-                               one_sided=inp.one_sided)
+                               one_sided=inp.one_sided, random_blocks=inp.random_blocks)
     assert got == want
 
 

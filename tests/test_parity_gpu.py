@@ -31,6 +31,7 @@ REDUCED = {
     "bf16-b4h16t16384-r512-g8-pad": dict(T=2100, H=3),
     "bf16-b1h12t4096-r256-g1-onesided": dict(T=1300),
     "bf16-b1h12t4096-rhead-g1": dict(T=1400),
+    "bf16-b1h12t4096-r96-g2-rand3": dict(T=1500),
 }
 
 
@@ -59,7 +60,7 @@ def test_workload_full_size_sampled(name, dtype):
     out = gpu_fwd(inp)
     rows = sample_rows(inp, n_random=1500, seed=w.seed)
     ref = oracle.rows(inp.q, inp.k, inp.v, inp.r, rows, inp.dilation, inp.global_idx,
-                      inp.key_padding_mask, one_sided=inp.one_sided)
+                      inp.key_padding_mask, one_sided=inp.one_sided, random_blocks=inp.random_blocks)
     got = out.float().cpu().double().reshape(-1, w.d).numpy()[rows]
     err = float(np.max(np.abs(got - ref)))
     print(f"  {len(rows)} rows, max abs err {err:.3e}", flush=True)
@@ -108,6 +109,26 @@ def test_window_forms(T, one_sided):
             assert err <= TOL[dt], err
 
 
+# ---- random key blocks (lf_attn_fwd_ex): ragged T, blocks that repeat or
+# overlap the window, globals inside random blocks, padding, both window forms
+@pytest.mark.parametrize("n_rand", [1, 3])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 300, 700])
+def test_random_blocks(T, n_rand):
+    for dt in ("f32", "bf16"):
+        for seed, pad in enumerate(("none", "right", "random")):
+            base = W.random_case(seed * 104729 + T + n_rand, B=2, H=3, T=T, dtype=dt, pad=pad, n_rand=n_rand)
+            rng = np.random.default_rng(seed * 17 + T)
+            one = bool(seed % 2)
+            r = [int(x) for x in rng.integers(0, 100, size=3)] if seed == 2 else int(rng.integers(0, 100))
+            inp = W.Inputs(base.q, base.k, base.v, r, base.dilation, base.global_idx, base.lengths,
+                           base.key_padding_mask, one_sided=one, random_blocks=base.random_blocks)
+            print(f"case T={T} n_rand={n_rand} dt={dt} pad={pad} r={r} one_sided={one} G={inp.global_idx}",
+                  flush=True)
+            out = gpu_fwd(inp)
+            err = max_err(out, oracle_full(inp))
+            assert err <= TOL[dt], err
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_named_edge_cases(dt):
     base = W.random_case(5, B=2, H=2, T=200, dtype=dt, pad="none")
@@ -141,7 +162,7 @@ def test_named_edge_cases(dt):
 def test_tracer_counts_exact_neighbour_sets(dt):
     for name in ["bf16-b1h12t4096-r256-g1", "bf16-b1h12t4096-r128-dil", "bf16-b2h12t4096-r256-g68",
                  "bf16-b4h16t16384-r512-g8-pad", "bf16-b1h12t4096-r256-g1-onesided",
-                 "bf16-b1h12t4096-rhead-g1"]:
+                 "bf16-b1h12t4096-rhead-g1", "bf16-b1h12t4096-r96-g2-rand3"]:
         w = W.workload(name)
         inp = W.make_inputs(w, dtype=dt, T=min(w.T, 1500), H=min(w.H, 4))
         B, H, T, d = inp.q.shape
