@@ -592,7 +592,7 @@ __device__ __forceinline__ void gkey_fold(WaveState<NP>& W, const GKey<NP>& g, f
 // ---------------------------------------------------------------------------
 // The tile kernel.
 
-template <int QB, int KS, typename ET, typename OT, bool PAD>
+template <int QB, int KS, typename ET, typename OT, bool PAD, bool RAND>
 __global__ __launch_bounds__(64 * QB * KS) __attribute__((amdgpu_waves_per_eu(Elem<ET>::NP == 1 ? LFK_WAVES_PER_EU_BF16 : LFK_WAVES_PER_EU_F32)))
 void tile_kernel(const Args A) {
     static_assert(QB == 2 && KS == 2, "four waves: two phases of two query blocks");
@@ -722,7 +722,7 @@ void tile_kernel(const Args A) {
     const int ngb = (tk.kind == 0 && !gvec) ? cdiv(n_g, KBLK) : 0;
     // random key blocks of this query block (undilated heads): each block of
     // 64 keys is two 32-key blocks, after the band and the global-key blocks
-    const int nrb = tk.kind == 0 ? 2 * P.n_rand : 0;
+    const int nrb = RAND && tk.kind == 0 ? 2 * P.n_rand : 0;   // RAND false: none, at compile time
     const int32_t* rrow = nrb > 0 ? P.rtab + ((size_t)tk.h * ((T + 63) >> 6) + (tk.m0 >> 6)) * P.n_rand : nullptr;
     // position of row 0 of random block position jr, or T for none (an empty
     // entry, or a position past this tile's list: a phase's last step can
@@ -1062,7 +1062,8 @@ void tile_kernel(const Args A) {
     // stages from the first random block on take the step with random blocks
     const int s_rand = nrb > 0 ? (nb + ngb) >> 1 : NS;
     for (; s < min(NS, s_rand); s++) step(General{}, s, (s & 1) * RG::STAGE, ((s + 1) & 1) * RG::STAGE);
-    for (; s < NS; s++) step(WithRandom{}, s, (s & 1) * RG::STAGE, ((s + 1) & 1) * RG::STAGE);
+    if constexpr (RAND)
+        for (; s < NS; s++) step(WithRandom{}, s, (s & 1) * RG::STAGE, ((s + 1) & 1) * RG::STAGE);
     __syncthreads();
 
     // ---- merge the KS phases of each query block (LDS); phase 0 keeps the result
@@ -1280,24 +1281,29 @@ extern "C" int lfk_grid(const lfk::Plan* P) {
 }
 
 // A: kernel argument (A->plan is the device copy of *P); P: host copy of the plan
-extern "C" hipError_t lfk_launch(const lfk::Args* A, const lfk::Plan* P, int dtype_bf16, void* stream) {
-    hipStream_t s = (hipStream_t)stream;
+// one instantiation per input type, padding and random blocks (each present
+// or not at compile time)
+template <typename ET, typename OT>
+static void launch_tiles(const lfk::Args* A, const lfk::Plan* P, hipStream_t s) {
     constexpr int QB = LFK_QB, KS = LFK_KS;
     const int grid = lfk_grid(P);
-    const bool pad = A->pad != nullptr;
+    const bool pad = A->pad != nullptr, rnd = P->n_rand > 0;
+    const dim3 g(grid), b(64 * QB * KS);
+    if (pad && rnd) hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, ET, OT, true, true>), g, b, 0, s, *A);
+    else if (pad) hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, ET, OT, true, false>), g, b, 0, s, *A);
+    else if (rnd) hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, ET, OT, false, true>), g, b, 0, s, *A);
+    else hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, ET, OT, false, false>), g, b, 0, s, *A);
+}
+
+extern "C" hipError_t lfk_launch(const lfk::Args* A, const lfk::Plan* P, int dtype_bf16, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
     if (dtype_bf16) {
-        if (pad)
-            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, __bf16, uint16_t, true>), dim3(grid), dim3(64 * QB * KS), 0, s, *A);
-        else
-            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, __bf16, uint16_t, false>), dim3(grid), dim3(64 * QB * KS), 0, s, *A);
+        launch_tiles<__bf16, uint16_t>(A, P, s);
     } else {
         const long long chunks = (long long)P->B * P->H * P->T * 8;
         hipLaunchKernelGGL(lfk::split_planes_kernel, dim3((unsigned)((chunks + 255) / 256), 2), dim3(256), 0, s,
                            (const float*)A->k, (const float*)A->v, (uint16_t*)P->kp, (uint16_t*)P->vp, chunks);
-        if (pad)
-            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, float, float, true>), dim3(grid), dim3(64 * QB * KS), 0, s, *A);
-        else
-            hipLaunchKernelGGL((lfk::tile_kernel<QB, KS, float, float, false>), dim3(grid), dim3(64 * QB * KS), 0, s, *A);
+        launch_tiles<float, float>(A, P, s);
     }
     return hipGetLastError();
 }
