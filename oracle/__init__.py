@@ -39,6 +39,8 @@ def open_library(path):
     lib.lf_oracle_neighbours2.restype = I
     lib.lf_oracle_count_pairs2.argtypes = [I, I, I, I, P, I, P, I, P, P, I, P]
     lib.lf_oracle_count_pairs2.restype = LL
+    lib.lf_oracle_bwd.argtypes = [P, P, P, P, I, I, I, I, I, P, I, P, I, P, P, I, P, P, P, P, I]
+    lib.lf_oracle_bwd.restype = I
     return lib
 
 
@@ -121,6 +123,29 @@ def fwd(q, k, v, r, dilation=None, global_idx=None, key_padding_mask=None, n_thr
     if nt < 0:
         raise ValueError("oracle rejected its arguments")
     return (out, nt) if return_threads else out
+
+
+def bwd(q, k, v, dy, r, dilation=None, global_idx=None, key_padding_mask=None, n_threads=0,
+        lib=None, one_sided=False, random_blocks=None):
+    """Gradients of the forward for the upstream gradient ``dy`` [B][H][T][d]:
+    returns (dq, dk, dv), numpy float64, same arguments as ``fwd``."""
+    lib = lib or _load()
+    qf, kf, vf, dyf = _f32(q), _f32(k), _f32(v), _f32(dy)
+    B, H, T, d = qf.shape
+    if dyf.shape != qf.shape:
+        raise ValueError("dy must have the shape of q")
+    r0, rad = _radius(r, H)
+    rb, nr = _rand_blocks(random_blocks, H, T)
+    dil = _i32(dilation)
+    g = _i32(global_idx if global_idx is not None else [])
+    pad = _u8(key_padding_mask)
+    dq, dk, dv = (np.zeros((B, H, T, d), dtype=np.float64) for _ in range(3))
+    nt = lib.lf_oracle_bwd(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(dyf), B, H, T, d, r0, _ptr(rad),
+                           int(bool(one_sided)), _ptr(rb), nr, _ptr(dil), _ptr(g), int(g.size), _ptr(pad),
+                           _ptr(dq), _ptr(dk), _ptr(dv), int(n_threads))
+    if nt < 0:
+        raise ValueError("oracle rejected its arguments")
+    return dq, dk, dv
 
 
 def rows(q, k, v, r, rows_flat, dilation=None, global_idx=None, key_padding_mask=None,

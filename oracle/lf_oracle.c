@@ -50,12 +50,24 @@
  * are widened exactly.  Sums run in ascending key order, so the result is
  * reproducible bit for bit.
  *
+ * Gradients (lf_oracle_bwd).  The pages give no backward pass; Longformer
+ * (ciallo.wiki) §5.2 only says that training cost grows linearly with the
+ * length.  What is computed is the derivative of the forward map above,
+ * from the chain rule through the softmax: with P_ij the weights of row i,
+ * dP_ij = dy_i . v_j and D_i = sum_j P_ij dP_ij,
+ *     dv_j += P_ij dy_i,   dS_ij = P_ij (dP_ij - D_i),
+ *     dq_i += dS_ij k_j / sqrt(d_k),   dk_j += dS_ij q_i / sqrt(d_k),
+ * summed over the same allowed pairs as the forward.  A padded query row is
+ * zero whatever q_i holds, so it passes no gradient.
+ *
  * Pins (checked in the CPU test suite): dense brute force with an explicit
  * T x T boolean mask on tiny T; closed-form neighbour counts; v == 1 gives
  * y == 1; q == 0 gives the plain mean of v over N(i); r = 0 with no globals
  * gives y_i = v_i; r >= T-1 equals textbook dense attention; a dilated
  * head equals delta undilated problems on the residue subsequences; keys
  * outside N(i) do not influence row i; global rows equal dense rows.
+ * Gradients: float64 autograd of the dense brute force, central finite
+ * differences, sum_j dk_j = 0 and sum_j dv_j = sum of dy over valid rows.
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -313,7 +325,130 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
 }
 
 /* ------------------------------------------------------------------ */
+/* Gradients: one thread per (b, h) at a time, so that the key-side sums of
+ * a head stay in one thread. */
+
+typedef struct {
+    job_t base;             /* shapes, sets and inputs; rows unused */
+    const float *dy;
+    double *dq, *dk, *dv;
+    long long n_bh;
+} bjob_t;
+
+static void grad_row(const float *qi, const float *dyi, const float *K, const float *V, int d,
+                     const int *nb, int n, double *s, double *dqi, double *dK, double *dV) {
+    if (n == 0) return;
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double m = -INFINITY;
+    for (int t = 0; t < n; t++) {
+        const float *kj = K + (size_t)nb[t] * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; c++) dot += (double)qi[c] * (double)kj[c];
+        s[t] = dot * inv_sqrt_d;
+        if (s[t] > m) m = s[t];
+    }
+    double l = 0.0;
+    for (int t = 0; t < n; t++) {
+        s[t] = exp(s[t] - m);
+        l += s[t];
+    }
+    /* P_ij in s; D_i = sum_j P_ij dP_ij */
+    double D = 0.0;
+    for (int t = 0; t < n; t++) {
+        s[t] /= l;
+        const float *vj = V + (size_t)nb[t] * d;
+        double dp = 0.0;
+        for (int c = 0; c < d; c++) dp += (double)dyi[c] * (double)vj[c];
+        D += s[t] * dp;
+    }
+    for (int t = 0; t < n; t++) {
+        const int j = nb[t];
+        const float *kj = K + (size_t)j * d, *vj = V + (size_t)j * d;
+        double dp = 0.0;
+        for (int c = 0; c < d; c++) dp += (double)dyi[c] * (double)vj[c];
+        const double ds = s[t] * (dp - D);
+        for (int c = 0; c < d; c++) {
+            dqi[c] += ds * inv_sqrt_d * (double)kj[c];
+            dK[(size_t)j * d + c] += ds * inv_sqrt_d * (double)qi[c];
+            dV[(size_t)j * d + c] += s[t] * (double)dyi[c];
+        }
+    }
+}
+
+static void *bworker(void *arg) {
+    bjob_t *bj = (bjob_t *)arg;
+    job_t *jb = &bj->base;
+    int *nb = (int *)malloc(sizeof(int) * (size_t)jb->T);
+    double *s = (double *)malloc(sizeof(double) * (size_t)jb->T);
+    unsigned char *mark = (unsigned char *)malloc((size_t)jb->T);
+    if (!nb || !s || !mark) { jb->err = 1; free(nb); free(s); free(mark); return NULL; }
+    const size_t nqb = ((size_t)jb->T + RAND_BLOCK - 1) / RAND_BLOCK;
+    for (long long bh = jb->tid; bh < bj->n_bh; bh += jb->n_threads) {
+        int b = (int)(bh / jb->H), h = (int)(bh % jb->H);
+        int delta = jb->dil ? jb->dil[h] : 1;
+        int rh = jb->rad ? jb->rad[h] : jb->r;
+        const unsigned char *padrow = jb->pad ? jb->pad + (size_t)b * jb->T : NULL;
+        const int *rb = jb->rblk ? jb->rblk + (size_t)h * nqb * jb->n_rand : NULL;
+        const size_t base = (size_t)bh * jb->T * jb->d;
+        for (size_t e = 0; e < (size_t)jb->T * jb->d; e++)
+            bj->dq[base + e] = bj->dk[base + e] = bj->dv[base + e] = 0.0;
+        for (int i = 0; i < jb->T; i++) {
+            int n = neighbours(jb->T, rh, delta, jb->one_sided, jb->G, padrow, i, nb, rb, jb->n_rand, mark);
+            grad_row(jb->q + base + (size_t)i * jb->d, bj->dy + base + (size_t)i * jb->d, jb->k + base,
+                     jb->v + base, jb->d, nb, n, s, bj->dq + base + (size_t)i * jb->d, bj->dk + base,
+                     bj->dv + base);
+        }
+    }
+    free(nb);
+    free(s);
+    free(mark);
+    return NULL;
+}
+
+/* ------------------------------------------------------------------ */
 /* Exported entry points (plain C ABI for ctypes). */
+
+/* Gradients of the full forward (same arguments as lf_oracle_fwd2) for the
+ * upstream gradient dy[B][H][T][d]: dq, dk, dv [B][H][T][d] in fp64.
+ * Returns the thread count used, or -1 on invalid arguments. */
+int lf_oracle_bwd(const float *q, const float *k, const float *v, const float *dy, int B, int H, int T,
+                  int d, int r, const int *radius, int one_sided, const int *rand_blocks, int n_rand,
+                  const int *dilation, const int *global_idx, int n_global,
+                  const unsigned char *key_padding_mask, double *dq, double *dk, double *dv,
+                  int n_threads) {
+    if (check_args(B, H, T, d, r, radius, one_sided, dilation)) return -1;
+    if (check_rand(H, T, dilation, rand_blocks, n_rand)) return -1;
+    if (n_global < 0 || (n_global > 0 && !global_idx)) return -1;
+    gset_t G;
+    if (gset_make(&G, global_idx, n_global, T)) return -1;
+    const long long n_bh = (long long)B * H;
+    if (n_threads <= 0) n_threads = host_threads();
+    if ((long long)n_threads > n_bh) n_threads = (int)n_bh;
+    bjob_t *jobs = (bjob_t *)calloc((size_t)n_threads, sizeof(bjob_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); free(G.pos); return -1; }
+    for (int t = 0; t < n_threads; t++) {
+        job_t j = {q, k, v, B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation, &G,
+                   key_padding_mask, NULL, 0, NULL, n_threads, t, 0};
+        jobs[t].base = j;
+        jobs[t].dy = dy;
+        jobs[t].dq = dq;
+        jobs[t].dk = dk;
+        jobs[t].dv = dv;
+        jobs[t].n_bh = n_bh;
+    }
+    for (int t = 1; t < n_threads; t++)
+        if (pthread_create(&th[t], NULL, bworker, &jobs[t])) { jobs[t].base.err = 1; th[t] = 0; }
+    bworker(&jobs[0]);
+    int err = 0;
+    for (int t = 1; t < n_threads; t++) if (th[t]) pthread_join(th[t], NULL);
+    for (int t = 0; t < n_threads; t++) err |= jobs[t].base.err;
+    free(jobs);
+    free(th);
+    free(G.pos);
+    return err ? -1 : n_threads;
+}
+
 
 /* Full forward: out[B][H][T][d] in fp64.  radius: [H] per-head radii or
  * NULL (then r for every head); one_sided: 0 two-sided, 1 one-sided.

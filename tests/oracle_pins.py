@@ -29,6 +29,11 @@ one of them.  The pins:
   blocks of 64): the brute force with the blocks added to each row's mask,
   an exact count for r = 0, and every block drawn for every query block
   giving dense attention.
+* gradients (the derivative of the forward map; the pages give no backward
+  pass): torch float64 autograd through the dense brute force, central
+  finite differences of the oracle's own forward, and the sum rules
+  sum_j dk_j = 0 (softmax weights sum to one, so the dS of a row sums to
+  zero) and sum_j dv_j = sum of dy over the rows that attend to something.
 """
 import numpy as np
 import torch
@@ -336,6 +341,103 @@ def check_rows_entry_point(lib=None):
         assert np.array_equal(part, full.reshape(-1, d)[sel])
 
 
+# --------------------------------------------------------------------------
+# gradients
+
+def dense_grads_autograd(c, dy):
+    """dq, dk, dv of sum(y * dy) through the dense masked forward, by torch
+    float64 autograd (an independent route to the same derivative)."""
+    q = c["q"].double().clone().requires_grad_(True)
+    k = c["k"].double().clone().requires_grad_(True)
+    v = c["v"].double().clone().requires_grad_(True)
+    B, H, T, d = q.shape
+    outs = []
+    for b in range(B):
+        pad_row = None if c["pad"] is None else np.asarray(c["pad"][b]).astype(bool)
+        per_h = []
+        for h in range(H):
+            rh = int(c["r"]) if np.isscalar(c["r"]) else int(c["r"][h])
+            A = allowed_matrix(T, rh, int(c["dil"][h]), c["G"], pad_row, c["one"],
+                               None if c["rb"] is None else c["rb"][h])
+            if pad_row is not None:
+                A = A & ~pad_row[:, None]
+            At = torch.from_numpy(A)
+            S = (q[b, h] @ k[b, h].T) / np.sqrt(d)
+            S = S.masked_fill(~At, float("-inf"))
+            live = At.any(dim=1, keepdim=True)
+            S = torch.where(live, S, torch.zeros_like(S))       # rows with no key: no NaN
+            P = torch.softmax(S, dim=1) * live
+            per_h.append(P @ v[b, h])
+        outs.append(torch.stack(per_h))
+    y = torch.stack(outs)
+    (y * torch.as_tensor(dy, dtype=torch.float64)).sum().backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+def _dy(seed, shape):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32)
+
+
+def check_grad_autograd(lib=None, n=16, tol=1e-11):
+    for e, c in enumerate(random_cases(n, seed0=7, Ts=(1, 2, 7, 33, 64, 97))):
+        dy = _dy(500 + e, c["q"].shape)
+        got = oracle.bwd(c["q"], c["k"], c["v"], dy, c["r"], c["dil"], c["G"], c["pad"], lib=lib,
+                         one_sided=c["one"], random_blocks=c["rb"])
+        ref = dense_grads_autograd(c, dy.numpy())
+        for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+            err = np.max(np.abs(a - b)) if a.size else 0.0
+            assert err <= tol * max(1.0, np.max(np.abs(b)) if b.size else 1.0), \
+                f"{name} vs autograd: {err} (T={c['q'].shape[2]}, r={c['r']}, one={c['one']})"
+
+
+def check_grad_finite_differences(lib=None):
+    # f(x) = sum(y(x) * dy); central differences with a step exact in float32
+    rng = np.random.default_rng(3)
+    B, H, T, d = 1, 2, 11, 4
+    q, k, v = _rand(77, B, H, T, d)
+    dy = _dy(78, (B, H, T, d)).numpy().astype(np.float64)
+    pad = np.zeros((B, T), dtype=np.uint8)
+    pad[0, 9] = 1
+    args = dict(r=[2, 1], dilation=[1, 2], global_idx=[4], key_padding_mask=pad)
+    dq, dk, dv = oracle.bwd(q, k, v, dy, lib=lib, **args)
+    h = 2.0 ** -10
+
+    def f(qq, kk, vv):
+        return float(np.sum(oracle.fwd(qq, kk, vv, lib=lib, **args) * dy))
+
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for _ in range(12):
+            idx = (0, int(rng.integers(0, H)), int(rng.integers(0, T)), int(rng.integers(0, d)))
+            xs = [q.clone(), k.clone(), v.clone()]
+            xs[which][idx] += h
+            fp = f(*xs)
+            xs[which][idx] -= 2 * h
+            fm = f(*xs)
+            fd = (fp - fm) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-5 * max(1.0, abs(fd)), (which, idx, fd, grad[idx])
+
+
+def check_grad_sum_rules(lib=None):
+    for e, c in enumerate(random_cases(12, seed0=11)):
+        dy = _dy(900 + e, c["q"].shape)
+        dq, dk, dv = oracle.bwd(c["q"], c["k"], c["v"], dy, c["r"], c["dil"], c["G"], c["pad"], lib=lib,
+                                one_sided=c["one"], random_blocks=c["rb"])
+        B, H, T, d = dq.shape
+        assert np.max(np.abs(dk.sum(axis=2)), initial=0.0) <= 1e-9
+        for b in range(B):
+            for h in range(H):
+                pad_row = None if c["pad"] is None else np.asarray(c["pad"][b])
+                # a valid query always attends to itself, a padded one to nothing
+                live = np.ones(T, dtype=bool) if pad_row is None else ~pad_row.astype(bool)
+                want = dy.numpy()[b, h][live].astype(np.float64).sum(axis=0)
+                assert np.max(np.abs(dv[b, h].sum(axis=0) - want), initial=0.0) <= 1e-9
+                if pad_row is not None:
+                    pr = pad_row.astype(bool)
+                    assert not np.any(dq[b, h][pr]) and not np.any(dk[b, h][pr]) and not np.any(dv[b, h][pr])
+
+
 ALL_CHECKS = [check_dense_bruteforce, check_closed_form_counts, check_neighbour_sets,
               check_invariants, check_identity_and_dense_limits, check_window_exclusivity,
-              check_dilation_split, check_rows_entry_point]
+              check_dilation_split, check_rows_entry_point, check_grad_autograd,
+              check_grad_finite_differences, check_grad_sum_rules]

@@ -43,6 +43,12 @@ MUTANTS = [
     ("random_block_shifted", "const int j0 = rb[e] * RAND_BLOCK;", "const int j0 = rb[e] * RAND_BLOCK + 1;"),
     ("random_padded_kept", "if (!(pad && pad[j])) mark[j] = 1;", "mark[j] = 1;"),
     ("random_block_of_wrong_query", "rblk + (size_t)(i / RAND_BLOCK) * n_rand", "rblk + (size_t)(i / RAND_BLOCK / 2) * n_rand"),
+    ("grad_no_D_term", "D += s[t] * dp;", ""),
+    ("grad_dk_unscaled", "dK[(size_t)j * d + c] += ds * inv_sqrt_d * (double)qi[c];",
+     "dK[(size_t)j * d + c] += ds * (double)qi[c];"),
+    ("grad_weights_unnormalised", "s[t] /= l;", ""),
+    ("grad_dq_from_v", "dqi[c] += ds * inv_sqrt_d * (double)kj[c];", "dqi[c] += ds * inv_sqrt_d * (double)vj[c];"),
+    ("grad_dv_sign", "dV[(size_t)j * d + c] += s[t] * (double)dyi[c];", "dV[(size_t)j * d + c] -= s[t] * (double)dyi[c];"),
 ]
 
 
