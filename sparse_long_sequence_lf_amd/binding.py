@@ -50,6 +50,8 @@ def load():
     lib.lf_attn_fwd.restype = I
     lib.lf_attn_fwd_ex.argtypes = [P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, I, P]
     lib.lf_attn_fwd_ex.restype = I
+    lib.lf_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P, I, P, P, P, P, I, P]
+    lib.lf_attn_bwd.restype = I
     lib.lf_last_error.argtypes = []
     lib.lf_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -161,6 +163,73 @@ def attn_fwd(q, k, v, r, dilation: Optional[Sequence[int]] = None,
         raise ValueError(f"r has {len(r)} radii for {H} heads")
     st = raw_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, r, dilation,
                  gl if gl else None, len(gl), kpm_ptr, out.data_ptr(), dt, sptr, one_sided, random_blocks)
+    if st != LF_OK:
+        raise LfError(st, last_error())
+    return out
+
+
+def raw_bwd(q_ptr, k_ptr, v_ptr, dy_ptr, B, H, T, d, r, one_sided, dilation, global_idx, n_global, kpm_ptr,
+            dq_ptr, dk_ptr, dv_ptr, dtype, stream_ptr) -> int:
+    """lf_attn_bwd with raw integer device pointers; ``r`` is one radius or
+    a list of H radii.  Returns the status."""
+    lib = load()
+    rl = [int(x) for x in r] if _per_head(r) else [int(r)] * int(H)
+    rad = (ctypes.c_int32 * max(1, len(rl)))(*rl)
+    dil = None
+    if dilation is not None:
+        dil = (ctypes.c_int32 * len(dilation))(*[int(x) for x in dilation])
+    g = None
+    if global_idx is not None:
+        g = (ctypes.c_int32 * max(1, len(global_idx)))(*[int(x) for x in global_idx])
+    return lib.lf_attn_bwd(q_ptr, k_ptr, v_ptr, dy_ptr, int(B), int(H), int(T), int(d), rad, int(bool(one_sided)),
+                           dil, g, int(n_global), kpm_ptr, dq_ptr, dk_ptr, dv_ptr, int(dtype), stream_ptr)
+
+
+def attn_bwd(q, k, v, dy, r, dilation: Optional[Sequence[int]] = None,
+             global_idx: Optional[Sequence[int]] = None, key_padding_mask=None, out=None, stream=None,
+             one_sided: bool = False):
+    """Gradients (dq, dk, dv) of the forward for the upstream gradient ``dy``,
+    torch tensors [B, H, T, 64] like q; same window, dilation, global and
+    padding arguments as ``attn_fwd`` (no random key blocks).  ``out`` may be
+    a tuple of three tensors like q to write into."""
+    import torch
+
+    if q.dtype == torch.bfloat16:
+        dt = LF_BF16
+    elif q.dtype == torch.float32:
+        dt = LF_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k", k), ("v", v), ("dy", dy)):
+        if t.dtype != q.dtype or t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{name} must match q in dtype, shape and device")
+    if q.dim() != 4:
+        raise ValueError("q, k, v, dy must be [B, H, T, d]")
+    if not (q.is_cuda and all(t.is_contiguous() for t in (q, k, v, dy))):
+        raise ValueError("q, k, v, dy must be contiguous device tensors")
+    B, H, T, d = q.shape
+    if _per_head(r) and len(r) != H:
+        raise ValueError(f"r has {len(r)} radii for {H} heads")
+    gl = list(global_idx) if global_idx is not None else []
+    if out is None:
+        out = tuple(torch.empty_like(q) for _ in range(3))
+    elif len(out) != 3 or any(o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() for o in out):
+        raise ValueError("out must be three contiguous tensors like q")
+    kpm_ptr = None
+    if key_padding_mask is not None:
+        kpm = key_padding_mask
+        if kpm.dtype == torch.bool:
+            kpm = kpm.to(torch.uint8)
+        if kpm.dtype != torch.uint8 or tuple(kpm.shape) != (B, T) or not kpm.is_cuda:
+            raise ValueError("key_padding_mask must be a uint8/bool device tensor [B, T]")
+        kpm = kpm.contiguous()
+        kpm_ptr = kpm.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = raw_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr(), B, H, T, d, r, one_sided, dilation,
+                 gl if gl else None, len(gl), kpm_ptr, out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
+                 dt, sptr)
     if st != LF_OK:
         raise LfError(st, last_error())
     return out

@@ -1,0 +1,489 @@
+// lf_bwd_kernels.hip -- gradients of the Longformer sparse self-attention
+// forward (dq, dk, dv) for gfx950.
+//
+// The pages describe no backward pass (Longformer, ciallo.wiki, §5.2 only
+// states that training cost grows linearly with the length).  These kernels
+// compute the derivative of the forward map over the same allowed pairs:
+// with P_ij the softmax weights of row i, dP_ij = dy_i . v_j,
+// D_i = sum_j P_ij dP_ij and dS_ij = P_ij (dP_ij - D_i),
+//     dq_i = sum_j dS_ij k_j / sqrt(d),  dk_j = sum_i dS_ij q_i / sqrt(d),
+//     dv_j = sum_i P_ij dy_i .
+// The allowed sets are those of the forward: the sliding window of radius
+// r_h with stride delta_h (Longformer, eightmm.github.io, "Sliding-Window
+// Attention"; ciallo.wiki §2.2.3), one- or two-sided ("Implementation
+// Reading"), the global set G both ways ("Global Attention"), and padded
+// keys and queries left out.
+//
+// Four launches on the call's stream, each position written by exactly one:
+//   rows_kernel   lane = a non-global query of one residue class: one pass
+//                 for the row's log-sum-exp and D_i (online), one for dq_i;
+//                 writes (lse_i, D_i) for the column kernels.
+//   grows_kernel  one workgroup per (b, h, global row): the same over every
+//                 valid key, lanes over keys, reduced through LDS.
+//   cols_kernel   lane = a non-global key of one residue class: dk_j, dv_j
+//                 from the queries whose window holds j, plus the global rows.
+//   gcols_kernel  one workgroup per (b, h, global key): every valid query.
+// The per-key loops of the lane kernels read the key (or query) rows through
+// wave-uniform addresses, so those rows arrive by scalar loads and every lane
+// does its own dot products on the vector units; no atomics, so results are
+// reproducible.  This is the plain vector-unit path; it does not use MFMA.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lf_kernels.h"
+
+namespace lfb {
+
+constexpr int D = LF_HEAD_DIM;
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+// A row of D channels held as fp32 values.
+struct RowF {
+    float x[D];
+};
+
+template <typename ET>
+__device__ __forceinline__ void load_row(const ET* __restrict__ p, RowF& r) {
+    if constexpr (sizeof(ET) == 2) {
+        const uint4* p4 = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+        for (int e = 0; e < D / 8; e++) {
+            const uint4 w = p4[e];
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                r.x[8 * e + 2 * t] = __uint_as_float(u[t] << 16);
+                r.x[8 * e + 2 * t + 1] = __uint_as_float(u[t] & 0xffff0000u);
+            }
+        }
+    } else {
+        const float4* p4 = reinterpret_cast<const float4*>(p);
+#pragma unroll
+        for (int e = 0; e < D / 4; e++) {
+            const float4 w = p4[e];
+            r.x[4 * e] = w.x;
+            r.x[4 * e + 1] = w.y;
+            r.x[4 * e + 2] = w.z;
+            r.x[4 * e + 3] = w.w;
+        }
+    }
+}
+
+__device__ __forceinline__ void zero_row(RowF& r) {
+#pragma unroll
+    for (int c = 0; c < D; c++) r.x[c] = 0.f;
+}
+
+__device__ __forceinline__ float dot(const RowF& a, const RowF& b) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < D; c += 2) {
+        s0 = __builtin_fmaf(a.x[c], b.x[c], s0);
+        s1 = __builtin_fmaf(a.x[c + 1], b.x[c + 1], s1);
+    }
+    return s0 + s1;
+}
+
+__device__ __forceinline__ void axpy(RowF& acc, float a, const RowF& x) {
+#pragma unroll
+    for (int c = 0; c < D; c++) acc.x[c] = __builtin_fmaf(a, x.x[c], acc.x[c]);
+}
+
+template <typename ET>
+__device__ __forceinline__ void store_row(ET* __restrict__ p, const RowF& r, float scale) {
+    if constexpr (sizeof(ET) == 2) {
+        uint4* p4 = reinterpret_cast<uint4*>(p);
+#pragma unroll
+        for (int e = 0; e < D / 8; e++) {
+            uint32_t u[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const __bf16 lo = (__bf16)(r.x[8 * e + 2 * t] * scale);
+                const __bf16 hi = (__bf16)(r.x[8 * e + 2 * t + 1] * scale);
+                u[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            }
+            p4[e] = make_uint4(u[0], u[1], u[2], u[3]);
+        }
+    } else {
+        float4* p4 = reinterpret_cast<float4*>(p);
+#pragma unroll
+        for (int e = 0; e < D / 4; e++)
+            p4[e] = make_float4(r.x[4 * e] * scale, r.x[4 * e + 1] * scale, r.x[4 * e + 2] * scale,
+                                r.x[4 * e + 3] * scale);
+    }
+}
+
+__device__ __forceinline__ bool is_global(const uint32_t* __restrict__ gmap, int i) {
+    return (gmap[i >> 5] >> (i & 31)) & 1u;
+}
+
+__device__ __forceinline__ bool padded(const uint8_t* __restrict__ pad, int i) { return pad && pad[i] != 0; }
+
+// One wave's share of the lane kernels: batch b, head h, residue class c of
+// stride delta, and class positions [t0, t0 + 64) of the nc in the class.
+struct Chunk {
+    int b, h, c, t0, nc, delta, r, ra;
+};
+
+__device__ __forceinline__ bool decode(const lfk::BwdArgs& A, long long task, Chunk& k) {
+    const long long per_b = A.head_chunk[A.H];
+    if (task >= (long long)A.B * per_b) return false;
+    k.b = (int)(task / per_b);
+    int rem = (int)(task - (long long)k.b * per_b);
+    int h = 0;
+    while (h + 1 < A.H && A.head_chunk[h + 1] <= rem) h++;
+    rem -= A.head_chunk[h];
+    k.h = h;
+    const int delta = A.dil[h];
+    const int T = A.T;
+    const int q = T / delta, rm = T - q * delta;
+    const int ch1 = (q + 1 + 63) >> 6, ch0 = (q + 63) >> 6;   // chunks of a class with q+1 / q members
+    if (rem < rm * ch1) {
+        k.c = rem / ch1;
+        k.t0 = (rem - k.c * ch1) * 64;
+        k.nc = q + 1;
+    } else {
+        rem -= rm * ch1;
+        k.c = rm + rem / ch0;
+        k.t0 = (rem % ch0) * 64;
+        k.nc = q;
+    }
+    k.delta = delta;
+    k.r = A.rad[h];
+    k.ra = A.one_sided ? 0 : k.r;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// dq and the row statistics of the non-global queries.
+
+template <typename ET>
+__global__ __launch_bounds__(256) void rows_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
+                                                   const ET* __restrict__ K, const ET* __restrict__ V,
+                                                   const ET* __restrict__ DY, ET* __restrict__ DQ,
+                                                   float2* __restrict__ stats) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    Chunk ck;
+    if (!decode(A, (long long)blockIdx.x * 4 + wave, ck)) return;
+    const int T = A.T;
+    const size_t bh = (size_t)ck.b * A.H + ck.h;
+    const ET* Kh = K + bh * T * D;
+    const ET* Vh = V + bh * T * D;
+    const uint8_t* pad = A.pad ? A.pad + (size_t)ck.b * T : nullptr;
+    const int t = ck.t0 + lane;
+    const bool in = t < ck.nc;
+    const int i = ck.c + t * ck.delta;
+    const bool glob_i = in && A.n_g > 0 && is_global(A.gmap, i);
+    const bool live = in && !glob_i && !padded(pad, i);
+    RowF q, dy;
+    if (live) {
+        load_row(Q + (bh * T + i) * D, q);
+        load_row(DY + (bh * T + i) * D, dy);
+    } else {
+        zero_row(q);
+        zero_row(dy);
+    }
+    const float sc = LOG2E / 8.0f;   // 1/sqrt(64), base 2
+    const int k_lo = max(ck.t0 - ck.r, 0), k_hi = min(ck.t0 + 63 + ck.ra, ck.nc - 1);
+
+    // pass 1: running max, sum and sum of p * dP
+    float m = -INFINITY, l = 0.f, dn = 0.f;
+    auto visit1 = [&](int j, bool on) {
+        RowF kr, vr;
+        load_row(Kh + (size_t)j * D, kr);
+        load_row(Vh + (size_t)j * D, vr);
+        const float s = dot(q, kr) * sc;
+        const float dp = dot(dy, vr);
+        if (on) {
+            const float mn = fmaxf(m, s);
+            const float al = ex2(m - mn), e = ex2(s - mn);
+            l = l * al + e;
+            dn = dn * al + e * dp;
+            m = mn;
+        }
+    };
+    for (int tk = k_lo; tk <= k_hi; tk++) {
+        const int j = ck.c + tk * ck.delta;
+        if (padded(pad, j) || (A.n_g > 0 && is_global(A.gmap, j))) continue;
+        visit1(j, live && tk - t >= -ck.r && tk - t <= ck.ra);
+    }
+    for (int g = 0; g < A.n_g; g++) {
+        const int j = A.glob[g];
+        if (padded(pad, j)) continue;
+        visit1(j, live);
+    }
+    const float lse = live ? m + lg2(l) : 0.f;
+    const float Dl = live ? dn / l : 0.f;
+
+    // pass 2: dq
+    RowF acc;
+    zero_row(acc);
+    auto visit2 = [&](int j, bool on) {
+        RowF kr, vr;
+        load_row(Kh + (size_t)j * D, kr);
+        load_row(Vh + (size_t)j * D, vr);
+        const float s = dot(q, kr) * sc;
+        const float dp = dot(dy, vr);
+        const float p = on ? ex2(s - lse) : 0.f;
+        axpy(acc, p * (dp - Dl), kr);
+    };
+    for (int tk = k_lo; tk <= k_hi; tk++) {
+        const int j = ck.c + tk * ck.delta;
+        if (padded(pad, j) || (A.n_g > 0 && is_global(A.gmap, j))) continue;
+        visit2(j, live && tk - t >= -ck.r && tk - t <= ck.ra);
+    }
+    for (int g = 0; g < A.n_g; g++) {
+        const int j = A.glob[g];
+        if (padded(pad, j)) continue;
+        visit2(j, live);
+    }
+    if (in && !glob_i) {
+        store_row(DQ + (bh * T + i) * D, acc, 0.125f);
+        stats[bh * T + i] = make_float2(lse, Dl);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dk and dv of the non-global keys.
+
+template <typename ET>
+__global__ __launch_bounds__(256) void cols_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
+                                                   const ET* __restrict__ K, const ET* __restrict__ V,
+                                                   const ET* __restrict__ DY, ET* __restrict__ DK,
+                                                   ET* __restrict__ DV, const float2* __restrict__ stats) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    Chunk ck;
+    if (!decode(A, (long long)blockIdx.x * 4 + wave, ck)) return;
+    const int T = A.T;
+    const size_t bh = (size_t)ck.b * A.H + ck.h;
+    const ET* Qh = Q + bh * T * D;
+    const ET* Yh = DY + bh * T * D;
+    const float2* Sh = stats + bh * T;
+    const uint8_t* pad = A.pad ? A.pad + (size_t)ck.b * T : nullptr;
+    const int t = ck.t0 + lane;
+    const bool in = t < ck.nc;
+    const int j = ck.c + t * ck.delta;
+    const bool glob_j = in && A.n_g > 0 && is_global(A.gmap, j);
+    const bool live = in && !glob_j && !padded(pad, j);
+    RowF kr, vr;
+    if (live) {
+        load_row(K + (bh * T + j) * D, kr);
+        load_row(V + (bh * T + j) * D, vr);
+    } else {
+        zero_row(kr);
+        zero_row(vr);
+    }
+    const float sc = LOG2E / 8.0f;
+    RowF dk, dv;
+    zero_row(dk);
+    zero_row(dv);
+    auto visit = [&](int i, bool on) {
+        RowF q, dy;
+        load_row(Qh + (size_t)i * D, q);
+        load_row(Yh + (size_t)i * D, dy);
+        const float2 st = Sh[i];
+        const float s = dot(q, kr) * sc;
+        const float dp = dot(dy, vr);
+        const float p = on ? ex2(s - st.x) : 0.f;
+        axpy(dv, p, dy);
+        axpy(dk, p * (dp - st.y), q);
+    };
+    // query i (class position tq) holds key position t' in its window iff
+    // tq - t' lies in [-ra, r]
+    const int q_lo = max(ck.t0 - ck.ra, 0), q_hi = min(ck.t0 + 63 + ck.r, ck.nc - 1);
+    for (int tq = q_lo; tq <= q_hi; tq++) {
+        const int i = ck.c + tq * ck.delta;
+        if (padded(pad, i) || (A.n_g > 0 && is_global(A.gmap, i))) continue;
+        visit(i, live && tq - t >= -ck.ra && tq - t <= ck.r);
+    }
+    for (int g = 0; g < A.n_g; g++) {
+        const int i = A.glob[g];
+        if (padded(pad, i)) continue;
+        visit(i, live);
+    }
+    if (in && !glob_j) {
+        store_row(DK + (bh * T + j) * D, dk, 0.125f);
+        store_row(DV + (bh * T + j) * D, dv, 1.0f);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Global rows and global keys: one workgroup each, lanes over the other side.
+
+// Sum x[tid][c] over the 256 threads into the first 64 (c = tid); red holds
+// 256 x 65 floats.
+__device__ __forceinline__ float block_sum_row(float* red, const RowF& x) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < D; c++) red[tid * 65 + c] = x.x[c];
+    __syncthreads();
+    float s = 0.f;
+    if (tid < D)
+        for (int e = 0; e < 256; e++) s += red[e * 65 + tid];
+    __syncthreads();
+    return s;
+}
+
+template <typename ET>
+__global__ __launch_bounds__(256) void grows_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
+                                                    const ET* __restrict__ K, const ET* __restrict__ V,
+                                                    const ET* __restrict__ DY, ET* __restrict__ DQ,
+                                                    float2* __restrict__ stats) {
+    __shared__ float red[256 * 65];
+    __shared__ float red_m[256], red_l[256], red_d[256];
+    const int tid = threadIdx.x;
+    const int gi = blockIdx.x % A.n_g;
+    const size_t bh = blockIdx.x / A.n_g;
+    const int b = (int)(bh / A.H);
+    const int T = A.T;
+    const int g = A.glob[gi];
+    const uint8_t* pad = A.pad ? A.pad + (size_t)b * T : nullptr;
+    ET* dq = DQ + (bh * T + g) * D;
+    if (padded(pad, g)) {
+        if (tid < D) dq[tid] = (ET)0.f;
+        return;
+    }
+    const ET* Kh = K + bh * T * D;
+    const ET* Vh = V + bh * T * D;
+    RowF q, dy;
+    load_row(Q + (bh * T + g) * D, q);
+    load_row(DY + (bh * T + g) * D, dy);
+    const float sc = LOG2E / 8.0f;
+    float m = -INFINITY, l = 0.f, dn = 0.f;
+    for (int j = tid; j < T; j += 256) {
+        if (padded(pad, j)) continue;
+        RowF kr, vr;
+        load_row(Kh + (size_t)j * D, kr);
+        load_row(Vh + (size_t)j * D, vr);
+        const float s = dot(q, kr) * sc;
+        const float dp = dot(dy, vr);
+        const float mn = fmaxf(m, s);
+        const float al = ex2(m - mn), e = ex2(s - mn);
+        l = l * al + e;
+        dn = dn * al + e * dp;
+        m = mn;
+    }
+    red_m[tid] = m;
+    red_l[tid] = l;
+    red_d[tid] = dn;
+    __syncthreads();
+    float M = -INFINITY;
+    for (int e = 0; e < 256; e++) M = fmaxf(M, red_m[e]);
+    float L = 0.f, DN = 0.f;
+    for (int e = 0; e < 256; e++) {
+        if (red_l[e] == 0.f) continue;   // a thread that met no valid key
+        const float w = ex2(red_m[e] - M);
+        L += red_l[e] * w;
+        DN += red_d[e] * w;
+    }
+    __syncthreads();
+    const float lse = M + lg2(L), Dl = DN / L;   // key g itself is valid, so L >= 1
+    RowF acc;
+    zero_row(acc);
+    for (int j = tid; j < T; j += 256) {
+        if (padded(pad, j)) continue;
+        RowF kr, vr;
+        load_row(Kh + (size_t)j * D, kr);
+        load_row(Vh + (size_t)j * D, vr);
+        const float s = dot(q, kr) * sc;
+        const float dp = dot(dy, vr);
+        const float p = ex2(s - lse);
+        axpy(acc, p * (dp - Dl), kr);
+    }
+    const float sum = block_sum_row(red, acc);
+    if (tid < D) {
+        if constexpr (sizeof(ET) == 2) dq[tid] = (ET)(sum * 0.125f);
+        else dq[tid] = sum * 0.125f;
+    }
+    if (tid == 0) stats[bh * T + g] = make_float2(lse, Dl);
+}
+
+template <typename ET>
+__global__ __launch_bounds__(256) void gcols_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
+                                                    const ET* __restrict__ K, const ET* __restrict__ V,
+                                                    const ET* __restrict__ DY, ET* __restrict__ DK,
+                                                    ET* __restrict__ DV, const float2* __restrict__ stats) {
+    __shared__ float red[256 * 65];
+    const int tid = threadIdx.x;
+    const int gi = blockIdx.x % A.n_g;
+    const size_t bh = blockIdx.x / A.n_g;
+    const int b = (int)(bh / A.H);
+    const int T = A.T;
+    const int g = A.glob[gi];
+    const uint8_t* pad = A.pad ? A.pad + (size_t)b * T : nullptr;
+    ET* dk = DK + (bh * T + g) * D;
+    ET* dv = DV + (bh * T + g) * D;
+    if (padded(pad, g)) {
+        if (tid < D) {
+            dk[tid] = (ET)0.f;
+            dv[tid] = (ET)0.f;
+        }
+        return;
+    }
+    const ET* Qh = Q + bh * T * D;
+    const ET* Yh = DY + bh * T * D;
+    RowF kr, vr;
+    load_row(K + (bh * T + g) * D, kr);
+    load_row(V + (bh * T + g) * D, vr);
+    const float sc = LOG2E / 8.0f;
+    RowF ak, av;
+    zero_row(ak);
+    zero_row(av);
+    // every valid query attends to a global key
+    for (int i = tid; i < T; i += 256) {
+        if (padded(pad, i)) continue;
+        RowF q, dy;
+        load_row(Qh + (size_t)i * D, q);
+        load_row(Yh + (size_t)i * D, dy);
+        const float2 st = stats[bh * T + i];
+        const float s = dot(q, kr) * sc;
+        const float dp = dot(dy, vr);
+        const float p = ex2(s - st.x);
+        axpy(av, p, dy);
+        axpy(ak, p * (dp - st.y), q);
+    }
+    const float sk = block_sum_row(red, ak);
+    const float sv = block_sum_row(red, av);
+    if (tid < D) {
+        if constexpr (sizeof(ET) == 2) {
+            dk[tid] = (ET)(sk * 0.125f);
+            dv[tid] = (ET)sv;
+        } else {
+            dk[tid] = sk * 0.125f;
+            dv[tid] = sv;
+        }
+    }
+}
+
+template <typename ET>
+hipError_t launch(const lfk::BwdArgs* A, const void* const* t, hipStream_t s) {
+    const ET* q = (const ET*)t[0];
+    const ET* k = (const ET*)t[1];
+    const ET* v = (const ET*)t[2];
+    const ET* dy = (const ET*)t[3];
+    ET* dq = (ET*)t[4];
+    ET* dk = (ET*)t[5];
+    ET* dv = (ET*)t[6];
+    float2* st = (float2*)A->stats;
+    const long long waves = (long long)A->B * A->head_chunk[A->H];
+    const dim3 gl((unsigned)((waves + 3) / 4)), blk(256);
+    const dim3 gg((unsigned)((long long)A->B * A->H * A->n_g));
+    hipLaunchKernelGGL(rows_kernel<ET>, gl, blk, 0, s, *A, q, k, v, dy, dq, st);
+    if (A->n_g > 0) hipLaunchKernelGGL(grows_kernel<ET>, gg, blk, 0, s, *A, q, k, v, dy, dq, st);
+    hipLaunchKernelGGL(cols_kernel<ET>, gl, blk, 0, s, *A, q, k, v, dy, dk, dv, st);
+    if (A->n_g > 0) hipLaunchKernelGGL(gcols_kernel<ET>, gg, blk, 0, s, *A, q, k, v, dy, dk, dv, st);
+    return hipGetLastError();
+}
+
+}  // namespace lfb
+
+// t = {q, k, v, dy, dq, dk, dv}
+extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs* A, const void* const* t, int dtype_bf16, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    return dtype_bf16 ? lfb::launch<__bf16>(A, t, s) : lfb::launch<float>(A, t, s);
+}

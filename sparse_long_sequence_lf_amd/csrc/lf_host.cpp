@@ -20,6 +20,7 @@
 #include "lf_kernels.h"
 
 extern "C" hipError_t lfk_launch(const lfk::Args *A, const lfk::Plan *P, int dtype_bf16, void *stream);
+extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs *A, const void *const *t, int dtype_bf16, void *stream);
 
 namespace {
 
@@ -64,6 +65,8 @@ struct Workspace {
     lfk::Plan shadow;
     bool shadow_valid = false;
     std::vector<uint32_t> aux_shadow;   // what aux holds: random-block table and global bitmap
+    Buffer bwd_tab, bwd_stats;          // backward: per-head tables and globals; row statistics
+    std::vector<uint32_t> bwd_shadow;   // what bwd_tab holds
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, void *>, Workspace> g_ws;
@@ -103,6 +106,18 @@ Workspace *workspace_for(void *stream) {
     return &g_ws[std::make_pair(dev, stream)];
 }
 
+// Host-to-device copy of a table the next kernels on `stream` read, finished
+// before returning: the copy is enqueued on the stream, then the stream is
+// drained.  A small copy from pageable memory was seen to land after the
+// following kernels had read the old table, so an upload does not rely on
+// the copy's own ordering.  Uploads happen only when a table changes (never
+// in steady state, and never during capture, which the callers refuse).
+hipError_t upload(void *dst, const void *src, size_t bytes, void *stream) {
+    hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) return e;
+    return hipStreamSynchronize((hipStream_t)stream);
+}
+
 // Device copy of *P on this stream's workspace; uploads only when it differs
 // from the last upload.  An upload cannot be recorded into a graph (its source
 // is a host temporary), so a changed plan during stream capture is refused.
@@ -117,7 +132,7 @@ lf_status_t upload_plan(Workspace &w, const lfk::Plan &P, void *stream, const lf
             return fail(LF_E_UNSUPPORTED,
                         "the call's shape, dilation or global set differs from the previous call on this stream "
                         "during stream capture; make one identical call outside capture first");
-        e = hipMemcpyAsync(w.plan.ptr, &P, sizeof P, hipMemcpyHostToDevice, (hipStream_t)stream);
+        e = upload(w.plan.ptr, &P, sizeof P, stream);
         if (e != hipSuccess) {
             w.shadow_valid = false;
             return fail(LF_E_HIP, "plan upload: %s", hipGetErrorString(e));
@@ -311,8 +326,7 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
                 return fail(LF_E_UNSUPPORTED,
                             "the random key blocks differ from the previous call on this stream during stream "
                             "capture; make one identical call outside capture first");
-            e = hipMemcpyAsync(w->aux.ptr, aux.data(), aux.size() * sizeof(uint32_t), hipMemcpyHostToDevice,
-                               (hipStream_t)stream);
+            e = upload(w->aux.ptr, aux.data(), aux.size() * sizeof(uint32_t), stream);
             if (e != hipSuccess) {
                 w->aux_shadow.clear();
                 return fail(LF_E_HIP, "random-block upload: %s", hipGetErrorString(e));
@@ -332,7 +346,123 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
     return LF_OK;
 }
 
+// Gradients (lf_attn_bwd): checks, the per-head tables, four launches.
+lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy, int B, int H, int T, int d,
+                     const int32_t *radius, int one_sided, const int32_t *dilation, const int32_t *global_idx,
+                     int n_global, const uint8_t *key_padding_mask, void *dq, void *dk, void *dv,
+                     lf_dtype_t dtype, void *stream) {
+    if (!q || !k || !v || !dy || !dq || !dk || !dv)
+        return fail(LF_E_INVALID, "q, k, v, dy, dq, dk and dv must be non-null");
+    if (!radius) return fail(LF_E_INVALID, "radius must be a host array of H radii");
+    if (dtype != LF_F32 && dtype != LF_BF16) return fail(LF_E_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (B < 1 || H < 1 || T < 1) return fail(LF_E_INVALID, "B, H, T must be >= 1 (got %d, %d, %d)", B, H, T);
+    if (d != LF_HEAD_DIM) return fail(LF_E_UNSUPPORTED, "head dimension %d: only %d is built", d, LF_HEAD_DIM);
+    if (H > LF_MAX_HEADS) return fail(LF_E_UNSUPPORTED, "H = %d exceeds %d", H, LF_MAX_HEADS);
+    if (T > LF_MAX_SEQ) return fail(LF_E_UNSUPPORTED, "T = %d exceeds %d", T, LF_MAX_SEQ);
+    if (one_sided != 0 && one_sided != 1) return fail(LF_E_INVALID, "one_sided = %d must be 0 or 1", one_sided);
+    for (int h = 0; h < H; h++)
+        if (radius[h] < 0) return fail(LF_E_INVALID, "radius[%d] = %d must be >= 0", h, radius[h]);
+    if (n_global < 0) return fail(LF_E_INVALID, "n_global = %d must be >= 0", n_global);
+    if (n_global > 0 && !global_idx) return fail(LF_E_INVALID, "global_idx is NULL with n_global = %d", n_global);
+    if (dilation)
+        for (int h = 0; h < H; h++) {
+            if (dilation[h] < 1) return fail(LF_E_INVALID, "dilation[%d] = %d must be >= 1", h, dilation[h]);
+            if (dilation[h] > LF_MAX_DILATION)
+                return fail(LF_E_UNSUPPORTED, "dilation[%d] = %d exceeds %d", h, dilation[h], LF_MAX_DILATION);
+        }
+    for (int i = 0; i < n_global; i++)
+        if (global_idx[i] < 0 || global_idx[i] >= T)
+            return fail(LF_E_INVALID, "global_idx[%d] = %d outside [0, %d)", i, global_idx[i], T);
+    const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)dy | (uintptr_t)dq |
+                           (uintptr_t)dk | (uintptr_t)dv) & 15u;
+    if (mis) return fail(LF_E_INVALID, "q, k, v, dy, dq, dk and dv must be 16-byte aligned");
+    if ((size_t)B * (size_t)H > (size_t)1 << 24)
+        return fail(LF_E_UNSUPPORTED, "B*H = %lld too large", (long long)B * H);
+    const size_t esize = dtype == LF_BF16 ? 2 : 4;
+    const size_t nbytes = (size_t)B * (size_t)H * (size_t)T * (size_t)d * esize;
+    const void *ins[4] = {q, k, v, dy};
+    void *outs[3] = {dq, dk, dv};
+    for (int o = 0; o < 3; o++) {
+        for (int e = 0; e < 4; e++)
+            if (overlaps(outs[o], nbytes, ins[e], nbytes)) return fail(LF_E_INVALID, "dq, dk, dv overlap an input");
+        for (int e = o + 1; e < 3; e++)
+            if (overlaps(outs[o], nbytes, outs[e], nbytes)) return fail(LF_E_INVALID, "dq, dk, dv overlap");
+    }
+    std::vector<int32_t> G(global_idx, global_idx + n_global);
+    std::sort(G.begin(), G.end());
+    G.erase(std::unique(G.begin(), G.end()), G.end());
+    if ((int)G.size() > LF_MAX_GLOBALS)
+        return fail(LF_E_UNSUPPORTED, "%zu distinct globals exceed %d", G.size(), LF_MAX_GLOBALS);
+    if ((long long)B * H * G.size() >= (1LL << 31))
+        return fail(LF_E_UNSUPPORTED, "too many global rows");
+
+    // table: rad[H] | dil[H] | head_chunk[H+1] | glob[n_g] | gmap[ceil(T/32)]
+    const size_t o_dil = H, o_hc = 2 * (size_t)H, o_glob = o_hc + H + 1, o_gmap = o_glob + G.size();
+    std::vector<uint32_t> tab(o_gmap + (size_t)cdiv(T, 32), 0u);
+    long long chunks = 0;
+    for (int h = 0; h < H; h++) {
+        const int delta = dilation ? dilation[h] : 1;
+        tab[h] = (uint32_t)std::min(radius[h], T);   // |i - j| < T: larger radii change nothing
+        tab[o_dil + h] = (uint32_t)delta;
+        tab[o_hc + h] = (uint32_t)chunks;
+        const long long qq = T / delta, rm = T % delta;
+        chunks += rm * cdiv(qq + 1, 64) + (delta - rm) * cdiv(qq, 64);
+    }
+    tab[o_hc + H] = (uint32_t)chunks;
+    if ((long long)B * chunks >= (1LL << 31)) return fail(LF_E_UNSUPPORTED, "problem needs too many waves");
+    for (size_t e = 0; e < G.size(); e++) {
+        tab[o_glob + e] = (uint32_t)G[e];
+        tab[o_gmap + (G[e] >> 5)] |= 1u << (G[e] & 31);
+    }
+
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    Workspace *w = workspace_for(stream);
+    if (!w) return fail(LF_E_HIP, "hipGetDevice failed");
+    lf_status_t st = grow(w->bwd_tab, tab.size() * sizeof(uint32_t), false, stream);
+    if (st != LF_OK) return st;
+    st = grow(w->bwd_stats, (size_t)B * H * T * 2 * sizeof(float), false, stream);
+    if (st != LF_OK) return st;
+    if (w->bwd_shadow != tab) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
+        if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+        if (cs != hipStreamCaptureStatusNone)
+            return fail(LF_E_UNSUPPORTED,
+                        "the call's shape, radii, dilation or global set differs from the previous backward call "
+                        "on this stream during stream capture; make one identical call outside capture first");
+        e = upload(w->bwd_tab.ptr, tab.data(), tab.size() * sizeof(uint32_t), stream);
+        if (e != hipSuccess) {
+            w->bwd_shadow.clear();
+            return fail(LF_E_HIP, "backward table upload: %s", hipGetErrorString(e));
+        }
+        w->bwd_shadow = tab;
+    }
+    const uint32_t *dt = (const uint32_t *)w->bwd_tab.ptr;
+    lfk::BwdArgs A;
+    A.pad = key_padding_mask;
+    A.gmap = dt + o_gmap;
+    A.glob = (const int32_t *)dt + o_glob;
+    A.rad = (const int32_t *)dt;
+    A.dil = (const int32_t *)dt + o_dil;
+    A.head_chunk = (const int32_t *)dt + o_hc;
+    A.stats = w->bwd_stats.ptr;
+    A.B = B; A.H = H; A.T = T; A.n_g = (int)G.size(); A.one_sided = one_sided;
+    const void *t[7] = {q, k, v, dy, dq, dk, dv};
+    hipError_t e = lfk_bwd_launch(&A, t, dtype == LF_BF16, stream);
+    if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return LF_OK;
+}
+
 }  // namespace
+
+extern "C" lf_status_t lf_attn_bwd(const void *q, const void *k, const void *v, const void *dy, int B, int H,
+                                   int T, int d, const int32_t *radius, int one_sided, const int32_t *dilation,
+                                   const int32_t *global_idx, int n_global, const uint8_t *key_padding_mask,
+                                   void *dq, void *dk, void *dv, lf_dtype_t dtype, void *stream) {
+    g_err.clear();
+    return attn_bwd(q, k, v, dy, B, H, T, d, radius, one_sided, dilation, global_idx, n_global, key_padding_mask,
+                    dq, dk, dv, dtype, stream);
+}
 
 extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T,
                                    int d, int r, const int32_t *dilation, const int32_t *global_idx,

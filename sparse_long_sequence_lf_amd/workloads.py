@@ -217,3 +217,10 @@ def random_case(seed: int, B: int, H: int, T: int, d: int = 64, dtype: str = "f3
         nqb = (T + 63) // 64
         rb = rng.integers(0, nqb, size=(H, nqb, n_rand)).astype(np.int32)
     return Inputs(q, k, v, r, dil, glob, lengths, kpm, random_blocks=rb)
+
+
+def make_grad(inp: Inputs, seed: int) -> torch.Tensor:
+    """An upstream gradient dy like q: float32 ``randn`` from a generator
+    seeded with ``seed``, cast (round to nearest even) to q's dtype."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    return torch.randn(tuple(inp.q.shape), generator=g, dtype=torch.float32).to(inp.q.dtype)

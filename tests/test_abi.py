@@ -185,3 +185,38 @@ def test_random_blocks_null_table_rejected(lib):
     st = lib.lf_attn_fwd_ex(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], rad, 0, None, 2, None, None,
                             0, None, a["out"], a["dtype"], None)
     assert st == lf.LF_E_INVALID and "rand_blocks" in lf.last_error()
+
+
+DY, DQ, DK, DV = 0x50000000, 0x60000000, 0x70000000, 0x80000000
+
+
+@pytest.mark.parametrize("name,kw,status", [
+    ("null dy", dict(dy=None), lf.LF_E_INVALID),
+    ("null dq", dict(dq=None), lf.LF_E_INVALID),
+    ("bad dtype", dict(dtype=7), lf.LF_E_UNSUPPORTED),
+    ("d = 128", dict(d=128), lf.LF_E_UNSUPPORTED),
+    ("T = 0", dict(T=0), lf.LF_E_INVALID),
+    ("negative radius", dict(r=[8, -1]), lf.LF_E_INVALID),
+    ("one_sided = 2", dict(one=2), lf.LF_E_INVALID),
+    ("dilation 0", dict(dil=[1, 0]), lf.LF_E_INVALID),
+    ("global out of range", dict(g=[128], ng=1), lf.LF_E_INVALID),
+    ("misaligned dk", dict(dk=DK + 2), lf.LF_E_INVALID),
+    ("dq overlaps q", dict(dq=Q + 64), lf.LF_E_INVALID),
+    ("dk overlaps dv", dict(dk=DV + 16), lf.LF_E_INVALID),
+])
+def test_bwd_rejects_bad_arguments(lib, name, kw, status):
+    a = dict(q=Q, k=K, v=V, dy=DY, B=1, H=2, T=128, d=64, r=[8, 8], one=0, dil=[1, 2], g=[0], ng=1, kpm=None,
+             dq=DQ, dk=DK, dv=DV, dtype=lf.LF_BF16)
+    a.update(kw)
+    rad = (ctypes.c_int32 * 2)(*a["r"])
+    dil = (ctypes.c_int32 * 2)(*a["dil"])
+    g = (ctypes.c_int32 * 1)(*a["g"])
+    st = lib.lf_attn_bwd(a["q"], a["k"], a["v"], a["dy"], a["B"], a["H"], a["T"], a["d"], rad, a["one"], dil, g,
+                         a["ng"], a["kpm"], a["dq"], a["dk"], a["dv"], a["dtype"], None)
+    assert st == status, (name, st, lf.last_error())
+    assert lf.last_error() != ""
+
+
+def test_bwd_null_radius_rejected(lib):
+    st = lib.lf_attn_bwd(Q, K, V, DY, 1, 2, 128, 64, None, 0, None, None, 0, None, DQ, DK, DV, lf.LF_BF16, None)
+    assert st == lf.LF_E_INVALID and "radius" in lf.last_error()

@@ -1,0 +1,116 @@
+"""GPU parity of the gradients (lf_attn_bwd, through the C ABI) against the
+fp64 oracle's derivative of the forward on identical seeded inputs.
+
+Bar, per tensor dq, dk, dv: max |gpu - oracle| <= tol * max(1, max |oracle|)
+with tol 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (fp32 arithmetic;
+bf16 results rounded once).  Padded positions must be exactly zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_long_sequence_lf_amd as lf
+from sparse_long_sequence_lf_amd import workloads as W
+from parity_utils import TOL, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def gpu_bwd(inp, dy):
+    dev = torch.device("cuda:0")
+    kpm = None if inp.key_padding_mask is None else inp.key_padding_mask.to(dev)
+    out = lf.attn_bwd(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), dy.to(dev), inp.r, inp.dilation,
+                      inp.global_idx, key_padding_mask=kpm, one_sided=inp.one_sided)
+    torch.cuda.synchronize()
+    return [o.float().cpu().double().numpy() for o in out]
+
+
+def check(inp, dy, dt, label):
+    got = gpu_bwd(inp, dy)
+    ref = oracle.bwd(inp.q, inp.k, inp.v, dy, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
+                     one_sided=inp.one_sided)
+    bad = []
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        scale = max(1.0, float(np.max(np.abs(b)))) if b.size else 1.0
+        err = float(np.max(np.abs(a - b))) if b.size else 0.0
+        where = np.unravel_index(int(np.argmax(np.abs(a - b))), b.shape)[:3] if b.size else ()
+        print(f"  {label} {name}: max abs err {err:.3e} (scale {scale:.2f}) at (b, h, i) = {where}", flush=True)
+        if err > TOL[dt] * scale:
+            bad.append((name, err, scale, where))
+    assert not bad, (label, bad)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        if inp.key_padding_mask is not None:
+            pad = inp.key_padding_mask.bool().numpy()
+            for bb in range(a.shape[0]):
+                assert not np.any(a[bb][:, pad[bb]]), (label, name, "padded rows not zero")
+
+
+@pytest.mark.parametrize("T", [1, 2, 33, 64, 65, 130, 257, 300])
+def test_bwd_random_cases(T):
+    for dt in ("f32", "bf16"):
+        for seed, pad in enumerate(("none", "right", "random")):
+            base = W.random_case(seed * 7919 + T, B=2, H=3, T=T, dtype=dt, pad=pad)
+            rng = np.random.default_rng(seed * 31 + T)
+            one = bool(seed % 2)
+            r = [int(x) for x in rng.integers(0, T + 3, size=3)] if seed == 2 else base.r
+            inp = W.Inputs(base.q, base.k, base.v, r, base.dilation, base.global_idx, base.lengths,
+                           base.key_padding_mask, one_sided=one)
+            dy = W.make_grad(inp, 100 + seed + T)
+            label = f"T={T} dt={dt} pad={pad} r={r} dil={inp.dilation} one_sided={one} G={inp.global_idx}"
+            print("case " + label, flush=True)
+            check(inp, dy, dt, label)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_bwd_named_edge_cases(dt):
+    base = W.random_case(5, B=2, H=2, T=200, dtype=dt, pad="none")
+    kpm = torch.zeros(2, 200, dtype=torch.uint8)
+    kpm[0, 150:] = 1
+    kpm[1, :] = 1                                                # a fully padded sequence
+    for r, G, dil, pad in [(0, [], [1, 1], None), (300, [], [1, 1], None), (5, list(range(200)), [1, 3], None),
+                           (7, [10, 12, 100], [1, 1], None), (3, [0, 199], [4, 5], None),
+                           (40, [50, 50, 50, 51], [3, 1], None), (9, [20, 160], [1, 2], kpm)]:
+        inp = W.Inputs(base.q, base.k, base.v, r, dil, G, None, pad)
+        dy = W.make_grad(inp, r + len(G))
+        label = f"dt={dt} r={r} G={G[:6]} dil={dil} pad={'yes' if pad is not None else 'no'}"
+        print("case " + label, flush=True)
+        check(inp, dy, dt, label)
+
+
+# workload shapes with the head count cut where the oracle would take long
+BWD_CASES = {
+    "fp32-b1h2t1024-r64-g1": dict(),
+    "bf16-b1h12t4096-r256-g1": dict(),
+    "bf16-b1h12t4096-r128-dil": dict(T=2048),
+    "bf16-b2h12t4096-r256-g68": dict(T=1024, H=4),
+    "bf16-b4h16t16384-r512-g8-pad": dict(T=2100, H=2),
+    "bf16-b1h12t4096-r256-g1-onesided": dict(T=2048),
+    "bf16-b1h12t4096-rhead-g1": dict(T=2048),
+}
+
+
+@pytest.mark.parametrize("dtype", ["native", "f32"])
+@pytest.mark.parametrize("name", list(BWD_CASES))
+def test_bwd_workloads(name, dtype):
+    w = W.workload(name)
+    dt = w.dtype if dtype == "native" else "f32"
+    inp = W.make_inputs(w, dtype=dt, **BWD_CASES[name])
+    dy = W.make_grad(inp, w.seed + 17)
+    label = f"{name} dtype={dt} shape={tuple(inp.q.shape)}"
+    print("case " + label, flush=True)
+    check(inp, dy, dt, label)
+
+
+def test_bwd_repeatable():
+    inp = W.make_inputs(W.workload("bf16-b2h12t4096-r256-g68"), T=1024, H=4)
+    dy = W.make_grad(inp, 3)
+    a = gpu_bwd(inp, dy)
+    b = gpu_bwd(inp, dy)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)

@@ -323,3 +323,16 @@ def test_workspace_reuse_across_dtypes_and_shapes():
         dt = "f32" if inp.q.dtype == torch.float32 else "bf16"
         print(f"  {tuple(inp.q.shape)} {dt} n_g={len(set(inp.global_idx))}: max abs err {err:.3e}", flush=True)
         assert err <= TOL[dt]
+
+
+def test_random_table_change_same_shape():
+    # consecutive calls of one shape and plan whose random-block tables differ:
+    # each call must see its own table
+    base = W.random_case(77, B=1, H=2, T=200, dtype="f32", pad="none", n_rand=2)
+    for s in range(3):
+        rb = np.random.default_rng(s).integers(0, 4, size=base.random_blocks.shape).astype(np.int32)
+        inp = W.Inputs(base.q, base.k, base.v, base.r, base.dilation, base.global_idx, base.lengths,
+                       base.key_padding_mask, random_blocks=rb)
+        print(f"case random table {s}", flush=True)
+        err = max_err(gpu_fwd(inp), oracle_full(inp))
+        assert err <= TOL["f32"], (s, err)
