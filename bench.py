@@ -142,6 +142,80 @@ def global_rows_probe(lf, W, steps):
                       "global_row_GBps_lower_bound": round(kv_bytes / (dt * 1e-6) / 1e9, 1)}), flush=True)
 
 
+# fp32 vector FMA rate without packed fp32 instructions (the library is built
+# with them off): 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz
+PEAK_VALU_F32_TFLOPS = 78.6
+
+
+def bench_backward(args, lf, W, metrics):
+    """lf_attn_bwd on the workload: W warmup calls, SETTLE_MS of untimed
+    calls, then K back-to-back calls timed with events on the call stream.
+    Useful FLOPs: 10 d per allowed pair (s = q.k, dP = dy.v, dv, dq, dk)."""
+    import torch
+    w = W.workload(args.workload)
+    inp = W.make_inputs(w)
+    if inp.random_blocks is not None:
+        print("bench.py: the backward pass takes no random key blocks", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    dy = W.make_grad(inp, w.seed + 17).to(dev)
+    kpm = None if inp.key_padding_mask is None else inp.key_padding_mask.to(dev)
+    B, H, T, d = q.shape
+    stream = torch.cuda.current_stream(dev)
+    outs = tuple(torch.empty_like(q) for _ in range(3))
+
+    def call():
+        lf.attn_bwd(q, k, v, dy, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm, out=outs,
+                    stream=stream, one_sided=inp.one_sided)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    n_untimed = args.warmup
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < SETTLE_MS:
+        call()
+        torch.cuda.synchronize()
+        n_untimed += 1
+    if args.profile_mode:
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        print(f"profile mode: {n_untimed} untimed backward calls then {args.steps} of {w.name}", flush=True)
+        return
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    pairs = metrics.useful_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
+                                 one_sided=inp.one_sided)
+    flops = 10 * d * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "useful TFLOP/s of the backward pass (dq, dk, dv), 10 d FLOP per allowed pair",
+        "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 arithmetic on " + ("bf16" if w.dtype == "bf16" else "f32") + " inputs",
+        "data": "synthetic (seeded N(0,1) q/k/v/dy; no dataset, no weights)",
+        "config": {"workload": w.name, "pass": "backward", "B": B, "H": H, "T": T, "d": d, "r": inp.r,
+                   "one_sided": inp.one_sided, "dilation": inp.dilation, "n_global": len(set(inp.global_idx)),
+                   "padded": inp.key_padding_mask is not None, "useful_pairs": pairs,
+                   "timing": f"eager back-to-back calls after {n_untimed} untimed calls"},
+        "roofline": {"bound": "alu", "kernel": "lfb rows + grows + cols + gcols (whole call)",
+                     "achieved": round(tf, 3), "peak": PEAK_VALU_F32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_VALU_F32_TFLOPS, 4), "traffic": None,
+                     "peak_note": "fp32 vector FMA without packed instructions; the published 157.3 "
+                                  "counts packed fp32",
+                     "algorithmic_flops": flops},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +227,8 @@ def main():
     ap.add_argument("--profile-mode", action="store_true")
     ap.add_argument("--global-rows-probe", action="store_true",
                     help="print the global-row HBM rate probe's line instead of the benchmark line")
+    ap.add_argument("--backward", action="store_true",
+                    help="time lf_attn_bwd (dq, dk, dv) on the workload instead of the forward")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -170,6 +246,11 @@ def main():
     if args.global_rows_probe:
         torch.cuda.set_device(0)
         global_rows_probe(lf, W, min(args.steps, 50))
+        return
+
+    if args.backward:
+        torch.cuda.set_device(0)
+        bench_backward(args, lf, W, metrics)
         return
 
     w = W.workload(args.workload)

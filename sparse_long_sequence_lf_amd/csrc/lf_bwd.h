@@ -1,0 +1,33 @@
+// lf_bwd.h -- the launch record shared by the host code of lf_attn_bwd
+// (lf_host.cpp) and the backward kernels (lf_bwd_kernels.hip).  Internal to
+// liblfattn.so; the public interface is include/lf_attn.h.
+#ifndef LF_BWD_H
+#define LF_BWD_H
+
+#include <stdint.h>
+
+#include "lf_attn.h"
+
+// Rows (queries or keys) of one residue class per wave in the backward's band
+// kernels; head_chunk counts chunks of this many class positions.
+#define LFB_ROWS_PER_WAVE 16
+
+// The backward launches' argument (lf_bwd_kernels.hip).  The tables live in
+// one device buffer of the workspace: radius, stride and wave-chunk prefix
+// per head, the sorted global positions and their bitmap.
+namespace lfk {
+
+struct BwdArgs {
+    const uint8_t *pad;          // [B][T] or null
+    const uint32_t *gmap;        // bit i set iff position i is global ([ceil(T/32)] words)
+    const int32_t *glob;         // [n_g] distinct globals, ascending
+    const int32_t *rad;          // [H] window radius per head (clamped to T)
+    const int32_t *dil;          // [H] stride per head
+    const int32_t *head_chunk;   // [H+1] prefix over heads of the class chunks (LFB_ROWS_PER_WAVE positions)
+    void *stats;                 // float2 [B*H][T]: (log2-sum-exp of the scaled scores, D_i)
+    int B, H, T, n_g, one_sided;
+};
+
+}  // namespace lfk
+
+#endif

@@ -23,14 +23,14 @@
 //   cols_kernel   lane = a non-global key of one residue class: dk_j, dv_j
 //                 from the queries whose window holds j, plus the global rows.
 //   gcols_kernel  one workgroup per (b, h, global key): every valid query.
-// The per-key loops of the lane kernels read the key (or query) rows through
-// wave-uniform addresses, so those rows arrive by scalar loads and every lane
-// does its own dot products on the vector units; no atomics, so results are
-// reproducible.  This is the plain vector-unit path; it does not use MFMA.
+// In the band kernels four lanes share a row (16 channels each) and a wave
+// holds 16 rows of one residue class; the other side's rows stream past,
+// the next one loaded while the current one is used.  No atomics, so results
+// are reproducible.  This is the plain vector-unit path; it does not use MFMA.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "lf_kernels.h"
+#include "lf_bwd.h"
 
 namespace lfb {
 
@@ -122,8 +122,143 @@ __device__ __forceinline__ bool is_global(const uint32_t* __restrict__ gmap, int
 
 __device__ __forceinline__ bool padded(const uint8_t* __restrict__ pad, int i) { return pad && pad[i] != 0; }
 
-// One wave's share of the lane kernels: batch b, head h, residue class c of
-// stride delta, and class positions [t0, t0 + 64) of the nc in the class.
+// The band kernels give each query (or key) row four lanes, each owning 16
+// of its 64 channels: a wave holds 16 rows, dot products end with a sum over
+// the four lanes (two DPP steps), and a lane keeps 16-channel slices only.
+constexpr int NQ = LFB_ROWS_PER_WAVE;   // rows per wave
+constexpr int CS = D / 4;               // channels per lane
+
+struct Slice {
+    float x[CS];
+};
+
+__device__ __forceinline__ void zero_slice(Slice& r) {
+#pragma unroll
+    for (int c = 0; c < CS; c++) r.x[c] = 0.f;
+}
+
+// A lane's 16-channel slice of an input row as loaded: bf16 rows stay packed
+// two channels per word (dot products take them as they are, with
+// v_dot2_f32_bf16; products of bf16 values are exact in fp32), fp32 rows are
+// plain floats.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <typename ET>
+struct In;
+template <>
+struct In<__bf16> {
+    uint32_t w[CS / 2];
+};
+template <>
+struct In<float> {
+    float x[CS];
+};
+
+template <typename ET>
+__device__ __forceinline__ void load_in(const ET* __restrict__ p, In<ET>& r) {
+    if constexpr (sizeof(ET) == 2) {
+        const uint4* p4 = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+        for (int e = 0; e < CS / 8; e++) {
+            const uint4 u = p4[e];
+            r.w[4 * e] = u.x;
+            r.w[4 * e + 1] = u.y;
+            r.w[4 * e + 2] = u.z;
+            r.w[4 * e + 3] = u.w;
+        }
+    } else {
+        const float4* p4 = reinterpret_cast<const float4*>(p);
+#pragma unroll
+        for (int e = 0; e < CS / 4; e++) {
+            const float4 u = p4[e];
+            r.x[4 * e] = u.x;
+            r.x[4 * e + 1] = u.y;
+            r.x[4 * e + 2] = u.z;
+            r.x[4 * e + 3] = u.w;
+        }
+    }
+}
+
+template <typename ET>
+__device__ __forceinline__ void zero_in(In<ET>& r) {
+    if constexpr (sizeof(ET) == 2) {
+#pragma unroll
+        for (int e = 0; e < CS / 2; e++) r.w[e] = 0u;
+    } else {
+#pragma unroll
+        for (int c = 0; c < CS; c++) r.x[c] = 0.f;
+    }
+}
+
+template <typename ET>
+__device__ __forceinline__ float dot_in(const In<ET>& a, const In<ET>& b) {
+    float s0 = 0.f, s1 = 0.f;
+    if constexpr (sizeof(ET) == 2) {
+#pragma unroll
+        for (int e = 0; e < CS / 2; e += 2) {
+            s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w[e]),
+                                                 __builtin_bit_cast(bf16x2_t, b.w[e]), s0, false);
+            s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w[e + 1]),
+                                                 __builtin_bit_cast(bf16x2_t, b.w[e + 1]), s1, false);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CS; c += 2) {
+            s0 = __builtin_fmaf(a.x[c], b.x[c], s0);
+            s1 = __builtin_fmaf(a.x[c + 1], b.x[c + 1], s1);
+        }
+    }
+    return s0 + s1;
+}
+
+// acc += a * x (x widened to fp32)
+template <typename ET>
+__device__ __forceinline__ void axpy_in(Slice& acc, float a, const In<ET>& x) {
+    if constexpr (sizeof(ET) == 2) {
+#pragma unroll
+        for (int e = 0; e < CS / 2; e++) {
+            acc.x[2 * e] = __builtin_fmaf(a, __uint_as_float(x.w[e] << 16), acc.x[2 * e]);
+            acc.x[2 * e + 1] = __builtin_fmaf(a, __uint_as_float(x.w[e] & 0xffff0000u), acc.x[2 * e + 1]);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CS; c++) acc.x[c] = __builtin_fmaf(a, x.x[c], acc.x[c]);
+    }
+}
+
+// Sum over the four lanes of a quad (lanes 4k .. 4k+3), in every lane.
+__device__ __forceinline__ float quad_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+    return x;
+}
+
+template <typename ET>
+__device__ __forceinline__ void store_slice(ET* __restrict__ p, const Slice& r, float scale) {
+    if constexpr (sizeof(ET) == 2) {
+        uint4* p4 = reinterpret_cast<uint4*>(p);
+#pragma unroll
+        for (int e = 0; e < CS / 8; e++) {
+            uint32_t u[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const __bf16 lo = (__bf16)(r.x[8 * e + 2 * t] * scale);
+                const __bf16 hi = (__bf16)(r.x[8 * e + 2 * t + 1] * scale);
+                u[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            }
+            p4[e] = make_uint4(u[0], u[1], u[2], u[3]);
+        }
+    } else {
+        float4* p4 = reinterpret_cast<float4*>(p);
+#pragma unroll
+        for (int e = 0; e < CS / 4; e++)
+            p4[e] = make_float4(r.x[4 * e] * scale, r.x[4 * e + 1] * scale, r.x[4 * e + 2] * scale,
+                                r.x[4 * e + 3] * scale);
+    }
+}
+
+// One wave's share of the band kernels: batch b, head h, residue class c of
+// stride delta, and class positions [t0, t0 + NQ) of the nc in the class.
 struct Chunk {
     int b, h, c, t0, nc, delta, r, ra;
 };
@@ -140,15 +275,15 @@ __device__ __forceinline__ bool decode(const lfk::BwdArgs& A, long long task, Ch
     const int delta = A.dil[h];
     const int T = A.T;
     const int q = T / delta, rm = T - q * delta;
-    const int ch1 = (q + 1 + 63) >> 6, ch0 = (q + 63) >> 6;   // chunks of a class with q+1 / q members
+    const int ch1 = (q + NQ) / NQ, ch0 = (q + NQ - 1) / NQ;   // chunks of a class with q+1 / q members
     if (rem < rm * ch1) {
         k.c = rem / ch1;
-        k.t0 = (rem - k.c * ch1) * 64;
+        k.t0 = (rem - k.c * ch1) * NQ;
         k.nc = q + 1;
     } else {
         rem -= rm * ch1;
         k.c = rm + rem / ch0;
-        k.t0 = (rem % ch0) * 64;
+        k.t0 = (rem % ch0) * NQ;
         k.nc = q;
     }
     k.delta = delta;
@@ -156,6 +291,91 @@ __device__ __forceinline__ bool decode(const lfk::BwdArgs& A, long long task, Ch
     k.ra = A.one_sided ? 0 : k.r;
     return true;
 }
+
+// The class positions in [lo, hi] whose row is neither padded nor global, in
+// ascending order: one ballot over 64 positions at a time (each lane tests
+// one), then scalar bit scans.  Every value is wave-uniform.
+struct ClassScan {
+    const lfk::BwdArgs& A;
+    const Chunk& ck;
+    const uint8_t* pad;
+    int hi, lane, base;
+    uint64_t mask;
+    __device__ ClassScan(const lfk::BwdArgs& A_, const Chunk& ck_, const uint8_t* pad_, int lo, int hi_, int lane_)
+        : A(A_), ck(ck_), pad(pad_), hi(hi_), lane(lane_) {
+        reset(lo);
+    }
+    __device__ void refill(int b) {
+        base = b;
+        const int x = b + lane;
+        bool ok = false;
+        if (x <= hi) {
+            const int j = ck.c + x * ck.delta;
+            ok = !padded(pad, j) && !(A.n_g > 0 && is_global(A.gmap, j));
+        }
+        mask = __ballot(ok);
+    }
+    __device__ void reset(int lo) { refill(lo); }
+    // smallest listed position >= x (x never below the previous answer), or hi + 1
+    __device__ int operator()(int x) {
+        for (;;) {
+            if (x > hi) return hi + 1;
+            if (x >= base + 64) refill(x);
+            const uint64_t m = mask >> (x - base);
+            if (m) return x + __builtin_ctzll(m);
+            x = base + 64;
+        }
+    }
+};
+
+// Visit the listed class positions from lo on in ascending order, with the
+// rows of the next PF positions loaded ahead (a ring of PF register slots,
+// unrolled so that every slot index is static).
+template <int PF, typename Load, typename Use>
+__device__ __forceinline__ void stream_rows(ClassScan& next, int lo, Load load, Use use) {
+    using Item = decltype(load(0));
+    const int hi = next.hi;
+    Item buf[PF];
+    int pos[PF];
+    int tk = next(lo);
+#pragma unroll
+    for (int p = 0; p < PF; p++) {
+        pos[p] = tk;
+        if (tk <= hi) {
+            buf[p] = load(tk);
+            tk = next(tk + 1);
+        }
+    }
+    bool done = false;
+    while (!done) {
+#pragma unroll
+        for (int p = 0; p < PF; p++) {
+            if (!done && pos[p] > hi) done = true;
+            if (!done) {
+                use(buf[p], pos[p]);
+                pos[p] = tk;
+                if (tk <= hi) {
+                    buf[p] = load(tk);
+                    tk = next(tk + 1);
+                }
+            }
+        }
+    }
+}
+
+template <typename ET>
+struct KV {
+    In<ET> k, v;
+};
+template <typename ET>
+struct QY {
+    In<ET> q, y;
+    float2 st;
+};
+
+// rows loaded ahead: four for bf16 rows, two for the twice larger fp32 rows
+template <typename ET>
+constexpr int PREFETCH = sizeof(ET) == 2 ? 4 : 2;
 
 // ---------------------------------------------------------------------------
 // dq and the row statistics of the non-global queries.
@@ -171,33 +391,35 @@ __global__ __launch_bounds__(256) void rows_kernel(const lfk::BwdArgs A, const E
     if (!decode(A, (long long)blockIdx.x * 4 + wave, ck)) return;
     const int T = A.T;
     const size_t bh = (size_t)ck.b * A.H + ck.h;
-    const ET* Kh = K + bh * T * D;
-    const ET* Vh = V + bh * T * D;
+    const int part = lane & 3;
+    const ET* Kh = K + bh * T * D + CS * part;
+    const ET* Vh = V + bh * T * D + CS * part;
     const uint8_t* pad = A.pad ? A.pad + (size_t)ck.b * T : nullptr;
-    const int t = ck.t0 + lane;
+    const int t = ck.t0 + (lane >> 2);
     const bool in = t < ck.nc;
     const int i = ck.c + t * ck.delta;
     const bool glob_i = in && A.n_g > 0 && is_global(A.gmap, i);
     const bool live = in && !glob_i && !padded(pad, i);
-    RowF q, dy;
+    In<ET> q, dy;
     if (live) {
-        load_row(Q + (bh * T + i) * D, q);
-        load_row(DY + (bh * T + i) * D, dy);
+        load_in(Q + (bh * T + i) * D + CS * part, q);
+        load_in(DY + (bh * T + i) * D + CS * part, dy);
     } else {
-        zero_row(q);
-        zero_row(dy);
+        zero_in(q);
+        zero_in(dy);
     }
     const float sc = LOG2E / 8.0f;   // 1/sqrt(64), base 2
-    const int k_lo = max(ck.t0 - ck.r, 0), k_hi = min(ck.t0 + 63 + ck.ra, ck.nc - 1);
+    const int k_lo = max(ck.t0 - ck.r, 0), k_hi = min(ck.t0 + NQ - 1 + ck.ra, ck.nc - 1);
+    // next class position >= x whose key is neither padded nor global (the
+    // globals take their own loop), or k_hi + 1
+    ClassScan next_key(A, ck, pad, k_lo, k_hi, lane);
+    auto in_window = [&](int tk) { return live && tk - t >= -ck.r && tk - t <= ck.ra; };
 
     // pass 1: running max, sum and sum of p * dP
     float m = -INFINITY, l = 0.f, dn = 0.f;
-    auto visit1 = [&](int j, bool on) {
-        RowF kr, vr;
-        load_row(Kh + (size_t)j * D, kr);
-        load_row(Vh + (size_t)j * D, vr);
-        const float s = dot(q, kr) * sc;
-        const float dp = dot(dy, vr);
+    auto acc1 = [&](const In<ET>& kr, const In<ET>& vr, bool on) {
+        const float s = quad_sum(dot_in(q, kr)) * sc;
+        const float dp = quad_sum(dot_in(dy, vr));
         if (on) {
             const float mn = fmaxf(m, s);
             const float al = ex2(m - mn), e = ex2(s - mn);
@@ -206,44 +428,48 @@ __global__ __launch_bounds__(256) void rows_kernel(const lfk::BwdArgs A, const E
             m = mn;
         }
     };
-    for (int tk = k_lo; tk <= k_hi; tk++) {
-        const int j = ck.c + tk * ck.delta;
-        if (padded(pad, j) || (A.n_g > 0 && is_global(A.gmap, j))) continue;
-        visit1(j, live && tk - t >= -ck.r && tk - t <= ck.ra);
-    }
+    auto load_kv = [&](int tk) {
+        KV<ET> x;
+        load_in(Kh + (size_t)(ck.c + tk * ck.delta) * D, x.k);
+        load_in(Vh + (size_t)(ck.c + tk * ck.delta) * D, x.v);
+        return x;
+    };
+    stream_rows<PREFETCH<ET>>(next_key, k_lo, load_kv,
+                          [&](const KV<ET>& x, int tk) { acc1(x.k, x.v, in_window(tk)); });
     for (int g = 0; g < A.n_g; g++) {
         const int j = A.glob[g];
         if (padded(pad, j)) continue;
-        visit1(j, live);
+        In<ET> kr, vr;
+        load_in(Kh + (size_t)j * D, kr);
+        load_in(Vh + (size_t)j * D, vr);
+        acc1(kr, vr, live);
     }
     const float lse = live ? m + lg2(l) : 0.f;
     const float Dl = live ? dn / l : 0.f;
 
     // pass 2: dq
-    RowF acc;
-    zero_row(acc);
-    auto visit2 = [&](int j, bool on) {
-        RowF kr, vr;
-        load_row(Kh + (size_t)j * D, kr);
-        load_row(Vh + (size_t)j * D, vr);
-        const float s = dot(q, kr) * sc;
-        const float dp = dot(dy, vr);
-        const float p = on ? ex2(s - lse) : 0.f;
-        axpy(acc, p * (dp - Dl), kr);
+    next_key.reset(k_lo);
+    Slice acc;
+    zero_slice(acc);
+    auto acc2 = [&](const In<ET>& kr, const In<ET>& vr, bool on) {
+        const float s = quad_sum(dot_in(q, kr)) * sc;
+        const float dp = quad_sum(dot_in(dy, vr));
+        const float ds = on ? ex2(s - lse) * (dp - Dl) : 0.f;
+        axpy_in(acc, ds, kr);
     };
-    for (int tk = k_lo; tk <= k_hi; tk++) {
-        const int j = ck.c + tk * ck.delta;
-        if (padded(pad, j) || (A.n_g > 0 && is_global(A.gmap, j))) continue;
-        visit2(j, live && tk - t >= -ck.r && tk - t <= ck.ra);
-    }
+    stream_rows<PREFETCH<ET>>(next_key, k_lo, load_kv,
+                          [&](const KV<ET>& x, int tk) { acc2(x.k, x.v, in_window(tk)); });
     for (int g = 0; g < A.n_g; g++) {
         const int j = A.glob[g];
         if (padded(pad, j)) continue;
-        visit2(j, live);
+        In<ET> kr, vr;
+        load_in(Kh + (size_t)j * D, kr);
+        load_in(Vh + (size_t)j * D, vr);
+        acc2(kr, vr, live);
     }
     if (in && !glob_i) {
-        store_row(DQ + (bh * T + i) * D, acc, 0.125f);
-        stats[bh * T + i] = make_float2(lse, Dl);
+        store_slice(DQ + (bh * T + i) * D + CS * part, acc, 0.125f);
+        if (part == 0) stats[bh * T + i] = make_float2(lse, Dl);
     }
 }
 
@@ -261,54 +487,61 @@ __global__ __launch_bounds__(256) void cols_kernel(const lfk::BwdArgs A, const E
     if (!decode(A, (long long)blockIdx.x * 4 + wave, ck)) return;
     const int T = A.T;
     const size_t bh = (size_t)ck.b * A.H + ck.h;
-    const ET* Qh = Q + bh * T * D;
-    const ET* Yh = DY + bh * T * D;
+    const int part = lane & 3;
+    const ET* Qh = Q + bh * T * D + CS * part;
+    const ET* Yh = DY + bh * T * D + CS * part;
     const float2* Sh = stats + bh * T;
     const uint8_t* pad = A.pad ? A.pad + (size_t)ck.b * T : nullptr;
-    const int t = ck.t0 + lane;
+    const int t = ck.t0 + (lane >> 2);
     const bool in = t < ck.nc;
     const int j = ck.c + t * ck.delta;
     const bool glob_j = in && A.n_g > 0 && is_global(A.gmap, j);
     const bool live = in && !glob_j && !padded(pad, j);
-    RowF kr, vr;
+    In<ET> kr, vr;
     if (live) {
-        load_row(K + (bh * T + j) * D, kr);
-        load_row(V + (bh * T + j) * D, vr);
+        load_in(K + (bh * T + j) * D + CS * part, kr);
+        load_in(V + (bh * T + j) * D + CS * part, vr);
     } else {
-        zero_row(kr);
-        zero_row(vr);
+        zero_in(kr);
+        zero_in(vr);
     }
     const float sc = LOG2E / 8.0f;
-    RowF dk, dv;
-    zero_row(dk);
-    zero_row(dv);
-    auto visit = [&](int i, bool on) {
-        RowF q, dy;
-        load_row(Qh + (size_t)i * D, q);
-        load_row(Yh + (size_t)i * D, dy);
-        const float2 st = Sh[i];
-        const float s = dot(q, kr) * sc;
-        const float dp = dot(dy, vr);
+    Slice dk, dv;
+    zero_slice(dk);
+    zero_slice(dv);
+    auto acc = [&](const In<ET>& q, const In<ET>& dy, float2 st, bool on) {
+        const float s = quad_sum(dot_in(q, kr)) * sc;
+        const float dp = quad_sum(dot_in(dy, vr));
         const float p = on ? ex2(s - st.x) : 0.f;
-        axpy(dv, p, dy);
-        axpy(dk, p * (dp - st.y), q);
+        axpy_in(dv, p, dy);
+        axpy_in(dk, p * (dp - st.y), q);
     };
-    // query i (class position tq) holds key position t' in its window iff
-    // tq - t' lies in [-ra, r]
-    const int q_lo = max(ck.t0 - ck.ra, 0), q_hi = min(ck.t0 + 63 + ck.r, ck.nc - 1);
-    for (int tq = q_lo; tq <= q_hi; tq++) {
-        const int i = ck.c + tq * ck.delta;
-        if (padded(pad, i) || (A.n_g > 0 && is_global(A.gmap, i))) continue;
-        visit(i, live && tq - t >= -ck.ra && tq - t <= ck.r);
-    }
+    // query i (class position tq) holds key position t in its window iff
+    // tq - t lies in [-ra, r]
+    const int q_lo = max(ck.t0 - ck.ra, 0), q_hi = min(ck.t0 + NQ - 1 + ck.r, ck.nc - 1);
+    ClassScan next_query(A, ck, pad, q_lo, q_hi, lane);
+    auto load_qy = [&](int tq) {
+        QY<ET> x;
+        const size_t i = ck.c + (size_t)tq * ck.delta;
+        load_in(Qh + i * D, x.q);
+        load_in(Yh + i * D, x.y);
+        x.st = Sh[i];
+        return x;
+    };
+    stream_rows<PREFETCH<ET>>(next_query, q_lo, load_qy, [&](const QY<ET>& x, int tq) {
+        acc(x.q, x.y, x.st, live && tq - t >= -ck.ra && tq - t <= ck.r);
+    });
     for (int g = 0; g < A.n_g; g++) {
         const int i = A.glob[g];
         if (padded(pad, i)) continue;
-        visit(i, live);
+        In<ET> q, dy;
+        load_in(Qh + (size_t)i * D, q);
+        load_in(Yh + (size_t)i * D, dy);
+        acc(q, dy, Sh[i], live);
     }
     if (in && !glob_j) {
-        store_row(DK + (bh * T + j) * D, dk, 0.125f);
-        store_row(DV + (bh * T + j) * D, dv, 1.0f);
+        store_slice(DK + (bh * T + j) * D + CS * part, dk, 0.125f);
+        store_slice(DV + (bh * T + j) * D + CS * part, dv, 1.0f);
     }
 }
 
@@ -470,7 +703,7 @@ hipError_t launch(const lfk::BwdArgs* A, const void* const* t, hipStream_t s) {
     ET* dk = (ET*)t[5];
     ET* dv = (ET*)t[6];
     float2* st = (float2*)A->stats;
-    const long long waves = (long long)A->B * A->head_chunk[A->H];
+    const long long waves = (long long)A->B * A->head_chunk[A->H];   // one wave per chunk of NQ rows
     const dim3 gl((unsigned)((waves + 3) / 4)), blk(256);
     const dim3 gg((unsigned)((long long)A->B * A->H * A->n_g));
     hipLaunchKernelGGL(rows_kernel<ET>, gl, blk, 0, s, *A, q, k, v, dy, dq, st);

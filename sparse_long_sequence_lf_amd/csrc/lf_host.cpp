@@ -18,6 +18,7 @@
 
 #include "lf_attn.h"
 #include "lf_kernels.h"
+#include "lf_bwd.h"
 
 extern "C" hipError_t lfk_launch(const lfk::Args *A, const lfk::Plan *P, int dtype_bf16, void *stream);
 extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs *A, const void *const *t, int dtype_bf16, void *stream);
@@ -406,7 +407,7 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
         tab[o_dil + h] = (uint32_t)delta;
         tab[o_hc + h] = (uint32_t)chunks;
         const long long qq = T / delta, rm = T % delta;
-        chunks += rm * cdiv(qq + 1, 64) + (delta - rm) * cdiv(qq, 64);
+        chunks += rm * cdiv(qq + 1, LFB_ROWS_PER_WAVE) + (delta - rm) * cdiv(qq, LFB_ROWS_PER_WAVE);
     }
     tab[o_hc + H] = (uint32_t)chunks;
     if ((long long)B * chunks >= (1LL << 31)) return fail(LF_E_UNSUPPORTED, "problem needs too many waves");

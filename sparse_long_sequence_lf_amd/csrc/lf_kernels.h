@@ -53,20 +53,6 @@ struct Plan {
     int32_t glob[LF_MAX_GLOBALS];
 };
 
-// The backward launches' argument (lf_bwd_kernels.hip).  The tables live in
-// one device buffer of the workspace: radius, stride and wave-chunk prefix
-// per head, the sorted global positions and their bitmap.
-struct BwdArgs {
-    const uint8_t *pad;          // [B][T] or null
-    const uint32_t *gmap;        // bit i set iff position i is global ([ceil(T/32)] words)
-    const int32_t *glob;         // [n_g] distinct globals, ascending
-    const int32_t *rad;          // [H] window radius per head (clamped to T)
-    const int32_t *dil;          // [H] stride per head
-    const int32_t *head_chunk;   // [H+1] prefix over heads of the 64-position class chunks
-    void *stats;                 // float2 [B*H][T]: (log2-sum-exp of the scaled scores, D_i)
-    int B, H, T, n_g, one_sided;
-};
-
 // The kernel argument: the call's tensors and the device copy of its plan.
 struct Args {
     const void *q, *k, *v;
