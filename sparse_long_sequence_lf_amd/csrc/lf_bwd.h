@@ -6,6 +6,8 @@
 
 #include <stdint.h>
 
+#include <hip/hip_runtime.h>
+
 #include "lf_attn.h"
 
 // Rows (queries or keys) of one residue class per wave in the backward's band
@@ -25,7 +27,10 @@ struct BwdArgs {
     const int32_t *dil;          // [H] stride per head
     const int32_t *head_chunk;   // [H+1] prefix over heads of the class chunks (LFB_ROWS_PER_WAVE positions)
     void *stats;                 // float2 [B*H][T]: (log2-sum-exp of the scaled scores, D_i)
+    float4 *gstat;               // [B*H*n_g][n_split]: a split's (max, sum, sum of p dP) of a global row
+    float *gpart;                // [B*H*n_g][n_split][192]: a split's partial dq, dk, dv of a global position
     int B, H, T, n_g, one_sided;
+    int n_split, split_len;      // global rows and columns: splits of split_len positions (256 x per-thread count)
 };
 
 }  // namespace lfk

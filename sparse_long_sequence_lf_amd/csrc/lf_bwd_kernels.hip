@@ -14,15 +14,19 @@
 // Reading"), the global set G both ways ("Global Attention"), and padded
 // keys and queries left out.
 //
-// Four launches on the call's stream, each position written by exactly one:
-//   rows_kernel   lane = a non-global query of one residue class: one pass
-//                 for the row's log-sum-exp and D_i (online), one for dq_i;
-//                 writes (lse_i, D_i) for the column kernels.
-//   grows_kernel  one workgroup per (b, h, global row): the same over every
-//                 valid key, lanes over keys, reduced through LDS.
+// Up to six launches on the call's stream; each output row is written by
+// exactly one thread:
+//   rows_kernel   non-global queries of one residue class: one pass with
+//                 online-rescaled sums gives the row's log-sum-exp, D_i and
+//                 dq_i; writes (lse_i, D_i) for the column kernels.
+//   grows_stats_kernel, grows_dq_kernel
+//                 global rows: every valid key, in splits of split_len keys
+//                 (one workgroup each, reduced through LDS): the splits'
+//                 (max, sum, sum of p dP), then their parts of dq.
 //   cols_kernel   lane = a non-global key of one residue class: dk_j, dv_j
 //                 from the queries whose window holds j, plus the global rows.
-//   gcols_kernel  one workgroup per (b, h, global key): every valid query.
+//   gcols_kernel  global keys: every valid query, in splits likewise.
+//   combine_kernel  adds the splits' parts of dq, dk, dv of the global positions.
 // In the band kernels four lanes share a row (16 channels each) and a wave
 // holds 16 rows of one residue class; the other side's rows stream past,
 // the next one loaded while the current one is used.  No atomics, so results
@@ -415,18 +419,35 @@ __global__ __launch_bounds__(256) void rows_kernel(const lfk::BwdArgs A, const E
     ClassScan next_key(A, ck, pad, k_lo, k_hi, lane);
     auto in_window = [&](int tk) { return live && tk - t >= -ck.r && tk - t <= ck.ra; };
 
-    // pass 1: running max, sum and sum of p * dP
+    // One pass with a running reference max m (base 2): l = sum e, dn = sum
+    // e dP, A = sum e dP k, Bk = sum e k with e = 2^(s - m).  Then
+    // lse = m + log2 l, D = dn / l and dq = (A - D Bk) / (8 l), the chain rule
+    // sum_j P_ij (dP_ij - D_i) k_j / sqrt(d) regrouped.  m is moved (and the
+    // sums rescaled) only when a score passes it by more than 8, so e stays
+    // below 2^8.
     float m = -INFINITY, l = 0.f, dn = 0.f;
-    auto acc1 = [&](const In<ET>& kr, const In<ET>& vr, bool on) {
+    Slice Aq, Bk;
+    zero_slice(Aq);
+    zero_slice(Bk);
+    auto accum = [&](const In<ET>& kr, const In<ET>& vr, bool on) {
         const float s = quad_sum(dot_in(q, kr)) * sc;
         const float dp = quad_sum(dot_in(dy, vr));
-        if (on) {
-            const float mn = fmaxf(m, s);
-            const float al = ex2(m - mn), e = ex2(s - mn);
-            l = l * al + e;
-            dn = dn * al + e * dp;
-            m = mn;
+        if (on && s > m + 8.f) {
+            const float al = ex2(m - s);
+            l *= al;
+            dn *= al;
+#pragma unroll
+            for (int c = 0; c < CS; c++) {
+                Aq.x[c] *= al;
+                Bk.x[c] *= al;
+            }
+            m = s;
         }
+        const float e = on ? ex2(s - m) : 0.f;
+        l += e;
+        dn += e * dp;
+        axpy_in(Aq, e * dp, kr);
+        axpy_in(Bk, e, kr);
     };
     auto load_kv = [&](int tk) {
         KV<ET> x;
@@ -435,38 +456,21 @@ __global__ __launch_bounds__(256) void rows_kernel(const lfk::BwdArgs A, const E
         return x;
     };
     stream_rows<PREFETCH<ET>>(next_key, k_lo, load_kv,
-                          [&](const KV<ET>& x, int tk) { acc1(x.k, x.v, in_window(tk)); });
+                              [&](const KV<ET>& x, int tk) { accum(x.k, x.v, in_window(tk)); });
     for (int g = 0; g < A.n_g; g++) {
         const int j = A.glob[g];
         if (padded(pad, j)) continue;
         In<ET> kr, vr;
         load_in(Kh + (size_t)j * D, kr);
         load_in(Vh + (size_t)j * D, vr);
-        acc1(kr, vr, live);
+        accum(kr, vr, live);
     }
     const float lse = live ? m + lg2(l) : 0.f;
     const float Dl = live ? dn / l : 0.f;
-
-    // pass 2: dq
-    next_key.reset(k_lo);
+    const float inv = live ? 1.f / l : 0.f;
     Slice acc;
-    zero_slice(acc);
-    auto acc2 = [&](const In<ET>& kr, const In<ET>& vr, bool on) {
-        const float s = quad_sum(dot_in(q, kr)) * sc;
-        const float dp = quad_sum(dot_in(dy, vr));
-        const float ds = on ? ex2(s - lse) * (dp - Dl) : 0.f;
-        axpy_in(acc, ds, kr);
-    };
-    stream_rows<PREFETCH<ET>>(next_key, k_lo, load_kv,
-                          [&](const KV<ET>& x, int tk) { acc2(x.k, x.v, in_window(tk)); });
-    for (int g = 0; g < A.n_g; g++) {
-        const int j = A.glob[g];
-        if (padded(pad, j)) continue;
-        In<ET> kr, vr;
-        load_in(Kh + (size_t)j * D, kr);
-        load_in(Vh + (size_t)j * D, vr);
-        acc2(kr, vr, live);
-    }
+#pragma unroll
+    for (int c = 0; c < CS; c++) acc.x[c] = (Aq.x[c] - Dl * Bk.x[c]) * inv;
     if (in && !glob_i) {
         store_slice(DQ + (bh * T + i) * D + CS * part, acc, 0.125f);
         if (part == 0) stats[bh * T + i] = make_float2(lse, Dl);
@@ -546,151 +550,213 @@ __global__ __launch_bounds__(256) void cols_kernel(const lfk::BwdArgs A, const E
 }
 
 // ---------------------------------------------------------------------------
-// Global rows and global keys: one workgroup each, lanes over the other side.
+// Global rows and global keys.  Each (b, h, global position) is split into
+// n_split ranges of split_len positions, one workgroup per range (256
+// threads, split_len / 256 positions each); partial results go to gstat and
+// gpart, and combine_kernel adds them up.
 
-// Sum x[tid][c] over the 256 threads into the first 64 (c = tid); red holds
-// 256 x 65 floats.
+// Sum x[tid][c] over the 256 threads into thread c < 64; red holds 256 x 65
+// floats.  Each thread first adds a quarter of one channel's column (64
+// rows), then 64 threads add the four quarters.
 __device__ __forceinline__ float block_sum_row(float* red, const RowF& x) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int c = 0; c < D; c++) red[tid * 65 + c] = x.x[c];
     __syncthreads();
+    const int c = tid & 63, r0 = (tid >> 6) * 64;
     float s = 0.f;
-    if (tid < D)
-        for (int e = 0; e < 256; e++) s += red[e * 65 + tid];
+    for (int e = 0; e < 64; e++) s += red[(r0 + e) * 65 + c];
+    __syncthreads();
+    red[tid] = s;
+    __syncthreads();
+    if (tid < D) s = red[tid] + red[64 + tid] + red[128 + tid] + red[192 + tid];
     __syncthreads();
     return s;
 }
 
+struct GTask {
+    size_t bh, rec;   // (b*H + h), record index (b*H + h)*n_g + gi
+    int b, g, sp, lo, hi;
+};
+
+__device__ __forceinline__ GTask gtask(const lfk::BwdArgs& A) {
+    GTask t;
+    t.sp = blockIdx.x % A.n_split;
+    t.rec = blockIdx.x / A.n_split;
+    const int gi = (int)(t.rec % A.n_g);
+    t.bh = t.rec / A.n_g;
+    t.b = (int)(t.bh / A.H);
+    t.g = A.glob[gi];
+    t.lo = t.sp * A.split_len;
+    t.hi = min(t.lo + A.split_len, A.T);
+    return t;
+}
+
+// pass 1 of a global row: (max, sum, sum of p dP) over the split's keys
 template <typename ET>
-__global__ __launch_bounds__(256) void grows_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
-                                                    const ET* __restrict__ K, const ET* __restrict__ V,
-                                                    const ET* __restrict__ DY, ET* __restrict__ DQ,
-                                                    float2* __restrict__ stats) {
-    __shared__ float red[256 * 65];
+__global__ __launch_bounds__(256) void grows_stats_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
+                                                          const ET* __restrict__ K, const ET* __restrict__ V,
+                                                          const ET* __restrict__ DY) {
     __shared__ float red_m[256], red_l[256], red_d[256];
     const int tid = threadIdx.x;
-    const int gi = blockIdx.x % A.n_g;
-    const size_t bh = blockIdx.x / A.n_g;
-    const int b = (int)(bh / A.H);
+    const GTask t = gtask(A);
     const int T = A.T;
-    const int g = A.glob[gi];
-    const uint8_t* pad = A.pad ? A.pad + (size_t)b * T : nullptr;
-    ET* dq = DQ + (bh * T + g) * D;
-    if (padded(pad, g)) {
-        if (tid < D) dq[tid] = (ET)0.f;
-        return;
-    }
-    const ET* Kh = K + bh * T * D;
-    const ET* Vh = V + bh * T * D;
-    RowF q, dy;
-    load_row(Q + (bh * T + g) * D, q);
-    load_row(DY + (bh * T + g) * D, dy);
-    const float sc = LOG2E / 8.0f;
+    const uint8_t* pad = A.pad ? A.pad + (size_t)t.b * T : nullptr;
     float m = -INFINITY, l = 0.f, dn = 0.f;
-    for (int j = tid; j < T; j += 256) {
-        if (padded(pad, j)) continue;
-        RowF kr, vr;
-        load_row(Kh + (size_t)j * D, kr);
-        load_row(Vh + (size_t)j * D, vr);
-        const float s = dot(q, kr) * sc;
-        const float dp = dot(dy, vr);
-        const float mn = fmaxf(m, s);
-        const float al = ex2(m - mn), e = ex2(s - mn);
-        l = l * al + e;
-        dn = dn * al + e * dp;
-        m = mn;
+    if (!padded(pad, t.g)) {
+        const ET* Kh = K + t.bh * T * D;
+        const ET* Vh = V + t.bh * T * D;
+        RowF q, dy;
+        load_row(Q + (t.bh * T + t.g) * D, q);
+        load_row(DY + (t.bh * T + t.g) * D, dy);
+        const float sc = LOG2E / 8.0f;
+        for (int j = t.lo + tid; j < t.hi; j += 256) {
+            if (padded(pad, j)) continue;
+            RowF kr, vr;
+            load_row(Kh + (size_t)j * D, kr);
+            load_row(Vh + (size_t)j * D, vr);
+            const float s = dot(q, kr) * sc;
+            const float dp = dot(dy, vr);
+            const float mn = fmaxf(m, s);
+            const float al = ex2(m - mn), e = ex2(s - mn);
+            l = l * al + e;
+            dn = dn * al + e * dp;
+            m = mn;
+        }
     }
     red_m[tid] = m;
     red_l[tid] = l;
     red_d[tid] = dn;
     __syncthreads();
-    float M = -INFINITY;
-    for (int e = 0; e < 256; e++) M = fmaxf(M, red_m[e]);
-    float L = 0.f, DN = 0.f;
-    for (int e = 0; e < 256; e++) {
-        if (red_l[e] == 0.f) continue;   // a thread that met no valid key
-        const float w = ex2(red_m[e] - M);
-        L += red_l[e] * w;
-        DN += red_d[e] * w;
+    if (tid == 0) {
+        float M = -INFINITY;
+        for (int e = 0; e < 256; e++) M = fmaxf(M, red_m[e]);
+        float L = 0.f, DN = 0.f;
+        for (int e = 0; e < 256; e++) {
+            if (red_l[e] == 0.f) continue;   // a thread that met no valid key
+            const float w = ex2(red_m[e] - M);
+            L += red_l[e] * w;
+            DN += red_d[e] * w;
+        }
+        A.gstat[t.rec * A.n_split + t.sp] = make_float4(M, L, DN, 0.f);
     }
-    __syncthreads();
-    const float lse = M + lg2(L), Dl = DN / L;   // key g itself is valid, so L >= 1
-    RowF acc;
-    zero_row(acc);
-    for (int j = tid; j < T; j += 256) {
-        if (padded(pad, j)) continue;
-        RowF kr, vr;
-        load_row(Kh + (size_t)j * D, kr);
-        load_row(Vh + (size_t)j * D, vr);
-        const float s = dot(q, kr) * sc;
-        const float dp = dot(dy, vr);
-        const float p = ex2(s - lse);
-        axpy(acc, p * (dp - Dl), kr);
-    }
-    const float sum = block_sum_row(red, acc);
-    if (tid < D) {
-        if constexpr (sizeof(ET) == 2) dq[tid] = (ET)(sum * 0.125f);
-        else dq[tid] = sum * 0.125f;
-    }
-    if (tid == 0) stats[bh * T + g] = make_float2(lse, Dl);
 }
 
+// pass 2 of a global row: the split's part of dq; split 0 also writes the
+// row's (lse, D) for the column kernels
+template <typename ET>
+__global__ __launch_bounds__(256) void grows_dq_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
+                                                       const ET* __restrict__ K, const ET* __restrict__ V,
+                                                       const ET* __restrict__ DY, float2* __restrict__ stats) {
+    __shared__ float red[256 * 65];
+    const int tid = threadIdx.x;
+    const GTask t = gtask(A);
+    const int T = A.T;
+    const uint8_t* pad = A.pad ? A.pad + (size_t)t.b * T : nullptr;
+    RowF acc;
+    zero_row(acc);
+    if (!padded(pad, t.g)) {
+        // the row's statistics from every split's record
+        const float4* gs = A.gstat + t.rec * A.n_split;
+        float M = -INFINITY;
+        for (int e = 0; e < A.n_split; e++) M = fmaxf(M, gs[e].x);
+        float L = 0.f, DN = 0.f;
+        for (int e = 0; e < A.n_split; e++) {
+            const float4 r = gs[e];
+            if (r.y == 0.f) continue;
+            const float w = ex2(r.x - M);
+            L += r.y * w;
+            DN += r.z * w;
+        }
+        const float lse = M + lg2(L), Dl = DN / L;   // key g itself is valid, so L >= 1
+        if (t.sp == 0 && tid == 0) stats[t.bh * T + t.g] = make_float2(lse, Dl);
+        const ET* Kh = K + t.bh * T * D;
+        const ET* Vh = V + t.bh * T * D;
+        RowF q, dy;
+        load_row(Q + (t.bh * T + t.g) * D, q);
+        load_row(DY + (t.bh * T + t.g) * D, dy);
+        const float sc = LOG2E / 8.0f;
+        for (int j = t.lo + tid; j < t.hi; j += 256) {
+            if (padded(pad, j)) continue;
+            RowF kr, vr;
+            load_row(Kh + (size_t)j * D, kr);
+            load_row(Vh + (size_t)j * D, vr);
+            const float s = dot(q, kr) * sc;
+            const float dp = dot(dy, vr);
+            axpy(acc, ex2(s - lse) * (dp - Dl), kr);
+        }
+    }
+    const float sum = block_sum_row(red, acc);
+    if (tid < D) A.gpart[(t.rec * A.n_split + t.sp) * 192 + tid] = sum;
+}
+
+// a global key: the split's part of dk and dv (every valid query attends to it)
 template <typename ET>
 __global__ __launch_bounds__(256) void gcols_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
                                                     const ET* __restrict__ K, const ET* __restrict__ V,
-                                                    const ET* __restrict__ DY, ET* __restrict__ DK,
-                                                    ET* __restrict__ DV, const float2* __restrict__ stats) {
+                                                    const ET* __restrict__ DY, const float2* __restrict__ stats) {
     __shared__ float red[256 * 65];
     const int tid = threadIdx.x;
-    const int gi = blockIdx.x % A.n_g;
-    const size_t bh = blockIdx.x / A.n_g;
-    const int b = (int)(bh / A.H);
+    const GTask t = gtask(A);
     const int T = A.T;
-    const int g = A.glob[gi];
-    const uint8_t* pad = A.pad ? A.pad + (size_t)b * T : nullptr;
-    ET* dk = DK + (bh * T + g) * D;
-    ET* dv = DV + (bh * T + g) * D;
-    if (padded(pad, g)) {
-        if (tid < D) {
-            dk[tid] = (ET)0.f;
-            dv[tid] = (ET)0.f;
-        }
-        return;
-    }
-    const ET* Qh = Q + bh * T * D;
-    const ET* Yh = DY + bh * T * D;
-    RowF kr, vr;
-    load_row(K + (bh * T + g) * D, kr);
-    load_row(V + (bh * T + g) * D, vr);
-    const float sc = LOG2E / 8.0f;
+    const uint8_t* pad = A.pad ? A.pad + (size_t)t.b * T : nullptr;
     RowF ak, av;
     zero_row(ak);
     zero_row(av);
-    // every valid query attends to a global key
-    for (int i = tid; i < T; i += 256) {
-        if (padded(pad, i)) continue;
-        RowF q, dy;
-        load_row(Qh + (size_t)i * D, q);
-        load_row(Yh + (size_t)i * D, dy);
-        const float2 st = stats[bh * T + i];
-        const float s = dot(q, kr) * sc;
-        const float dp = dot(dy, vr);
-        const float p = ex2(s - st.x);
-        axpy(av, p, dy);
-        axpy(ak, p * (dp - st.y), q);
+    if (!padded(pad, t.g)) {
+        const ET* Qh = Q + t.bh * T * D;
+        const ET* Yh = DY + t.bh * T * D;
+        RowF kr, vr;
+        load_row(K + (t.bh * T + t.g) * D, kr);
+        load_row(V + (t.bh * T + t.g) * D, vr);
+        const float sc = LOG2E / 8.0f;
+        for (int i = t.lo + tid; i < t.hi; i += 256) {
+            if (padded(pad, i)) continue;
+            RowF q, dy;
+            load_row(Qh + (size_t)i * D, q);
+            load_row(Yh + (size_t)i * D, dy);
+            const float2 st = stats[t.bh * T + i];
+            const float s = dot(q, kr) * sc;
+            const float dp = dot(dy, vr);
+            const float p = ex2(s - st.x);
+            axpy(av, p, dy);
+            axpy(ak, p * (dp - st.y), q);
+        }
     }
     const float sk = block_sum_row(red, ak);
     const float sv = block_sum_row(red, av);
+    float* rec = A.gpart + (t.rec * A.n_split + t.sp) * 192;
     if (tid < D) {
-        if constexpr (sizeof(ET) == 2) {
-            dk[tid] = (ET)(sk * 0.125f);
-            dv[tid] = (ET)sv;
-        } else {
-            dk[tid] = sk * 0.125f;
-            dv[tid] = sv;
+        rec[64 + tid] = sk;
+        rec[128 + tid] = sv;
+    }
+}
+
+// dq of each global row and dk, dv of each global key: the sum of the splits
+// (zero at a padded position)
+template <typename ET>
+__global__ __launch_bounds__(64) void combine_kernel(const lfk::BwdArgs A, ET* __restrict__ DQ,
+                                                     ET* __restrict__ DK, ET* __restrict__ DV) {
+    const int c = threadIdx.x;
+    const size_t rec = blockIdx.x;
+    const int gi = (int)(rec % A.n_g);
+    const size_t bh = rec / A.n_g;
+    const int b = (int)(bh / A.H);
+    const int g = A.glob[gi];
+    const int T = A.T;
+    float sq = 0.f, sk = 0.f, sv = 0.f;
+    if (!padded(A.pad ? A.pad + (size_t)b * T : nullptr, g)) {
+        const float* p = A.gpart + rec * A.n_split * 192;
+        for (int e = 0; e < A.n_split; e++) {
+            sq += p[e * 192 + c];
+            sk += p[e * 192 + 64 + c];
+            sv += p[e * 192 + 128 + c];
         }
     }
+    const size_t o = (bh * T + g) * D + c;
+    DQ[o] = (ET)(sq * 0.125f);
+    DK[o] = (ET)(sk * 0.125f);
+    DV[o] = (ET)sv;
 }
 
 template <typename ET>
@@ -705,11 +771,18 @@ hipError_t launch(const lfk::BwdArgs* A, const void* const* t, hipStream_t s) {
     float2* st = (float2*)A->stats;
     const long long waves = (long long)A->B * A->head_chunk[A->H];   // one wave per chunk of NQ rows
     const dim3 gl((unsigned)((waves + 3) / 4)), blk(256);
-    const dim3 gg((unsigned)((long long)A->B * A->H * A->n_g));
+    const long long recs = (long long)A->B * A->H * A->n_g;
+    const dim3 gs((unsigned)(recs * A->n_split)), gc((unsigned)recs);
     hipLaunchKernelGGL(rows_kernel<ET>, gl, blk, 0, s, *A, q, k, v, dy, dq, st);
-    if (A->n_g > 0) hipLaunchKernelGGL(grows_kernel<ET>, gg, blk, 0, s, *A, q, k, v, dy, dq, st);
+    if (A->n_g > 0) {
+        hipLaunchKernelGGL(grows_stats_kernel<ET>, gs, blk, 0, s, *A, q, k, v, dy);
+        hipLaunchKernelGGL(grows_dq_kernel<ET>, gs, blk, 0, s, *A, q, k, v, dy, st);
+    }
     hipLaunchKernelGGL(cols_kernel<ET>, gl, blk, 0, s, *A, q, k, v, dy, dk, dv, st);
-    if (A->n_g > 0) hipLaunchKernelGGL(gcols_kernel<ET>, gg, blk, 0, s, *A, q, k, v, dy, dk, dv, st);
+    if (A->n_g > 0) {
+        hipLaunchKernelGGL(gcols_kernel<ET>, gs, blk, 0, s, *A, q, k, v, dy, st);
+        hipLaunchKernelGGL(combine_kernel<ET>, gc, dim3(64), 0, s, *A, dq, dk, dv);
+    }
     return hipGetLastError();
 }
 

@@ -66,7 +66,7 @@ struct Workspace {
     lfk::Plan shadow;
     bool shadow_valid = false;
     std::vector<uint32_t> aux_shadow;   // what aux holds: random-block table and global bitmap
-    Buffer bwd_tab, bwd_stats;          // backward: per-head tables and globals; row statistics
+    Buffer bwd_tab, bwd_stats, bwd_gpart;   // backward: tables; row statistics; global-split records
     std::vector<uint32_t> bwd_shadow;   // what bwd_tab holds
 };
 std::mutex g_ws_mu;
@@ -423,6 +423,21 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     if (st != LF_OK) return st;
     st = grow(w->bwd_stats, (size_t)B * H * T * 2 * sizeof(float), false, stream);
     if (st != LF_OK) return st;
+    // global rows and keys: splits of a multiple of 256 positions, as many
+    // as bring the grid to about 2048 workgroups (at most 64, at least 1)
+    const long long recs = (long long)B * H * (long long)G.size();
+    long long want = recs > 0 ? std::min(64LL, std::max(1LL, cdiv(2048, recs))) : 1;
+    want = std::min(want, cdiv(T, 256));
+    const long long per_thread = cdiv(T, 256 * want);
+    const int split_len = (int)(256 * per_thread);
+    const int n_split = (int)cdiv(T, split_len);
+    const size_t n_rec = (size_t)recs * n_split;
+    if (n_rec >= ((size_t)1 << 31)) return fail(LF_E_UNSUPPORTED, "too many global-row splits");
+    const size_t gstat_bytes = (n_rec * 16 + 255) / 256 * 256;
+    if (n_rec > 0) {
+        st = grow(w->bwd_gpart, gstat_bytes + n_rec * 192 * sizeof(float), false, stream);
+        if (st != LF_OK) return st;
+    }
     if (w->bwd_shadow != tab) {
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
@@ -448,6 +463,10 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     A.head_chunk = (const int32_t *)dt + o_hc;
     A.stats = w->bwd_stats.ptr;
     A.B = B; A.H = H; A.T = T; A.n_g = (int)G.size(); A.one_sided = one_sided;
+    A.n_split = n_split;
+    A.split_len = split_len;
+    A.gstat = n_rec > 0 ? (float4 *)w->bwd_gpart.ptr : nullptr;
+    A.gpart = n_rec > 0 ? (float *)((char *)w->bwd_gpart.ptr + gstat_bytes) : nullptr;
     const void *t[7] = {q, k, v, dy, dq, dk, dv};
     hipError_t e = lfk_bwd_launch(&A, t, dtype == LF_BF16, stream);
     if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
