@@ -10,9 +10,15 @@
 
 #include "lf_attn.h"
 
-// Rows (queries or keys) of one residue class per wave in the backward's band
-// kernels; head_chunk counts chunks of this many class positions.
-#define LFB_ROWS_PER_WAVE 16
+// Lanes that share one row (query or key) in the backward's band kernels, 4
+// or 8; a wave holds 64 / that many rows of one residue class, and
+// head_chunk counts chunks of that many class positions.  Four measured
+// faster: eight lanes per row (twice the waves, half the registers) took
+// 922 against 743 us on the T = 4096, r = 256 shape.
+#ifndef LFB_LANES_PER_ROW
+#define LFB_LANES_PER_ROW 4
+#endif
+#define LFB_ROWS_PER_WAVE (64 / LFB_LANES_PER_ROW)
 
 // The backward launches' argument (lf_bwd_kernels.hip).  The tables live in
 // one device buffer of the workspace: radius, stride and wave-chunk prefix

@@ -129,8 +129,10 @@ __device__ __forceinline__ bool padded(const uint8_t* __restrict__ pad, int i) {
 // The band kernels give each query (or key) row four lanes, each owning 16
 // of its 64 channels: a wave holds 16 rows, dot products end with a sum over
 // the four lanes (two DPP steps), and a lane keeps 16-channel slices only.
+constexpr int LPR = LFB_LANES_PER_ROW;  // lanes per row
 constexpr int NQ = LFB_ROWS_PER_WAVE;   // rows per wave
-constexpr int CS = D / 4;               // channels per lane
+constexpr int CS = D / LPR;             // channels per lane
+static_assert(LPR == 4 || LPR == 8, "four or eight lanes per row");
 
 struct Slice {
     float x[CS];
@@ -230,10 +232,12 @@ __device__ __forceinline__ void axpy_in(Slice& acc, float a, const In<ET>& x) {
     }
 }
 
-// Sum over the four lanes of a quad (lanes 4k .. 4k+3), in every lane.
+// Sum over the LPR lanes of a row (an aligned group), in every lane of it.
 __device__ __forceinline__ float quad_sum(float x) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lane ^ 1
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+    if constexpr (LPR == 8)   // the other quad of the group of 8 (lane i reads lane 7 - i)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
     return x;
 }
 
@@ -395,11 +399,11 @@ __global__ __launch_bounds__(256) void rows_kernel(const lfk::BwdArgs A, const E
     if (!decode(A, (long long)blockIdx.x * 4 + wave, ck)) return;
     const int T = A.T;
     const size_t bh = (size_t)ck.b * A.H + ck.h;
-    const int part = lane & 3;
+    const int part = lane & (LPR - 1);
     const ET* Kh = K + bh * T * D + CS * part;
     const ET* Vh = V + bh * T * D + CS * part;
     const uint8_t* pad = A.pad ? A.pad + (size_t)ck.b * T : nullptr;
-    const int t = ck.t0 + (lane >> 2);
+    const int t = ck.t0 + lane / LPR;
     const bool in = t < ck.nc;
     const int i = ck.c + t * ck.delta;
     const bool glob_i = in && A.n_g > 0 && is_global(A.gmap, i);
@@ -491,12 +495,12 @@ __global__ __launch_bounds__(256) void cols_kernel(const lfk::BwdArgs A, const E
     if (!decode(A, (long long)blockIdx.x * 4 + wave, ck)) return;
     const int T = A.T;
     const size_t bh = (size_t)ck.b * A.H + ck.h;
-    const int part = lane & 3;
+    const int part = lane & (LPR - 1);
     const ET* Qh = Q + bh * T * D + CS * part;
     const ET* Yh = DY + bh * T * D + CS * part;
     const float2* Sh = stats + bh * T;
     const uint8_t* pad = A.pad ? A.pad + (size_t)ck.b * T : nullptr;
-    const int t = ck.t0 + (lane >> 2);
+    const int t = ck.t0 + lane / LPR;
     const bool in = t < ck.nc;
     const int j = ck.c + t * ck.delta;
     const bool glob_j = in && A.n_g > 0 && is_global(A.gmap, j);
