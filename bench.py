@@ -154,9 +154,6 @@ def bench_backward(args, lf, W, metrics):
     import torch
     w = W.workload(args.workload)
     inp = W.make_inputs(w)
-    if inp.random_blocks is not None:
-        print("bench.py: the backward pass takes no random key blocks", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     dy = W.make_grad(inp, w.seed + 17).to(dev)
@@ -167,7 +164,7 @@ def bench_backward(args, lf, W, metrics):
 
     def call():
         lf.attn_bwd(q, k, v, dy, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm, out=outs,
-                    stream=stream, one_sided=inp.one_sided)
+                    stream=stream, one_sided=inp.one_sided, random_blocks=inp.random_blocks)
 
     for _ in range(args.warmup):
         call()
@@ -193,7 +190,7 @@ def bench_backward(args, lf, W, metrics):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     pairs = metrics.useful_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
-                                 one_sided=inp.one_sided)
+                                 one_sided=inp.one_sided, random_blocks=inp.random_blocks)
     flops = 10 * d * pairs
     tf = flops / (ms * 1e-3) / 1e12
     line = {
@@ -204,6 +201,7 @@ def bench_backward(args, lf, W, metrics):
         "data": "synthetic (seeded N(0,1) q/k/v/dy; no dataset, no weights)",
         "config": {"workload": w.name, "pass": "backward", "B": B, "H": H, "T": T, "d": d, "r": inp.r,
                    "one_sided": inp.one_sided, "dilation": inp.dilation, "n_global": len(set(inp.global_idx)),
+                   "n_rand": 0 if inp.random_blocks is None else int(inp.random_blocks.shape[2]),
                    "padded": inp.key_padding_mask is not None, "useful_pairs": pairs,
                    "timing": f"eager back-to-back calls after {n_untimed} untimed calls"},
         "roofline": {"bound": "alu", "kernel": "lfb rows + grows + cols + gcols (whole call)",

@@ -150,8 +150,7 @@ const char *lf_last_error(void);
  *
  * The pages give no backward pass; Longformer (ciallo.wiki) §5.2 only says
  * that training cost grows linearly with the length.  This is the
- * derivative of the forward of lf_attn_fwd_ex (without random key blocks)
- * over the same allowed pairs: with P_ij the softmax weights of row i,
+ * derivative of the forward of lf_attn_fwd_ex over the same allowed pairs: with P_ij the softmax weights of row i,
  * dP_ij = dy_i . v_j, D_i = sum_j P_ij dP_ij, dS_ij = P_ij (dP_ij - D_i):
  *     dq_i = sum_j dS_ij k_j / sqrt(d),   dk_j = sum_i dS_ij q_i / sqrt(d),
  *     dv_j = sum_i P_ij dy_i.
@@ -160,8 +159,8 @@ const char *lf_last_error(void);
  *   dy        DEVICE [B][H][T][d] of `dtype`: the gradient of the loss with
  *             respect to the forward's output.  Rows of padded queries are
  *             ignored (their output is zero whatever q holds).
- *   radius, one_sided, dilation, global_idx, n_global, key_padding_mask:
- *             as lf_attn_fwd_ex (radius is a HOST array of H radii).
+ *   radius, one_sided, rand_blocks, n_rand, dilation, global_idx, n_global,
+ *   key_padding_mask: as lf_attn_fwd_ex (radius, rand_blocks are HOST arrays).
  *   dq, dk, dv DEVICE [B][H][T][d] of `dtype`, written in full (zero rows
  *             at padded positions).  They must not overlap one another or
  *             the inputs.
@@ -172,13 +171,13 @@ const char *lf_last_error(void);
  *   call; LF_E_INVALID / LF_E_UNSUPPORTED enqueue nothing.  The call keeps
  *   a per-(device, stream) workspace (row statistics, 8 bytes per query
  *   row, and its tables); a change of shape, radii, dilation or globals
- *   during stream capture is LF_E_UNSUPPORTED.
+ *   or random key blocks during stream capture is LF_E_UNSUPPORTED.
  */
 lf_status_t lf_attn_bwd(const void *q, const void *k, const void *v, const void *dy,
                         int B, int H, int T, int d, const int32_t *radius, int one_sided,
-                        const int32_t *dilation, const int32_t *global_idx, int n_global,
-                        const uint8_t *key_padding_mask, void *dq, void *dk, void *dv,
-                        lf_dtype_t dtype, void *stream);
+                        const int32_t *rand_blocks, int n_rand, const int32_t *dilation,
+                        const int32_t *global_idx, int n_global, const uint8_t *key_padding_mask,
+                        void *dq, void *dk, void *dv, lf_dtype_t dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -50,7 +50,7 @@ def load():
     lib.lf_attn_fwd.restype = I
     lib.lf_attn_fwd_ex.argtypes = [P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, I, P]
     lib.lf_attn_fwd_ex.restype = I
-    lib.lf_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P, I, P, P, P, P, I, P]
+    lib.lf_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, P, P, I, P]
     lib.lf_attn_bwd.restype = I
     lib.lf_last_error.argtypes = []
     lib.lf_last_error.restype = ctypes.c_char_p
@@ -169,7 +169,7 @@ def attn_fwd(q, k, v, r, dilation: Optional[Sequence[int]] = None,
 
 
 def raw_bwd(q_ptr, k_ptr, v_ptr, dy_ptr, B, H, T, d, r, one_sided, dilation, global_idx, n_global, kpm_ptr,
-            dq_ptr, dk_ptr, dv_ptr, dtype, stream_ptr) -> int:
+            dq_ptr, dk_ptr, dv_ptr, dtype, stream_ptr, random_blocks=None) -> int:
     """lf_attn_bwd with raw integer device pointers; ``r`` is one radius or
     a list of H radii.  Returns the status."""
     lib = load()
@@ -181,17 +181,18 @@ def raw_bwd(q_ptr, k_ptr, v_ptr, dy_ptr, B, H, T, d, r, one_sided, dilation, glo
     g = None
     if global_idx is not None:
         g = (ctypes.c_int32 * max(1, len(global_idx)))(*[int(x) for x in global_idx])
+    rt, nr = _rand_table(random_blocks)
     return lib.lf_attn_bwd(q_ptr, k_ptr, v_ptr, dy_ptr, int(B), int(H), int(T), int(d), rad, int(bool(one_sided)),
-                           dil, g, int(n_global), kpm_ptr, dq_ptr, dk_ptr, dv_ptr, int(dtype), stream_ptr)
+                           rt, nr, dil, g, int(n_global), kpm_ptr, dq_ptr, dk_ptr, dv_ptr, int(dtype), stream_ptr)
 
 
 def attn_bwd(q, k, v, dy, r, dilation: Optional[Sequence[int]] = None,
              global_idx: Optional[Sequence[int]] = None, key_padding_mask=None, out=None, stream=None,
-             one_sided: bool = False):
+             one_sided: bool = False, random_blocks=None):
     """Gradients (dq, dk, dv) of the forward for the upstream gradient ``dy``,
-    torch tensors [B, H, T, 64] like q; same window, dilation, global and
-    padding arguments as ``attn_fwd`` (no random key blocks).  ``out`` may be
-    a tuple of three tensors like q to write into."""
+    torch tensors [B, H, T, 64] like q; the same window, dilation, global,
+    random-block and padding arguments as ``attn_fwd``.  ``out`` may be a
+    tuple of three tensors like q to write into."""
     import torch
 
     if q.dtype == torch.bfloat16:
@@ -229,7 +230,7 @@ def attn_bwd(q, k, v, dy, r, dilation: Optional[Sequence[int]] = None,
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     st = raw_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr(), B, H, T, d, r, one_sided, dilation,
                  gl if gl else None, len(gl), kpm_ptr, out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
-                 dt, sptr)
+                 dt, sptr, random_blocks)
     if st != LF_OK:
         raise LfError(st, last_error())
     return out

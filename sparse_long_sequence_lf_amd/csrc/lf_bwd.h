@@ -37,6 +37,11 @@ struct BwdArgs {
     float *gpart;                // [B*H*n_g][n_split][192]: a split's partial dq, dk, dv of a global position
     int B, H, T, n_g, one_sided;
     int n_split, split_len;      // global rows and columns: splits of split_len positions (256 x per-thread count)
+    // random key blocks of 64 (undilated heads only), or n_rand = 0
+    const int32_t *rtab;         // [H][ceil(T/64)][n_rand] key blocks per query block, ascending, -1 = none
+    const int32_t *inv_off;      // [H][ceil(T/64) + 1] CSR offsets into inv_list per key block
+    const int32_t *inv_list;     // query blocks that drew the key block, ascending
+    int n_rand;
 };
 
 }  // namespace lfk

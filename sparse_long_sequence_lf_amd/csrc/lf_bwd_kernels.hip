@@ -469,6 +469,20 @@ __global__ __launch_bounds__(256) void rows_kernel(const lfk::BwdArgs A, const E
         load_in(Vh + (size_t)j * D, vr);
         accum(kr, vr, live);
     }
+    if (A.n_rand > 0) {
+        // the random key blocks of this wave's query block (undilated, so
+        // class position = position and the 16 queries share one block);
+        // keys already in a query's window count there
+        const int32_t* rb = A.rtab + ((size_t)ck.h * ((T + 63) >> 6) + (ck.t0 >> 6)) * A.n_rand;
+        for (int e = 0; e < A.n_rand; e++) {
+            const int rho = rb[e];
+            if (rho < 0) break;   // the list is ascending, -1 after the last
+            ClassScan rnd(A, ck, pad, 64 * rho, min(64 * rho + 63, T - 1), lane);
+            stream_rows<PREFETCH<ET>>(rnd, 64 * rho, load_kv, [&](const KV<ET>& x, int tk) {
+                accum(x.k, x.v, live && !(tk - t >= -ck.r && tk - t <= ck.ra));
+            });
+        }
+    }
     const float lse = live ? m + lg2(l) : 0.f;
     const float Dl = live ? dn / l : 0.f;
     const float inv = live ? 1.f / l : 0.f;
@@ -546,6 +560,19 @@ __global__ __launch_bounds__(256) void cols_kernel(const lfk::BwdArgs A, const E
         load_in(Qh + (size_t)i * D, q);
         load_in(Yh + (size_t)i * D, dy);
         acc(q, dy, Sh[i], live);
+    }
+    if (A.n_rand > 0) {
+        // the query blocks that drew this wave's key block (undilated); a
+        // query whose window already holds the key counts there
+        const int kb = ck.t0 >> 6;
+        const int32_t* off = A.inv_off + (size_t)ck.h * (((T + 63) >> 6) + 1);
+        for (int e = off[kb]; e < off[kb + 1]; e++) {
+            const int beta = A.inv_list[e];
+            ClassScan rnd(A, ck, pad, 64 * beta, min(64 * beta + 63, T - 1), lane);
+            stream_rows<PREFETCH<ET>>(rnd, 64 * beta, load_qy, [&](const QY<ET>& x, int tq) {
+                acc(x.q, x.y, x.st, live && !(tq - t >= -ck.ra && tq - t <= ck.r));
+            });
+        }
     }
     if (in && !glob_j) {
         store_slice(DK + (bh * T + j) * D + CS * part, dk, 0.125f);

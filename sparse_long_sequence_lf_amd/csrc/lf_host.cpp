@@ -349,9 +349,10 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
 
 // Gradients (lf_attn_bwd): checks, the per-head tables, four launches.
 lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy, int B, int H, int T, int d,
-                     const int32_t *radius, int one_sided, const int32_t *dilation, const int32_t *global_idx,
-                     int n_global, const uint8_t *key_padding_mask, void *dq, void *dk, void *dv,
-                     lf_dtype_t dtype, void *stream) {
+                     const int32_t *radius, int one_sided, const int32_t *rand_blocks, int n_rand,
+                     const int32_t *dilation, const int32_t *global_idx, int n_global,
+                     const uint8_t *key_padding_mask, void *dq, void *dk, void *dv, lf_dtype_t dtype,
+                     void *stream) {
     if (!q || !k || !v || !dy || !dq || !dk || !dv)
         return fail(LF_E_INVALID, "q, k, v, dy, dq, dk and dv must be non-null");
     if (!radius) return fail(LF_E_INVALID, "radius must be a host array of H radii");
@@ -374,6 +375,20 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     for (int i = 0; i < n_global; i++)
         if (global_idx[i] < 0 || global_idx[i] >= T)
             return fail(LF_E_INVALID, "global_idx[%d] = %d outside [0, %d)", i, global_idx[i], T);
+    const long long nqb = cdiv(T, 64);
+    if (n_rand < 0) return fail(LF_E_INVALID, "n_rand = %d must be >= 0", n_rand);
+    if (n_rand > 0) {
+        if (!rand_blocks) return fail(LF_E_INVALID, "rand_blocks is NULL with n_rand = %d", n_rand);
+        if (n_rand > LF_MAX_RAND_BLOCKS)
+            return fail(LF_E_UNSUPPORTED, "n_rand = %d exceeds %d", n_rand, LF_MAX_RAND_BLOCKS);
+        for (int h = 0; h < H; h++)
+            if (dilation && dilation[h] != 1)
+                return fail(LF_E_UNSUPPORTED, "random key blocks need undilated heads (dilation[%d] = %d)", h,
+                            dilation[h]);
+        for (long long e = 0; e < (long long)H * nqb * n_rand; e++)
+            if (rand_blocks[e] < 0 || rand_blocks[e] >= nqb)
+                return fail(LF_E_INVALID, "rand_blocks[%lld] = %d outside [0, %lld)", e, rand_blocks[e], nqb);
+    }
     const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)dy | (uintptr_t)dq |
                            (uintptr_t)dk | (uintptr_t)dv) & 15u;
     if (mis) return fail(LF_E_INVALID, "q, k, v, dy, dq, dk and dv must be 16-byte aligned");
@@ -398,8 +413,37 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
         return fail(LF_E_UNSUPPORTED, "too many global rows");
 
     // table: rad[H] | dil[H] | head_chunk[H+1] | glob[n_g] | gmap[ceil(T/32)]
+    //        | rtab[H][nqb][n_rand] | inv_off[H][nqb+1] | inv_list
     const size_t o_dil = H, o_hc = 2 * (size_t)H, o_glob = o_hc + H + 1, o_gmap = o_glob + G.size();
-    std::vector<uint32_t> tab(o_gmap + (size_t)cdiv(T, 32), 0u);
+    const size_t o_rtab = o_gmap + (size_t)cdiv(T, 32);
+    const size_t n_rt = n_rand > 0 ? (size_t)H * nqb * n_rand : 0;
+    const size_t o_off = o_rtab + n_rt, n_off = n_rand > 0 ? (size_t)H * (nqb + 1) : 0;
+    const size_t o_inv = o_off + n_off;
+    std::vector<uint32_t> tab(o_inv, 0u);
+    if (n_rand > 0) {
+        // each query block's draws sorted, duplicates dropped (-1 after the
+        // last), and per key block the query blocks that drew it, ascending
+        std::vector<int32_t> row(n_rand);
+        std::vector<std::vector<int32_t>> inv((size_t)nqb);
+        for (int h = 0; h < H; h++) {
+            for (auto &x : inv) x.clear();
+            for (long long qb = 0; qb < nqb; qb++) {
+                const size_t base = ((size_t)h * nqb + qb) * n_rand;
+                std::copy(rand_blocks + base, rand_blocks + base + n_rand, row.begin());
+                std::sort(row.begin(), row.end());
+                const size_t u = std::unique(row.begin(), row.end()) - row.begin();
+                for (int e = 0; e < n_rand; e++) tab[o_rtab + base + e] = (uint32_t)(e < (int)u ? row[e] : -1);
+                for (size_t e = 0; e < u; e++) inv[row[e]].push_back((int32_t)qb);
+            }
+            size_t at = tab.size() - o_inv;
+            for (long long kb = 0; kb < nqb; kb++) {
+                tab[o_off + (size_t)h * (nqb + 1) + kb] = (uint32_t)at;
+                for (int32_t qb : inv[kb]) tab.push_back((uint32_t)qb);
+                at += inv[kb].size();
+            }
+            tab[o_off + (size_t)h * (nqb + 1) + nqb] = (uint32_t)at;
+        }
+    }
     long long chunks = 0;
     for (int h = 0; h < H; h++) {
         const int delta = dilation ? dilation[h] : 1;
@@ -467,6 +511,10 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     A.split_len = split_len;
     A.gstat = n_rec > 0 ? (float4 *)w->bwd_gpart.ptr : nullptr;
     A.gpart = n_rec > 0 ? (float *)((char *)w->bwd_gpart.ptr + gstat_bytes) : nullptr;
+    A.n_rand = n_rand;
+    A.rtab = n_rand > 0 ? (const int32_t *)dt + o_rtab : nullptr;
+    A.inv_off = n_rand > 0 ? (const int32_t *)dt + o_off : nullptr;
+    A.inv_list = n_rand > 0 ? (const int32_t *)dt + o_inv : nullptr;
     const void *t[7] = {q, k, v, dy, dq, dk, dv};
     hipError_t e = lfk_bwd_launch(&A, t, dtype == LF_BF16, stream);
     if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -476,12 +524,13 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
 }  // namespace
 
 extern "C" lf_status_t lf_attn_bwd(const void *q, const void *k, const void *v, const void *dy, int B, int H,
-                                   int T, int d, const int32_t *radius, int one_sided, const int32_t *dilation,
-                                   const int32_t *global_idx, int n_global, const uint8_t *key_padding_mask,
-                                   void *dq, void *dk, void *dv, lf_dtype_t dtype, void *stream) {
+                                   int T, int d, const int32_t *radius, int one_sided, const int32_t *rand_blocks,
+                                   int n_rand, const int32_t *dilation, const int32_t *global_idx, int n_global,
+                                   const uint8_t *key_padding_mask, void *dq, void *dk, void *dv, lf_dtype_t dtype,
+                                   void *stream) {
     g_err.clear();
-    return attn_bwd(q, k, v, dy, B, H, T, d, radius, one_sided, dilation, global_idx, n_global, key_padding_mask,
-                    dq, dk, dv, dtype, stream);
+    return attn_bwd(q, k, v, dy, B, H, T, d, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
+                    n_global, key_padding_mask, dq, dk, dv, dtype, stream);
 }
 
 extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T,

@@ -203,6 +203,8 @@ DY, DQ, DK, DV = 0x50000000, 0x60000000, 0x70000000, 0x80000000
     ("misaligned dk", dict(dk=DK + 2), lf.LF_E_INVALID),
     ("dq overlaps q", dict(dq=Q + 64), lf.LF_E_INVALID),
     ("dk overlaps dv", dict(dk=DV + 16), lf.LF_E_INVALID),
+    ("random block out of range", dict(dil=[1, 1], rb=[0, 2, 1, 1, 0, 0, 1, 0]), lf.LF_E_INVALID),
+    ("random blocks on a dilated head", dict(rb=[0, 1, 1, 1, 0, 0, 1, 0]), lf.LF_E_UNSUPPORTED),
 ])
 def test_bwd_rejects_bad_arguments(lib, name, kw, status):
     a = dict(q=Q, k=K, v=V, dy=DY, B=1, H=2, T=128, d=64, r=[8, 8], one=0, dil=[1, 2], g=[0], ng=1, kpm=None,
@@ -211,12 +213,16 @@ def test_bwd_rejects_bad_arguments(lib, name, kw, status):
     rad = (ctypes.c_int32 * 2)(*a["r"])
     dil = (ctypes.c_int32 * 2)(*a["dil"])
     g = (ctypes.c_int32 * 1)(*a["g"])
-    st = lib.lf_attn_bwd(a["q"], a["k"], a["v"], a["dy"], a["B"], a["H"], a["T"], a["d"], rad, a["one"], dil, g,
-                         a["ng"], a["kpm"], a["dq"], a["dk"], a["dv"], a["dtype"], None)
+    rb = a.get("rb")
+    rt = None if rb is None else (ctypes.c_int32 * len(rb))(*rb)
+    nr = 0 if rb is None else len(rb) // (2 * 2)
+    st = lib.lf_attn_bwd(a["q"], a["k"], a["v"], a["dy"], a["B"], a["H"], a["T"], a["d"], rad, a["one"], rt, nr,
+                         dil, g, a["ng"], a["kpm"], a["dq"], a["dk"], a["dv"], a["dtype"], None)
     assert st == status, (name, st, lf.last_error())
     assert lf.last_error() != ""
 
 
 def test_bwd_null_radius_rejected(lib):
-    st = lib.lf_attn_bwd(Q, K, V, DY, 1, 2, 128, 64, None, 0, None, None, 0, None, DQ, DK, DV, lf.LF_BF16, None)
+    st = lib.lf_attn_bwd(Q, K, V, DY, 1, 2, 128, 64, None, 0, None, 0, None, None, 0, None, DQ, DK, DV, lf.LF_BF16,
+                         None)
     assert st == lf.LF_E_INVALID and "radius" in lf.last_error()

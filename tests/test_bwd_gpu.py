@@ -26,7 +26,8 @@ def gpu_bwd(inp, dy):
     dev = torch.device("cuda:0")
     kpm = None if inp.key_padding_mask is None else inp.key_padding_mask.to(dev)
     out = lf.attn_bwd(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), dy.to(dev), inp.r, inp.dilation,
-                      inp.global_idx, key_padding_mask=kpm, one_sided=inp.one_sided)
+                      inp.global_idx, key_padding_mask=kpm, one_sided=inp.one_sided,
+                      random_blocks=inp.random_blocks)
     torch.cuda.synchronize()
     return [o.float().cpu().double().numpy() for o in out]
 
@@ -34,7 +35,7 @@ def gpu_bwd(inp, dy):
 def check(inp, dy, dt, label):
     got = gpu_bwd(inp, dy)
     ref = oracle.bwd(inp.q, inp.k, inp.v, dy, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
-                     one_sided=inp.one_sided)
+                     one_sided=inp.one_sided, random_blocks=inp.random_blocks)
     bad = []
     for name, a, b in zip(("dq", "dk", "dv"), got, ref):
         scale = max(1.0, float(np.max(np.abs(b)))) if b.size else 1.0
@@ -67,6 +68,25 @@ def test_bwd_random_cases(T):
             check(inp, dy, dt, label)
 
 
+@pytest.mark.parametrize("n_rand", [1, 3])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 300, 700])
+def test_bwd_random_blocks(T, n_rand):
+    # random key blocks that overlap the window, duplicated draws, globals
+    # inside drawn blocks, padding, both window forms, one radius per head
+    for dt in ("f32", "bf16"):
+        for seed, pad in enumerate(("none", "right", "random")):
+            base = W.random_case(seed * 104729 + T + n_rand, B=2, H=3, T=T, dtype=dt, pad=pad, n_rand=n_rand)
+            rng = np.random.default_rng(seed * 17 + T)
+            one = bool(seed % 2)
+            r = [int(x) for x in rng.integers(0, 100, size=3)] if seed == 2 else int(rng.integers(0, 100))
+            inp = W.Inputs(base.q, base.k, base.v, r, base.dilation, base.global_idx, base.lengths,
+                           base.key_padding_mask, one_sided=one, random_blocks=base.random_blocks)
+            dy = W.make_grad(inp, 300 + seed + T)
+            label = f"T={T} n_rand={n_rand} dt={dt} pad={pad} r={r} one_sided={one} G={inp.global_idx}"
+            print("case " + label, flush=True)
+            check(inp, dy, dt, label)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_bwd_named_edge_cases(dt):
     base = W.random_case(5, B=2, H=2, T=200, dtype=dt, pad="none")
@@ -92,6 +112,7 @@ BWD_CASES = {
     "bf16-b4h16t16384-r512-g8-pad": dict(T=2100, H=2),
     "bf16-b1h12t4096-r256-g1-onesided": dict(T=2048),
     "bf16-b1h12t4096-rhead-g1": dict(T=2048),
+    "bf16-b1h12t4096-r96-g2-rand3": dict(T=2048),
 }
 
 
