@@ -31,7 +31,9 @@ struct BwdArgs {
     const int32_t *glob;         // [n_g] distinct globals, ascending
     const int32_t *rad;          // [H] window radius per head (clamped to T)
     const int32_t *dil;          // [H] stride per head
-    const int32_t *head_chunk;   // [H+1] prefix over heads of the class chunks (LFB_ROWS_PER_WAVE positions)
+    const int32_t *head_chunk;   // [H+1] prefix of the class chunks (LFB_ROWS_PER_WAVE positions) over the heads
+                                 // in the order hord lists them
+    const int32_t *hord;         // [H] heads by decreasing radius: the longest waves are dealt out first
     void *stats;                 // float2 [B*H][T]: (log2-sum-exp of the scaled scores, D_i)
     float4 *gstat;               // [B*H*n_g][n_split]: a split's (max, sum, sum of p dP) of a global row
     float *gpart;                // [B*H*n_g][n_split][192]: a split's partial dq, dk, dv of a global position

@@ -276,9 +276,10 @@ __device__ __forceinline__ bool decode(const lfk::BwdArgs& A, long long task, Ch
     if (task >= (long long)A.B * per_b) return false;
     k.b = (int)(task / per_b);
     int rem = (int)(task - (long long)k.b * per_b);
-    int h = 0;
-    while (h + 1 < A.H && A.head_chunk[h + 1] <= rem) h++;
-    rem -= A.head_chunk[h];
+    int o = 0;
+    while (o + 1 < A.H && A.head_chunk[o + 1] <= rem) o++;
+    rem -= A.head_chunk[o];
+    const int h = A.hord[o];
     k.h = h;
     const int delta = A.dil[h];
     const int T = A.T;

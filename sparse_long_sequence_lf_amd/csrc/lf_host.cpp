@@ -412,9 +412,10 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     if ((long long)B * H * G.size() >= (1LL << 31))
         return fail(LF_E_UNSUPPORTED, "too many global rows");
 
-    // table: rad[H] | dil[H] | head_chunk[H+1] | glob[n_g] | gmap[ceil(T/32)]
+    // table: rad[H] | dil[H] | head_chunk[H+1] | hord[H] | glob[n_g] | gmap[ceil(T/32)]
     //        | rtab[H][nqb][n_rand] | inv_off[H][nqb+1] | inv_list
-    const size_t o_dil = H, o_hc = 2 * (size_t)H, o_glob = o_hc + H + 1, o_gmap = o_glob + G.size();
+    const size_t o_dil = H, o_hc = 2 * (size_t)H, o_ord = o_hc + H + 1, o_glob = o_ord + H;
+    const size_t o_gmap = o_glob + G.size();
     const size_t o_rtab = o_gmap + (size_t)cdiv(T, 32);
     const size_t n_rt = n_rand > 0 ? (size_t)H * nqb * n_rand : 0;
     const size_t o_off = o_rtab + n_rt, n_off = n_rand > 0 ? (size_t)H * (nqb + 1) : 0;
@@ -444,12 +445,18 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
             tab[o_off + (size_t)h * (nqb + 1) + nqb] = (uint32_t)at;
         }
     }
+    // waves are dealt out head by head, the heads of the largest radius first
+    std::vector<int> hord(H);
+    for (int h = 0; h < H; h++) hord[h] = h;
+    std::stable_sort(hord.begin(), hord.end(), [&](int a, int b) { return radius[a] > radius[b]; });
     long long chunks = 0;
-    for (int h = 0; h < H; h++) {
+    for (int o = 0; o < H; o++) {
+        const int h = hord[o];
         const int delta = dilation ? dilation[h] : 1;
         tab[h] = (uint32_t)std::min(radius[h], T);   // |i - j| < T: larger radii change nothing
         tab[o_dil + h] = (uint32_t)delta;
-        tab[o_hc + h] = (uint32_t)chunks;
+        tab[o_hc + o] = (uint32_t)chunks;
+        tab[o_ord + o] = (uint32_t)h;
         const long long qq = T / delta, rm = T % delta;
         chunks += rm * cdiv(qq + 1, LFB_ROWS_PER_WAVE) + (delta - rm) * cdiv(qq, LFB_ROWS_PER_WAVE);
     }
@@ -505,6 +512,7 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     A.rad = (const int32_t *)dt;
     A.dil = (const int32_t *)dt + o_dil;
     A.head_chunk = (const int32_t *)dt + o_hc;
+    A.hord = (const int32_t *)dt + o_ord;
     A.stats = w->bwd_stats.ptr;
     A.B = B; A.H = H; A.T = T; A.n_g = (int)G.size(); A.one_sided = one_sided;
     A.n_split = n_split;
