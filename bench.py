@@ -232,7 +232,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build measures one GPU only; --gpus must be 1 "
-              "(the per-(batch, head) sharding across GPUs is described in DESIGN.md, not built)",
+              "(sharding the (batch, head) pairs across GPUs is not built)",
               file=sys.stderr)
         sys.exit(2)
 
