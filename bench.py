@@ -231,7 +231,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only; --gpus must be 1 "
+        print("bench.py measures one GPU only; --gpus must be 1 "
               "(sharding the (batch, head) pairs across GPUs is not built)",
               file=sys.stderr)
         sys.exit(2)

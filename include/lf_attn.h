@@ -43,12 +43,12 @@ typedef enum {
 typedef enum {
     LF_OK = 0,
     LF_E_INVALID = 1,     /* an argument breaks the contract below; nothing was enqueued */
-    LF_E_UNSUPPORTED = 2, /* valid but outside what this build implements; nothing enqueued */
+    LF_E_UNSUPPORTED = 2, /* valid but outside what the library implements; nothing enqueued */
     LF_E_NOMEM = 3,       /* the workspace could not be allocated; nothing enqueued */
     LF_E_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } lf_status_t;
 
-/* Limits of this build (LF_E_UNSUPPORTED beyond them). */
+/* Limits of the library (LF_E_UNSUPPORTED beyond them). */
 #define LF_HEAD_DIM 64        /* d must equal this */
 #define LF_MAX_HEADS 128      /* H */
 #define LF_MAX_GLOBALS 512    /* distinct global positions */
