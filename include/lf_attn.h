@@ -164,8 +164,10 @@ const char *lf_last_error(void);
  *   dq, dk, dv DEVICE [B][H][T][d] of `dtype`, written in full (zero rows
  *             at padded positions).  They must not overlap one another or
  *             the inputs.
- *   Arithmetic in fp32 (bf16 inputs are widened exactly); results rounded
- *   to `dtype` (bf16 to nearest even).  Every result is written by exactly
+ *   Arithmetic in fp32 (bf16 inputs are widened exactly), except that with
+ *   bf16 inputs the sums over queries that make dk and dv take each
+ *   query's weight rounded to bf16; results rounded to `dtype` (bf16 to
+ *   nearest even).  Every result is written by exactly
  *   one thread, without atomics: repeated calls give the same bits.
  *   Ownership and errors as lf_attn_fwd: all checks run before any HIP
  *   call; LF_E_INVALID / LF_E_UNSUPPORTED enqueue nothing.  The call keeps

@@ -232,6 +232,25 @@ __device__ __forceinline__ void axpy_in(Slice& acc, float a, const In<ET>& x) {
     }
 }
 
+// acc += a * x for a bf16 row x without widening it: each channel pair takes
+// two v_dot2_f32_bf16 against (a, 0) and (0, a), a rounded to bf16 (a
+// relative error of at most 2^-9 per term; fp32 rows take plain FMAs).
+template <typename ET>
+__device__ __forceinline__ void axpy_w(Slice& acc, float a, const In<ET>& x) {
+    if constexpr (sizeof(ET) == 2) {
+        const uint32_t ab = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a);
+        const bf16x2_t lo = __builtin_bit_cast(bf16x2_t, ab), hi = __builtin_bit_cast(bf16x2_t, ab << 16);
+#pragma unroll
+        for (int e = 0; e < CS / 2; e++) {
+            const bf16x2_t xe = __builtin_bit_cast(bf16x2_t, x.w[e]);
+            acc.x[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(xe, lo, acc.x[2 * e], false);
+            acc.x[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(xe, hi, acc.x[2 * e + 1], false);
+        }
+    } else {
+        axpy_in(acc, a, x);
+    }
+}
+
 // Sum over the LPR lanes of a row (an aligned group), in every lane of it.
 __device__ __forceinline__ float quad_sum(float x) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lane ^ 1
@@ -536,8 +555,8 @@ __global__ __launch_bounds__(256) void cols_kernel(const lfk::BwdArgs A, const E
         const float s = quad_sum(dot_in(q, kr)) * sc;
         const float dp = quad_sum(dot_in(dy, vr));
         const float p = on ? ex2(s - st.x) : 0.f;
-        axpy_in(dv, p, dy);
-        axpy_in(dk, p * (dp - st.y), q);
+        axpy_w(dv, p, dy);
+        axpy_w(dk, p * (dp - st.y), q);
     };
     // query i (class position tq) holds key position t in its window iff
     // tq - t lies in [-ra, r]
