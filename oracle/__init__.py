@@ -39,6 +39,8 @@ def open_library(path):
     lib.lf_oracle_neighbours2.restype = I
     lib.lf_oracle_count_pairs2.argtypes = [I, I, I, I, P, I, P, I, P, P, I, P]
     lib.lf_oracle_count_pairs2.restype = LL
+    lib.lf_oracle_fwd_lse.argtypes = [P, P, P, I, I, I, I, I, P, I, P, I, P, P, I, P, P, P, I]
+    lib.lf_oracle_fwd_lse.restype = I
     lib.lf_oracle_bwd.argtypes = [P, P, P, P, I, I, I, I, I, P, I, P, I, P, P, I, P, P, P, P, I]
     lib.lf_oracle_bwd.restype = I
     return lib
@@ -123,6 +125,29 @@ def fwd(q, k, v, r, dilation=None, global_idx=None, key_padding_mask=None, n_thr
     if nt < 0:
         raise ValueError("oracle rejected its arguments")
     return (out, nt) if return_threads else out
+
+
+def fwd_lse(q, k, v, r, dilation=None, global_idx=None, key_padding_mask=None, n_threads=0, lib=None,
+            one_sided=False, random_blocks=None):
+    """The forward and each row's log-sum-exp (natural log of its softmax
+    denominator over N(i); -inf for a padded query): (out, lse), numpy
+    float64 [B][H][T][d] and [B][H][T]."""
+    lib = lib or _load()
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    B, H, T, d = qf.shape
+    r0, rad = _radius(r, H)
+    rb, nr = _rand_blocks(random_blocks, H, T)
+    dil = _i32(dilation)
+    g = _i32(global_idx if global_idx is not None else [])
+    pad = _u8(key_padding_mask)
+    out = np.zeros((B, H, T, d), dtype=np.float64)
+    lse = np.zeros((B, H, T), dtype=np.float64)
+    nt = lib.lf_oracle_fwd_lse(_ptr(qf), _ptr(kf), _ptr(vf), B, H, T, d, r0, _ptr(rad), int(bool(one_sided)),
+                               _ptr(rb), nr, _ptr(dil), _ptr(g), int(g.size), _ptr(pad), _ptr(out), _ptr(lse),
+                               int(n_threads))
+    if nt < 0:
+        raise ValueError("oracle rejected its arguments")
+    return out, lse
 
 
 def bwd(q, k, v, dy, r, dilation=None, global_idx=None, key_padding_mask=None, n_threads=0,

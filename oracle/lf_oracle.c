@@ -181,8 +181,9 @@ static int neighbours(int T, int r, int delta, int one_sided, const gset_t *G,
 /* One output row: softmax over N(i) of q_i . k_j / sqrt(d), weights on v. */
 
 static void attend_row(const float *qi, const float *K, const float *V, int d,
-                       const int *nb, int n, double *s, double *yi) {
+                       const int *nb, int n, double *s, double *yi, double *lse) {
     for (int c = 0; c < d; c++) yi[c] = 0.0;
+    if (lse) *lse = -INFINITY;
     if (n == 0) return;
     const double inv_sqrt_d = 1.0 / sqrt((double)d);
     double m = -INFINITY;
@@ -198,6 +199,8 @@ static void attend_row(const float *qi, const float *K, const float *V, int d,
         s[t] = exp(s[t] - m);
         l += s[t];
     }
+    /* log of the softmax denominator: log sum_j exp(s_j) = m + log l */
+    if (lse) *lse = m + log(l);
     for (int t = 0; t < n; t++) {
         const float *vj = V + (size_t)nb[t] * d;
         double w = s[t];
@@ -222,6 +225,7 @@ typedef struct {
     const long long *rows;  /* NULL: all rows in order */
     long long n_rows;
     double *out;
+    double *lse;            /* [n_rows] log-sum-exp of each row's scores, or NULL */
     int n_threads, tid;
     int err;
 } job_t;
@@ -249,7 +253,7 @@ static void *worker(void *arg) {
             int n = neighbours(jb->T, rh, delta, jb->one_sided, jb->G, padrow, i, nb, rb, jb->n_rand, mark);
             const size_t base = (size_t)bh * jb->T * jb->d;
             attend_row(jb->q + base + (size_t)i * jb->d, jb->k + base, jb->v + base,
-                       jb->d, nb, n, s, jb->out + (size_t)e * jb->d);
+                       jb->d, nb, n, s, jb->out + (size_t)e * jb->d, jb->lse ? jb->lse + e : NULL);
         }
     }
     free(nb);
@@ -296,7 +300,7 @@ static int check_args(int B, int H, int T, int d, int r, const int *rad, int one
 static int run(const float *q, const float *k, const float *v, int B, int H, int T, int d, int r,
                const int *rad, int one_sided, const int *rblk, int n_rand, const int *dil,
                const int *gidx, int ng, const unsigned char *pad, const long long *rows,
-               long long n_rows, double *out, int n_threads) {
+               long long n_rows, double *out, double *lse, int n_threads) {
     if (check_args(B, H, T, d, r, rad, one_sided, dil)) return -1;
     if (check_rand(H, T, dil, rblk, n_rand)) return -1;
     if (ng < 0 || (ng > 0 && !gidx)) return -1;
@@ -309,7 +313,7 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     if (!jobs || !th) { free(jobs); free(th); free(G.pos); return -1; }
     int err = 0;
     for (int t = 0; t < n_threads; t++) {
-        job_t j = {q, k, v, B, H, T, d, r, rad, one_sided, rblk, n_rand, dil, &G, pad, rows, n_rows, out,
+        job_t j = {q, k, v, B, H, T, d, r, rad, one_sided, rblk, n_rand, dil, &G, pad, rows, n_rows, out, lse,
                    n_threads, t, 0};
         jobs[t] = j;
     }
@@ -429,7 +433,7 @@ int lf_oracle_bwd(const float *q, const float *k, const float *v, const float *d
     if (!jobs || !th) { free(jobs); free(th); free(G.pos); return -1; }
     for (int t = 0; t < n_threads; t++) {
         job_t j = {q, k, v, B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation, &G,
-                   key_padding_mask, NULL, 0, NULL, n_threads, t, 0};
+                   key_padding_mask, NULL, 0, NULL, NULL, n_threads, t, 0};
         jobs[t].base = j;
         jobs[t].dy = dy;
         jobs[t].dq = dq;
@@ -459,7 +463,19 @@ int lf_oracle_fwd2(const float *q, const float *k, const float *v, int B, int H,
                    const unsigned char *key_padding_mask, double *out, int n_threads) {
     long long n = (long long)B * H * T;
     return run(q, k, v, B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
-               n_global, key_padding_mask, NULL, n, out, n_threads);
+               n_global, key_padding_mask, NULL, n, out, NULL, n_threads);
+}
+
+/* The same forward, also writing lse[(b*H + h)*T + i] = log sum_{j in N(i)}
+ * exp(q_i . k_j / sqrt(d)), the natural log of row i's softmax denominator
+ * (-inf for a padded query, whose set is empty). */
+int lf_oracle_fwd_lse(const float *q, const float *k, const float *v, int B, int H, int T, int d,
+                      int r, const int *radius, int one_sided, const int *rand_blocks, int n_rand,
+                      const int *dilation, const int *global_idx, int n_global,
+                      const unsigned char *key_padding_mask, double *out, double *lse, int n_threads) {
+    long long n = (long long)B * H * T;
+    return run(q, k, v, B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
+               n_global, key_padding_mask, NULL, n, out, lse, n_threads);
 }
 
 int lf_oracle_fwd(const float *q, const float *k, const float *v, int B, int H, int T, int d,
@@ -478,7 +494,7 @@ int lf_oracle_rows2(const float *q, const float *k, const float *v, int B, int H
     for (long long e = 0; e < n_rows; e++)
         if (rows[e] < 0 || rows[e] >= (long long)B * H * T) return -1;
     return run(q, k, v, B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
-               n_global, key_padding_mask, rows, n_rows, out_rows, n_threads);
+               n_global, key_padding_mask, rows, n_rows, out_rows, NULL, n_threads);
 }
 
 int lf_oracle_rows(const float *q, const float *k, const float *v, int B, int H, int T, int d,

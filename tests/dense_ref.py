@@ -64,3 +64,26 @@ def dense_masked_attention(q, k, v, r, dilation=None, globals_=(), pad=None, one
             y[~rows_ok] = 0.0
             out[b, h] = y
     return out
+
+
+def dense_masked_lse(q, k, r, dilation=None, globals_=(), pad=None, one_sided=False, rand_blocks=None):
+    """log sum_{j allowed} exp(q_i . k_j / sqrt(d)) per row from the same
+    T x T mask, by numpy's logaddexp reduction; -inf for a padded query and
+    for a row with no allowed key."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, T, d = q.shape
+    out = np.full((B, H, T), -np.inf)
+    for b in range(B):
+        pad_row = None if pad is None else np.asarray(pad[b]).astype(bool)
+        for h in range(H):
+            delta = 1 if dilation is None else int(dilation[h])
+            rh = int(r) if np.isscalar(r) else int(r[h])
+            A = allowed_matrix(T, rh, delta, globals_, pad_row, one_sided,
+                               None if rand_blocks is None else rand_blocks[h])
+            S = np.where(A, q[b, h] @ k[b, h].T / np.sqrt(d), -np.inf)
+            lse = np.logaddexp.reduce(S, axis=1) if T else np.zeros(0)
+            if pad_row is not None:
+                lse[pad_row] = -np.inf
+            out[b, h] = lse
+    return out

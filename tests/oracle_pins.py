@@ -29,6 +29,11 @@ one of them.  The pins:
   blocks of 64): the brute force with the blocks added to each row's mask,
   an exact count for r = 0, and every block drawn for every query block
   giving dense attention.
+* the log-sum-exp of each row (the statistic a backward pass rebuilds the
+  weights from): the brute force's logaddexp over the allowed scores of its
+  mask, log |N(i)| for q = 0 (every score zero), and the dense limit equal to
+  torch.logsumexp of the scaled scores; the forward written with it,
+  sum_j exp(s_ij - lse_i) v_j, equals the forward itself;
 * gradients (the derivative of the forward map; the pages give no backward
   pass): torch float64 autograd through the dense brute force, central
   finite differences of the oracle's own forward, and the sum rules
@@ -39,7 +44,7 @@ import numpy as np
 import torch
 
 import oracle
-from dense_ref import allowed_matrix, dense_masked_attention
+from dense_ref import allowed_matrix, dense_masked_attention, dense_masked_lse
 
 
 def _rand(seed, B, H, T, d):
@@ -437,7 +442,56 @@ def check_grad_sum_rules(lib=None):
                     assert not np.any(dq[b, h][pr]) and not np.any(dk[b, h][pr]) and not np.any(dv[b, h][pr])
 
 
-ALL_CHECKS = [check_dense_bruteforce, check_closed_form_counts, check_neighbour_sets,
+# --------------------------------------------------------------------------
+# log-sum-exp of each row
+
+def check_lse(lib=None):
+    # against the dense brute force, every kind of case
+    for c in random_cases(20, seed0=5):
+        y, lse = oracle.fwd_lse(c["q"], c["k"], c["v"], c["r"], c["dil"], c["G"], c["pad"], lib=lib,
+                                one_sided=c["one"], random_blocks=c["rb"])
+        ref = dense_masked_lse(c["q"].numpy(), c["k"].numpy(), c["r"], c["dil"], c["G"], c["pad"], c["one"],
+                               c["rb"])
+        fin = np.isfinite(ref)
+        assert np.array_equal(fin, np.isfinite(lse)), "lse: -inf rows differ from the brute force"
+        assert np.max(np.abs(lse[fin] - ref[fin]), initial=0.0) <= 1e-12
+        y2 = oracle.fwd(c["q"], c["k"], c["v"], c["r"], c["dil"], c["G"], c["pad"], lib=lib, one_sided=c["one"],
+                        random_blocks=c["rb"])
+        assert np.array_equal(y, y2)
+        # the forward rebuilt from lse: y_i = sum_j exp(s_ij - lse_i) v_j over the mask
+        B, H, T, d = c["q"].shape
+        for b in range(B):
+            pad_row = None if c["pad"] is None else np.asarray(c["pad"][b]).astype(bool)
+            for h in range(H):
+                delta = 1 if c["dil"] is None else int(c["dil"][h])
+                rh = int(c["r"]) if np.isscalar(c["r"]) else int(c["r"][h])
+                A = allowed_matrix(T, rh, delta, c["G"], pad_row, c["one"],
+                                   None if c["rb"] is None else c["rb"][h])
+                S = c["q"][b, h].double().numpy() @ c["k"][b, h].double().numpy().T / np.sqrt(d)
+                lrow = np.where(np.isfinite(lse[b, h]), lse[b, h], 0.0)[:, None]
+                P = np.where(A, np.exp(S - lrow), 0.0)
+                if pad_row is not None:
+                    P[pad_row] = 0.0
+                want = P @ c["v"][b, h].double().numpy()
+                assert np.max(np.abs(want - y[b, h]), initial=0.0) <= 1e-12
+    # q = 0: every score is zero, so lse_i = log |N(i)|
+    g = torch.Generator().manual_seed(5)
+    for T, r, dil, G in [(40, 3, [1, 2], [0, 17]), (100, 9, [3, 1], []), (7, 20, [1, 1], [6])]:
+        k, v = [torch.randn(1, 2, T, 8, generator=g) for _ in range(2)]
+        q0 = torch.zeros_like(k)
+        _, lse = oracle.fwd_lse(q0, k, v, r, dil, G, None, lib=lib)
+        for h in range(2):
+            cnt = allowed_matrix(T, r, dil[h], G, None).sum(axis=1)
+            assert np.max(np.abs(lse[0, h] - np.log(cnt))) <= 1e-12
+    # r >= T - 1, no padding: the dense limit is torch.logsumexp of the scaled scores
+    for T in (1, 9, 130):
+        q, k, v = [torch.randn(2, 3, T, 16, generator=g) for _ in range(3)]
+        _, lse = oracle.fwd_lse(q, k, v, T, None, [], None, lib=lib)
+        ref = torch.logsumexp(q.double() @ k.double().transpose(-1, -2) / 4.0, dim=-1).numpy()
+        assert np.max(np.abs(lse - ref)) <= 1e-12
+
+
+ALL_CHECKS = [check_dense_bruteforce, check_lse, check_closed_form_counts, check_neighbour_sets,
               check_invariants, check_identity_and_dense_limits, check_window_exclusivity,
               check_dilation_split, check_rows_entry_point, check_grad_autograd,
               check_grad_finite_differences, check_grad_sum_rules]

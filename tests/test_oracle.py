@@ -43,6 +43,9 @@ MUTANTS = [
     ("random_block_shifted", "const int j0 = rb[e] * RAND_BLOCK;", "const int j0 = rb[e] * RAND_BLOCK + 1;"),
     ("random_padded_kept", "if (!(pad && pad[j])) mark[j] = 1;", "mark[j] = 1;"),
     ("random_block_of_wrong_query", "rblk + (size_t)(i / RAND_BLOCK) * n_rand", "rblk + (size_t)(i / RAND_BLOCK / 2) * n_rand"),
+    ("lse_without_max", "if (lse) *lse = m + log(l);", "if (lse) *lse = log(l);"),
+    ("lse_base_two", "if (lse) *lse = m + log(l);", "if (lse) *lse = m + log2(l);"),
+    ("lse_of_padded_row_zero", "if (lse) *lse = -INFINITY;", "if (lse) *lse = 0.0;"),
     ("grad_no_D_term", "D += s[t] * dp;", ""),
     ("grad_dk_unscaled", "dK[(size_t)j * d + c] += ds * inv_sqrt_d * (double)qi[c];",
      "dK[(size_t)j * d + c] += ds * (double)qi[c];"),
