@@ -36,7 +36,11 @@ extern "C" {
 
 /* Element type of q, k, v and out. */
 typedef enum {
-    LF_F32 = 0,  /* IEEE binary32; products use a hi/lo bf16 split with fp32 accumulation */
+    LF_F32 = 0,  /* IEEE binary32.  Each product is taken on the bf16 matrix cores from
+                    three bf16 parts per operand (hi + mid + lo carry all 24 significand
+                    bits), adding the six part products down to 2^-16 of the leading
+                    one, with fp32 accumulation: the error stays that of fp32 arithmetic
+                    (scores of a few hundred included). */
     LF_BF16 = 1  /* bfloat16; fp32 accumulation; out rounded to nearest-even */
 } lf_dtype_t;
 
@@ -49,7 +53,8 @@ typedef enum {
 } lf_status_t;
 
 /* Limits of the library (LF_E_UNSUPPORTED beyond them). */
-#define LF_HEAD_DIM 64        /* d must equal this */
+#define LF_HEAD_DIM 64        /* d of lf_attn_bwd; the forward takes any of LF_FWD_HEAD_DIMS */
+#define LF_FWD_HEAD_DIMS {32, 64, 128}
 #define LF_MAX_HEADS 128      /* H */
 #define LF_MAX_GLOBALS 512    /* distinct global positions */
 #define LF_MAX_SEQ ((1 << 24) - 1)  /* T: one head of fp32 K or V stays below 4 GiB */
@@ -63,7 +68,9 @@ typedef enum {
  *             `dtype`, 16-byte aligned.  Read only.
  *   B, H, T   batch, heads, sequence length; each >= 1 (T <= LF_MAX_SEQ,
  *             H <= LF_MAX_HEADS).
- *   d         head dimension; must be LF_HEAD_DIM (64).
+ *   d         head dimension: 32, 64 or 128 (the 1/sqrt(d) scale follows it).
+ *             One head of q, k or v (T * d elements) must stay below 2 GiB,
+ *             and below 2 GiB / 1.5 for fp32 (its three bf16 planes).
  *   r         one-sided window radius in window steps, r >= 0; the window
  *             holds 2r+1 keys away from the sequence ends.  r >= T means
  *             every key of the (dilated) class.
@@ -127,6 +134,11 @@ lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v,
  *   n_rand    random key blocks per query block, 0 .. LF_MAX_RAND_BLOCKS;
  *             with n_rand > 0 every head must be undilated (delta = 1), else
  *             LF_E_UNSUPPORTED.
+ *   lse       DEVICE float [B][H][T], 4-byte aligned, or NULL: when given,
+ *             row i receives log(sum_{j in N(i)} exp(q_i . k_j / sqrt(d))),
+ *             the natural log of its softmax denominator (the statistic a
+ *             backward pass needs to rebuild the weights); -inf for a padded
+ *             query row.  Must not overlap the other tensors.
  *   All other arguments, the ownership and the error behaviour are those
  *   of lf_attn_fwd; one_sided outside {0, 1}, a negative radius or n_rand,
  *   or a block index out of range is LF_E_INVALID.
@@ -138,7 +150,7 @@ lf_status_t lf_attn_fwd_ex(const void *q, const void *k, const void *v,
                            const int32_t *dilation,
                            const int32_t *global_idx, int n_global,
                            const uint8_t *key_padding_mask,
-                           void *out, lf_dtype_t dtype, void *stream);
+                           void *out, float *lse, lf_dtype_t dtype, void *stream);
 
 /* Text describing the last non-OK status returned on the calling thread
  * (empty string if none).  The pointer stays valid until the next call on

@@ -21,7 +21,8 @@ LF_E_UNSUPPORTED = 2
 LF_E_NOMEM = 3
 LF_E_HIP = 4
 STATUS_NAMES = {0: "LF_OK", 1: "LF_E_INVALID", 2: "LF_E_UNSUPPORTED", 3: "LF_E_NOMEM", 4: "LF_E_HIP"}
-HEAD_DIM = 64
+HEAD_DIM = 64          # d of the backward
+FWD_HEAD_DIMS = (32, 64, 128)
 MAX_HEADS = 128
 MAX_GLOBALS = 512
 MAX_RAND_BLOCKS = 8
@@ -48,7 +49,7 @@ def load():
     I = ctypes.c_int
     lib.lf_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I, P]
     lib.lf_attn_fwd.restype = I
-    lib.lf_attn_fwd_ex.argtypes = [P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, I, P]
+    lib.lf_attn_fwd_ex.argtypes = [P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, P, I, P]
     lib.lf_attn_fwd_ex.restype = I
     lib.lf_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, P, P, I, P]
     lib.lf_attn_bwd.restype = I
@@ -67,45 +68,79 @@ def _per_head(r):
     return not isinstance(r, int) and hasattr(r, "__len__")
 
 
-def _rand_table(random_blocks):
-    """(ctypes int32 array, n_rand) of random key blocks [H][ceil(T/64)][n], or (None, 0)."""
+def _rand_table(random_blocks, H=None, T=None):
+    """(ctypes int32 array, n_rand) of random key blocks [H][ceil(T/64)][n], or (None, 0).
+    With H and T given, the table's first two extents must be H and ceil(T/64)."""
     if random_blocks is None:
         return None, 0
     import numpy as np
     a = np.ascontiguousarray(np.asarray(random_blocks, dtype=np.int32))
     if a.ndim != 3:
         raise ValueError("random_blocks must be [H][ceil(T/64)][n_rand]")
+    if H is not None and T is not None and a.shape[:2] != (int(H), (int(T) + 63) // 64):
+        raise ValueError(f"random_blocks has shape {a.shape}; expected [{int(H)}][{(int(T) + 63) // 64}][n_rand]")
     flat = a.reshape(-1)
     return (ctypes.c_int32 * max(1, flat.size))(*flat.tolist()), int(a.shape[2])
 
 
+def _dilation_array(dilation, H):
+    if dilation is None:
+        return None
+    if len(dilation) != int(H):
+        raise ValueError(f"dilation has {len(dilation)} entries for {int(H)} heads")
+    return (ctypes.c_int32 * len(dilation))(*[int(x) for x in dilation])
+
+
 def raw_fwd(q_ptr, k_ptr, v_ptr, B, H, T, d, r, dilation, global_idx, n_global, kpm_ptr, out_ptr,
-            dtype, stream_ptr, one_sided=False, random_blocks=None) -> int:
+            dtype, stream_ptr, one_sided=False, random_blocks=None, lse_ptr=None) -> int:
     """Call the library with raw integer device pointers; returns the status.
     ``r`` is one radius (lf_attn_fwd) or a list of H radii; a list,
-    ``one_sided`` or ``random_blocks`` goes to lf_attn_fwd_ex."""
+    ``one_sided``, ``random_blocks`` or ``lse_ptr`` goes to lf_attn_fwd_ex."""
     lib = load()
-    dil = None
-    if dilation is not None:
-        dil = (ctypes.c_int32 * len(dilation))(*[int(x) for x in dilation])
+    dil = _dilation_array(dilation, H)
     g = None
     if global_idx is not None:
         g = (ctypes.c_int32 * max(1, len(global_idx)))(*[int(x) for x in global_idx])
-    if _per_head(r) or one_sided or random_blocks is not None:
+    if _per_head(r) or one_sided or random_blocks is not None or lse_ptr is not None:
         rl = [int(x) for x in r] if _per_head(r) else [int(r)] * int(H)
+        if len(rl) != int(H):
+            raise ValueError(f"r has {len(rl)} radii for {int(H)} heads")
         rad = (ctypes.c_int32 * max(1, len(rl)))(*rl)
-        rt, nr = _rand_table(random_blocks)
+        rt, nr = _rand_table(random_blocks, H, T)
         return lib.lf_attn_fwd_ex(q_ptr, k_ptr, v_ptr, int(B), int(H), int(T), int(d), rad,
                                   int(one_sided) if not isinstance(one_sided, bool) else int(one_sided),
-                                  rt, nr, dil, g, int(n_global), kpm_ptr, out_ptr, int(dtype), stream_ptr)
+                                  rt, nr, dil, g, int(n_global), kpm_ptr, out_ptr, lse_ptr, int(dtype), stream_ptr)
     return lib.lf_attn_fwd(q_ptr, k_ptr, v_ptr, int(B), int(H), int(T), int(d), int(r), dil, g,
                            int(n_global), kpm_ptr, out_ptr, int(dtype), stream_ptr)
 
 
+def _padding_arg(key_padding_mask, B, T, stream):
+    """(pointer, tensor) of the [B, T] byte mask, or (None, None).  A mask that
+    needs converting (bool, or not contiguous) becomes a temporary, which is
+    recorded on the call's stream so that the caching allocator keeps it
+    until the kernels have read it."""
+    import torch
+    if key_padding_mask is None:
+        return None, None
+    kpm = key_padding_mask
+    if kpm.dtype == torch.bool:
+        kpm = kpm.to(torch.uint8)
+    if kpm.dtype != torch.uint8 or tuple(kpm.shape) != (B, T) or not kpm.is_cuda:
+        raise ValueError("key_padding_mask must be a uint8/bool device tensor [B, T]")
+    kpm = kpm.contiguous()
+    if kpm is not key_padding_mask and stream is not None and hasattr(stream, "cuda_stream"):
+        kpm.record_stream(stream)
+    return kpm.data_ptr(), kpm
+
+
 def attn_fwd(q, k, v, r, dilation: Optional[Sequence[int]] = None,
              global_idx: Optional[Sequence[int]] = None, global_attention_mask=None,
-             key_padding_mask=None, out=None, stream=None, one_sided: bool = False, random_blocks=None):
-    """Longformer sparse attention forward on torch tensors [B, H, T, 64].
+             key_padding_mask=None, out=None, stream=None, one_sided: bool = False, random_blocks=None,
+             lse=None):
+    """Longformer sparse attention forward on torch tensors [B, H, T, d], d in {32, 64, 128}.
+
+    ``lse``: an fp32 device tensor [B, H, T] that receives each row's
+    log-sum-exp of its scaled scores (natural log), or None.
 
     ``r`` is the window radius, or a list with one radius per head;
     ``one_sided`` keeps only the window keys at or before each query;
@@ -147,22 +182,21 @@ def attn_fwd(q, k, v, r, dilation: Optional[Sequence[int]] = None,
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
-    kpm_ptr = None
-    if key_padding_mask is not None:
-        kpm = key_padding_mask
-        if kpm.dtype == torch.bool:
-            kpm = kpm.to(torch.uint8)
-        if kpm.dtype != torch.uint8 or tuple(kpm.shape) != (B, T) or not kpm.is_cuda:
-            raise ValueError("key_padding_mask must be a uint8/bool device tensor [B, T]")
-        kpm = kpm.contiguous()
-        kpm_ptr = kpm.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    kpm_ptr, _kpm = _padding_arg(key_padding_mask, B, T, stream)
     if _per_head(r) and len(r) != H:
         raise ValueError(f"r has {len(r)} radii for {H} heads")
+    lse_ptr = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous() or \
+                lse.device != q.device:
+            raise ValueError("lse must be a contiguous float32 device tensor [B, H, T]")
+        lse_ptr = lse.data_ptr()
     st = raw_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, r, dilation,
-                 gl if gl else None, len(gl), kpm_ptr, out.data_ptr(), dt, sptr, one_sided, random_blocks)
+                 gl if gl else None, len(gl), kpm_ptr, out.data_ptr(), dt, sptr, one_sided, random_blocks,
+                 lse_ptr)
     if st != LF_OK:
         raise LfError(st, last_error())
     return out
@@ -174,14 +208,14 @@ def raw_bwd(q_ptr, k_ptr, v_ptr, dy_ptr, B, H, T, d, r, one_sided, dilation, glo
     a list of H radii.  Returns the status."""
     lib = load()
     rl = [int(x) for x in r] if _per_head(r) else [int(r)] * int(H)
+    if len(rl) != int(H):
+        raise ValueError(f"r has {len(rl)} radii for {int(H)} heads")
     rad = (ctypes.c_int32 * max(1, len(rl)))(*rl)
-    dil = None
-    if dilation is not None:
-        dil = (ctypes.c_int32 * len(dilation))(*[int(x) for x in dilation])
+    dil = _dilation_array(dilation, H)
     g = None
     if global_idx is not None:
         g = (ctypes.c_int32 * max(1, len(global_idx)))(*[int(x) for x in global_idx])
-    rt, nr = _rand_table(random_blocks)
+    rt, nr = _rand_table(random_blocks, H, T)
     return lib.lf_attn_bwd(q_ptr, k_ptr, v_ptr, dy_ptr, int(B), int(H), int(T), int(d), rad, int(bool(one_sided)),
                            rt, nr, dil, g, int(n_global), kpm_ptr, dq_ptr, dk_ptr, dv_ptr, int(dtype), stream_ptr)
 
@@ -216,18 +250,10 @@ def attn_bwd(q, k, v, dy, r, dilation: Optional[Sequence[int]] = None,
         out = tuple(torch.empty_like(q) for _ in range(3))
     elif len(out) != 3 or any(o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() for o in out):
         raise ValueError("out must be three contiguous tensors like q")
-    kpm_ptr = None
-    if key_padding_mask is not None:
-        kpm = key_padding_mask
-        if kpm.dtype == torch.bool:
-            kpm = kpm.to(torch.uint8)
-        if kpm.dtype != torch.uint8 or tuple(kpm.shape) != (B, T) or not kpm.is_cuda:
-            raise ValueError("key_padding_mask must be a uint8/bool device tensor [B, T]")
-        kpm = kpm.contiguous()
-        kpm_ptr = kpm.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    kpm_ptr, _kpm = _padding_arg(key_padding_mask, B, T, stream)
     st = raw_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr(), B, H, T, d, r, one_sided, dilation,
                  gl if gl else None, len(gl), kpm_ptr, out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
                  dt, sptr, random_blocks)
@@ -253,7 +279,7 @@ class Prepared:
         dt = LF_BF16 if q.dtype == torch.bfloat16 else LF_F32
         self.out = torch.empty_like(q) if out is None else out
         gl = list(global_idx) if global_idx is not None else []
-        self._dil = (ctypes.c_int32 * H)(*[int(x) for x in dilation]) if dilation is not None else None
+        self._dil = _dilation_array(dilation, H)
         self._g = (ctypes.c_int32 * max(1, len(gl)))(*gl) if gl else None
         kpm = None
         if key_padding_mask is not None:
@@ -266,10 +292,10 @@ class Prepared:
         if _per_head(r) or one_sided or random_blocks is not None:
             rl = [int(x) for x in r] if _per_head(r) else [int(r)] * H
             self._rad = (ctypes.c_int32 * H)(*rl)
-            self._rt, nr = _rand_table(random_blocks)
+            self._rt, nr = _rand_table(random_blocks, H, T)
             self._fn = lib.lf_attn_fwd_ex
             self._args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, self._rad, int(bool(one_sided)),
-                          self._rt, nr, self._dil, self._g, len(gl), kptr, self.out.data_ptr(), dt, sptr)
+                          self._rt, nr, self._dil, self._g, len(gl), kptr, self.out.data_ptr(), None, dt, sptr)
         else:
             self._fn = lib.lf_attn_fwd
             self._args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, int(r), self._dil, self._g,

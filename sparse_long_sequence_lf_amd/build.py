@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblfattn.so")
-SOURCES = [os.path.join(CSRC, "lf_host.cpp"), os.path.join(CSRC, "lf_attn_kernels.hip"),
+SOURCES = [os.path.join(CSRC, "lf_host.cpp"), os.path.join(CSRC, "lf_fwd_kernels.hip"),
            os.path.join(CSRC, "lf_bwd_kernels.hip")]
 PEAK_LIB = os.path.join(PKG, "libmfmapeak.so")
 PEAK_SOURCE = os.path.join(CSRC, "mfma_peak.hip")

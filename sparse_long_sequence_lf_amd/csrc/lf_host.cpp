@@ -18,9 +18,11 @@
 
 #include "lf_attn.h"
 #include "lf_kernels.h"
+#include "lf_decode.h"
 #include "lf_bwd.h"
 
 extern "C" hipError_t lfk_launch(const lfk::Args *A, const lfk::Plan *P, int dtype_bf16, void *stream);
+extern "C" int lfk_supports_d(int d);
 extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs *A, const void *const *t, int dtype_bf16, void *stream);
 
 namespace {
@@ -156,15 +158,22 @@ namespace {
 lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T, int d, int r,
                      const int32_t *radius, int one_sided, const int32_t *rand_blocks, int n_rand,
                      const int32_t *dilation, const int32_t *global_idx, int n_global,
-                     const uint8_t *key_padding_mask, void *out, lf_dtype_t dtype, void *stream) {
+                     const uint8_t *key_padding_mask, void *out, float *lse, lf_dtype_t dtype, void *stream) {
     g_err.clear();
     // ---- argument checks: no HIP call before all of them pass
     if (!q || !k || !v || !out) return fail(LF_E_INVALID, "q, k, v and out must be non-null");
     if (dtype != LF_F32 && dtype != LF_BF16) return fail(LF_E_UNSUPPORTED, "unknown dtype %d", (int)dtype);
     if (B < 1 || H < 1 || T < 1) return fail(LF_E_INVALID, "B, H, T must be >= 1 (got %d, %d, %d)", B, H, T);
-    if (d != LF_HEAD_DIM) return fail(LF_E_UNSUPPORTED, "head dimension %d: only %d is built", d, LF_HEAD_DIM);
+    if (!lfk_supports_d(d)) return fail(LF_E_UNSUPPORTED, "head dimension %d: only 32, 64 and 128 are built", d);
     if (H > LF_MAX_HEADS) return fail(LF_E_UNSUPPORTED, "H = %d exceeds %d", H, LF_MAX_HEADS);
     if (T > LF_MAX_SEQ) return fail(LF_E_UNSUPPORTED, "T = %d exceeds %d", T, LF_MAX_SEQ);
+    {
+        // one head's rows as the kernels address them (the fp32 input, or its
+        // three bf16 planes) must stay below 2^31 bytes
+        const long long row = dtype == LF_BF16 ? 2LL * d : 6LL * d;
+        if ((long long)T * row >= (1LL << 31))
+            return fail(LF_E_UNSUPPORTED, "T = %d with d = %d: one head exceeds the 2 GiB a kernel addresses", T, d);
+    }
     if (r < 0) return fail(LF_E_INVALID, "window radius r = %d must be >= 0", r);
     if (one_sided != 0 && one_sided != 1) return fail(LF_E_INVALID, "one_sided = %d must be 0 or 1", one_sided);
     if (radius)
@@ -198,12 +207,17 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
     }
     const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u;
     if (mis) return fail(LF_E_INVALID, "q, k, v and out must be 16-byte aligned");
+    if (((uintptr_t)lse & 3u) != 0) return fail(LF_E_INVALID, "lse must be 4-byte aligned");
     const size_t esize = dtype == LF_BF16 ? 2 : 4;
     const size_t nbytes = (size_t)B * (size_t)H * (size_t)T * (size_t)d * esize;
     if ((size_t)B * (size_t)H > (size_t)1 << 24)
         return fail(LF_E_UNSUPPORTED, "B*H = %lld too large", (long long)B * H);
     if (overlaps(out, nbytes, q, nbytes) || overlaps(out, nbytes, k, nbytes) || overlaps(out, nbytes, v, nbytes))
         return fail(LF_E_INVALID, "out overlaps q, k or v");
+    const size_t lbytes = (size_t)B * (size_t)H * (size_t)T * sizeof(float);
+    if (lse && (overlaps(lse, lbytes, q, nbytes) || overlaps(lse, lbytes, k, nbytes) ||
+                overlaps(lse, lbytes, v, nbytes) || overlaps(lse, lbytes, out, nbytes)))
+        return fail(LF_E_INVALID, "lse overlaps q, k, v or out");
 
     // ---- normalise G: a set of positions, ascending
     std::vector<int32_t> G(global_idx, global_idx + n_global);
@@ -213,11 +227,10 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
         return fail(LF_E_UNSUPPORTED, "%zu distinct globals exceed %d", G.size(), LF_MAX_GLOBALS);
 
     // ---- plan
-    constexpr int QB = LFK_QB;
-    constexpr int BM = 32 * QB;
+    constexpr int BM = LFK_BM;
     lfk::Plan P;
     std::memset(&P, 0, sizeof P);
-    P.B = B; P.H = H; P.T = T;
+    P.B = B; P.H = H; P.T = T; P.d = d;
     // |i - j| < T always, so radii beyond T change nothing
     P.r = 0;
     for (int h = 0; h < H; h++) {
@@ -250,51 +263,46 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
         if (P.rad[h] != P.rad[0]) P.band_chunk = 8;
     P.n_g = (int)G.size();
     for (int i = 0; i < P.n_g; i++) P.glob[i] = G[i];
-    long long start = 0;
-    for (int h = 0; h < H; h++) {
-        const int delta = dilation ? dilation[h] : 1;
-        P.dil[h] = delta;
-        P.head_start[h] = (int)start;
-        const long long qq = T / delta, rem = T % delta;
-        start += rem * cdiv(qq + 1, BM) + (delta - rem) * cdiv(qq, BM);
-    }
-    P.head_start[H] = (int)start;
-    P.uniform_head_tasks = (int)(start / H);
-    for (int h = 0; h < H; h++)
-        if (P.head_start[h + 1] - P.head_start[h] != P.uniform_head_tasks) P.uniform_head_tasks = 0;
-    P.band_tasks_per_batch = (int)start;
+    const long long start = lfk::fill_band_plan(P, B, H, T, dilation);
     const long long n_band = (long long)B * start;
     long long n_glob_tasks = 0;
     size_t cnt_bytes = 0, scratch_bytes = 0;
     if (P.n_g > 0) {
-        P.n_ggroups = (int)cdiv(cdiv(P.n_g, 32), QB);
+        P.n_ggroups = (int)cdiv(P.n_g, BM);
         P.g_pad = P.n_ggroups * BM;
-        // a split about as long as a band tile's key range (64 + 2r keys),
-        // so both kinds of task cost about the same (measured faster than
-        // the shortest splits); at least 256 keys, and at most 16 splits
-        // (bounds the partial records and the combine's reads)
-        long long sl = cdiv((long long)BM + 2LL * P.r, 64) * 64;
-        if (sl < 256) sl = 256;
-        const long long sl16 = cdiv(cdiv(T, 16), 32) * 32;
-        if (sl < sl16) sl = sl16;
+        // about one global-row task per compute unit (256): a few long
+        // tasks would land as an extra workgroup on a few units and stretch
+        // the call by a band tile's time; short ones spread that work
+        // evenly.  At most 64 splits per head (bounds the combine's reads),
+        // at least 64 keys a split.
+        const long long per = (long long)B * H * P.n_ggroups;
+        long long ns = 256 / per;
+        if (ns < 1) ns = 1;
+        if (ns > 64) ns = 64;
+        long long sl = cdiv(cdiv(T, ns), 32) * 32;
+        if (sl < 64) sl = 64;
         P.split_len = (int)(sl < T ? sl : cdiv(T, 32) * 32);
         P.n_split = (int)cdiv(T, P.split_len);
         n_glob_tasks = (long long)B * H * P.n_split * P.n_ggroups;
+        P.mg_per_bh = lfk::magic_for((long long)P.n_split * P.n_ggroups);
+        P.mg_nsplit = lfk::magic_for(P.n_split);
         cnt_bytes = (size_t)B * H * sizeof(int);
-        scratch_bytes = (size_t)B * H * P.n_split * P.g_pad * 272;  // 272-byte partial records
+        // partial records of d + 4 floats: O[d], m, l, 0, 0
+        scratch_bytes = (size_t)B * H * P.n_split * P.g_pad * (size_t)(d + 4) * sizeof(float);
     }
     if (n_band + n_glob_tasks > (1LL << 30))
         return fail(LF_E_UNSUPPORTED, "problem needs %lld workgroups", n_band + n_glob_tasks);
     P.n_band_tasks = (int)n_band;
     P.n_tasks = (int)(n_band + n_glob_tasks);
-    // fp32: K and V are split into bf16 hi/lo planes (same byte size as the
-    // fp32 tensors) ahead of the tile kernel
+    // fp32: K and V are split into three bf16 planes per row (1.5 times the
+    // fp32 tensors' bytes) ahead of the tile kernel
     size_t planes_off = 0;
+    const size_t plane_bytes = nbytes / 4 * 6;
     if (dtype == LF_F32) {
-        if ((long long)B * H * T * 8 / 256 >= (1LL << 31))
+        if ((long long)B * H * T * (d / 8) / 256 >= (1LL << 31))
             return fail(LF_E_UNSUPPORTED, "fp32 problem too large for the plane split");
         planes_off = (scratch_bytes + 255) / 256 * 256;
-        scratch_bytes = planes_off + 2 * nbytes;
+        scratch_bytes = planes_off + 2 * plane_bytes;
     }
 
     // ---- HIP work
@@ -313,7 +321,7 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
         }
         if (dtype == LF_F32) {
             P.kp = ws + planes_off;
-            P.vp = ws + planes_off + nbytes;
+            P.vp = ws + planes_off + plane_bytes;
         }
     }
     if (n_rand > 0) {
@@ -340,6 +348,7 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
     lfk::Args A;
     A.q = q; A.k = k; A.v = v; A.out = out;
     A.pad = key_padding_mask;
+    A.lse = lse;
     lf_status_t st = upload_plan(*w, P, stream, &A.plan);
     if (st != LF_OK) return st;
     hipError_t e = lfk_launch(&A, &P, dtype == LF_BF16, stream);
@@ -546,16 +555,16 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
                                    int n_global, const uint8_t *key_padding_mask, void *out,
                                    lf_dtype_t dtype, void *stream) {
     return attn_fwd(q, k, v, B, H, T, d, r, nullptr, 0, nullptr, 0, dilation, global_idx, n_global,
-                    key_padding_mask, out, dtype, stream);
+                    key_padding_mask, out, nullptr, dtype, stream);
 }
 
 extern "C" lf_status_t lf_attn_fwd_ex(const void *q, const void *k, const void *v, int B, int H, int T,
                                       int d, const int32_t *radius, int one_sided, const int32_t *rand_blocks,
                                       int n_rand, const int32_t *dilation, const int32_t *global_idx,
-                                      int n_global, const uint8_t *key_padding_mask, void *out,
+                                      int n_global, const uint8_t *key_padding_mask, void *out, float *lse,
                                       lf_dtype_t dtype, void *stream) {
     g_err.clear();
     if (!radius) return fail(LF_E_INVALID, "radius must be a host array of H radii");
     return attn_fwd(q, k, v, B, H, T, d, 0, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
-                    n_global, key_padding_mask, out, dtype, stream);
+                    n_global, key_padding_mask, out, lse, dtype, stream);
 }

@@ -1,5 +1,5 @@
 // lf_kernels.h -- the launch records shared by the host planner
-// (lf_host.cpp) and the gfx950 kernels (lf_attn_kernels.hip).  Internal to
+// (lf_host.cpp) and the gfx950 kernels (lf_fwd_kernels.hip).  Internal to
 // liblfattn.so; the public interface is include/lf_attn.h.
 #ifndef LF_KERNELS_H
 #define LF_KERNELS_H
@@ -8,48 +8,61 @@
 
 #include "lf_attn.h"
 
-// Tile shape: LFK_QB query blocks of 32 per workgroup, LFK_KS key phases
-// per query block (waves per workgroup = LFK_QB * LFK_KS = 4).
-#define LFK_QB 2
-#define LFK_KS 2
-// Register budget: waves per SIMD the tile kernel is compiled for, one per
-// workgroup of four waves resident on a compute unit (bf16: four workgroups,
-// as many as its LDS allows; fp32 inputs double the LDS and the registers).
-#ifndef LFK_WAVES_PER_EU_BF16
-#define LFK_WAVES_PER_EU_BF16 4
-#endif
-#ifndef LFK_WAVES_PER_EU_F32
-#define LFK_WAVES_PER_EU_F32 2
-#endif
+// Tile shape: two query blocks of 32 per workgroup and two key phases per
+// query block (four waves), so a band tile holds 64 queries.
+#define LFK_BM 64
 
 namespace lfk {
+
+// Division by a divisor d fixed for the call, for 0 <= n < 2^31:
+//   s == 0:  n / 1 = n
+//   s >= 1:  n / d = mulhi(n, m) >> (s - 1),  m = ceil(2^(31 + s) / d),  s = ceil(log2 d)
+// (the error of the rounded-up reciprocal stays below 1/d for n < 2^31).
+// Built on the host by magic_for(); one scalar multiply on the GPU.
+struct Magic {
+    uint32_t m;
+    int32_t s;
+};
 
 // Everything about a call except the tensors: shape, per-head tables, the
 // global set and workspace pointers.  Lives in device memory (one copy per
 // (device, stream) workspace), re-uploaded only when it changes, so the
 // kernel argument stays small (launch cost grows with argument size).
 struct Plan {
-    const void *kp, *vp;     // K and V as bf16 planes [B*H][T][2][64] (fp32 input only)
-    float *part;             // global-row partials [B*H][n_split][g_pad] x 272 B: O[64], m, l, 0, 0
+    const void *kp, *vp;     // fp32 input: K and V as three bf16 planes per row [B*H][T][3][d]
+    float *part;             // global-row partials [B*H][n_split][g_pad] records of d + 4 floats: O[d], m, l, 0, 0
     int *counter;            // [B*H] finished global-row workgroups; zero between calls
-    int B, H, T, r;          // r already clamped to T
+    int B, H, T, d;
+    int r;                   // largest radius (clamped to T)
     int n_g;                 // distinct globals (sorted ascending in glob)
-    int g_pad;               // n_ggroups * 32 * LFK_QB
-    int n_ggroups;           // groups of 32*LFK_QB global queries
+    int g_pad;               // n_ggroups * LFK_BM
+    int n_ggroups;           // groups of LFK_BM global queries
     int n_split, split_len;  // global-row key splits (split_len multiple of 32)
     int n_band_tasks;        // B * band_tasks_per_batch
     int band_tasks_per_batch;
     int uniform_head_tasks;  // band tasks per head when every head has the same count, else 0
     int n_tasks;             // band + global-row tasks
+    Magic mg_tpb;            // / band_tasks_per_batch
+    Magic mg_uht;            // / uniform_head_tasks
+    Magic mg_per_bh;         // / (n_split * n_ggroups)
+    Magic mg_nsplit;         // / n_split
+    Magic mg_H;              // / H
+    int one_sided;           // 1: the window keeps the keys at or before the query
+    const int32_t *rtab;     // random key blocks [H][ceil(T/64)][n_rand] (-1 = none), or null
+    const uint32_t *gmap;    // bit j set iff position j is global ([ceil(T/32)] words), or null
+    int n_rand;              // random key blocks (of 64 keys) per query block of 64
+    int band_chunk;          // 0: each die takes a contiguous eighth of the band tiles;
+                             // C > 0: runs of C tiles are dealt to the dies in turn
     int head_start[LF_MAX_HEADS + 1];  // band-task prefix over heads
-    int32_t dil[LF_MAX_HEADS];      // 32-bit: a head's entry is one scalar load
-    int32_t rad[LF_MAX_HEADS];      // window radius per head (clamped to T)
-    int one_sided;                  // 1: the window keeps the keys at or before the query
-    const int32_t *rtab;            // random key blocks [H][ceil(T/64)][n_rand] (-1 = none), or null
-    const uint32_t *gmap;           // bit j set iff position j is global ([ceil(T/32)] words), or null
-    int n_rand;                     // random key blocks (of 64 keys) per query block of 64
-    int band_chunk;                 // 0: each die takes a contiguous eighth of the band tiles;
-                                    // C > 0: runs of C tiles are dealt to the dies in turn
+    int32_t dil[LF_MAX_HEADS];   // dilation delta_h
+    int32_t rad[LF_MAX_HEADS];   // window radius per head (clamped to T)
+    int32_t hq[LF_MAX_HEADS];    // T / delta_h: length of the shorter residue classes
+    int32_t hrem[LF_MAX_HEADS];  // T % delta_h: classes 0 .. hrem-1 hold hq + 1 positions
+    int32_t htb[LF_MAX_HEADS];   // tiles of a class of hq + 1 positions
+    int32_t hts[LF_MAX_HEADS];   // tiles of a class of hq positions
+    Magic mg_tb[LF_MAX_HEADS];   // / htb
+    Magic mg_ts[LF_MAX_HEADS];   // / hts
+    Magic mg_dil[LF_MAX_HEADS];  // / delta_h
     int32_t glob[LF_MAX_GLOBALS];
 };
 
@@ -59,6 +72,7 @@ struct Args {
     void *out;
     const uint8_t *pad;      // [B][T] or null
     const Plan *plan;
+    float *lse;              // [B][H][T] natural log of each row's softmax denominator, or null
 };
 
 }  // namespace lfk

@@ -1,0 +1,119 @@
+// CPU check of the division by call constants and of the band-task and
+// global-row-task decodes the tile kernel runs (lf_decode.h, compiled here
+// with g++): every division exact, every task decoded to a distinct
+// (b, h, class, tile) inside its ranges, in the order of a plain decode
+// written with ordinary division.  Prints "OK <count>" or the first failure.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <random>
+#include <set>
+#include <tuple>
+#include <vector>
+
+#include "lf_decode.h"
+
+using namespace lfk;
+
+static int fails = 0;
+#define CHECK(c, ...)                         \
+    do {                                      \
+        if (!(c)) {                           \
+            if (fails++ < 10) {               \
+                std::printf("FAIL: " __VA_ARGS__); \
+                std::printf("\n");            \
+            }                                 \
+        }                                     \
+    } while (0)
+
+int main() {
+    long long checked = 0;
+    // ---- n / d
+    std::mt19937_64 rng(12345);
+    std::vector<long long> ds = {1, 2, 3, 5, 7, 63, 64, 65, 96, 100, 255, 256, 257, 1000, 4095, 4096, 4097,
+                                 65535, 65536, 65537, 1 << 20, (1 << 20) + 1, (1 << 24) - 1, 1 << 24,
+                                 (1LL << 30) - 1, 1LL << 30, (1LL << 31) - 1};
+    for (int i = 0; i < 2000; i++) ds.push_back(1 + (long long)(rng() % ((1ULL << 31) - 1)));
+    for (int i = 0; i < 2000; i++) ds.push_back(1 + (long long)(rng() % 5000));
+    for (long long d : ds) {
+        const Magic g = magic_for(d);
+        std::vector<long long> ns = {0, 1, d - 1, d, d + 1, 2 * d - 1, 2 * d, (1LL << 31) - 1, (1LL << 31) - 2,
+                                     ((1LL << 31) - 1) / d * d, ((1LL << 31) - 1) / d * d - 1};
+        for (int i = 0; i < 300; i++) ns.push_back((long long)(rng() % (1ULL << 31)));
+        for (long long n : ns) {
+            if (n < 0 || n >= (1LL << 31)) continue;
+            const int q = mdiv((int)n, g);
+            CHECK(q == n / d, "mdiv(%lld, %lld) = %d, want %lld", n, d, q, n / d);
+            checked++;
+        }
+    }
+    // ---- band-task decode on shapes with uniform and unequal heads
+    struct Shape { int B, H, T; std::vector<int32_t> dil; };
+    std::vector<Shape> shapes = {
+        {1, 12, 4096, {1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1}},
+        {1, 12, 4096, {1, 1, 2, 2, 2, 2, 3, 3, 3, 3, 4, 4}},
+        {4, 16, 16384, {}},
+        {2, 3, 1, {1, 2, 3}},
+        {3, 5, 777, {1, 7, 64, 65, 1000}},
+        {2, 4, 130, {3, 3, 3, 3}},
+        {1, 2, 65, {65535, 1}},
+    };
+    for (int i = 0; i < 40; i++) {
+        Shape s;
+        s.B = 1 + (int)(rng() % 4);
+        s.H = 1 + (int)(rng() % 9);
+        s.T = 1 + (int)(rng() % 3000);
+        for (int h = 0; h < s.H; h++) s.dil.push_back(1 + (int32_t)(rng() % 9));
+        shapes.push_back(s);
+    }
+    for (const Shape& sh : shapes) {
+        Plan P;
+        std::memset(&P, 0, sizeof P);
+        const int32_t* dil = sh.dil.empty() ? nullptr : sh.dil.data();
+        const long long tpb = fill_band_plan(P, sh.B, sh.H, sh.T, dil);
+        // the plain decode: ordinary division, in the same task order
+        long long t = 0;
+        std::set<std::tuple<int, int, int, int>> seen;
+        for (int b = 0; b < sh.B; b++)
+            for (int h = 0; h < sh.H; h++) {
+                const int delta = dil ? dil[h] : 1;
+                for (int c = 0; c < delta && c < sh.T; c++) {
+                    const int n = (sh.T - c + delta - 1) / delta;
+                    const int tiles = (n + LFK_BM - 1) / LFK_BM;
+                    for (int tile = 0; tile < tiles; tile++, t++) {
+                        const BandTask k = decode_band(P, (int)t);
+                        CHECK(k.b == b && k.h == h && k.c == c && k.tile == tile && k.n == n,
+                              "T=%d task %lld -> (%d,%d,%d,%d,n=%d), want (%d,%d,%d,%d,n=%d)", sh.T, t, k.b, k.h,
+                              k.c, k.tile, k.n, b, h, c, tile, n);
+                        CHECK(seen.insert(std::make_tuple(k.b, k.h, k.c, k.tile)).second, "task %lld repeats", t);
+                        checked++;
+                    }
+                }
+            }
+        CHECK(t == tpb * sh.B, "T=%d: %lld tasks, plan says %lld", sh.T, t, tpb * sh.B);
+        // global-row tasks: every (bh, group, split) once, in order
+        for (int ng : {1, 3}) {
+            for (int ns : {1, 7, 16}) {
+                P.n_split = ns;
+                P.n_ggroups = ng;
+                P.mg_per_bh = magic_for((long long)ns * ng);
+                P.mg_nsplit = magic_for(ns);
+                long long g = 0;
+                for (int bh = 0; bh < sh.B * sh.H; bh++)
+                    for (int grp = 0; grp < ng; grp++)
+                        for (int sp = 0; sp < ns; sp++, g++) {
+                            const RowTask k = decode_rows(P, (int)g);
+                            CHECK(k.bh == bh && k.grp == grp && k.split == sp, "row task %lld", g);
+                            CHECK(mdiv(bh, P.mg_H) == bh / sh.H, "bh / H");
+                            checked++;
+                        }
+            }
+        }
+    }
+    if (fails) {
+        std::printf("FAILED %d\n", fails);
+        return 1;
+    }
+    std::printf("OK %lld\n", checked);
+    return 0;
+}

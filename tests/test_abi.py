@@ -46,6 +46,8 @@ def test_header_limits_match_binding():
     assert re.search(r"#define LF_HEAD_DIM (\d+)", text).group(1) == str(binding.HEAD_DIM)
     assert re.search(r"#define LF_MAX_HEADS (\d+)", text).group(1) == str(binding.MAX_HEADS)
     assert re.search(r"#define LF_MAX_GLOBALS (\d+)", text).group(1) == str(binding.MAX_GLOBALS)
+    dims = re.search(r"#define LF_FWD_HEAD_DIMS \{([0-9, ]+)\}", text).group(1)
+    assert tuple(int(x) for x in dims.split(",")) == binding.FWD_HEAD_DIMS
 
 
 # fake, aligned, never-dereferenced device addresses
@@ -67,8 +69,9 @@ BAD = [
     ("B_zero", dict(B=0), lf.LF_E_INVALID),
     ("H_neg", dict(H=-1, dil=None), lf.LF_E_INVALID),
     ("T_zero", dict(T=0), lf.LF_E_INVALID),
-    ("d_32", dict(d=32), lf.LF_E_UNSUPPORTED),
-    ("d_128", dict(d=128), lf.LF_E_UNSUPPORTED),
+    ("d_16", dict(d=16), lf.LF_E_UNSUPPORTED),
+    ("d_48", dict(d=48), lf.LF_E_UNSUPPORTED),
+    ("d_256", dict(d=256), lf.LF_E_UNSUPPORTED),
     ("r_neg", dict(r=-1), lf.LF_E_INVALID),
     ("dilation_zero", dict(dil=[1, 0]), lf.LF_E_INVALID),
     ("dilation_huge", dict(dil=[1, 70000]), lf.LF_E_UNSUPPORTED),
@@ -84,6 +87,8 @@ BAD = [
     ("too_many_heads", dict(H=129, dil=None), lf.LF_E_UNSUPPORTED),
     ("too_many_globals", dict(T=4096, g=list(range(600)), ng=600), lf.LF_E_UNSUPPORTED),
     ("T_too_long", dict(T=1 << 24), lf.LF_E_UNSUPPORTED),
+    # one head of fp32 d = 128 in three bf16 planes: 768 bytes a row, past 2 GiB
+    ("head_too_large_fp32_d128", dict(T=3 << 20, d=128, dtype=lf.LF_F32, dil=None, H=1, g=[0]), lf.LF_E_UNSUPPORTED),
 ]
 
 
@@ -125,7 +130,7 @@ def call_ex(radius, one_sided, **kw):
 BAD_EX = [
     ("radius_negative", dict(radius=[3, -1], one_sided=False), lf.LF_E_INVALID),
     ("one_sided_two", dict(radius=[3, 4], one_sided=2), lf.LF_E_INVALID),
-    ("d_32", dict(radius=[3, 4], one_sided=True, d=32), lf.LF_E_UNSUPPORTED),
+    ("d_96", dict(radius=[3, 4], one_sided=True, d=96), lf.LF_E_UNSUPPORTED),
     ("null_q", dict(radius=[3, 4], one_sided=True, q=None), lf.LF_E_INVALID),
 ]
 
@@ -141,7 +146,7 @@ def test_ex_invalid_arguments_rejected(lib, name, kw, status):
         dil = (ctypes.c_int32 * 2)(*a["dil"])
         g = (ctypes.c_int32 * 1)(*a["g"])
         st = lib.lf_attn_fwd_ex(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], rad, 2, None, 0, dil, g,
-                                a["ng"], None, a["out"], a["dtype"], None)
+                                a["ng"], None, a["out"], None, a["dtype"], None)
     else:
         st = call_ex(radius, one, **kw)
     assert st == status, (name, st, lf.last_error())
@@ -151,8 +156,37 @@ def test_ex_invalid_arguments_rejected(lib, name, kw, status):
 def test_ex_null_radius_rejected(lib):
     a = dict(GOOD)
     st = lib.lf_attn_fwd_ex(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], None, 0, None, 0, None, None,
-                            0, None, a["out"], a["dtype"], None)
+                            0, None, a["out"], None, a["dtype"], None)
     assert st == lf.LF_E_INVALID and "radius" in lf.last_error()
+
+
+LSE = 0x48000000
+
+
+@pytest.mark.parametrize("name,lse,status", [
+    ("lse misaligned", LSE + 2, lf.LF_E_INVALID),
+    ("lse overlaps out", OUT + 256, lf.LF_E_INVALID),
+    ("lse overlaps q", Q, lf.LF_E_INVALID),
+])
+def test_ex_bad_lse_rejected(lib, name, lse, status):
+    a = dict(GOOD)
+    st = lf.raw_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], [3, 4], a["dil"], a["g"], a["ng"],
+                    a["kpm"], a["out"], a["dtype"], None, False, None, lse)
+    assert st == status, (name, st, lf.last_error())
+    assert "lse" in lf.last_error()
+
+
+def test_binding_checks_table_sizes(lib):
+    a = dict(GOOD)
+    with pytest.raises(ValueError, match="dilation"):
+        lf.raw_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], 8, [1, 2, 3], a["g"], a["ng"],
+                   a["kpm"], a["out"], a["dtype"], None)
+    with pytest.raises(ValueError, match="random_blocks"):
+        lf.raw_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], 8, None, a["g"], a["ng"],
+                   a["kpm"], a["out"], a["dtype"], None, False, np.zeros((2, 3, 1), np.int32))
+    with pytest.raises(ValueError, match="radii"):
+        lf.raw_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], [8, 8, 8], None, a["g"], a["ng"],
+                   a["kpm"], a["out"], a["dtype"], None)
 
 
 def _rb(H, T, n, fill=0):
@@ -183,7 +217,7 @@ def test_random_blocks_null_table_rejected(lib):
     a = dict(GOOD)
     rad = (ctypes.c_int32 * 2)(8, 8)
     st = lib.lf_attn_fwd_ex(a["q"], a["k"], a["v"], a["B"], a["H"], a["T"], a["d"], rad, 0, None, 2, None, None,
-                            0, None, a["out"], a["dtype"], None)
+                            0, None, a["out"], None, a["dtype"], None)
     assert st == lf.LF_E_INVALID and "rand_blocks" in lf.last_error()
 
 
