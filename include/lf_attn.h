@@ -60,6 +60,7 @@ typedef enum {
 #define LF_MAX_SEQ ((1 << 24) - 1)  /* T: one head of fp32 K or V stays below 4 GiB */
 #define LF_MAX_DILATION 65535 /* delta */
 #define LF_MAX_RAND_BLOCKS 8  /* random key blocks per query block (lf_attn_fwd_ex) */
+#define LF_NOALLOC_SCRATCH_BYTES (64 << 20) /* device workspace of lf_attn_fwd_noalloc, per GPU */
 
 /*
  * lf_attn_fwd -- enqueue the forward pass on `stream`.
@@ -151,6 +152,34 @@ lf_status_t lf_attn_fwd_ex(const void *q, const void *k, const void *v,
                            const int32_t *global_idx, int n_global,
                            const uint8_t *key_padding_mask,
                            void *out, float *lse, lf_dtype_t dtype, void *stream);
+
+/*
+ * lf_attn_fwd_noalloc -- lf_attn_fwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, result and error behaviour as
+ * lf_attn_fwd; the call itself performs no allocation (no hipMalloc, no
+ * hipFree, no allocating library routine) and no host-to-device copy.
+ *
+ * Its workspace (the plan, the global-row completion counters and partial
+ * records, and for fp32 inputs the three bf16 planes of K and V) is one
+ * file-scope device array of LF_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds until the process exits.  A call whose workspace
+ * would exceed it returns LF_E_UNSUPPORTED before any HIP call (the needed
+ * size grows with B*H*T*d for fp32 inputs and with B*H*n_global*T for
+ * globals).  The plan reaches the GPU as kernel arguments of small copy
+ * launches on `stream`, which also clear the counters, so the call can be
+ * captured into a graph, also with a plan that differs from the last call.
+ *
+ * Every call on one GPU uses that GPU's single array: calls that overlap in
+ * time on one GPU (on different streams, or concurrent graph replays) race
+ * and may corrupt each other's results; order them on one stream.
+ */
+lf_status_t lf_attn_fwd_noalloc(const void *q, const void *k, const void *v,
+                                int B, int H, int T, int d, int r,
+                                const int32_t *dilation,
+                                const int32_t *global_idx, int n_global,
+                                const uint8_t *key_padding_mask,
+                                void *out, lf_dtype_t dtype, void *stream);
 
 /* Text describing the last non-OK status returned on the calling thread
  * (empty string if none).  The pointer stays valid until the next call on

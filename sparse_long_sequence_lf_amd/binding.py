@@ -51,6 +51,8 @@ def load():
     lib.lf_attn_fwd.restype = I
     lib.lf_attn_fwd_ex.argtypes = [P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, P, I, P]
     lib.lf_attn_fwd_ex.restype = I
+    lib.lf_attn_fwd_noalloc.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I, P]
+    lib.lf_attn_fwd_noalloc.restype = I
     lib.lf_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, P, P, I, P]
     lib.lf_attn_bwd.restype = I
     lib.lf_last_error.argtypes = []

@@ -48,6 +48,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "lf_kernels.h"
@@ -1283,7 +1284,71 @@ __global__ __launch_bounds__(256) void split_planes_kernel(const float* __restri
     for (int p = 0; p < 3; p++) *(u32x4*)(dst + row * 3 * D + p * D + ch * 8) = parts[p];
 }
 
+// ---------------------------------------------------------------------------
+// The allocation-free entry point's workspace: one array per GPU, held until
+// the process ends.  Host code never passes `scratch` itself to a kernel (on
+// the host that name is a stand-in, not the device address): it passes the
+// address hipGetSymbolAddress returns for the current device.
+
+static __device__ __align__(256) char scratch[LF_NOALLOC_SCRATCH_BYTES];
+
+// A piece of the plan passed by value (a kernel argument is captured with
+// the launch, so the copy works inside graph capture): words [0, n) go to
+// dst; the first piece also clears n_zero ints at zero (the global-row
+// completion counters).  One workgroup of 256 threads.
+struct PlanPiece {
+    uint32_t* dst;
+    int* zero;
+    int n, n_zero;
+    uint32_t w[880];
+};
+static_assert(sizeof(PlanPiece) <= 3584, "plan piece fits a kernel argument");
+
+__global__ __launch_bounds__(256) void plan_piece_kernel(const PlanPiece c) {
+    for (int i = threadIdx.x; i < c.n; i += 256) c.dst[i] = c.w[i];
+    for (int i = threadIdx.x; i < c.n_zero; i += 256) c.zero[i] = 0;
+}
+
 }  // namespace lfk
+
+// address of this device's scratch array, looked up once per device with
+// that device current
+extern "C" hipError_t lfk_noalloc_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* addr[256] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 256) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(lfk::scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
+// copy `bytes` of a plan (a multiple of 4) to dst in pieces passed by value,
+// the first one also clearing n_zero ints at zero; all on `stream`
+extern "C" hipError_t lfk_write_plan(const void* plan, size_t bytes, void* dst, int* zero, int n_zero, void* stream) {
+    const uint32_t* src = (const uint32_t*)plan;
+    const size_t words = bytes / 4;
+    lfk::PlanPiece c;
+    for (size_t w0 = 0; w0 < words || (w0 == 0 && n_zero > 0); w0 += 880) {
+        const size_t n = words - w0 < 880 ? words - w0 : 880;
+        c.dst = (uint32_t*)dst + w0;
+        c.n = (int)n;
+        for (size_t i = 0; i < n; i++) c.w[i] = src[w0 + i];
+        c.zero = zero;
+        c.n_zero = w0 == 0 ? n_zero : 0;
+        hipLaunchKernelGGL(lfk::plan_piece_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, c);
+        if (n == 0) break;
+    }
+    return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // launchers (called from the host library)

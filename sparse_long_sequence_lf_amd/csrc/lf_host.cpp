@@ -23,6 +23,8 @@
 
 extern "C" hipError_t lfk_launch(const lfk::Args *A, const lfk::Plan *P, int dtype_bf16, void *stream);
 extern "C" int lfk_supports_d(int d);
+extern "C" hipError_t lfk_noalloc_scratch(void **ptr);
+extern "C" hipError_t lfk_write_plan(const void *plan, size_t bytes, void *dst, int *zero, int n_zero, void *stream);
 extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs *A, const void *const *t, int dtype_bf16, void *stream);
 
 namespace {
@@ -158,7 +160,8 @@ namespace {
 lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T, int d, int r,
                      const int32_t *radius, int one_sided, const int32_t *rand_blocks, int n_rand,
                      const int32_t *dilation, const int32_t *global_idx, int n_global,
-                     const uint8_t *key_padding_mask, void *out, float *lse, lf_dtype_t dtype, void *stream) {
+                     const uint8_t *key_padding_mask, void *out, float *lse, lf_dtype_t dtype, void *stream,
+                     bool noalloc = false) {
     g_err.clear();
     // ---- argument checks: no HIP call before all of them pass
     if (!q || !k || !v || !out) return fail(LF_E_INVALID, "q, k, v and out must be non-null");
@@ -303,6 +306,41 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
             return fail(LF_E_UNSUPPORTED, "fp32 problem too large for the plane split");
         planes_off = (scratch_bytes + 255) / 256 * 256;
         scratch_bytes = planes_off + 2 * plane_bytes;
+    }
+
+    if (noalloc) {
+        // the static scratch array: plan, counters, partial records, planes
+        auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+        const size_t plan_bytes = up(sizeof(lfk::Plan));
+        const size_t cnt_off = plan_bytes, part_off = cnt_off + up(cnt_bytes);
+        const size_t total = part_off + scratch_bytes;
+        if (n_rand > 0) return fail(LF_E_UNSUPPORTED, "random key blocks are not taken without allocation");
+        if (total > (size_t)LF_NOALLOC_SCRATCH_BYTES)
+            return fail(LF_E_UNSUPPORTED,
+                        "this call needs a workspace of %zu bytes; the allocation-free entry point has %d",
+                        total, (int)LF_NOALLOC_SCRATCH_BYTES);
+        void *base = nullptr;
+        hipError_t e = lfk_noalloc_scratch(&base);
+        if (e != hipSuccess) return fail(LF_E_HIP, "scratch address: %s", hipGetErrorString(e));
+        char *ws = (char *)base + part_off;
+        if (P.n_g > 0) {
+            P.counter = (int *)((char *)base + cnt_off);
+            P.part = (float *)ws;
+        }
+        if (dtype == LF_F32) {
+            P.kp = ws + planes_off;
+            P.vp = ws + planes_off + plane_bytes;
+        }
+        e = lfk_write_plan(&P, sizeof P, base, P.n_g > 0 ? P.counter : nullptr, P.n_g > 0 ? B * H : 0, stream);
+        if (e != hipSuccess) return fail(LF_E_HIP, "plan copy launch: %s", hipGetErrorString(e));
+        lfk::Args A;
+        A.q = q; A.k = k; A.v = v; A.out = out;
+        A.pad = key_padding_mask;
+        A.lse = lse;
+        A.plan = (const lfk::Plan *)base;
+        e = lfk_launch(&A, &P, dtype == LF_BF16, stream);
+        if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
+        return LF_OK;
     }
 
     // ---- HIP work
@@ -556,6 +594,14 @@ extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, 
                                    lf_dtype_t dtype, void *stream) {
     return attn_fwd(q, k, v, B, H, T, d, r, nullptr, 0, nullptr, 0, dilation, global_idx, n_global,
                     key_padding_mask, out, nullptr, dtype, stream);
+}
+
+extern "C" lf_status_t lf_attn_fwd_noalloc(const void *q, const void *k, const void *v, int B, int H, int T,
+                                           int d, int r, const int32_t *dilation, const int32_t *global_idx,
+                                           int n_global, const uint8_t *key_padding_mask, void *out,
+                                           lf_dtype_t dtype, void *stream) {
+    return attn_fwd(q, k, v, B, H, T, d, r, nullptr, 0, nullptr, 0, dilation, global_idx, n_global,
+                    key_padding_mask, out, nullptr, dtype, stream, true);
 }
 
 extern "C" lf_status_t lf_attn_fwd_ex(const void *q, const void *k, const void *v, int B, int H, int T,

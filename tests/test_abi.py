@@ -260,3 +260,14 @@ def test_bwd_null_radius_rejected(lib):
     st = lib.lf_attn_bwd(Q, K, V, DY, 1, 2, 128, 64, None, 0, None, 0, None, None, 0, None, DQ, DK, DV, lf.LF_BF16,
                          None)
     assert st == lf.LF_E_INVALID and "radius" in lf.last_error()
+
+
+def test_noalloc_refuses_workspace_beyond_scratch(lib):
+    # fp32 inputs need 2 x 1.5 x the K bytes of bf16 planes in the scratch
+    # array: T = 2^22 at d = 64 is past its LF_NOALLOC_SCRATCH_BYTES; refused
+    # before any HIP call (fake, far-apart device addresses)
+    st = lib.lf_attn_fwd_noalloc(1 << 40, 2 << 40, 3 << 40, 1, 4, 1 << 22, 64, 8, None, None, 0, None, 4 << 40,
+                                 lf.LF_F32, None)
+    assert st == lf.LF_E_UNSUPPORTED and "workspace" in lf.last_error()
+    st = lib.lf_attn_fwd_noalloc(Q, K, V, 1, 2, 128, 64, -1, None, None, 0, None, OUT, lf.LF_BF16, None)
+    assert st == lf.LF_E_INVALID
