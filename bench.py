@@ -142,15 +142,16 @@ def global_rows_probe(lf, W, steps):
                       "global_row_GBps_lower_bound": round(kv_bytes / (dt * 1e-6) / 1e9, 1)}), flush=True)
 
 
-# fp32 vector FMA rate without packed fp32 instructions (the library is built
-# with them off): 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz
-PEAK_VALU_F32_TFLOPS = 78.6
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 
 
 def bench_backward(args, lf, W, metrics):
-    """lf_attn_bwd on the workload: W warmup calls, SETTLE_MS of untimed
-    calls, then K back-to-back calls timed with events on the call stream.
-    Useful FLOPs: 10 d per allowed pair (s = q.k, dP = dy.v, dv, dq, dk)."""
+    """The gradients on the workload, given the forward's output and lse
+    (lf_attn_bwd_ex, as a training step calls it after its forward): W
+    warmup calls, SETTLE_MS of untimed calls, then K back-to-back calls
+    timed with events on the call stream; then K calls of lf_attn_bwd, which
+    runs the forward itself.  Useful FLOPs: 10 d per allowed pair (s = q.k,
+    dP = dy.v, dv, dq, dk), against the bf16 matrix-core peak."""
     import torch
     w = W.workload(args.workload)
     inp = W.make_inputs(w)
@@ -161,10 +162,14 @@ def bench_backward(args, lf, W, metrics):
     B, H, T, d = q.shape
     stream = torch.cuda.current_stream(dev)
     outs = tuple(torch.empty_like(q) for _ in range(3))
+    lse = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+    y = lf.attn_fwd(q, k, v, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm, lse=lse, stream=stream,
+                    one_sided=inp.one_sided, random_blocks=inp.random_blocks)
 
-    def call():
+    def call(given=True):
         lf.attn_bwd(q, k, v, dy, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm, out=outs,
-                    stream=stream, one_sided=inp.one_sided, random_blocks=inp.random_blocks)
+                    stream=stream, one_sided=inp.one_sided, random_blocks=inp.random_blocks,
+                    y=y if given else None, lse=lse if given else None)
 
     for _ in range(args.warmup):
         call()
@@ -181,34 +186,42 @@ def bench_backward(args, lf, W, metrics):
         torch.cuda.synchronize()
         print(f"profile mode: {n_untimed} untimed backward calls then {args.steps} of {w.name}", flush=True)
         return
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+
+    def timed(given):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            call(given)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms = timed(True)
+    ms_with_fwd = timed(False)
     pairs = metrics.useful_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
                                  one_sided=inp.one_sided, random_blocks=inp.random_blocks)
     flops = 10 * d * pairs
     tf = flops / (ms * 1e-3) / 1e12
+    bf16 = w.dtype == "bf16"
     line = {
         "metric": "useful TFLOP/s of the backward pass (dq, dk, dv), 10 d FLOP per allowed pair",
         "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32 arithmetic on " + ("bf16" if w.dtype == "bf16" else "f32") + " inputs",
+        "ms_per_step": round(ms, 5), "ms_per_step_with_forward": round(ms_with_fwd, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic (seeded N(0,1) q/k/v/dy; no dataset, no weights)",
         "config": {"workload": w.name, "pass": "backward", "B": B, "H": H, "T": T, "d": d, "r": inp.r,
                    "one_sided": inp.one_sided, "dilation": inp.dilation, "n_global": len(set(inp.global_idx)),
                    "n_rand": 0 if inp.random_blocks is None else int(inp.random_blocks.shape[2]),
                    "padded": inp.key_padding_mask is not None, "useful_pairs": pairs,
-                   "timing": f"eager back-to-back calls after {n_untimed} untimed calls"},
-        "roofline": {"bound": "alu", "kernel": "lfb rows + grows + cols + gcols (whole call)",
-                     "achieved": round(tf, 3), "peak": PEAK_VALU_F32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / PEAK_VALU_F32_TFLOPS, 4), "traffic": None,
-                     "peak_note": "fp32 vector FMA without packed instructions; the published 157.3 "
-                                  "counts packed fp32",
+                   "timing": f"eager back-to-back calls after {n_untimed} untimed calls; value and "
+                             "ms_per_step with the forward's output and lse given (lf_attn_bwd_ex), "
+                             "ms_per_step_with_forward running it too (lf_attn_bwd)"},
+        "roofline": {"bound": "mfma" if bf16 else "alu",
+                     "kernel": "whole call: statistics, global rows and keys, dq and dk/dv band kernels",
+                     "achieved": round(tf, 3), "peak": PEAK_BF16_TFLOPS if bf16 else 157.3, "unit": "TFLOP/s",
+                     "frac": round(tf / (PEAK_BF16_TFLOPS if bf16 else 157.3), 4), "traffic": None,
                      "algorithmic_flops": flops},
     }
     print(json.dumps(line), flush=True)

@@ -186,17 +186,23 @@ lf_status_t lf_attn_fwd_noalloc(const void *q, const void *k, const void *v,
  * this thread. */
 const char *lf_last_error(void);
 
+/* A hash of the sources this library was built from (16 hex digits), so
+ * that a loader can refuse a build older than the sources beside it. */
+const char *lf_build_hash(void);
+
 /*
  * lf_attn_bwd -- enqueue the gradients of the forward pass on `stream`.
  *
  * The pages give no backward pass; Longformer (ciallo.wiki) §5.2 only says
  * that training cost grows linearly with the length.  This is the
- * derivative of the forward of lf_attn_fwd_ex over the same allowed pairs: with P_ij the softmax weights of row i,
- * dP_ij = dy_i . v_j, D_i = sum_j P_ij dP_ij, dS_ij = P_ij (dP_ij - D_i):
+ * derivative of the forward of lf_attn_fwd_ex over the same allowed pairs:
+ * with P_ij the softmax weights of row i, dP_ij = dy_i . v_j,
+ * D_i = sum_j P_ij dP_ij (= dy_i . y_i, y the forward's output) and
+ * dS_ij = P_ij (dP_ij - D_i):
  *     dq_i = sum_j dS_ij k_j / sqrt(d),   dk_j = sum_i dS_ij q_i / sqrt(d),
  *     dv_j = sum_i P_ij dy_i.
  *
- *   q, k, v   DEVICE [B][H][T][d] of `dtype`, the forward's inputs.
+ *   q, k, v   DEVICE [B][H][T][d] of `dtype`, the forward's inputs; d = 64.
  *   dy        DEVICE [B][H][T][d] of `dtype`: the gradient of the loss with
  *             respect to the forward's output.  Rows of padded queries are
  *             ignored (their output is zero whatever q holds).
@@ -205,22 +211,45 @@ const char *lf_last_error(void);
  *   dq, dk, dv DEVICE [B][H][T][d] of `dtype`, written in full (zero rows
  *             at padded positions).  They must not overlap one another or
  *             the inputs.
- *   Arithmetic in fp32 (bf16 inputs are widened exactly), except that with
- *   bf16 inputs the sums over queries that make dk and dv take each
- *   query's weight rounded to bf16; results rounded to `dtype` (bf16 to
- *   nearest even).  Every result is written by exactly
- *   one thread, without atomics: repeated calls give the same bits.
- *   Ownership and errors as lf_attn_fwd: all checks run before any HIP
- *   call; LF_E_INVALID / LF_E_UNSUPPORTED enqueue nothing.  The call keeps
- *   a per-(device, stream) workspace (row statistics, 8 bytes per query
- *   row, and its tables); a change of shape, radii, dilation or globals
- *   or random key blocks during stream capture is LF_E_UNSUPPORTED.
+ *
+ * bf16 inputs run on the matrix cores: the weights come from the forward's
+ * per-row log-sum-exp, which lf_attn_bwd obtains by running the forward
+ * into its workspace first (lf_attn_bwd_ex takes the caller's instead).
+ * Products of bf16 values accumulate in fp32; the weights P and the dS_ij
+ * enter the products over rows as bf16 (rounded to nearest even), and D_i
+ * is taken from the bf16 output y.  fp32 inputs run on the vector units in
+ * fp32 throughout, recomputing each row's statistics.  Results are rounded
+ * to `dtype` (bf16 to nearest even).  Every result is written by exactly
+ * one thread, without atomics: repeated calls give the same bits.
+ * Ownership and errors as lf_attn_fwd: all checks run before any HIP
+ * call; LF_E_INVALID / LF_E_UNSUPPORTED enqueue nothing.  The call keeps
+ * a per-(device, stream) workspace (row statistics, 8 bytes per query
+ * row, its tables, and for lf_attn_bwd on bf16 the forward's output and
+ * lse); a change of shape, radii, dilation or globals or random key
+ * blocks during stream capture is LF_E_UNSUPPORTED.
  */
 lf_status_t lf_attn_bwd(const void *q, const void *k, const void *v, const void *dy,
                         int B, int H, int T, int d, const int32_t *radius, int one_sided,
                         const int32_t *rand_blocks, int n_rand, const int32_t *dilation,
                         const int32_t *global_idx, int n_global, const uint8_t *key_padding_mask,
                         void *dq, void *dk, void *dv, lf_dtype_t dtype, void *stream);
+
+/*
+ * lf_attn_bwd_ex -- lf_attn_bwd with the forward's results supplied.
+ *
+ *   out       DEVICE [B][H][T][d] of `dtype`, 16-byte aligned: the output of
+ *             lf_attn_fwd_ex for the same inputs and arguments.
+ *   lse       DEVICE [B][H][T] floats, 4-byte aligned: that call's lse.
+ * Both given or both NULL (NULL: as lf_attn_bwd).  With bf16 inputs they
+ * replace the forward pass lf_attn_bwd would run; fp32 inputs do not read
+ * them.  Neither may overlap dq, dk or dv.  Other arguments as lf_attn_bwd.
+ */
+lf_status_t lf_attn_bwd_ex(const void *q, const void *k, const void *v, const void *dy,
+                           const void *out, const float *lse,
+                           int B, int H, int T, int d, const int32_t *radius, int one_sided,
+                           const int32_t *rand_blocks, int n_rand, const int32_t *dilation,
+                           const int32_t *global_idx, int n_global, const uint8_t *key_padding_mask,
+                           void *dq, void *dk, void *dv, lf_dtype_t dtype, void *stream);
 
 #ifdef __cplusplus
 }

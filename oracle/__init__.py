@@ -46,11 +46,22 @@ def open_library(path):
     return lib
 
 
+def _built_hash(path):
+    """The source hash recorded beside an oracle build, or None."""
+    try:
+        with open(path + ".hash") as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
 def _load():
+    """The oracle library, (re)built with gcc when it is missing or was built
+    from another version of lf_oracle.c."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            from . import build as _b
+        from . import build as _b
+        if not os.path.exists(_LIB_PATH) or _built_hash(_LIB_PATH) != _b.source_hash():
             _b.build()
         _lib = open_library(_LIB_PATH)
     return _lib

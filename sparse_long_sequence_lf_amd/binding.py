@@ -45,6 +45,7 @@ def load():
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m sparse_long_sequence_lf_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
+    _check_fresh(lib)
     P = ctypes.c_void_p
     I = ctypes.c_int
     lib.lf_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I, P]
@@ -55,10 +56,24 @@ def load():
     lib.lf_attn_fwd_noalloc.restype = I
     lib.lf_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, P, P, I, P]
     lib.lf_attn_bwd.restype = I
+    lib.lf_attn_bwd_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, P, P, I, P]
+    lib.lf_attn_bwd_ex.restype = I
     lib.lf_last_error.argtypes = []
     lib.lf_last_error.restype = ctypes.c_char_p
     _lib = lib
     return lib
+
+
+def _check_fresh(lib):
+    """Refuse a library built from other sources than the ones beside it."""
+    from . import build as _build
+
+    lib.lf_build_hash.argtypes = []
+    lib.lf_build_hash.restype = ctypes.c_char_p
+    built, now = lib.lf_build_hash().decode(), _build.source_hash()
+    if built != now:
+        raise RuntimeError(f"{LIB_PATH} was built from other sources (hash {built}, sources {now}): "
+                           "rebuild it with `python -m sparse_long_sequence_lf_amd.build`")
 
 
 def last_error() -> str:
@@ -205,9 +220,10 @@ def attn_fwd(q, k, v, r, dilation: Optional[Sequence[int]] = None,
 
 
 def raw_bwd(q_ptr, k_ptr, v_ptr, dy_ptr, B, H, T, d, r, one_sided, dilation, global_idx, n_global, kpm_ptr,
-            dq_ptr, dk_ptr, dv_ptr, dtype, stream_ptr, random_blocks=None) -> int:
-    """lf_attn_bwd with raw integer device pointers; ``r`` is one radius or
-    a list of H radii.  Returns the status."""
+            dq_ptr, dk_ptr, dv_ptr, dtype, stream_ptr, random_blocks=None, y_ptr=None, lse_ptr=None) -> int:
+    """lf_attn_bwd (lf_attn_bwd_ex when the forward's output ``y_ptr`` and
+    ``lse_ptr`` are given) with raw integer device pointers; ``r`` is one
+    radius or a list of H radii.  Returns the status."""
     lib = load()
     rl = [int(x) for x in r] if _per_head(r) else [int(r)] * int(H)
     if len(rl) != int(H):
@@ -218,17 +234,23 @@ def raw_bwd(q_ptr, k_ptr, v_ptr, dy_ptr, B, H, T, d, r, one_sided, dilation, glo
     if global_idx is not None:
         g = (ctypes.c_int32 * max(1, len(global_idx)))(*[int(x) for x in global_idx])
     rt, nr = _rand_table(random_blocks, H, T)
+    if y_ptr is not None or lse_ptr is not None:
+        return lib.lf_attn_bwd_ex(q_ptr, k_ptr, v_ptr, dy_ptr, y_ptr, lse_ptr, int(B), int(H), int(T), int(d), rad,
+                                  int(bool(one_sided)), rt, nr, dil, g, int(n_global), kpm_ptr, dq_ptr, dk_ptr,
+                                  dv_ptr, int(dtype), stream_ptr)
     return lib.lf_attn_bwd(q_ptr, k_ptr, v_ptr, dy_ptr, int(B), int(H), int(T), int(d), rad, int(bool(one_sided)),
                            rt, nr, dil, g, int(n_global), kpm_ptr, dq_ptr, dk_ptr, dv_ptr, int(dtype), stream_ptr)
 
 
 def attn_bwd(q, k, v, dy, r, dilation: Optional[Sequence[int]] = None,
              global_idx: Optional[Sequence[int]] = None, key_padding_mask=None, out=None, stream=None,
-             one_sided: bool = False, random_blocks=None):
+             one_sided: bool = False, random_blocks=None, y=None, lse=None):
     """Gradients (dq, dk, dv) of the forward for the upstream gradient ``dy``,
     torch tensors [B, H, T, 64] like q; the same window, dilation, global,
     random-block and padding arguments as ``attn_fwd``.  ``out`` may be a
-    tuple of three tensors like q to write into."""
+    tuple of three tensors like q to write into.  ``y`` and ``lse``: the
+    forward's output (like q) and its lse (float32 [B, H, T]) from the same
+    arguments, both or neither (then bf16 input runs the forward first)."""
     import torch
 
     if q.dtype == torch.bfloat16:
@@ -256,9 +278,19 @@ def attn_bwd(q, k, v, dy, r, dilation: Optional[Sequence[int]] = None,
         stream = torch.cuda.current_stream(q.device)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     kpm_ptr, _kpm = _padding_arg(key_padding_mask, B, T, stream)
+    if (y is None) != (lse is None):
+        raise ValueError("y and lse are given together or not at all")
+    y_ptr = lse_ptr = None
+    if y is not None:
+        if y.dtype != q.dtype or y.shape != q.shape or y.device != q.device or not y.is_contiguous():
+            raise ValueError("y must be a contiguous tensor like q")
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or lse.device != q.device \
+                or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [B, H, T] tensor on q's device")
+        y_ptr, lse_ptr = y.data_ptr(), lse.data_ptr()
     st = raw_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr(), B, H, T, d, r, one_sided, dilation,
                  gl if gl else None, len(gl), kpm_ptr, out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
-                 dt, sptr, random_blocks)
+                 dt, sptr, random_blocks, y_ptr, lse_ptr)
     if st != LF_OK:
         raise LfError(st, last_error())
     return out

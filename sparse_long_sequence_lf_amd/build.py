@@ -3,6 +3,8 @@ and libmfmapeak.so (the benchmark's MFMA-rate probe, not part of the library).
 
     python -m sparse_long_sequence_lf_amd.build
 """
+import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -13,8 +15,26 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblfattn.so")
 SOURCES = [os.path.join(CSRC, "lf_host.cpp"), os.path.join(CSRC, "lf_fwd_kernels.hip"),
-           os.path.join(CSRC, "lf_bwd_kernels.hip")]
+           os.path.join(CSRC, "lf_bwd_kernels.hip"), os.path.join(CSRC, "lf_bwd_mfma.hip")]
 PEAK_LIB = os.path.join(PKG, "libmfmapeak.so")
+
+
+def hashed_files():
+    """The files liblfattn.so is built from: its sources, the internal
+    headers beside them and the public header."""
+    return sorted(SOURCES + glob.glob(os.path.join(CSRC, "lf_*.h")) + [os.path.join(INCLUDE, "lf_attn.h")])
+
+
+def source_hash() -> str:
+    """Hash of the library's sources (names and contents); compiled into the
+    library (lf_build_hash) so that a loader can refuse a stale build."""
+    h = hashlib.sha256()
+    for path in hashed_files():
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
 PEAK_SOURCE = os.path.join(CSRC, "mfma_peak.hip")
 
 # gfx950 only; packed fp32 VALU ops are kept out of the generated code;
@@ -33,7 +53,7 @@ def build(out: str = LIB, defines=(), verbose: bool = False) -> str:
     objs = []
     tmpdir = os.path.join(PKG, "_build")
     os.makedirs(tmpdir, exist_ok=True)
-    dflags = ["-D" + d for d in defines]
+    dflags = ["-D" + d for d in defines] + ['-DLF_SOURCE_HASH="%s"' % source_hash()]
     for src in SOURCES:
         obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []

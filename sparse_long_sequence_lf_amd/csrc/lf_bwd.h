@@ -34,10 +34,13 @@ struct BwdArgs {
     const int32_t *head_chunk;   // [H+1] prefix of the class chunks (LFB_ROWS_PER_WAVE positions) over the heads
                                  // in the order hord lists them
     const int32_t *hord;         // [H] heads by decreasing radius: the longest waves are dealt out first
-    void *stats;                 // float2 [B*H][T]: (log2-sum-exp of the scaled scores, D_i)
+    void *stats;                 // float2 [B*H][T]: (log2-sum-exp of the scaled scores, D_i); the
+                                 // same layout as the prep kernel of lf_bwd_mfma.hip writes
     float4 *gstat;               // [B*H*n_g][n_split]: a split's (max, sum, sum of p dP) of a global row
     float *gpart;                // [B*H*n_g][n_split][192]: a split's partial dq, dk, dv of a global position
     int B, H, T, n_g, one_sided;
+    int n_chunks;                // head_chunk[H]: class chunks of one batch entry (the host's copy)
+    int stats_given;             // 1: stats holds every row's (lse, D) before the launches (bf16 path)
     int n_split, split_len;      // global rows and columns: splits of split_len positions (256 x per-thread count)
     // random key blocks of 64 (undilated heads only), or n_rand = 0
     const int32_t *rtab;         // [H][ceil(T/64)][n_rand] key blocks per query block, ascending, -1 = none

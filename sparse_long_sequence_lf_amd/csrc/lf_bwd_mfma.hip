@@ -1,0 +1,822 @@
+// lf_bwd_mfma.hip -- the gradients of the Longformer sparse self-attention
+// forward on the gfx950 matrix cores (bf16 inputs, d = 64), for every
+// non-global query (dq) and every non-global key (dk, dv).
+//
+// The pages give no backward pass (Longformer, ciallo.wiki, §5.2 only says
+// that training cost grows linearly with the length).  What is computed is
+// the derivative of the forward map over its allowed pairs.  With the row
+// statistics of the forward (lse_i, the log of row i's softmax denominator)
+// the weights are P_ij = exp(s_ij - lse_i); with dP_ij = dy_i . v_j and
+// D_i = sum_j P_ij dP_ij = dy_i . y_i (y the forward's output),
+//     dS_ij = P_ij (dP_ij - D_i),
+//     dq_i = sum_j dS_ij k_j / sqrt(d),  dk_j = sum_i dS_ij q_i / sqrt(d),
+//     dv_j = sum_i P_ij dy_i.
+//
+// The tiles are the forward's: 64 consecutive positions of one dilation
+// residue class (Longformer, ciallo.wiki §2.2.3), where query t and key u
+// of the class are a band pair when u - t lies in [-r, ra] (ra = r
+// two-sided, 0 one-sided; eightmm.github.io, "Sliding-Window Attention",
+// "Implementation Reading").  Each pair of the allowed set is counted once:
+//   * band blocks: the band pairs, global keys and rows among them;
+//   * global blocks: a non-global query with the global keys outside its
+//     band (dq), or a key with the global queries whose band misses it (dk,
+//     dv) ("Global Attention": a global row reads every key, every row
+//     reads the global keys);
+//   * random blocks (undilated heads): a query block's drawn key blocks
+//     without the keys of the window or of G, and for dk, dv the query
+//     blocks that drew the key block, without global queries.
+// The global rows' dq and the global keys' dk, dv come from the vector
+// kernels of lf_bwd_kernels.hip.
+//
+// Three launches:
+//   prep_kernel  per row: (lse_i log2 e, D_i = dy_i . y_i); a padded row (lse
+//                = -inf) gets (+inf, 0), so its weights vanish.
+//   dq_kernel    query-major: a tile of 64 class queries (two blocks of 32,
+//                two key phases, four waves) streams its key blocks through
+//                an LDS ring: S^T = K Q^T, dP^T = V dY^T,
+//                dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (12 MFMAs a block).
+//   dkdv_kernel  key-major: a tile of 64 class keys streams the blocks of
+//                the queries that read them: S = Q K^T, dP = dY V^T,
+//                dS = P (dP - D), dV^T += dY^T P, dK^T += Q^T dS (16 MFMAs).
+// Every output row is written by one lane: no atomics, reproducible results.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lf_kernels.h"
+#include "lf_decode.h"
+#include "lf_device.h"
+
+namespace lfk {
+namespace bwd {
+
+constexpr int D = 64;
+constexpr int BM = LFK_BM;
+constexpr float SC = ScaleLog2<64>::v;   // log2(e) / 8
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int ROWB = 2 * D;              // bytes of a bf16 row
+constexpr int GT = LF_MAX_GLOBALS;
+
+// LDS forms of a block of 32 rows x 64 channels (4 KiB each), each 1 KiB
+// piece written by one buffer_load_dwordx4 ... lds of a wave:
+//   row form  byte ks*1024 + row*32 + hs*16: channels 16ks + 8h .. +7,
+//             hs = h ^ ((row >> 3) & 1); read as the MFMA operand of one
+//             row per lane (lane p of piece ks loads row p/2)
+//   tr form   byte cb*2048 + row*64 + 16j: channels 32cb + 8j .. +7; read
+//             with ds_read_b64_tr_b16 (lane p of piece (cb, half) loads row
+//             16 half + p/4, channels 32cb + 8(p & 3) ..)
+// The tr form feeds the products whose contraction runs over the block's
+// rows (dQ^T = K^T dS^T; dV^T = dY^T P, dK^T = Q^T dS), in the row order in
+// which a 32x32 accumulator packs into the other operand.
+
+struct Tile {
+    int b, h, bh, c, delta, n, m0, r, ra;
+};
+
+__device__ __forceinline__ Tile decode_tile(const Plan& P, int t) {
+    const BandTask bt = decode_band(P, t);
+    Tile k;
+    k.b = bt.b;
+    k.h = bt.h;
+    k.bh = bt.b * P.H + bt.h;
+    k.c = bt.c;
+    k.delta = P.dil[bt.h];
+    k.n = bt.n;
+    k.m0 = bt.tile * BM;
+    k.r = P.rad[bt.h];
+    k.ra = P.one_sided ? 0 : k.r;
+    return k;
+}
+
+// each of the 8 dies (blockIdx % 8) takes a contiguous eighth of the tiles,
+// so that neighbouring tiles, which read the same rows, share its L2; -1
+// for a slot past the end
+__device__ __forceinline__ int tile_of_block(const Plan& P) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int nb = P.n_band_tasks;
+    const int nb_x = (nb >> 3) + (xcd < (nb & 7)), nb_o = xcd * (nb >> 3) + min(xcd, nb & 7);
+    return slot < nb_x ? nb_o + slot : -1;
+}
+
+// One row as the MFMA operand of a 32x32x16 product, row per lane: lane l
+// gets channels 16ks + 8(l/32) .. +7 of row pos (zeros for pos < 0).
+__device__ __forceinline__ void load_operand(__amdgpu_buffer_rsrc_t rs, int pos, int lg, bf16x8 (&x)[4]) {
+    const uint32_t off = pos >= 0 ? (uint32_t)pos * ROWB : kPastEnd;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+        x[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 2u * (16 * ks + 8 * lg), 0, 0));
+}
+
+// row-form fragment: lane l supplies row l%32, channels 16ks + 8(l/32) .. +7
+__device__ __forceinline__ void read_rows(const char* p, bf16x8 (&x)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) x[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p + 1024 * ks));
+}
+
+// tr-form fragment [st][cb] (p: the form's base plus the lane's part)
+__device__ __forceinline__ void read_tr(const char* p, bf16x8 (&x)[2][2]) {
+#pragma unroll
+    for (int st = 0; st < 2; st++)
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++) {
+            const char* a = p + cb * 2048 + 16 * st * 64;
+            x[st][cb] = cat_tr(ds_tr16(a), ds_tr16(a + 8 * 64));
+        }
+}
+
+// accumulator elements 8st .. 8st+7 -> bf16 operand st
+__device__ __forceinline__ void pack_operand(const float (&p)[16], bf16x8 (&x)[2]) {
+#pragma unroll
+    for (int st = 0; st < 2; st++) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; e++) w[e] = pack_bf16(p[8 * st + 2 * e], p[8 * st + 2 * e + 1]);
+        x[st] = __builtin_bit_cast(bf16x8, w);
+    }
+}
+
+// Write a transposed accumulator pair (this lane's row: channels
+// 32cb + 8j + 4lg + e) as a bf16 row: lanes l and l^32 trade channel groups
+// with v_permlane32_swap so that each writes 8 consecutive channels (the
+// lower lane keeps group 2m and takes its partner's, the upper lane keeps
+// 2m+1 likewise).  zero: write zeros.
+__device__ __forceinline__ void store_row(uint16_t* row, const f32x16 (&acc)[2], float scale, bool zero, int lg) {
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++) {
+        uint32_t g[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float y0 = zero ? 0.f : acc[cb][4 * j] * scale, y1 = zero ? 0.f : acc[cb][4 * j + 1] * scale;
+            const float y2 = zero ? 0.f : acc[cb][4 * j + 2] * scale, y3 = zero ? 0.f : acc[cb][4 * j + 3] * scale;
+            g[j][0] = pack_bf16(y0, y1);
+            g[j][1] = pack_bf16(y2, y3);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; m++) {
+            const auto r0 = __builtin_amdgcn_permlane32_swap(g[2 * m][0], g[2 * m + 1][0], false, false);
+            const auto r1 = __builtin_amdgcn_permlane32_swap(g[2 * m][1], g[2 * m + 1][1], false, false);
+            *(u32x4*)(row + 32 * cb + 16 * m + 8 * lg) = (u32x4){r0[0], r1[0], r0[1], r1[1]};
+        }
+    }
+}
+
+__device__ __forceinline__ bool is_global(const uint32_t* gmap, int pos) {
+    return (gmap[pos >> 5] >> (pos & 31)) & 1u;
+}
+
+// rows of a block starting at position p0 (step 1) that lie at or past T
+__device__ __forceinline__ uint32_t past_end(int p0, int T) {
+    const int valid = T - p0;
+    return valid >= 32 ? 0u : (valid <= 0 ? 0xffffffffu : 0xffffffffu << valid);
+}
+
+// The global tables of a tile, for slots [0, ngb * 32): the position a
+// slot's rows load from (T: no global, or a padded one), its class index
+// in the tile's class (kNotInClass: another class), and per 32 slots the
+// ones that are no live global.
+template <bool PAD>
+__device__ void build_gtab(const Plan& P, const Tile& tk, const uint8_t* padrow, int ngb, int* gld, int* gcls,
+                           uint32_t* gbad, int wave, int lane) {
+    const int n_g = P.n_g, T = P.T;
+    for (int base = 64 * wave; base < ngb * KBLK; base += 256) {
+        const int slot = base + lane;
+        const bool inr = slot < n_g;
+        const int pos = inr ? P.glob[slot] : T;
+        const bool padded = PAD && inr && padrow[pos] != 0;
+        int cls = kNotInClass;
+        const int dpos = pos - tk.c;
+        if (inr && dpos >= 0) {
+            const int q = dpos / tk.delta;
+            if (q * tk.delta == dpos) cls = q;
+        }
+        if (slot < ngb * KBLK) {
+            gld[slot] = padded ? T : pos;
+            gcls[slot] = cls;
+        }
+        const uint64_t badm = __ballot(!inr || padded);
+        if (lane == 0) {
+            gbad[base >> 5] = (uint32_t)badm;
+            if (base + 32 < ngb * KBLK) gbad[(base >> 5) + 1] = (uint32_t)(badm >> 32);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+
+// (lse_i log2 e, D_i) per row; eight lanes per row, 8 channels each
+__global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ out, const float* __restrict__ lse,
+                                                   const uint16_t* __restrict__ dy, float2* __restrict__ stats,
+                                                   long long rows) {
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long row = gid >> 3;
+    const int part = (int)(gid & 7);
+    float s = 0.f;
+    float l = kNegInf;
+    if (row < rows) {
+        const u32x4 a = *(const u32x4*)(out + row * D + 8 * part);
+        const u32x4 b = *(const u32x4*)(dy + row * D + 8 * part);
+#pragma unroll
+        for (int e = 0; e < 4; e++) s += bf_lo(a[e]) * bf_lo(b[e]) + bf_hi(a[e]) * bf_hi(b[e]);
+        l = lse[row];
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (row < rows && part == 0) {
+        const bool none = !(l > kNegInf);   // a padded row
+        stats[row] = make_float2(none ? __builtin_huge_valf() : l * kLog2e, none ? 0.f : s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Shared by both band kernels: the tile's block list.  Blocks 0 .. nb-1 are
+// the band (class blocks kb_lo ..), then ngb global blocks (32 slots each),
+// then nrb random blocks (32 rows each, two per drawn block of 64); stage s
+// of the ring holds blocks 2s and 2s+1, and phase ph works on block 2s+ph.
+
+enum { kBand = 0, kGlob = 1, kRand = 2, kNone = 3 };
+
+struct Blocks {
+    int nb, ngb, nrb, nblk, kb_lo;
+    __device__ __forceinline__ int kind(int j) const {
+        return j < nb ? kBand : (j < nb + ngb ? kGlob : (j < nblk ? kRand : kNone));
+    }
+};
+
+// ---------------------------------------------------------------------------
+// dq.  Per block in LDS: K row form at 0, V row form at 4096, K tr form at
+// 8192.  Waves (qb, ph): qb = query block of the tile, ph = key phase.  A
+// wave of query block 0 loads K row form and V row form pieces 0-1 of its
+// phase's block, one of query block 1 V row pieces 2-3 and K tr form.
+
+template <bool PAD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void dq_kernel(const BwdBandArgs A) {
+    constexpr int BLK = 12288, STAGE = 2 * BLK, RING = 2 * STAGE;
+    __shared__ __attribute__((aligned(16))) char smem[RING];
+    __shared__ __attribute__((aligned(16))) int gld[GT];
+    __shared__ __attribute__((aligned(16))) int gcls[GT];
+    __shared__ uint32_t gbad[GT / 32];
+    const Plan& P = *A.plan;
+    const int task = tile_of_block(P);
+    if (task < 0) return;
+    const Tile tk = decode_tile(P, task);
+    const int T = P.T;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    const int qb = wave & 1, ph = wave >> 1, lq = lane & 31, lg = lane >> 5;
+    const int r = tk.r, ra = tk.ra;
+    const size_t head = (size_t)tk.bh * T;
+    const uint8_t* padrow = PAD ? A.pad + (size_t)tk.b * T : nullptr;
+
+    const int mq0 = tk.m0 + 32 * qb;             // this wave's first query (class index)
+    const bool wave_active = mq0 < tk.n;
+    const int m_me = mq0 + lq;
+    const int my_pos = m_me < tk.n ? tk.c + tk.delta * m_me : -1;
+
+    Blocks bl;
+    {
+        int lo_k = tk.m0 - r; if (lo_k < 0) lo_k = 0;
+        int hi_k = tk.m0 + BM - 1 + ra; if (hi_k > tk.n - 1) hi_k = tk.n - 1;
+        bl.kb_lo = lo_k / KBLK;
+        bl.nb = hi_k / KBLK - bl.kb_lo + 1;
+        bl.ngb = P.n_g > 0 ? (P.n_g + KBLK - 1) / KBLK : 0;
+        bl.nrb = P.n_rand > 0 ? 2 * P.n_rand : 0;
+        bl.nblk = bl.nb + bl.ngb + bl.nrb;
+    }
+    const int NS = (bl.nblk + 1) >> 1;
+    // random key blocks of this query block (undilated: tile = query block)
+    const int32_t* rrow = bl.nrb > 0 ? P.rtab + ((size_t)tk.h * ((T + 63) >> 6) + (tk.m0 >> 6)) * P.n_rand : nullptr;
+    auto rand_p0 = [&](int jr) -> int {   // row 0 of random block jr, T for none
+        if (jr < 0 || jr >= bl.nrb) return T;
+        const int rho = rrow[jr >> 1];
+        return rho >= 0 ? 64 * rho + 32 * (jr & 1) : T;
+    };
+    // band blocks with keys for this wave's queries, and those needing no mask
+    int j_lo = 0, j_hi = -1, ji_lo = 0, ji_hi = -1;
+    if (wave_active) {
+        int a = mq0 - r; if (a < 0) a = 0;
+        int z = mq0 + 31 + ra; if (z > tk.n - 1) z = tk.n - 1;
+        j_lo = a / KBLK - bl.kb_lo;
+        j_hi = z / KBLK - bl.kb_lo;
+        ji_lo = ((mq0 + 31 - r + 31) >> 5) - bl.kb_lo;
+        ji_hi = min((mq0 + ra - 31) >> 5, (tk.n - 32) >> 5) - bl.kb_lo;
+    }
+
+    // ---- loads
+    const bool w0 = qb == 0;
+    const int rowR = lane >> 1, rowT0 = lane >> 2, rowT1 = 16 + (lane >> 2);
+    const uint32_t colR = 16u * ((lane & 1) ^ ((rowR >> 3) & 1)), colT = 16u * (lane & 3);
+    const uint32_t voR = (uint32_t)min((long long)tk.delta * rowR, (long long)T) * ROWB + colR;
+    const uint32_t voT0 = (uint32_t)min((long long)tk.delta * rowT0, (long long)T) * ROWB + colT;
+    const uint32_t voT1 = (uint32_t)min((long long)tk.delta * rowT1, (long long)T) * ROWB + colT;
+    const char* khead = (const char*)A.k + head * ROWB;
+    const char* vhead = (const char*)A.v + head * ROWB;
+    auto row0_of = [&](int j) -> int { return tk.c + tk.delta * (bl.kb_lo + j) * KBLK; };
+    auto win = [&](const char* base, int p0) -> __amdgpu_buffer_rsrc_t {
+        return buffer_rsrc(base + (uint64_t)p0 * ROWB, p0 < T ? (uint32_t)(T - p0) * ROWB : 0u);
+    };
+    // block jb into the ring slot at off.  pm: padded rows of the block,
+    // whose V rows and K tr-form rows load as zeros (NaN or Inf stored at a
+    // padded key must not reach a product); global slots load through gld.
+    auto issue = [&](int s, int off, uint32_t pm) {
+        const int jb = 2 * s + ph;
+        const int kd = bl.kind(jb);
+        if (kd == kNone) return;
+        char* dst = smem + off + ph * BLK;
+        __amdgpu_buffer_rsrc_t rk, rv;
+        uint32_t oR, oT0, oT1;
+        if (kd == kGlob) {
+            const int sl0 = (jb - bl.nb) * KBLK;
+            rk = buffer_rsrc(khead, (uint32_t)T * ROWB);
+            rv = buffer_rsrc(vhead, (uint32_t)T * ROWB);
+            oR = (uint32_t)gld[sl0 + rowR] * ROWB + colR;
+            oT0 = (uint32_t)gld[sl0 + rowT0] * ROWB + colT;
+            oT1 = (uint32_t)gld[sl0 + rowT1] * ROWB + colT;
+        } else {
+            // p0 is the same in every lane; said so, the descriptors stay scalar
+            const int p0 = uniform(kd == kBand ? row0_of(jb) : rand_p0(jb - bl.nb - bl.ngb));
+            rk = win(khead, p0);
+            rv = win(vhead, p0);
+            oR = voR;
+            oT0 = voT0;
+            oT1 = voT1;
+        }
+        const uint32_t oRz = PAD && ((pm >> rowR) & 1u) ? kPastEnd : oR;
+        if (w0) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) load_lds16(rk, dst + 1024 * ks, oR, 32 * ks);
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) load_lds16(rv, dst + 4096 + 1024 * ks, oRz, 32 * ks);
+        } else {
+#pragma unroll
+            for (int ks = 2; ks < 4; ks++) load_lds16(rv, dst + 4096 + 1024 * ks, oRz, 32 * ks);
+            const uint32_t a = PAD && ((pm >> rowT0) & 1u) ? kPastEnd : oT0;
+            const uint32_t b = PAD && ((pm >> rowT1) & 1u) ? kPastEnd : oT1;
+#pragma unroll
+            for (int x = 0; x < 4; x++)
+                load_lds16(rk, dst + 8192 + (x >> 1) * 2048 + (x & 1) * 1024, (x & 1) ? b : a, 64 * (x >> 1));
+        }
+    };
+    // padding: lane l < 32 reads the byte of row l of this phase's block two
+    // stages ahead; a ballot one stage ahead makes the block's padded-row word
+    const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, PAD ? (uint32_t)T : 0u);
+    auto pad_at = [&](int s) -> uint32_t {
+        const int q = 2 * s + ph;
+        const int kd = bl.kind(q);
+        const int pos = kd == kBand ? row0_of(q) + tk.delta * lq
+                                    : (kd == kRand ? rand_p0(q - bl.nb - bl.ngb) + lq : T);
+        return __builtin_amdgcn_raw_buffer_load_b8(rpad, (uint32_t)min(pos, T), 0, 0);
+    };
+    auto pad_word = [&](uint32_t byte) -> uint32_t { return (uint32_t)__ballot(lane < 32 && byte != 0u); };
+
+    // this lane's query: Q and dY as operands, its statistics
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc((const char*)A.q + head * ROWB, (uint32_t)T * ROWB);
+    const __amdgpu_buffer_rsrc_t ry = buffer_rsrc((const char*)A.dy + head * ROWB, (uint32_t)T * ROWB);
+    bf16x8 qh[4], yh[4];
+    load_operand(rq, my_pos, lg, qh);
+    load_operand(ry, my_pos, lg, yh);
+    float2 st = make_float2(__builtin_huge_valf(), 0.f);
+    if (my_pos >= 0) st = ((const float2*)A.stats)[head + my_pos];
+    f32x16 acc[2] = {(f32x16){}, (f32x16){}};
+    const int kbase = ph * BLK + lq * 32 + ((lg ^ ((lq >> 3) & 1)) << 4);
+    const int tbase = ph * BLK + 8192 + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) +
+                      8 * (lane & 3);
+
+    uint32_t pm_cur = 0u, pbyte = 0u;
+    if constexpr (PAD) {
+        pm_cur = pad_at(0);
+        pbyte = pad_at(1);
+    }
+    const bool early0 = bl.kind(ph) != kGlob;
+    if (early0) issue(0, 0, 0u);
+    if (bl.ngb > 0) {
+        build_gtab<PAD>(P, tk, padrow, bl.ngb, gld, gcls, gbad, wave, lane);
+        __syncthreads();
+    }
+    if (!early0) issue(0, 0, 0u);
+    barrier_lds_loads();
+    const float nl = -st.x, Dq = st.y;
+    if constexpr (PAD) {
+        pm_cur = pad_word(pm_cur);
+        // stage 0 went out before its padding word was known: clear what this
+        // wave brought for padded rows
+        if (pm_cur != 0u) {
+            char* dst = smem + ph * BLK + 16 * lane;
+            const bool pR = (pm_cur >> rowR) & 1u, pT0 = (pm_cur >> rowT0) & 1u, pT1 = (pm_cur >> rowT1) & 1u;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            if (w0) {
+                if (pR) {
+                    *(u32x4*)(dst + 4096) = z;
+                    *(u32x4*)(dst + 5120) = z;
+                }
+            } else {
+                if (pR) {
+                    *(u32x4*)(dst + 6144) = z;
+                    *(u32x4*)(dst + 7168) = z;
+                }
+#pragma unroll
+                for (int x = 0; x < 4; x++)
+                    if ((x & 1) ? pT1 : pT0) *(u32x4*)(dst + 8192 + (x >> 1) * 2048 + (x & 1) * 1024) = z;
+            }
+        }
+        __syncthreads();
+    }
+
+    for (int s = 0; s < NS; s++) {
+        if (s > 0) barrier_lds_loads();   // stage s landed; stage s-1 no longer read
+        const int oc = (s & 1) * STAGE, on = ((s + 1) & 1) * STAGE;
+        const int j = 2 * s + ph;
+        const int kd = bl.kind(j);
+        const bool rel = kd == kBand ? (j >= j_lo && j <= j_hi) : (kd != kNone && wave_active);
+        bf16x8 kf[4], vf[4];
+        if (rel) {
+            read_rows(smem + oc + kbase, kf);
+            read_rows(smem + oc + 4096 + kbase, vf);
+        }
+        uint32_t pm_next = 0u;
+        if constexpr (PAD) {
+            pm_next = pad_word(pbyte);
+            pbyte = pad_at(s + 2);
+        }
+        if (s + 1 < NS) issue(s + 1, on, pm_next);
+        if (rel) {
+            f32x16 sc = {}, dp = {};
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) sc = mfma(kf[ks], qh[ks], sc);
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) dp = mfma(vf[ks], yh[ks], dp);
+            // K^T operands, read while the products run
+            bf16x8 tf[2][2];
+            read_tr(smem + oc + tbase, tf);
+            if (kd == kBand) {
+                if (!(j >= ji_lo && j <= ji_hi && (!PAD || pm_cur == 0u))) {
+                    mask_window(sc, m_me - r - (bl.kb_lo + j) * KBLK - 4 * lg, r + ra);
+                    const int valid = tk.n - (bl.kb_lo + j) * KBLK;
+                    uint32_t bad = valid >= KBLK ? 0u : (0xffffffffu << valid);
+                    if constexpr (PAD) bad |= pm_cur;
+                    if (bad != 0u) mask_bits(sc, ~lane_bits(bad, lg));
+                }
+            } else if (kd == kGlob) {
+                const int sl0 = (j - bl.nb) * KBLK;
+                mask_global(sc, gbad[sl0 >> 5], gcls + sl0, m_me, r, r + ra, lg);
+            } else {
+                // random keys: not in this query's window, not global, not padded
+                const int p0 = rand_p0(j - bl.nb - bl.ngb);
+                mask_window_out(sc, m_me - r - p0 - 4 * lg, r + ra);
+                uint32_t bad = past_end(p0, T);
+                if (p0 < T) bad |= A.gmap[p0 >> 5];
+                if constexpr (PAD) bad |= pm_cur;
+                if (bad != 0u) mask_bits(sc, ~lane_bits(bad, lg));
+            }
+            float ds[16];
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], SC, nl));
+                ds[i] = p * (dp[i] - Dq);
+            }
+            bf16x8 dso[2];
+            pack_operand(ds, dso);
+#pragma unroll
+            for (int st2 = 0; st2 < 2; st2++)
+#pragma unroll
+                for (int cb = 0; cb < 2; cb++) acc[cb] = mfma(tf[st2][cb], dso[st2], acc[cb]);
+        }
+        pm_cur = pm_next;
+    }
+    __syncthreads();
+
+    // the two phases' sums meet through LDS
+    f32x4* mbuf = (f32x4*)smem + (qb * 64 + lane) * 8;
+    if (ph == 1) {
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                mbuf[4 * cb + i] = (f32x4){acc[cb][4 * i], acc[cb][4 * i + 1], acc[cb][4 * i + 2], acc[cb][4 * i + 3]};
+    }
+    __syncthreads();
+    if (ph == 1 || my_pos < 0) return;
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const f32x4 x = mbuf[4 * cb + i];
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[cb][4 * i + e] += x[e];
+        }
+    if (is_global(A.gmap, my_pos)) return;   // the global-row kernels write it
+    const bool zero = PAD && padrow[my_pos] != 0;
+    store_row((uint16_t*)A.dq + (head + my_pos) * D, acc, 0.125f, zero, lg);
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv.  Per block in LDS: Q row form at 0, dY row form at 4096, Q tr form
+// at 8192, dY tr form at 12288, then the block's 32 values lse log2 e and
+// 32 values D at 16384.  Waves (kb, ph): kb = key block of the tile, ph =
+// query phase.  A wave of key block 0 loads the row forms of its phase's
+// block, one of key block 1 the tr forms and the statistics.
+
+template <bool PAD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dkdv_kernel(const BwdBandArgs A) {
+    constexpr int BLK = 16384 + 256, STAGE = 2 * BLK, RING = 2 * STAGE;
+    __shared__ __attribute__((aligned(16))) char smem[RING];
+    __shared__ __attribute__((aligned(16))) int gld[GT];
+    __shared__ __attribute__((aligned(16))) int gcls[GT];
+    __shared__ uint32_t gbad[GT / 32];
+    const Plan& P = *A.plan;
+    const int task = tile_of_block(P);
+    if (task < 0) return;
+    const Tile tk = decode_tile(P, task);
+    const int T = P.T;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    const int kb = wave & 1, ph = wave >> 1, lq = lane & 31, lg = lane >> 5;
+    const int r = tk.r, ra = tk.ra;
+    const size_t head = (size_t)tk.bh * T;
+    const uint8_t* padrow = PAD ? A.pad + (size_t)tk.b * T : nullptr;
+
+    const int mk0 = tk.m0 + 32 * kb;             // this wave's first key (class index)
+    const bool wave_active = mk0 < tk.n;
+    const int m_me = mk0 + lq;
+    const int my_pos = m_me < tk.n ? tk.c + tk.delta * m_me : -1;
+
+    // query t reads key u when u - t is in [-r, ra]: key u is read by the
+    // queries [u - ra, u + r]
+    Blocks bl;
+    {
+        int lo_q = tk.m0 - ra; if (lo_q < 0) lo_q = 0;
+        int hi_q = tk.m0 + BM - 1 + r; if (hi_q > tk.n - 1) hi_q = tk.n - 1;
+        bl.kb_lo = lo_q / KBLK;
+        bl.nb = hi_q / KBLK - bl.kb_lo + 1;
+        bl.ngb = P.n_g > 0 ? (P.n_g + KBLK - 1) / KBLK : 0;
+        bl.nrb = 0;
+    }
+    // random blocks: the query blocks that drew this key block (undilated)
+    int ioff = 0;
+    if (P.n_rand > 0) {
+        const int32_t* off = A.inv_off + (size_t)tk.h * (((T + 63) >> 6) + 1) + (tk.m0 >> 6);
+        ioff = off[0];
+        bl.nrb = 2 * (off[1] - off[0]);
+    }
+    bl.nblk = bl.nb + bl.ngb + bl.nrb;
+    const int NS = (bl.nblk + 1) >> 1;
+    auto rand_p0 = [&](int jr) -> int {
+        if (jr < 0 || jr >= bl.nrb) return T;
+        return 64 * A.inv_list[ioff + (jr >> 1)] + 32 * (jr & 1);
+    };
+    int j_lo = 0, j_hi = -1, ji_lo = 0, ji_hi = -1;
+    if (wave_active) {
+        int a = mk0 - ra; if (a < 0) a = 0;
+        int z = mk0 + 31 + r; if (z > tk.n - 1) z = tk.n - 1;
+        j_lo = a / KBLK - bl.kb_lo;
+        j_hi = z / KBLK - bl.kb_lo;
+        // every query q0 .. q0+31 of the block reads every key mk0 .. mk0+31
+        ji_lo = ((mk0 + 31 - ra + 31) >> 5) - bl.kb_lo;
+        ji_hi = min((mk0 + r - 31) >> 5, (tk.n - 32) >> 5) - bl.kb_lo;
+    }
+
+    // ---- loads
+    const bool w0 = kb == 0;
+    const int rowR = lane >> 1, rowT0 = lane >> 2, rowT1 = 16 + (lane >> 2);
+    const uint32_t colR = 16u * ((lane & 1) ^ ((rowR >> 3) & 1)), colT = 16u * (lane & 3);
+    const uint32_t voR = (uint32_t)min((long long)tk.delta * rowR, (long long)T) * ROWB + colR;
+    const uint32_t voT0 = (uint32_t)min((long long)tk.delta * rowT0, (long long)T) * ROWB + colT;
+    const uint32_t voT1 = (uint32_t)min((long long)tk.delta * rowT1, (long long)T) * ROWB + colT;
+    // statistics: lane l < 32 brings the lse of row l, lane l >= 32 the D of row l - 32
+    const uint32_t voS = (uint32_t)min((long long)tk.delta * lq, (long long)T) * 8u + 4u * lg;
+    const char* qhead = (const char*)A.q + head * ROWB;
+    const char* yhead = (const char*)A.dy + head * ROWB;
+    const char* shead = (const char*)(A.stats + 2 * head);
+    auto row0_of = [&](int j) -> int { return tk.c + tk.delta * (bl.kb_lo + j) * KBLK; };
+    auto win = [&](const char* base, int p0, int rb) -> __amdgpu_buffer_rsrc_t {
+        return buffer_rsrc(base + (uint64_t)p0 * rb, p0 < T ? (uint32_t)(T - p0) * rb : 0u);
+    };
+    // block jb into the ring slot at off; pm: padded query rows, loaded as
+    // zeros in every form (their statistics give them zero weight)
+    auto issue = [&](int s, int off, uint32_t pm) {
+        const int jb = 2 * s + ph;
+        const int kd = bl.kind(jb);
+        if (kd == kNone) return;
+        char* dst = smem + off + ph * BLK;
+        __amdgpu_buffer_rsrc_t rq, ry, rs;
+        uint32_t oR, oT0, oT1, oS;
+        if (kd == kGlob) {
+            const int sl0 = (jb - bl.nb) * KBLK;
+            rq = buffer_rsrc(qhead, (uint32_t)T * ROWB);
+            ry = buffer_rsrc(yhead, (uint32_t)T * ROWB);
+            rs = buffer_rsrc(shead, (uint32_t)T * 8u);
+            oR = (uint32_t)gld[sl0 + rowR] * ROWB + colR;
+            oT0 = (uint32_t)gld[sl0 + rowT0] * ROWB + colT;
+            oT1 = (uint32_t)gld[sl0 + rowT1] * ROWB + colT;
+            oS = (uint32_t)gld[sl0 + lq] * 8u + 4u * lg;
+        } else {
+            const int p0 = uniform(kd == kBand ? row0_of(jb) : rand_p0(jb - bl.nb - bl.ngb));
+            rq = win(qhead, p0, ROWB);
+            ry = win(yhead, p0, ROWB);
+            rs = win(shead, p0, 8);
+            oR = voR;
+            oT0 = voT0;
+            oT1 = voT1;
+            oS = voS;
+        }
+        if (w0) {
+            const uint32_t o = PAD && ((pm >> rowR) & 1u) ? kPastEnd : oR;
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) load_lds16(rq, dst + 1024 * ks, o, 32 * ks);
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) load_lds16(ry, dst + 4096 + 1024 * ks, o, 32 * ks);
+        } else {
+            const uint32_t a = PAD && ((pm >> rowT0) & 1u) ? kPastEnd : oT0;
+            const uint32_t b = PAD && ((pm >> rowT1) & 1u) ? kPastEnd : oT1;
+#pragma unroll
+            for (int x = 0; x < 4; x++) {
+                const uint32_t o = (x & 1) ? b : a;
+                load_lds16(rq, dst + 8192 + (x >> 1) * 2048 + (x & 1) * 1024, o, 64 * (x >> 1));
+                load_lds16(ry, dst + 12288 + (x >> 1) * 2048 + (x & 1) * 1024, o, 64 * (x >> 1));
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(dst + 16384), 4, oS, 0, 0, 0);
+        }
+    };
+    const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, PAD ? (uint32_t)T : 0u);
+    auto pad_at = [&](int s) -> uint32_t {
+        const int q = 2 * s + ph;
+        const int kd = bl.kind(q);
+        const int pos = kd == kBand ? row0_of(q) + tk.delta * lq
+                                    : (kd == kRand ? rand_p0(q - bl.nb - bl.ngb) + lq : T);
+        return __builtin_amdgcn_raw_buffer_load_b8(rpad, (uint32_t)min(pos, T), 0, 0);
+    };
+    auto pad_word = [&](uint32_t byte) -> uint32_t { return (uint32_t)__ballot(lane < 32 && byte != 0u); };
+
+    // this lane's key: K and V as operands
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((const char*)A.k + head * ROWB, (uint32_t)T * ROWB);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc((const char*)A.v + head * ROWB, (uint32_t)T * ROWB);
+    bf16x8 kh[4], vh[4];
+    load_operand(rk, my_pos, lg, kh);
+    load_operand(rv, my_pos, lg, vh);
+    f32x16 ak[2] = {(f32x16){}, (f32x16){}}, av[2] = {(f32x16){}, (f32x16){}};
+    const int rbase = ph * BLK + lq * 32 + ((lg ^ ((lq >> 3) & 1)) << 4);
+    const int tbase = ph * BLK + 8192 + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) +
+                      8 * (lane & 3);
+    const int sbase = ph * BLK + 16384 + 16 * lg;   // lse of this lane's rows 8q4 + 4lg .. +3 at +32 q4
+
+    uint32_t pm_cur = 0u, pbyte = 0u;
+    if constexpr (PAD) {
+        pm_cur = pad_at(0);
+        pbyte = pad_at(1);
+    }
+    const bool early0 = bl.kind(ph) != kGlob;
+    if (early0) issue(0, 0, 0u);
+    if (bl.ngb > 0) {
+        build_gtab<PAD>(P, tk, padrow, bl.ngb, gld, gcls, gbad, wave, lane);
+        __syncthreads();
+    }
+    if (!early0) issue(0, 0, 0u);
+    barrier_lds_loads();
+    if constexpr (PAD) {
+        pm_cur = pad_word(pm_cur);
+        if (pm_cur != 0u) {
+            char* dst = smem + ph * BLK + 16 * lane;
+            const bool pR = (pm_cur >> rowR) & 1u, pT0 = (pm_cur >> rowT0) & 1u, pT1 = (pm_cur >> rowT1) & 1u;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            if (w0) {
+                if (pR) {
+#pragma unroll
+                    for (int ks = 0; ks < 8; ks++) *(u32x4*)(dst + 1024 * ks) = z;
+                }
+            } else {
+#pragma unroll
+                for (int x = 0; x < 4; x++)
+                    if ((x & 1) ? pT1 : pT0) {
+                        *(u32x4*)(dst + 8192 + (x >> 1) * 2048 + (x & 1) * 1024) = z;
+                        *(u32x4*)(dst + 12288 + (x >> 1) * 2048 + (x & 1) * 1024) = z;
+                    }
+            }
+        }
+        __syncthreads();
+    }
+
+    for (int s = 0; s < NS; s++) {
+        if (s > 0) barrier_lds_loads();
+        const int oc = (s & 1) * STAGE, on = ((s + 1) & 1) * STAGE;
+        const int j = 2 * s + ph;
+        const int kd = bl.kind(j);
+        const bool rel = kd == kBand ? (j >= j_lo && j <= j_hi) : (kd != kNone && wave_active);
+        bf16x8 qf[4], yf[4];
+        if (rel) {
+            read_rows(smem + oc + rbase, qf);
+            read_rows(smem + oc + 4096 + rbase, yf);
+        }
+        uint32_t pm_next = 0u;
+        if constexpr (PAD) {
+            pm_next = pad_word(pbyte);
+            pbyte = pad_at(s + 2);
+        }
+        if (s + 1 < NS) issue(s + 1, on, pm_next);
+        if (rel) {
+            f32x16 sc = {}, dp = {};
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) sc = mfma(qf[ks], kh[ks], sc);
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) dp = mfma(yf[ks], vh[ks], dp);
+            // statistics and the transposed operands, read while the products run
+            f32x4 l4[4], d4[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++) {
+                l4[q4] = *(const f32x4*)(smem + oc + sbase + 32 * q4);
+                d4[q4] = *(const f32x4*)(smem + oc + sbase + 128 + 32 * q4);
+            }
+            bf16x8 qt[2][2], yt[2][2];
+            read_tr(smem + oc + tbase, qt);
+            read_tr(smem + oc + 4096 + tbase, yt);
+            // element i: query row 8(i>>2) + 4lg + (i&3) of the block, this lane's key
+            if (kd == kBand) {
+                if (!(j >= ji_lo && j <= ji_hi)) {
+                    mask_window(sc, m_me - ra - (bl.kb_lo + j) * KBLK - 4 * lg, r + ra);
+                    const int valid = tk.n - (bl.kb_lo + j) * KBLK;
+                    if (valid < KBLK) mask_bits(sc, ~lane_bits(0xffffffffu << valid, lg));
+                }
+            } else if (kd == kGlob) {
+                const int sl0 = (j - bl.nb) * KBLK;
+                mask_global(sc, gbad[sl0 >> 5], gcls + sl0, m_me, ra, r + ra, lg);
+            } else {
+                // random queries: this key outside their window, not global
+                const int p0 = rand_p0(j - bl.nb - bl.ngb);
+                mask_window_out(sc, m_me - ra - p0 - 4 * lg, r + ra);
+                uint32_t bad = past_end(p0, T);
+                if (p0 < T) bad |= A.gmap[p0 >> 5];
+                if (bad != 0u) mask_bits(sc, ~lane_bits(bad, lg));
+            }
+            float p[16], ds[16];
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], SC, -l4[i >> 2][i & 3]));
+                ds[i] = p[i] * (dp[i] - d4[i >> 2][i & 3]);
+            }
+            bf16x8 po[2], dso[2];
+            pack_operand(p, po);
+            pack_operand(ds, dso);
+#pragma unroll
+            for (int st2 = 0; st2 < 2; st2++)
+#pragma unroll
+                for (int cb = 0; cb < 2; cb++) {
+                    av[cb] = mfma(yt[st2][cb], po[st2], av[cb]);
+                    ak[cb] = mfma(qt[st2][cb], dso[st2], ak[cb]);
+                }
+        }
+        pm_cur = pm_next;
+    }
+    __syncthreads();
+
+    f32x4* mbuf = (f32x4*)smem + (kb * 64 + lane) * 16;
+    if (ph == 1) {
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                mbuf[4 * cb + i] = (f32x4){ak[cb][4 * i], ak[cb][4 * i + 1], ak[cb][4 * i + 2], ak[cb][4 * i + 3]};
+                mbuf[8 + 4 * cb + i] = (f32x4){av[cb][4 * i], av[cb][4 * i + 1], av[cb][4 * i + 2], av[cb][4 * i + 3]};
+            }
+    }
+    __syncthreads();
+    if (ph == 1 || my_pos < 0) return;
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const f32x4 x = mbuf[4 * cb + i], y = mbuf[8 + 4 * cb + i];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                ak[cb][4 * i + e] += x[e];
+                av[cb][4 * i + e] += y[e];
+            }
+        }
+    if (is_global(A.gmap, my_pos)) return;   // the global-key kernels write it
+    const bool zero = PAD && padrow[my_pos] != 0;
+    store_row((uint16_t*)A.dk + (head + my_pos) * D, ak, 0.125f, zero, lg);
+    store_row((uint16_t*)A.dv + (head + my_pos) * D, av, 1.0f, zero, lg);
+}
+
+}  // namespace bwd
+}  // namespace lfk
+
+extern "C" int lfk_bwd_band_grid(const lfk::Plan* P) { return 8 * ((P->n_band_tasks + 7) / 8); }
+
+extern "C" hipError_t lfk_bwd_prep(const void* out, const float* lse, const void* dy, float2* stats, long long rows,
+                                   void* stream) {
+    const long long threads = rows * 8;
+    hipLaunchKernelGGL(lfk::bwd::prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, (const uint16_t*)out, lse, (const uint16_t*)dy, stats, rows);
+    return hipGetLastError();
+}
+
+// A: argument of both band kernels (A->plan: device copy of *P)
+extern "C" hipError_t lfk_bwd_band(const lfk::BwdBandArgs* A, const lfk::Plan* P, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 g(lfk_bwd_band_grid(P)), b(256);
+    if (A->pad) {
+        hipLaunchKernelGGL(lfk::bwd::dq_kernel<true>, g, b, 0, s, *A);
+        hipLaunchKernelGGL(lfk::bwd::dkdv_kernel<true>, g, b, 0, s, *A);
+    } else {
+        hipLaunchKernelGGL(lfk::bwd::dq_kernel<false>, g, b, 0, s, *A);
+        hipLaunchKernelGGL(lfk::bwd::dkdv_kernel<false>, g, b, 0, s, *A);
+    }
+    return hipGetLastError();
+}

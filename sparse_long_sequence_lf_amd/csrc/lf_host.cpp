@@ -26,6 +26,10 @@ extern "C" int lfk_supports_d(int d);
 extern "C" hipError_t lfk_noalloc_scratch(void **ptr);
 extern "C" hipError_t lfk_write_plan(const void *plan, size_t bytes, void *dst, int *zero, int n_zero, void *stream);
 extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs *A, const void *const *t, int dtype_bf16, void *stream);
+extern "C" hipError_t lfk_bwd_global_launch(const lfk::BwdArgs *A, const void *const *t, void *stream);
+extern "C" hipError_t lfk_bwd_prep(const void *out, const float *lse, const void *dy, float2 *stats, long long rows,
+                                   void *stream);
+extern "C" hipError_t lfk_bwd_band(const lfk::BwdBandArgs *A, const lfk::Plan *P, void *stream);
 
 namespace {
 
@@ -71,6 +75,7 @@ struct Workspace {
     bool shadow_valid = false;
     std::vector<uint32_t> aux_shadow;   // what aux holds: random-block table and global bitmap
     Buffer bwd_tab, bwd_stats, bwd_gpart;   // backward: tables; row statistics; global-split records
+    Buffer bwd_fwd;                   // backward (bf16) without the forward's results: its output and lse
     std::vector<uint32_t> bwd_shadow;   // what bwd_tab holds
 };
 std::mutex g_ws_mu;
@@ -153,17 +158,19 @@ lf_status_t upload_plan(Workspace &w, const lfk::Plan &P, void *stream, const lf
 
 extern "C" const char *lf_last_error(void) { return g_err.c_str(); }
 
+#ifndef LF_SOURCE_HASH
+#define LF_SOURCE_HASH "unset"
+#endif
+extern "C" const char *lf_build_hash(void) { return LF_SOURCE_HASH; }
+
 namespace {
 
-// The call behind both entry points: radius is NULL (r for every head) or
-// one radius per head.
-lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T, int d, int r,
-                     const int32_t *radius, int one_sided, const int32_t *rand_blocks, int n_rand,
-                     const int32_t *dilation, const int32_t *global_idx, int n_global,
-                     const uint8_t *key_padding_mask, void *out, float *lse, lf_dtype_t dtype, void *stream,
-                     bool noalloc = false) {
-    g_err.clear();
-    // ---- argument checks: no HIP call before all of them pass
+// Argument checks of a forward call (no HIP call): radius is NULL (r for
+// every head) or one radius per head.
+lf_status_t check_fwd(const void *q, const void *k, const void *v, int B, int H, int T, int d, int r,
+                      const int32_t *radius, int one_sided, const int32_t *rand_blocks, int n_rand,
+                      const int32_t *dilation, const int32_t *global_idx, int n_global, const void *out,
+                      const float *lse, lf_dtype_t dtype) {
     if (!q || !k || !v || !out) return fail(LF_E_INVALID, "q, k, v and out must be non-null");
     if (dtype != LF_F32 && dtype != LF_BF16) return fail(LF_E_UNSUPPORTED, "unknown dtype %d", (int)dtype);
     if (B < 1 || H < 1 || T < 1) return fail(LF_E_INVALID, "B, H, T must be >= 1 (got %d, %d, %d)", B, H, T);
@@ -222,6 +229,27 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
                 overlaps(lse, lbytes, v, nbytes) || overlaps(lse, lbytes, out, nbytes)))
         return fail(LF_E_INVALID, "lse overlaps q, k, v or out");
 
+    return LF_OK;
+}
+
+// What a forward call needs besides its tensors: the plan (workspace
+// pointers still unset), the random-block table with the global bitmap, and
+// the sizes of its workspace parts.
+struct FwdPlan {
+    lfk::Plan P;
+    std::vector<uint32_t> aux;   // rtab [H][ceil(T/64)][n_rand], then the global bitmap [ceil(T/32)]
+    size_t cnt_bytes = 0;        // global-row completion counters
+    size_t scratch_bytes = 0;    // global-row partial records, then (fp32) the planes of K and V
+    size_t planes_off = 0, plane_bytes = 0;
+};
+
+// The plan of a checked forward call (no HIP call).
+lf_status_t plan_fwd(int B, int H, int T, int d, int r, const int32_t *radius, int one_sided,
+                     const int32_t *rand_blocks, int n_rand, const int32_t *dilation, const int32_t *global_idx,
+                     int n_global, lf_dtype_t dtype, FwdPlan &F) {
+    const long long nqb = cdiv(T, 64);
+    const size_t esize = dtype == LF_BF16 ? 2 : 4;
+    const size_t nbytes = (size_t)B * (size_t)H * (size_t)T * (size_t)d * esize;
     // ---- normalise G: a set of positions, ascending
     std::vector<int32_t> G(global_idx, global_idx + n_global);
     std::sort(G.begin(), G.end());
@@ -231,7 +259,7 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
 
     // ---- plan
     constexpr int BM = LFK_BM;
-    lfk::Plan P;
+    lfk::Plan &P = F.P;
     std::memset(&P, 0, sizeof P);
     P.B = B; P.H = H; P.T = T; P.d = d;
     // |i - j| < T always, so radii beyond T change nothing
@@ -245,7 +273,8 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
     // random key blocks: each query block's list sorted, duplicates dropped
     // (-1 fills the rest), then a bitmap of the global positions (a random
     // block leaves the globals to their own path)
-    std::vector<uint32_t> aux;
+    std::vector<uint32_t> &aux = F.aux;
+    aux.clear();
     if (n_rand > 0) {
         const size_t nt = (size_t)H * nqb * n_rand;
         aux.resize(nt + (size_t)cdiv(T, 32), 0u);
@@ -269,7 +298,8 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
     const long long start = lfk::fill_band_plan(P, B, H, T, dilation);
     const long long n_band = (long long)B * start;
     long long n_glob_tasks = 0;
-    size_t cnt_bytes = 0, scratch_bytes = 0;
+    size_t &cnt_bytes = F.cnt_bytes, &scratch_bytes = F.scratch_bytes;
+    cnt_bytes = scratch_bytes = 0;
     if (P.n_g > 0) {
         P.n_ggroups = (int)cdiv(P.n_g, BM);
         P.g_pad = P.n_ggroups * BM;
@@ -299,21 +329,82 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
     P.n_tasks = (int)(n_band + n_glob_tasks);
     // fp32: K and V are split into three bf16 planes per row (1.5 times the
     // fp32 tensors' bytes) ahead of the tile kernel
-    size_t planes_off = 0;
-    const size_t plane_bytes = nbytes / 4 * 6;
+    F.planes_off = 0;
+    F.plane_bytes = nbytes / 4 * 6;
     if (dtype == LF_F32) {
         if ((long long)B * H * T * (d / 8) / 256 >= (1LL << 31))
             return fail(LF_E_UNSUPPORTED, "fp32 problem too large for the plane split");
-        planes_off = (scratch_bytes + 255) / 256 * 256;
-        scratch_bytes = planes_off + 2 * plane_bytes;
+        F.planes_off = (scratch_bytes + 255) / 256 * 256;
+        scratch_bytes = F.planes_off + 2 * F.plane_bytes;
     }
 
+    return LF_OK;
+}
+
+// With g_ws_mu held: the stream's workspace for the plan (counters,
+// partials, planes, random-block table) and the plan on the device.
+lf_status_t bind_fwd(Workspace &w, FwdPlan &F, bool fp32, void *stream, const lfk::Plan **dev_plan) {
+    if (F.scratch_bytes > 0) {
+        lf_status_t st = grow(w.counters, F.cnt_bytes, true, stream);
+        if (st != LF_OK) return st;
+        st = grow(w.scratch, F.scratch_bytes, false, stream);
+        if (st != LF_OK) return st;
+        char *ws = (char *)w.scratch.ptr;
+        if (F.P.n_g > 0) {
+            F.P.counter = (int *)w.counters.ptr;
+            F.P.part = (float *)ws;
+        }
+        if (fp32) {
+            F.P.kp = ws + F.planes_off;
+            F.P.vp = ws + F.planes_off + F.plane_bytes;
+        }
+    }
+    if (F.P.n_rand > 0) {
+        lf_status_t st = grow(w.aux, F.aux.size() * sizeof(uint32_t), false, stream);
+        if (st != LF_OK) return st;
+        if (w.aux_shadow != F.aux) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
+            if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+            if (cs != hipStreamCaptureStatusNone)
+                return fail(LF_E_UNSUPPORTED,
+                            "the random key blocks differ from the previous call on this stream during stream "
+                            "capture; make one identical call outside capture first");
+            e = upload(w.aux.ptr, F.aux.data(), F.aux.size() * sizeof(uint32_t), stream);
+            if (e != hipSuccess) {
+                w.aux_shadow.clear();
+                return fail(LF_E_HIP, "random-block upload: %s", hipGetErrorString(e));
+            }
+            w.aux_shadow = F.aux;
+        }
+        F.P.rtab = (const int32_t *)w.aux.ptr;
+        F.P.gmap = (const uint32_t *)w.aux.ptr + (size_t)F.P.H * cdiv(F.P.T, 64) * F.P.n_rand;
+    }
+    return upload_plan(w, F.P, stream, dev_plan);
+}
+
+// The call behind the forward entry points: radius is NULL (r for every
+// head) or one radius per head.
+lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T, int d, int r,
+                     const int32_t *radius, int one_sided, const int32_t *rand_blocks, int n_rand,
+                     const int32_t *dilation, const int32_t *global_idx, int n_global,
+                     const uint8_t *key_padding_mask, void *out, float *lse, lf_dtype_t dtype, void *stream,
+                     bool noalloc = false) {
+    g_err.clear();
+    // no HIP call before every check has passed
+    lf_status_t st = check_fwd(q, k, v, B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation,
+                               global_idx, n_global, out, lse, dtype);
+    if (st != LF_OK) return st;
+    FwdPlan F;
+    st = plan_fwd(B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation, global_idx, n_global, dtype, F);
+    if (st != LF_OK) return st;
+    lfk::Plan &P = F.P;
     if (noalloc) {
         // the static scratch array: plan, counters, partial records, planes
         auto up = [](size_t x) { return (x + 255) / 256 * 256; };
         const size_t plan_bytes = up(sizeof(lfk::Plan));
-        const size_t cnt_off = plan_bytes, part_off = cnt_off + up(cnt_bytes);
-        const size_t total = part_off + scratch_bytes;
+        const size_t cnt_off = plan_bytes, part_off = cnt_off + up(F.cnt_bytes);
+        const size_t total = part_off + F.scratch_bytes;
         if (n_rand > 0) return fail(LF_E_UNSUPPORTED, "random key blocks are not taken without allocation");
         if (total > (size_t)LF_NOALLOC_SCRATCH_BYTES)
             return fail(LF_E_UNSUPPORTED,
@@ -328,8 +419,8 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
             P.part = (float *)ws;
         }
         if (dtype == LF_F32) {
-            P.kp = ws + planes_off;
-            P.vp = ws + planes_off + plane_bytes;
+            P.kp = ws + F.planes_off;
+            P.vp = ws + F.planes_off + F.plane_bytes;
         }
         e = lfk_write_plan(&P, sizeof P, base, P.n_g > 0 ? P.counter : nullptr, P.n_g > 0 ? B * H : 0, stream);
         if (e != hipSuccess) return fail(LF_E_HIP, "plan copy launch: %s", hipGetErrorString(e));
@@ -343,65 +434,34 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
         return LF_OK;
     }
 
-    // ---- HIP work
     std::lock_guard<std::mutex> lock(g_ws_mu);
     Workspace *w = workspace_for(stream);
     if (!w) return fail(LF_E_HIP, "hipGetDevice failed");
-    if (scratch_bytes > 0) {
-        lf_status_t st = grow(w->counters, cnt_bytes, true, stream);
-        if (st != LF_OK) return st;
-        st = grow(w->scratch, scratch_bytes, false, stream);
-        if (st != LF_OK) return st;
-        char *ws = (char *)w->scratch.ptr;
-        if (P.n_g > 0) {
-            P.counter = (int *)w->counters.ptr;
-            P.part = (float *)ws;
-        }
-        if (dtype == LF_F32) {
-            P.kp = ws + planes_off;
-            P.vp = ws + planes_off + plane_bytes;
-        }
-    }
-    if (n_rand > 0) {
-        lf_status_t st = grow(w->aux, aux.size() * sizeof(uint32_t), false, stream);
-        if (st != LF_OK) return st;
-        if (w->aux_shadow != aux) {
-            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-            hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
-            if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
-            if (cs != hipStreamCaptureStatusNone)
-                return fail(LF_E_UNSUPPORTED,
-                            "the random key blocks differ from the previous call on this stream during stream "
-                            "capture; make one identical call outside capture first");
-            e = upload(w->aux.ptr, aux.data(), aux.size() * sizeof(uint32_t), stream);
-            if (e != hipSuccess) {
-                w->aux_shadow.clear();
-                return fail(LF_E_HIP, "random-block upload: %s", hipGetErrorString(e));
-            }
-            w->aux_shadow = aux;
-        }
-        P.rtab = (const int32_t *)w->aux.ptr;
-        P.gmap = (const uint32_t *)w->aux.ptr + (size_t)H * nqb * n_rand;
-    }
     lfk::Args A;
     A.q = q; A.k = k; A.v = v; A.out = out;
     A.pad = key_padding_mask;
     A.lse = lse;
-    lf_status_t st = upload_plan(*w, P, stream, &A.plan);
+    st = bind_fwd(*w, F, dtype == LF_F32, stream, &A.plan);
     if (st != LF_OK) return st;
     hipError_t e = lfk_launch(&A, &P, dtype == LF_BF16, stream);
     if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
     return LF_OK;
 }
 
-// Gradients (lf_attn_bwd): checks, the per-head tables, four launches.
-lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy, int B, int H, int T, int d,
-                     const int32_t *radius, int one_sided, const int32_t *rand_blocks, int n_rand,
-                     const int32_t *dilation, const int32_t *global_idx, int n_global,
-                     const uint8_t *key_padding_mask, void *dq, void *dk, void *dv, lf_dtype_t dtype,
+// Gradients (lf_attn_bwd, lf_attn_bwd_ex): checks, the tables, the launches.
+// bf16: the forward's output and statistics (given, or computed here into
+// the workspace), the row statistics, the global rows' and keys' vector
+// kernels, then the matrix-core band kernels.  fp32: the vector kernels,
+// which find the statistics themselves (out and lse are not read).
+lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy, const void *out,
+                     const float *lse, int B, int H, int T, int d, const int32_t *radius, int one_sided,
+                     const int32_t *rand_blocks, int n_rand, const int32_t *dilation, const int32_t *global_idx,
+                     int n_global, const uint8_t *key_padding_mask, void *dq, void *dk, void *dv, lf_dtype_t dtype,
                      void *stream) {
     if (!q || !k || !v || !dy || !dq || !dk || !dv)
         return fail(LF_E_INVALID, "q, k, v, dy, dq, dk and dv must be non-null");
+    if ((out == nullptr) != (lse == nullptr))
+        return fail(LF_E_INVALID, "out and lse are given together or not at all");
     if (!radius) return fail(LF_E_INVALID, "radius must be a host array of H radii");
     if (dtype != LF_F32 && dtype != LF_BF16) return fail(LF_E_UNSUPPORTED, "unknown dtype %d", (int)dtype);
     if (B < 1 || H < 1 || T < 1) return fail(LF_E_INVALID, "B, H, T must be >= 1 (got %d, %d, %d)", B, H, T);
@@ -450,6 +510,14 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
             if (overlaps(outs[o], nbytes, ins[e], nbytes)) return fail(LF_E_INVALID, "dq, dk, dv overlap an input");
         for (int e = o + 1; e < 3; e++)
             if (overlaps(outs[o], nbytes, outs[e], nbytes)) return fail(LF_E_INVALID, "dq, dk, dv overlap");
+    }
+    if (out) {
+        if (((uintptr_t)out & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
+            return fail(LF_E_INVALID, "out must be 16-byte and lse 4-byte aligned");
+        const size_t lbytes = (size_t)B * (size_t)H * (size_t)T * sizeof(float);
+        for (int o = 0; o < 3; o++)
+            if (overlaps(outs[o], nbytes, out, nbytes) || overlaps(outs[o], nbytes, lse, lbytes))
+                return fail(LF_E_INVALID, "dq, dk, dv overlap out or lse");
     }
     std::vector<int32_t> G(global_idx, global_idx + n_global);
     std::sort(G.begin(), G.end());
@@ -509,6 +577,14 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     }
     tab[o_hc + H] = (uint32_t)chunks;
     if ((long long)B * chunks >= (1LL << 31)) return fail(LF_E_UNSUPPORTED, "problem needs too many waves");
+    // bf16: the forward's plan (its band tiles are the band kernels' tiles)
+    const bool mfma = dtype == LF_BF16;
+    FwdPlan F;
+    if (mfma) {
+        lf_status_t st = plan_fwd(B, H, T, d, 0, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
+                                  n_global, dtype, F);
+        if (st != LF_OK) return st;
+    }
     for (size_t e = 0; e < G.size(); e++) {
         tab[o_glob + e] = (uint32_t)G[e];
         tab[o_gmap + (G[e] >> 5)] |= 1u << (G[e] & 31);
@@ -559,6 +635,8 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     A.rad = (const int32_t *)dt;
     A.dil = (const int32_t *)dt + o_dil;
     A.head_chunk = (const int32_t *)dt + o_hc;
+    A.n_chunks = (int)chunks;
+    A.stats_given = mfma ? 1 : 0;
     A.hord = (const int32_t *)dt + o_ord;
     A.stats = w->bwd_stats.ptr;
     A.B = B; A.H = H; A.T = T; A.n_g = (int)G.size(); A.one_sided = one_sided;
@@ -571,8 +649,47 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     A.inv_off = n_rand > 0 ? (const int32_t *)dt + o_off : nullptr;
     A.inv_list = n_rand > 0 ? (const int32_t *)dt + o_inv : nullptr;
     const void *t[7] = {q, k, v, dy, dq, dk, dv};
-    hipError_t e = lfk_bwd_launch(&A, t, dtype == LF_BF16, stream);
-    if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
+    if (!mfma) {
+        hipError_t e = lfk_bwd_launch(&A, t, 0, stream);
+        if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
+        return LF_OK;
+    }
+    const lfk::Plan *dplan = nullptr;
+    st = bind_fwd(*w, F, false, stream, &dplan);
+    if (st != LF_OK) return st;
+    const size_t rows = (size_t)B * H * T;
+    hipError_t e;
+    if (!out) {
+        // the forward, into the workspace: output rows, then lse
+        const size_t ybytes = (nbytes + 255) / 256 * 256;
+        st = grow(w->bwd_fwd, ybytes + rows * sizeof(float), false, stream);
+        if (st != LF_OK) return st;
+        lfk::Args FA;
+        FA.q = q; FA.k = k; FA.v = v;
+        FA.out = w->bwd_fwd.ptr;
+        FA.pad = key_padding_mask;
+        FA.lse = (float *)((char *)w->bwd_fwd.ptr + ybytes);
+        FA.plan = dplan;
+        e = lfk_launch(&FA, &F.P, 1, stream);
+        if (e != hipSuccess) return fail(LF_E_HIP, "forward launch: %s", hipGetErrorString(e));
+        out = FA.out;
+        lse = FA.lse;
+    }
+    e = lfk_bwd_prep(out, lse, dy, (float2 *)A.stats, (long long)rows, stream);
+    if (e != hipSuccess) return fail(LF_E_HIP, "statistics launch: %s", hipGetErrorString(e));
+    e = lfk_bwd_global_launch(&A, t, stream);
+    if (e != hipSuccess) return fail(LF_E_HIP, "global-row launch: %s", hipGetErrorString(e));
+    lfk::BwdBandArgs BA;
+    BA.q = q; BA.k = k; BA.v = v; BA.dy = dy;
+    BA.dq = dq; BA.dk = dk; BA.dv = dv;
+    BA.pad = key_padding_mask;
+    BA.plan = dplan;
+    BA.stats = (const float *)A.stats;
+    BA.gmap = A.gmap;
+    BA.inv_off = A.inv_off;
+    BA.inv_list = A.inv_list;
+    e = lfk_bwd_band(&BA, &F.P, stream);
+    if (e != hipSuccess) return fail(LF_E_HIP, "band launch: %s", hipGetErrorString(e));
     return LF_OK;
 }
 
@@ -584,8 +701,18 @@ extern "C" lf_status_t lf_attn_bwd(const void *q, const void *k, const void *v, 
                                    const uint8_t *key_padding_mask, void *dq, void *dk, void *dv, lf_dtype_t dtype,
                                    void *stream) {
     g_err.clear();
-    return attn_bwd(q, k, v, dy, B, H, T, d, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
-                    n_global, key_padding_mask, dq, dk, dv, dtype, stream);
+    return attn_bwd(q, k, v, dy, nullptr, nullptr, B, H, T, d, radius, one_sided, rand_blocks, n_rand, dilation,
+                    global_idx, n_global, key_padding_mask, dq, dk, dv, dtype, stream);
+}
+
+extern "C" lf_status_t lf_attn_bwd_ex(const void *q, const void *k, const void *v, const void *dy, const void *out,
+                                      const float *lse, int B, int H, int T, int d, const int32_t *radius,
+                                      int one_sided, const int32_t *rand_blocks, int n_rand, const int32_t *dilation,
+                                      const int32_t *global_idx, int n_global, const uint8_t *key_padding_mask,
+                                      void *dq, void *dk, void *dv, lf_dtype_t dtype, void *stream) {
+    g_err.clear();
+    return attn_bwd(q, k, v, dy, out, lse, B, H, T, d, radius, one_sided, rand_blocks, n_rand, dilation,
+                    global_idx, n_global, key_padding_mask, dq, dk, dv, dtype, stream);
 }
 
 extern "C" lf_status_t lf_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int T,

@@ -75,6 +75,20 @@ struct Args {
     float *lse;              // [B][H][T] natural log of each row's softmax denominator, or null
 };
 
+// The argument of the matrix-core backward kernels (lf_bwd_mfma.hip): bf16
+// tensors [B][H][T][64], the forward's plan (band tiles, radii, strides,
+// global set, random key blocks) and the row statistics.
+struct BwdBandArgs {
+    const void *q, *k, *v, *dy;
+    void *dq, *dk, *dv;
+    const uint8_t *pad;      // [B][T] or null
+    const Plan *plan;
+    const float *stats;      // [B*H][T][2]: (lse * log2 e, D = dy . y); (+inf, 0) for a padded row
+    const uint32_t *gmap;    // bit j set iff position j is global ([ceil(T/32)] words)
+    const int32_t *inv_off;  // random blocks: [H][ceil(T/64) + 1] offsets into inv_list per key block
+    const int32_t *inv_list; // the query blocks that drew each key block, ascending
+};
+
 }  // namespace lfk
 
 #endif

@@ -29,7 +29,9 @@ from typing import Dict, List
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = ["sparse_long_sequence_lf_amd/csrc/lf_fwd_kernels.hip",
-                  "sparse_long_sequence_lf_amd/csrc/lf_kernels.h"]
+                  "sparse_long_sequence_lf_amd/csrc/lf_kernels.h",
+                  "sparse_long_sequence_lf_amd/csrc/lf_device.h",
+                  "sparse_long_sequence_lf_amd/csrc/lf_decode.h"]
 KERNEL_NAME = "tile_kernel"
 COPY_BYTES = 1 << 28   # the calibration copy in bench.py --profile-mode
 

@@ -135,3 +135,45 @@ def test_bwd_repeatable():
     b = gpu_bwd(inp, dy)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["bf16-b1h12t4096-r256-g1", "bf16-b2h12t4096-r256-g68",
+                                  "bf16-b4h16t16384-r512-g8-pad", "bf16-b1h12t4096-r96-g2-rand3"])
+def test_bwd_with_forward_results(name):
+    # lf_attn_bwd_ex fed the forward's own output and lse gives the bits of
+    # lf_attn_bwd (which runs that forward itself), and both meet the oracle
+    w = W.workload(name)
+    inp = W.make_inputs(w, **{k: v for k, v in BWD_CASES[name].items()})
+    dy = W.make_grad(inp, w.seed + 29)
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    kpm = None if inp.key_padding_mask is None else inp.key_padding_mask.to(dev)
+    B, H, T, _ = q.shape
+    lse = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+    y = lf.attn_fwd(q, k, v, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm, lse=lse,
+                    one_sided=inp.one_sided, random_blocks=inp.random_blocks)
+    got = lf.attn_bwd(q, k, v, dy.to(dev), inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm,
+                      one_sided=inp.one_sided, random_blocks=inp.random_blocks, y=y, lse=lse)
+    torch.cuda.synchronize()
+    got = [g.float().cpu().double().numpy() for g in got]
+    print(f"case {name} shape={tuple(q.shape)}", flush=True)
+    ref_gpu = gpu_bwd(inp, dy)
+    for a, b in zip(got, ref_gpu):
+        assert np.array_equal(a, b)
+    check(inp, dy, "bf16", name + " (forward results given)")
+
+
+def test_bwd_ex_argument_checks():
+    inp = W.random_case(3, B=1, H=2, T=100, dtype="bf16", pad="none")
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    dy = W.make_grad(inp, 1).to(dev)
+    lse = torch.empty(1, 2, 100, dtype=torch.float32, device=dev)
+    y = torch.empty_like(q)
+    with pytest.raises(ValueError):
+        lf.attn_bwd(q, k, v, dy, inp.r, inp.dilation, inp.global_idx, y=y)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    # lse inside dq: rejected before any work
+    bad_lse = grads[0].view(torch.float32).reshape(-1)[: 200].view(1, 2, 100)
+    with pytest.raises(lf.LfError):
+        lf.attn_bwd(q, k, v, dy, inp.r, inp.dilation, inp.global_idx, out=grads, y=y, lse=bad_lse)
