@@ -90,10 +90,19 @@ typedef enum {
  *             there asynchronously; the call returns before it finishes.
  *
  * Ownership: the caller owns every buffer; the library keeps no pointer
- * after returning.  The library keeps one small device workspace per
- * (device, stream) pair for the global rows; it grows with hipMalloc on
- * first use of a larger problem (so call once outside graph capture before
- * capturing) and lives until the process exits.
+ * after returning.  The library keeps one device workspace per (device,
+ * stream) pair: global-row partials, the call's plan and tables (a few
+ * configurations at once, so that calls alternating between them reuse
+ * them).  A call never waits for the device: a plan or table it lacks is
+ * written by a kernel on `stream`, and a buffer it outgrows is replaced
+ * with hipMalloc, the old one freed once the stream has passed its last
+ * use.  During stream capture nothing is allocated: a call that would
+ * have to grow the workspace is LF_E_UNSUPPORTED (make one call of that
+ * size on the stream first).  What a captured call uses stays reserved for
+ * the graph until the process exits.  A graph shares its stream's
+ * workspace: do not replay it concurrently with calls on that stream or
+ * with another replay of a graph captured on it (the global-row partials
+ * and counters would race).
  *
  * Errors: all argument checks run before any HIP call; on LF_E_INVALID or
  * LF_E_UNSUPPORTED nothing is enqueued and `out` is untouched.  On any

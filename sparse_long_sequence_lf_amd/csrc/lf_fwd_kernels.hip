@@ -133,6 +133,66 @@ struct Task {
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Task t from the kernel argument's decode fields (every head with the same
+// stride and radius): the same Task as decode_task, with no memory access.
+__device__ __forceinline__ Task decode_task_fast(const FastDecode& f, int t) {
+    Task k;
+    if (t < f.n_band) {
+        k.kind = 0;
+        k.bh = mdiv(t, f.mg_tph);
+        const int x = t - k.bh * f.tph;
+        k.b = mdiv(k.bh, f.mg_H);
+        k.h = k.bh - k.b * f.H;
+        k.delta = f.delta;
+        int tile;
+        if (f.delta == 1) {
+            k.c = 0;
+            tile = x;
+            k.n = f.T;
+        } else if (x < f.hrem * f.htb) {
+            k.c = mdiv(x, f.mg_htb);
+            tile = x - k.c * f.htb;
+            k.n = f.hq + 1;
+        } else {
+            const int y = x - f.hrem * f.htb;
+            const int cc = mdiv(y, f.mg_hts);
+            k.c = f.hrem + cc;
+            tile = y - cc * f.hts;
+            k.n = f.hq;
+        }
+        k.m0 = tile * BM;
+        k.r = f.r;
+        k.ra = f.ra;
+        int lo_k = k.m0 - k.r; if (lo_k < 0) lo_k = 0;
+        int hi_k = k.m0 + BM - 1 + k.ra; if (hi_k > k.n - 1) hi_k = k.n - 1;
+        k.kb_lo = lo_k / KBLK;
+        k.nband = hi_k / KBLK - k.kb_lo + 1;
+        k.key_end = k.n;
+        k.split = 0;
+    } else {
+        const int g = t - f.n_band;
+        k.kind = 1;
+        k.r = 0;
+        k.ra = 0;
+        k.bh = mdiv(g, f.mg_per_bh);
+        const int rem = g - k.bh * (f.n_split * f.n_ggroups);
+        const int grp = mdiv(rem, f.mg_nsplit);
+        k.split = rem - grp * f.n_split;
+        k.b = mdiv(k.bh, f.mg_H);
+        k.h = k.bh - k.b * f.H;
+        k.delta = 1;
+        k.c = 0;
+        k.n = f.T;
+        k.m0 = grp * BM;
+        const int j0 = k.split * f.split_len;
+        int j1 = j0 + f.split_len; if (j1 > f.T) j1 = f.T;
+        k.kb_lo = j0 / KBLK;
+        k.nband = cdiv(j1 - j0, KBLK);
+        k.key_end = j1;
+    }
+    return k;
+}
+
 __device__ __forceinline__ Task decode_task(const Plan& P, int t) {
     Task k;
     if (t < P.n_band_tasks) {
@@ -275,16 +335,25 @@ __device__ __forceinline__ VFrag<D, NP> load_v(const WaveState<D, NP>& W, const 
 template <int NP>
 struct PFrag { bf16x8 p[NP][2]; };
 
-// p = 2^(s*scale - m) for one block as P^T operands; returns ps plus this
-// lane's part of the block's row sum
-template <int D, int NP>
-__device__ __forceinline__ float block_weights(const WaveState<D, NP>& W, const f32x16& s, PFrag<NP>& pf, float ps) {
+// p = 2^(s*scale - m) for one block; returns this lane's part of the
+// block's row sum (a tree of fp32 adds)
+template <int D>
+__device__ __forceinline__ float block_exp(float nms, const f32x16& s, float (&p)[16]) {
     constexpr float SC = ScaleLog2<D>::v;
-    const float nms = W.nms;
-    float p[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], SC, nms));
-    // P^T operands: step st covers accumulator elements 8st .. 8st+7
+    float t8[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) t8[i] = p[2 * i] + p[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 4; i++) t8[i] += t8[i + 4];
+    return (t8[0] + t8[2]) + (t8[1] + t8[3]);
+}
+
+// the weights as P^T operands (step st covers accumulator elements
+// 8st .. 8st+7), one per bf16 part
+template <int NP>
+__device__ __forceinline__ void block_pack(const float (&p)[16], PFrag<NP>& pf) {
 #pragma unroll
     for (int st = 0; st < 2; st++) {
         Raw32 x;
@@ -295,13 +364,6 @@ __device__ __forceinline__ float block_weights(const WaveState<D, NP>& W, const 
 #pragma unroll
         for (int q = 0; q < NP; q++) pf.p[q][st] = as_bf16x8(parts[q]);
     }
-    // row sum of the fp32 weights by a tree of adds
-    float t8[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) t8[i] = p[2 * i] + p[2 * i + 1];
-#pragma unroll
-    for (int i = 0; i < 4; i++) t8[i] += t8[i + 4];
-    return ps + ((t8[0] + t8[2]) + (t8[1] + t8[3]));
 }
 
 // O^T += V^T P^T
@@ -316,10 +378,14 @@ __device__ __forceinline__ void block_product(WaveState<D, NP>& W, const PFrag<N
             for (int i = 0; i < PR::n; i++) W.o[cb] = mfma(f.v[st][cb][PR::a[i]], pf.p[PR::b[i]][st], W.o[cb]);
 }
 
+// one block: the running maximum, the weights, their row sum and O^T += V^T P^T
 template <int D, int NP>
 __device__ __forceinline__ void block_pv(WaveState<D, NP>& W, const f32x16& s, const VFrag<D, NP>& f) {
+    update_max<D, NP>(W, s);
+    float p[16];
+    W.lp += block_exp<D>(W.nms, s, p);
     PFrag<NP> pf;
-    W.lp = block_weights<D, NP>(W, s, pf, W.lp);
+    block_pack<NP>(p, pf);
     block_product<D, NP>(W, pf, f);
 }
 
@@ -445,14 +511,15 @@ void tile_kernel(const Args A) {
     // the global-row tasks first, then a contiguous eighth of the band tasks
     // (neighbouring tiles share keys in its L2).
     const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
+    const bool fast = A.fd.on != 0;
     int task_id;
     {
-        const int nb = P.n_band_tasks, ng = P.n_tasks - P.n_band_tasks;
+        const int nb = fast ? A.fd.n_band : P.n_band_tasks, ng = (fast ? A.fd.n_tasks : P.n_tasks) - nb;
         const int nb_x = (nb >> 3) + (xcd < (nb & 7)), nb_o = xcd * (nb >> 3) + min(xcd, nb & 7);
         const int ng_x = (ng >> 3) + (xcd < (ng & 7)), ng_o = xcd * (ng >> 3) + min(xcd, ng & 7);
         if (slot_in_xcd < ng_x) {
             task_id = nb + ng_o + slot_in_xcd;
-        } else if (P.band_chunk > 0) {
+        } else if (!fast && P.band_chunk > 0) {
             // tiles of unequal cost (one radius per head): runs of C tiles go
             // to the dies in turn, so that every die gets a share of each head
             const int C = P.band_chunk, sb = slot_in_xcd - ng_x;
@@ -465,8 +532,8 @@ void tile_kernel(const Args A) {
             return;
         }
     }
-    const Task tk = decode_task(P, task_id);
-    const int T = P.T;
+    const Task tk = fast ? decode_task_fast(A.fd, task_id) : decode_task(P, task_id);
+    const int T = fast ? A.fd.T : P.T;
     if constexpr (PAD) {
         // A band tile whose queries are all padded writes zero rows and ends
         // here: a padded query's output is zero whatever its keys.  Every
@@ -510,7 +577,7 @@ void tile_kernel(const Args A) {
     // kernel-argument scalars used inside the loop live in registers (a value
     // select between an LDS table entry and a kernel argument would otherwise
     // become a flat load, which waits on every load in flight)
-    const int n_g = P.n_g, r = tk.r, ra = tk.ra;
+    const int n_g = fast ? A.fd.n_g : P.n_g, r = tk.r, ra = tk.ra;
     const uint32_t head_bytes = (uint32_t)T * ROWB;
     const void* kplanes = NP == 1 ? A.k : P.kp;   // bf16 input is its own plane
     const void* vplanes = NP == 1 ? A.v : P.vp;
@@ -565,6 +632,9 @@ void tile_kernel(const Args A) {
         }
     }
     const int NS = dead ? 0 : cdiv(nblk, 2);
+    auto blk = [&](int s) -> int { return 2 * s + ph; };   // this phase's block of stage s
+    // stages [0, s_fast) hold band blocks only and so does the stage after each
+    const int s_fast = dead ? 0 : max((nb >> 1) - 1, 0);
     const int sb_end = (nb - ph + 1) >> 1;       // this wave's steps [0, sb_end) hold band (or dense) blocks
     int j_lo = 0, j_hi = -1;                     // band blocks with keys for this wave's queries
     int ji_lo = 0, ji_hi = -1;                   // band blocks that need no mask
@@ -632,13 +702,13 @@ void tile_kernel(const Args A) {
     // cannot reach the products).
     auto issue_band = [&](int s, int off, uint32_t pm) {
         const bool padA = PAD && !kwave && ((pm >> rowA) & 1u), padB = PAD && !kwave && ((pm >> rowB) & 1u);
-        put(window_at(row0_of(2 * s + bw)), smem + off + bw * G::BLK, padA ? kPastEnd : voA0, padB ? kPastEnd : voB0);
+        put(window_at(row0_of(blk(s))), smem + off + bw * G::BLK, padA ? kPastEnd : voA0, padB ? kPastEnd : voB0);
     };
     // any stage: band, global-key or random block, or nothing past the list;
     // padded global keys load as zeros through their table entry
     auto issue_stage = [&](int s, int off, uint32_t pm) {
         const bool padA = PAD && !kwave && ((pm >> rowA) & 1u), padB = PAD && !kwave && ((pm >> rowB) & 1u);
-        const int jb = 2 * s + bw;
+        const int jb = blk(s);
         if (jb >= nblk) return;
         char* dst = smem + off + bw * G::BLK;
         if (jb < nb) {
@@ -659,7 +729,7 @@ void tile_kernel(const Args A) {
     // zero (not padded; the range test covers them).
     const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, PAD ? (uint32_t)T : 0u);
     auto pad_at = [&](int s) -> uint32_t {
-        const int q = 2 * s + ph;
+        const int q = blk(s);
         const int pos = q < nb ? row0_of(q) + tk.delta * lq
                                : (q >= nb + ngb && q < nblk ? rand_p0(q - nb - ngb) + lq : T);
         return __builtin_amdgcn_raw_buffer_load_b8(rpad, (uint32_t)min(pos, T), 0, 0);
@@ -702,7 +772,7 @@ void tile_kernel(const Args A) {
     // global-key block in stage 0, found only when the band has fewer than
     // two blocks, is loaded once its table is there).  Padded V rows of stage
     // 0 are cleared once it has landed.
-    const bool early0 = bw < nb;
+    const bool early0 = blk(0) < nb;
     if (early0) issue_stage(0, 0, 0u);
     // padding: pm_cur = padded rows of this wave's block of stage s (in step
     // s), pbyte = the bytes of stage s+1 (in flight)
@@ -796,7 +866,7 @@ void tile_kernel(const Args A) {
     // for the V reads, and the other waves of the SIMD run meanwhile.
     auto band_step = [&](int s, int oc, int on) {
         barrier_lds_loads();           // stage s landed; stage s-1 no longer read
-        const int j = 2 * s + ph;
+        const int j = blk(s);
         const bool rel = j >= j_lo && j <= j_hi;
         KFrag<D, NP> kf;
         VFrag<D, NP> vf;
@@ -821,7 +891,6 @@ void tile_kernel(const Args A) {
                 if constexpr (PAD) bad |= pm_cur;
                 if (bad != 0u) mask_bits(sc, ~lane_bits(bad, lg));
             }
-            update_max<D, NP>(W, sc);
             block_pv<D, NP>(W, sc, vf);
         }
         pm_cur = pm_next;
@@ -834,7 +903,7 @@ void tile_kernel(const Args A) {
         constexpr int MODE = decltype(mode)::value;
         barrier_lds_loads();           // stage s landed; stage s-1 no longer read
         const bool band = s < sb_end;
-        const int jb = 2 * s + ph;     // sequence position
+        const int jb = blk(s);         // sequence position
         const int j = min(jb, nb - 1); // its band block (band positions)
         const bool cur = band ? (j >= j_lo && j <= j_hi) : (s < sg_end);
         // The block's bad-row word, wave-uniform so that every test on it is
@@ -888,7 +957,6 @@ void tile_kernel(const Args A) {
                 if (tk.kind == 0) mask_window(sc, m_me - r - (tk.kb_lo + j) * KBLK - 4 * lg, r + ra);
                 if (bad != 0u) mask_bits(sc, ~lane_bits(bad, lg));
             }
-            update_max<D, NP>(W, sc);
             block_pv<D, NP>(W, sc, vf);
         }
         pm_cur = pm_next;
@@ -900,7 +968,6 @@ void tile_kernel(const Args A) {
     using General = std::integral_constant<int, 1>;
     using WithRandom = std::integral_constant<int, 2>;
     constexpr int S1 = G::NBUF == 2 ? G::STAGE : 0;
-    const int s_fast = dead ? 0 : max((nb >> 1) - 1, 0);
     int s = 0;
     for (; s + 1 < s_fast; s += 2) {
         band_step(s, 0, S1);

@@ -59,99 +59,190 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 //    must read zero at the start of every call: the allocation is zeroed
 //    and every call's kernel returns each counter it uses to zero.  Nothing
 //    else is ever stored there.
-//  * scratch: the global-row partials and, for fp32 input, the bf16 hi/lo
-//    planes of K and V; no contents carry over between calls.
-//  * plan: the device copy of the call's lfk::Plan, with a host shadow of
-//    what it holds; it is re-uploaded (in stream order) only when it changes.
+//  * scratch: the global-row partials and, for fp32 input, the bf16 planes
+//    of K and V; no contents carry over between calls.
+//  * plan, aux, bwd: device copies of the call's lfk::Plan, random-block
+//    table and backward tables, kSlots of each keyed by content, so that
+//    calls alternating between a few configurations reuse them.  A missing
+//    one is written into the least recently used slot by a small kernel
+//    that carries the bytes in its arguments: the write is ordered on the
+//    stream like the kernels that read it, the host never waits for it, and
+//    a write recorded in a graph replays with its own bytes.
 //
-// Buffers only grow; an old buffer is released after the stream has drained it.
+// No call waits for the device.  A buffer too small for a call is replaced;
+// the old one is released once an event recorded after the work that used
+// it has passed (checked at later calls).  During stream capture nothing
+// is allocated or released: a call that needs a larger buffer is refused.
+// Whatever a captured call used (buffers, slots) is pinned: never released
+// or overwritten with other contents, so that the graph stays valid while
+// later calls on the stream move on to other buffers and slots.  A slot
+// written during capture holds its contents only once the graph has run,
+// so other calls do not use it.
+constexpr int kSlots = 4;
+
 struct Buffer {
     void *ptr = nullptr;
     size_t bytes = 0;
+    bool pinned = false;
+};
+struct Slot {
+    Buffer buf;
+    std::vector<uint32_t> shadow;   // what buf holds, if valid
+    bool valid = false;
+    uint64_t used = 0;              // call count at the last use (least recently used goes first)
+};
+struct Retired {
+    void *ptr;
+    hipEvent_t done;
 };
 struct Workspace {
-    Buffer counters, scratch, plan, aux;
-    lfk::Plan shadow;
-    bool shadow_valid = false;
-    std::vector<uint32_t> aux_shadow;   // what aux holds: random-block table and global bitmap
-    Buffer bwd_tab, bwd_stats, bwd_gpart;   // backward: tables; row statistics; global-split records
-    Buffer bwd_fwd;                   // backward (bf16) without the forward's results: its output and lse
-    std::vector<uint32_t> bwd_shadow;   // what bwd_tab holds
+    Buffer counters, scratch;
+    Slot plan[kSlots], aux[kSlots], bwd[kSlots];
+    Buffer bwd_stats, bwd_gpart;   // backward: row statistics; global-split records
+    Buffer bwd_fwd;                // backward (bf16) without the forward's results: its output and lse
+    std::vector<Retired> retired;
+    uint64_t calls = 0;
+    bool capturing = false;        // the current call is being captured
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, void *>, Workspace> g_ws;
 
-lf_status_t grow(Buffer &b, size_t bytes, bool zero, void *stream) {
-    if (b.bytes >= bytes) return LF_OK;
-    hipError_t e;
-    if (b.ptr) {
-        e = hipStreamSynchronize((hipStream_t)stream);
-        if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
-        (void)hipFree(b.ptr);
-        b.ptr = nullptr;
-        b.bytes = 0;
+// release the retired buffers whose work has finished
+void reap(Workspace &w) {
+    size_t k = 0;
+    for (size_t i = 0; i < w.retired.size(); i++) {
+        if (hipEventQuery(w.retired[i].done) == hipSuccess) {
+            (void)hipFree(w.retired[i].ptr);
+            (void)hipEventDestroy(w.retired[i].done);
+        } else {
+            w.retired[k++] = w.retired[i];
+        }
     }
+    w.retired.resize(k);
+}
+
+// give up b: freed once the stream has passed the work enqueued so far, or
+// kept for good when a captured graph refers to it
+lf_status_t retire(Workspace &w, Buffer &b, void *stream) {
+    if (b.ptr && !b.pinned) {
+        hipEvent_t ev;
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventRecord(ev, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(LF_E_HIP, "retiring a workspace buffer: %s", hipGetErrorString(e));
+        w.retired.push_back({b.ptr, ev});
+    }
+    b = Buffer();
+    return LF_OK;
+}
+
+// b holds at least `bytes` bytes (zeroed when first allocated if `zero`);
+// during capture it must already, and is pinned
+lf_status_t grow(Workspace &w, Buffer &b, size_t bytes, bool zero, void *stream) {
+    if (b.bytes >= bytes) {
+        if (w.capturing) b.pinned = true;
+        return LF_OK;
+    }
+    if (w.capturing)
+        return fail(LF_E_UNSUPPORTED,
+                    "this call needs a larger workspace than the stream has during stream capture; make one "
+                    "call of this size on the stream outside capture first");
+    lf_status_t st = retire(w, b, stream);
+    if (st != LF_OK) return st;
     const size_t want = std::max(bytes, (size_t)1 << 16);
-    e = hipMalloc(&b.ptr, want);
+    hipError_t e = hipMalloc(&b.ptr, want);
     if (e != hipSuccess) {
         b.ptr = nullptr;
         (void)hipGetLastError();
         return fail(LF_E_NOMEM, "workspace of %zu bytes: %s", want, hipGetErrorString(e));
     }
     if (zero) {
-        e = hipMemset(b.ptr, 0, want);
+        e = hipMemsetAsync(b.ptr, 0, want, (hipStream_t)stream);
         if (e != hipSuccess) {
             (void)hipFree(b.ptr);
             b.ptr = nullptr;
-            return fail(LF_E_HIP, "hipMemset: %s", hipGetErrorString(e));
+            return fail(LF_E_HIP, "hipMemsetAsync: %s", hipGetErrorString(e));
         }
     }
     b.bytes = want;
     return LF_OK;
 }
 
-Workspace *workspace_for(void *stream) {
+// the workspace of the calling thread's device and `stream`, its retired
+// buffers reaped and its capture state taken
+Workspace *workspace_for(void *stream, lf_status_t *st) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-    return &g_ws[std::make_pair(dev, stream)];
-}
-
-// Host-to-device copy of a table the next kernels on `stream` read, finished
-// before returning: the copy is enqueued on the stream, then the stream is
-// drained.  A small copy from pageable memory was seen to land after the
-// following kernels had read the old table, so an upload does not rely on
-// the copy's own ordering.  Uploads happen only when a table changes (never
-// in steady state, and never during capture, which the callers refuse).
-hipError_t upload(void *dst, const void *src, size_t bytes, void *stream) {
-    hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
-    if (e != hipSuccess) return e;
-    return hipStreamSynchronize((hipStream_t)stream);
-}
-
-// Device copy of *P on this stream's workspace; uploads only when it differs
-// from the last upload.  An upload cannot be recorded into a graph (its source
-// is a host temporary), so a changed plan during stream capture is refused.
-lf_status_t upload_plan(Workspace &w, const lfk::Plan &P, void *stream, const lfk::Plan **dev_plan) {
-    lf_status_t st = grow(w.plan, sizeof(lfk::Plan), false, stream);
-    if (st != LF_OK) return st;
-    if (!w.shadow_valid || std::memcmp(&w.shadow, &P, sizeof P) != 0) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
-        if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
-        if (cs != hipStreamCaptureStatusNone)
-            return fail(LF_E_UNSUPPORTED,
-                        "the call's shape, dilation or global set differs from the previous call on this stream "
-                        "during stream capture; make one identical call outside capture first");
-        e = upload(w.plan.ptr, &P, sizeof P, stream);
-        if (e != hipSuccess) {
-            w.shadow_valid = false;
-            return fail(LF_E_HIP, "plan upload: %s", hipGetErrorString(e));
-        }
-        std::memcpy(&w.shadow, &P, sizeof P);
-        w.shadow_valid = true;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *st = fail(LF_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+        return nullptr;
     }
-    *dev_plan = (const lfk::Plan *)w.plan.ptr;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing((hipStream_t)stream, &cs);
+    if (e != hipSuccess) {
+        *st = fail(LF_E_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+        return nullptr;
+    }
+    Workspace *w = &g_ws[std::make_pair(dev, stream)];
+    w->capturing = cs != hipStreamCaptureStatusNone;
+    w->calls++;
+    if (!w->capturing) reap(*w);
+    *st = LF_OK;
+    return w;
+}
+
+// A device copy of `words` among the slots: an existing one when a slot
+// holds it, else written into the least recently used unpinned slot.
+lf_status_t put_table(Workspace &w, Slot (&slots)[kSlots], const uint32_t *words, size_t n, void *stream,
+                      const void **dev, const char *what) {
+    for (Slot &sl : slots)
+        if (sl.valid && sl.shadow.size() == n && std::memcmp(sl.shadow.data(), words, n * 4) == 0) {
+            sl.used = w.calls;
+            if (w.capturing) sl.buf.pinned = true;
+            *dev = sl.buf.ptr;
+            return LF_OK;
+        }
+    Slot *victim = nullptr;
+    for (Slot &sl : slots) {
+        if (sl.buf.pinned) continue;
+        if (!victim || !sl.valid || (victim->valid && sl.used < victim->used)) victim = &sl;
+        if (!victim->valid) break;
+    }
+    if (!victim)
+        return fail(LF_E_UNSUPPORTED, "every %s slot of this stream is held by a captured graph", what);
+    // a slot is never grown during capture: it is allocated large enough first
+    if (victim->buf.bytes < n * 4) {
+        if (w.capturing)
+            return fail(LF_E_UNSUPPORTED,
+                        "the %s of this call needs a new slot during stream capture; make one identical call on "
+                        "the stream outside capture first", what);
+        lf_status_t st = grow(w, victim->buf, n * 4, false, stream);
+        if (st != LF_OK) return st;
+    }
+    hipError_t e = lfk_write_plan(words, n * 4, victim->buf.ptr, nullptr, 0, stream);
+    if (e != hipSuccess) {
+        victim->valid = false;
+        return fail(LF_E_HIP, "%s upload: %s", what, hipGetErrorString(e));
+    }
+    victim->used = w.calls;
+    if (w.capturing) {
+        // holds the words only once the graph runs
+        victim->buf.pinned = true;
+        victim->valid = false;
+        victim->shadow.clear();
+    } else {
+        victim->shadow.assign(words, words + n);
+        victim->valid = true;
+    }
+    *dev = victim->buf.ptr;
     return LF_OK;
+}
+
+// device copy of *P on this stream's workspace
+lf_status_t upload_plan(Workspace &w, const lfk::Plan &P, void *stream, const lfk::Plan **dev_plan) {
+    const void *dev = nullptr;
+    lf_status_t st = put_table(w, w.plan, (const uint32_t *)&P, sizeof P / 4, stream, &dev, "plan");
+    *dev_plan = (const lfk::Plan *)dev;
+    return st;
 }
 
 }  // namespace
@@ -345,9 +436,9 @@ lf_status_t plan_fwd(int B, int H, int T, int d, int r, const int32_t *radius, i
 // partials, planes, random-block table) and the plan on the device.
 lf_status_t bind_fwd(Workspace &w, FwdPlan &F, bool fp32, void *stream, const lfk::Plan **dev_plan) {
     if (F.scratch_bytes > 0) {
-        lf_status_t st = grow(w.counters, F.cnt_bytes, true, stream);
+        lf_status_t st = grow(w, w.counters, F.cnt_bytes, true, stream);
         if (st != LF_OK) return st;
-        st = grow(w.scratch, F.scratch_bytes, false, stream);
+        st = grow(w, w.scratch, F.scratch_bytes, false, stream);
         if (st != LF_OK) return st;
         char *ws = (char *)w.scratch.ptr;
         if (F.P.n_g > 0) {
@@ -360,27 +451,47 @@ lf_status_t bind_fwd(Workspace &w, FwdPlan &F, bool fp32, void *stream, const lf
         }
     }
     if (F.P.n_rand > 0) {
-        lf_status_t st = grow(w.aux, F.aux.size() * sizeof(uint32_t), false, stream);
+        const void *dev = nullptr;
+        lf_status_t st = put_table(w, w.aux, F.aux.data(), F.aux.size(), stream, &dev, "random-block table");
         if (st != LF_OK) return st;
-        if (w.aux_shadow != F.aux) {
-            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-            hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
-            if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
-            if (cs != hipStreamCaptureStatusNone)
-                return fail(LF_E_UNSUPPORTED,
-                            "the random key blocks differ from the previous call on this stream during stream "
-                            "capture; make one identical call outside capture first");
-            e = upload(w.aux.ptr, F.aux.data(), F.aux.size() * sizeof(uint32_t), stream);
-            if (e != hipSuccess) {
-                w.aux_shadow.clear();
-                return fail(LF_E_HIP, "random-block upload: %s", hipGetErrorString(e));
-            }
-            w.aux_shadow = F.aux;
-        }
-        F.P.rtab = (const int32_t *)w.aux.ptr;
-        F.P.gmap = (const uint32_t *)w.aux.ptr + (size_t)F.P.H * cdiv(F.P.T, 64) * F.P.n_rand;
+        F.P.rtab = (const int32_t *)dev;
+        F.P.gmap = (const uint32_t *)dev + (size_t)F.P.H * cdiv(F.P.T, 64) * F.P.n_rand;
     }
     return upload_plan(w, F.P, stream, dev_plan);
+}
+
+// The kernel argument's decode fields: set when every head has the same
+// stride and radius (the plan's per-head tables are then not read to find
+// a task), else off.
+lfk::FastDecode fast_decode(const lfk::Plan &P) {
+    lfk::FastDecode f;
+    std::memset(&f, 0, sizeof f);
+    for (int h = 1; h < P.H; h++)
+        if (P.dil[h] != P.dil[0] || P.rad[h] != P.rad[0]) return f;
+    f.on = 1;
+    f.n_band = P.n_band_tasks;
+    f.n_tasks = P.n_tasks;
+    f.tph = P.head_start[1];
+    f.mg_tph = lfk::magic_for(f.tph);
+    f.mg_H = P.mg_H;
+    f.H = P.H;
+    f.T = P.T;
+    f.delta = P.dil[0];
+    f.r = P.rad[0];
+    f.ra = P.one_sided ? 0 : P.rad[0];
+    f.hq = P.hq[0];
+    f.hrem = P.hrem[0];
+    f.htb = P.htb[0];
+    f.hts = P.hts[0];
+    f.mg_htb = P.mg_tb[0];
+    f.mg_hts = P.mg_ts[0];
+    f.n_g = P.n_g;
+    f.n_split = P.n_split;
+    f.n_ggroups = P.n_ggroups;
+    f.split_len = P.split_len;
+    f.mg_per_bh = P.mg_per_bh;
+    f.mg_nsplit = P.mg_nsplit;
+    return f;
 }
 
 // The call behind the forward entry points: radius is NULL (r for every
@@ -429,20 +540,22 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
         A.pad = key_padding_mask;
         A.lse = lse;
         A.plan = (const lfk::Plan *)base;
+        A.fd = fast_decode(P);
         e = lfk_launch(&A, &P, dtype == LF_BF16, stream);
         if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
         return LF_OK;
     }
 
     std::lock_guard<std::mutex> lock(g_ws_mu);
-    Workspace *w = workspace_for(stream);
-    if (!w) return fail(LF_E_HIP, "hipGetDevice failed");
+    Workspace *w = workspace_for(stream, &st);
+    if (!w) return st;
     lfk::Args A;
     A.q = q; A.k = k; A.v = v; A.out = out;
     A.pad = key_padding_mask;
     A.lse = lse;
     st = bind_fwd(*w, F, dtype == LF_F32, stream, &A.plan);
     if (st != LF_OK) return st;
+    A.fd = fast_decode(P);
     hipError_t e = lfk_launch(&A, &P, dtype == LF_BF16, stream);
     if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
     return LF_OK;
@@ -591,11 +704,10 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     }
 
     std::lock_guard<std::mutex> lock(g_ws_mu);
-    Workspace *w = workspace_for(stream);
-    if (!w) return fail(LF_E_HIP, "hipGetDevice failed");
-    lf_status_t st = grow(w->bwd_tab, tab.size() * sizeof(uint32_t), false, stream);
-    if (st != LF_OK) return st;
-    st = grow(w->bwd_stats, (size_t)B * H * T * 2 * sizeof(float), false, stream);
+    lf_status_t st;
+    Workspace *w = workspace_for(stream, &st);
+    if (!w) return st;
+    st = grow(*w, w->bwd_stats, (size_t)B * H * T * 2 * sizeof(float), false, stream);
     if (st != LF_OK) return st;
     // global rows and keys: splits of a multiple of 256 positions, as many
     // as bring the grid to about 2048 workgroups (at most 64, at least 1)
@@ -609,25 +721,13 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     if (n_rec >= ((size_t)1 << 31)) return fail(LF_E_UNSUPPORTED, "too many global-row splits");
     const size_t gstat_bytes = (n_rec * 16 + 255) / 256 * 256;
     if (n_rec > 0) {
-        st = grow(w->bwd_gpart, gstat_bytes + n_rec * 192 * sizeof(float), false, stream);
+        st = grow(*w, w->bwd_gpart, gstat_bytes + n_rec * 192 * sizeof(float), false, stream);
         if (st != LF_OK) return st;
     }
-    if (w->bwd_shadow != tab) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
-        if (e != hipSuccess) return fail(LF_E_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
-        if (cs != hipStreamCaptureStatusNone)
-            return fail(LF_E_UNSUPPORTED,
-                        "the call's shape, radii, dilation or global set differs from the previous backward call "
-                        "on this stream during stream capture; make one identical call outside capture first");
-        e = upload(w->bwd_tab.ptr, tab.data(), tab.size() * sizeof(uint32_t), stream);
-        if (e != hipSuccess) {
-            w->bwd_shadow.clear();
-            return fail(LF_E_HIP, "backward table upload: %s", hipGetErrorString(e));
-        }
-        w->bwd_shadow = tab;
-    }
-    const uint32_t *dt = (const uint32_t *)w->bwd_tab.ptr;
+    const void *dtab = nullptr;
+    st = put_table(*w, w->bwd, tab.data(), tab.size(), stream, &dtab, "backward table");
+    if (st != LF_OK) return st;
+    const uint32_t *dt = (const uint32_t *)dtab;
     lfk::BwdArgs A;
     A.pad = key_padding_mask;
     A.gmap = dt + o_gmap;
@@ -662,7 +762,7 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     if (!out) {
         // the forward, into the workspace: output rows, then lse
         const size_t ybytes = (nbytes + 255) / 256 * 256;
-        st = grow(w->bwd_fwd, ybytes + rows * sizeof(float), false, stream);
+        st = grow(*w, w->bwd_fwd, ybytes + rows * sizeof(float), false, stream);
         if (st != LF_OK) return st;
         lfk::Args FA;
         FA.q = q; FA.k = k; FA.v = v;
@@ -670,6 +770,7 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
         FA.pad = key_padding_mask;
         FA.lse = (float *)((char *)w->bwd_fwd.ptr + ybytes);
         FA.plan = dplan;
+        FA.fd = fast_decode(F.P);
         e = lfk_launch(&FA, &F.P, 1, stream);
         if (e != hipSuccess) return fail(LF_E_HIP, "forward launch: %s", hipGetErrorString(e));
         out = FA.out;

@@ -66,6 +66,23 @@ struct Plan {
     int32_t glob[LF_MAX_GLOBALS];
 };
 
+// Task decode for calls whose heads share one stride and one radius, carried
+// in the kernel argument itself: a workgroup knows its tile after the one
+// load of its arguments, instead of after a chain of dependent loads from
+// the plan (its scalars, then the per-head tables).
+struct FastDecode {
+    int on;                  // 1: every head has stride delta and radius r (the fields below are set)
+    int n_band, n_tasks;     // band tasks; band + global-row tasks
+    int tph;                 // band tasks per (b, h)
+    Magic mg_tph;            // / tph
+    Magic mg_H;              // / H
+    int H, T, delta, r, ra;
+    int hq, hrem, htb, hts;  // class lengths and tiles per class (as in Plan)
+    Magic mg_htb, mg_hts;
+    int n_g, n_split, n_ggroups, split_len;
+    Magic mg_per_bh, mg_nsplit;
+};
+
 // The kernel argument: the call's tensors and the device copy of its plan.
 struct Args {
     const void *q, *k, *v;
@@ -73,6 +90,7 @@ struct Args {
     const uint8_t *pad;      // [B][T] or null
     const Plan *plan;
     float *lse;              // [B][H][T] natural log of each row's softmax denominator, or null
+    FastDecode fd;
 };
 
 // The argument of the matrix-core backward kernels (lf_bwd_mfma.hip): bf16
