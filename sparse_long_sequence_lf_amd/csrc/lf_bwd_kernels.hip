@@ -807,11 +807,25 @@ __global__ __launch_bounds__(64) void combine_kernel(const lfk::BwdArgs A, ET* _
     const int T = A.T;
     float sq = 0.f, sk = 0.f, sv = 0.f;
     if (!padded(A.pad ? A.pad + (size_t)b * T : nullptr, g)) {
+        // eight splits' loads in flight at a time (splits past the last
+        // repeat it with weight 0)
         const float* p = A.gpart + rec * A.n_split * 192;
-        for (int e = 0; e < A.n_split; e++) {
-            sq += p[e * 192 + c];
-            sk += p[e * 192 + 64 + c];
-            sv += p[e * 192 + 128 + c];
+        for (int e0 = 0; e0 < A.n_split; e0 += 8) {
+            float xq[8], xk[8], xv[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int e = min(e0 + i, A.n_split - 1);
+                xq[i] = p[e * 192 + c];
+                xk[i] = p[e * 192 + 64 + c];
+                xv[i] = p[e * 192 + 128 + c];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const float w = e0 + i < A.n_split ? 1.f : 0.f;
+                sq += w * xq[i];
+                sk += w * xk[i];
+                sv += w * xv[i];
+            }
         }
     }
     const size_t o = (bh * T + g) * D + c;

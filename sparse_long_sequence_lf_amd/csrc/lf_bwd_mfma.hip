@@ -28,13 +28,14 @@
 // The global rows' dq and the global keys' dk, dv come from the vector
 // kernels of lf_bwd_kernels.hip.
 //
-// Three launches:
-//   prep_kernel  per row: (lse_i log2 e, D_i = dy_i . y_i); a padded row (lse
-//                = -inf) gets (+inf, 0), so its weights vanish.
+// Two launches, the global-row kernels of lf_bwd_kernels.hip between them:
 //   dq_kernel    query-major: a tile of 64 class queries (two blocks of 32,
 //                two key phases, four waves) streams its key blocks through
 //                an LDS ring: S^T = K Q^T, dP^T = V dY^T,
 //                dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (12 MFMAs a block).
+//                It also writes each row's statistics (lse_i log2 e,
+//                D_i = dy_i . y_i; a padded row, lse = -inf, gets (+inf, 0),
+//                so its weights vanish) for the kernels after it.
 //   dkdv_kernel  key-major: a tile of 64 class keys streams the blocks of
 //                the queries that read them: S = Q K^T, dP = dY V^T,
 //                dS = P (dP - D), dV^T += dY^T P, dK^T += Q^T dS (16 MFMAs).
@@ -203,31 +204,6 @@ __device__ void build_gtab(const Plan& P, const Tile& tk, const uint8_t* padrow,
 
 // ---------------------------------------------------------------------------
 
-// (lse_i log2 e, D_i) per row; eight lanes per row, 8 channels each
-__global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ out, const float* __restrict__ lse,
-                                                   const uint16_t* __restrict__ dy, float2* __restrict__ stats,
-                                                   long long rows) {
-    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long row = gid >> 3;
-    const int part = (int)(gid & 7);
-    float s = 0.f;
-    float l = kNegInf;
-    if (row < rows) {
-        const u32x4 a = *(const u32x4*)(out + row * D + 8 * part);
-        const u32x4 b = *(const u32x4*)(dy + row * D + 8 * part);
-#pragma unroll
-        for (int e = 0; e < 4; e++) s += bf_lo(a[e]) * bf_lo(b[e]) + bf_hi(a[e]) * bf_hi(b[e]);
-        l = lse[row];
-    }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    if (row < rows && part == 0) {
-        const bool none = !(l > kNegInf);   // a padded row
-        stats[row] = make_float2(none ? __builtin_huge_valf() : l * kLog2e, none ? 0.f : s);
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Shared by both band kernels: the tile's block list.  Blocks 0 .. nb-1 are
 // the band (class blocks kb_lo ..), then ngb global blocks (32 slots each),
@@ -368,14 +344,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     };
     auto pad_word = [&](uint32_t byte) -> uint32_t { return (uint32_t)__ballot(lane < 32 && byte != 0u); };
 
-    // this lane's query: Q and dY as operands, its statistics
+    // this lane's query: Q and dY as operands, the forward's output row and
+    // lse for its statistics
     const __amdgpu_buffer_rsrc_t rq = buffer_rsrc((const char*)A.q + head * ROWB, (uint32_t)T * ROWB);
     const __amdgpu_buffer_rsrc_t ry = buffer_rsrc((const char*)A.dy + head * ROWB, (uint32_t)T * ROWB);
-    bf16x8 qh[4], yh[4];
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc((const char*)A.y + head * ROWB, (uint32_t)T * ROWB);
+    bf16x8 qh[4], yh[4], oh[4];
     load_operand(rq, my_pos, lg, qh);
     load_operand(ry, my_pos, lg, yh);
-    float2 st = make_float2(__builtin_huge_valf(), 0.f);
-    if (my_pos >= 0) st = ((const float2*)A.stats)[head + my_pos];
+    load_operand(ro, my_pos, lg, oh);
+    const float lse_nat = my_pos >= 0 ? A.lse[head + my_pos] : kNegInf;
     f32x16 acc[2] = {(f32x16){}, (f32x16){}};
     const int kbase = ph * BLK + lq * 32 + ((lg ^ ((lq >> 3) & 1)) << 4);
     const int tbase = ph * BLK + 8192 + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) +
@@ -394,7 +372,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     }
     if (!early0) issue(0, 0, 0u);
     barrier_lds_loads();
-    const float nl = -st.x, Dq = st.y;
+    // D = dy . y over this lane's 32 channels, then the other half's
+    float dsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+        const u32x4 a = __builtin_bit_cast(u32x4, yh[ks]), b = __builtin_bit_cast(u32x4, oh[ks]);
+#pragma unroll
+        for (int e = 0; e < 4; e++) dsum += bf_lo(a[e]) * bf_lo(b[e]) + bf_hi(a[e]) * bf_hi(b[e]);
+    }
+    dsum = halves_sum(dsum);
+    const bool no_row = !(lse_nat > kNegInf);   // a padded row, or no row
+    const float nl = no_row ? kNegInf : -lse_nat * kLog2e, Dq = no_row ? 0.f : dsum;
+    // every row's statistics, for the dk/dv and global-row kernels (each row
+    // is in one tile; the phase-0 waves write them)
+    if (ph == 0 && lg == 0 && my_pos >= 0) ((float2*)A.stats)[head + my_pos] = make_float2(-nl, Dq);
     if constexpr (PAD) {
         pm_cur = pad_word(pm_cur);
         // stage 0 went out before its padding word was known: clear what this
@@ -799,24 +790,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 
 extern "C" int lfk_bwd_band_grid(const lfk::Plan* P) { return 8 * ((P->n_band_tasks + 7) / 8); }
 
-extern "C" hipError_t lfk_bwd_prep(const void* out, const float* lse, const void* dy, float2* stats, long long rows,
-                                   void* stream) {
-    const long long threads = rows * 8;
-    hipLaunchKernelGGL(lfk::bwd::prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       (hipStream_t)stream, (const uint16_t*)out, lse, (const uint16_t*)dy, stats, rows);
+// A: argument of the band kernels (A->plan: device copy of *P).  The dq
+// kernel also writes every row's statistics, which the dk/dv kernel and
+// the global-row kernels read: launch it first.
+extern "C" hipError_t lfk_bwd_dq(const lfk::BwdBandArgs* A, const lfk::Plan* P, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 g(lfk_bwd_band_grid(P)), b(256);
+    if (A->pad)
+        hipLaunchKernelGGL(lfk::bwd::dq_kernel<true>, g, b, 0, s, *A);
+    else
+        hipLaunchKernelGGL(lfk::bwd::dq_kernel<false>, g, b, 0, s, *A);
     return hipGetLastError();
 }
 
-// A: argument of both band kernels (A->plan: device copy of *P)
-extern "C" hipError_t lfk_bwd_band(const lfk::BwdBandArgs* A, const lfk::Plan* P, void* stream) {
+extern "C" hipError_t lfk_bwd_dkdv(const lfk::BwdBandArgs* A, const lfk::Plan* P, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     const dim3 g(lfk_bwd_band_grid(P)), b(256);
-    if (A->pad) {
-        hipLaunchKernelGGL(lfk::bwd::dq_kernel<true>, g, b, 0, s, *A);
+    if (A->pad)
         hipLaunchKernelGGL(lfk::bwd::dkdv_kernel<true>, g, b, 0, s, *A);
-    } else {
-        hipLaunchKernelGGL(lfk::bwd::dq_kernel<false>, g, b, 0, s, *A);
+    else
         hipLaunchKernelGGL(lfk::bwd::dkdv_kernel<false>, g, b, 0, s, *A);
-    }
     return hipGetLastError();
 }

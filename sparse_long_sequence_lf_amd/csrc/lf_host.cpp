@@ -27,9 +27,8 @@ extern "C" hipError_t lfk_noalloc_scratch(void **ptr);
 extern "C" hipError_t lfk_write_plan(const void *plan, size_t bytes, void *dst, int *zero, int n_zero, void *stream);
 extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs *A, const void *const *t, int dtype_bf16, void *stream);
 extern "C" hipError_t lfk_bwd_global_launch(const lfk::BwdArgs *A, const void *const *t, void *stream);
-extern "C" hipError_t lfk_bwd_prep(const void *out, const float *lse, const void *dy, float2 *stats, long long rows,
-                                   void *stream);
-extern "C" hipError_t lfk_bwd_band(const lfk::BwdBandArgs *A, const lfk::Plan *P, void *stream);
+extern "C" hipError_t lfk_bwd_dq(const lfk::BwdBandArgs *A, const lfk::Plan *P, void *stream);
+extern "C" hipError_t lfk_bwd_dkdv(const lfk::BwdBandArgs *A, const lfk::Plan *P, void *stream);
 
 namespace {
 
@@ -776,21 +775,24 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
         out = FA.out;
         lse = FA.lse;
     }
-    e = lfk_bwd_prep(out, lse, dy, (float2 *)A.stats, (long long)rows, stream);
-    if (e != hipSuccess) return fail(LF_E_HIP, "statistics launch: %s", hipGetErrorString(e));
-    e = lfk_bwd_global_launch(&A, t, stream);
-    if (e != hipSuccess) return fail(LF_E_HIP, "global-row launch: %s", hipGetErrorString(e));
     lfk::BwdBandArgs BA;
     BA.q = q; BA.k = k; BA.v = v; BA.dy = dy;
+    BA.y = out;
+    BA.lse = lse;
     BA.dq = dq; BA.dk = dk; BA.dv = dv;
     BA.pad = key_padding_mask;
     BA.plan = dplan;
-    BA.stats = (const float *)A.stats;
+    BA.stats = (float *)A.stats;
     BA.gmap = A.gmap;
     BA.inv_off = A.inv_off;
     BA.inv_list = A.inv_list;
-    e = lfk_bwd_band(&BA, &F.P, stream);
-    if (e != hipSuccess) return fail(LF_E_HIP, "band launch: %s", hipGetErrorString(e));
+    // dq first: it writes every row's statistics
+    e = lfk_bwd_dq(&BA, &F.P, stream);
+    if (e != hipSuccess) return fail(LF_E_HIP, "dq launch: %s", hipGetErrorString(e));
+    e = lfk_bwd_global_launch(&A, t, stream);
+    if (e != hipSuccess) return fail(LF_E_HIP, "global-row launch: %s", hipGetErrorString(e));
+    e = lfk_bwd_dkdv(&BA, &F.P, stream);
+    if (e != hipSuccess) return fail(LF_E_HIP, "dk/dv launch: %s", hipGetErrorString(e));
     return LF_OK;
 }
 

@@ -94,14 +94,18 @@ struct Args {
 };
 
 // The argument of the matrix-core backward kernels (lf_bwd_mfma.hip): bf16
-// tensors [B][H][T][64], the forward's plan (band tiles, radii, strides,
-// global set, random key blocks) and the row statistics.
+// tensors [B][H][T][64], the forward's output y and lse, the forward's plan
+// (band tiles, radii, strides, global set, random key blocks) and the row
+// statistics.
 struct BwdBandArgs {
     const void *q, *k, *v, *dy;
+    const void *y;           // the forward's output
+    const float *lse;        // [B][H][T] its natural log-sum-exp (-inf for a padded row)
     void *dq, *dk, *dv;
     const uint8_t *pad;      // [B][T] or null
     const Plan *plan;
-    const float *stats;      // [B*H][T][2]: (lse * log2 e, D = dy . y); (+inf, 0) for a padded row
+    float *stats;            // [B*H][T][2]: (lse * log2 e, D = dy . y); (+inf, 0) for a padded row,
+                             // written by the dq kernel, read by the dk/dv and global-row kernels
     const uint32_t *gmap;    // bit j set iff position j is global ([ceil(T/32)] words)
     const int32_t *inv_off;  // random blocks: [H][ceil(T/64) + 1] offsets into inv_list per key block
     const int32_t *inv_list; // the query blocks that drew each key block, ascending
