@@ -1,5 +1,7 @@
 // lf_bwd.h -- the launch record shared by the host code of lf_attn_bwd
-// (lf_host.cpp) and the backward kernels (lf_bwd_kernels.hip).  Internal to
+// (lf_host.cpp) and the fp32 backward kernels (lf_bwd_kernels.hip); bf16
+// input takes the matrix-core kernels of lf_bwd_mfma.hip, whose argument is
+// in lf_kernels.h.  Internal to
 // liblfattn.so; the public interface is include/lf_attn.h.
 #ifndef LF_BWD_H
 #define LF_BWD_H
@@ -34,13 +36,11 @@ struct BwdArgs {
     const int32_t *head_chunk;   // [H+1] prefix of the class chunks (LFB_ROWS_PER_WAVE positions) over the heads
                                  // in the order hord lists them
     const int32_t *hord;         // [H] heads by decreasing radius: the longest waves are dealt out first
-    void *stats;                 // float2 [B*H][T]: (log2-sum-exp of the scaled scores, D_i); the
-                                 // same layout as the prep kernel of lf_bwd_mfma.hip writes
+    void *stats;                 // float2 [B*H][T]: (log2-sum-exp of the scaled scores, D_i)
     float4 *gstat;               // [B*H*n_g][n_split]: a split's (max, sum, sum of p dP) of a global row
     float *gpart;                // [B*H*n_g][n_split][192]: a split's partial dq, dk, dv of a global position
     int B, H, T, n_g, one_sided;
     int n_chunks;                // head_chunk[H]: class chunks of one batch entry (the host's copy)
-    int stats_given;             // 1: stats holds every row's (lse, D) before the launches (bf16 path)
     int n_split, split_len;      // global rows and columns: splits of split_len positions (256 x per-thread count)
     // random key blocks of 64 (undilated heads only), or n_rand = 0
     const int32_t *rtab;         // [H][ceil(T/64)][n_rand] key blocks per query block, ascending, -1 = none

@@ -1,5 +1,6 @@
 // lf_bwd_kernels.hip -- gradients of the Longformer sparse self-attention
-// forward (dq, dk, dv) for gfx950.
+// forward (dq, dk, dv) for fp32 input on gfx950, in fp32 on the vector units
+// (bf16 input runs on the matrix cores: lf_bwd_mfma.hip).
 //
 // The pages describe no backward pass (Longformer, ciallo.wiki, §5.2 only
 // states that training cost grows linearly with the length).  These kernels
@@ -693,9 +694,8 @@ __global__ __launch_bounds__(256) void grows_stats_kernel(const lfk::BwdArgs A, 
     }
 }
 
-// pass 2 of a global row: the split's part of dq.  Its (lse, D) come from
-// the forward's statistics when given, else from the pass-1 records (and
-// split 0 writes them for the column kernels).
+// pass 2 of a global row: the split's part of dq; split 0 also writes the
+// row's (lse, D) for the column kernels
 template <typename ET>
 __global__ __launch_bounds__(256) void grows_dq_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
                                                        const ET* __restrict__ K, const ET* __restrict__ V,
@@ -708,29 +708,20 @@ __global__ __launch_bounds__(256) void grows_dq_kernel(const lfk::BwdArgs A, con
     RowF acc;
     zero_row(acc);
     if (!padded(pad, t.g)) {
-        float lse, Dl;
-        if (A.stats_given) {
-            // from the forward's statistics
-            const float2 st = stats[t.bh * T + t.g];
-            lse = st.x;
-            Dl = st.y;
-        } else {
-            // the row's statistics from every split's record
-            const float4* gs = A.gstat + t.rec * A.n_split;
-            float M = -INFINITY;
-            for (int e = 0; e < A.n_split; e++) M = fmaxf(M, gs[e].x);
-            float L = 0.f, DN = 0.f;
-            for (int e = 0; e < A.n_split; e++) {
-                const float4 r = gs[e];
-                if (r.y == 0.f) continue;
-                const float w = ex2(r.x - M);
-                L += r.y * w;
-                DN += r.z * w;
-            }
-            lse = M + lg2(L);   // key g itself is valid, so L >= 1
-            Dl = DN / L;
-            if (t.sp == 0 && tid == 0) stats[t.bh * T + t.g] = make_float2(lse, Dl);
+        // the row's statistics from every split's record
+        const float4* gs = A.gstat + t.rec * A.n_split;
+        float M = -INFINITY;
+        for (int e = 0; e < A.n_split; e++) M = fmaxf(M, gs[e].x);
+        float L = 0.f, DN = 0.f;
+        for (int e = 0; e < A.n_split; e++) {
+            const float4 r = gs[e];
+            if (r.y == 0.f) continue;
+            const float w = ex2(r.x - M);
+            L += r.y * w;
+            DN += r.z * w;
         }
+        const float lse = M + lg2(L), Dl = DN / L;   // key g itself is valid, so L >= 1
+        if (t.sp == 0 && tid == 0) stats[t.bh * T + t.g] = make_float2(lse, Dl);
         const ET* Kh = K + t.bh * T * D;
         const ET* Vh = V + t.bh * T * D;
         RowF q, dy;
@@ -863,28 +854,8 @@ hipError_t launch(const lfk::BwdArgs* A, const void* const* t, hipStream_t s) {
 
 }  // namespace lfb
 
-// t = {q, k, v, dy, dq, dk, dv}
-extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs* A, const void* const* t, int dtype_bf16, void* stream) {
-    hipStream_t s = (hipStream_t)stream;
-    return dtype_bf16 ? lfb::launch<__bf16>(A, t, s) : lfb::launch<float>(A, t, s);
+// fp32 tensors t = {q, k, v, dy, dq, dk, dv}
+extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs* A, const void* const* t, void* stream) {
+    return lfb::launch<float>(A, t, (hipStream_t)stream);
 }
 
-// The global rows' dq and the global keys' dk, dv of bf16 input, with the
-// row statistics given (A->stats_given, A->stats filled): the splits' parts,
-// then their sums.  t as above.
-extern "C" hipError_t lfk_bwd_global_launch(const lfk::BwdArgs* A, const void* const* t, void* stream) {
-    hipStream_t s = (hipStream_t)stream;
-    using ET = __bf16;
-    if (A->n_g == 0) return hipSuccess;
-    const ET* q = (const ET*)t[0];
-    const ET* k = (const ET*)t[1];
-    const ET* v = (const ET*)t[2];
-    const ET* dy = (const ET*)t[3];
-    float2* st = (float2*)A->stats;
-    const long long recs = (long long)A->B * A->H * A->n_g;
-    const dim3 gs((unsigned)(recs * A->n_split)), gc((unsigned)recs), blk(256);
-    hipLaunchKernelGGL(lfb::grows_dq_kernel<ET>, gs, blk, 0, s, *A, q, k, v, dy, st);
-    hipLaunchKernelGGL(lfb::gcols_kernel<ET>, gs, blk, 0, s, *A, q, k, v, dy, st);
-    hipLaunchKernelGGL(lfb::combine_kernel<ET>, gc, dim3(64), 0, s, *A, (ET*)t[4], (ET*)t[5], (ET*)t[6]);
-    return hipGetLastError();
-}

@@ -71,32 +71,127 @@ constexpr int GT = LF_MAX_GLOBALS;
 // which a 32x32 accumulator packs into the other operand.
 
 struct Tile {
+    int kind;            // 0: band tile; 1: the global rows (dq) or global keys (dk, dv) of one split
     int b, h, bh, c, delta, n, m0, r, ra;
+    int split, lo, hi;   // kind 1: the split and the rows it streams, [lo, hi)
 };
 
 __device__ __forceinline__ Tile decode_tile(const Plan& P, int t) {
-    const BandTask bt = decode_band(P, t);
     Tile k;
-    k.b = bt.b;
-    k.h = bt.h;
-    k.bh = bt.b * P.H + bt.h;
-    k.c = bt.c;
-    k.delta = P.dil[bt.h];
-    k.n = bt.n;
-    k.m0 = bt.tile * BM;
-    k.r = P.rad[bt.h];
-    k.ra = P.one_sided ? 0 : k.r;
+    if (t < P.n_band_tasks) {
+        const BandTask bt = decode_band(P, t);
+        k.kind = 0;
+        k.b = bt.b;
+        k.h = bt.h;
+        k.bh = bt.b * P.H + bt.h;
+        k.c = bt.c;
+        k.delta = P.dil[bt.h];
+        k.n = bt.n;
+        k.m0 = bt.tile * BM;
+        k.r = P.rad[bt.h];
+        k.ra = P.one_sided ? 0 : k.r;
+        k.split = 0;
+        k.lo = 0;
+        k.hi = k.n;
+    } else {
+        const RowTask rt = decode_rows(P, t - P.n_band_tasks);
+        k.kind = 1;
+        k.bh = rt.bh;
+        k.b = mdiv(rt.bh, P.mg_H);
+        k.h = rt.bh - k.b * P.H;
+        k.c = 0;
+        k.delta = 1;
+        k.n = P.T;
+        k.m0 = rt.grp * BM;
+        k.r = 0;
+        k.ra = 0;
+        k.split = rt.split;
+        k.lo = rt.split * P.split_len;
+        k.hi = min(k.lo + P.split_len, P.T);
+    }
     return k;
 }
 
-// each of the 8 dies (blockIdx % 8) takes a contiguous eighth of the tiles,
-// so that neighbouring tiles, which read the same rows, share its L2; -1
-// for a slot past the end
+// Each of the 8 dies (blockIdx % 8) takes an eighth of the global tasks
+// first (they are short and end with a combine), then a contiguous eighth
+// of the band tiles, so that neighbouring tiles, which read the same rows,
+// share its L2; -1 for a slot past the end.
 __device__ __forceinline__ int tile_of_block(const Plan& P) {
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int nb = P.n_band_tasks;
+    const int xcd = blockIdx.x & 7;
+    int slot = blockIdx.x >> 3;
+    const int nb = P.n_band_tasks, ng = P.n_tasks - P.n_band_tasks;
+    const int ng_x = (ng >> 3) + (xcd < (ng & 7)), ng_o = xcd * (ng >> 3) + min(xcd, ng & 7);
+    if (slot < ng_x) return nb + ng_o + slot;
+    slot -= ng_x;
     const int nb_x = (nb >> 3) + (xcd < (nb & 7)), nb_o = xcd * (nb >> 3) + min(xcd, nb & 7);
     return slot < nb_x ? nb_o + slot : -1;
+}
+
+// The last of the n_split * n_ggroups workgroups of head (b, h) to finish
+// a global task returns true (and the counter to zero for the next call):
+// every partial record of the head is then written.  The records cross
+// dies, so they are written and read with the agent-coherent policy.
+__device__ __forceinline__ bool last_arriver(const Plan& P, int* counter, int bh, char* smem) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's record stores have completed
+    __syncthreads();
+    int* flag = (int*)smem;
+    if (threadIdx.x == 0) {
+        const int done = __hip_atomic_fetch_add(counter + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = done == P.n_split * P.n_ggroups - 1;
+        if (last) __hip_atomic_store(counter + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+    }
+    __syncthreads();
+    return *flag != 0;
+}
+
+// write a partial record: this lane's channels 32cb + 8j + 4lg .. +3 of an
+// O^T-form accumulator pair at float offset `rec` (+ 64 * part)
+__device__ __forceinline__ void store_record(__amdgpu_buffer_rsrc_t rs, uint32_t rec, const f32x16 (&acc)[2],
+                                             int lg) {
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const f32x4 o4 = {acc[cb][4 * j], acc[cb][4 * j + 1], acc[cb][4 * j + 2], acc[cb][4 * j + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), rs,
+                                                   4u * (rec + 32 * cb + 8 * j + 4 * lg), 0, kCoherent);
+        }
+}
+
+// Sum of the splits' records of head bh: thread task (gi, part, c4) adds
+// channels 4 c4 .. +3 of part `part` of global slot gi over the splits and
+// writes them to the part's output row (bf16, times scale[part]); zeros at
+// a padded position.  nparts: 1 (dq) or 2 (dk, dv); records hold 64 floats
+// per part.
+__device__ __forceinline__ void combine_records(const Plan& P, __amdgpu_buffer_rsrc_t rs, int nparts, int bh,
+                                                const uint8_t* padrow, uint16_t* out0, uint16_t* out1,
+                                                float scale0, float scale1) {
+    const int n_g = P.n_g, T = P.T;
+    const uint32_t rstride = 64u * nparts;                         // floats per record
+    const uint32_t sstride = (uint32_t)P.g_pad * rstride;          // floats between splits of a slot
+    for (int task = threadIdx.x; task < n_g * nparts * 16; task += 256) {
+        const int gi = task / (nparts * 16), rem = task % (nparts * 16), part = rem / 16, c4 = rem % 16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int sp0 = 0; sp0 < P.n_split; sp0 += 8) {
+            f32x4 o[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const uint32_t rec = (uint32_t)min(sp0 + i, P.n_split - 1) * sstride + (uint32_t)gi * rstride +
+                                     64u * part + 4u * c4;
+                o[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4u * rec, 0, kCoherent));
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                if (sp0 + i < P.n_split) acc += o[i];
+        }
+        const int pos = P.glob[gi];
+        const float sc = part == 0 ? scale0 : scale1;
+        uint16_t* row = (part == 0 ? out0 : out1) + ((size_t)bh * T + pos) * D + 4 * c4;
+        u32x2 w = {pack_bf16(acc[0] * sc, acc[1] * sc), pack_bf16(acc[2] * sc, acc[3] * sc)};
+        if (padrow && padrow[pos] != 0) w = (u32x2){0u, 0u};   // zeros, whatever the records hold
+        *(u32x2*)row = w;
+    }
 }
 
 // One row as the MFMA operand of a 32x32x16 product, row per lane: lane l
@@ -243,21 +338,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const size_t head = (size_t)tk.bh * T;
     const uint8_t* padrow = PAD ? A.pad + (size_t)tk.b * T : nullptr;
 
-    const int mq0 = tk.m0 + 32 * qb;             // this wave's first query (class index)
-    const bool wave_active = mq0 < tk.n;
+    // this wave's 32 queries (band: class positions; kind 1: global slots) and this lane's
+    const int mq0 = tk.m0 + 32 * qb;
     const int m_me = mq0 + lq;
-    const int my_pos = m_me < tk.n ? tk.c + tk.delta * m_me : -1;
+    const bool glob_task = tk.kind == 1;
+    const bool wave_active = mq0 < (glob_task ? P.n_g : tk.n);
+    int my_pos = -1;
+    if (!glob_task && m_me < tk.n) my_pos = tk.c + tk.delta * m_me;
+    if (glob_task && m_me < P.n_g) my_pos = P.glob[m_me];
+    const int key_end = glob_task ? tk.hi : tk.n;   // keys at or past it (class index) are none
 
     Blocks bl;
-    {
+    if (!glob_task) {
         int lo_k = tk.m0 - r; if (lo_k < 0) lo_k = 0;
         int hi_k = tk.m0 + BM - 1 + ra; if (hi_k > tk.n - 1) hi_k = tk.n - 1;
         bl.kb_lo = lo_k / KBLK;
         bl.nb = hi_k / KBLK - bl.kb_lo + 1;
         bl.ngb = P.n_g > 0 ? (P.n_g + KBLK - 1) / KBLK : 0;
         bl.nrb = P.n_rand > 0 ? 2 * P.n_rand : 0;
-        bl.nblk = bl.nb + bl.ngb + bl.nrb;
+    } else {
+        // a global row reads every key: the split's keys, no window
+        bl.kb_lo = tk.lo / KBLK;
+        bl.nb = (tk.hi - tk.lo + KBLK - 1) / KBLK;
+        bl.ngb = 0;
+        bl.nrb = 0;
     }
+    bl.nblk = bl.nb + bl.ngb + bl.nrb;
     const int NS = (bl.nblk + 1) >> 1;
     // random key blocks of this query block (undilated: tile = query block)
     const int32_t* rrow = bl.nrb > 0 ? P.rtab + ((size_t)tk.h * ((T + 63) >> 6) + (tk.m0 >> 6)) * P.n_rand : nullptr;
@@ -268,13 +374,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     };
     // band blocks with keys for this wave's queries, and those needing no mask
     int j_lo = 0, j_hi = -1, ji_lo = 0, ji_hi = -1;
-    if (wave_active) {
+    if (wave_active && !glob_task) {
         int a = mq0 - r; if (a < 0) a = 0;
         int z = mq0 + 31 + ra; if (z > tk.n - 1) z = tk.n - 1;
         j_lo = a / KBLK - bl.kb_lo;
         j_hi = z / KBLK - bl.kb_lo;
         ji_lo = ((mq0 + 31 - r + 31) >> 5) - bl.kb_lo;
         ji_hi = min((mq0 + ra - 31) >> 5, (tk.n - 32) >> 5) - bl.kb_lo;
+    } else if (wave_active) {
+        j_hi = bl.nb - 1;
+        ji_hi = ((key_end - 32) >> 5) - bl.kb_lo;
     }
 
     // ---- loads
@@ -385,7 +494,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const float nl = no_row ? kNegInf : -lse_nat * kLog2e, Dq = no_row ? 0.f : dsum;
     // every row's statistics, for the dk/dv and global-row kernels (each row
     // is in one tile; the phase-0 waves write them)
-    if (ph == 0 && lg == 0 && my_pos >= 0) ((float2*)A.stats)[head + my_pos] = make_float2(-nl, Dq);
+    if (!glob_task && ph == 0 && lg == 0 && my_pos >= 0) ((float2*)A.stats)[head + my_pos] = make_float2(-nl, Dq);
     if constexpr (PAD) {
         pm_cur = pad_word(pm_cur);
         // stage 0 went out before its padding word was known: clear what this
@@ -440,8 +549,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             read_tr(smem + oc + tbase, tf);
             if (kd == kBand) {
                 if (!(j >= ji_lo && j <= ji_hi && (!PAD || pm_cur == 0u))) {
-                    mask_window(sc, m_me - r - (bl.kb_lo + j) * KBLK - 4 * lg, r + ra);
-                    const int valid = tk.n - (bl.kb_lo + j) * KBLK;
+                    if (!glob_task) mask_window(sc, m_me - r - (bl.kb_lo + j) * KBLK - 4 * lg, r + ra);
+                    const int valid = key_end - (bl.kb_lo + j) * KBLK;
                     uint32_t bad = valid >= KBLK ? 0u : (0xffffffffu << valid);
                     if constexpr (PAD) bad |= pm_cur;
                     if (bad != 0u) mask_bits(sc, ~lane_bits(bad, lg));
@@ -485,6 +594,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
                 mbuf[4 * cb + i] = (f32x4){acc[cb][4 * i], acc[cb][4 * i + 1], acc[cb][4 * i + 2], acc[cb][4 * i + 3]};
     }
     __syncthreads();
+    if (glob_task) {
+        // this split's part of the global rows' dq, then the last of the
+        // head's tasks adds the parts up
+        const uint32_t rstride = (uint32_t)P.g_pad * 64u;
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(A.part_q + (size_t)tk.bh * P.n_split * rstride,
+                                                      (uint32_t)P.n_split * rstride * 4u);
+        if (ph == 0 && wave_active && m_me < P.n_g) {
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const f32x4 x = mbuf[4 * cb + i];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) acc[cb][4 * i + e] += x[e];
+                }
+            store_record(rs, (uint32_t)tk.split * rstride + (uint32_t)m_me * 64u, acc, lg);
+        }
+        if (last_arriver(P, A.count_q, tk.bh, smem))
+            combine_records(P, rs, 1, tk.bh, padrow, (uint16_t*)A.dq, nullptr, 0.125f, 0.f);
+        return;
+    }
     if (ph == 1 || my_pos < 0) return;
 #pragma unroll
     for (int cb = 0; cb < 2; cb++)
@@ -494,7 +624,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 #pragma unroll
             for (int e = 0; e < 4; e++) acc[cb][4 * i + e] += x[e];
         }
-    if (is_global(A.gmap, my_pos)) return;   // the global-row kernels write it
+    if (is_global(A.gmap, my_pos)) return;   // the global-row tasks write it
     const bool zero = PAD && padrow[my_pos] != 0;
     store_row((uint16_t*)A.dq + (head + my_pos) * D, acc, 0.125f, zero, lg);
 }
@@ -524,25 +654,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const size_t head = (size_t)tk.bh * T;
     const uint8_t* padrow = PAD ? A.pad + (size_t)tk.b * T : nullptr;
 
-    const int mk0 = tk.m0 + 32 * kb;             // this wave's first key (class index)
-    const bool wave_active = mk0 < tk.n;
+    // this wave's 32 keys (band: class positions; kind 1: global slots) and this lane's
+    const int mk0 = tk.m0 + 32 * kb;
     const int m_me = mk0 + lq;
-    const int my_pos = m_me < tk.n ? tk.c + tk.delta * m_me : -1;
+    const bool glob_task = tk.kind == 1;
+    const bool wave_active = mk0 < (glob_task ? P.n_g : tk.n);
+    int my_pos = -1;
+    if (!glob_task && m_me < tk.n) my_pos = tk.c + tk.delta * m_me;
+    if (glob_task && m_me < P.n_g) my_pos = P.glob[m_me];
+    const int q_end = glob_task ? tk.hi : tk.n;   // queries at or past it (class index) are none
 
     // query t reads key u when u - t is in [-r, ra]: key u is read by the
-    // queries [u - ra, u + r]
+    // queries [u - ra, u + r]; every query reads a global key
     Blocks bl;
-    {
+    if (!glob_task) {
         int lo_q = tk.m0 - ra; if (lo_q < 0) lo_q = 0;
         int hi_q = tk.m0 + BM - 1 + r; if (hi_q > tk.n - 1) hi_q = tk.n - 1;
         bl.kb_lo = lo_q / KBLK;
         bl.nb = hi_q / KBLK - bl.kb_lo + 1;
         bl.ngb = P.n_g > 0 ? (P.n_g + KBLK - 1) / KBLK : 0;
-        bl.nrb = 0;
+    } else {
+        bl.kb_lo = tk.lo / KBLK;
+        bl.nb = (tk.hi - tk.lo + KBLK - 1) / KBLK;
+        bl.ngb = 0;
     }
+    bl.nrb = 0;
     // random blocks: the query blocks that drew this key block (undilated)
     int ioff = 0;
-    if (P.n_rand > 0) {
+    if (P.n_rand > 0 && !glob_task) {
         const int32_t* off = A.inv_off + (size_t)tk.h * (((T + 63) >> 6) + 1) + (tk.m0 >> 6);
         ioff = off[0];
         bl.nrb = 2 * (off[1] - off[0]);
@@ -554,7 +693,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         return 64 * A.inv_list[ioff + (jr >> 1)] + 32 * (jr & 1);
     };
     int j_lo = 0, j_hi = -1, ji_lo = 0, ji_hi = -1;
-    if (wave_active) {
+    if (wave_active && !glob_task) {
         int a = mk0 - ra; if (a < 0) a = 0;
         int z = mk0 + 31 + r; if (z > tk.n - 1) z = tk.n - 1;
         j_lo = a / KBLK - bl.kb_lo;
@@ -562,6 +701,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         // every query q0 .. q0+31 of the block reads every key mk0 .. mk0+31
         ji_lo = ((mk0 + 31 - ra + 31) >> 5) - bl.kb_lo;
         ji_hi = min((mk0 + r - 31) >> 5, (tk.n - 32) >> 5) - bl.kb_lo;
+    } else if (wave_active) {
+        j_hi = bl.nb - 1;
+        ji_hi = ((q_end - 32) >> 5) - bl.kb_lo;
     }
 
     // ---- loads
@@ -720,8 +862,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             // element i: query row 8(i>>2) + 4lg + (i&3) of the block, this lane's key
             if (kd == kBand) {
                 if (!(j >= ji_lo && j <= ji_hi)) {
-                    mask_window(sc, m_me - ra - (bl.kb_lo + j) * KBLK - 4 * lg, r + ra);
-                    const int valid = tk.n - (bl.kb_lo + j) * KBLK;
+                    if (!glob_task) mask_window(sc, m_me - ra - (bl.kb_lo + j) * KBLK - 4 * lg, r + ra);
+                    const int valid = q_end - (bl.kb_lo + j) * KBLK;
                     if (valid < KBLK) mask_bits(sc, ~lane_bits(0xffffffffu << valid, lg));
                 }
             } else if (kd == kGlob) {
@@ -767,19 +909,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             }
     }
     __syncthreads();
-    if (ph == 1 || my_pos < 0) return;
+    auto merge = [&]() {
 #pragma unroll
-    for (int cb = 0; cb < 2; cb++)
+        for (int cb = 0; cb < 2; cb++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const f32x4 x = mbuf[4 * cb + i], y = mbuf[8 + 4 * cb + i];
+            for (int i = 0; i < 4; i++) {
+                const f32x4 x = mbuf[4 * cb + i], y = mbuf[8 + 4 * cb + i];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                ak[cb][4 * i + e] += x[e];
-                av[cb][4 * i + e] += y[e];
+                for (int e = 0; e < 4; e++) {
+                    ak[cb][4 * i + e] += x[e];
+                    av[cb][4 * i + e] += y[e];
+                }
             }
+    };
+    if (glob_task) {
+        // this split's part of the global keys' dk and dv, then the last of
+        // the head's tasks adds the parts up
+        const uint32_t rstride = (uint32_t)P.g_pad * 128u;
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(A.part_kv + (size_t)tk.bh * P.n_split * rstride,
+                                                      (uint32_t)P.n_split * rstride * 4u);
+        if (ph == 0 && wave_active && m_me < P.n_g) {
+            merge();
+            const uint32_t rec = (uint32_t)tk.split * rstride + (uint32_t)m_me * 128u;
+            store_record(rs, rec, ak, lg);
+            store_record(rs, rec + 64u, av, lg);
         }
-    if (is_global(A.gmap, my_pos)) return;   // the global-key kernels write it
+        if (last_arriver(P, A.count_kv, tk.bh, smem))
+            combine_records(P, rs, 2, tk.bh, padrow, (uint16_t*)A.dk, (uint16_t*)A.dv, 0.125f, 1.0f);
+        return;
+    }
+    if (ph == 1 || my_pos < 0) return;
+    merge();
+    if (is_global(A.gmap, my_pos)) return;   // the global-key tasks write it
     const bool zero = PAD && padrow[my_pos] != 0;
     store_row((uint16_t*)A.dk + (head + my_pos) * D, ak, 0.125f, zero, lg);
     store_row((uint16_t*)A.dv + (head + my_pos) * D, av, 1.0f, zero, lg);
@@ -788,7 +949,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 }  // namespace bwd
 }  // namespace lfk
 
-extern "C" int lfk_bwd_band_grid(const lfk::Plan* P) { return 8 * ((P->n_band_tasks + 7) / 8); }
+// grid of the band kernels: the slots of the 8 dies, each holding an eighth
+// of the global tasks and of the band tiles
+extern "C" int lfk_bwd_band_grid(const lfk::Plan* P) {
+    const int nb = P->n_band_tasks, ng = P->n_tasks - P->n_band_tasks;
+    return 8 * ((nb + 7) / 8 + (ng + 7) / 8);
+}
 
 // A: argument of the band kernels (A->plan: device copy of *P).  The dq
 // kernel also writes every row's statistics, which the dk/dv kernel and

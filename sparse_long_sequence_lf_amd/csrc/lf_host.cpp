@@ -25,8 +25,7 @@ extern "C" hipError_t lfk_launch(const lfk::Args *A, const lfk::Plan *P, int dty
 extern "C" int lfk_supports_d(int d);
 extern "C" hipError_t lfk_noalloc_scratch(void **ptr);
 extern "C" hipError_t lfk_write_plan(const void *plan, size_t bytes, void *dst, int *zero, int n_zero, void *stream);
-extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs *A, const void *const *t, int dtype_bf16, void *stream);
-extern "C" hipError_t lfk_bwd_global_launch(const lfk::BwdArgs *A, const void *const *t, void *stream);
+extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs *A, const void *const *t, void *stream);
 extern "C" hipError_t lfk_bwd_dq(const lfk::BwdBandArgs *A, const lfk::Plan *P, void *stream);
 extern "C" hipError_t lfk_bwd_dkdv(const lfk::BwdBandArgs *A, const lfk::Plan *P, void *stream);
 
@@ -98,6 +97,7 @@ struct Workspace {
     Buffer counters, scratch;
     Slot plan[kSlots], aux[kSlots], bwd[kSlots];
     Buffer bwd_stats, bwd_gpart;   // backward: row statistics; global-split records
+    Buffer bwd_count;              // backward (bf16): the global tasks' completion counters
     Buffer bwd_fwd;                // backward (bf16) without the forward's results: its output and lse
     std::vector<Retired> retired;
     uint64_t calls = 0;
@@ -561,10 +561,11 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
 }
 
 // Gradients (lf_attn_bwd, lf_attn_bwd_ex): checks, the tables, the launches.
-// bf16: the forward's output and statistics (given, or computed here into
-// the workspace), the row statistics, the global rows' and keys' vector
-// kernels, then the matrix-core band kernels.  fp32: the vector kernels,
-// which find the statistics themselves (out and lse are not read).
+// bf16: the forward's output and lse (given, or computed here into the
+// workspace), then the two matrix-core kernels: dq (it also writes the row
+// statistics and takes the global rows as split tasks), then dk and dv (the
+// global keys likewise).  fp32: the vector kernels, which find the
+// statistics themselves (out and lse are not read).
 lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy, const void *out,
                      const float *lse, int B, int H, int T, int d, const int32_t *radius, int one_sided,
                      const int32_t *rand_blocks, int n_rand, const int32_t *dilation, const int32_t *global_idx,
@@ -719,7 +720,7 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     const size_t n_rec = (size_t)recs * n_split;
     if (n_rec >= ((size_t)1 << 31)) return fail(LF_E_UNSUPPORTED, "too many global-row splits");
     const size_t gstat_bytes = (n_rec * 16 + 255) / 256 * 256;
-    if (n_rec > 0) {
+    if (n_rec > 0 && !mfma) {
         st = grow(*w, w->bwd_gpart, gstat_bytes + n_rec * 192 * sizeof(float), false, stream);
         if (st != LF_OK) return st;
     }
@@ -735,7 +736,6 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     A.dil = (const int32_t *)dt + o_dil;
     A.head_chunk = (const int32_t *)dt + o_hc;
     A.n_chunks = (int)chunks;
-    A.stats_given = mfma ? 1 : 0;
     A.hord = (const int32_t *)dt + o_ord;
     A.stats = w->bwd_stats.ptr;
     A.B = B; A.H = H; A.T = T; A.n_g = (int)G.size(); A.one_sided = one_sided;
@@ -749,7 +749,7 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     A.inv_list = n_rand > 0 ? (const int32_t *)dt + o_inv : nullptr;
     const void *t[7] = {q, k, v, dy, dq, dk, dv};
     if (!mfma) {
-        hipError_t e = lfk_bwd_launch(&A, t, 0, stream);
+        hipError_t e = lfk_bwd_launch(&A, t, stream);
         if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
         return LF_OK;
     }
@@ -786,11 +786,26 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     BA.gmap = A.gmap;
     BA.inv_off = A.inv_off;
     BA.inv_list = A.inv_list;
-    // dq first: it writes every row's statistics
+    BA.part_q = BA.part_kv = nullptr;
+    BA.count_q = BA.count_kv = nullptr;
+    if (F.P.n_g > 0) {
+        // the global tasks' partial records (64 floats a split and slot for
+        // dq, 128 for dk and dv) and their two sets of completion counters
+        const size_t recs = (size_t)B * H * F.P.n_split * F.P.g_pad;
+        const size_t q_bytes = (recs * 64 * sizeof(float) + 255) / 256 * 256;
+        st = grow(*w, w->bwd_gpart, q_bytes + recs * 128 * sizeof(float), false, stream);
+        if (st != LF_OK) return st;
+        st = grow(*w, w->bwd_count, 2 * (size_t)B * H * sizeof(int), true, stream);
+        if (st != LF_OK) return st;
+        BA.part_q = (float *)w->bwd_gpart.ptr;
+        BA.part_kv = (float *)((char *)w->bwd_gpart.ptr + q_bytes);
+        BA.count_q = (int *)w->bwd_count.ptr;
+        BA.count_kv = BA.count_q + (size_t)B * H;
+    }
+    // dq first: it writes every row's statistics; the global rows and keys
+    // are tasks of the two kernels
     e = lfk_bwd_dq(&BA, &F.P, stream);
     if (e != hipSuccess) return fail(LF_E_HIP, "dq launch: %s", hipGetErrorString(e));
-    e = lfk_bwd_global_launch(&A, t, stream);
-    if (e != hipSuccess) return fail(LF_E_HIP, "global-row launch: %s", hipGetErrorString(e));
     e = lfk_bwd_dkdv(&BA, &F.P, stream);
     if (e != hipSuccess) return fail(LF_E_HIP, "dk/dv launch: %s", hipGetErrorString(e));
     return LF_OK;

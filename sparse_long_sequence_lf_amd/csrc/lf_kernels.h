@@ -109,6 +109,12 @@ struct BwdBandArgs {
     const uint32_t *gmap;    // bit j set iff position j is global ([ceil(T/32)] words)
     const int32_t *inv_off;  // random blocks: [H][ceil(T/64) + 1] offsets into inv_list per key block
     const int32_t *inv_list; // the query blocks that drew each key block, ascending
+    // global tasks (the plan's global-row splits): partial records and
+    // completion counters (zero between calls; the last task of a head
+    // returns its counter to zero)
+    float *part_q;           // [B*H][n_split][g_pad][64]: a split's part of a global row's dq
+    float *part_kv;          // [B*H][n_split][g_pad][128]: a split's part of a global key's dk, dv
+    int *count_q, *count_kv; // [B*H] each
 };
 
 }  // namespace lfk
