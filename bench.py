@@ -96,50 +96,87 @@ def cpu_baseline(inp, flops, seconds):
                       f"{reps} passes in {el:.1f} s, fp64"}
 
 
-def global_rows_probe(lf, W, steps):
-    """HBM rate of the global-row work: the padded shape with r = 0 (band
-    queries read one key plus the globals) timed with its 8 globals and with
-    none; the difference is charged to the global rows, whose algorithmic
-    bytes are every valid K and V row of each (b, h) once.  An upper bound on
-    their time (the band tiles' global-key blocks fall in it too), so the
-    rate is a lower bound."""
+def global_rows_bytes(inp):
+    """Algorithmic HBM bytes of the global rows alone: every valid K and V row
+    of each (b, h) read once, plus the global rows' q read and out written."""
+    B, H, T, d = inp.q.shape
+    es = inp.q.element_size()
+    lengths = inp.lengths if inp.lengths is not None else [T] * B
+    if inp.key_padding_mask is not None and inp.lengths is None:
+        lengths = [int((inp.key_padding_mask[b] == 0).sum()) for b in range(B)]
+    n_g = len(set(inp.global_idx))
+    return sum(lengths) * H * 2 * d * es + 2 * B * H * n_g * d * es
+
+
+def bench_global_rows(args, lf, W, metrics):
+    """lf_attn_fwd_global_rows on the workload (the global rows alone, the
+    same tasks the whole forward runs for them): W warmup calls, SETTLE_MS of
+    untimed calls, then K back-to-back calls timed with events on the call
+    stream.  Bound: HBM (each global row group streams every valid K and V
+    row of its head)."""
     import torch
-    dev = torch.device("cuda:0")
-    w = W.workload("bf16-b4h16t16384-r0-g8-pad")
+    w = W.workload(args.workload)
     inp = W.make_inputs(w)
+    if not inp.global_idx:
+        raise SystemExit(f"{w.name} has no global rows")
+    dev = torch.device("cuda:0")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
-    kpm = inp.key_padding_mask.to(dev)
-    H, d = inp.q.shape[1], inp.q.shape[3]
-    kv_bytes = sum(inp.lengths) * H * 2 * d * inp.q.element_size()
-    us = {}
-    for name, G in (("with_globals", list(inp.global_idx)), ("without_globals", [])):
-        side = torch.cuda.Stream(dev)
-        with torch.cuda.stream(side):
-            call = lf.Prepared(q, k, v, inp.r, inp.dilation, G, kpm, stream=side)
-            for _ in range(5):
-                call()
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
-                for _ in range(steps):
-                    call()
+    kpm = None if inp.key_padding_mask is None else inp.key_padding_mask.to(dev)
+    B, H, T, d = q.shape
+    stream = torch.cuda.current_stream(dev)
+    out = torch.zeros_like(q)
+    G = list(inp.global_idx)
+
+    def call():
+        lf.attn_fwd_global_rows(q, k, v, G, key_padding_mask=kpm, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    n_untimed = args.warmup
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < SETTLE_MS:
+        for _ in range(20):
+            call()
         torch.cuda.synchronize()
-        best = None
-        for _ in range(3):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            t = a.elapsed_time(b) / steps * 1e3
-            best = t if best is None else min(best, t)
-        us[name] = best
-    dt = us["with_globals"] - us["without_globals"]
-    print(json.dumps({"probe": "global-row HBM rate", "workload": w.name,
-                      "us_per_call": {k_: round(v_, 3) for k_, v_ in us.items()},
-                      "global_row_us": round(dt, 3), "global_row_algorithmic_bytes": kv_bytes,
-                      "global_row_GBps_lower_bound": round(kv_bytes / (dt * 1e-6) / 1e9, 1)}), flush=True)
+        n_untimed += 20
+    if args.profile_mode:
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        from sparse_long_sequence_lf_amd.profiling import COPY_BYTES
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"profile mode: {n_untimed} untimed global-row calls then {args.steps} of {w.name}, "
+              f"one {COPY_BYTES} B copy", flush=True)
+        return
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = global_rows_bytes(inp)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name + "-globalrows")
+    line = {
+        "metric": "HBM GB/s of the global rows alone (lf_attn_fwd_global_rows)", "value": round(gbps, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v; no dataset, no weights)",
+        "config": {"workload": w.name, "pass": "global rows", "B": B, "H": H, "T": T, "d": d,
+                   "n_global": len(set(G)), "padded": kpm is not None, "algorithmic_bytes": nbytes,
+                   "timing": f"eager back-to-back calls after {n_untimed} untimed calls"},
+        "roofline": {"bound": "hbm", "kernel": "tile_kernel, global-row tasks and their combine",
+                     "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(gbps / 8000.0, 4),
+                     "traffic": traffic},
+    }
+    print(json.dumps(line), flush=True)
 
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
@@ -236,8 +273,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-mode", action="store_true")
-    ap.add_argument("--global-rows-probe", action="store_true",
-                    help="print the global-row HBM rate probe's line instead of the benchmark line")
+    ap.add_argument("--global-rows", action="store_true",
+                    help="time lf_attn_fwd_global_rows (the global rows alone) on the workload")
     ap.add_argument("--backward", action="store_true",
                     help="time lf_attn_bwd (dq, dk, dv) on the workload instead of the forward")
     args = ap.parse_args()
@@ -254,9 +291,9 @@ def main():
     from sparse_long_sequence_lf_amd import metrics
     from sparse_long_sequence_lf_amd import workloads as W
 
-    if args.global_rows_probe:
+    if args.global_rows:
         torch.cuda.set_device(0)
-        global_rows_probe(lf, W, min(args.steps, 50))
+        bench_global_rows(args, lf, W, metrics)
         return
 
     if args.backward:

@@ -97,9 +97,11 @@ typedef enum {
  * written by a kernel on `stream`, and a buffer it outgrows is replaced
  * with hipMalloc, the old one freed once the stream has passed its last
  * use.  During stream capture nothing is allocated: a call that would
- * have to grow the workspace is LF_E_UNSUPPORTED (make one call of that
- * size on the stream first).  What a captured call uses stays reserved for
- * the graph until the process exits.  A graph shares its stream's
+ * have to grow the workspace, or that needs a new plan slot after earlier
+ * captures took every free one, is LF_E_UNSUPPORTED (make one identical
+ * call on the stream outside capture first).  What a captured call uses
+ * stays reserved for the graph until the process exits; later calls get
+ * new slots and buffers instead.  A graph shares its stream's
  * workspace: do not replay it concurrently with calls on that stream or
  * with another replay of a graph captured on it (the global-row partials
  * and counters would race).
@@ -189,6 +191,30 @@ lf_status_t lf_attn_fwd_noalloc(const void *q, const void *k, const void *v,
                                 const int32_t *global_idx, int n_global,
                                 const uint8_t *key_padding_mask,
                                 void *out, lf_dtype_t dtype, void *stream);
+
+/*
+ * lf_attn_fwd_global_rows -- only the global rows of lf_attn_fwd: for every
+ * (b, h) and every i in G, out[b][h][i] (and lse[b][h][i] when lse is not
+ * NULL) as lf_attn_fwd and lf_attn_fwd_ex write them.  A global row attends
+ * to every valid key (Longformer, eightmm.github.io, "Global Attention";
+ * the N(i) = { 0 .. T-1 } case above), so no window, dilation, side or
+ * random-block argument applies.  Every other row of out and lse is left as
+ * it was.  For a caller that needs the global tokens' outputs alone, such as
+ * a classification head reading the first token of the last layer.
+ *
+ *   q, k, v, B, H, T, d, global_idx, n_global, key_padding_mask, dtype,
+ *   stream: as lf_attn_fwd.  n_global == 0 enqueues nothing.
+ *   out       DEVICE pointer [B][H][T][d] in `dtype`; only the rows at the
+ *             global positions are written.
+ *   lse       DEVICE pointer [B][H][T] of floats, or NULL: as lf_attn_fwd_ex,
+ *             at the global positions only.
+ *   Ownership, workspace and errors: as lf_attn_fwd.
+ */
+lf_status_t lf_attn_fwd_global_rows(const void *q, const void *k, const void *v,
+                                    int B, int H, int T, int d,
+                                    const int32_t *global_idx, int n_global,
+                                    const uint8_t *key_padding_mask,
+                                    void *out, float *lse, lf_dtype_t dtype, void *stream);
 
 /* Text describing the last non-OK status returned on the calling thread
  * (empty string if none).  The pointer stays valid until the next call on

@@ -54,6 +54,8 @@ def load():
     lib.lf_attn_fwd_ex.restype = I
     lib.lf_attn_fwd_noalloc.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I, P]
     lib.lf_attn_fwd_noalloc.restype = I
+    lib.lf_attn_fwd_global_rows.argtypes = [P, P, P, I, I, I, I, P, I, P, P, P, I, P]
+    lib.lf_attn_fwd_global_rows.restype = I
     lib.lf_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, P, P, I, P]
     lib.lf_attn_bwd.restype = I
     lib.lf_attn_bwd_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, P, I, P, I, P, P, I, P, P, P, P, I, P]
@@ -214,6 +216,49 @@ def attn_fwd(q, k, v, r, dilation: Optional[Sequence[int]] = None,
     st = raw_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, r, dilation,
                  gl if gl else None, len(gl), kpm_ptr, out.data_ptr(), dt, sptr, one_sided, random_blocks,
                  lse_ptr)
+    if st != LF_OK:
+        raise LfError(st, last_error())
+    return out
+
+
+def attn_fwd_global_rows(q, k, v, global_idx: Sequence[int], key_padding_mask=None, out=None, stream=None,
+                         lse=None):
+    """lf_attn_fwd_global_rows: only the rows at the positions ``global_idx``
+    of the forward's output (and of ``lse``, a float32 [B, H, T] tensor, when
+    given) are written; a global row attends to every valid key, so no
+    window argument applies.  Every other row of ``out`` keeps its value."""
+    import torch
+
+    if q.dtype == torch.bfloat16:
+        dt = LF_BF16
+    elif q.dtype == torch.float32:
+        dt = LF_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype or t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{name} must match q in dtype, shape and device")
+    if q.dim() != 4 or not (q.is_cuda and q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous device tensors [B, H, T, d]")
+    B, H, T, d = q.shape
+    if out is None:
+        out = torch.zeros_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    lse_ptr = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous() or \
+                lse.device != q.device:
+            raise ValueError("lse must be a contiguous float32 device tensor [B, H, T]")
+        lse_ptr = lse.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    kpm_ptr, _kpm = _padding_arg(key_padding_mask, B, T, stream)
+    gl = [int(x) for x in global_idx]
+    g = (ctypes.c_int32 * max(1, len(gl)))(*gl)
+    st = load().lf_attn_fwd_global_rows(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, T, d, g, len(gl), kpm_ptr,
+                                        out.data_ptr(), lse_ptr, dt, sptr)
     if st != LF_OK:
         raise LfError(st, last_error())
     return out

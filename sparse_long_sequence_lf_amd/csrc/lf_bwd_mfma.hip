@@ -58,17 +58,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int ROWB = 2 * D;              // bytes of a bf16 row
 constexpr int GT = LF_MAX_GLOBALS;
 
-// LDS forms of a block of 32 rows x 64 channels (4 KiB each), each 1 KiB
-// piece written by one buffer_load_dwordx4 ... lds of a wave:
-//   row form  byte ks*1024 + row*32 + hs*16: channels 16ks + 8h .. +7,
-//             hs = h ^ ((row >> 3) & 1); read as the MFMA operand of one
-//             row per lane (lane p of piece ks loads row p/2)
-//   tr form   byte cb*2048 + row*64 + 16j: channels 32cb + 8j .. +7; read
-//             with ds_read_b64_tr_b16 (lane p of piece (cb, half) loads row
-//             16 half + p/4, channels 32cb + 8(p & 3) ..)
-// The tr form feeds the products whose contraction runs over the block's
-// rows (dQ^T = K^T dS^T; dV^T = dY^T P, dK^T = Q^T dS), in the row order in
-// which a 32x32 accumulator packs into the other operand.
+// LDS form of a block of 32 rows x 64 channels (4 KiB): channel
+// 32cb + 8j + e of row `row` at byte
+//     cb*2048 + row*64 + 16*(j ^ ((row >> 2) & 3)) + 2e.
+// One form serves both reads without bank conflicts: the row operand
+// (ds_read_b128; lane l takes row l%32, channels 16ks + 8(l/32) .. +7) and
+// the transposed operand of the products whose contraction runs over the
+// block's rows (dQ^T = K^T dS^T; dV^T = dY^T P, dK^T = Q^T dS), read with
+// ds_read_b64_tr_b16 in the row order in which a 32x32 accumulator packs
+// into the other operand.  Each 1 KiB piece (cb, half: rows 16half ..
+// +15) is written by one buffer_load_dwordx4 ... lds of a wave: lane p
+// brings row 16half + p/4, channels 32cb + 8((p & 3) ^ ((p >> 4) & 3)) ..
+// +7.
 
 struct Tile {
     int kind;            // 0: band tile; 1: the global rows (dq) or global keys (dk, dv) of one split
@@ -112,19 +113,13 @@ __device__ __forceinline__ Tile decode_tile(const Plan& P, int t) {
     return k;
 }
 
-// Each of the 8 dies (blockIdx % 8) takes an eighth of the global tasks
-// first (they are short and end with a combine), then a contiguous eighth
-// of the band tiles, so that neighbouring tiles, which read the same rows,
-// share its L2; -1 for a slot past the end.
+// Each of the 8 dies (blockIdx % 8) takes its band tiles (a contiguous
+// eighth, or the run the plan cut by cost, so that neighbouring tiles, which
+// read the same rows, share its L2) and its global tasks: after the tiles,
+// where the short global tasks fill the tail of the tiles' last round, or
+// before them when they are the longer kind; -1 for a slot past the end.
 __device__ __forceinline__ int tile_of_block(const Plan& P) {
-    const int xcd = blockIdx.x & 7;
-    int slot = blockIdx.x >> 3;
-    const int nb = P.n_band_tasks, ng = P.n_tasks - P.n_band_tasks;
-    const int ng_x = (ng >> 3) + (xcd < (ng & 7)), ng_o = xcd * (ng >> 3) + min(xcd, ng & 7);
-    if (slot < ng_x) return nb + ng_o + slot;
-    slot -= ng_x;
-    const int nb_x = (nb >> 3) + (xcd < (nb & 7)), nb_o = xcd * (nb >> 3) + min(xcd, nb & 7);
-    return slot < nb_x ? nb_o + slot : -1;
+    return task_of_slot(P, blockIdx.x & 7, blockIdx.x >> 3, P.bwd_globals_first != 0);
 }
 
 // The last of the n_split * n_ggroups workgroups of head (b, h) to finish
@@ -203,21 +198,52 @@ __device__ __forceinline__ void load_operand(__amdgpu_buffer_rsrc_t rs, int pos,
         x[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 2u * (16 * ks + 8 * lg), 0, 0));
 }
 
-// row-form fragment: lane l supplies row l%32, channels 16ks + 8(l/32) .. +7
-__device__ __forceinline__ void read_rows(const char* p, bf16x8 (&x)[4]) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) x[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p + 1024 * ks));
+// Per-lane byte offsets of the two reads of a block (see the form above).
+struct FormLane {
+    int r0, r1;   // row operand: row l%32, channel groups 2(ks&1) + l/32 (ks even, odd)
+    int t0, t1;   // transposed operand: rows 4(l/32) + (l&15)/4 and 8 more
+    __device__ __forceinline__ FormLane(int lane) {
+        const int lq = lane & 31, lg = lane >> 5, sw = (lq >> 2) & 3;
+        r0 = lq * 64 + 16 * (lg ^ sw);
+        r1 = lq * 64 + 16 * (lg ^ sw ^ 2);
+        const int row = 4 * lg + ((lane & 15) >> 2), j = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        t0 = row * 64 + 16 * (j ^ lg) + 8 * (lane & 1);
+        t1 = (row + 8) * 64 + 16 * (j ^ lg ^ 2) + 8 * (lane & 1);
+    }
+};
+
+// row operand: lane l supplies row l%32, channels 16ks + 8(l/32) .. +7
+__device__ __forceinline__ void read_rows(const char* blk, const FormLane& f, bf16x8 (&x)[4]) {
+    x[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(blk + f.r0));
+    x[1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(blk + f.r1));
+    x[2] = __builtin_bit_cast(bf16x8, *(const u32x4*)(blk + 2048 + f.r0));
+    x[3] = __builtin_bit_cast(bf16x8, *(const u32x4*)(blk + 2048 + f.r1));
 }
 
-// tr-form fragment [st][cb] (p: the form's base plus the lane's part)
-__device__ __forceinline__ void read_tr(const char* p, bf16x8 (&x)[2][2]) {
+// transposed operand [st][cb]: rows 16st .. +15, channels 32cb .. +31
+__device__ __forceinline__ void read_tr(const char* blk, const FormLane& f, bf16x8 (&x)[2][2]) {
 #pragma unroll
     for (int st = 0; st < 2; st++)
 #pragma unroll
         for (int cb = 0; cb < 2; cb++) {
-            const char* a = p + cb * 2048 + 16 * st * 64;
-            x[st][cb] = cat_tr(ds_tr16(a), ds_tr16(a + 8 * 64));
+            const char* a = blk + cb * 2048 + st * 1024;
+            x[st][cb] = cat_tr(ds_tr16(a + f.t0), ds_tr16(a + f.t1));
         }
+}
+
+// the four pieces of a block into LDS at dst: o0, o1 the lane's row
+// offsets for rows p/4 and 16 + p/4 (with the channel group of the form)
+__device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t o0, uint32_t o1) {
+#pragma unroll
+    for (int x = 0; x < 4; x++) load_lds16(rs, dst + (x >> 1) * 2048 + (x & 1) * 1024, (x & 1) ? o1 : o0, 64 * (x >> 1));
+}
+
+// zeros over this lane's part of a block where its rows are padded
+__device__ __forceinline__ void zero_block_rows(char* dst, int lane, bool pad0, bool pad1) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int x = 0; x < 4; x++)
+        if ((x & 1) ? pad1 : pad0) *(u32x4*)(dst + (x >> 1) * 2048 + (x & 1) * 1024 + 16 * lane) = z;
 }
 
 // accumulator elements 8st .. 8st+7 -> bf16 operand st
@@ -315,14 +341,13 @@ struct Blocks {
 };
 
 // ---------------------------------------------------------------------------
-// dq.  Per block in LDS: K row form at 0, V row form at 4096, K tr form at
-// 8192.  Waves (qb, ph): qb = query block of the tile, ph = key phase.  A
-// wave of query block 0 loads K row form and V row form pieces 0-1 of its
-// phase's block, one of query block 1 V row pieces 2-3 and K tr form.
+// dq.  Per block in LDS: K at 0, V at 4096, both in the form above.
+// Waves (qb, ph): qb = query block of the tile, ph = key phase.  A wave of
+// query block 0 loads K of its phase's block, one of query block 1 V.
 
 template <bool PAD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void dq_kernel(const BwdBandArgs A) {
-    constexpr int BLK = 12288, STAGE = 2 * BLK, RING = 2 * STAGE;
+    constexpr int BLK = 8192, STAGE = 2 * BLK, RING = 2 * STAGE;
     __shared__ __attribute__((aligned(16))) char smem[RING];
     __shared__ __attribute__((aligned(16))) int gld[GT];
     __shared__ __attribute__((aligned(16))) int gcls[GT];
@@ -388,11 +413,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 
     // ---- loads
     const bool w0 = qb == 0;
-    const int rowR = lane >> 1, rowT0 = lane >> 2, rowT1 = 16 + (lane >> 2);
-    const uint32_t colR = 16u * ((lane & 1) ^ ((rowR >> 3) & 1)), colT = 16u * (lane & 3);
-    const uint32_t voR = (uint32_t)min((long long)tk.delta * rowR, (long long)T) * ROWB + colR;
-    const uint32_t voT0 = (uint32_t)min((long long)tk.delta * rowT0, (long long)T) * ROWB + colT;
-    const uint32_t voT1 = (uint32_t)min((long long)tk.delta * rowT1, (long long)T) * ROWB + colT;
+    const int row0 = lane >> 2, row1 = 16 + (lane >> 2);
+    const uint32_t colU = 16u * ((lane & 3) ^ ((lane >> 4) & 3));
+    const uint32_t vo0 = (uint32_t)min((long long)tk.delta * row0, (long long)T) * ROWB + colU;
+    const uint32_t vo1 = (uint32_t)min((long long)tk.delta * row1, (long long)T) * ROWB + colU;
     const char* khead = (const char*)A.k + head * ROWB;
     const char* vhead = (const char*)A.v + head * ROWB;
     auto row0_of = [&](int j) -> int { return tk.c + tk.delta * (bl.kb_lo + j) * KBLK; };
@@ -400,46 +424,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         return buffer_rsrc(base + (uint64_t)p0 * ROWB, p0 < T ? (uint32_t)(T - p0) * ROWB : 0u);
     };
     // block jb into the ring slot at off.  pm: padded rows of the block,
-    // whose V rows and K tr-form rows load as zeros (NaN or Inf stored at a
-    // padded key must not reach a product); global slots load through gld.
+    // which load as zeros (NaN or Inf stored at a padded key must not reach
+    // a product); global slots load through gld.
     auto issue = [&](int s, int off, uint32_t pm) {
         const int jb = 2 * s + ph;
         const int kd = bl.kind(jb);
         if (kd == kNone) return;
-        char* dst = smem + off + ph * BLK;
-        __amdgpu_buffer_rsrc_t rk, rv;
-        uint32_t oR, oT0, oT1;
+        char* dst = smem + off + ph * BLK + (w0 ? 0 : 4096);
+        __amdgpu_buffer_rsrc_t rs;
+        uint32_t o0, o1;
         if (kd == kGlob) {
             const int sl0 = (jb - bl.nb) * KBLK;
-            rk = buffer_rsrc(khead, (uint32_t)T * ROWB);
-            rv = buffer_rsrc(vhead, (uint32_t)T * ROWB);
-            oR = (uint32_t)gld[sl0 + rowR] * ROWB + colR;
-            oT0 = (uint32_t)gld[sl0 + rowT0] * ROWB + colT;
-            oT1 = (uint32_t)gld[sl0 + rowT1] * ROWB + colT;
+            rs = buffer_rsrc(w0 ? khead : vhead, (uint32_t)T * ROWB);
+            o0 = (uint32_t)gld[sl0 + row0] * ROWB + colU;
+            o1 = (uint32_t)gld[sl0 + row1] * ROWB + colU;
         } else {
-            // p0 is the same in every lane; said so, the descriptors stay scalar
+            // p0 is the same in every lane; said so, the descriptor stays scalar
             const int p0 = uniform(kd == kBand ? row0_of(jb) : rand_p0(jb - bl.nb - bl.ngb));
-            rk = win(khead, p0);
-            rv = win(vhead, p0);
-            oR = voR;
-            oT0 = voT0;
-            oT1 = voT1;
+            rs = win(w0 ? khead : vhead, p0);
+            o0 = vo0;
+            o1 = vo1;
         }
-        const uint32_t oRz = PAD && ((pm >> rowR) & 1u) ? kPastEnd : oR;
-        if (w0) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) load_lds16(rk, dst + 1024 * ks, oR, 32 * ks);
-#pragma unroll
-            for (int ks = 0; ks < 2; ks++) load_lds16(rv, dst + 4096 + 1024 * ks, oRz, 32 * ks);
-        } else {
-#pragma unroll
-            for (int ks = 2; ks < 4; ks++) load_lds16(rv, dst + 4096 + 1024 * ks, oRz, 32 * ks);
-            const uint32_t a = PAD && ((pm >> rowT0) & 1u) ? kPastEnd : oT0;
-            const uint32_t b = PAD && ((pm >> rowT1) & 1u) ? kPastEnd : oT1;
-#pragma unroll
-            for (int x = 0; x < 4; x++)
-                load_lds16(rk, dst + 8192 + (x >> 1) * 2048 + (x & 1) * 1024, (x & 1) ? b : a, 64 * (x >> 1));
-        }
+        if (PAD && ((pm >> row0) & 1u)) o0 = kPastEnd;
+        if (PAD && ((pm >> row1) & 1u)) o1 = kPastEnd;
+        load_block(rs, dst, o0, o1);
     };
     // padding: lane l < 32 reads the byte of row l of this phase's block two
     // stages ahead; a ballot one stage ahead makes the block's padded-row word
@@ -464,9 +472,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     load_operand(ro, my_pos, lg, oh);
     const float lse_nat = my_pos >= 0 ? A.lse[head + my_pos] : kNegInf;
     f32x16 acc[2] = {(f32x16){}, (f32x16){}};
-    const int kbase = ph * BLK + lq * 32 + ((lg ^ ((lq >> 3) & 1)) << 4);
-    const int tbase = ph * BLK + 8192 + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) +
-                      8 * (lane & 3);
+    const FormLane fl(lane);
 
     uint32_t pm_cur = 0u, pbyte = 0u;
     if constexpr (PAD) {
@@ -499,25 +505,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         pm_cur = pad_word(pm_cur);
         // stage 0 went out before its padding word was known: clear what this
         // wave brought for padded rows
-        if (pm_cur != 0u) {
-            char* dst = smem + ph * BLK + 16 * lane;
-            const bool pR = (pm_cur >> rowR) & 1u, pT0 = (pm_cur >> rowT0) & 1u, pT1 = (pm_cur >> rowT1) & 1u;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            if (w0) {
-                if (pR) {
-                    *(u32x4*)(dst + 4096) = z;
-                    *(u32x4*)(dst + 5120) = z;
-                }
-            } else {
-                if (pR) {
-                    *(u32x4*)(dst + 6144) = z;
-                    *(u32x4*)(dst + 7168) = z;
-                }
-#pragma unroll
-                for (int x = 0; x < 4; x++)
-                    if ((x & 1) ? pT1 : pT0) *(u32x4*)(dst + 8192 + (x >> 1) * 2048 + (x & 1) * 1024) = z;
-            }
-        }
+        if (pm_cur != 0u)
+            zero_block_rows(smem + ph * BLK + (w0 ? 0 : 4096), lane, (pm_cur >> row0) & 1u, (pm_cur >> row1) & 1u);
         __syncthreads();
     }
 
@@ -529,8 +518,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         const bool rel = kd == kBand ? (j >= j_lo && j <= j_hi) : (kd != kNone && wave_active);
         bf16x8 kf[4], vf[4];
         if (rel) {
-            read_rows(smem + oc + kbase, kf);
-            read_rows(smem + oc + 4096 + kbase, vf);
+            read_rows(smem + oc + ph * BLK, fl, kf);
+            read_rows(smem + oc + ph * BLK + 4096, fl, vf);
         }
         uint32_t pm_next = 0u;
         if constexpr (PAD) {
@@ -544,9 +533,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             for (int ks = 0; ks < 4; ks++) sc = mfma(kf[ks], qh[ks], sc);
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) dp = mfma(vf[ks], yh[ks], dp);
-            // K^T operands, read while the products run
-            bf16x8 tf[2][2];
-            read_tr(smem + oc + tbase, tf);
             if (kd == kBand) {
                 if (!(j >= ji_lo && j <= ji_hi && (!PAD || pm_cur == 0u))) {
                     if (!glob_task) mask_window(sc, m_me - r - (bl.kb_lo + j) * KBLK - 4 * lg, r + ra);
@@ -575,6 +561,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             }
             bf16x8 dso[2];
             pack_operand(ds, dso);
+            // K^T operands, read only now: the scheduling barrier keeps the
+            // compiler from hoisting the reads above the products, where
+            // their registers overflow the budget of three workgroups per
+            // CU and spill
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 tf[2][2];
+            read_tr(smem + oc + ph * BLK, fl, tf);
 #pragma unroll
             for (int st2 = 0; st2 < 2; st2++)
 #pragma unroll
@@ -630,15 +623,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv.  Per block in LDS: Q row form at 0, dY row form at 4096, Q tr form
-// at 8192, dY tr form at 12288, then the block's 32 values lse log2 e and
-// 32 values D at 16384.  Waves (kb, ph): kb = key block of the tile, ph =
-// query phase.  A wave of key block 0 loads the row forms of its phase's
-// block, one of key block 1 the tr forms and the statistics.
+// dk, dv.  Per block in LDS: Q at 0, dY at 4096 (both in the form above),
+// then the block's 32 values lse log2 e and 32 values D at 8192.  Waves
+// (kb, ph): kb = key block of the tile, ph = query phase.  A wave of key
+// block 0 loads Q of its phase's block, one of key block 1 dY and the
+// statistics.
 
 template <bool PAD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dkdv_kernel(const BwdBandArgs A) {
-    constexpr int BLK = 16384 + 256, STAGE = 2 * BLK, RING = 2 * STAGE;
+    constexpr int BLK = 8192 + 256, STAGE = 2 * BLK, RING = 2 * STAGE;
     __shared__ __attribute__((aligned(16))) char smem[RING];
     __shared__ __attribute__((aligned(16))) int gld[GT];
     __shared__ __attribute__((aligned(16))) int gcls[GT];
@@ -708,11 +701,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 
     // ---- loads
     const bool w0 = kb == 0;
-    const int rowR = lane >> 1, rowT0 = lane >> 2, rowT1 = 16 + (lane >> 2);
-    const uint32_t colR = 16u * ((lane & 1) ^ ((rowR >> 3) & 1)), colT = 16u * (lane & 3);
-    const uint32_t voR = (uint32_t)min((long long)tk.delta * rowR, (long long)T) * ROWB + colR;
-    const uint32_t voT0 = (uint32_t)min((long long)tk.delta * rowT0, (long long)T) * ROWB + colT;
-    const uint32_t voT1 = (uint32_t)min((long long)tk.delta * rowT1, (long long)T) * ROWB + colT;
+    const int row0 = lane >> 2, row1 = 16 + (lane >> 2);
+    const uint32_t colU = 16u * ((lane & 3) ^ ((lane >> 4) & 3));
+    const uint32_t vo0 = (uint32_t)min((long long)tk.delta * row0, (long long)T) * ROWB + colU;
+    const uint32_t vo1 = (uint32_t)min((long long)tk.delta * row1, (long long)T) * ROWB + colU;
     // statistics: lane l < 32 brings the lse of row l, lane l >= 32 the D of row l - 32
     const uint32_t voS = (uint32_t)min((long long)tk.delta * lq, (long long)T) * 8u + 4u * lg;
     const char* qhead = (const char*)A.q + head * ROWB;
@@ -723,50 +715,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         return buffer_rsrc(base + (uint64_t)p0 * rb, p0 < T ? (uint32_t)(T - p0) * rb : 0u);
     };
     // block jb into the ring slot at off; pm: padded query rows, loaded as
-    // zeros in every form (their statistics give them zero weight)
+    // zeros (their statistics give them zero weight)
     auto issue = [&](int s, int off, uint32_t pm) {
         const int jb = 2 * s + ph;
         const int kd = bl.kind(jb);
         if (kd == kNone) return;
         char* dst = smem + off + ph * BLK;
-        __amdgpu_buffer_rsrc_t rq, ry, rs;
-        uint32_t oR, oT0, oT1, oS;
+        __amdgpu_buffer_rsrc_t rs, rst;
+        uint32_t o0, o1, oS;
         if (kd == kGlob) {
             const int sl0 = (jb - bl.nb) * KBLK;
-            rq = buffer_rsrc(qhead, (uint32_t)T * ROWB);
-            ry = buffer_rsrc(yhead, (uint32_t)T * ROWB);
-            rs = buffer_rsrc(shead, (uint32_t)T * 8u);
-            oR = (uint32_t)gld[sl0 + rowR] * ROWB + colR;
-            oT0 = (uint32_t)gld[sl0 + rowT0] * ROWB + colT;
-            oT1 = (uint32_t)gld[sl0 + rowT1] * ROWB + colT;
+            rs = buffer_rsrc(w0 ? qhead : yhead, (uint32_t)T * ROWB);
+            rst = buffer_rsrc(shead, (uint32_t)T * 8u);
+            o0 = (uint32_t)gld[sl0 + row0] * ROWB + colU;
+            o1 = (uint32_t)gld[sl0 + row1] * ROWB + colU;
             oS = (uint32_t)gld[sl0 + lq] * 8u + 4u * lg;
         } else {
             const int p0 = uniform(kd == kBand ? row0_of(jb) : rand_p0(jb - bl.nb - bl.ngb));
-            rq = win(qhead, p0, ROWB);
-            ry = win(yhead, p0, ROWB);
-            rs = win(shead, p0, 8);
-            oR = voR;
-            oT0 = voT0;
-            oT1 = voT1;
+            rs = win(w0 ? qhead : yhead, p0, ROWB);
+            rst = win(shead, p0, 8);
+            o0 = vo0;
+            o1 = vo1;
             oS = voS;
         }
-        if (w0) {
-            const uint32_t o = PAD && ((pm >> rowR) & 1u) ? kPastEnd : oR;
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) load_lds16(rq, dst + 1024 * ks, o, 32 * ks);
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) load_lds16(ry, dst + 4096 + 1024 * ks, o, 32 * ks);
-        } else {
-            const uint32_t a = PAD && ((pm >> rowT0) & 1u) ? kPastEnd : oT0;
-            const uint32_t b = PAD && ((pm >> rowT1) & 1u) ? kPastEnd : oT1;
-#pragma unroll
-            for (int x = 0; x < 4; x++) {
-                const uint32_t o = (x & 1) ? b : a;
-                load_lds16(rq, dst + 8192 + (x >> 1) * 2048 + (x & 1) * 1024, o, 64 * (x >> 1));
-                load_lds16(ry, dst + 12288 + (x >> 1) * 2048 + (x & 1) * 1024, o, 64 * (x >> 1));
-            }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(dst + 16384), 4, oS, 0, 0, 0);
-        }
+        if (PAD && ((pm >> row0) & 1u)) o0 = kPastEnd;
+        if (PAD && ((pm >> row1) & 1u)) o1 = kPastEnd;
+        load_block(rs, dst + (w0 ? 0 : 4096), o0, o1);
+        if (!w0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rst, LDS_PTR(dst + 8192), 4, oS, 0, 0, 0);
     };
     const __amdgpu_buffer_rsrc_t rpad = buffer_rsrc(padrow, PAD ? (uint32_t)T : 0u);
     auto pad_at = [&](int s) -> uint32_t {
@@ -785,10 +760,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     load_operand(rk, my_pos, lg, kh);
     load_operand(rv, my_pos, lg, vh);
     f32x16 ak[2] = {(f32x16){}, (f32x16){}}, av[2] = {(f32x16){}, (f32x16){}};
-    const int rbase = ph * BLK + lq * 32 + ((lg ^ ((lq >> 3) & 1)) << 4);
-    const int tbase = ph * BLK + 8192 + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) +
-                      8 * (lane & 3);
-    const int sbase = ph * BLK + 16384 + 16 * lg;   // lse of this lane's rows 8q4 + 4lg .. +3 at +32 q4
+    const FormLane fl(lane);
+    const int sbase = ph * BLK + 8192 + 16 * lg;   // lse of this lane's rows 8q4 + 4lg .. +3 at +32 q4
 
     uint32_t pm_cur = 0u, pbyte = 0u;
     if constexpr (PAD) {
@@ -805,24 +778,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     barrier_lds_loads();
     if constexpr (PAD) {
         pm_cur = pad_word(pm_cur);
-        if (pm_cur != 0u) {
-            char* dst = smem + ph * BLK + 16 * lane;
-            const bool pR = (pm_cur >> rowR) & 1u, pT0 = (pm_cur >> rowT0) & 1u, pT1 = (pm_cur >> rowT1) & 1u;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            if (w0) {
-                if (pR) {
-#pragma unroll
-                    for (int ks = 0; ks < 8; ks++) *(u32x4*)(dst + 1024 * ks) = z;
-                }
-            } else {
-#pragma unroll
-                for (int x = 0; x < 4; x++)
-                    if ((x & 1) ? pT1 : pT0) {
-                        *(u32x4*)(dst + 8192 + (x >> 1) * 2048 + (x & 1) * 1024) = z;
-                        *(u32x4*)(dst + 12288 + (x >> 1) * 2048 + (x & 1) * 1024) = z;
-                    }
-            }
-        }
+        if (pm_cur != 0u)
+            zero_block_rows(smem + ph * BLK + (w0 ? 0 : 4096), lane, (pm_cur >> row0) & 1u, (pm_cur >> row1) & 1u);
         __syncthreads();
     }
 
@@ -834,8 +791,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         const bool rel = kd == kBand ? (j >= j_lo && j <= j_hi) : (kd != kNone && wave_active);
         bf16x8 qf[4], yf[4];
         if (rel) {
-            read_rows(smem + oc + rbase, qf);
-            read_rows(smem + oc + 4096 + rbase, yf);
+            read_rows(smem + oc + ph * BLK, fl, qf);
+            read_rows(smem + oc + ph * BLK + 4096, fl, yf);
         }
         uint32_t pm_next = 0u;
         if constexpr (PAD) {
@@ -849,16 +806,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             for (int ks = 0; ks < 4; ks++) sc = mfma(qf[ks], kh[ks], sc);
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) dp = mfma(yf[ks], vh[ks], dp);
-            // statistics and the transposed operands, read while the products run
+            // the statistics, read while the products run
             f32x4 l4[4], d4[4];
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++) {
                 l4[q4] = *(const f32x4*)(smem + oc + sbase + 32 * q4);
                 d4[q4] = *(const f32x4*)(smem + oc + sbase + 128 + 32 * q4);
             }
-            bf16x8 qt[2][2], yt[2][2];
-            read_tr(smem + oc + tbase, qt);
-            read_tr(smem + oc + 4096 + tbase, yt);
             // element i: query row 8(i>>2) + 4lg + (i&3) of the block, this lane's key
             if (kd == kBand) {
                 if (!(j >= ji_lo && j <= ji_hi)) {
@@ -886,6 +840,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             bf16x8 po[2], dso[2];
             pack_operand(p, po);
             pack_operand(ds, dso);
+            // Q^T and dY^T operands, read only now (as in the dq kernel: read
+            // beside the products they made the kernel spill)
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 qt[2][2], yt[2][2];
+            read_tr(smem + oc + ph * BLK, fl, qt);
+            read_tr(smem + oc + ph * BLK + 4096, fl, yt);
 #pragma unroll
             for (int st2 = 0; st2 < 2; st2++)
 #pragma unroll
@@ -952,8 +912,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 // grid of the band kernels: the slots of the 8 dies, each holding an eighth
 // of the global tasks and of the band tiles
 extern "C" int lfk_bwd_band_grid(const lfk::Plan* P) {
-    const int nb = P->n_band_tasks, ng = P->n_tasks - P->n_band_tasks;
-    return 8 * ((nb + 7) / 8 + (ng + 7) / 8);
+    return 8 * lfk::slots_per_die(*P);
 }
 
 // A: argument of the band kernels (A->plan: device copy of *P).  The dq

@@ -74,6 +74,92 @@ inline long long fill_band_plan(Plan& P, int B, int H, int T, const int32_t* dil
     return start;
 }
 
+// Heads with unequal radii make band tiles of unequal cost.  The band tasks
+// (batch-major, then head, then class and tile) are cut into 8 contiguous
+// runs of about equal cost, one per die: each die still streams neighbouring
+// tiles (which share keys in its L2), and no die is left with the expensive
+// heads alone.  A tile's cost is its key steps plus a fixed part (set-up,
+// Q loads, output stores) worth about 14 steps of 32 keys.  The global-row
+// tasks of a head go to the die that holds the middle of its band tiles, so
+// that the keys they stream are the ones that die's L2 already holds.
+inline void split_by_cost(Plan& P) {
+    for (int x = 0; x < 9; x++) P.band_die[x] = P.glob_die[x] = 0;
+    const long long n_band = P.n_band_tasks;
+    bool equal = true;
+    for (int h = 1; h < P.H; h++) equal &= P.rad[h] == P.rad[0];
+    if (equal || n_band == 0) return;
+    double head_cost[LF_MAX_HEADS];
+    for (int h = 0; h < P.H; h++) {
+        const double keys = (P.one_sided ? P.rad[h] : 2.0 * P.rad[h]) + LFK_BM;
+        head_cost[h] = 14.0 + keys / 32.0;
+    }
+    double total = 0;
+    for (int h = 0; h < P.H; h++) total += head_cost[h] * (P.head_start[h + 1] - P.head_start[h]);
+    total *= P.B;
+    const long long tpb = P.band_tasks_per_batch;
+    double acc = 0;
+    int die = 1;
+    for (int b = 0; b < P.B && die < 8; b++)
+        for (int h = 0; h < P.H && die < 8; h++)
+            for (long long t = b * tpb + P.head_start[h]; t < b * tpb + P.head_start[h + 1]; t++) {
+                // task t opens die `die` once the tasks before it hold that die's share
+                while (die < 8 && acc >= total * die / 8.0) P.band_die[die++] = (int)t;
+                acc += head_cost[h];
+            }
+    while (die < 8) P.band_die[die++] = (int)n_band;
+    P.band_die[8] = (int)n_band;
+    // global-row tasks: (b, h)-major, n_split * n_ggroups per head
+    const long long per_bh = (long long)P.n_split * P.n_ggroups;
+    int x = 0;
+    for (int bh = 0; bh < P.B * P.H && P.n_tasks > P.n_band_tasks; bh++) {
+        const long long mid = (long long)(bh / P.H) * tpb + (P.head_start[bh % P.H] + P.head_start[bh % P.H + 1]) / 2;
+        while (x < 7 && mid >= P.band_die[x + 1]) P.glob_die[++x] = (int)(bh * per_bh);
+    }
+    while (x < 7) P.glob_die[++x] = P.n_tasks - P.n_band_tasks;
+    P.glob_die[8] = P.n_tasks - P.n_band_tasks;
+}
+
+// Workgroup slots per die: its global-row tasks, then its band tasks (an
+// eighth of each, or the runs the plan cut by cost).
+inline int slots_per_die(const Plan& P) {
+    const int nb = P.n_band_tasks, ng = P.n_tasks - P.n_band_tasks;
+    if (P.band_die[8] == 0) return (nb + 7) / 8 + (ng + 7) / 8;
+    int m = 0;
+    for (int x = 0; x < 8; x++) {
+        const int n = P.band_die[x + 1] - P.band_die[x] + P.glob_die[x + 1] - P.glob_die[x];
+        m = m > n ? m : n;
+    }
+    return m;
+}
+
+// The task of workgroup slot `slot` of die `xcd`, -1 past the die's tasks.
+// globals_first: the die's global-row tasks take its first slots (they are
+// short and end with a combine), else its last (they fill the tail of the
+// band tiles' last round).
+LF_HD int task_of_slot(const Plan& P, int xcd, int slot, bool globals_first) {
+    const int nb = P.n_band_tasks, ng = P.n_tasks - P.n_band_tasks;
+    int g_o, g_n, b_o, b_n;
+    if (P.band_die[8] > 0) {
+        g_o = P.glob_die[xcd];
+        g_n = P.glob_die[xcd + 1] - g_o;
+        b_o = P.band_die[xcd];
+        b_n = P.band_die[xcd + 1] - b_o;
+    } else {
+        g_n = (ng >> 3) + (xcd < (ng & 7));
+        g_o = xcd * (ng >> 3) + (xcd < (ng & 7) ? xcd : (ng & 7));
+        b_n = (nb >> 3) + (xcd < (nb & 7));
+        b_o = xcd * (nb >> 3) + (xcd < (nb & 7) ? xcd : (nb & 7));
+    }
+    if (globals_first) {
+        if (slot < g_n) return nb + g_o + slot;
+        slot -= g_n;
+        return slot < b_n ? b_o + slot : -1;
+    }
+    if (slot < b_n) return b_o + slot;
+    slot -= b_n;
+    return slot < g_n ? nb + g_o + slot : -1;
+}
+
 // Band task t of the plan -> (b, h, residue class c, class length n, tile).
 // Tasks run batch-major, then head, then class, then tile; classes
 // 0 .. hrem-1 of a head hold hq + 1 positions (htb tiles each), the others

@@ -509,28 +509,27 @@ void tile_kernel(const Args A) {
 
     // ---- which task.  Each of the 8 dies (blockIdx % 8) takes an eighth of
     // the global-row tasks first, then a contiguous eighth of the band tasks
-    // (neighbouring tiles share keys in its L2).
+    // (neighbouring tiles share keys in its L2), or the runs the plan cut by
+    // cost when the heads' tiles differ in cost.
     const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
     const bool fast = A.fd.on != 0;
     int task_id;
-    {
+    if (A.global_rows_only) {
+        // an eighth of the global-row tasks per die, nothing else
         const int nb = fast ? A.fd.n_band : P.n_band_tasks, ng = (fast ? A.fd.n_tasks : P.n_tasks) - nb;
+        const int ng_x = (ng >> 3) + (xcd < (ng & 7)), ng_o = xcd * (ng >> 3) + min(xcd, ng & 7);
+        if (slot_in_xcd >= ng_x) return;
+        task_id = nb + ng_o + slot_in_xcd;
+    } else if (fast) {
+        const int nb = A.fd.n_band, ng = A.fd.n_tasks - nb;
         const int nb_x = (nb >> 3) + (xcd < (nb & 7)), nb_o = xcd * (nb >> 3) + min(xcd, nb & 7);
         const int ng_x = (ng >> 3) + (xcd < (ng & 7)), ng_o = xcd * (ng >> 3) + min(xcd, ng & 7);
-        if (slot_in_xcd < ng_x) {
-            task_id = nb + ng_o + slot_in_xcd;
-        } else if (!fast && P.band_chunk > 0) {
-            // tiles of unequal cost (one radius per head): runs of C tiles go
-            // to the dies in turn, so that every die gets a share of each head
-            const int C = P.band_chunk, sb = slot_in_xcd - ng_x;
-            const int t = ((sb / C) * 8 + xcd) * C + sb % C;
-            if (t >= nb) return;
-            task_id = t;
-        } else if (slot_in_xcd - ng_x < nb_x) {
-            task_id = nb_o + (slot_in_xcd - ng_x);
-        } else {
-            return;
-        }
+        if (slot_in_xcd < ng_x) task_id = nb + ng_o + slot_in_xcd;
+        else if (slot_in_xcd - ng_x < nb_x) task_id = nb_o + (slot_in_xcd - ng_x);
+        else return;
+    } else {
+        task_id = task_of_slot(P, xcd, slot_in_xcd, true);
+        if (task_id < 0) return;
     }
     const Task tk = fast ? decode_task_fast(A.fd, task_id) : decode_task(P, task_id);
     const int T = fast ? A.fd.T : P.T;
@@ -1262,10 +1261,7 @@ extern "C" hipError_t lfk_write_plan(const void* plan, size_t bytes, void* dst, 
 // grid: the task slots of the 8 dies, each die holding ceil(n/8) band and
 // ceil(n/8) global-row slots
 extern "C" int lfk_grid(const lfk::Plan* P) {
-    const int nb = P->n_band_tasks, ng = P->n_tasks - P->n_band_tasks;
-    const int C = P->band_chunk;
-    const int band_slots = C > 0 ? ((nb + C - 1) / C + 7) / 8 * C : (nb + 7) / 8;
-    return 8 * (band_slots + (ng + 7) / 8);
+    return 8 * lfk::slots_per_die(*P);
 }
 
 // A: kernel argument (A->plan is the device copy of *P); P: host copy of the plan.
@@ -1273,7 +1269,7 @@ extern "C" int lfk_grid(const lfk::Plan* P) {
 // blocks (each present or not at compile time).
 template <int D, typename ET, typename OT>
 static void launch_tiles(const lfk::Args* A, const lfk::Plan* P, hipStream_t s) {
-    const int grid = lfk_grid(P);
+    const int grid = A->global_rows_only ? 8 * ((P->n_tasks - P->n_band_tasks + 7) / 8) : lfk_grid(P);
     const bool pad = A->pad != nullptr, rnd = P->n_rand > 0;
     const dim3 g(grid), b(256);
     if (pad && rnd) hipLaunchKernelGGL((lfk::tile_kernel<D, ET, OT, true, true>), g, b, 0, s, *A);

@@ -60,9 +60,10 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 //  * scratch: the global-row partials and, for fp32 input, the bf16 planes
 //    of K and V; no contents carry over between calls.
 //  * plan, aux, bwd: device copies of the call's lfk::Plan, random-block
-//    table and backward tables, kSlots of each keyed by content, so that
-//    calls alternating between a few configurations reuse them.  A missing
-//    one is written into the least recently used slot by a small kernel
+//    table and backward tables, kSlots of each keyed by content (plus one
+//    more for each slot a captured graph holds), so that calls alternating
+//    between a few configurations reuse them.  A missing one is written
+//    into the least recently used free slot by a small kernel
 //    that carries the bytes in its arguments: the write is ordered on the
 //    stream like the kernels that read it, the host never waits for it, and
 //    a write recorded in a graph replays with its own bytes.
@@ -95,7 +96,8 @@ struct Retired {
 };
 struct Workspace {
     Buffer counters, scratch;
-    Slot plan[kSlots], aux[kSlots], bwd[kSlots];
+    std::vector<Slot> plan = std::vector<Slot>(kSlots), aux = std::vector<Slot>(kSlots),
+                      bwd = std::vector<Slot>(kSlots);
     Buffer bwd_stats, bwd_gpart;   // backward: row statistics; global-split records
     Buffer bwd_count;              // backward (bf16): the global tasks' completion counters
     Buffer bwd_fwd;                // backward (bf16) without the forward's results: its output and lse
@@ -190,8 +192,10 @@ Workspace *workspace_for(void *stream, lf_status_t *st) {
 }
 
 // A device copy of `words` among the slots: an existing one when a slot
-// holds it, else written into the least recently used unpinned slot.
-lf_status_t put_table(Workspace &w, Slot (&slots)[kSlots], const uint32_t *words, size_t n, void *stream,
+// holds it, else written into the least recently used unpinned slot.  A
+// slot held by a graph is replaced by a new one (outside capture), so that
+// eager calls always keep kSlots free slots.
+lf_status_t put_table(Workspace &w, std::vector<Slot> &slots, const uint32_t *words, size_t n, void *stream,
                       const void **dev, const char *what) {
     for (Slot &sl : slots)
         if (sl.valid && sl.shadow.size() == n && std::memcmp(sl.shadow.data(), words, n * 4) == 0) {
@@ -200,6 +204,9 @@ lf_status_t put_table(Workspace &w, Slot (&slots)[kSlots], const uint32_t *words
             *dev = sl.buf.ptr;
             return LF_OK;
         }
+    int free_slots = 0;
+    for (const Slot &sl : slots) free_slots += !sl.buf.pinned;
+    if (free_slots < kSlots && !w.capturing) slots.emplace_back();
     Slot *victim = nullptr;
     for (Slot &sl : slots) {
         if (sl.buf.pinned) continue;
@@ -207,7 +214,9 @@ lf_status_t put_table(Workspace &w, Slot (&slots)[kSlots], const uint32_t *words
         if (!victim->valid) break;
     }
     if (!victim)
-        return fail(LF_E_UNSUPPORTED, "every %s slot of this stream is held by a captured graph", what);
+        return fail(LF_E_UNSUPPORTED,
+                    "every %s slot of this stream is held by a captured graph; make one identical call on the "
+                    "stream outside capture first", what);
     // a slot is never grown during capture: it is allocated large enough first
     if (victim->buf.bytes < n * 4) {
         if (w.capturing)
@@ -378,11 +387,6 @@ lf_status_t plan_fwd(int B, int H, int T, int d, int r, const int32_t *radius, i
         for (int g : G) aux[nt + (g >> 5)] |= 1u << (g & 31);
     }
     P.n_rand = n_rand;
-    // heads with unequal radii make tiles of unequal cost: deal runs of 8
-    // tiles to the dies in turn instead of one contiguous eighth per die
-    P.band_chunk = 0;
-    for (int h = 1; h < H; h++)
-        if (P.rad[h] != P.rad[0]) P.band_chunk = 8;
     P.n_g = (int)G.size();
     for (int i = 0; i < P.n_g; i++) P.glob[i] = G[i];
     const long long start = lfk::fill_band_plan(P, B, H, T, dilation);
@@ -417,6 +421,11 @@ lf_status_t plan_fwd(int B, int H, int T, int d, int r, const int32_t *radius, i
         return fail(LF_E_UNSUPPORTED, "problem needs %lld workgroups", n_band + n_glob_tasks);
     P.n_band_tasks = (int)n_band;
     P.n_tasks = (int)(n_band + n_glob_tasks);
+    lfk::split_by_cost(P);
+    // Backward: a die's global tasks go after its band tiles and fill the
+    // tail of their last round, unless they are the longer kind (a split
+    // longer than a band tile's key range), which then start first.
+    P.bwd_globals_first = P.n_g > 0 && P.split_len > (one_sided ? P.r : 2 * P.r) + BM;
     // fp32: K and V are split into three bf16 planes per row (1.5 times the
     // fp32 tensors' bytes) ahead of the tile kernel
     F.planes_off = 0;
@@ -499,12 +508,13 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
                      const int32_t *radius, int one_sided, const int32_t *rand_blocks, int n_rand,
                      const int32_t *dilation, const int32_t *global_idx, int n_global,
                      const uint8_t *key_padding_mask, void *out, float *lse, lf_dtype_t dtype, void *stream,
-                     bool noalloc = false) {
+                     bool noalloc = false, bool global_rows_only = false) {
     g_err.clear();
     // no HIP call before every check has passed
     lf_status_t st = check_fwd(q, k, v, B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation,
                                global_idx, n_global, out, lse, dtype);
     if (st != LF_OK) return st;
+    if (global_rows_only && n_global == 0) return LF_OK;
     FwdPlan F;
     st = plan_fwd(B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation, global_idx, n_global, dtype, F);
     if (st != LF_OK) return st;
@@ -534,7 +544,7 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
         }
         e = lfk_write_plan(&P, sizeof P, base, P.n_g > 0 ? P.counter : nullptr, P.n_g > 0 ? B * H : 0, stream);
         if (e != hipSuccess) return fail(LF_E_HIP, "plan copy launch: %s", hipGetErrorString(e));
-        lfk::Args A;
+        lfk::Args A{};
         A.q = q; A.k = k; A.v = v; A.out = out;
         A.pad = key_padding_mask;
         A.lse = lse;
@@ -548,10 +558,11 @@ lf_status_t attn_fwd(const void *q, const void *k, const void *v, int B, int H, 
     std::lock_guard<std::mutex> lock(g_ws_mu);
     Workspace *w = workspace_for(stream, &st);
     if (!w) return st;
-    lfk::Args A;
+    lfk::Args A{};
     A.q = q; A.k = k; A.v = v; A.out = out;
     A.pad = key_padding_mask;
     A.lse = lse;
+    A.global_rows_only = global_rows_only;
     st = bind_fwd(*w, F, dtype == LF_F32, stream, &A.plan);
     if (st != LF_OK) return st;
     A.fd = fast_decode(P);
@@ -763,7 +774,7 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
         const size_t ybytes = (nbytes + 255) / 256 * 256;
         st = grow(*w, w->bwd_fwd, ybytes + rows * sizeof(float), false, stream);
         if (st != LF_OK) return st;
-        lfk::Args FA;
+        lfk::Args FA{};
         FA.q = q; FA.k = k; FA.v = v;
         FA.out = w->bwd_fwd.ptr;
         FA.pad = key_padding_mask;
@@ -847,6 +858,15 @@ extern "C" lf_status_t lf_attn_fwd_noalloc(const void *q, const void *k, const v
                                            lf_dtype_t dtype, void *stream) {
     return attn_fwd(q, k, v, B, H, T, d, r, nullptr, 0, nullptr, 0, dilation, global_idx, n_global,
                     key_padding_mask, out, nullptr, dtype, stream, true);
+}
+
+extern "C" lf_status_t lf_attn_fwd_global_rows(const void *q, const void *k, const void *v, int B, int H, int T,
+                                               int d, const int32_t *global_idx, int n_global,
+                                               const uint8_t *key_padding_mask, void *out, float *lse,
+                                               lf_dtype_t dtype, void *stream) {
+    // a global row sees every valid key: the window takes no part (radius 0)
+    return attn_fwd(q, k, v, B, H, T, d, 0, nullptr, 0, nullptr, 0, nullptr, global_idx, n_global,
+                    key_padding_mask, out, lse, dtype, stream, false, true);
 }
 
 extern "C" lf_status_t lf_attn_fwd_ex(const void *q, const void *k, const void *v, int B, int H, int T,

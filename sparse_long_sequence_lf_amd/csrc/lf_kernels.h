@@ -51,8 +51,12 @@ struct Plan {
     const int32_t *rtab;     // random key blocks [H][ceil(T/64)][n_rand] (-1 = none), or null
     const uint32_t *gmap;    // bit j set iff position j is global ([ceil(T/32)] words), or null
     int n_rand;              // random key blocks (of 64 keys) per query block of 64
-    int band_chunk;          // 0: each die takes a contiguous eighth of the band tiles;
-                             // C > 0: runs of C tiles are dealt to the dies in turn
+    int band_die[9];         // band_die[8] == 0: each die takes a contiguous eighth of the
+                             // band tasks and of the global-row tasks; else die x takes band
+                             // tasks [band_die[x], band_die[x+1]) and global-row tasks
+                             // [glob_die[x], glob_die[x+1]) (numbered from 0)
+    int glob_die[9];
+    int bwd_globals_first;   // the backward kernels take a die's global tasks before its band tiles
     int head_start[LF_MAX_HEADS + 1];  // band-task prefix over heads
     int32_t dil[LF_MAX_HEADS];   // dilation delta_h
     int32_t rad[LF_MAX_HEADS];   // window radius per head (clamped to T)
@@ -90,6 +94,7 @@ struct Args {
     const uint8_t *pad;      // [B][T] or null
     const Plan *plan;
     float *lse;              // [B][H][T] natural log of each row's softmax denominator, or null
+    int global_rows_only;    // 1: the grid holds the global-row tasks alone
     FastDecode fd;
 };
 

@@ -6,6 +6,10 @@ profiles/ and the HBM-traffic record bench.py reads).
         --cmd "..." --out-json profiles/tile_kernel_hbm_traffic.json --out-txt FILE
     python -m sparse_long_sequence_lf_amd.profiling counters DIR --workload W --cmd "..." --out FILE \
         [--useful-flops F --kernel-us U --hbm-bytes B]
+    python -m sparse_long_sequence_lf_amd.profiling take --workload W [--backward] [--out-dir profiles]
+
+`take` runs the rocprofv3 passes itself (each a child process under a time
+limit) and writes every summary of the workload.
 
 DIR, FETCH_DIR, WRITE_DIR are rocprofv3 output directories written with
 `-f csv` (kernel trace with --stats; one --pmc FETCH_SIZE run; one --pmc
@@ -23,7 +27,9 @@ import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
+from types import SimpleNamespace
 from typing import Dict, List
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -89,16 +95,19 @@ def cmd_stats(a) -> None:
         short = name if len(name) <= 70 else name[:67] + "..."
         lines.append(f"{short:70s} {len(v):6d} {statistics.mean(v) / 1e3:9.2f} {min(v) / 1e3:9.2f} {max(v) / 1e3:9.2f}")
     tile = [x for n, v in durs.items() if KERNEL_NAME in n for x in v]
+    steady_us = None
     if tile:
         steady = tile[a.skip:] if len(tile) > a.skip else tile
         lines += ["", f"tile kernel average duration: {statistics.mean(tile) / 1e3:.2f} us over {len(tile)} dispatches",
                   f"tile kernel steady-state average (first {a.skip} dispatches, the untimed warmup and clock-settle calls, left out): "
                   f"{statistics.mean(steady) / 1e3:.2f} us over {len(steady)}, median {statistics.median(steady) / 1e3:.2f} us",
                   f"kernel sources sha: {kernel_sha()}"]
+        steady_us = statistics.mean(steady) / 1e3
     text = "\n".join(lines) + "\n"
     with open(a.out, "w") as f:
         f.write(text)
     sys.stdout.write(text)
+    return steady_us
 
 
 def cmd_traffic(a) -> None:
@@ -134,6 +143,7 @@ def cmd_traffic(a) -> None:
     with open(a.out_txt, "w") as f:
         f.write(text)
     sys.stdout.write(text)
+    return fetch_b + write_b
 
 
 COUNTER_SET = ["MfmaUtil", "VALUBusy", "SALUBusy", "MfmaFlopsBF16", "LDSBankConflict"]
@@ -173,6 +183,95 @@ def cmd_counters(a) -> None:
     sys.stdout.write(text)
 
 
+def _profile_run(a, work, tag, prof_args, steps, warmup):
+    """One rocprofv3 run of bench.py --profile-mode (a child process, under
+    `timeout -s KILL`); returns its output directory, the untimed calls
+    bench.py reported and the command as the summaries state it."""
+    d = os.path.join(work, f"{_name(a)}{'_bwd' if a.backward else ''}_{tag}")
+    tail = ["--profile-mode", "--workload", a.workload, "--steps", str(steps), "--warmup", str(warmup)]
+    if a.backward:
+        tail.insert(0, "--backward")
+    if a.global_rows:
+        tail.insert(0, "--global-rows")
+    cmd = ["timeout", "-s", "KILL", str(a.timeout), "rocprofv3", *prof_args, "-f", "csv", "-d", d, "-o", tag, "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), *tail]
+    shown = f"cd /tmp && rocprofv3 {' '.join(prof_args)} -f csv -d <out> -o {tag} -- python3 <repo>/bench.py {' '.join(tail)}"
+    print(f"step: {tag}: {shown}", flush=True)
+    p = subprocess.run(cmd, cwd="/tmp", env=dict(os.environ, TMPDIR="/tmp"), capture_output=True, text=True)
+    with open(d + ".log", "w") as f:
+        f.write(p.stdout + p.stderr)
+    done = [ln for ln in p.stdout.splitlines() if ln.startswith("profile mode:")]
+    if not done:
+        raise SystemExit(f"{tag}: bench.py did not finish (exit {p.returncode}); see {d}.log")
+    if p.returncode != 0:
+        # rocprofv3 itself can exit abnormally after a complete run
+        print(f"  note: rocprofv3 exited {p.returncode} after bench.py finished", flush=True)
+    return d, int(done[0].split()[2]), shown
+
+
+def _name(a) -> str:
+    """The workload's name in the summaries (-globalrows: the global rows alone)."""
+    return a.workload + ("-globalrows" if a.global_rows else "")
+
+
+def cmd_take(a) -> None:
+    """Kernel trace, HBM bytes (FETCH_SIZE, then WRITE_SIZE) and utilisation
+    counters of one workload, each from its own rocprofv3 run, and their
+    summaries under --out-dir."""
+    from sparse_long_sequence_lf_amd import metrics
+    from sparse_long_sequence_lf_amd import workloads as W
+    work = os.path.abspath(a.work_dir)
+    out = os.path.abspath(a.out_dir)
+    os.makedirs(work, exist_ok=True)
+    os.makedirs(out, exist_ok=True)
+    made_by = f"python -m sparse_long_sequence_lf_amd.profiling take --workload {a.workload}" + \
+        (" --backward" if a.backward else "") + (" --global-rows" if a.global_rows else "")
+    name = _name(a)
+    if a.backward:
+        d, skip, shown = _profile_run(a, work, "kt", ["--kernel-trace", "--stats"], 20, 3)
+        cmd_stats(SimpleNamespace(dir=d, workload=a.workload + " (backward)", cmd=f"{shown}\n    (run by: {made_by})",
+                                  out=os.path.join(out, f"bwd_kernels_{a.workload}_trace.txt"), skip=0))
+        return
+    d, skip, shown = _profile_run(a, work, "kt", ["--kernel-trace", "--stats"], 50, 10)
+    kernel_us = cmd_stats(SimpleNamespace(dir=d, workload=name, cmd=f"{shown}\n    (run by: {made_by})",
+                                          out=os.path.join(out, f"tile_kernel_{name}_trace.txt"), skip=skip))
+    fd, _, shown_f = _profile_run(a, work, "f", ["--pmc", "FETCH_SIZE"], 10, 2)
+    wd, _, _ = _profile_run(a, work, "w", ["--pmc", "WRITE_SIZE"], 10, 2)
+    hbm = cmd_traffic(SimpleNamespace(fetch_dir=fd, write_dir=wd, workload=name,
+                                      cmd=shown_f.replace("--pmc FETCH_SIZE", "--pmc FETCH_SIZE (then WRITE_SIZE)") +
+                                      f"\n    (run by: {made_by})",
+                                      out_json=os.path.join(out, "tile_kernel_hbm_traffic.json"),
+                                      out_txt=os.path.join(out, f"tile_kernel_{name}_hbm.txt")))
+    ud, _, shown_u = _profile_run(a, work, "u", ["--pmc", *COUNTER_SET], 10, 2)
+    w = W.workload(a.workload)
+    inp = W.make_inputs(w)
+    B, H, T, dd = inp.q.shape
+    useful = 0.0
+    if not a.global_rows:
+        pairs = metrics.useful_pairs(B, H, T, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask,
+                                     one_sided=inp.one_sided, random_blocks=inp.random_blocks)
+        useful = 4.0 * dd * pairs
+    cmd_counters(SimpleNamespace(dir=ud, workload=name, cmd=f"{shown_u}\n    (run by: {made_by})",
+                                 out=os.path.join(out, f"tile_kernel_{name}_util.txt"),
+                                 useful_flops=useful, kernel_us=kernel_us or 0.0, hbm_bytes=hbm))
+    if a.global_rows:
+        sys.path.insert(0, ROOT)
+        import bench
+        alg = bench.global_rows_bytes(inp)
+        text = (f"# HBM rate of the global rows alone: {a.workload}\n\n"
+                f"lf_attn_fwd_global_rows runs the global-row tasks of the tile kernel (the same tasks, and\n"
+                f"the same combine, as the whole forward runs for those rows) and nothing else.\n\n"
+                f"run by: {made_by}\n\n"
+                f"tile kernel steady-state average: {kernel_us:.2f} us per launch\n"
+                f"algorithmic bytes (every valid K and V row of each (b, h) once, plus the global rows'\n"
+                f"q read and out written): {alg / 1e6:.3f} MB -> {alg / (kernel_us * 1e-6) / 1e9:.0f} GB/s\n"
+                f"counter bytes (FETCH_SIZE + WRITE_SIZE, scaled by the calibration copy): {hbm / 1e6:.3f} MB -> "
+                f"{hbm / (kernel_us * 1e-6) / 1e9:.0f} GB/s ({hbm / alg:.2f} x algorithmic)\n"
+                f"kernel sources sha: {kernel_sha()}\n")
+        with open(os.path.join(out, "global_rows_hbm_rate.txt"), "w") as f:
+            f.write(text)
+        sys.stdout.write(text)
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -197,8 +296,15 @@ def main(argv=None) -> None:
     c.add_argument("--useful-flops", type=float, default=0.0)
     c.add_argument("--kernel-us", type=float, default=0.0)
     c.add_argument("--hbm-bytes", type=float, default=0.0)
+    k = sub.add_parser("take")
+    k.add_argument("--workload", required=True)
+    k.add_argument("--backward", action="store_true", help="kernel trace of the backward call only")
+    k.add_argument("--global-rows", action="store_true", help="the global rows alone (lf_attn_fwd_global_rows)")
+    k.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    k.add_argument("--work-dir", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    k.add_argument("--timeout", type=int, default=150, help="seconds per rocprofv3 run")
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters, "take": cmd_take}[a.what](a)
 
 
 if __name__ == "__main__":

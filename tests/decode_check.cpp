@@ -109,6 +109,52 @@ int main() {
                         }
             }
         }
+        // workgroup slots -> tasks: with equal radii (an eighth per die) and
+        // with unequal ones (runs cut by cost), every task exactly once
+        for (int unequal = 0; unequal < 2; unequal++) {
+            for (int h = 0; h < sh.H; h++) P.rad[h] = unequal ? (int32_t)(rng() % 600) : 256;
+            P.one_sided = (int)(rng() % 2);
+            P.n_split = 1 + (int)(rng() % 9);
+            P.n_ggroups = 1 + (int)(rng() % 3);
+            P.n_band_tasks = (int)(tpb * sh.B);
+            P.n_tasks = P.n_band_tasks + (rng() % 2 ? sh.B * sh.H * P.n_split * P.n_ggroups : 0);
+            split_by_cost(P);
+            const bool cut = P.band_die[8] > 0;
+            CHECK(cut == (unequal && sh.H > 1 && P.n_band_tasks > 0 && [&] {
+                      for (int h = 1; h < sh.H; h++) if (P.rad[h] != P.rad[0]) return true;
+                      return false; }()), "T=%d: cost cut %d", sh.T, (int)cut);
+            const int spd = slots_per_die(P);
+            for (int first = 0; first < 2; first++) {
+                std::vector<int> hits(P.n_tasks, 0);
+                for (int x = 0; x < 8; x++)
+                    for (int sl = 0; sl < spd; sl++) {
+                        const int t = task_of_slot(P, x, sl, first != 0);
+                        CHECK(t >= -1 && t < P.n_tasks, "slot (%d,%d) -> %d", x, sl, t);
+                        if (t >= 0 && t < P.n_tasks) hits[t]++;
+                        // the global-row tasks of a die come first, or last
+                        if (t >= 0 && sl > 0) {
+                            const int tp = task_of_slot(P, x, sl - 1, first != 0);
+                            const bool g = t >= P.n_band_tasks, gp = tp >= P.n_band_tasks;
+                            CHECK(tp >= 0 && (first ? (!g || gp) : (g || !gp)), "die %d: task order", x);
+                        }
+                    }
+                for (int t = 0; t < P.n_tasks; t++)
+                    CHECK(hits[t] == 1, "T=%d: task %d taken %d times", sh.T, t, hits[t]);
+                checked += P.n_tasks;
+            }
+            if (cut) {
+                for (int x = 0; x < 8; x++)
+                    CHECK(P.band_die[x] <= P.band_die[x + 1] && P.glob_die[x] <= P.glob_die[x + 1], "runs not ordered");
+                // a head's global-row tasks sit on the die of the middle of its band tiles
+                const int per_bh = P.n_split * P.n_ggroups;
+                for (int x = 0; x < 8 && P.n_tasks > P.n_band_tasks; x++)
+                    for (int g = P.glob_die[x]; g < P.glob_die[x + 1]; g++) {
+                        const int bh = g / per_bh, b = bh / sh.H, h = bh % sh.H;
+                        const long long mid = (long long)b * tpb + (P.head_start[h] + P.head_start[h + 1]) / 2;
+                        CHECK(mid >= P.band_die[x] && (mid < P.band_die[x + 1] || x == 7), "head %d off its die", bh);
+                    }
+            }
+        }
     }
     if (fails) {
         std::printf("FAILED %d\n", fails);

@@ -271,3 +271,37 @@ def test_noalloc_refuses_workspace_beyond_scratch(lib):
     assert st == lf.LF_E_UNSUPPORTED and "workspace" in lf.last_error()
     st = lib.lf_attn_fwd_noalloc(Q, K, V, 1, 2, 128, 64, -1, None, None, 0, None, OUT, lf.LF_BF16, None)
     assert st == lf.LF_E_INVALID
+
+
+GR_BAD = [
+    ("null_q", dict(q=None), lf.LF_E_INVALID),
+    ("global_out_of_range", dict(g=[128]), lf.LF_E_INVALID),
+    ("global_negative", dict(g=[-1]), lf.LF_E_INVALID),
+    ("d_48", dict(d=48), lf.LF_E_UNSUPPORTED),
+    ("out_is_v", dict(out=V), lf.LF_E_INVALID),
+    ("too_many_globals", dict(T=4096, g=list(range(600))), lf.LF_E_UNSUPPORTED),
+]
+
+
+def _gr(lib, q=Q, k=K, v=V, B=1, H=2, T=128, d=64, g=(0, 5), out=OUT, lse=None, dtype=lf.LF_BF16):
+    ga = (ctypes.c_int32 * max(1, len(g)))(*g)
+    return lib.lf_attn_fwd_global_rows(q, k, v, B, H, T, d, ga, len(g), None, out, lse, dtype, None)
+
+
+@pytest.mark.parametrize("name,kw,status", GR_BAD, ids=[b[0] for b in GR_BAD])
+def test_global_rows_invalid_arguments_rejected(lib, name, kw, status):
+    st = _gr(lib, **kw)
+    assert st == status, (name, st, lf.last_error())
+    assert lf.last_error() != ""
+
+
+def test_global_rows_without_globals_enqueues_nothing(lib):
+    # no global position: LF_OK before any HIP call (none is made here, where
+    # there is no GPU), and the host stand-ins for the tensors stay untouched
+    buf = np.full(2 * 128 * 64, 3.0, dtype=np.float32)
+    out = np.full_like(buf, 5.0)
+    st = _gr(lib, q=buf.ctypes.data, k=buf.ctypes.data + 0, v=buf.ctypes.data, out=out.ctypes.data, g=(),
+             dtype=lf.LF_F32)
+    # q, k and v share one buffer here: reading is allowed, only out must not alias
+    assert st == lf.LF_OK, lf.last_error()
+    assert np.all(out == 5.0)

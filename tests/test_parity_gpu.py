@@ -326,3 +326,40 @@ def test_random_table_change_same_shape():
         print(f"case random table {s}", flush=True)
         err = max_err(gpu_fwd(inp), oracle_full(inp))
         assert err <= TOL["f32"], (s, err)
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=81, B=1, H=3, T=700, dtype="bf16", r=40, n_global=3, pad="none"),
+    dict(seed=82, B=2, H=2, T=530, dtype="f32", r=5, n_global=70, pad="right"),
+    dict(seed=83, B=3, H=4, T=300, dtype="bf16", r=0, n_global=130, pad="random"),
+    dict(seed=84, B=1, H=2, T=97, dtype="f32", r=9, n_global=1, pad="random"),
+], ids=["bf16-3g", "f32-70g-right", "bf16-130g-random", "f32-1g-ragged"])
+def test_global_rows_only(case):
+    # lf_attn_fwd_global_rows: the global rows (out and lse) equal the oracle's
+    # and, bit for bit, those of the whole forward; every other row keeps the
+    # value it held before the call
+    c = dict(case)
+    inp = W.random_case(c.pop("seed"), **c, max_dil=3)
+    B, H, T, d = inp.q.shape
+    q, k, v = (x.to("cuda:0") for x in (inp.q, inp.k, inp.v))
+    kpm = None if inp.key_padding_mask is None else inp.key_padding_mask.to("cuda:0")
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((B, H, T), 5.0, dtype=torch.float32, device="cuda:0")
+    lf.attn_fwd_global_rows(q, k, v, inp.global_idx, key_padding_mask=kpm, out=out, lse=lse)
+    full = torch.empty_like(q)
+    full_lse = torch.empty_like(lse)
+    lf.attn_fwd(q, k, v, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm, out=full, lse=full_lse)
+    torch.cuda.synchronize()
+    G = sorted(set(inp.global_idx))
+    is_g = torch.zeros(T, dtype=torch.bool)
+    is_g[G] = True
+    dt = "f32" if inp.q.dtype == torch.float32 else "bf16"
+    ref = oracle_full(inp)
+    err = max_err(out[:, :, G], ref[:, :, G])
+    print(f"  {tuple(inp.q.shape)} {dt} n_g={len(G)}: global rows max abs err {err:.3e}", flush=True)
+    assert err <= TOL[dt]
+    assert torch.equal(out[:, :, G], full[:, :, G])
+    assert torch.equal(lse[:, :, G], full_lse[:, :, G])
+    rest = out[:, :, ~is_g.to("cuda:0")]
+    assert bool((rest == 7.0).all()), "a row outside G was written"
+    assert bool((lse[:, :, ~is_g.to("cuda:0")] == 5.0).all()), "an lse outside G was written"
