@@ -99,7 +99,9 @@ def _rand_table(random_blocks, H=None, T=None):
     if H is not None and T is not None and a.shape[:2] != (int(H), (int(T) + 63) // 64):
         raise ValueError(f"random_blocks has shape {a.shape}; expected [{int(H)}][{(int(T) + 63) // 64}][n_rand]")
     flat = a.reshape(-1)
-    return (ctypes.c_int32 * max(1, flat.size))(*flat.tolist()), int(a.shape[2])
+    if flat.size == 0:
+        return (ctypes.c_int32 * 1)(), int(a.shape[2])
+    return (ctypes.c_int32 * flat.size).from_buffer_copy(flat.tobytes()), int(a.shape[2])
 
 
 def _dilation_array(dilation, H):

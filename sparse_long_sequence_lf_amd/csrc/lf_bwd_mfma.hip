@@ -24,18 +24,20 @@
 //     reads the global keys);
 //   * random blocks (undilated heads): a query block's drawn key blocks
 //     without the keys of the window or of G, and for dk, dv the query
-//     blocks that drew the key block, without global queries.
-// The global rows' dq and the global keys' dk, dv come from the vector
-// kernels of lf_bwd_kernels.hip.
+//     blocks that drew the key block, without global queries;
+//   * global tasks (task kind 1): the global rows' dq over one split of the
+//     keys, the global keys' dk, dv over one split of the queries; each
+//     writes an fp32 partial record, and the last task of a head adds the
+//     splits in order and writes the rows.
 //
-// Two launches, the global-row kernels of lf_bwd_kernels.hip between them:
+// Two launches:
 //   dq_kernel    query-major: a tile of 64 class queries (two blocks of 32,
 //                two key phases, four waves) streams its key blocks through
 //                an LDS ring: S^T = K Q^T, dP^T = V dY^T,
 //                dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (12 MFMAs a block).
 //                It also writes each row's statistics (lse_i log2 e,
 //                D_i = dy_i . y_i; a padded row, lse = -inf, gets (+inf, 0),
-//                so its weights vanish) for the kernels after it.
+//                so its weights vanish) for the dk/dv kernel.
 //   dkdv_kernel  key-major: a tile of 64 class keys streams the blocks of
 //                the queries that read them: S = Q K^T, dP = dY V^T,
 //                dS = P (dP - D), dV^T += dY^T P, dK^T += Q^T dS (16 MFMAs).

@@ -28,7 +28,7 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "PROFILE_WORKLOADS", "make_inputs", "workload"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "workload"]
 
 
 @dataclass(frozen=True)
@@ -90,21 +90,10 @@ WORKLOADS: List[Workload] = [
 ]
 
 
-# Shapes used only for profiles: the padded workload with r = 0, where each
-# band query reads one key plus the globals, so that the global rows (every
-# valid K and V row read per (b, h)) carry nearly all of the kernel's memory
-# traffic.
-PROFILE_WORKLOADS: List[Workload] = [
-    Workload("bf16-b4h16t16384-r0-g8-pad", 1005, 4, 16, 16384, 64, 0, "bf16", scale=0.5,
-             n_random_globals=8, random_global_hi_from_min_len=True, len_lo=8192, len_hi=16384,
-             description="the padded workload with r=0: global rows dominate the memory traffic (profiles only)"),
-]
-
-
 def workload(name_or_index) -> Workload:
     if isinstance(name_or_index, int):
         return WORKLOADS[name_or_index]
-    for w in WORKLOADS + PROFILE_WORKLOADS:
+    for w in WORKLOADS:
         if w.name == name_or_index:
             return w
     raise KeyError(name_or_index)
