@@ -38,14 +38,17 @@ KERNEL_SOURCES = ["sparse_long_sequence_lf_amd/csrc/lf_fwd_kernels.hip",
                   "sparse_long_sequence_lf_amd/csrc/lf_kernels.h",
                   "sparse_long_sequence_lf_amd/csrc/lf_device.h",
                   "sparse_long_sequence_lf_amd/csrc/lf_decode.h"]
+BWD_SOURCES = ["sparse_long_sequence_lf_amd/csrc/lf_bwd_mfma.hip",
+               "sparse_long_sequence_lf_amd/csrc/lf_bwd_kernels.hip",
+               "sparse_long_sequence_lf_amd/csrc/lf_bwd.h"] + KERNEL_SOURCES
 KERNEL_NAME = "tile_kernel"
 COPY_BYTES = 1 << 28   # the calibration copy in bench.py --profile-mode
 
 
-def kernel_sha() -> str:
+def kernel_sha(sources=None) -> str:
     """Digest of the kernel sources: a traffic record taken on other sources is stale."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -96,6 +99,13 @@ def cmd_stats(a) -> None:
         lines.append(f"{short:70s} {len(v):6d} {statistics.mean(v) / 1e3:9.2f} {min(v) / 1e3:9.2f} {max(v) / 1e3:9.2f}")
     tile = [x for n, v in durs.items() if KERNEL_NAME in n for x in v]
     steady_us = None
+    if getattr(a, "backward", False):
+        bwd = {n: v for n, v in durs.items() if "bwd" in n or "lfb" in n}
+        lines += ["", "The tile_kernel line is the one forward call that makes the output and lse handed to every",
+                  f"backward call.  Sum of the backward kernels' averages: "
+                  f"{sum(statistics.mean(v) for v in bwd.values()) / 1e3:.2f} us per call.",
+                  f"backward kernel sources sha: {kernel_sha(BWD_SOURCES)}"]
+        tile = []
     if tile:
         steady = tile[a.skip:] if len(tile) > a.skip else tile
         lines += ["", f"tile kernel average duration: {statistics.mean(tile) / 1e3:.2f} us over {len(tile)} dispatches",
@@ -230,7 +240,8 @@ def cmd_take(a) -> None:
     if a.backward:
         d, skip, shown = _profile_run(a, work, "kt", ["--kernel-trace", "--stats"], 20, 3)
         cmd_stats(SimpleNamespace(dir=d, workload=a.workload + " (backward)", cmd=f"{shown}\n    (run by: {made_by})",
-                                  out=os.path.join(out, f"bwd_kernels_{a.workload}_trace.txt"), skip=0))
+                                  out=os.path.join(out, f"bwd_kernels_{a.workload}_trace.txt"), skip=0,
+                                  backward=True))
         return
     d, skip, shown = _profile_run(a, work, "kt", ["--kernel-trace", "--stats"], 50, 10)
     kernel_us = cmd_stats(SimpleNamespace(dir=d, workload=name, cmd=f"{shown}\n    (run by: {made_by})",
