@@ -177,3 +177,19 @@ def test_bwd_ex_argument_checks():
     bad_lse = grads[0].view(torch.float32).reshape(-1)[: 200].view(1, 2, 100)
     with pytest.raises(lf.LfError):
         lf.attn_bwd(q, k, v, dy, inp.r, inp.dilation, inp.global_idx, out=grads, y=y, lse=bad_lse)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_bwd_unequal_radii_many_globals(dt):
+    # per-die runs of equal cost (unequal radii) with several groups of
+    # global rows and keys, both orders of a die's tasks (splits shorter and
+    # longer than a band tile's key range)
+    for seed, (B, H, T, n_g, pad) in enumerate([(3, 5, 500, 70, "right"), (2, 7, 700, 140, "random"),
+                                                (1, 4, 2000, 3, "none")]):
+        base = W.random_case(9300 + seed, B=B, H=H, T=T, dtype=dt, n_global=n_g, pad=pad, max_dil=3)
+        rng = np.random.default_rng(9400 + seed)
+        rads = [int(x) for x in rng.integers(0, 64, size=H)]
+        inp = W.Inputs(base.q, base.k, base.v, rads, base.dilation, base.global_idx, base.lengths,
+                       base.key_padding_mask, one_sided=bool(seed % 2))
+        dy = W.make_grad(inp, 9500 + seed)
+        check(inp, dy, dt, f"B={B} H={H} T={T} n_g={len(set(inp.global_idx))} radii={rads} dil={inp.dilation}")

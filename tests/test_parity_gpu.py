@@ -363,3 +363,19 @@ def test_global_rows_only(case):
     rest = out[:, :, ~is_g.to("cuda:0")]
     assert bool((rest == 7.0).all()), "a row outside G was written"
     assert bool((lse[:, :, ~is_g.to("cuda:0")] == 5.0).all()), "an lse outside G was written"
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_unequal_radii_many_globals(dt):
+    # heads of unequal radii cut into per-die runs of equal cost, with two and
+    # three groups of global rows assigned to the dies of their heads' tiles
+    for seed, (B, H, T, n_g, pad) in enumerate([(3, 5, 500, 70, "right"), (2, 7, 700, 140, "random"),
+                                                (4, 3, 260, 65, "none")]):
+        base = W.random_case(9100 + seed, B=B, H=H, T=T, dtype=dt, n_global=n_g, pad=pad, max_dil=3)
+        rng = np.random.default_rng(9200 + seed)
+        rads = [int(x) for x in rng.integers(0, T // 2, size=H)]
+        inp = W.Inputs(base.q, base.k, base.v, rads, base.dilation, base.global_idx, base.lengths,
+                       base.key_padding_mask, one_sided=bool(seed % 2))
+        print(f"case B={B} H={H} T={T} n_g={len(set(inp.global_idx))} radii={rads} dil={inp.dilation}", flush=True)
+        err = max_err(gpu_fwd(inp), oracle_full(inp))
+        assert err <= TOL[dt], err
