@@ -58,7 +58,6 @@
 namespace lfk {
 
 constexpr int BM = LFK_BM;                // queries per band tile
-constexpr int kVecGlobals = 2;                 // band tasks take up to this many global keys on the VALU
 
 template <typename T> struct Elem;
 template <> struct Elem<__bf16> { static constexpr int NP = 1; };
@@ -600,10 +599,15 @@ void tile_kernel(const Args A) {
     // then the random blocks, in sequence positions q; stage s holds
     // positions 2s and 2s+1, and this wave works on position 2s + ph.
     const int nb = tk.nband;
-    // A band task with at most kVecGlobals globals takes the global keys on
-    // the vector units before the band (below): a global-key block would cost
-    // a whole step of the loop for one or two keys.  With more globals they
-    // follow the band blocks in the ring.
+    // A band task with a single global takes the key on the vector units
+    // before the band (below): a global-key block would cost a whole step of
+    // the loop for one key.  With more globals they follow the band blocks in
+    // the ring: from two on, one step for up to 32 keys costs less than the
+    // vector path run once per key (18.0 -> 17.2 us with globals {0, T-1} on
+    // the headline shape).  Tiles with random blocks keep two globals on the
+    // vector path: there a global-key step measured no faster and moved more
+    // bytes (32.9 against 29.8 MB a launch).
+    constexpr int kVecGlobals = RAND ? 2 : 1;
     const bool gvec = tk.kind == 0 && n_g > 0 && n_g <= kVecGlobals;
     const int ngb = (tk.kind == 0 && !gvec) ? cdiv(n_g, KBLK) : 0;
     // random key blocks of this query block (undilated heads): each block of
