@@ -28,8 +28,8 @@
 //                 from the queries whose window holds j, plus the global rows.
 //   gcols_kernel  global keys: every valid query, in splits likewise.
 //   combine_kernel  adds the splits' parts of dq, dk, dv of the global positions.
-// In the band kernels four lanes share a row (16 channels each) and a wave
-// holds 16 rows of one residue class; the other side's rows stream past,
+// In the band kernels eight lanes share a row (8 channels each) and a wave
+// holds 8 rows of one residue class; the other side's rows stream past,
 // the next one loaded while the current one is used.  No atomics, so results
 // are reproducible.  This is the plain vector-unit path; it does not use MFMA.
 #include <hip/hip_runtime.h>
@@ -645,11 +645,23 @@ __device__ __forceinline__ GTask gtask(const lfk::BwdArgs& A) {
 }
 
 // pass 1 of a global row: (max, sum, sum of p dP) over the split's keys
+// (m, l, dn) += (m2, l2, d2): two partial softmax sums over disjoint key
+// sets, each l = sum 2^(s - m) and dn = sum 2^(s - m) dP; a part that met no
+// valid key has m = -inf and l = dn = 0
+__device__ __forceinline__ void merge_stats(float& m, float& l, float& dn, float m2, float l2, float d2) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) return;
+    const float a = ex2(m - M), b = ex2(m2 - M);
+    l = l * a + l2 * b;
+    dn = dn * a + d2 * b;
+    m = M;
+}
+
 template <typename ET>
 __global__ __launch_bounds__(256) void grows_stats_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
                                                           const ET* __restrict__ K, const ET* __restrict__ V,
                                                           const ET* __restrict__ DY) {
-    __shared__ float red_m[256], red_l[256], red_d[256];
+    __shared__ float red_m[4], red_l[4], red_d[4];
     const int tid = threadIdx.x;
     const GTask t = gtask(A);
     const int T = A.T;
@@ -676,20 +688,21 @@ __global__ __launch_bounds__(256) void grows_stats_kernel(const lfk::BwdArgs A, 
             m = mn;
         }
     }
-    red_m[tid] = m;
-    red_l[tid] = l;
-    red_d[tid] = dn;
+    // (max, sum, weighted sum) of the 256 threads: within each wave by
+    // lane exchanges, then the four waves' results through LDS
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float m2 = __shfl_xor(m, o), l2 = __shfl_xor(l, o), d2 = __shfl_xor(dn, o);
+        merge_stats(m, l, dn, m2, l2, d2);
+    }
+    if ((tid & 63) == 0) {
+        red_m[tid >> 6] = m;
+        red_l[tid >> 6] = l;
+        red_d[tid >> 6] = dn;
+    }
     __syncthreads();
     if (tid == 0) {
-        float M = -INFINITY;
-        for (int e = 0; e < 256; e++) M = fmaxf(M, red_m[e]);
-        float L = 0.f, DN = 0.f;
-        for (int e = 0; e < 256; e++) {
-            if (red_l[e] == 0.f) continue;   // a thread that met no valid key
-            const float w = ex2(red_m[e] - M);
-            L += red_l[e] * w;
-            DN += red_d[e] * w;
-        }
+        float M = red_m[0], L = red_l[0], DN = red_d[0];
+        for (int e = 1; e < 4; e++) merge_stats(M, L, DN, red_m[e], red_l[e], red_d[e]);
         A.gstat[t.rec * A.n_split + t.sp] = make_float4(M, L, DN, 0.f);
     }
 }
