@@ -12,15 +12,17 @@
 
 #include "lf_attn.h"
 
-// Lanes that share one row (query or key) in the backward's band kernels, 4
-// or 8; a wave holds 64 / that many rows of one residue class, and
+// Lanes that share one row (query or key) in the backward's band kernels,
+// 4, 8 or 16; a wave holds 64 / that many rows of one residue class, and
 // head_chunk counts chunks of that many class positions.  These kernels
 // serve fp32 inputs, the precision path, which is most used on small
-// problems: there eight lanes a row (twice the waves) measured faster
-// (B = 1, H = 2, T = 1024, r = 64: 179 -> 140 us a call), while on the
-// T = 4096, r = 256 shape with 12 heads four were (743 against 922 us).
+// problems: there more lanes a row (more waves, fewer registers) measured
+// faster (B = 1, H = 2, T = 1024, r = 64: 179 us at four, 140 at eight,
+// 105 at sixteen, with the global-row statistics reduced across lanes),
+// while on the T = 4096, r = 256 shape with 12 heads four were faster than
+// eight (743 against 922 us).
 #ifndef LFB_LANES_PER_ROW
-#define LFB_LANES_PER_ROW 8
+#define LFB_LANES_PER_ROW 16
 #endif
 #define LFB_ROWS_PER_WAVE (64 / LFB_LANES_PER_ROW)
 

@@ -28,8 +28,8 @@
 //                 from the queries whose window holds j, plus the global rows.
 //   gcols_kernel  global keys: every valid query, in splits likewise.
 //   combine_kernel  adds the splits' parts of dq, dk, dv of the global positions.
-// In the band kernels eight lanes share a row (8 channels each) and a wave
-// holds 8 rows of one residue class; the other side's rows stream past,
+// In the band kernels sixteen lanes share a row (4 channels each) and a
+// wave holds 4 rows of one residue class; the other side's rows stream past,
 // the next one loaded while the current one is used.  No atomics, so results
 // are reproducible.  This is the plain vector-unit path; it does not use MFMA.
 #include <hip/hip_runtime.h>
@@ -133,7 +133,7 @@ __device__ __forceinline__ bool padded(const uint8_t* __restrict__ pad, int i) {
 constexpr int LPR = LFB_LANES_PER_ROW;  // lanes per row
 constexpr int NQ = LFB_ROWS_PER_WAVE;   // rows per wave
 constexpr int CS = D / LPR;             // channels per lane
-static_assert(LPR == 4 || LPR == 8, "four or eight lanes per row");
+static_assert(LPR == 4 || LPR == 8 || LPR == 16, "four, eight or sixteen lanes per row");
 
 struct Slice {
     float x[CS];
@@ -256,8 +256,10 @@ __device__ __forceinline__ void axpy_w(Slice& acc, float a, const In<ET>& x) {
 __device__ __forceinline__ float quad_sum(float x) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lane ^ 1
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lane ^ 2
-    if constexpr (LPR == 8)   // the other quad of the group of 8 (lane i reads lane 7 - i)
+    if constexpr (LPR >= 8)   // the other quad of the group of 8 (lane i reads lane 7 - i)
         x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+    if constexpr (LPR == 16)  // the other half of the row of 16 (lane i reads lane 15 - i)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
     return x;
 }
 
