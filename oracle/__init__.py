@@ -43,6 +43,10 @@ def open_library(path):
     lib.lf_oracle_fwd_lse.restype = I
     lib.lf_oracle_bwd.argtypes = [P, P, P, P, I, I, I, I, I, P, I, P, I, P, P, I, P, P, P, P, I]
     lib.lf_oracle_bwd.restype = I
+    lib.lf_oracle_bwd_rows.argtypes = [P, P, P, P, I, I, I, I, I, P, I, P, I, P, P, I, P, P, LL, P, I]
+    lib.lf_oracle_bwd_rows.restype = I
+    lib.lf_oracle_bwd_keys.argtypes = [P, P, P, P, I, I, I, I, I, P, I, P, I, P, P, I, P, P, LL, P, P, I]
+    lib.lf_oracle_bwd_keys.restype = I
     return lib
 
 
@@ -182,6 +186,49 @@ def bwd(q, k, v, dy, r, dilation=None, global_idx=None, key_padding_mask=None, n
     if nt < 0:
         raise ValueError("oracle rejected its arguments")
     return dq, dk, dv
+
+
+def _bwd_selected(q, k, v, dy, r, flat, dilation, global_idx, key_padding_mask, n_threads, lib, one_sided,
+                  random_blocks, keys):
+    lib = lib or _load()
+    qf, kf, vf, dyf = _f32(q), _f32(k), _f32(v), _f32(dy)
+    B, H, T, d = qf.shape
+    if dyf.shape != qf.shape:
+        raise ValueError("dy must have the shape of q")
+    r0, rad = _radius(r, H)
+    rb, nr = _rand_blocks(random_blocks, H, T)
+    dil = _i32(dilation)
+    g = _i32(global_idx if global_idx is not None else [])
+    pad = _u8(key_padding_mask)
+    sel = np.ascontiguousarray(np.asarray(flat, dtype=np.int64).reshape(-1))
+    o1 = np.zeros((sel.size, d), dtype=np.float64)
+    common = (_ptr(qf), _ptr(kf), _ptr(vf), _ptr(dyf), B, H, T, d, r0, _ptr(rad), int(bool(one_sided)),
+              _ptr(rb), nr, _ptr(dil), _ptr(g), int(g.size), _ptr(pad), _ptr(sel), int(sel.size))
+    if keys:
+        o2 = np.zeros((sel.size, d), dtype=np.float64)
+        nt = lib.lf_oracle_bwd_keys(*common, _ptr(o1), _ptr(o2), int(n_threads))
+    else:
+        o2 = None
+        nt = lib.lf_oracle_bwd_rows(*common, _ptr(o1), int(n_threads))
+    if nt < 0:
+        raise ValueError("oracle rejected its arguments")
+    return (o1, o2) if keys else o1
+
+
+def bwd_rows(q, k, v, dy, r, rows_flat, dilation=None, global_idx=None, key_padding_mask=None, n_threads=0,
+             lib=None, one_sided=False, random_blocks=None):
+    """dq of chosen query rows: rows_flat[e] = (b*H + h)*T + i -> dq[e][d]
+    (the rows of ``bwd``'s dq, bit for bit, without computing the rest)."""
+    return _bwd_selected(q, k, v, dy, r, rows_flat, dilation, global_idx, key_padding_mask, n_threads, lib,
+                         one_sided, random_blocks, keys=False)
+
+
+def bwd_keys(q, k, v, dy, r, keys_flat, dilation=None, global_idx=None, key_padding_mask=None, n_threads=0,
+             lib=None, one_sided=False, random_blocks=None):
+    """dk and dv of chosen key positions: keys_flat[e] = (b*H + h)*T + j ->
+    (dk[e][d], dv[e][d]); the sums run over every row that attends to j."""
+    return _bwd_selected(q, k, v, dy, r, keys_flat, dilation, global_idx, key_padding_mask, n_threads, lib,
+                         one_sided, random_blocks, keys=True)
 
 
 def rows(q, k, v, r, rows_flat, dilation=None, global_idx=None, key_padding_mask=None,

@@ -67,7 +67,9 @@
  * head equals delta undilated problems on the residue subsequences; keys
  * outside N(i) do not influence row i; global rows equal dense rows.
  * Gradients: float64 autograd of the dense brute force, central finite
- * differences, sum_j dk_j = 0 and sum_j dv_j = sum of dy over valid rows.
+ * differences, sum_j dk_j = 0 and sum_j dv_j = sum of dy over valid rows;
+ * the gradient at chosen rows and keys (lf_oracle_bwd_rows, _keys) against
+ * autograd and, bit for bit, the whole gradient.
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -339,9 +341,10 @@ typedef struct {
     long long n_bh;
 } bjob_t;
 
-static void grad_row(const float *qi, const float *dyi, const float *K, const float *V, int d,
-                     const int *nb, int n, double *s, double *dqi, double *dK, double *dV) {
-    if (n == 0) return;
+/* Row i's weights P_ij = softmax_j(s_ij) over N(i), into s (in the order of
+ * nb), and D_i = sum_j P_ij dP_ij with dP_ij = dy_i . v_j. */
+static double row_weights(const float *qi, const float *dyi, const float *K, const float *V, int d,
+                          const int *nb, int n, double *s) {
     const double inv_sqrt_d = 1.0 / sqrt((double)d);
     double m = -INFINITY;
     for (int t = 0; t < n; t++) {
@@ -356,7 +359,6 @@ static void grad_row(const float *qi, const float *dyi, const float *K, const fl
         s[t] = exp(s[t] - m);
         l += s[t];
     }
-    /* P_ij in s; D_i = sum_j P_ij dP_ij */
     double D = 0.0;
     for (int t = 0; t < n; t++) {
         s[t] /= l;
@@ -365,16 +367,35 @@ static void grad_row(const float *qi, const float *dyi, const float *K, const fl
         for (int c = 0; c < d; c++) dp += (double)dyi[c] * (double)vj[c];
         D += s[t] * dp;
     }
+    return D;
+}
+
+/* dS_ij = P_ij (dP_ij - D_i) for the key at position t of row i's list. */
+static double row_ds(const float *dyi, const float *V, int d, const int *nb, const double *s, double D,
+                     int t) {
+    const float *vj = V + (size_t)nb[t] * d;
+    double dp = 0.0;
+    for (int c = 0; c < d; c++) dp += (double)dyi[c] * (double)vj[c];
+    return s[t] * (dp - D);
+}
+
+/* Row i's contributions: dq_i, and (when dK, dV are given) its terms of
+ * dk_j and dv_j for every j in N(i). */
+static void grad_row(const float *qi, const float *dyi, const float *K, const float *V, int d,
+                     const int *nb, int n, double *s, double *dqi, double *dK, double *dV) {
+    if (n == 0) return;
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    const double D = row_weights(qi, dyi, K, V, d, nb, n, s);
     for (int t = 0; t < n; t++) {
         const int j = nb[t];
-        const float *kj = K + (size_t)j * d, *vj = V + (size_t)j * d;
-        double dp = 0.0;
-        for (int c = 0; c < d; c++) dp += (double)dyi[c] * (double)vj[c];
-        const double ds = s[t] * (dp - D);
+        const float *kj = K + (size_t)j * d;
+        const double ds = row_ds(dyi, V, d, nb, s, D, t);
         for (int c = 0; c < d; c++) {
             dqi[c] += ds * inv_sqrt_d * (double)kj[c];
-            dK[(size_t)j * d + c] += ds * inv_sqrt_d * (double)qi[c];
-            dV[(size_t)j * d + c] += s[t] * (double)dyi[c];
+            if (dK) {
+                dK[(size_t)j * d + c] += ds * inv_sqrt_d * (double)qi[c];
+                dV[(size_t)j * d + c] += s[t] * (double)dyi[c];
+            }
         }
     }
 }
@@ -407,6 +428,118 @@ static void *bworker(void *arg) {
     free(s);
     free(mark);
     return NULL;
+}
+
+/* ------------------------------------------------------------------ */
+/* Gradients at chosen positions, for checks at sizes where the whole
+ * gradient would take too long: dq of chosen query rows, dk and dv of chosen
+ * key positions.  The arithmetic is lf_oracle_bwd's: a row's weights and dS
+ * come from row_weights and row_ds, and a key's sums run over the rows i that
+ * attend to it in ascending order, the order in which the whole gradient
+ * adds them, so both give the same bits. */
+
+typedef struct {
+    job_t base;             /* shapes, sets and inputs; rows = the chosen positions */
+    const float *dy;
+    double *o1, *o2;        /* dq of the rows; or dk and dv of the keys */
+    int keys;               /* 0: query rows, 1: key positions */
+} sjob_t;
+
+/* Position of key j in row i's sorted list, or -1 when j is not in N(i). */
+static int find_key(const int *nb, int n, int j) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = lo + (hi - lo) / 2;
+        if (nb[mid] < j) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo < n && nb[lo] == j ? lo : -1;
+}
+
+static void *sworker(void *arg) {
+    sjob_t *sj = (sjob_t *)arg;
+    job_t *jb = &sj->base;
+    const int T = jb->T, d = jb->d;
+    int *nb = (int *)malloc(sizeof(int) * (size_t)T);
+    double *s = (double *)malloc(sizeof(double) * (size_t)T);
+    unsigned char *mark = (unsigned char *)malloc((size_t)T);
+    if (!nb || !s || !mark) { jb->err = 1; free(nb); free(s); free(mark); return NULL; }
+    const size_t nqb = ((size_t)T + RAND_BLOCK - 1) / RAND_BLOCK;
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    for (long long e = jb->tid; e < jb->n_rows; e += jb->n_threads) {
+        const long long flat = jb->rows[e];
+        const long long bh = flat / T;
+        const int x = (int)(flat % T);
+        const int b = (int)(bh / jb->H), h = (int)(bh % jb->H);
+        const int delta = jb->dil ? jb->dil[h] : 1;
+        const int rh = jb->rad ? jb->rad[h] : jb->r;
+        const unsigned char *padrow = jb->pad ? jb->pad + (size_t)b * T : NULL;
+        const int *rb = jb->rblk ? jb->rblk + (size_t)h * nqb * jb->n_rand : NULL;
+        const size_t base = (size_t)bh * T * d;
+        const float *Q = jb->q + base, *K = jb->k + base, *V = jb->v + base, *DY = sj->dy + base;
+        if (!sj->keys) {
+            double *dqi = sj->o1 + (size_t)e * d;
+            for (int c = 0; c < d; c++) dqi[c] = 0.0;
+            const int n = neighbours(T, rh, delta, jb->one_sided, jb->G, padrow, x, nb, rb, jb->n_rand, mark);
+            grad_row(Q + (size_t)x * d, DY + (size_t)x * d, K, V, d, nb, n, s, dqi, NULL, NULL);
+            continue;
+        }
+        double *dkj = sj->o1 + (size_t)e * d, *dvj = sj->o2 + (size_t)e * d;
+        for (int c = 0; c < d; c++) dkj[c] = dvj[c] = 0.0;
+        for (int i = 0; i < T; i++) {
+            const int n = neighbours(T, rh, delta, jb->one_sided, jb->G, padrow, i, nb, rb, jb->n_rand, mark);
+            const int t = find_key(nb, n, x);
+            if (t < 0) continue;
+            const float *qi = Q + (size_t)i * d, *dyi = DY + (size_t)i * d;
+            const double D = row_weights(qi, dyi, K, V, d, nb, n, s);
+            const double ds = row_ds(dyi, V, d, nb, s, D, t);
+            for (int c = 0; c < d; c++) {
+                dkj[c] += ds * inv_sqrt_d * (double)qi[c];
+                dvj[c] += s[t] * (double)dyi[c];
+            }
+        }
+    }
+    free(nb);
+    free(s);
+    free(mark);
+    return NULL;
+}
+
+static int srun(const float *q, const float *k, const float *v, const float *dy, int B, int H, int T, int d,
+                int r, const int *rad, int one_sided, const int *rblk, int n_rand, const int *dil,
+                const int *gidx, int ng, const unsigned char *pad, const long long *pos, long long n_pos,
+                double *o1, double *o2, int keys, int n_threads) {
+    if (check_args(B, H, T, d, r, rad, one_sided, dil)) return -1;
+    if (check_rand(H, T, dil, rblk, n_rand)) return -1;
+    if (ng < 0 || (ng > 0 && !gidx) || n_pos < 0 || (n_pos > 0 && !pos)) return -1;
+    for (long long e = 0; e < n_pos; e++)
+        if (pos[e] < 0 || pos[e] >= (long long)B * H * T) return -1;
+    gset_t G;
+    if (gset_make(&G, gidx, ng, T)) return -1;
+    if (n_threads <= 0) n_threads = host_threads();
+    if ((long long)n_threads > n_pos) n_threads = n_pos > 0 ? (int)n_pos : 1;
+    sjob_t *jobs = (sjob_t *)calloc((size_t)n_threads, sizeof(sjob_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); free(G.pos); return -1; }
+    for (int t = 0; t < n_threads; t++) {
+        job_t j = {q, k, v, B, H, T, d, r, rad, one_sided, rblk, n_rand, dil, &G, pad, pos, n_pos, NULL, NULL,
+                   n_threads, t, 0};
+        jobs[t].base = j;
+        jobs[t].dy = dy;
+        jobs[t].o1 = o1;
+        jobs[t].o2 = o2;
+        jobs[t].keys = keys;
+    }
+    for (int t = 1; t < n_threads; t++)
+        if (pthread_create(&th[t], NULL, sworker, &jobs[t])) { jobs[t].base.err = 1; th[t] = 0; }
+    sworker(&jobs[0]);
+    int err = 0;
+    for (int t = 1; t < n_threads; t++) if (th[t]) pthread_join(th[t], NULL);
+    for (int t = 0; t < n_threads; t++) err |= jobs[t].base.err;
+    free(jobs);
+    free(th);
+    free(G.pos);
+    return err ? -1 : n_threads;
 }
 
 /* ------------------------------------------------------------------ */
@@ -453,6 +586,29 @@ int lf_oracle_bwd(const float *q, const float *k, const float *v, const float *d
     return err ? -1 : n_threads;
 }
 
+
+/* dq of chosen query rows (same arguments as lf_oracle_bwd): rows[e] =
+ * (b*H + h)*T + i -> dq_rows[e][d].  Returns the thread count used, or -1 on
+ * invalid arguments. */
+int lf_oracle_bwd_rows(const float *q, const float *k, const float *v, const float *dy, int B, int H,
+                       int T, int d, int r, const int *radius, int one_sided, const int *rand_blocks,
+                       int n_rand, const int *dilation, const int *global_idx, int n_global,
+                       const unsigned char *key_padding_mask, const long long *rows, long long n_rows,
+                       double *dq_rows, int n_threads) {
+    return srun(q, k, v, dy, B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
+                n_global, key_padding_mask, rows, n_rows, dq_rows, NULL, 0, n_threads);
+}
+
+/* dk and dv of chosen key positions: keys[e] = (b*H + h)*T + j ->
+ * dk_keys[e][d], dv_keys[e][d]. */
+int lf_oracle_bwd_keys(const float *q, const float *k, const float *v, const float *dy, int B, int H,
+                       int T, int d, int r, const int *radius, int one_sided, const int *rand_blocks,
+                       int n_rand, const int *dilation, const int *global_idx, int n_global,
+                       const unsigned char *key_padding_mask, const long long *keys, long long n_keys,
+                       double *dk_keys, double *dv_keys, int n_threads) {
+    return srun(q, k, v, dy, B, H, T, d, r, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
+                n_global, key_padding_mask, keys, n_keys, dk_keys, dv_keys, 1, n_threads);
+}
 
 /* Full forward: out[B][H][T][d] in fp64.  radius: [H] per-head radii or
  * NULL (then r for every head); one_sided: 0 two-sided, 1 one-sided.

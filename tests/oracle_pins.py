@@ -38,7 +38,9 @@ one of them.  The pins:
   pass): torch float64 autograd through the dense brute force, central
   finite differences of the oracle's own forward, and the sum rules
   sum_j dk_j = 0 (softmax weights sum to one, so the dS of a row sums to
-  zero) and sum_j dv_j = sum of dy over the rows that attend to something.
+  zero) and sum_j dv_j = sum of dy over the rows that attend to something;
+  the gradient at chosen rows and keys (used where the whole gradient would
+  take too long) against autograd and, bit for bit, the whole gradient.
 """
 import numpy as np
 import torch
@@ -442,6 +444,32 @@ def check_grad_sum_rules(lib=None):
                     assert not np.any(dq[b, h][pr]) and not np.any(dk[b, h][pr]) and not np.any(dv[b, h][pr])
 
 
+def check_grad_selected_positions(lib=None):
+    # dq of chosen rows and dk, dv of chosen keys (the entry points that make
+    # full-size sampled checks possible): torch autograd of the dense brute
+    # force, and the same bits as the whole gradient
+    for e, c in enumerate(random_cases(12, seed0=13, Ts=(1, 7, 33, 64, 130))):
+        dy = _dy(1300 + e, c["q"].shape)
+        B, H, T, d = c["q"].shape
+        n = B * H * T
+        sel = np.random.default_rng(e).choice(n, size=min(n, 24), replace=False)
+        sel[-1] = n - 1
+        args = (c["q"], c["k"], c["v"], dy, c["r"])
+        kw = dict(dilation=c["dil"], global_idx=c["G"], key_padding_mask=c["pad"], lib=lib, one_sided=c["one"],
+                  random_blocks=c["rb"])
+        dq_s = oracle.bwd_rows(*args, sel, **kw)
+        dk_s, dv_s = oracle.bwd_keys(*args, sel, **kw)
+        ref = dense_grads_autograd(c, dy.numpy())
+        for name, got, want in (("dq", dq_s, ref[0]), ("dk", dk_s, ref[1]), ("dv", dv_s, ref[2])):
+            want = want.reshape(-1, d)[sel]
+            err = np.max(np.abs(got - want)) if got.size else 0.0
+            assert err <= 1e-11 * max(1.0, np.max(np.abs(want)) if want.size else 1.0), \
+                f"{name} at chosen positions vs autograd: {err} (T={T})"
+        whole = oracle.bwd(*args, **kw)
+        for got, w in zip((dq_s, dk_s, dv_s), whole):
+            assert np.array_equal(got, w.reshape(-1, d)[sel])
+
+
 # --------------------------------------------------------------------------
 # log-sum-exp of each row
 
@@ -494,4 +522,4 @@ def check_lse(lib=None):
 ALL_CHECKS = [check_dense_bruteforce, check_lse, check_closed_form_counts, check_neighbour_sets,
               check_invariants, check_identity_and_dense_limits, check_window_exclusivity,
               check_dilation_split, check_rows_entry_point, check_grad_autograd,
-              check_grad_finite_differences, check_grad_sum_rules]
+              check_grad_finite_differences, check_grad_sum_rules, check_grad_selected_positions]

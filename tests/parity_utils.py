@@ -74,3 +74,19 @@ def sample_rows(inp, n_random, seed=0):
                         rows.add(base + x)
     rows |= set(int(x) for x in rng.choice(B * H * T, size=n_random, replace=False))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def sample_keys(inp, n_heads, n_random, seed=0):
+    """Key positions for sampled full-size gradient parity (a key's dk, dv sum
+    over every row that attends to it, so a global key costs a whole head):
+    in n_heads (b, h) pairs (the first, the last, the rest random) the
+    positions sample_rows would take there; anywhere, n_random random keys."""
+    B, H, T, d = inp.q.shape
+    rng = np.random.default_rng(seed)
+    heads = {0, B * H - 1}
+    while len(heads) < min(n_heads, B * H):
+        heads.add(int(rng.integers(0, B * H)))
+    every = sample_rows(inp, n_random=0, seed=seed)
+    keys = set(int(x) for x in every if int(x) // T in heads)
+    keys |= set(int(x) for x in rng.choice(B * H * T, size=min(n_random, B * H * T), replace=False))
+    return np.array(sorted(keys), dtype=np.int64)

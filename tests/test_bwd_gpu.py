@@ -12,7 +12,7 @@ import torch
 import oracle
 import sparse_long_sequence_lf_amd as lf
 from sparse_long_sequence_lf_amd import workloads as W
-from parity_utils import TOL, require_gpu
+from parity_utils import TOL, require_gpu, sample_keys, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -126,6 +126,44 @@ def test_bwd_workloads(name, dtype):
     label = f"{name} dtype={dt} shape={tuple(inp.q.shape)}"
     print("case " + label, flush=True)
     check(inp, dy, dt, label)
+
+
+# ---- every workload at its full size (the size the benchmark times): dq of
+# sampled rows, dk and dv of sampled keys
+@pytest.mark.parametrize("name", [w.name for w in W.WORKLOADS])
+def test_bwd_full_size_sampled(name):
+    w = W.workload(name)
+    inp = W.make_inputs(w)
+    dy = W.make_grad(inp, w.seed + 41)
+    B, H, T, d = inp.q.shape
+    print(f"case {name} shape={tuple(inp.q.shape)} full size", flush=True)
+    dev = torch.device("cuda:0")
+    kpm = None if inp.key_padding_mask is None else inp.key_padding_mask.to(dev)
+    grads = lf.attn_bwd(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), dy.to(dev), inp.r, inp.dilation,
+                        inp.global_idx, key_padding_mask=kpm, one_sided=inp.one_sided,
+                        random_blocks=inp.random_blocks)
+    torch.cuda.synchronize()
+    rows = sample_rows(inp, n_random=1500, seed=w.seed)
+    keys = sample_keys(inp, n_heads=3, n_random=200, seed=w.seed + 1)
+    kw = dict(dilation=inp.dilation, global_idx=inp.global_idx, key_padding_mask=inp.key_padding_mask,
+              one_sided=inp.one_sided, random_blocks=inp.random_blocks)
+    ref_dq = oracle.bwd_rows(inp.q, inp.k, inp.v, dy, inp.r, rows, **kw)
+    ref_dk, ref_dv = oracle.bwd_keys(inp.q, inp.k, inp.v, dy, inp.r, keys, **kw)
+    bad = []
+    for nm, g, sel, ref in (("dq", grads[0], rows, ref_dq), ("dk", grads[1], keys, ref_dk),
+                            ("dv", grads[2], keys, ref_dv)):
+        got = g.reshape(-1, d)[torch.from_numpy(sel).to(dev)].float().cpu().double().numpy()
+        scale = max(1.0, float(np.max(np.abs(ref))))
+        err = float(np.max(np.abs(got - ref)))
+        print(f"  {nm}: {len(sel)} positions, max abs err {err:.3e} (scale {scale:.2f})", flush=True)
+        if err > TOL[w.dtype] * scale:
+            bad.append((nm, err, scale))
+    assert not bad, (name, bad)
+    if inp.key_padding_mask is not None:
+        pad = inp.key_padding_mask.to(dev).bool()
+        for g in grads:
+            for b in range(B):
+                assert not torch.any(g[b][:, pad[b]]), (name, "padded rows not zero")
 
 
 def test_bwd_repeatable():

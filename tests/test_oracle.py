@@ -50,7 +50,10 @@ MUTANTS = [
     ("grad_dk_unscaled", "dK[(size_t)j * d + c] += ds * inv_sqrt_d * (double)qi[c];",
      "dK[(size_t)j * d + c] += ds * (double)qi[c];"),
     ("grad_weights_unnormalised", "s[t] /= l;", ""),
-    ("grad_dq_from_v", "dqi[c] += ds * inv_sqrt_d * (double)kj[c];", "dqi[c] += ds * inv_sqrt_d * (double)vj[c];"),
+    ("grad_dq_from_v", "dqi[c] += ds * inv_sqrt_d * (double)kj[c];", "dqi[c] += ds * inv_sqrt_d * (double)V[(size_t)j * d + c];"),
+    ("keys_dv_from_q", "dvj[c] += s[t] * (double)dyi[c];", "dvj[c] += s[t] * (double)qi[c];"),
+    ("keys_search_off_by_one", "return lo < n && nb[lo] == j ? lo : -1;",
+     "return lo + 1 < n && nb[lo] == j ? lo + 1 : -1;"),
     ("grad_dv_sign", "dV[(size_t)j * d + c] += s[t] * (double)dyi[c];", "dV[(size_t)j * d + c] -= s[t] * (double)dyi[c];"),
 ]
 
