@@ -100,8 +100,12 @@ struct Geo {
     static_assert(2 * 64 * (16 * CB + 4) * 4 <= RING, "phase merge area inside the ring");
 };
 
-// waves per SIMD each instantiation is compiled for (registers: 512 / that)
-template <int D, int NP> struct Occupancy { static constexpr int v = NP == 1 ? (D == 128 ? 2 : 4) : (D == 32 ? 2 : 1); };
+// waves per SIMD each instantiation is compiled for (registers: 512 / that).
+// bf16 at d = 64 with both padding and random blocks takes three: at four it
+// spilled 20 bytes a lane.
+template <int D, int NP, bool PAD, bool RAND> struct Occupancy {
+    static constexpr int v = NP == 1 ? (D == 128 ? 2 : (D == 64 && PAD && RAND ? 3 : 4)) : (D == 32 ? 2 : 1);
+};
 
 // the plane products of a split product a*b, smallest first: with three
 // parts per operand the six (i, j) with i + j <= 2; with one part (bf16) the
@@ -491,7 +495,7 @@ __device__ __forceinline__ void gkey_fold(WaveState<D, NP>& W, const GKey<D, NP>
 // The tile kernel.
 
 template <int D, typename ET, typename OT, bool PAD, bool RAND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Occupancy<D, Elem<ET>::NP>::v)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Occupancy<D, Elem<ET>::NP, PAD, RAND>::v)))
 void tile_kernel(const Args A) {
     constexpr int NP = Elem<ET>::NP;
     using G = Geo<D, NP>;
@@ -813,8 +817,13 @@ void tile_kernel(const Args A) {
         __syncthreads();
     }
     if (!early0) issue_stage(0, 0, 0u);
-    barrier_lds_loads();               // Q and stage 0 have landed
+    // Without padding nothing reads stage 0 before the first step, whose own
+    // barrier waits for it: the Q and global-key registers are waited for
+    // where they are used, so the phase-0 waves fold the global key while
+    // stage 0 is still landing.  (With no block at all nothing was issued.)
+    // With padding, stage 0's padded V rows are cleared here first.
     if constexpr (PAD) {
+        barrier_lds_loads();           // Q and stage 0 have landed
         pm_cur = pad_word(pm_cur);
         // the V loader clears the 16-byte pieces it brought for padded rows
         const bool padA = ((pm_cur >> rowA) & 1u) != 0u, padB = ((pm_cur >> rowB) & 1u) != 0u;
