@@ -53,7 +53,7 @@ typedef enum {
 } lf_status_t;
 
 /* Limits of the library (LF_E_UNSUPPORTED beyond them). */
-#define LF_HEAD_DIM 64        /* d of lf_attn_bwd; the forward takes any of LF_FWD_HEAD_DIMS */
+#define LF_HEAD_DIM 64        /* d of the matrix-core backward (bf16); every call takes any of LF_FWD_HEAD_DIMS */
 #define LF_FWD_HEAD_DIMS {32, 64, 128}
 #define LF_MAX_HEADS 128      /* H */
 #define LF_MAX_GLOBALS 512    /* distinct global positions */
@@ -237,7 +237,8 @@ const char *lf_build_hash(void);
  *     dq_i = sum_j dS_ij k_j / sqrt(d),   dk_j = sum_i dS_ij q_i / sqrt(d),
  *     dv_j = sum_i P_ij dy_i.
  *
- *   q, k, v   DEVICE [B][H][T][d] of `dtype`, the forward's inputs; d = 64.
+ *   q, k, v   DEVICE [B][H][T][d] of `dtype`, the forward's inputs; d one
+ *             of LF_FWD_HEAD_DIMS (32, 64, 128).
  *   dy        DEVICE [B][H][T][d] of `dtype`: the gradient of the loss with
  *             respect to the forward's output.  Rows of padded queries are
  *             ignored (their output is zero whatever q holds).
@@ -247,13 +248,16 @@ const char *lf_build_hash(void);
  *             at padded positions).  They must not overlap one another or
  *             the inputs.
  *
- * bf16 inputs run on the matrix cores: the weights come from the forward's
- * per-row log-sum-exp, which lf_attn_bwd obtains by running the forward
- * into its workspace first (lf_attn_bwd_ex takes the caller's instead).
- * Products of bf16 values accumulate in fp32; the weights P and the dS_ij
- * enter the products over rows as bf16 (rounded to nearest even), and D_i
- * is taken from the bf16 output y.  fp32 inputs run on the vector units in
- * fp32 throughout, recomputing each row's statistics.  Results are rounded
+ * bf16 inputs at d = 64 run on the matrix cores: the weights come from the
+ * forward's per-row log-sum-exp, which lf_attn_bwd obtains by running the
+ * forward into its workspace first (lf_attn_bwd_ex takes the caller's
+ * instead).  Products of bf16 values accumulate in fp32; the weights P and
+ * the dS_ij enter the products over rows as bf16 (rounded to nearest even),
+ * and D_i is taken from the bf16 output y.  fp32 inputs (every d) and bf16
+ * inputs at d = 32 and 128 run on the vector units in fp32 arithmetic,
+ * recomputing each row's statistics (bf16 products are exact in fp32; in
+ * the sums over rows of dk and dv a bf16 row is scaled by its weight
+ * rounded to bf16).  Results are rounded
  * to `dtype` (bf16 to nearest even).  Every result is written by exactly
  * one thread, without atomics: repeated calls give the same bits.
  * Ownership and errors as lf_attn_fwd: all checks run before any HIP
@@ -275,9 +279,9 @@ lf_status_t lf_attn_bwd(const void *q, const void *k, const void *v, const void 
  *   out       DEVICE [B][H][T][d] of `dtype`, 16-byte aligned: the output of
  *             lf_attn_fwd_ex for the same inputs and arguments.
  *   lse       DEVICE [B][H][T] floats, 4-byte aligned: that call's lse.
- * Both given or both NULL (NULL: as lf_attn_bwd).  With bf16 inputs they
- * replace the forward pass lf_attn_bwd would run; fp32 inputs do not read
- * them.  Neither may overlap dq, dk or dv.  Other arguments as lf_attn_bwd.
+ * Both given or both NULL (NULL: as lf_attn_bwd).  With bf16 inputs at
+ * d = 64 they replace the forward pass lf_attn_bwd would run; the vector-unit
+ * path (fp32, bf16 at d = 32 or 128) does not read them.  Neither may overlap dq, dk or dv.  Other arguments as lf_attn_bwd.
  */
 lf_status_t lf_attn_bwd_ex(const void *q, const void *k, const void *v, const void *dy,
                            const void *out, const float *lse,

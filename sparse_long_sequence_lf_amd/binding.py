@@ -21,7 +21,7 @@ LF_E_UNSUPPORTED = 2
 LF_E_NOMEM = 3
 LF_E_HIP = 4
 STATUS_NAMES = {0: "LF_OK", 1: "LF_E_INVALID", 2: "LF_E_UNSUPPORTED", 3: "LF_E_NOMEM", 4: "LF_E_HIP"}
-HEAD_DIM = 64          # d of the backward
+HEAD_DIM = 64          # d of the matrix-core backward (bf16); the backward takes every d of FWD_HEAD_DIMS
 FWD_HEAD_DIMS = (32, 64, 128)
 MAX_HEADS = 128
 MAX_GLOBALS = 512

@@ -1,7 +1,8 @@
 // lf_bwd.h -- the launch record shared by the host code of lf_attn_bwd
-// (lf_host.cpp) and the fp32 backward kernels (lf_bwd_kernels.hip); bf16
-// input takes the matrix-core kernels of lf_bwd_mfma.hip, whose argument is
-// in lf_kernels.h.  Internal to
+// (lf_host.cpp) and the vector-unit backward kernels (lf_bwd_kernels.hip:
+// fp32 input, and bf16 input at d = 32 and 128); bf16 input at d = 64 takes
+// the matrix-core kernels of lf_bwd_mfma.hip, whose argument is in
+// lf_kernels.h.  Internal to
 // liblfattn.so; the public interface is include/lf_attn.h.
 #ifndef LF_BWD_H
 #define LF_BWD_H
@@ -16,7 +17,7 @@
 // 4, 8 or 16; a wave holds 64 / that many rows of one residue class, and
 // head_chunk counts chunks of that many class positions.  These kernels
 // serve fp32 inputs, the precision path, which is most used on small
-// problems: there more lanes a row (more waves, fewer registers) measured
+// problems (and bf16 inputs at d = 32 and 128): there more lanes a row (more waves, fewer registers) measured
 // faster (B = 1, H = 2, T = 1024, r = 64: 179 us at four, 140 at eight,
 // 105 at sixteen, with the global-row statistics reduced across lanes),
 // while on the T = 4096, r = 256 shape with 12 heads four were faster than
@@ -42,10 +43,10 @@ struct BwdArgs {
     const int32_t *hord;         // [H] heads by decreasing radius: the longest waves are dealt out first
     void *stats;                 // float2 [B*H][T]: (log2-sum-exp of the scaled scores, D_i)
     float4 *gstat;               // [B*H*n_g][n_split]: a split's (max, sum, sum of p dP) of a global row
-    float *gpart;                // [B*H*n_g][n_split][192]: a split's partial dq, dk, dv of a global position
+    float *gpart;                // [B*H*n_g][n_split][3 d]: a split's partial dq, dk, dv of a global position
     int B, H, T, n_g, one_sided;
     int n_chunks;                // head_chunk[H]: class chunks of one batch entry (the host's copy)
-    int n_split, split_len;      // global rows and columns: splits of split_len positions (256 x per-thread count)
+    int n_split, split_len;      // global rows and columns: splits of split_len positions (a multiple of 64)
     // random key blocks of 64 (undilated heads only), or n_rand = 0
     const int32_t *rtab;         // [H][ceil(T/64)][n_rand] key blocks per query block, ascending, -1 = none
     const int32_t *inv_off;      // [H][ceil(T/64) + 1] CSR offsets into inv_list per key block

@@ -25,7 +25,7 @@ extern "C" hipError_t lfk_launch(const lfk::Args *A, const lfk::Plan *P, int dty
 extern "C" int lfk_supports_d(int d);
 extern "C" hipError_t lfk_noalloc_scratch(void **ptr);
 extern "C" hipError_t lfk_write_plan(const void *plan, size_t bytes, void *dst, int *zero, int n_zero, void *stream);
-extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs *A, const void *const *t, void *stream);
+extern "C" hipError_t lfk_bwd_launch(const lfk::BwdArgs *A, const void *const *t, int d, int bf16, void *stream);
 extern "C" hipError_t lfk_bwd_dq(const lfk::BwdBandArgs *A, const lfk::Plan *P, void *stream);
 extern "C" hipError_t lfk_bwd_dkdv(const lfk::BwdBandArgs *A, const lfk::Plan *P, void *stream);
 
@@ -589,7 +589,7 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     if (!radius) return fail(LF_E_INVALID, "radius must be a host array of H radii");
     if (dtype != LF_F32 && dtype != LF_BF16) return fail(LF_E_UNSUPPORTED, "unknown dtype %d", (int)dtype);
     if (B < 1 || H < 1 || T < 1) return fail(LF_E_INVALID, "B, H, T must be >= 1 (got %d, %d, %d)", B, H, T);
-    if (d != LF_HEAD_DIM) return fail(LF_E_UNSUPPORTED, "head dimension %d: only %d is built", d, LF_HEAD_DIM);
+    if (!lfk_supports_d(d)) return fail(LF_E_UNSUPPORTED, "head dimension %d: only 32, 64 and 128 are built", d);
     if (H > LF_MAX_HEADS) return fail(LF_E_UNSUPPORTED, "H = %d exceeds %d", H, LF_MAX_HEADS);
     if (T > LF_MAX_SEQ) return fail(LF_E_UNSUPPORTED, "T = %d exceeds %d", T, LF_MAX_SEQ);
     if (one_sided != 0 && one_sided != 1) return fail(LF_E_INVALID, "one_sided = %d must be 0 or 1", one_sided);
@@ -701,8 +701,9 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     }
     tab[o_hc + H] = (uint32_t)chunks;
     if ((long long)B * chunks >= (1LL << 31)) return fail(LF_E_UNSUPPORTED, "problem needs too many waves");
-    // bf16: the forward's plan (its band tiles are the band kernels' tiles)
-    const bool mfma = dtype == LF_BF16;
+    // bf16 at d = 64: the matrix-core kernels on the forward's plan (its band
+    // tiles are their tiles); fp32, and bf16 at other d: the vector units
+    const bool mfma = dtype == LF_BF16 && d == LF_HEAD_DIM;
     FwdPlan F;
     if (mfma) {
         lf_status_t st = plan_fwd(B, H, T, d, 0, radius, one_sided, rand_blocks, n_rand, dilation, global_idx,
@@ -720,19 +721,21 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     if (!w) return st;
     st = grow(*w, w->bwd_stats, (size_t)B * H * T * 2 * sizeof(float), false, stream);
     if (st != LF_OK) return st;
-    // global rows and keys: splits of a multiple of 256 positions, as many
-    // as bring the grid to about 2048 workgroups (at most 64, at least 1)
+    // global rows and keys (vector path): splits of a multiple of 64
+    // positions (a workgroup's 64 groups of four lanes take one position
+    // each in turn), as many as bring the grid to about 2048 workgroups (at
+    // most 64, at least 1)
     const long long recs = (long long)B * H * (long long)G.size();
     long long want = recs > 0 ? std::min(64LL, std::max(1LL, cdiv(2048, recs))) : 1;
-    want = std::min(want, cdiv(T, 256));
-    const long long per_thread = cdiv(T, 256 * want);
-    const int split_len = (int)(256 * per_thread);
+    want = std::min(want, cdiv(T, 64));
+    const long long per_group = cdiv(T, 64 * want);
+    const int split_len = (int)(64 * per_group);
     const int n_split = (int)cdiv(T, split_len);
     const size_t n_rec = (size_t)recs * n_split;
     if (n_rec >= ((size_t)1 << 31)) return fail(LF_E_UNSUPPORTED, "too many global-row splits");
     const size_t gstat_bytes = (n_rec * 16 + 255) / 256 * 256;
     if (n_rec > 0 && !mfma) {
-        st = grow(*w, w->bwd_gpart, gstat_bytes + n_rec * 192 * sizeof(float), false, stream);
+        st = grow(*w, w->bwd_gpart, gstat_bytes + n_rec * 3 * (size_t)d * sizeof(float), false, stream);
         if (st != LF_OK) return st;
     }
     const void *dtab = nullptr;
@@ -760,7 +763,7 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     A.inv_list = n_rand > 0 ? (const int32_t *)dt + o_inv : nullptr;
     const void *t[7] = {q, k, v, dy, dq, dk, dv};
     if (!mfma) {
-        hipError_t e = lfk_bwd_launch(&A, t, stream);
+        hipError_t e = lfk_bwd_launch(&A, t, d, dtype == LF_BF16, stream);
         if (e != hipSuccess) return fail(LF_E_HIP, "kernel launch: %s", hipGetErrorString(e));
         return LF_OK;
     }

@@ -228,7 +228,8 @@ DY, DQ, DK, DV = 0x50000000, 0x60000000, 0x70000000, 0x80000000
     ("null dy", dict(dy=None), lf.LF_E_INVALID),
     ("null dq", dict(dq=None), lf.LF_E_INVALID),
     ("bad dtype", dict(dtype=7), lf.LF_E_UNSUPPORTED),
-    ("d = 128", dict(d=128), lf.LF_E_UNSUPPORTED),
+    ("d = 96", dict(d=96), lf.LF_E_UNSUPPORTED),
+    ("d = 16", dict(d=16), lf.LF_E_UNSUPPORTED),
     ("T = 0", dict(T=0), lf.LF_E_INVALID),
     ("negative radius", dict(r=[8, -1]), lf.LF_E_INVALID),
     ("one_sided = 2", dict(one=2), lf.LF_E_INVALID),

@@ -103,6 +103,27 @@ def test_bwd_named_edge_cases(dt):
         check(inp, dy, dt, label)
 
 
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_bwd_head_dims(d, dt):
+    # d = 32 and 128 (the vector-unit kernels for both dtypes): ragged T,
+    # dilation, globals over several splits, padding, one-sided windows,
+    # random key blocks
+    for seed, (B, H, T, pad, n_g, n_rand, one) in enumerate([(2, 3, 1, "none", 0, 0, False),
+                                                             (2, 3, 65, "right", 1, 0, False),
+                                                             (2, 3, 300, "random", 2, 0, True),
+                                                             (1, 2, 700, "right", 3, 0, False),
+                                                             (2, 2, 257, "none", 1, 2, False)]):
+        base = W.random_case(7100 + 31 * seed + d, B=B, H=H, T=T, d=d, dtype=dt, pad=pad, n_global=n_g,
+                             n_rand=n_rand)
+        inp = W.Inputs(base.q, base.k, base.v, base.r, base.dilation, base.global_idx, base.lengths,
+                       base.key_padding_mask, one_sided=one, random_blocks=base.random_blocks)
+        dy = W.make_grad(inp, 7200 + seed)
+        label = f"d={d} dt={dt} B={B} H={H} T={T} r={inp.r} dil={inp.dilation} G={inp.global_idx} pad={pad}"
+        print("case " + label, flush=True)
+        check(inp, dy, dt, label)
+
+
 # workload shapes with the head count cut where the oracle would take long
 BWD_CASES = {
     "fp32-b1h2t1024-r64-g1": dict(),
