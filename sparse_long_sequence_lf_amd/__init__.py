@@ -1,4 +1,4 @@
-"""Longformer sparse self-attention forward for AMD Instinct MI355X (gfx950).
+"""Longformer sparse self-attention (forward and backward) for AMD Instinct MI355X (gfx950).
 
 The compute lives in liblfattn.so (C ABI, include/lf_attn.h); this package
 only marshals torch tensors into it.

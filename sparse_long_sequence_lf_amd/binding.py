@@ -293,11 +293,13 @@ def attn_bwd(q, k, v, dy, r, dilation: Optional[Sequence[int]] = None,
              global_idx: Optional[Sequence[int]] = None, key_padding_mask=None, out=None, stream=None,
              one_sided: bool = False, random_blocks=None, y=None, lse=None):
     """Gradients (dq, dk, dv) of the forward for the upstream gradient ``dy``,
-    torch tensors [B, H, T, 64] like q; the same window, dilation, global,
+    torch tensors [B, H, T, d] like q (d in {32, 64, 128}); the same window, dilation, global,
     random-block and padding arguments as ``attn_fwd``.  ``out`` may be a
     tuple of three tensors like q to write into.  ``y`` and ``lse``: the
     forward's output (like q) and its lse (float32 [B, H, T]) from the same
-    arguments, both or neither (then bf16 input runs the forward first)."""
+    arguments, both or neither (then bf16 input at d = 64 runs the forward
+    first; the vector-unit path, fp32 or bf16 at d = 32 and 128, reads
+    neither)."""
     import torch
 
     if q.dtype == torch.bfloat16:
