@@ -14,18 +14,20 @@
 #include "lf_attn.h"
 
 // Lanes that share one row (query or key) in the backward's band kernels,
-// 4, 8 or 16; a wave holds 64 / that many rows of one residue class, and
-// head_chunk counts chunks of that many class positions.  These kernels
-// serve fp32 inputs, the precision path, which is most used on small
-// problems (and bf16 inputs at d = 32 and 128): there more lanes a row (more waves, fewer registers) measured
-// faster (B = 1, H = 2, T = 1024, r = 64: 179 us at four, 140 at eight,
-// 105 at sixteen, with the global-row statistics reduced across lanes),
-// while on the T = 4096, r = 256 shape with 12 heads four were faster than
-// eight (743 against 922 us).
-#ifndef LFB_LANES_PER_ROW
-#define LFB_LANES_PER_ROW 16
-#endif
-#define LFB_ROWS_PER_WAVE (64 / LFB_LANES_PER_ROW)
+// 4, 8 or 16, chosen per call (BwdArgs::lpr); a wave holds 64 / that many
+// rows of one residue class, and head_chunk counts chunks of that many class
+// positions.  These kernels serve fp32 inputs, the precision path (and bf16
+// inputs at d = 32 and 128).  Fewer lanes a row means fewer waves, each
+// holding more channels in registers.  Measured on B = 1, H = 12, T = 4096,
+// r = 256 (one global): fp32 d = 64 1042 us at eight, 1270 at sixteen,
+// 1658 at four (176 registers); fp32 d = 128 1741 at sixteen, 2812 at eight; fp32 d = 32 536
+// at four, 1220 at sixteen; bf16 d = 128 1312 at eight, 1577 at sixteen.
+// So the host takes the fewest lanes that leave each lane 8 fp32 or 16 bf16
+// channels (four at the least), and doubles them while that would make
+// fewer than LFB_MIN_WAVES waves: small problems want more waves (B = 1,
+// H = 2, T = 1024, r = 64, fp32: 179 us at four, 140 at eight, 105 at
+// sixteen).
+#define LFB_MIN_WAVES 2048
 
 // The backward launches' argument (lf_bwd_kernels.hip).  The tables live in
 // one device buffer of the workspace: radius, stride and wave-chunk prefix
@@ -38,7 +40,7 @@ struct BwdArgs {
     const int32_t *glob;         // [n_g] distinct globals, ascending
     const int32_t *rad;          // [H] window radius per head (clamped to T)
     const int32_t *dil;          // [H] stride per head
-    const int32_t *head_chunk;   // [H+1] prefix of the class chunks (LFB_ROWS_PER_WAVE positions) over the heads
+    const int32_t *head_chunk;   // [H+1] prefix of the class chunks (64 / lpr positions) over the heads
                                  // in the order hord lists them
     const int32_t *hord;         // [H] heads by decreasing radius: the longest waves are dealt out first
     void *stats;                 // float2 [B*H][T]: (log2-sum-exp of the scaled scores, D_i)
@@ -52,6 +54,7 @@ struct BwdArgs {
     const int32_t *inv_off;      // [H][ceil(T/64) + 1] CSR offsets into inv_list per key block
     const int32_t *inv_list;     // query blocks that drew the key block, ascending
     int n_rand;
+    int lpr;                     // lanes per row of the band kernels: 4, 8 or 16
 };
 
 }  // namespace lfk

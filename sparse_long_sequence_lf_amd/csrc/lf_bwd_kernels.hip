@@ -62,12 +62,10 @@ __device__ __forceinline__ bool is_global(const uint32_t* __restrict__ gmap, int
 __device__ __forceinline__ bool padded(const uint8_t* __restrict__ pad, int i) { return pad && pad[i] != 0; }
 
 // Lanes per row: the band kernels give each query (or key) row LPR lanes
-// (a wave holds NQ rows), the global-row and global-key kernels give each
-// position LPG lanes.  Dot products end with a sum over a row's lanes.
-constexpr int LPR = LFB_LANES_PER_ROW;
-constexpr int NQ = LFB_ROWS_PER_WAVE;
+// (4, 8 or 16, chosen per call: a wave holds 64 / LPR rows), the global-row
+// and global-key kernels give each position LPG lanes.  Dot products end
+// with a sum over a row's lanes.
 constexpr int LPG = 4;
-static_assert(LPR == 4 || LPR == 8 || LPR == 16, "four, eight or sixteen lanes per row");
 
 // A lane's N channels of a row, as fp32 values.
 template <int N>
@@ -251,11 +249,13 @@ __device__ __forceinline__ void store_slice(ET* __restrict__ p, const Slice<N>& 
 }
 
 // One wave's share of the band kernels: batch b, head h, residue class c of
-// stride delta, and class positions [t0, t0 + NQ) of the nc in the class.
+// stride delta, and class positions [t0, t0 + NQ) of the nc in the class
+// (NQ = rows per wave).
 struct Chunk {
     int b, h, c, t0, nc, delta, r, ra;
 };
 
+template <int NQ>
 __device__ __forceinline__ bool decode(const lfk::BwdArgs& A, long long task, Chunk& k) {
     const long long per_b = A.head_chunk[A.H];
     if (task >= (long long)A.B * per_b) return false;
@@ -374,16 +374,17 @@ constexpr int PREFETCH = sizeof(ET) == 2 ? 4 : 2;
 // ---------------------------------------------------------------------------
 // dq and the row statistics of the non-global queries.
 
-template <int D, typename ET>
+template <int D, typename ET, int LPR>
 __global__ __launch_bounds__(256) void rows_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
                                                    const ET* __restrict__ K, const ET* __restrict__ V,
                                                    const ET* __restrict__ DY, ET* __restrict__ DQ,
                                                    float2* __restrict__ stats) {
     constexpr int CS = D / LPR;   // channels per lane
+    constexpr int NQ = 64 / LPR;  // rows per wave
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     Chunk ck;
-    if (!decode(A, (long long)blockIdx.x * 4 + wave, ck)) return;
+    if (!decode<NQ>(A, (long long)blockIdx.x * 4 + wave, ck)) return;
     const int T = A.T;
     const size_t bh = (size_t)ck.b * A.H + ck.h;
     const int part = lane & (LPR - 1);
@@ -485,16 +486,17 @@ __global__ __launch_bounds__(256) void rows_kernel(const lfk::BwdArgs A, const E
 // ---------------------------------------------------------------------------
 // dk and dv of the non-global keys.
 
-template <int D, typename ET>
+template <int D, typename ET, int LPR>
 __global__ __launch_bounds__(256) void cols_kernel(const lfk::BwdArgs A, const ET* __restrict__ Q,
                                                    const ET* __restrict__ K, const ET* __restrict__ V,
                                                    const ET* __restrict__ DY, ET* __restrict__ DK,
                                                    ET* __restrict__ DV, const float2* __restrict__ stats) {
     constexpr int CS = D / LPR;
+    constexpr int NQ = 64 / LPR;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     Chunk ck;
-    if (!decode(A, (long long)blockIdx.x * 4 + wave, ck)) return;
+    if (!decode<NQ>(A, (long long)blockIdx.x * 4 + wave, ck)) return;
     const int T = A.T;
     const size_t bh = (size_t)ck.b * A.H + ck.h;
     const int part = lane & (LPR - 1);
@@ -810,6 +812,33 @@ __global__ __launch_bounds__(D) void combine_kernel(const lfk::BwdArgs A, ET* __
     DV[o] = (ET)sv;
 }
 
+template <int D, typename ET, int LPR>
+void launch_band(const lfk::BwdArgs* A, const void* const* t, hipStream_t s, bool cols) {
+    const long long waves = (long long)A->B * A->n_chunks;   // one wave per chunk of 64 / LPR rows
+    const dim3 gl((unsigned)((waves + 3) / 4)), blk(256);
+    const ET* const* in = (const ET* const*)t;
+    float2* st = (float2*)A->stats;
+    if (!cols)
+        hipLaunchKernelGGL((rows_kernel<D, ET, LPR>), gl, blk, 0, s, *A, in[0], in[1], in[2], in[3], (ET*)t[4], st);
+    else
+        hipLaunchKernelGGL((cols_kernel<D, ET, LPR>), gl, blk, 0, s, *A, in[0], in[1], in[2], in[3], (ET*)t[5],
+                           (ET*)t[6], st);
+}
+
+template <int D, typename ET>
+void launch_band_any(const lfk::BwdArgs* A, const void* const* t, hipStream_t s, bool cols) {
+    // four lanes a row would hold d / 4 = 32 fp32 channels per operand at
+    // d = 128: eight at the least there
+    if constexpr (D <= 64) {
+        if (A->lpr == 4) {
+            launch_band<D, ET, 4>(A, t, s, cols);
+            return;
+        }
+    }
+    if (A->lpr <= 8) launch_band<D, ET, 8>(A, t, s, cols);
+    else launch_band<D, ET, 16>(A, t, s, cols);
+}
+
 template <int D, typename ET>
 hipError_t launch(const lfk::BwdArgs* A, const void* const* t, hipStream_t s) {
     const ET* q = (const ET*)t[0];
@@ -820,16 +849,15 @@ hipError_t launch(const lfk::BwdArgs* A, const void* const* t, hipStream_t s) {
     ET* dk = (ET*)t[5];
     ET* dv = (ET*)t[6];
     float2* st = (float2*)A->stats;
-    const long long waves = (long long)A->B * A->n_chunks;   // one wave per chunk of NQ rows
-    const dim3 gl((unsigned)((waves + 3) / 4)), blk(256);
+    const dim3 blk(256);
     const long long recs = (long long)A->B * A->H * A->n_g;
     const dim3 gs((unsigned)(recs * A->n_split)), gc((unsigned)recs);
-    hipLaunchKernelGGL((rows_kernel<D, ET>), gl, blk, 0, s, *A, q, k, v, dy, dq, st);
+    launch_band_any<D, ET>(A, t, s, false);
     if (A->n_g > 0) {
         hipLaunchKernelGGL((grows_stats_kernel<D, ET>), gs, blk, 0, s, *A, q, k, v, dy);
         hipLaunchKernelGGL((grows_dq_kernel<D, ET>), gs, blk, 0, s, *A, q, k, v, dy, st);
     }
-    hipLaunchKernelGGL((cols_kernel<D, ET>), gl, blk, 0, s, *A, q, k, v, dy, dk, dv, st);
+    launch_band_any<D, ET>(A, t, s, true);
     if (A->n_g > 0) {
         hipLaunchKernelGGL((gcols_kernel<D, ET>), gs, blk, 0, s, *A, q, k, v, dy, st);
         hipLaunchKernelGGL((combine_kernel<D, ET>), gc, dim3(D), 0, s, *A, dq, dk, dv);

@@ -684,6 +684,13 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
             tab[o_off + (size_t)h * (nqb + 1) + nqb] = (uint32_t)at;
         }
     }
+    // lanes per row of the vector-unit band kernels (lf_bwd.h): as few as
+    // leave a lane 8 fp32 channels or 16 bf16 channels (four at the least),
+    // doubled while the problem would make fewer than LFB_MIN_WAVES waves
+    const long long all_rows = (long long)B * H * T;
+    int lpr = std::max(4, dtype == LF_BF16 ? d / 16 : d / 8);
+    while (lpr < 16 && all_rows * lpr / 64 < LFB_MIN_WAVES) lpr *= 2;
+    const int rows_per_wave = 64 / lpr;
     // waves are dealt out head by head, the heads of the largest radius first
     std::vector<int> hord(H);
     for (int h = 0; h < H; h++) hord[h] = h;
@@ -697,7 +704,7 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
         tab[o_hc + o] = (uint32_t)chunks;
         tab[o_ord + o] = (uint32_t)h;
         const long long qq = T / delta, rm = T % delta;
-        chunks += rm * cdiv(qq + 1, LFB_ROWS_PER_WAVE) + (delta - rm) * cdiv(qq, LFB_ROWS_PER_WAVE);
+        chunks += rm * cdiv(qq + 1, rows_per_wave) + (delta - rm) * cdiv(qq, rows_per_wave);
     }
     tab[o_hc + H] = (uint32_t)chunks;
     if ((long long)B * chunks >= (1LL << 31)) return fail(LF_E_UNSUPPORTED, "problem needs too many waves");
@@ -758,6 +765,7 @@ lf_status_t attn_bwd(const void *q, const void *k, const void *v, const void *dy
     A.gstat = n_rec > 0 ? (float4 *)w->bwd_gpart.ptr : nullptr;
     A.gpart = n_rec > 0 ? (float *)((char *)w->bwd_gpart.ptr + gstat_bytes) : nullptr;
     A.n_rand = n_rand;
+    A.lpr = lpr;
     A.rtab = n_rand > 0 ? (const int32_t *)dt + o_rtab : nullptr;
     A.inv_off = n_rand > 0 ? (const int32_t *)dt + o_off : nullptr;
     A.inv_list = n_rand > 0 ? (const int32_t *)dt + o_inv : nullptr;

@@ -108,14 +108,17 @@ def test_bwd_named_edge_cases(dt):
 def test_bwd_head_dims(d, dt):
     # d = 32 and 128 (the vector-unit kernels for both dtypes): ragged T,
     # dilation, globals over several splits, padding, one-sided windows,
-    # random key blocks
-    for seed, (B, H, T, pad, n_g, n_rand, one) in enumerate([(2, 3, 1, "none", 0, 0, False),
-                                                             (2, 3, 65, "right", 1, 0, False),
-                                                             (2, 3, 300, "random", 2, 0, True),
-                                                             (1, 2, 700, "right", 3, 0, False),
-                                                             (2, 2, 257, "none", 1, 2, False)]):
+    # random key blocks; the last two cases have rows enough for eight and
+    # four lanes a row (four only at d = 32)
+    for seed, (B, H, T, pad, n_g, n_rand, one, r) in enumerate([(2, 3, 1, "none", 0, 0, False, None),
+                                                                (2, 3, 65, "right", 1, 0, False, None),
+                                                                (2, 3, 300, "random", 2, 0, True, None),
+                                                                (1, 2, 700, "right", 3, 0, False, None),
+                                                                (2, 2, 257, "none", 1, 2, False, None),
+                                                                (1, 4, 4200, "right", 2, 0, False, 150),
+                                                                (2, 4, 4200, "random", 1, 0, True, 100)]):
         base = W.random_case(7100 + 31 * seed + d, B=B, H=H, T=T, d=d, dtype=dt, pad=pad, n_global=n_g,
-                             n_rand=n_rand)
+                             n_rand=n_rand, r=r)
         inp = W.Inputs(base.q, base.k, base.v, base.r, base.dilation, base.global_idx, base.lengths,
                        base.key_padding_mask, one_sided=one, random_blocks=base.random_blocks)
         dy = W.make_grad(inp, 7200 + seed)
