@@ -26,12 +26,13 @@
 //                 global rows: every valid key, in splits of split_len keys
 //                 (one workgroup each, reduced through LDS): the splits'
 //                 (max, sum, sum of p dP), then their parts of dq.
-//   cols_kernel   lane = a non-global key of one residue class: dk_j, dv_j
-//                 from the queries whose window holds j, plus the global rows.
+//   cols_kernel   non-global keys of one residue class: dk_j, dv_j from the
+//                 queries whose window holds j, plus the global rows.
 //   gcols_kernel  global keys: every valid query, in splits likewise.
 //   combine_kernel  adds the splits' parts of dq, dk, dv of the global positions.
-// In the band kernels sixteen lanes share a row (d / 16 channels each) and a
-// wave holds 4 rows of one residue class; the other side's rows stream past,
+// In the band kernels 4, 8 or 16 lanes share a row (chosen per call; see
+// lf_bwd.h) and a wave holds 64 / that many rows of one residue class; the
+// other side's rows stream past,
 // the next one loaded while the current one is used.  In the global-row and
 // global-key kernels four lanes share a position (d / 4 channels each) and a
 // workgroup's 64 groups of four take a split's positions in turn.  No
