@@ -34,7 +34,10 @@ from typing import Dict, List
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
+# the kernels and the host code that plans their tasks (the plan decides
+# what a launch runs: split counts, task order)
 KERNEL_SOURCES = ["sparse_long_sequence_lf_amd/csrc/lf_fwd_kernels.hip",
+                  "sparse_long_sequence_lf_amd/csrc/lf_host.cpp",
                   "sparse_long_sequence_lf_amd/csrc/lf_kernels.h",
                   "sparse_long_sequence_lf_amd/csrc/lf_device.h",
                   "sparse_long_sequence_lf_amd/csrc/lf_decode.h"]
