@@ -397,21 +397,7 @@ lf_status_t plan_fwd(int B, int H, int T, int d, int r, const int32_t *radius, i
     if (P.n_g > 0) {
         P.n_ggroups = (int)cdiv(P.n_g, BM);
         P.g_pad = P.n_ggroups * BM;
-        // about 144 global-row tasks in all (a little over one per two
-        // compute units), no split longer than 4096 keys, at most 64 splits
-        // per head (which bounds the combine's reads), at least 64 keys a
-        // split.  A split shares its unit with band tiles and slows them, so
-        // fewer, longer splits disturb fewer units: on B1 H12 T4096 r256
-        // with one global, 228 splits of 224 keys took 16.43 us a forward
-        // call and 144 of 352 keys 15.54 us (one-sided 13.96 -> 12.84 us).
-        const long long per = (long long)B * H * P.n_ggroups;
-        long long ns = std::max(144 / per, cdiv(T, 4096));
-        if (ns < 1) ns = 1;
-        if (ns > 64) ns = 64;
-        long long sl = cdiv(cdiv(T, ns), 32) * 32;
-        if (sl < 64) sl = 64;
-        P.split_len = (int)(sl < T ? sl : cdiv(T, 32) * 32);
-        P.n_split = (int)cdiv(T, P.split_len);
+        lfk::global_splits((long long)B * H * P.n_ggroups, T, &P.split_len, &P.n_split);
         n_glob_tasks = (long long)B * H * P.n_split * P.n_ggroups;
         P.mg_per_bh = lfk::magic_for((long long)P.n_split * P.n_ggroups);
         P.mg_nsplit = lfk::magic_for(P.n_split);

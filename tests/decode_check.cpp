@@ -156,6 +156,34 @@ int main() {
             }
         }
     }
+    // ---- the global-row split plan: splits cover [0, T) exactly, lengths are
+    // multiples of 32 of at least 64 keys (or the whole 32-rounded sequence),
+    // at most 64 splits, no split over 4096 keys unless 64 splits cannot
+    // cover T otherwise, and about 144 tasks when T is short enough (between
+    // half and all of them: lengths rounded up to 32 keys make fewer splits)
+    {
+        std::vector<int> Ts = {1, 31, 32, 33, 63, 64, 65, 100, 128, 700, 1000, 1024, 4095, 4096, 4097, 8192,
+                               16384, 65536, 262143, 262144, 262145, 1 << 20, (1 << 24) - 1};
+        for (int i = 0; i < 300; i++) Ts.push_back(1 + (int)(rng() % (1 << 24)));
+        std::vector<long long> pers = {1, 2, 3, 11, 12, 13, 47, 48, 64, 143, 144, 145, 1000, 1LL << 20};
+        for (int T : Ts)
+            for (long long per : pers) {
+                int sl = 0, ns = 0;
+                global_splits(per, T, &sl, &ns);
+                const long long T32 = ((long long)T + 31) / 32 * 32;
+                CHECK(sl % 32 == 0 && (sl >= 64 || sl == T32), "T %d per %lld: split %d", T, per, sl);
+                CHECK(ns >= 1 && ns <= 64, "T %d per %lld: %d splits", T, per, ns);
+                CHECK((long long)ns * sl >= T && (long long)(ns - 1) * sl < T, "T %d per %lld: %d x %d", T, per, ns, sl);
+                CHECK(sl <= 4096 || (long long)T > 64LL * 4096 || sl == T32, "T %d per %lld: split %d", T, per, sl);
+                if ((long long)T <= 4096 && per <= 144 && T >= 64LL * 144 / per)
+                    CHECK(2 * per * ns >= 144 - per && per * ns <= 144 + per, "T %d per %lld: %lld tasks", T, per, per * ns);
+                checked++;
+            }
+        // the headline shape: B1 H12, one global, T = 4096 -> 12 splits of 352 keys
+        int sl = 0, ns = 0;
+        global_splits(12, 4096, &sl, &ns);
+        CHECK(sl == 352 && ns == 12, "headline split %d x %d", ns, sl);
+    }
     if (fails) {
         std::printf("FAILED %d\n", fails);
         return 1;
