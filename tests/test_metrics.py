@@ -70,3 +70,17 @@ def test_workload_counts_closed_form():
     assert metrics.useful_pairs(1, 2, 1024, 64, None, [0]) == 259708
     assert metrics.useful_pairs(1, 12, 4096, 256, None, [0]) == 24517608
     assert metrics.useful_pairs(1, 12, 4096, 128, [1, 1, 2, 2, 2, 2, 3, 3, 3, 3, 4, 4], []) == 12136704
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # one GPU only: bench.py exits with status 2 and says why, before it
+    # touches torch or the library
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU only" in res.stderr
+    assert res.stdout == ""
