@@ -379,3 +379,38 @@ def test_unequal_radii_many_globals(dt):
         print(f"case B={B} H={H} T={T} n_g={len(set(inp.global_idx))} radii={rads} dil={inp.dilation}", flush=True)
         err = max_err(gpu_fwd(inp), oracle_full(inp))
         assert err <= TOL[dt], err
+
+
+@pytest.mark.parametrize("case", [
+    # one (b, h): 64 splits of 64 keys, the most a head takes (the combine
+    # reads eight rounds of eight records)
+    dict(seed=91, B=1, H=1, T=4096, dtype="f32", r=30, n_global=1, pad="none"),
+    # two heads, a ragged length: 53 splits of 96 keys, the last one short
+    dict(seed=92, B=1, H=2, T=5000, dtype="bf16", r=70, n_global=3, pad="none"),
+    # twelve heads: 12 splits of 352 keys (the headline's split plan) with padding
+    dict(seed=93, B=1, H=12, T=4096, dtype="f32", r=16, n_global=2, pad="right"),
+], ids=["f32-64splits", "bf16-53splits-ragged", "f32-12splits-pad"])
+def test_global_row_split_counts(case):
+    # the global-row split plan at its extremes: every global row (and its
+    # lse) against the oracle, and a sample of the other rows
+    c = dict(case)
+    inp = W.random_case(c.pop("seed"), **c, max_dil=1)
+    B, H, T, d = inp.q.shape
+    dt = "f32" if inp.q.dtype == torch.float32 else "bf16"
+    print(f"case {tuple(inp.q.shape)} {dt} r={inp.r} G={sorted(set(inp.global_idx))}", flush=True)
+    q, k, v = (x.to("cuda:0") for x in (inp.q, inp.k, inp.v))
+    kpm = None if inp.key_padding_mask is None else inp.key_padding_mask.to("cuda:0")
+    lse = torch.empty(B, H, T, dtype=torch.float32, device="cuda:0")
+    out = lf.attn_fwd(q, k, v, inp.r, inp.dilation, inp.global_idx, key_padding_mask=kpm, lse=lse)
+    torch.cuda.synchronize()
+    G = sorted(set(inp.global_idx))
+    rows = sorted(set(G) | set(range(0, T, 97)) | {T - 1})
+    ref, ref_lse = oracle.fwd_lse(inp.q, inp.k, inp.v, inp.r, inp.dilation, inp.global_idx, inp.key_padding_mask)
+    err = max_err(out[:, :, rows], ref[:, :, rows])
+    print(f"  rows {len(rows)}: max abs err {err:.3e}", flush=True)
+    assert err <= TOL[dt], err
+    got_lse = lse[:, :, G].cpu().double().numpy()
+    want_lse = ref_lse[:, :, G]
+    fin = np.isfinite(want_lse)
+    assert np.array_equal(np.isfinite(got_lse), fin)
+    assert np.max(np.abs(got_lse[fin] - want_lse[fin]), initial=0.0) <= 1e-4 * max(1.0, np.max(np.abs(want_lse[fin]), initial=0.0))
